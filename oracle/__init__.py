@@ -1,0 +1,304 @@
+"""CPU oracle for FP8 scaled quantization and the scaled FP8 GEMM.
+
+TEST INFRASTRUCTURE ONLY.  The product path (the HIP library and its Python
+binding) never imports, links or runs anything in this package; only the tests,
+the smoke check and the benchmark's CPU-baseline leg do.  It shares no code
+with the HIP path.
+
+The element-wise parts live in plain C (``fp8_oracle.c``, built with gcc,
+OpenMP over elements); this module marshals numpy arrays into it and adds the
+GEMM reference, which uses numpy's float64 matmul as its one library step.
+
+Conventions: bf16 tensors are numpy ``uint16`` arrays of bf16 bit patterns;
+FP8 codes are ``uint8``; scales are ``float32`` scalars.  ``fmt`` is 0 for
+E4M3FN, 1 for E5M2.
+
+Pages cited (title, section): "Megatron FP8" (sections 1-28),
+"[Pytorch][Common] Hybrid quantization #2817" (TransformerEngine PR),
+"Low Precision Training and Rollout" (vime documentation).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+E4M3FN, E5M2 = 0, 1
+F32, BF16 = 0, 1
+ALGO_MAX, ALGO_MOST_RECENT = 0, 1
+PER_TENSOR, BLOCK_1x128_128x128 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp8_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into ``oracle/liboracle.so``."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
+            vp, fp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)
+            lib.orc_decode.restype = ctypes.c_double
+            lib.orc_decode.argtypes = [i32, i32]
+            lib.orc_fmax.restype = ctypes.c_double
+            lib.orc_fmax.argtypes = [i32]
+            lib.orc_max_code.argtypes = [i32]
+            lib.orc_encode.restype = ctypes.c_uint8
+            lib.orc_encode.argtypes = [i32, f32]
+            lib.orc_encode_buffer.argtypes = [i32, vp, i64, vp]
+            lib.orc_amax.restype = f32
+            lib.orc_amax.argtypes = [vp, i32, i64]
+            lib.orc_current_scale.argtypes = [f32, i32, i32, fp, fp]
+            lib.orc_quantize.argtypes = [vp, i32, i64, i32, f32, vp]
+            lib.orc_dequantize.argtypes = [vp, i32, i64, f32, vp]
+            lib.orc_quantize_rowwise_colwise.argtypes = [vp, i32, i64, i64, i32, f32, vp, vp]
+            lib.orc_quantize_block.argtypes = [vp, i32, i64, i64, i32, i64, i64, vp, vp]
+            lib.orc_transpose.argtypes = [vp, i64, i64, i64, vp]
+            lib.orc_delayed_update.argtypes = [vp, i32, i32, i32, f32, i64, i32, i32, i32, vp, vp]
+            lib.orc_decode_buffer.argtypes = [vp, i32, i64, vp]
+            lib.orc_num_threads.restype = i32
+            _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle needs contiguous arrays"
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _dtype_of(x: np.ndarray) -> int:
+    if x.dtype == np.float32:
+        return F32
+    if x.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle inputs are float32 or uint16 (bf16 bit patterns), got %s" % x.dtype)
+
+
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
+
+
+# --------------------------------------------------------------- formats ----
+def decode(fmt: int, code: int) -> float:
+    """Value of one code ("Megatron FP8", section 2 bit layouts and specials)."""
+    return float(_load().orc_decode(fmt, int(code)))
+
+
+def decode_table(fmt: int) -> np.ndarray:
+    """float64[256]: the value of every code of the format."""
+    return np.array([decode(fmt, c) for c in range(256)], dtype=np.float64)
+
+
+def fmax(fmt: int) -> float:
+    """FP8_MAX: 448 for E4M3FN, 57344 for E5M2."""
+    return float(_load().orc_fmax(fmt))
+
+
+def max_code(fmt: int) -> int:
+    return int(_load().orc_max_code(fmt))
+
+
+def encode(fmt: int, y) -> np.ndarray:
+    """Saturating round-to-nearest-even encode of already-scaled float32 values."""
+    y = np.ascontiguousarray(np.asarray(y, dtype=np.float32))
+    q = np.empty(y.shape, dtype=np.uint8)
+    _load().orc_encode_buffer(fmt, _ptr(y), y.size, _ptr(q))
+    return q
+
+
+# ----------------------------------------------------------------- scaling ---
+def amax(x: np.ndarray) -> np.float32:
+    """max |x| over the tensor; NaN -> canonical NaN; empty -> 0."""
+    x = np.ascontiguousarray(x)
+    return np.float32(_load().orc_amax(_ptr(x), _dtype_of(x), x.size))
+
+
+def current_scale(amax_value, fmt: int, margin: int = 0):
+    """(scale_inv, scale) of current scaling ("Megatron FP8", sections 4 and 10)."""
+    si, sc = ctypes.c_float(), ctypes.c_float()
+    _load().orc_current_scale(ctypes.c_float(np.float32(amax_value)), fmt, int(margin),
+                              ctypes.byref(si), ctypes.byref(sc))
+    return np.float32(si.value), np.float32(sc.value)
+
+
+def reciprocal(s) -> np.float32:
+    """binary32 1/s, the quantizing multiplier paired with a dequant scale s."""
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+        return np.float32(1.0) / np.float32(s)
+
+
+def quantize(x: np.ndarray, fmt: int, scale) -> np.ndarray:
+    """codes of fl32(x * scale), elementwise ("Megatron FP8", section 4)."""
+    x = np.ascontiguousarray(x)
+    q = np.empty(x.shape, dtype=np.uint8)
+    _load().orc_quantize(_ptr(x), _dtype_of(x), x.size, fmt, ctypes.c_float(np.float32(scale)), _ptr(q))
+    return q
+
+
+def dequantize(q: np.ndarray, fmt: int, scale_inv) -> np.ndarray:
+    """fl32(value(q) * scale_inv), elementwise."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    y = np.empty(q.shape, dtype=np.float32)
+    _load().orc_dequantize(_ptr(q), fmt, q.size, ctypes.c_float(np.float32(scale_inv)), _ptr(y))
+    return y
+
+
+def quantize_tensor(x: np.ndarray, fmt: int, *, amax_in=None, margin: int = 0, scale_inv_in=None):
+    """Per-tensor quantization with either current scaling (from ``amax_in``)
+    or a given dequant scale (``scale_inv_in``, the delayed-scaling state).
+
+    Returns dict(q, scale_inv, scale, amax) where ``amax`` is max|x| of this
+    input (the value delayed scaling records after the cast)."""
+    if (amax_in is None) == (scale_inv_in is None):
+        raise ValueError("exactly one of amax_in / scale_inv_in")
+    if amax_in is not None:
+        s, sc = current_scale(amax_in, fmt, margin)
+    else:
+        s = np.float32(scale_inv_in)
+        sc = reciprocal(s)
+    return dict(q=quantize(x, fmt, sc), scale_inv=s, scale=sc, amax=amax(x))
+
+
+def quantize_rowwise_colwise(x: np.ndarray, fmt: int, scale):
+    """Rowwise codes [rows][cols] and columnwise codes [cols][rows] of a 2-D
+    tensor with one per-tensor scale, the columnwise copy taken from the
+    original input ("Hybrid quantization #2817": rowwise and columnwise
+    storage, columnwise source "original")."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    q_row = np.empty((rows, cols), dtype=np.uint8)
+    q_col = np.empty((cols, rows), dtype=np.uint8)
+    _load().orc_quantize_rowwise_colwise(_ptr(x), _dtype_of(x), rows, cols, fmt,
+                                         ctypes.c_float(np.float32(scale)), _ptr(q_row), _ptr(q_col))
+    return q_row, q_col
+
+
+def transpose(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    xt = np.empty((cols, rows), dtype=x.dtype)
+    _load().orc_transpose(_ptr(x), rows, cols, x.itemsize, _ptr(xt))
+    return xt
+
+
+def quantize_blocks(x: np.ndarray, fmt: int, block_rows: int, block_cols: int):
+    """Codes and per-block dequant scales of block current scaling, margin 0
+    ("Low Precision Training and Rollout": 128x128 block FP8 with FP32 scales)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    if rows % block_rows or cols % block_cols:
+        raise ValueError("blocks must tile the matrix")
+    q = np.empty((rows, cols), dtype=np.uint8)
+    s = np.empty((rows // block_rows, cols // block_cols), dtype=np.float32)
+    _load().orc_quantize_block(_ptr(x), _dtype_of(x), rows, cols, fmt, block_rows, block_cols, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quantize_block(x: np.ndarray, fmt: int, block_rows: int):
+    """Block quantization with rowwise and columnwise copies.
+
+    block_rows 128: 128x128 blocks; block_rows 1: 1x128 blocks.  The columnwise
+    copy is the same rule applied to the transposed input, so for 128x128 it
+    is the transpose of the rowwise codes and scales, and for 1x128 it is a
+    fresh quantization of x^T in 1x128 blocks (128 consecutive rows of one
+    column of x share a scale).  Returns q_row [R][C], s_row [R/br][C/128],
+    q_col [C][R], s_col [C/br][R/128]."""
+    q_row, s_row = quantize_blocks(x, fmt, block_rows, 128)
+    q_col, s_col = quantize_blocks(transpose(x), fmt, block_rows, 128)
+    return q_row, s_row, q_col, s_col
+
+
+def delayed_update(hist: np.ndarray, col: int, new_amax, step: int, fmt: int, margin: int,
+                   algo: int, scale: np.ndarray, scale_inv: np.ndarray) -> None:
+    """In-place delayed-scaling update of column ``col`` of ``hist``
+    [history_len][n_cols] and of ``scale``/``scale_inv`` [n_cols]
+    ("Megatron FP8", section 5)."""
+    assert hist.dtype == np.float32 and hist.flags["C_CONTIGUOUS"] and hist.ndim == 2
+    assert scale.dtype == np.float32 and scale_inv.dtype == np.float32
+    L, ncols = hist.shape
+    _load().orc_delayed_update(_ptr(hist), L, ncols, col, ctypes.c_float(np.float32(new_amax)), int(step),
+                               fmt, int(margin), int(algo), _ptr(scale), _ptr(scale_inv))
+
+
+# -------------------------------------------------------------------- GEMM ---
+def decode_codes(q: np.ndarray, fmt: int) -> np.ndarray:
+    """float64 values of a code buffer."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    out = np.empty(q.shape, dtype=np.float64)
+    _load().orc_decode_buffer(_ptr(q), fmt, q.size, _ptr(out))
+    return out
+
+
+def gemm_reference(A: np.ndarray, fa: int, sA, B: np.ndarray, fb: int, sB, mode: int = PER_TENSOR) -> np.ndarray:
+    """float64 reference of C = (A*sA)(B*sB)^T for FP8 codes A [M][K], B [N][K].
+
+    Per tensor: sA, sB are the two dequant scales and
+    R = sA*sB * sum_k val(A[m,k]) val(B[n,k]).
+    Block: sA [M][K/128] (1x128 blocks of A), sB [N/128][K/128] (128x128 blocks
+    of B), and each 128-wide slice of K is summed on its own and weighted by
+    its two block scales:
+    R = sum_kb sA[m,kb] sB[n//128,kb] sum_{k in kb} val(A[m,k]) val(B[n,k]).
+
+    "Megatron FP8", section 27: products are promoted and summed at full
+    precision and only the finished dot product is rounded to the output type;
+    section 6: fp32 accumulation, bf16 output.  Here the sums are float64, in
+    which every E4M3 x E4M3 sum at these sizes is exact."""
+    a = decode_codes(A, fa)
+    b = decode_codes(B, fb)
+    if mode == PER_TENSOR:
+        return (a @ b.T) * (float(np.float32(sA)) * float(np.float32(sB)))
+    M, K = a.shape
+    N = b.shape[0]
+    sA = np.asarray(sA, dtype=np.float64)
+    sB = np.asarray(sB, dtype=np.float64)
+    R = np.zeros((M, N), dtype=np.float64)
+    row_block_of_n = np.arange(N) // 128
+    for kb in range(K // 128):
+        part = a[:, kb * 128:(kb + 1) * 128] @ b[:, kb * 128:(kb + 1) * 128].T
+        R += part * sA[:, kb][:, None] * sB[row_block_of_n, kb][None, :]
+    return R
+
+
+def gemm_reference_entries(A: np.ndarray, fa: int, sA, B: np.ndarray, fb: int, sB, rows, cols,
+                           mode: int = PER_TENSOR) -> np.ndarray:
+    """The same reference at chosen (row, col) positions only, one dot
+    product per entry, for checks at sizes where the full product is too
+    slow on the host."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    ta = decode_table(fa)
+    tb = decode_table(fb)
+    out = np.empty(rows.shape[0], dtype=np.float64)
+    K = A.shape[1]
+    for i, (m, n) in enumerate(zip(rows, cols)):
+        av = ta[A[m]]
+        bv = tb[B[n]]
+        if mode == PER_TENSOR:
+            out[i] = float(np.dot(av, bv)) * (float(np.float32(sA)) * float(np.float32(sB)))
+        else:
+            acc = 0.0
+            for kb in range(K // 128):
+                sl = slice(kb * 128, (kb + 1) * 128)
+                acc += float(np.dot(av[sl], bv[sl])) * float(sA[m, kb]) * float(sB[n // 128, kb])
+            out[i] = acc
+    return out

@@ -1,0 +1,451 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every test here runs on the CPU.  Each one checks the oracle against something
+other than itself: values the pages print, torch's float8 dtypes (a library
+routine), numpy, brute force on small inputs, closed forms and invariants.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from conftest import read_golden
+
+E4, E5 = oracle.E4M3FN, oracle.E5M2
+TORCH_DT = {E4: torch.float8_e4m3fn, E5: torch.float8_e5m2}
+MANT = {E4: 3, E5: 2}
+
+
+def f32_bits(x):
+    return np.asarray(x, dtype=np.float32).view(np.uint32)
+
+
+def torch_encode_clamped(y: np.ndarray, fmt: int) -> np.ndarray:
+    """torch's float8 cast of values clamped to +-FP8_MAX first (torch's cast
+    itself does not saturate).  NaN passes through the clamp."""
+    fm = oracle.fmax(fmt)
+    t = torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32)).clamp(-fm, fm)
+    return t.to(TORCH_DT[fmt]).view(torch.uint8).numpy()
+
+
+# ----------------------------------------------------------- format pins ----
+def test_format_constants_match_printed_values():
+    """"Megatron FP8", section 2 prints (bias, e_max, max) = (7, 8, 448.0) and
+    (15, 15, 57344.0) and the minimum normals 2^-6 / 2^-14."""
+    for name, bias, emax, mx, lmin in read_golden("format_stats.txt"):
+        fmt = E4 if name == "E4M3FN" else E5
+        assert oracle.fmax(fmt) == float(mx)
+        vals = oracle.decode_table(fmt)
+        # bias: the exponent field of the code whose value is 1.0
+        one = [c for c in range(128) if vals[c] == 1.0]
+        assert len(one) == 1
+        assert one[0] >> MANT[fmt] == int(bias)
+        # e_max: exponent of the largest finite value
+        assert math.floor(math.log2(oracle.fmax(fmt))) == int(emax)
+        # min normal: the smallest code with a nonzero exponent field
+        assert vals[1 << MANT[fmt]] == 2.0 ** int(lmin)
+        assert all(0 < vals[c] < 2.0 ** int(lmin) for c in range(1, 1 << MANT[fmt]))
+
+
+def test_decode_all_codes_matches_torch():
+    """All 512 codes decode bit-identically to torch's float8 dtypes (NaN as a class)."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    for fmt in (E4, E5):
+        ref = codes.view(TORCH_DT[fmt]).to(torch.float64).numpy()
+        got = oracle.decode_table(fmt)
+        nan = np.isnan(ref)
+        assert np.array_equal(nan, np.isnan(got))
+        assert np.array_equal(ref[~nan], got[~nan])
+        assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan]))
+
+
+def test_value_sets_counts_and_specials():
+    """E4M3FN: 254 finite codes, 253 distinct values (+0 == -0), NaN only at
+    0x7F/0xFF, no Inf.  E5M2: 248 finite codes, +-Inf at 0x7C/0xFC, six NaN codes."""
+    v4, v5 = oracle.decode_table(E4), oracle.decode_table(E5)
+    assert np.isfinite(v4).sum() == 254 and len(set(v4[np.isfinite(v4)])) == 253
+    assert [c for c in range(256) if np.isnan(v4[c])] == [0x7F, 0xFF]
+    assert not np.isinf(v4).any()
+    assert np.isfinite(v5).sum() == 248 and len(set(v5[np.isfinite(v5)])) == 247
+    assert v5[0x7C] == np.inf and v5[0xFC] == -np.inf
+    assert [c for c in range(256) if np.isnan(v5[c])] == [0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF]
+    # non-negative finite codes are ordered by value
+    for fmt, v in ((E4, v4), (E5, v5)):
+        pos = v[: oracle.max_code(fmt) + 1]
+        assert np.all(np.diff(pos) > 0)
+        assert v[oracle.max_code(fmt)] == oracle.fmax(fmt)
+        # E5M2 set equals the IEEE-style enumeration that skips the all-ones
+        # exponent; E4M3FN adds the seven values 256..448 of that exponent
+    assert len(v5[: 0x7C]) == 124
+    assert sorted(v4[0x78:0x7F]) == [256.0, 288.0, 320.0, 352.0, 384.0, 416.0, 448.0]
+
+
+# ----------------------------------------------------------- encode pins ----
+def _probe_values(fmt: int) -> np.ndarray:
+    """Inputs concentrated where encoders go wrong: every bf16 pattern at a few
+    scales, every midpoint between neighbouring codes and its binary32
+    neighbours, every code value and its neighbours, random bit patterns."""
+    rng = np.random.default_rng(123 + fmt)
+    all_bf16 = workloads.bf16_bits_to_f32(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+    with np.errstate(over="ignore", invalid="ignore"):
+        parts = [all_bf16 * np.float32(s) for s in (1.0, 2.0 ** -7, 2.0 ** 7, 1.0 / 3.0, 3.7, 0.29877)]
+    v = oracle.decode_table(fmt)[: oracle.max_code(fmt) + 1]
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)  # midpoints are exact in binary32
+    assert np.array_equal(mids.astype(np.float64), (v[:-1] + v[1:]) / 2)
+    pts = np.concatenate([mids, v.astype(np.float32), np.float32([oracle.fmax(fmt) * 1.0625])])
+    b = pts.view(np.uint32).astype(np.int64)
+    for d in (-2, -1, 1, 2):
+        parts.append(np.clip(b + d, 0, 0x7F7FFFFF).astype(np.uint32).view(np.float32))
+    parts.append(pts)
+    parts.append(rng.integers(0, 2 ** 32, 1 << 20, dtype=np.uint64).astype(np.uint32).view(np.float32))
+    y = np.concatenate([p.astype(np.float32) for p in parts])
+    return np.concatenate([y, -y])
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_encode_matches_torch_on_clamped_inputs(fmt):
+    """torch's RNE float8 cast of pre-clamped values (a library routine) agrees
+    with the oracle's nearest-value encode, NaN signs included."""
+    y = _probe_values(fmt)
+    got = oracle.encode(fmt, y)
+    ref = torch_encode_clamped(y, fmt)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(hex(int(f32_bits(y[i]))), hex(got[i]), hex(ref[i])) for i in bad[:10]]
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_encode_brute_force_nearest(fmt):
+    """Exhaustive nearest search over all 256 decoded values (ties to the even
+    code, sign copied) on random inputs: an independent statement of the
+    definition."""
+    rng = np.random.default_rng(7)
+    fm = oracle.fmax(fmt)
+    y = np.concatenate([rng.standard_normal(20000) * fm / 3, rng.standard_normal(20000) * fm * 1e-3,
+                        rng.uniform(-2 * fm, 2 * fm, 5000)]).astype(np.float32)
+    table = oracle.decode_table(fmt)
+    finite = [c for c in range(256) if np.isfinite(table[c])]
+    got = oracle.encode(fmt, y)
+    for val, g in zip(y.astype(np.float64), got):
+        a = min(abs(val), fm)
+        best = None
+        for c in finite:
+            if (c >> 7) != int(np.signbit(val)):
+                continue
+            d = abs(abs(table[c]) - a)
+            if best is None or d < best[0] or (d == best[0] and (c & 1) == 0):
+                best = (d, c)
+        assert g == best[1], (val, hex(g), hex(best[1]))
+
+
+def test_encode_ties_golden():
+    for row in read_golden("encode_ties.txt"):
+        fmt = E4 if row[0] == "E4M3FN" else E5
+        if len(row) == 5 and row[2] == "p":
+            value = np.float32(float(row[1]) * 2.0 ** int(row[3]))
+            code = int(row[4], 16)
+        else:
+            value = np.float32(float(row[1]))
+            code = int(row[2], 16)
+        assert oracle.encode(fmt, [value])[0] == code, (row, hex(oracle.encode(fmt, [value])[0]))
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_encode_invariants(fmt):
+    table = oracle.decode_table(fmt)
+    finite = [c for c in range(256) if np.isfinite(table[c])]
+    # round trip of every finite code
+    assert all(oracle.encode(fmt, [np.float32(table[c])])[0] == c for c in finite)
+    # saturation and NaN
+    fm = oracle.fmax(fmt)
+    mc = oracle.max_code(fmt)
+    sat = oracle.encode(fmt, np.float32([fm * 1.5, np.inf, -np.inf, -fm * 4, np.nan, -np.nan]))
+    assert list(sat) == [mc, mc, 0x80 | mc, 0x80 | mc, 0x7F, 0xFF]
+    # monotone in value
+    rng = np.random.default_rng(1)
+    y = np.sort(rng.uniform(-2 * fm, 2 * fm, 50000).astype(np.float32))
+    dec = table[oracle.encode(fmt, y)]
+    assert np.all(np.diff(dec) >= 0)
+    # worst-case relative error 2^-(m+1) in the normal range ("Megatron FP8",
+    # section 23); absolute error at most half the subnormal step below it
+    m = MANT[fmt]
+    min_normal = table[1 << m]
+    yy = rng.uniform(0, fm, 200000).astype(np.float64)
+    yy = np.concatenate([yy, rng.uniform(0, min_normal, 20000)]).astype(np.float32)
+    dv = table[oracle.encode(fmt, yy)]
+    yd = yy.astype(np.float64)
+    normal = yd >= min_normal
+    assert np.all(np.abs(dv[normal] - yd[normal]) <= yd[normal] * 2.0 ** -(m + 1))
+    assert np.all(np.abs(dv[~normal] - yd[~normal]) <= table[1] / 2)
+
+
+# ------------------------------------------------------ scaling pins --------
+def test_amax_matches_numpy():
+    x = workloads.tensor_fp32()
+    assert oracle.amax(x) == np.abs(x).max() == np.float32(2000.0)
+    xb = workloads.delayed_step(3, 256, 384)
+    assert oracle.amax(xb) == np.abs(workloads.bf16_bits_to_f32(xb)).max()
+    y = x.copy()
+    y[5, 7] = -np.nan
+    a = oracle.amax(y)
+    assert np.isnan(a) and f32_bits(a) == 0x7FC00000
+    assert oracle.amax(np.zeros(0, np.float32)) == 0.0
+    assert oracle.amax(np.float32([-0.0, -3.0, np.inf])) == np.inf
+
+
+def test_worked_example_scale():
+    """"Megatron FP8", section 4: x = [-920, 3.5, 511], margin 1 gives
+    s* = 920/448 and s = 2 s*."""
+    g = {r[0]: r[1] for r in read_golden("worked_example.txt")}
+    x = np.float32([g["x0"], g["x1"], g["x2"]])
+    margin = int(g["margin"])
+    a = oracle.amax(x)
+    assert a == np.float32(g["amax"])
+    s_star = np.float32(g["s_star_num"]) / np.float32(g["s_star_den"])
+    s, sc = oracle.current_scale(a, E4, margin)
+    assert s == s_star * np.float32(g["s_factor"])
+    assert f32_bits(s) == 0x40836DB7
+    assert sc == np.float32(1) / s and f32_bits(sc) == 0x3E79525D
+    r = oracle.quantize_tensor(x, E4, amax_in=a, margin=margin)
+    # codes of the scaled values by torch's cast (values already within +-448)
+    ref = torch_encode_clamped(x * sc, E4)
+    assert list(r["q"]) == list(ref) == [0xF6, 0x36, 0x70]
+    # the amax element lands on FP8_MAX / 2^margin exactly
+    assert oracle.decode(E4, r["q"][0]) == -448.0 / 2 ** margin
+    assert list(oracle.dequantize(r["q"], E4, s)) == [np.float32(-224.0) * s, np.float32(0.875) * s,
+                                                       np.float32(128.0) * s]
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_amax_element_lands_on_fmax(fmt):
+    """Invariant: with current scaling and margin 0, an element equal to amax is
+    encoded as +-FP8_MAX, whatever the amax (no overflow, no early clip)."""
+    rng = np.random.default_rng(5)
+    amaxes = np.exp(rng.uniform(np.log(1e-10), np.log(1e30), 20000)).astype(np.float32)
+    mc = oracle.max_code(fmt)
+    for a in amaxes:
+        s, sc = oracle.current_scale(a, fmt, 0)
+        q = oracle.quantize(np.float32([a, -a]), fmt, sc)
+        assert list(q) == [mc, 0x80 | mc], (a, s, sc, q)
+
+
+def test_current_scale_floor_and_specials():
+    s, sc = oracle.current_scale(0.0, E4, 0)
+    assert f32_bits(s) == 0x2720D7C5  # fl32(fl32(1e-12) / 448)
+    s, sc = oracle.current_scale(np.float32(np.nan), E4, 0)
+    assert np.isnan(s) and np.isnan(sc)
+    s, sc = oracle.current_scale(np.float32(np.inf), E5, 0)
+    assert s == np.inf and sc == 0.0
+    # margin multiplies by an exact power of two
+    s0, _ = oracle.current_scale(1234.5, E5, 0)
+    for m in (-3, 1, 5):
+        sm, _ = oracle.current_scale(1234.5, E5, m)
+        assert sm == s0 * np.float32(2.0 ** m)
+
+
+def test_tensor_fp32_scalars():
+    x = workloads.tensor_fp32()
+    r = oracle.quantize_tensor(x, E4, amax_in=oracle.amax(x), margin=1)
+    assert r["amax"] == 2000.0
+    assert f32_bits(r["scale_inv"]) == 0x410EDB6E and f32_bits(r["scale"]) == 0x3DE56041
+    # the sixteen +-2000 outliers land on +-224 = 448 / 2^margin
+    big = np.abs(x) == 2000.0
+    assert big.sum() == 16
+    assert set(r["q"][big].tolist()) <= {0x76, 0xF6}
+
+
+def test_quantize_matches_torch_cast():
+    """A whole tensor: oracle codes == torch cast of clamp(x * scale)."""
+    for fmt in (E4, E5):
+        x = workloads.tensor_fp32(256, 512, seed=11)
+        s, sc = oracle.current_scale(oracle.amax(x), fmt, 1)
+        assert np.array_equal(oracle.quantize(x, fmt, sc), torch_encode_clamped(x * sc, fmt))
+        xb = workloads.delayed_step(2, 128, 256)
+        s, sc = oracle.current_scale(oracle.amax(xb), fmt, 0)
+        xf = workloads.bf16_bits_to_f32(xb)
+        assert np.array_equal(oracle.quantize(xb, fmt, sc), torch_encode_clamped(xf * sc, fmt))
+
+
+def test_dequantize_pins():
+    codes = np.arange(256, dtype=np.uint8)
+    for fmt in (E4, E5):
+        ref = torch.from_numpy(codes).view(TORCH_DT[fmt]).float().numpy()
+        for s in (1.0, 0.5, 2.0 ** 20):
+            got = oracle.dequantize(codes, fmt, s)
+            want = ref * np.float32(s)
+            nan = np.isnan(want)
+            assert np.array_equal(np.isnan(got), nan)
+            assert np.array_equal(got[~nan], want[~nan])
+    # quantize -> dequantize error bound (relative 2^-(m+1) above the normal
+    # range of the scaled values)
+    x = workloads.tensor_fp32(128, 128, seed=3)
+    for fmt in (E4, E5):
+        r = oracle.quantize_tensor(x, fmt, amax_in=oracle.amax(x), margin=0)
+        y = oracle.dequantize(r["q"], fmt, r["scale_inv"]).astype(np.float64)
+        xs = np.abs(x.astype(np.float64))
+        min_normal = oracle.decode(fmt, 1 << MANT[fmt]) * float(r["scale_inv"])
+        n = xs >= min_normal
+        assert np.all(np.abs(y[n] - x[n]) <= xs[n] * 2.0 ** -(MANT[fmt] + 1) * (1 + 1e-6))
+
+
+def test_rowwise_colwise_is_transpose():
+    x = workloads.delayed_step(1, 192, 320)
+    s, sc = oracle.current_scale(oracle.amax(x), E5, 0)
+    q_row, q_col = oracle.quantize_rowwise_colwise(x, E5, sc)
+    assert np.array_equal(q_row, oracle.quantize(x, E5, sc))
+    assert np.array_equal(q_col, q_row.T)
+    assert np.array_equal(oracle.transpose(x), x.T)
+
+
+# ---------------------------------------------------------- delayed pins ----
+def test_delayed_ring_golden():
+    rows = read_golden("delayed_ring.txt")
+    hist = np.zeros((2, 1), np.float32)
+    scale = np.ones(1, np.float32)
+    scale_inv = np.ones(1, np.float32)
+    for step, a, s_used, ring in rows:
+        assert scale_inv[0] == np.float32(s_used), (step, scale_inv)
+        assert scale[0] == np.float32(1) / np.float32(s_used)
+        oracle.delayed_update(hist, 0, np.float32(a), int(step), E4, 0, oracle.ALGO_MAX, scale, scale_inv)
+        assert list(hist[:, 0]) == [float(v) for v in ring.split(",")]
+
+
+def test_delayed_replay_invariants():
+    """32 updates on one shared ring of 16 with alternating formats: the ring
+    holds the last 16 amaxes at slot t % 16 and each scale is max(window) /
+    FP8_MAX of the format that consumes it; "most_recent" uses only the value
+    just written; a second column is untouched by updates of the first."""
+    rng = np.random.default_rng(9)
+    amaxes = np.float32(np.abs(rng.standard_normal(32)) * 3)
+    hist = np.zeros((16, 2), np.float32)
+    hist[:, 1] = 7.0
+    scale = np.ones(2, np.float32)
+    scale_inv = np.ones(2, np.float32)
+    for t in range(32):
+        fmt_next = E4 if (t + 1) % 2 == 0 else E5
+        oracle.delayed_update(hist, 0, amaxes[t], t, fmt_next, 0, oracle.ALGO_MAX, scale, scale_inv)
+        window = amaxes[max(0, t - 15): t + 1]
+        assert scale_inv[0] == window.max() / np.float32(oracle.fmax(fmt_next))
+        assert hist[t % 16, 0] == amaxes[t]
+    assert np.array_equal(hist[:, 0], amaxes[16:])
+    assert np.all(hist[:, 1] == 7.0) and scale[1] == 1.0
+    h2 = np.zeros((4, 1), np.float32)
+    sc2, si2 = np.ones(1, np.float32), np.ones(1, np.float32)
+    for t, a in enumerate([5.0, 1.0, 3.0]):
+        oracle.delayed_update(h2, 0, a, t, E4, 2, oracle.ALGO_MOST_RECENT, sc2, si2)
+        assert si2[0] == np.float32(a) / np.float32(448) * np.float32(4)
+    # a NaN in the window: eff is NaN, not > 0, so the factor falls back to 1
+    oracle.delayed_update(h2, 0, np.float32(np.nan), 3, E4, 0, oracle.ALGO_MAX, sc2, si2)
+    assert si2[0] == 1.0 and sc2[0] == 1.0
+
+
+# ------------------------------------------------------------ block pins ----
+def test_block_128x128_invariants():
+    x = workloads.block_weight(384, 256, seed=21)
+    x[:128, :128] = 0  # an all-zero block
+    q_row, s_row, q_col, s_col = oracle.quantize_block(x, E4, 128)
+    assert q_row.shape == (384, 256) and s_row.shape == (3, 2)
+    assert np.array_equal(q_col, q_row.T) and np.array_equal(s_col, s_row.T)
+    assert f32_bits(s_row[0, 0]) == 0x2720D7C5 and np.all(q_row[:128, :128] == 0)
+    for I in range(3):
+        for J in range(2):
+            blk = np.ascontiguousarray(x[I * 128:(I + 1) * 128, J * 128:(J + 1) * 128])
+            # a block is quantized exactly like a tensor of its own with current scaling
+            r = oracle.quantize_tensor(blk, E4, amax_in=oracle.amax(blk), margin=0)
+            assert s_row[I, J] == r["scale_inv"]
+            assert np.array_equal(q_row[I * 128:(I + 1) * 128, J * 128:(J + 1) * 128], r["q"])
+            if (I, J) != (0, 0):
+                assert np.any((q_row[I * 128:(I + 1) * 128, J * 128:(J + 1) * 128] & 0x7F) == 0x7E)
+
+
+def test_block_1x128_invariants():
+    x = workloads.block_act(256, 384, seed=22)
+    q_row, s_row, q_col, s_col = oracle.quantize_block(x, E4, 1)
+    assert s_row.shape == (256, 3) and q_col.shape == (384, 256) and s_col.shape == (384, 2)
+    xf = workloads.bf16_bits_to_f32(x)
+    for i in (0, 17, 255):
+        for J in range(3):
+            seg = np.ascontiguousarray(x[i, J * 128:(J + 1) * 128])
+            r = oracle.quantize_tensor(seg, E4, amax_in=oracle.amax(seg))
+            assert s_row[i, J] == r["scale_inv"]
+            assert np.array_equal(q_row[i, J * 128:(J + 1) * 128], r["q"])
+    for j in (0, 200, 383):
+        for I in range(2):
+            seg = np.ascontiguousarray(x[I * 128:(I + 1) * 128, j])
+            r = oracle.quantize_tensor(seg, E4, amax_in=oracle.amax(seg))
+            assert s_col[j, I] == r["scale_inv"]
+            assert np.array_equal(q_col[j, I * 128:(I + 1) * 128], r["q"])
+    # every row segment contains its +-FP8_MAX
+    assert np.all(np.any((q_row.reshape(256, 3, 128) & 0x7F) == 0x7E, axis=2) | (
+        np.abs(xf).reshape(256, 3, 128).max(axis=2) == 0))
+
+
+# ------------------------------------------------------------- GEMM pins ----
+def _brute_gemm(A, fa, sA, B, fb, sB, mode):
+    ta, tb = oracle.decode_table(fa), oracle.decode_table(fb)
+    M, K = A.shape
+    N = B.shape[0]
+    R = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                w = ta[A[m, k]] * tb[B[n, k]]
+                if mode == oracle.PER_TENSOR:
+                    acc += w
+                else:
+                    acc += w * sA[m, k // 128] * sB[n // 128, k // 128]
+            R[m, n] = acc * (float(sA) * float(sB) if mode == oracle.PER_TENSOR else 1.0)
+    return R
+
+
+def _random_codes(rng, shape, fmt):
+    c = rng.integers(0, 256, shape).astype(np.uint8)
+    t = oracle.decode_table(fmt)
+    bad = ~np.isfinite(t[c])
+    c[bad] = 0x38
+    return c
+
+
+def test_gemm_reference_brute_force_per_tensor():
+    rng = np.random.default_rng(31)
+    A = _random_codes(rng, (5, 256), E4)
+    B = _random_codes(rng, (7, 256), E5)
+    R = oracle.gemm_reference(A, E4, np.float32(0.75), B, E5, np.float32(3.0))
+    assert np.allclose(R, _brute_gemm(A, E4, np.float32(0.75), B, E5, np.float32(3.0), oracle.PER_TENSOR),
+                       rtol=1e-12, atol=0)
+    ent = oracle.gemm_reference_entries(A, E4, np.float32(0.75), B, E5, np.float32(3.0), [0, 4, 2], [6, 0, 3])
+    assert np.allclose(ent, R[[0, 4, 2], [6, 0, 3]], rtol=1e-12, atol=0)
+
+
+def test_gemm_reference_brute_force_block():
+    rng = np.random.default_rng(32)
+    M, N, K = 3, 256, 384
+    A = _random_codes(rng, (M, K), E5)
+    B = _random_codes(rng, (N, K), E4)
+    sA = np.float32(rng.uniform(0.1, 2, (M, K // 128)))
+    sB = np.float32(rng.uniform(0.1, 2, (N // 128, K // 128)))
+    R = oracle.gemm_reference(A, E5, sA, B, E4, sB, oracle.BLOCK_1x128_128x128)
+    ref = _brute_gemm(A, E5, sA, B, E4, sB, oracle.BLOCK_1x128_128x128)
+    assert np.allclose(R, ref, rtol=1e-12, atol=1e-300)
+    ent = oracle.gemm_reference_entries(A, E5, sA, B, E4, sB, [2, 0], [255, 129], oracle.BLOCK_1x128_128x128)
+    assert np.allclose(ent, ref[[2, 0], [255, 129]], rtol=1e-12, atol=0)
+
+
+def test_gemm_reference_exact_special_cases():
+    """Entries in {0, +-1}: integer sums; all-ones block scales reduce block
+    mode to the per-tensor product; A = 0 gives 0."""
+    rng = np.random.default_rng(33)
+    one, m_one, zero = 0x38, 0xB8, 0x00
+    A = rng.choice(np.uint8([one, m_one, zero]), (16, 128))
+    B = rng.choice(np.uint8([one, m_one, zero]), (24, 128))
+    av = np.where(A == one, 1, np.where(A == m_one, -1, 0))
+    bv = np.where(B == one, 1, np.where(B == m_one, -1, 0))
+    R = oracle.gemm_reference(A, E4, 1.0, B, E4, 1.0)
+    assert np.array_equal(R, (av @ bv.T).astype(np.float64))
+    Rb = oracle.gemm_reference(A, E4, np.ones((16, 1), np.float32), B, E4, np.ones((1, 1), np.float32),
+                               oracle.BLOCK_1x128_128x128)
+    assert np.array_equal(Rb, R)
+    assert not oracle.gemm_reference(np.zeros_like(A), E4, 1.0, B, E4, 1.0).any()
