@@ -191,16 +191,27 @@ void orc_current_scale(float amax, int fmt, int margin, float *scale_inv, float 
     *scale = 1.0f / s;
 }
 
-/* Per-tensor cast, [MFP8] section 4: each element is multiplied by the
- * quantizing scale in binary32 and the product is encoded (saturation and
- * round-to-nearest-even inside orc_encode). */
+/* Code of one scaled element, [MFP8] section 4: the element is multiplied by
+ * the quantizing scale in binary32 and the product is encoded (saturation and
+ * round-to-nearest-even inside orc_encode).  IEEE 754 leaves the sign of a NaN
+ * produced by an invalid product (Inf * 0) unspecified, and hardware differs,
+ * so a NaN product takes the sign rule of multiplication: sign(x) XOR
+ * sign(scale).  For a NaN x and a positive scale that is x's own sign. */
+static uint8_t encode_product(int fmt, float x, float scale)
+{
+    float y = x * scale;
+    if (isnan(y)) {
+        int sx = signbit(x) ? 1 : 0, ss = signbit(scale) ? 1 : 0;
+        return (uint8_t)(((sx ^ ss) << 7) | 0x7F);
+    }
+    return orc_encode(fmt, y);
+}
+
+/* Per-tensor cast: every element with the same quantizing scale. */
 void orc_quantize(const void *x, int dtype, int64_t n, int fmt, float scale, uint8_t *q)
 {
 #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < n; ++i) {
-        float y = load_elem(x, dtype, i) * scale;
-        q[i] = orc_encode(fmt, y);
-    }
+    for (int64_t i = 0; i < n; ++i) q[i] = encode_product(fmt, load_elem(x, dtype, i), scale);
 }
 
 /* Dequantize: value of the code times scale_inv, rounded to binary32
@@ -225,8 +236,7 @@ void orc_quantize_rowwise_colwise(const void *x, int dtype, int64_t rows, int64_
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < rows; ++i)
         for (int64_t j = 0; j < cols; ++j) {
-            float y = load_elem(x, dtype, i * cols + j) * scale;
-            uint8_t c = orc_encode(fmt, y);
+            uint8_t c = encode_product(fmt, load_elem(x, dtype, i * cols + j), scale);
             if (q_row) q_row[i * cols + j] = c;
             if (q_col) q_col[j * rows + i] = c;
         }
@@ -259,7 +269,7 @@ void orc_quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, in
             s_out[I * nbc + J] = s;
             for (int64_t i = I * br; i < (I + 1) * br; ++i)
                 for (int64_t j = J * bc; j < (J + 1) * bc; ++j)
-                    q[i * cols + j] = orc_encode(fmt, load_elem(x, dtype, i * cols + j) * sc);
+                    q[i * cols + j] = encode_product(fmt, load_elem(x, dtype, i * cols + j), sc);
         }
 }
 

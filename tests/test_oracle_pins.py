@@ -449,3 +449,13 @@ def test_gemm_reference_exact_special_cases():
                                oracle.BLOCK_1x128_128x128)
     assert np.array_equal(Rb, R)
     assert not oracle.gemm_reference(np.zeros_like(A), E4, 1.0, B, E4, 1.0).any()
+
+
+def test_nan_product_sign_rule():
+    """NaN products take sign(x) XOR sign(scale) (the sign rule of
+    multiplication; IEEE 754 leaves an invalid product's NaN sign open)."""
+    nan = np.float32(np.nan)
+    x = np.float32([np.inf, -np.inf, 1.0, -nan, nan, -2.0])
+    assert list(oracle.quantize(x, E4, np.float32(0.0))) == [0x7F, 0xFF, 0x00, 0xFF, 0x7F, 0x80]
+    assert list(oracle.quantize(x, E5, nan)) == [0x7F, 0xFF, 0x7F, 0xFF, 0x7F, 0xFF]
+    assert list(oracle.quantize(x, E4, np.float32(-1.0))) == [0xFE, 0x7E, 0xB8, 0x7F, 0xFF, 0x40]
