@@ -1,0 +1,295 @@
+"""Benchmark of the FP8 scaled-quantization hot path on one MI355X.
+
+Headline workload (one "step" = one pass of the path over one batch): the
+delayed-scaling schedule on 8192x8192 bf16 tensors -- each step casts its
+tensor to FP8 with the stored scale (E4M3FN on even steps, E5M2 on odd
+steps) with the input amax fused into the same pass, then updates the
+amax-history ring (length 16, max) and derives the next scale.  The 32
+distinct inputs (4 GiB) are resident in HBM before timing and cycled, so the
+256 MB last-level cache cannot serve repeats.
+
+value = algorithmic bytes moved per step (2 B read + 1 B written per element)
+/ time, in GB/s.  The roofline object is that of the cast kernel, its duration
+taken from HIP events recorded around each cast launch inside the timed
+region, on the stream it runs on.
+
+Every other row of the hot path (amax, current scaling, dequantize, rowwise +
+columnwise, 128x128 and 1x128 block quantization, per-tensor and block-scaled
+GEMMs) is timed at its own workload size and reported under "rows".
+
+The CPU oracle is timed on the host cores on a bounded sample of the same
+workload ("cpu_baseline").
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=64)
+    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--rows", type=int, default=1, help="also time every row of the path (1) or not (0)")
+    p.add_argument("--cpu-baseline", type=int, default=1)
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_scaled_quantization_reduce_amd as fq
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    E4, E5 = fq.E4M3FN, fq.E5M2
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ------------------------------------------------ headline: delayed ----
+    T = 32
+    rows, cols = 8192, 8192
+    n = rows * cols
+    t0 = time.time()
+    host_inputs = workloads.parallel_map(workloads.delayed_step, range(T), workers=16)
+    xs = [to_dev(h) for h in host_inputs]
+    print("# inputs ready in %.1fs" % (time.time() - t0), file=sys.stderr, flush=True)
+    qbufs = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(2)]
+    qsi = [torch.empty(1, device=dev) for _ in range(2)]
+    am = torch.empty(1, device=dev)
+    hist = torch.zeros((16, 1), device=dev)
+    sc = torch.ones(1, device=dev)
+    si = torch.ones(1, device=dev)
+
+    def step(t, ev=None):
+        fmt = E4 if t % 2 == 0 else E5
+        fmt_next = E4 if (t + 1) % 2 == 0 else E5
+        if ev is not None:
+            ev[0].record(stream)
+        fq.fp8_quantize_tensor(xs[t % T], fmt, qbufs[t % 2], scale_inv_in=si, scale_inv_out=qsi[t % 2],
+                               amax_out=am, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fq.fp8_update_scale_delayed(hist, 0, am, t, fmt_next, 0, fq.ALGO_MAX, sc, si, stream=stream)
+
+    t = 0
+    for _ in range(args.warmup):
+        step(t)
+        t += 1
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        step(t, evs[k])
+        t += 1
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    cast_ms = [a.elapsed_time(b) for a, b in evs]
+    cast_avg_ms = float(np.mean(cast_ms))
+    bytes_per_step = 3 * n
+    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    achieved = bytes_per_step / (cast_avg_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "quantize GB/s (% HBM peak); scaled FP8 GEMM TFLOPS (% MFMA peak)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->fp8 (fp32 scale arithmetic)",
+        "data": "synthetic (seeded numpy generators, resident in HBM)",
+        "config": {"workload": "delayed scaling, 32 steps of 8192x8192 bf16, E4M3FN/E5M2 alternating, "
+                               "amax history 16 (max), fused input amax",
+                   "tensor": [rows, cols], "history_len": 16, "distinct_inputs": T,
+                   "bytes_per_step": bytes_per_step, "host_wall_s": round(wall, 4)},
+        "roofline": {"kernel": "cast_kernel (fused amax)", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel_avg_us": round(cast_avg_ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": bytes_per_step},
+    }
+
+    # -------------------------------------------------------- every row ----
+    if args.rows:
+        result["rows"] = time_rows(fq, torch, np, workloads, to_dev, xs, stream)
+
+    # ------------------------------------------------------ CPU baseline ----
+    if args.cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(np, host_inputs, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def _time(torch, stream, fn, reps, rotate=1):
+    """Average ms of fn(i) over reps launches, HIP events on `stream`."""
+    for i in range(2):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(reps):
+        fn(i % rotate)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def time_rows(fq, torch, np, workloads, to_dev, xs, stream):
+    dev = "cuda"
+    out = {}
+    n = xs[0].numel()
+    E4, E5 = fq.E4M3FN, fq.E5M2
+    am = torch.empty(1, device=dev)
+    si = torch.empty(1, device=dev)
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+
+    def gbs(nbytes, ms):
+        g = nbytes / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 5), "GB/s": round(g, 1), "frac_hbm": round(g / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes": int(nbytes)}
+
+    # a1 amax over bf16 8192^2 (2 B/elem)
+    ms = _time(torch, stream, lambda i: fq.fp8_amax(xs[i], am, stream=stream), 20, rotate=len(xs))
+    out["amax_bf16_8192x8192"] = gbs(2 * n, ms)
+
+    # a1+a2+a3 current scaling: amax pass + cast pass (5 B/elem)
+    def current(i):
+        fq.fp8_amax(xs[i], am, stream=stream)
+        fq.fp8_quantize_tensor(xs[i], E4, q, amax_in=am, margin=0, scale_inv_out=si, stream=stream)
+    ms = _time(torch, stream, current, 20, rotate=len(xs))
+    out["current_scaling_amax+cast_bf16_8192x8192"] = gbs(5 * n, ms)
+
+    # a4 dequantize 8192^2 codes -> fp32 (1 + 4 B/elem)
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    qs = [torch.randint(0, 256, (n,), dtype=torch.uint8, device=dev) for _ in range(3)]
+    ms = _time(torch, stream, lambda i: fq.fp8_dequantize(qs[i], E4, si, y, stream=stream), 20, rotate=3)
+    out["dequantize_8192x8192_to_fp32"] = gbs(5 * n, ms)
+
+    # a7 rowwise + columnwise per-tensor cast 8192^2 bf16 (2 + 1 + 1 B/elem)
+    qr = torch.empty((8192, 8192), dtype=torch.uint8, device=dev)
+    qc = torch.empty((8192, 8192), dtype=torch.uint8, device=dev)
+    sc1 = torch.full((1,), 0.01, device=dev)
+    x2 = [x.view(8192, 8192) for x in xs]
+    ms = _time(torch, stream, lambda i: fq.fp8_quantize_rowwise_colwise(
+        x2[i], E4, q_row=qr, q_col=qc, scale_inv_in=sc1, stream=stream), 20, rotate=len(xs))
+    out["rowwise_colwise_bf16_8192x8192"] = gbs(4 * n, ms)
+
+    # a8 block quantization of the 7168x4096 weight (128x128) and the
+    # 4096x7168 activation (1x128), both with their columnwise copies
+    W = torch.randn((7168, 4096), device=dev, generator=torch.Generator(device=dev).manual_seed(1)) * 0.02
+    Ws = [(W * (1 + 0.01 * k)).to(torch.bfloat16) for k in range(10)]
+    qw, qwt = torch.empty((7168, 4096), dtype=torch.uint8, device=dev), torch.empty((4096, 7168), dtype=torch.uint8, device=dev)
+    sw, swt = torch.empty((56, 32), device=dev), torch.empty((32, 56), device=dev)
+    ms = _time(torch, stream, lambda i: fq.fp8_quantize_block(Ws[i], E4, 128, qw, sw, qwt, swt, stream=stream),
+               20, rotate=len(Ws))
+    nW = 7168 * 4096
+    out["block128x128_bf16_7168x4096_with_colwise"] = gbs(4 * nW + 2 * 4 * (nW // 16384), ms)
+    X = torch.randn((4096, 7168), device=dev, generator=torch.Generator(device=dev).manual_seed(2))
+    Xs = [(X * (1 + 0.01 * k)).to(torch.bfloat16) for k in range(10)]
+    qx, qxt = torch.empty((4096, 7168), dtype=torch.uint8, device=dev), torch.empty((7168, 4096), dtype=torch.uint8, device=dev)
+    sx, sxt = torch.empty((4096, 56), device=dev), torch.empty((7168, 32), device=dev)
+    ms = _time(torch, stream, lambda i: fq.fp8_quantize_block(Xs[i], E4, 1, qx, sx, qxt, sxt, stream=stream),
+               20, rotate=len(Xs))
+    out["block1x128_bf16_4096x7168_with_colwise"] = gbs(4 * nW + 4 * (nW // 128) * 2, ms)
+    del Ws, Xs, W, X
+
+    def tflops(flop, ms):
+        tf = flop / (ms * 1e-3) / 1e12
+        return {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / FP8_MFMA_PEAK_TFLOPS, 4),
+                "flop": int(flop)}
+
+    # a9 per-tensor GEMM 8192^3 E4M3 x E4M3 -> bf16 with output amax
+    g = torch.Generator(device=dev).manual_seed(3)
+    A = torch.randint(0, 256, (8192, 8192), dtype=torch.uint8, device=dev, generator=g)
+    B = torch.randint(0, 256, (8192, 8192), dtype=torch.uint8, device=dev, generator=g)
+    A[(A & 0x7F) == 0x7F] = 0  # no NaN codes
+    B[(B & 0x7F) == 0x7F] = 0
+    C = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+    s1 = torch.full((1,), 1e-3, device=dev)
+    cam = torch.empty(1, device=dev)
+    ms = _time(torch, stream, lambda i: fq.fp8_scaled_gemm(A, E4, s1, B, E4, s1, fq.PER_TENSOR, C, cam,
+                                                            stream=stream), 10)
+    out["gemm_per_tensor_e4m3_8192x8192x8192"] = tflops(2 * 8192 ** 3, ms)
+    del A, B, C
+
+    # a10 block-scaled GEMMs of the MLP block: fprop 4096x14336x4096 (E4M3 x
+    # E4M3) and dgrad 4096x4096x14336 (E5M2 x E4M3)
+    Xq = torch.randint(0, 0x7E, (4096, 4096), dtype=torch.uint8, device=dev, generator=g)
+    Wq = torch.randint(0, 0x7E, (14336, 4096), dtype=torch.uint8, device=dev, generator=g)
+    sx = torch.rand((4096, 32), device=dev, generator=g) + 0.5
+    sw = torch.rand((112, 32), device=dev, generator=g) + 0.5
+    Y = torch.empty((4096, 14336), dtype=torch.bfloat16, device=dev)
+    ms = _time(torch, stream, lambda i: fq.fp8_scaled_gemm(Xq, E4, sx, Wq, E4, sw, fq.BLOCK_1x128_128x128, Y, cam,
+                                                            stream=stream), 10)
+    out["gemm_block_fprop_4096x14336x4096"] = tflops(2 * 4096 * 14336 * 4096, ms)
+    dYq = torch.randint(0, 0x7B, (4096, 14336), dtype=torch.uint8, device=dev, generator=g)
+    Wtq = torch.randint(0, 0x7E, (4096, 14336), dtype=torch.uint8, device=dev, generator=g)
+    sdy = torch.rand((4096, 112), device=dev, generator=g) + 0.5
+    swt = torch.rand((32, 112), device=dev, generator=g) + 0.5
+    dX = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+    ms = _time(torch, stream, lambda i: fq.fp8_scaled_gemm(dYq, E5, sdy, Wtq, E4, swt, fq.BLOCK_1x128_128x128, dX,
+                                                            cam, stream=stream), 10)
+    out["gemm_block_dgrad_4096x4096x14336"] = tflops(2 * 4096 * 4096 * 14336, ms)
+    return out
+
+
+def cpu_baseline(np, host_inputs, seconds):
+    """The oracle's delayed-scaling steps on the host, over the first inputs
+    until `seconds` of work have been done (at least one step)."""
+    import oracle
+
+    hist = np.zeros((16, 1), np.float32)
+    sc, si = np.ones(1, np.float32), np.ones(1, np.float32)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        t = done
+        x = host_inputs[t % len(host_inputs)]
+        fmt = oracle.E4M3FN if t % 2 == 0 else oracle.E5M2
+        fmt_next = oracle.E4M3FN if (t + 1) % 2 == 0 else oracle.E5M2
+        r = oracle.quantize_tensor(x, fmt, scale_inv_in=si[0])
+        oracle.delayed_update(hist, 0, r["amax"], t, fmt_next, 0, oracle.ALGO_MAX, sc, si)
+        done += 1
+        if time.perf_counter() - t0 >= seconds or done >= len(host_inputs):
+            break
+    el = time.perf_counter() - t0
+    nbytes = 3 * host_inputs[0].size * done
+    return {"value": round(nbytes / el / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of the 32 delayed-scaling steps (8192x8192 bf16 each: cast with fused amax + ring "
+                      "update), %.1f s" % (done, el)}
+
+
+if __name__ == "__main__":
+    main()

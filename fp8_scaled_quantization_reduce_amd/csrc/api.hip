@@ -1,0 +1,297 @@
+// api.hip -- the extern "C" entry points declared in include/fp8q.h.
+//
+// Host-side validation happens before any HIP call, so argument errors are
+// reported without touching the device; valid calls only enqueue kernels on
+// the caller's stream.  Messages for the last error are thread-local.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/fp8q.h"
+#include "fp8q_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok()
+{
+    g_err[0] = '\0';
+    return FP8Q_OK;
+}
+
+int hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) return fail(FP8Q_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool valid_fmt(int32_t f) { return f == FP8Q_E4M3FN || f == FP8Q_E5M2; }
+bool valid_dtype(int32_t d) { return d == FP8Q_F32 || d == FP8Q_BF16; }
+int64_t dsize(int32_t d) { return d == FP8Q_F32 ? 4 : 2; }
+
+bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    if (!a || !b || na <= 0 || nb <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+// Scale-source checks shared by the per-tensor quantizers.
+int check_scale_src(const char *fn, const float *amax_in, const float *scale_inv_in, const float *scale_inv_out,
+                    const float *scale_out, const float *amax_out)
+{
+    if ((amax_in == nullptr) == (scale_inv_in == nullptr))
+        return fail(FP8Q_EINVAL, "%s: exactly one of amax_in / scale_inv_in must be given", fn);
+    const float *in = amax_in ? amax_in : scale_inv_in;
+    if (!aligned(in, 4)) return fail(FP8Q_EINVAL, "%s: scale input not 4-byte aligned", fn);
+    const float *outs[3] = {scale_inv_out, scale_out, amax_out};
+    for (const float *o : outs) {
+        if (!o) continue;
+        if (!aligned(o, 4)) return fail(FP8Q_EINVAL, "%s: scalar output not 4-byte aligned", fn);
+        if (o == in) return fail(FP8Q_EINVAL, "%s: a scalar output aliases the scale input", fn);
+    }
+    if ((scale_inv_out && (scale_inv_out == scale_out || scale_inv_out == amax_out)) ||
+        (scale_out && scale_out == amax_out))
+        return fail(FP8Q_EINVAL, "%s: scalar outputs alias each other", fn);
+    return FP8Q_OK;
+}
+
+fp8q::ScaleSrc make_src(const float *amax_in, int32_t margin, const float *scale_inv_in)
+{
+    return fp8q::ScaleSrc{amax_in, scale_inv_in, (int)margin};
+}
+
+} // namespace
+
+namespace fp8q {
+
+// One reduction scratch per (device, stream): calls on one stream run in
+// order, so they can share it; different streams never do.  Allocated on the
+// first call that needs it and held until the process ends.
+hipError_t get_grid_scratch(hipStream_t s, GridScratch **out)
+{
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, GridScratch *> table;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(dev, s);
+    auto it = table.find(key);
+    if (it != table.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    void *p = nullptr;
+    e = hipMalloc(&p, 256);
+    if (e != hipSuccess) return e;
+    GridScratch *gs = static_cast<GridScratch *>(p);
+    e = launch_zero_scratch(gs, s);
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return e;
+    }
+    table.emplace(key, gs);
+    *out = gs;
+    return hipSuccess;
+}
+
+} // namespace fp8q
+
+extern "C" {
+
+const char *fp8q_last_error(void) { return g_err; }
+
+int fp8_amax(const void *x, int32_t dtype, int64_t n, float *amax, void *stream)
+{
+    const char *fn = "fp8_amax";
+    if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+    if (n < 0) return fail(FP8Q_EINVAL, "%s: negative n", fn);
+    if (!amax || !aligned(amax, 4)) return fail(FP8Q_EINVAL, "%s: amax must be a 4-byte aligned pointer", fn);
+    if (n > 0 && (!x || !aligned(x, 16))) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
+    if (overlap(x, n * dsize(dtype), amax, 4)) return fail(FP8Q_EINVAL, "%s: amax overlaps x", fn);
+    fp8q::GridScratch *gs = nullptr;
+    hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
+    if (e != hipSuccess) return hip_status(e, fn);
+    return hip_status(fp8q::launch_amax(x, dtype, n, amax, gs, (hipStream_t)stream), fn);
+}
+
+int fp8_quantize_tensor(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *amax_in, int32_t margin,
+                        const float *scale_inv_in, uint8_t *q, float *scale_inv_out, float *scale_out,
+                        float *amax_out, void *stream)
+{
+    const char *fn = "fp8_quantize_tensor";
+    if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+    if (!valid_fmt(fmt)) return fail(FP8Q_EINVAL, "%s: unknown format %d", fn, (int)fmt);
+    if (n < 0) return fail(FP8Q_EINVAL, "%s: negative n", fn);
+    int st = check_scale_src(fn, amax_in, scale_inv_in, scale_inv_out, scale_out, amax_out);
+    if (st) return st;
+    if (n > 0) {
+        if (!x || !aligned(x, 16)) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
+        if (!q || !aligned(q, 16)) return fail(FP8Q_EINVAL, "%s: q must be a 16-byte aligned pointer", fn);
+        if (overlap(x, n * dsize(dtype), q, n)) return fail(FP8Q_EINVAL, "%s: q overlaps x", fn);
+    }
+    fp8q::GridScratch *gs = nullptr;
+    if (amax_out) {
+        hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
+        if (e != hipSuccess) return hip_status(e, fn);
+    }
+    return hip_status(fp8q::launch_cast(x, dtype, n, fmt, make_src(amax_in, margin, scale_inv_in), q, scale_inv_out,
+                                        scale_out, amax_out, gs, (hipStream_t)stream),
+                      fn);
+}
+
+int fp8_dequantize(const uint8_t *q, int32_t fmt, int64_t n, const float *scale_inv, float *y, void *stream)
+{
+    const char *fn = "fp8_dequantize";
+    if (!valid_fmt(fmt)) return fail(FP8Q_EINVAL, "%s: unknown format %d", fn, (int)fmt);
+    if (n < 0) return fail(FP8Q_EINVAL, "%s: negative n", fn);
+    if (!scale_inv || !aligned(scale_inv, 4)) return fail(FP8Q_EINVAL, "%s: scale_inv must be 4-byte aligned", fn);
+    if (n > 0) {
+        if (!q || !aligned(q, 16)) return fail(FP8Q_EINVAL, "%s: q must be a 16-byte aligned pointer", fn);
+        if (!y || !aligned(y, 16)) return fail(FP8Q_EINVAL, "%s: y must be a 16-byte aligned pointer", fn);
+        if (overlap(q, n, y, 4 * n)) return fail(FP8Q_EINVAL, "%s: y overlaps q", fn);
+    }
+    return hip_status(fp8q::launch_dequant(q, fmt, n, scale_inv, y, (hipStream_t)stream), fn);
+}
+
+int fp8_quantize_rowwise_colwise(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt,
+                                 const float *amax_in, int32_t margin, const float *scale_inv_in, uint8_t *q_row,
+                                 uint8_t *q_col, float *scale_inv_out, float *scale_out, float *amax_out,
+                                 void *stream)
+{
+    const char *fn = "fp8_quantize_rowwise_colwise";
+    if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+    if (!valid_fmt(fmt)) return fail(FP8Q_EINVAL, "%s: unknown format %d", fn, (int)fmt);
+    if (rows < 0 || cols < 0) return fail(FP8Q_EINVAL, "%s: negative shape", fn);
+    if (rows % 16 || cols % 16) return fail(FP8Q_EUNSUPPORTED, "%s: rows and cols must be multiples of 16", fn);
+    if (!q_row && !q_col) return fail(FP8Q_EINVAL, "%s: at least one of q_row / q_col is needed", fn);
+    if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 31)
+        return fail(FP8Q_EUNSUPPORTED, "%s: a dimension exceeds 2^31", fn);
+    int st = check_scale_src(fn, amax_in, scale_inv_in, scale_inv_out, scale_out, amax_out);
+    if (st) return st;
+    const int64_t n = rows * cols;
+    if (n > 0) {
+        if (!x || !aligned(x, 16)) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
+        if ((q_row && !aligned(q_row, 16)) || (q_col && !aligned(q_col, 16)))
+            return fail(FP8Q_EINVAL, "%s: q_row / q_col must be 16-byte aligned", fn);
+        if (overlap(x, n * dsize(dtype), q_row, n) || overlap(x, n * dsize(dtype), q_col, n) ||
+            overlap(q_row, n, q_col, n))
+            return fail(FP8Q_EINVAL, "%s: output buffers overlap", fn);
+    }
+    fp8q::GridScratch *gs = nullptr;
+    if (amax_out) {
+        hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
+        if (e != hipSuccess) return hip_status(e, fn);
+    }
+    return hip_status(fp8q::launch_rowwise_colwise(x, dtype, rows, cols, fmt, make_src(amax_in, margin, scale_inv_in),
+                                                   q_row, q_col, scale_inv_out, scale_out, amax_out, gs,
+                                                   (hipStream_t)stream),
+                      fn);
+}
+
+int fp8_quantize_block(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt, int32_t block_rows,
+                       uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col, void *stream)
+{
+    const char *fn = "fp8_quantize_block";
+    if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+    if (!valid_fmt(fmt)) return fail(FP8Q_EINVAL, "%s: unknown format %d", fn, (int)fmt);
+    if (block_rows != 1 && block_rows != 128) return fail(FP8Q_EINVAL, "%s: block_rows must be 1 or 128", fn);
+    if (rows < 0 || cols < 0) return fail(FP8Q_EINVAL, "%s: negative shape", fn);
+    if (rows % 128 || cols % 128) return fail(FP8Q_EUNSUPPORTED, "%s: rows and cols must be multiples of 128", fn);
+    if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 31)
+        return fail(FP8Q_EUNSUPPORTED, "%s: a dimension exceeds 2^31", fn);
+    if ((q_col == nullptr) != (s_col == nullptr)) return fail(FP8Q_EINVAL, "%s: give both q_col and s_col or neither", fn);
+    const int64_t n = rows * cols;
+    if (n == 0) return ok();
+    if (!x || !aligned(x, 16)) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
+    if (!q_row || !aligned(q_row, 16) || !s_row || !aligned(s_row, 4))
+        return fail(FP8Q_EINVAL, "%s: q_row (16-byte) and s_row (4-byte) must be aligned pointers", fn);
+    if (q_col && (!aligned(q_col, 16) || !aligned(s_col, 4)))
+        return fail(FP8Q_EINVAL, "%s: q_col / s_col misaligned", fn);
+    const int64_t ns_row = (rows / block_rows) * (cols / 128) * 4;
+    const int64_t ns_col = (block_rows == 128 ? (cols / 128) * (rows / 128) : cols * (rows / 128)) * 4;
+    if (overlap(x, n * dsize(dtype), q_row, n) || overlap(x, n * dsize(dtype), q_col, n) || overlap(q_row, n, q_col, n) ||
+        overlap(s_row, ns_row, s_col, ns_col) || overlap(q_row, n, s_row, ns_row) || overlap(q_col, n, s_col, ns_col) ||
+        overlap(x, n * dsize(dtype), s_row, ns_row) || overlap(x, n * dsize(dtype), s_col, ns_col))
+        return fail(FP8Q_EINVAL, "%s: buffers overlap", fn);
+    return hip_status(fp8q::launch_block(x, dtype, rows, cols, fmt, block_rows, q_row, s_row, q_col, s_col,
+                                         (hipStream_t)stream),
+                      fn);
+}
+
+int fp8_update_scale_delayed(float *hist, int32_t history_len, int32_t n_cols, int32_t col, const float *new_amax,
+                             int64_t step, int32_t fmt, int32_t margin, int32_t algo, float *scale, float *scale_inv,
+                             void *stream)
+{
+    const char *fn = "fp8_update_scale_delayed";
+    if (!valid_fmt(fmt)) return fail(FP8Q_EINVAL, "%s: unknown format %d", fn, (int)fmt);
+    if (algo != FP8Q_ALGO_MAX && algo != FP8Q_ALGO_MOST_RECENT)
+        return fail(FP8Q_EINVAL, "%s: unknown algo %d", fn, (int)algo);
+    if (history_len < 1 || n_cols < 1 || col < 0 || col >= n_cols)
+        return fail(FP8Q_EINVAL, "%s: need history_len >= 1 and 0 <= col < n_cols", fn);
+    if (step < 0) return fail(FP8Q_EINVAL, "%s: negative step", fn);
+    if (!hist || !new_amax || !scale || !scale_inv || !aligned(hist, 4) || !aligned(new_amax, 4) ||
+        !aligned(scale, 4) || !aligned(scale_inv, 4))
+        return fail(FP8Q_EINVAL, "%s: hist, new_amax, scale, scale_inv must be 4-byte aligned pointers", fn);
+    const int64_t nh = (int64_t)history_len * n_cols * 4;
+    if (overlap(hist, nh, scale, 4 * n_cols) || overlap(hist, nh, scale_inv, 4 * n_cols) ||
+        overlap(scale, 4 * n_cols, scale_inv, 4 * n_cols) || overlap(new_amax, 4, scale, 4 * n_cols) ||
+        overlap(new_amax, 4, scale_inv, 4 * n_cols))
+        return fail(FP8Q_EINVAL, "%s: state buffers overlap", fn);
+    return hip_status(fp8q::launch_delayed(hist, history_len, n_cols, col, new_amax, step, fmt, margin, algo, scale,
+                                           scale_inv, (hipStream_t)stream),
+                      fn);
+}
+
+int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb, const float *sB,
+                    int64_t M, int64_t N, int64_t K, int32_t mode, void *C, int32_t c_dtype, float *amax_out,
+                    void *stream)
+{
+    const char *fn = "fp8_scaled_gemm";
+    if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(FP8Q_EINVAL, "%s: unknown operand format", fn);
+    if (mode != FP8Q_PER_TENSOR && mode != FP8Q_BLOCK_1x128_128x128)
+        return fail(FP8Q_EINVAL, "%s: unknown scaling mode %d", fn, (int)mode);
+    if (!valid_dtype(c_dtype)) return fail(FP8Q_EINVAL, "%s: unknown output dtype %d", fn, (int)c_dtype);
+    if (c_dtype != FP8Q_BF16) return fail(FP8Q_EUNSUPPORTED, "%s: only bf16 output is implemented", fn);
+    if (M < 0 || N < 0 || K < 0) return fail(FP8Q_EINVAL, "%s: negative shape", fn);
+    if (M % 128 || N % 128 || K % 128) return fail(FP8Q_EUNSUPPORTED, "%s: M, N, K must be multiples of 128", fn);
+    if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31)
+        return fail(FP8Q_EUNSUPPORTED, "%s: a dimension exceeds 2^31", fn);
+    if (!sA || !sB || !aligned(sA, 4) || !aligned(sB, 4))
+        return fail(FP8Q_EINVAL, "%s: sA and sB must be 4-byte aligned pointers", fn);
+    if (amax_out && !aligned(amax_out, 4)) return fail(FP8Q_EINVAL, "%s: amax_out misaligned", fn);
+    if (M == 0 || N == 0) {
+        if (amax_out) return hip_status(fp8q::launch_fill_u32(reinterpret_cast<uint32_t *>(amax_out), 0u,
+                                                              (hipStream_t)stream), fn);
+        return ok();
+    }
+    if (!C || !aligned(C, 16)) return fail(FP8Q_EINVAL, "%s: C must be a 16-byte aligned pointer", fn);
+    if (K > 0 && (!A || !B || !aligned(A, 16) || !aligned(B, 16)))
+        return fail(FP8Q_EINVAL, "%s: A and B must be 16-byte aligned pointers", fn);
+    if (overlap(C, M * N * 2, A, M * K) || overlap(C, M * N * 2, B, N * K) || overlap(C, M * N * 2, amax_out, 4))
+        return fail(FP8Q_EINVAL, "%s: C overlaps an input", fn);
+    fp8q::GridScratch *gs = nullptr;
+    if (amax_out) {
+        hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
+        if (e != hipSuccess) return hip_status(e, fn);
+    }
+    return hip_status(fp8q::launch_gemm(A, fa, sA, B, fb, sB, M, N, K, mode, C, amax_out, gs, (hipStream_t)stream),
+                      fn);
+}
+
+} // extern "C"

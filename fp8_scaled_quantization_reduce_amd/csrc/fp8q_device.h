@@ -1,0 +1,185 @@
+// fp8q_device.h -- device-side building blocks of the gfx950 FP8 kernels:
+// the scaled saturating cast, magnitude-bit maxima, wavefront and block
+// reductions, and the scale arithmetic.
+//
+// Pages cited (title, section): "Megatron FP8" (sections 1-28).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+constexpr int kE4M3 = 0;
+constexpr int kE5M2 = 1;
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+// FP8_MAX per format ("Megatron FP8", section 2: 448 for E4M3FN, 57344 for
+// E5M2) and the code of +FP8_MAX.
+template <int F> struct Fmt;
+template <> struct Fmt<kE4M3> {
+    static constexpr float kMax = 448.0f;
+    static constexpr uint32_t kMaxCode = 0x7E;
+};
+template <> struct Fmt<kE5M2> {
+    static constexpr float kMax = 57344.0f;
+    static constexpr uint32_t kMaxCode = 0x7B;
+};
+
+// The amax floor of current scaling ("Megatron FP8", section 4: amax is
+// clamped below at 1e-12 before the division).
+constexpr float kAmaxFloor = 1e-12f;
+constexpr uint32_t kCanonicalNaN = 0x7FC00000u;
+constexpr uint32_t kInfBits = 0x7F800000u;
+
+// ---------------------------------------------------------------- cast ----
+// Two scaled values -> two codes in the low (kHi = false) or high half of a
+// dword.  The hardware converter rounds to nearest even but does not
+// saturate, so the value is first clamped to [-FP8_MAX, FP8_MAX] with med3.
+// med3 turns NaN into -FP8_MAX; encode4s / encode1 repair NaN lanes.
+template <int F, bool kHi>
+__device__ __forceinline__ int cvt2(float a, float b, int old)
+{
+    const float ca = __builtin_amdgcn_fmed3f(a, -Fmt<F>::kMax, Fmt<F>::kMax);
+    const float cb = __builtin_amdgcn_fmed3f(b, -Fmt<F>::kMax, Fmt<F>::kMax);
+    if constexpr (F == kE4M3)
+        return __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, old, kHi);
+    else
+        return __builtin_amdgcn_cvt_pk_bf8_f32(ca, cb, old, kHi);
+}
+
+// Code byte of a NaN product x*scale: 0x7F with the sign bit
+// sign(x) XOR sign(scale).
+__device__ __forceinline__ uint32_t nan_code(float x, float scale)
+{
+    return 0x7Fu | (((__float_as_uint(x) ^ __float_as_uint(scale)) >> 24) & 0x80u);
+}
+
+// Four elements x[k] times their scales s[k] -> one dword of four codes
+// (byte k = code of x[k] * s[k]).
+template <int F>
+__device__ __forceinline__ uint32_t encode4s(float x0, float x1, float x2, float x3, float s0, float s1, float s2,
+                                             float s3)
+{
+    const float y0 = x0 * s0, y1 = x1 * s1, y2 = x2 * s2, y3 = x3 * s3;
+    int r = cvt2<F, false>(y0, y1, 0);
+    r = cvt2<F, true>(y2, y3, r);
+    uint32_t c = (uint32_t)r;
+    // NaN products are rare: one compare per element, a branch per dword.
+    const bool any_nan = (y0 != y0) | (y1 != y1) | (y2 != y2) | (y3 != y3);
+    if (__builtin_expect(any_nan, 0)) {
+        if (y0 != y0) c = (c & 0xFFFFFF00u) | nan_code(x0, s0);
+        if (y1 != y1) c = (c & 0xFFFF00FFu) | (nan_code(x1, s1) << 8);
+        if (y2 != y2) c = (c & 0xFF00FFFFu) | (nan_code(x2, s2) << 16);
+        if (y3 != y3) c = (c & 0x00FFFFFFu) | (nan_code(x3, s3) << 24);
+    }
+    return c;
+}
+
+// Four elements with one scale.
+template <int F>
+__device__ __forceinline__ uint32_t encode4(float x0, float x1, float x2, float x3, float scale)
+{
+    return encode4s<F>(x0, x1, x2, x3, scale, scale, scale, scale);
+}
+
+// One element -> its code byte.
+template <int F>
+__device__ __forceinline__ uint32_t encode1(float x, float scale)
+{
+    const float y = x * scale;
+    const uint32_t c = (uint32_t)cvt2<F, false>(y, y, 0) & 0xFFu;
+    return (y != y) ? nan_code(x, scale) : c;
+}
+
+// bf16 pair in a dword -> two exact floats.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ------------------------------------------------------- magnitude max ----
+// The amax of a tensor is the maximum of |x| over magnitude bit patterns:
+// for non-negative IEEE values the unsigned order of the bits is the numeric
+// order, and every NaN pattern lies above +Inf, so the integer maximum is
+// exact, independent of order, and detects NaN.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t w)
+{
+    u16x2 v;
+    __builtin_memcpy(&v, &w, 4);
+    return v;
+}
+
+// running max of the two bf16 magnitudes held in w (packed 16-bit max)
+__device__ __forceinline__ u16x2 bf16_absmax2(u16x2 acc, uint32_t w)
+{
+    return __builtin_elementwise_max(acc, as_u16x2(w & 0x7FFF7FFFu));
+}
+
+// packed bf16 magnitude max -> fp32 magnitude bits
+__device__ __forceinline__ uint32_t bf16_absmax_to_f32bits(u16x2 acc)
+{
+    const uint32_t m = acc.x > acc.y ? acc.x : acc.y;
+    return m << 16;
+}
+
+__device__ __forceinline__ uint32_t f32_absbits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// A magnitude maximum in fp32 bits -> the amax value's bits (NaN -> canonical).
+__device__ __forceinline__ uint32_t canonical_amax_bits(uint32_t m) { return m > kInfBits ? kCanonicalNaN : m; }
+
+// ---------------------------------------------------------- reductions ----
+// Wavefront (64 lanes) max of an unsigned value with DPP row shifts and row
+// broadcasts; the result is valid in lane 63 and returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    // row_shr:1,2,4,8 give each lane 15 of every 16-lane row the row max
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));
+    // row_bcast:15 (rows 1 and 3) and row_bcast:31 (rows 2 and 3)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Block max (blockDim.x = kThreads, a multiple of 64); every thread gets the
+// result.  `lds` must hold kThreads/64 words.
+template <int kThreads>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *lds)
+{
+    constexpr int kWaves = kThreads / 64;
+    v = wave_max_u32(v);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[wave] = v;
+    __syncthreads();
+    uint32_t r = lds[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = max(r, lds[w]);
+    __syncthreads();
+    return r;
+}
+
+// ------------------------------------------------------ scale arithmetic --
+// Current scaling ("Megatron FP8", sections 4 and 10):
+//   s = fl32(max(amax, 1e-12) / FP8_MAX) * 2^margin   (dequant multiplier)
+//   scale = fl32(1 / s)                                (quant multiplier)
+// The divisions are IEEE correctly rounded (the default for HIP float
+// division); a NaN amax propagates.
+struct Scales {
+    float s;     // scale_inv: value = code value * s
+    float scale; // quantization multiplier
+};
+
+__device__ __forceinline__ Scales current_scales(float amax, float fmax, int margin)
+{
+    const float ac = (amax != amax) ? amax : (amax > kAmaxFloor ? amax : kAmaxFloor);
+    const float s = ldexpf(ac / fmax, margin);
+    return Scales{s, 1.0f / s};
+}
+
+__device__ __forceinline__ Scales given_scales(float s) { return Scales{s, 1.0f / s}; }
+
+} // namespace fp8q

@@ -1,0 +1,55 @@
+// fp8q_launch.h -- internal launchers behind the C ABI.  Arguments are
+// already validated by the API layer; each launcher only enqueues kernels on
+// `s` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+// Grid-wide reduction scratch: every block folds its magnitude max into
+// `max_bits` and takes a ticket; the last block publishes the result and puts
+// both words back to zero, so the next launch on the same stream finds them
+// zero again.  One per (device, stream); see get_grid_scratch.
+struct GridScratch {
+    uint32_t max_bits;
+    uint32_t ticket;
+};
+
+// The scratch of the calling thread's current device and stream `s`,
+// allocated (and zeroed on `s`) the first time that pair is seen.
+hipError_t get_grid_scratch(hipStream_t s, GridScratch **out);
+
+// Where a per-tensor scale comes from: exactly one pointer is non-null.
+struct ScaleSrc {
+    const float *amax_in;      // current scaling from this amax
+    const float *scale_inv_in; // a given dequant scale s
+    int margin;                // current scaling only
+};
+
+hipError_t launch_fill_u32(uint32_t *p, uint32_t v, hipStream_t s);
+
+hipError_t launch_zero_scratch(GridScratch *gs, hipStream_t s);
+
+hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScratch *gs, hipStream_t s);
+
+hipError_t launch_cast(const void *x, int dtype, int64_t n, int fmt, ScaleSrc src, uint8_t *q, float *scale_inv_out,
+                       float *scale_out, float *amax_out, GridScratch *gs, hipStream_t s);
+
+hipError_t launch_dequant(const uint8_t *q, int fmt, int64_t n, const float *scale_inv, float *y, hipStream_t s);
+
+hipError_t launch_rowwise_colwise(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, ScaleSrc src,
+                                  uint8_t *q_row, uint8_t *q_col, float *scale_inv_out, float *scale_out,
+                                  float *amax_out, GridScratch *gs, hipStream_t s);
+
+hipError_t launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int block_rows, uint8_t *q_row,
+                        float *s_row, uint8_t *q_col, float *s_col, hipStream_t s);
+
+hipError_t launch_delayed(float *hist, int history_len, int n_cols, int col, const float *new_amax, int64_t step,
+                          int fmt, int margin, int algo, float *scale, float *scale_inv, hipStream_t s);
+
+hipError_t launch_gemm(const uint8_t *A, int fa, const float *sA, const uint8_t *B, int fb, const float *sB, int64_t M,
+                       int64_t N, int64_t K, int mode, void *C, float *amax_out, GridScratch *gs, hipStream_t s);
+
+} // namespace fp8q

@@ -1,0 +1,682 @@
+// quant.hip -- gfx950 kernels for the FP8 quantization side of the hot path:
+// amax reduction, per-tensor scaled cast (optionally with the input amax
+// fused in), dequantization, the delayed-scaling update, the rowwise +
+// columnwise cast and block quantization.
+//
+// All element kernels are HBM-bound streams: 16-byte loads and stores per
+// lane, several loads in flight per lane, and a VALU budget of a few
+// instructions per element (the hardware converter does the rounding).
+//
+// Pages cited (title, section):
+//   "Megatron FP8": section 2 (formats), 4 (scaling factors), 5 (delayed
+//   scaling), 10 (margin), 23 (round-to-nearest-even);
+//   "[Pytorch][Common] Hybrid quantization #2817" (rowwise/columnwise storage);
+//   "Low Precision Training and Rollout" (128x128 block FP8, FP32 scales).
+#include "fp8q_device.h"
+#include "fp8q_launch.h"
+
+namespace fp8q {
+
+constexpr int kThreads = 256;
+constexpr int kMaxStreamBlocks = 2048; // 8 blocks of 256 lanes per CU on 256 CUs
+
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static int stream_grid(int64_t work_items, int items_per_thread)
+{
+    int64_t blocks = ceil_div(work_items, (int64_t)kThreads * items_per_thread);
+    if (blocks < 1) blocks = 1;
+    if (blocks > kMaxStreamBlocks) blocks = kMaxStreamBlocks;
+    return (int)blocks;
+}
+
+template <int F>
+__device__ __forceinline__ Scales resolve_scales(const ScaleSrc &src)
+{
+    if (src.amax_in) return current_scales(*src.amax_in, Fmt<F>::kMax, src.margin);
+    return given_scales(*src.scale_inv_in);
+}
+
+__global__ void fill_u32_kernel(uint32_t *p, uint32_t v)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0) *p = v;
+}
+
+hipError_t launch_fill_u32(uint32_t *p, uint32_t v, hipStream_t s)
+{
+    fill_u32_kernel<<<1, 64, 0, s>>>(p, v);
+    return hipGetLastError();
+}
+
+__global__ void zero_scratch_kernel(GridScratch *gs)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        gs->max_bits = 0u;
+        gs->ticket = 0u;
+    }
+}
+
+hipError_t launch_zero_scratch(GridScratch *gs, hipStream_t s)
+{
+    zero_scratch_kernel<<<1, 64, 0, s>>>(gs);
+    return hipGetLastError();
+}
+
+// Grid-wide magnitude max without a separate initialisation launch: each
+// block folds its max into the scratch word and takes a ticket; the block
+// that draws the last ticket reads the final max, resets the scratch to zero
+// for the next launch and writes the result (every committed value is
+// already canonical, so the max is too).  Must be reached by every lane.
+__device__ __forceinline__ void grid_amax_commit(uint32_t m, GridScratch *gs, uint32_t *out)
+{
+    __shared__ uint32_t red[kThreads / 64];
+    m = block_max_u32<kThreads>(m, red);
+    if (threadIdx.x == 0) {
+        atomicMax(&gs->max_bits, canonical_amax_bits(m));
+        __threadfence();
+        const uint32_t nblocks = gridDim.x * gridDim.y * gridDim.z;
+        if (atomicAdd(&gs->ticket, 1u) == nblocks - 1) {
+            __threadfence();
+            const uint32_t v = atomicExch(&gs->max_bits, 0u);
+            atomicExch(&gs->ticket, 0u);
+            *out = v;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ amax --
+// amax = max |x| ("Megatron FP8", section 4).  Grid-stride over 16-byte
+// vectors, four in flight per lane; the tail (< one vector) is read by the
+// first lanes of the grid.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const void *__restrict__ x, int64_t n, GridScratch *gs,
+                                                        uint32_t *__restrict__ out)
+{
+    constexpr int kPer = DT == kBF16 ? 8 : 4; // elements per 16-byte vector
+    const int64_t nvec = n / kPer;
+    const uint4 *__restrict__ xv = reinterpret_cast<const uint4 *>(x);
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    uint32_t m = 0;
+    u16x2 m2 = {0, 0};
+    auto acc = [&](const uint4 &v) {
+        if constexpr (DT == kBF16) {
+            m2 = bf16_absmax2(m2, v.x);
+            m2 = bf16_absmax2(m2, v.y);
+            m2 = bf16_absmax2(m2, v.z);
+            m2 = bf16_absmax2(m2, v.w);
+        } else {
+            m = max(m, v.x & 0x7FFFFFFFu);
+            m = max(m, v.y & 0x7FFFFFFFu);
+            m = max(m, v.z & 0x7FFFFFFFu);
+            m = max(m, v.w & 0x7FFFFFFFu);
+        }
+    };
+    for (; i + 3 * stride < nvec; i += 4 * stride) {
+        const uint4 v0 = xv[i], v1 = xv[i + stride], v2 = xv[i + 2 * stride], v3 = xv[i + 3 * stride];
+        acc(v0);
+        acc(v1);
+        acc(v2);
+        acc(v3);
+    }
+    for (; i < nvec; i += stride) acc(xv[i]);
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t < n - nvec * kPer) {
+        const int64_t e = nvec * kPer + t;
+        if constexpr (DT == kBF16)
+            m = max(m, ((uint32_t)(reinterpret_cast<const uint16_t *>(x)[e] & 0x7FFFu)) << 16);
+        else
+            m = max(m, reinterpret_cast<const uint32_t *>(x)[e] & 0x7FFFFFFFu);
+    }
+    if constexpr (DT == kBF16) m = max(m, bf16_absmax_to_f32bits(m2));
+    grid_amax_commit(m, gs, out);
+}
+
+hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScratch *gs, hipStream_t s)
+{
+    uint32_t *out = reinterpret_cast<uint32_t *>(amax);
+    if (dtype == kBF16)
+        amax_kernel<kBF16><<<stream_grid(n / 8, 4), kThreads, 0, s>>>(x, n, gs, out);
+    else
+        amax_kernel<kF32><<<stream_grid(n / 4, 4), kThreads, 0, s>>>(x, n, gs, out);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ cast --
+// Load 16 consecutive elements (one chunk) as floats.
+template <int DT> struct Chunk16;
+template <> struct Chunk16<kBF16> {
+    uint4 a, b; // 16 bf16
+    __device__ __forceinline__ void load(const void *x, int64_t c)
+    {
+        const uint4 *p = reinterpret_cast<const uint4 *>(x) + 2 * c;
+        a = p[0];
+        b = p[1];
+    }
+    __device__ __forceinline__ float get(int k) const
+    {
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        return (k & 1) ? bf16_hi(w[k >> 1]) : bf16_lo(w[k >> 1]);
+    }
+    __device__ __forceinline__ void absmax(uint32_t &, u16x2 &m2) const
+    {
+        m2 = bf16_absmax2(m2, a.x);
+        m2 = bf16_absmax2(m2, a.y);
+        m2 = bf16_absmax2(m2, a.z);
+        m2 = bf16_absmax2(m2, a.w);
+        m2 = bf16_absmax2(m2, b.x);
+        m2 = bf16_absmax2(m2, b.y);
+        m2 = bf16_absmax2(m2, b.z);
+        m2 = bf16_absmax2(m2, b.w);
+    }
+};
+template <> struct Chunk16<kF32> {
+    uint4 v[4]; // 16 floats
+    __device__ __forceinline__ void load(const void *x, int64_t c)
+    {
+        const uint4 *p = reinterpret_cast<const uint4 *>(x) + 4 * c;
+        v[0] = p[0];
+        v[1] = p[1];
+        v[2] = p[2];
+        v[3] = p[3];
+    }
+    __device__ __forceinline__ float get(int k) const
+    {
+        const uint4 &q = v[k >> 2];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        return __uint_as_float(w[k & 3]);
+    }
+    __device__ __forceinline__ void absmax(uint32_t &m, u16x2 &) const
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            m = max(m, v[j].x & 0x7FFFFFFFu);
+            m = max(m, v[j].y & 0x7FFFFFFFu);
+            m = max(m, v[j].z & 0x7FFFFFFFu);
+            m = max(m, v[j].w & 0x7FFFFFFFu);
+        }
+    }
+};
+
+template <int F, int DT>
+__device__ __forceinline__ uint4 encode_chunk(const Chunk16<DT> &c, float scale)
+{
+    uint4 o;
+    o.x = encode4<F>(c.get(0), c.get(1), c.get(2), c.get(3), scale);
+    o.y = encode4<F>(c.get(4), c.get(5), c.get(6), c.get(7), scale);
+    o.z = encode4<F>(c.get(8), c.get(9), c.get(10), c.get(11), scale);
+    o.w = encode4<F>(c.get(12), c.get(13), c.get(14), c.get(15), scale);
+    return o;
+}
+
+// Per-tensor cast ("Megatron FP8", section 4): q = encode(fl32(x * scale)).
+// Every lane derives the scale from the device scalar (no host round trip);
+// block 0 publishes it.  With kAmax the input's magnitude max is reduced in
+// the same pass (delayed scaling records it after the cast, section 5).
+template <int F, int DT, bool kAmax>
+__global__ __launch_bounds__(kThreads) void cast_kernel(const void *__restrict__ x, int64_t n, ScaleSrc src,
+                                                        uint8_t *__restrict__ q, float *scale_inv_out,
+                                                        float *scale_out, GridScratch *gs, uint32_t *amax_out)
+{
+    const Scales sc = resolve_scales<F>(src);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (scale_inv_out) *scale_inv_out = sc.s;
+        if (scale_out) *scale_out = sc.scale;
+    }
+    const int64_t nch = n >> 4;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    uint4 *__restrict__ qv = reinterpret_cast<uint4 *>(q);
+    uint32_t m = 0;
+    u16x2 m2 = {0, 0};
+    for (; c + stride < nch; c += 2 * stride) {
+        Chunk16<DT> a, b;
+        a.load(x, c);
+        b.load(x, c + stride);
+        if constexpr (kAmax) {
+            a.absmax(m, m2);
+            b.absmax(m, m2);
+        }
+        qv[c] = encode_chunk<F, DT>(a, sc.scale);
+        qv[c + stride] = encode_chunk<F, DT>(b, sc.scale);
+    }
+    if (c < nch) {
+        Chunk16<DT> a;
+        a.load(x, c);
+        if constexpr (kAmax) a.absmax(m, m2);
+        qv[c] = encode_chunk<F, DT>(a, sc.scale);
+    }
+    // tail: fewer than 16 elements, one per lane of block 0
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t < n - (nch << 4)) {
+        const int64_t e = (nch << 4) + t;
+        float v;
+        if constexpr (DT == kBF16)
+            v = __uint_as_float(((uint32_t)reinterpret_cast<const uint16_t *>(x)[e]) << 16);
+        else
+            v = reinterpret_cast<const float *>(x)[e];
+        if constexpr (kAmax) m = max(m, f32_absbits(v));
+        q[e] = (uint8_t)encode1<F>(v, sc.scale);
+    }
+    if constexpr (kAmax) {
+        if constexpr (DT == kBF16) m = max(m, bf16_absmax_to_f32bits(m2));
+        grid_amax_commit(m, gs, amax_out);
+    }
+}
+
+template <int F, int DT>
+static hipError_t launch_cast_t(const void *x, int64_t n, ScaleSrc src, uint8_t *q, float *scale_inv_out,
+                                float *scale_out, float *amax_out, GridScratch *gs, hipStream_t s)
+{
+    const int grid = stream_grid(n >> 4, 2);
+    if (amax_out)
+        cast_kernel<F, DT, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs,
+                                                           reinterpret_cast<uint32_t *>(amax_out));
+    else
+        cast_kernel<F, DT, false><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_cast(const void *x, int dtype, int64_t n, int fmt, ScaleSrc src, uint8_t *q, float *scale_inv_out,
+                       float *scale_out, float *amax_out, GridScratch *gs, hipStream_t s)
+{
+    if (fmt == kE4M3) {
+        if (dtype == kBF16) return launch_cast_t<kE4M3, kBF16>(x, n, src, q, scale_inv_out, scale_out, amax_out, gs, s);
+        return launch_cast_t<kE4M3, kF32>(x, n, src, q, scale_inv_out, scale_out, amax_out, gs, s);
+    }
+    if (dtype == kBF16) return launch_cast_t<kE5M2, kBF16>(x, n, src, q, scale_inv_out, scale_out, amax_out, gs, s);
+    return launch_cast_t<kE5M2, kF32>(x, n, src, q, scale_inv_out, scale_out, amax_out, gs, s);
+}
+
+// --------------------------------------------------------------- dequant --
+template <int F, bool kHi>
+__device__ __forceinline__ float2 dec2(uint32_t w)
+{
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    v2f r;
+    if constexpr (F == kE4M3)
+        r = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHi);
+    else
+        r = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, kHi);
+    return make_float2(r.x, r.y);
+}
+
+// y = fl32(value(q) * scale_inv) ("Megatron FP8", section 4).  The hardware
+// decoder gives the exact value of every code.
+template <int F>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__restrict__ q, int64_t n,
+                                                           const float *__restrict__ scale_inv, float *__restrict__ y)
+{
+    const float s = *scale_inv;
+    const int64_t nch = n >> 4;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const uint4 *__restrict__ qv = reinterpret_cast<const uint4 *>(q);
+    float4 *__restrict__ yv = reinterpret_cast<float4 *>(y);
+    for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nch; c += stride) {
+        const uint4 v = qv[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float2 lo = dec2<F, false>(w[j]);
+            const float2 hi = dec2<F, true>(w[j]);
+            yv[4 * c + j] = make_float4(lo.x * s, lo.y * s, hi.x * s, hi.y * s);
+        }
+    }
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t < n - (nch << 4)) {
+        const int64_t e = (nch << 4) + t;
+        y[e] = dec2<F, false>((uint32_t)q[e]).x * s;
+    }
+}
+
+hipError_t launch_dequant(const uint8_t *q, int fmt, int64_t n, const float *scale_inv, float *y, hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    const int grid = stream_grid(n >> 4, 2);
+    if (fmt == kE4M3)
+        dequant_kernel<kE4M3><<<grid, kThreads, 0, s>>>(q, n, scale_inv, y);
+    else
+        dequant_kernel<kE5M2><<<grid, kThreads, 0, s>>>(q, n, scale_inv, y);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------- delayed --
+// Delayed-scaling update ("Megatron FP8", section 5): write the new amax at
+// slot step % L of column col, reduce the column (max, NaN-propagating) or take
+// the value just written, derive s = eff / FP8_MAX * 2^margin (1 when eff is
+// not > 0) and its reciprocal.  One block; L may be any length.
+__global__ __launch_bounds__(kThreads) void delayed_kernel(float *__restrict__ hist, int L, int n_cols, int col,
+                                                           const float *__restrict__ new_amax, int slot, float fmax,
+                                                           int margin, int algo, float *__restrict__ scale,
+                                                           float *__restrict__ scale_inv)
+{
+    __shared__ uint32_t red[kThreads / 64];
+    __shared__ uint32_t nan_red[kThreads / 64];
+    const float a = *new_amax;
+    // Largest value of the column, as an order-preserving key of the float
+    // (negative values flip all bits, positive values set the sign bit).
+    uint32_t key = 0;
+    uint32_t saw_nan = 0;
+    for (int j = threadIdx.x; j < L; j += kThreads) {
+        const float h = (j == slot) ? a : hist[(int64_t)j * n_cols + col];
+        const uint32_t b = __float_as_uint(h);
+        if (h != h) saw_nan = 1;
+        else key = max(key, (b & 0x80000000u) ? ~b : (b | 0x80000000u));
+    }
+    key = block_max_u32<kThreads>(key, red);
+    saw_nan = block_max_u32<kThreads>(saw_nan, nan_red);
+    if (threadIdx.x == 0) {
+        hist[(int64_t)slot * n_cols + col] = a;
+        float eff;
+        if (algo == 0) {
+            const uint32_t b = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+            eff = saw_nan ? __uint_as_float(kCanonicalNaN) : __uint_as_float(b);
+        } else {
+            eff = a;
+        }
+        const float s = (eff > 0.0f) ? ldexpf(eff / fmax, margin) : 1.0f;
+        scale_inv[col] = s;
+        scale[col] = 1.0f / s;
+    }
+}
+
+hipError_t launch_delayed(float *hist, int history_len, int n_cols, int col, const float *new_amax, int64_t step,
+                          int fmt, int margin, int algo, float *scale, float *scale_inv, hipStream_t s)
+{
+    const int slot = (int)(step % history_len);
+    const float fmax = fmt == kE4M3 ? Fmt<kE4M3>::kMax : Fmt<kE5M2>::kMax;
+    delayed_kernel<<<1, kThreads, 0, s>>>(hist, history_len, n_cols, col, new_amax, slot, fmax, margin, algo, scale,
+                                          scale_inv);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------- tile kernels --
+// A 128x128 tile per block of 256 lanes.  Lane (ig = tid / 8, jg = tid % 8)
+// owns rows 4*ig .. 4*ig+3 and columns 16*jg .. 16*jg+15 of the tile: four
+// rows of 16 elements, read as 16-byte vectors and written as one 16-byte
+// vector of codes per row (8 lanes cover a 128-byte row segment).
+//
+// The columnwise copy goes through LDS: each lane transposes its 4x16 codes
+// in registers (byte permutes) into 16 dwords, one per column, each holding
+// four consecutive rows; the dwords land in LDS as a [128 col][128 row] byte
+// tile, rotated by 8 dwords per 16 columns so that the writes of a wave spread
+// over all banks while every 16-byte read stays contiguous.
+enum TileMode { kTilePerTensor = 0, kTileBlock128 = 1, kTileBlock1x128 = 2 };
+
+constexpr int kTile = 128;
+
+// 4x4 byte transpose: d[r] holds row r (bytes = columns 0..3); e[c] returns
+// column c (bytes = rows 0..3).
+__device__ __forceinline__ void transpose4x4(const uint32_t d0, const uint32_t d1, const uint32_t d2,
+                                             const uint32_t d3, uint32_t e[4])
+{
+    const uint32_t lo01 = __builtin_amdgcn_perm(d1, d0, 0x05010400u); // d0.b0 d1.b0 d0.b1 d1.b1
+    const uint32_t hi01 = __builtin_amdgcn_perm(d1, d0, 0x07030602u); // d0.b2 d1.b2 d0.b3 d1.b3
+    const uint32_t lo23 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+    e[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    e[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    e[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    e[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+}
+
+// dword address in the transposed LDS tile of (tile column j, row dword d)
+__device__ __forceinline__ int tlds_addr(int j, int d) { return j * 32 + ((d + 8 * (j >> 4)) & 31); }
+
+// A lane's 4 rows x 16 columns of input as floats.
+template <int DT> struct Patch {
+    float v[4][16];
+    __device__ __forceinline__ void load(const void *x, int64_t ld, int64_t r0, int64_t c0)
+    {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (DT == kBF16) {
+                const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) +
+                                                                 (r0 + r) * ld + c0);
+                const uint4 a = p[0], b = p[1];
+                const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    v[r][2 * k] = bf16_lo(w[k]);
+                    v[r][2 * k + 1] = bf16_hi(w[k]);
+                }
+            } else {
+                const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) +
+                                                                   (r0 + r) * ld + c0);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float4 f = p[k];
+                    v[r][4 * k] = f.x;
+                    v[r][4 * k + 1] = f.y;
+                    v[r][4 * k + 2] = f.z;
+                    v[r][4 * k + 3] = f.w;
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void zero()
+    {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) v[r][k] = 0.0f;
+    }
+};
+
+// Store the lane's 4x16 codes (cw[r][0..3] = row r, 16 codes) transposed into LDS.
+__device__ __forceinline__ void stage_transposed(uint32_t *tl, const uint32_t cw[4][4], int ig, int jg)
+{
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        uint32_t e[4];
+        transpose4x4(cw[0][q4], cw[1][q4], cw[2][q4], cw[3][q4], e);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tl[tlds_addr(jg * 16 + q4 * 4 + k, ig)] = e[k];
+    }
+}
+
+// Write the transposed tile from LDS to q_col [cols][rows]: output row
+// (tile column j), 16 consecutive rows k*16 .. k*16+15 per 16-byte store.
+__device__ __forceinline__ void store_transposed(const uint32_t *tl, uint8_t *q_col, int64_t rows, int64_t cols,
+                                                 int64_t row0, int64_t col0)
+{
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int p = threadIdx.x + u * kThreads;
+        const int j = p >> 3, k = p & 7;
+        if (col0 + j < cols && row0 + 16 * k < rows) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(tl + tlds_addr(j, 4 * k));
+            *reinterpret_cast<uint4 *>(q_col + (col0 + j) * rows + row0 + 16 * k) = v;
+        }
+    }
+}
+
+template <int F, int DT, int kMode, bool kAmax>
+__global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__ x, int64_t rows, int64_t cols,
+                                                        ScaleSrc src, uint8_t *__restrict__ q_row,
+                                                        uint8_t *__restrict__ q_col, float *__restrict__ s_row,
+                                                        float *__restrict__ s_col, float *scale_inv_out,
+                                                        float *scale_out, GridScratch *gs, uint32_t *amax_out)
+{
+    __shared__ uint32_t tl[kTile * 32];            // transposed codes, 16 KiB
+    __shared__ uint32_t red[kThreads / 64];
+    __shared__ uint32_t colmax[kMode == kTileBlock1x128 ? 32 * kTile : 1];
+    __shared__ float colscale[kMode == kTileBlock1x128 ? kTile : 1];
+
+    const int ig = threadIdx.x >> 3, jg = threadIdx.x & 7;
+    const int64_t row0 = (int64_t)blockIdx.y * kTile, col0 = (int64_t)blockIdx.x * kTile;
+    const int64_t r0 = row0 + 4 * ig, c0 = col0 + 16 * jg;
+    const bool valid = (r0 < rows) && (c0 < cols); // rows % 4 == 0, cols % 16 == 0
+
+    Patch<DT> p;
+    if (valid) p.load(x, cols, r0, c0);
+    else p.zero();
+
+    uint32_t cw[4][4]; // rowwise codes
+
+    if constexpr (kMode == kTilePerTensor) {
+        const Scales sc = resolve_scales<F>(src);
+        if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+            if (scale_inv_out) *scale_inv_out = sc.s;
+            if (scale_out) *scale_out = sc.scale;
+        }
+        if constexpr (kAmax) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(p.v[r][k]));
+            grid_amax_commit(m, gs, amax_out);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                cw[r][q4] = encode4<F>(p.v[r][4 * q4], p.v[r][4 * q4 + 1], p.v[r][4 * q4 + 2], p.v[r][4 * q4 + 3],
+                                       sc.scale);
+    } else if constexpr (kMode == kTileBlock128) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(p.v[r][k]));
+        m = block_max_u32<kThreads>(m, red);
+        const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
+        if (threadIdx.x == 0) {
+            s_row[blockIdx.y * (cols / kTile) + blockIdx.x] = sc.s;
+            if (s_col) s_col[blockIdx.x * (rows / kTile) + blockIdx.y] = sc.s;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                cw[r][q4] = encode4<F>(p.v[r][4 * q4], p.v[r][4 * q4 + 1], p.v[r][4 * q4 + 2], p.v[r][4 * q4 + 3],
+                                       sc.scale);
+    } else { // 1x128 blocks: one scale per row segment, one per column segment
+        // row segments: the 8 lanes jg = 0..7 of a row group hold the row's 128 columns
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(p.v[r][k]));
+            m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+            m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+            m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+            const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
+            if (jg == 0) s_row[(r0 + r) * (cols / kTile) + blockIdx.x] = sc.s;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                cw[r][q4] = encode4<F>(p.v[r][4 * q4], p.v[r][4 * q4 + 1], p.v[r][4 * q4 + 2], p.v[r][4 * q4 + 3],
+                                       sc.scale);
+        }
+        // column segments: reduce each column's 128 rows through LDS
+        if (q_col) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m = max(m, f32_absbits(p.v[r][k]));
+                colmax[ig * kTile + 16 * jg + k] = m;
+            }
+            __syncthreads();
+            if (threadIdx.x < kTile) {
+                uint32_t m = 0;
+#pragma unroll 8
+                for (int g = 0; g < 32; ++g) m = max(m, colmax[g * kTile + threadIdx.x]);
+                const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
+                colscale[threadIdx.x] = sc.scale;
+                s_col[(col0 + threadIdx.x) * (rows / kTile) + blockIdx.y] = sc.s;
+            }
+            __syncthreads();
+        }
+    }
+
+    if (q_row && valid) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) = make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
+    }
+    if (q_col) {
+        if constexpr (kMode == kTileBlock1x128) {
+            // columnwise codes use the column-segment scales
+            uint32_t cc[4][4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int k = 4 * q4;
+                    const float *cs = colscale + 16 * jg + k;
+                    cc[r][q4] = encode4s<F>(p.v[r][k], p.v[r][k + 1], p.v[r][k + 2], p.v[r][k + 3], cs[0], cs[1],
+                                            cs[2], cs[3]);
+                }
+            stage_transposed(tl, cc, ig, jg);
+        } else {
+            stage_transposed(tl, cw, ig, jg);
+        }
+        __syncthreads();
+        store_transposed(tl, q_col, rows, cols, row0, col0);
+    }
+}
+
+template <int F, int DT>
+static hipError_t launch_rc_t(const void *x, int64_t rows, int64_t cols, ScaleSrc src, uint8_t *q_row, uint8_t *q_col,
+                              float *scale_inv_out, float *scale_out, float *amax_out, GridScratch *gs, hipStream_t s)
+{
+    const dim3 grid((unsigned)ceil_div(cols, kTile), (unsigned)ceil_div(rows, kTile));
+    if (amax_out)
+        tile_kernel<F, DT, kTilePerTensor, true><<<grid, kThreads, 0, s>>>(
+            x, rows, cols, src, q_row, q_col, nullptr, nullptr, scale_inv_out, scale_out, gs,
+            reinterpret_cast<uint32_t *>(amax_out));
+    else
+        tile_kernel<F, DT, kTilePerTensor, false><<<grid, kThreads, 0, s>>>(
+            x, rows, cols, src, q_row, q_col, nullptr, nullptr, scale_inv_out, scale_out, gs, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_rowwise_colwise(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, ScaleSrc src,
+                                  uint8_t *q_row, uint8_t *q_col, float *scale_inv_out, float *scale_out,
+                                  float *amax_out, GridScratch *gs, hipStream_t s)
+{
+    if (rows == 0 || cols == 0) {
+        // still publish the scales and an amax of 0
+        return launch_cast(x, dtype, 0, fmt, src, nullptr, scale_inv_out, scale_out, amax_out, gs, s);
+    }
+    if (fmt == kE4M3) {
+        if (dtype == kBF16)
+            return launch_rc_t<kE4M3, kBF16>(x, rows, cols, src, q_row, q_col, scale_inv_out, scale_out, amax_out, gs,
+                                             s);
+        return launch_rc_t<kE4M3, kF32>(x, rows, cols, src, q_row, q_col, scale_inv_out, scale_out, amax_out, gs, s);
+    }
+    if (dtype == kBF16)
+        return launch_rc_t<kE5M2, kBF16>(x, rows, cols, src, q_row, q_col, scale_inv_out, scale_out, amax_out, gs, s);
+    return launch_rc_t<kE5M2, kF32>(x, rows, cols, src, q_row, q_col, scale_inv_out, scale_out, amax_out, gs, s);
+}
+
+template <int F, int DT>
+static hipError_t launch_block_t(const void *x, int64_t rows, int64_t cols, int block_rows, uint8_t *q_row,
+                                 float *s_row, uint8_t *q_col, float *s_col, hipStream_t s)
+{
+    const dim3 grid((unsigned)(cols / kTile), (unsigned)(rows / kTile));
+    const ScaleSrc none{nullptr, nullptr, 0};
+    if (block_rows == 128)
+        tile_kernel<F, DT, kTileBlock128, false><<<grid, kThreads, 0, s>>>(x, rows, cols, none, q_row, q_col, s_row,
+                                                                          s_col, nullptr, nullptr, nullptr, nullptr);
+    else
+        tile_kernel<F, DT, kTileBlock1x128, false><<<grid, kThreads, 0, s>>>(
+            x, rows, cols, none, q_row, q_col, s_row, s_col, nullptr, nullptr, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int block_rows, uint8_t *q_row,
+                        float *s_row, uint8_t *q_col, float *s_col, hipStream_t s)
+{
+    if (rows == 0 || cols == 0) return hipSuccess;
+    if (fmt == kE4M3) {
+        if (dtype == kBF16) return launch_block_t<kE4M3, kBF16>(x, rows, cols, block_rows, q_row, s_row, q_col, s_col, s);
+        return launch_block_t<kE4M3, kF32>(x, rows, cols, block_rows, q_row, s_row, q_col, s_col, s);
+    }
+    if (dtype == kBF16) return launch_block_t<kE5M2, kBF16>(x, rows, cols, block_rows, q_row, s_row, q_col, s_col, s);
+    return launch_block_t<kE5M2, kF32>(x, rows, cols, block_rows, q_row, s_row, q_col, s_col, s);
+}
+
+} // namespace fp8q

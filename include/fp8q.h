@@ -1,0 +1,185 @@
+/*
+ * fp8q.h -- C ABI of the FP8 scaled-quantization and scaled-FP8-GEMM library
+ * (libfp8q.so, HIP kernels for gfx950 / MI355X).
+ *
+ * Pages cited (title, section):
+ *   [MFP8]   "Megatron FP8" (sections 1-28)
+ *   [HYBRID] "[Pytorch][Common] Hybrid quantization #2817" (TransformerEngine PR)
+ *   [VIME]   "Low Precision Training and Rollout" (vime documentation)
+ *
+ * Conventions for every call below
+ *  - All pointers are DEVICE memory owned by the caller, unless stated.  The
+ *    library never copies device->host and never synchronises: each call
+ *    enqueues its kernels on `stream` (a hipStream_t; NULL = the default
+ *    stream) and returns.  The only device memory it allocates is a 256-byte
+ *    reduction scratch per (device, stream) pair, on the first call on that
+ *    pair that reduces an amax, held until the process ends.  Calls on one
+ *    stream share that scratch in stream order; two host threads that enqueue
+ *    on the same stream handle concurrently must serialise their calls.
+ *  - Enum-valued arguments are passed as int32_t (values below).
+ *  - Tensors are dense and row-major.  FP8 tensors are arrays of 8-bit codes
+ *    (uint8_t).  bf16 tensors are arrays of 16-bit bf16 patterns.
+ *  - Element buffers (x, q, y, C) must be 16-byte aligned; scalar and scale
+ *    buffers 4-byte aligned.
+ *  - Errors: arguments are validated on the host before any HIP call.  A
+ *    non-zero status is returned and a message is kept for
+ *    fp8q_last_error() (thread-local).  Nothing is written on error.  A
+ *    launch failure reported by the runtime returns FP8Q_EHIP.
+ *  - Numerics: scales, amaxes and the scaled values are binary32 with
+ *    round-to-nearest-even.  The FP8 cast saturates to +-FP8_MAX and rounds to
+ *    nearest, ties to even.  NaN is kept: a NaN product x*scale becomes code
+ *    0x7F with the sign bit set to sign(x) XOR sign(scale).
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define FP8Q_OK 0
+#define FP8Q_EINVAL 1      /* bad pointer, size, alignment or enum value */
+#define FP8Q_EUNSUPPORTED 2 /* valid request this build does not implement */
+#define FP8Q_EHIP 3        /* the HIP runtime reported an error */
+
+/* FP8 formats, [MFP8] section 2.  E4M3FN: bias 7, max 448, no Inf, NaN only
+ * S.1111.111.  E5M2: bias 15, max 57344, IEEE Inf and NaN. */
+#define FP8Q_E4M3FN 0
+#define FP8Q_E5M2 1
+
+/* element types of high-precision tensors */
+#define FP8Q_F32 0
+#define FP8Q_BF16 1
+
+/* delayed-scaling history reduction, [MFP8] section 5 */
+#define FP8Q_ALGO_MAX 0
+#define FP8Q_ALGO_MOST_RECENT 1
+
+/* GEMM scaling modes */
+#define FP8Q_PER_TENSOR 0
+#define FP8Q_BLOCK_1x128_128x128 1
+
+/*
+ * fp8_amax -- *amax = max_i |x_i| over n elements ([MFP8] section 4, the
+ * amax of compute_fp8_scale; section 11, tensor_amax).
+ *   x      [n] elements of type `dtype` (FP8Q_F32 or FP8Q_BF16)
+ *   amax   one float, written (overwritten) by the call
+ * A NaN element gives the canonical NaN 0x7FC00000; n == 0 gives 0.
+ * The result is exact (an integer max over magnitude bits, order-free).
+ */
+int fp8_amax(const void *x, int32_t dtype, int64_t n, float *amax, void *stream);
+
+/*
+ * fp8_quantize_tensor -- per-tensor scaled cast to FP8 ([MFP8] section 4
+ * current scaling; section 5 delayed scaling, which consumes a stored scale).
+ * Exactly one of amax_in / scale_inv_in is non-NULL:
+ *   amax_in      (current scaling) s = fl32(max(*amax_in, 1e-12) / FP8_MAX) * 2^margin
+ *   scale_inv_in (given scale)     s = *scale_inv_in, margin ignored
+ * then scale = fl32(1 / s) and q_i = encode(fl32(x_i * scale)).
+ *   x              [n] of `dtype`
+ *   q              [n] FP8 codes of format `fmt`
+ *   scale_inv_out  (nullable) receives s, the dequantization multiplier
+ *   scale_out      (nullable) receives scale, the quantization multiplier
+ *   amax_out       (nullable) receives max_i |x_i| of this input (fused, for
+ *                  delayed scaling's history), defined as in fp8_amax
+ * Output buffers must not overlap the inputs.
+ */
+int fp8_quantize_tensor(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *amax_in,
+                        int32_t margin, const float *scale_inv_in, uint8_t *q, float *scale_inv_out,
+                        float *scale_out, float *amax_out, void *stream);
+
+/*
+ * fp8_dequantize -- y_i = fl32(value(q_i) * *scale_inv) ([MFP8] section 4: the
+ * cached inverse makes dequantization one element multiply; section 23:
+ * reconstruction = fp8 value times scale).  With scale_inv = 1 over the 256
+ * codes this is the decode table of the format.  NaN codes give a NaN
+ * (payload unspecified); E5M2 Inf codes give +-Inf.
+ *   q [n] codes, y [n] float32 output.
+ */
+int fp8_dequantize(const uint8_t *q, int32_t fmt, int64_t n, const float *scale_inv, float *y, void *stream);
+
+/*
+ * fp8_quantize_rowwise_colwise -- one per-tensor scale, two layouts ([HYBRID]:
+ * a quantized tensor holds rowwise and columnwise storage; the columnwise one
+ * is quantized from the original input).  Scale selection as in
+ * fp8_quantize_tensor.
+ *   x      [rows][cols] of `dtype`; rows and cols multiples of 16
+ *   q_row  (nullable) [rows][cols] codes
+ *   q_col  (nullable) [cols][rows] codes, q_col[j][i] = q_row[i][j]
+ *   scale_inv_out, scale_out, amax_out (nullable) as in fp8_quantize_tensor
+ * At least one of q_row / q_col must be given.
+ */
+int fp8_quantize_rowwise_colwise(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt,
+                                 const float *amax_in, int32_t margin, const float *scale_inv_in, uint8_t *q_row,
+                                 uint8_t *q_col, float *scale_inv_out, float *scale_out, float *amax_out,
+                                 void *stream);
+
+/*
+ * fp8_quantize_block -- block current scaling with FP32 block scales
+ * ([VIME] "BF16 Training with FP8 Rollout": 128x128 weight blocks;
+ * "FP8 Quick Start": blockwise recipe with FP32 scales).  Each block gets
+ * s_b = fl32(max(amax_b, 1e-12) / FP8_MAX) (margin 0), scale_b = fl32(1/s_b),
+ * and its elements are cast with scale_b.  The stored scales are the s_b
+ * (dequantization multipliers).
+ *   x           [rows][cols] of `dtype`; rows, cols multiples of 128
+ *   block_rows  128: 128x128 blocks.  1: 1x128 blocks (one row, 128 columns).
+ *   q_row [rows][cols] codes, s_row [rows/block_rows][cols/128]
+ *   q_col, s_col (nullable, both or neither): the columnwise copy, i.e. the
+ *     same rule applied to x^T: q_col [cols][rows].
+ *     128x128: q_col = q_row^T, s_col [cols/128][rows/128] = s_row^T.
+ *     1x128:   blocks of 128 consecutive rows of one column of x,
+ *              s_col [cols][rows/128].
+ */
+int fp8_quantize_block(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt, int32_t block_rows,
+                       uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col, void *stream);
+
+/*
+ * fp8_update_scale_delayed -- delayed-scaling state update ([MFP8] section 5,
+ * the amax-history ring and the fp8_meta update).
+ *   hist       [history_len][n_cols] float history, column `col` is updated
+ *   new_amax   one float (device), the amax measured by the step just run
+ *   step       host count of earlier updates of this column; the value is
+ *              written at slot step % history_len
+ *   fmt        format whose FP8_MAX the new scale targets (the format of the
+ *              tensor that will consume it)
+ *   algo       FP8Q_ALGO_MAX: eff = max of the column's history (NaN if any
+ *              NaN); FP8Q_ALGO_MOST_RECENT: eff = *new_amax
+ *   scale, scale_inv  [n_cols]; entry `col` receives
+ *              s = eff > 0 ? fl32(eff / FP8_MAX) * 2^margin : 1  (scale_inv)
+ *              and fl32(1 / s) (scale)
+ * The initial state of a column is hist = 0, scale = scale_inv = 1.
+ */
+int fp8_update_scale_delayed(float *hist, int32_t history_len, int32_t n_cols, int32_t col, const float *new_amax,
+                             int64_t step, int32_t fmt, int32_t margin, int32_t algo, float *scale, float *scale_inv,
+                             void *stream);
+
+/*
+ * fp8_scaled_gemm -- C = (A * sA) (B * sB)^T on FP8 codes with fp32
+ * accumulation ([MFP8] section 6: FP8 operands, fp32 accumulation, bf16
+ * output; section 27: products promoted to fp32 and summed, one downcast of
+ * the finished dot product).
+ *   A [M][K] codes of format fa, B [N][K] codes of format fb (both
+ *   K-contiguous), C [M][N] output of type c_dtype (FP8Q_BF16).
+ *   mode FP8Q_PER_TENSOR: sA, sB point to one float each (dequant scales);
+ *        C = bf16(fl32(fl32(sA*sB) * acc)).
+ *   mode FP8Q_BLOCK_1x128_128x128: sA [M][K/128] (1x128 blocks of A),
+ *        sB [N/128][K/128] (128x128 blocks of B); each 128-wide K slice is
+ *        accumulated separately and added as acc += sA[m,kb]*sB[n/128,kb]*part.
+ *   amax_out (nullable) receives max |C| over the emitted bf16 values.
+ * M, N, K must be multiples of 128 (FP8Q_EUNSUPPORTED otherwise).
+ */
+int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb, const float *sB,
+                    int64_t M, int64_t N, int64_t K, int32_t mode, void *C, int32_t c_dtype, float *amax_out,
+                    void *stream);
+
+/* Message of the last non-OK status returned on this thread ("" if none). */
+const char *fp8q_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

@@ -1,0 +1,122 @@
+"""The C-ABI library loads on a machine without a GPU, exports every entry
+point the header declares, and rejects bad arguments on the host before any
+HIP call (every case below fails validation, so nothing reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+fq = pytest.importorskip("fp8_scaled_quantization_reduce_amd")
+
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+L = fq.lib
+S = 0  # default stream handle (never used: every call fails validation)
+BAD = 0x1000  # a 16-byte aligned fake device address, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return set(re.findall(r"^(?:int|const char \*)\s*(\w+)\(", text, flags=re.M))
+
+
+def test_header_and_library_agree():
+    names = declared_functions()
+    assert names == set(fq.SIGNATURES), names ^ set(fq.SIGNATURES)
+    for name in names:
+        assert hasattr(L, name), name
+    # the binding sets an argument list of the declared arity
+    text = open(HEADER).read()
+    for name in names:
+        decl = re.search(r"^(?:int|const char \*)\s*%s\((.*?)\);" % name, text, flags=re.S | re.M).group(1)
+        arity = 0 if decl.strip() == "void" else decl.count(",") + 1
+        assert arity == len(fq.SIGNATURES[name]), name
+
+
+def test_enum_values_match_header():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define (FP8Q_\w+) (\d+)", text))
+    assert int(defs["FP8Q_E4M3FN"]) == fq.E4M3FN and int(defs["FP8Q_E5M2"]) == fq.E5M2
+    assert int(defs["FP8Q_F32"]) == fq.F32 and int(defs["FP8Q_BF16"]) == fq.BF16
+    assert int(defs["FP8Q_EINVAL"]) == fq.EINVAL and int(defs["FP8Q_EUNSUPPORTED"]) == fq.EUNSUPPORTED
+    assert int(defs["FP8Q_PER_TENSOR"]) == fq.PER_TENSOR
+    assert int(defs["FP8Q_BLOCK_1x128_128x128"]) == fq.BLOCK_1x128_128x128
+
+
+def _expect(status, code, fragment):
+    assert status == code, (status, fq.last_error())
+    assert fragment in fq.last_error(), fq.last_error()
+
+
+def test_amax_validation():
+    _expect(L.fp8_amax(BAD, 7, 16, BAD, S), fq.EINVAL, "dtype")
+    _expect(L.fp8_amax(BAD, fq.F32, -1, BAD, S), fq.EINVAL, "negative")
+    _expect(L.fp8_amax(BAD + 4, fq.F32, 16, BAD + 0x100, S), fq.EINVAL, "16-byte")
+    _expect(L.fp8_amax(None, fq.F32, 16, BAD, S), fq.EINVAL, "16-byte")
+    _expect(L.fp8_amax(BAD, fq.F32, 16, None, S), fq.EINVAL, "amax")
+    _expect(L.fp8_amax(BAD, fq.F32, 16, BAD + 8, S), fq.EINVAL, "overlaps")
+
+
+def test_quantize_tensor_validation():
+    q = BAD + 0x10000
+    _expect(L.fp8_quantize_tensor(BAD, fq.BF16, 64, 5, BAD + 0x800, 0, None, q, None, None, None, S),
+            fq.EINVAL, "format")
+    _expect(L.fp8_quantize_tensor(BAD, fq.BF16, 64, 0, None, 0, None, q, None, None, None, S),
+            fq.EINVAL, "exactly one")
+    _expect(L.fp8_quantize_tensor(BAD, fq.BF16, 64, 0, BAD + 0x800, 0, BAD + 0x900, q, None, None, None, S),
+            fq.EINVAL, "exactly one")
+    _expect(L.fp8_quantize_tensor(BAD, fq.BF16, 64, 0, BAD + 0x800, 0, None, q, None, None, BAD + 0x800, S),
+            fq.EINVAL, "aliases")
+    _expect(L.fp8_quantize_tensor(BAD, fq.BF16, 64, 0, BAD + 0x800, 0, None, q + 1, None, None, None, S),
+            fq.EINVAL, "q must")
+    _expect(L.fp8_quantize_tensor(BAD, fq.BF16, 64, 0, BAD + 0x800, 0, None, BAD + 32, None, None, None, S),
+            fq.EINVAL, "overlaps")
+    _expect(L.fp8_quantize_tensor(BAD, fq.BF16, 64, 0, BAD + 0x802, 0, None, q, None, None, None, S),
+            fq.EINVAL, "aligned")
+
+
+def test_dequant_and_rowwise_colwise_validation():
+    _expect(L.fp8_dequantize(BAD, 3, 16, BAD + 0x800, BAD + 0x1000, S), fq.EINVAL, "format")
+    _expect(L.fp8_dequantize(BAD, 0, 16, None, BAD + 0x1000, S), fq.EINVAL, "scale_inv")
+    _expect(L.fp8_dequantize(BAD, 0, 16, BAD + 0x800, BAD + 8, S), fq.EINVAL, "16-byte")
+    rc = L.fp8_quantize_rowwise_colwise
+    _expect(rc(BAD, fq.BF16, 24, 32, 0, BAD + 0x800, 0, None, BAD + 0x10000, None, None, None, None, S),
+            fq.EUNSUPPORTED, "multiples of 16")
+    _expect(rc(BAD, fq.BF16, 32, 32, 0, BAD + 0x800, 0, None, None, None, None, None, None, S),
+            fq.EINVAL, "at least one")
+    _expect(rc(BAD, fq.BF16, 32, 32, 0, BAD + 0x800, 0, None, BAD + 0x10000, BAD + 0x10010, None, None, None, S),
+            fq.EINVAL, "overlap")
+
+
+def test_block_and_delayed_validation():
+    blk = L.fp8_quantize_block
+    _expect(blk(BAD, fq.BF16, 128, 128, 0, 64, BAD + 0x10000, BAD + 0x20000, None, None, S), fq.EINVAL, "block_rows")
+    _expect(blk(BAD, fq.BF16, 128, 200, 0, 128, BAD + 0x10000, BAD + 0x20000, None, None, S),
+            fq.EUNSUPPORTED, "multiples of 128")
+    _expect(blk(BAD, fq.BF16, 128, 128, 0, 1, BAD + 0x10000, BAD + 0x20000, BAD + 0x30000, None, S),
+            fq.EINVAL, "both")
+    up = L.fp8_update_scale_delayed
+    _expect(up(BAD, 16, 1, 1, BAD + 0x100, 0, 0, 0, 0, BAD + 0x200, BAD + 0x300, S), fq.EINVAL, "col")
+    _expect(up(BAD, 16, 1, 0, BAD + 0x100, 0, 0, 0, 9, BAD + 0x200, BAD + 0x300, S), fq.EINVAL, "algo")
+    _expect(up(BAD, 16, 1, 0, BAD + 0x100, -2, 0, 0, 0, BAD + 0x200, BAD + 0x300, S), fq.EINVAL, "step")
+    _expect(up(BAD, 16, 1, 0, BAD + 0x100, 0, 0, 0, 0, BAD + 0x8, BAD + 0x300, S), fq.EINVAL, "overlap")
+
+
+def test_gemm_validation():
+    g = L.fp8_scaled_gemm
+    A, B, C = BAD + 0x100000, BAD + 0x200000, BAD + 0x300000
+    _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 0, C, fq.F32, None, S), fq.EUNSUPPORTED, "bf16")
+    _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 100, 128, 0, C, fq.BF16, None, S), fq.EUNSUPPORTED, "multiples")
+    _expect(g(A, 2, BAD, B, 0, BAD + 4, 128, 128, 128, 0, C, fq.BF16, None, S), fq.EINVAL, "format")
+    _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 5, C, fq.BF16, None, S), fq.EINVAL, "mode")
+    _expect(g(A, 0, None, B, 0, BAD + 4, 128, 128, 128, 0, C, fq.BF16, None, S), fq.EINVAL, "sA")
+    _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 0, A + 64, fq.BF16, None, S), fq.EINVAL, "overlaps")
+    _expect(g(A + 8, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 0, C, fq.BF16, None, S), fq.EINVAL, "16-byte")
+
+
+def test_last_error_is_thread_local_string():
+    L.fp8_amax(BAD, 9, 16, BAD, S)
+    msg = fq.last_error()
+    assert isinstance(msg, str) and msg.startswith("fp8_amax")

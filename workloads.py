@@ -24,6 +24,8 @@ The second parameter of N(.,.) is a standard deviation.
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -105,3 +107,10 @@ def special_values_f32() -> np.ndarray:
                      0x7F800001, 0x7FFFFFFF, 0x7F7FFFFF, 0xFF7FFFFF, 0x00000001, 0x80000001,
                      0x007FFFFF, 0x00800000, 0x3F800000, 0xBF800000], dtype=np.uint32)
     return bits.view(np.float32)
+
+
+def parallel_map(fn, items, workers: int = 8):
+    """Generate several seeded inputs at once (numpy's generators release the
+    GIL while filling large arrays); results keep the order of ``items``."""
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))
