@@ -97,14 +97,9 @@ hipError_t get_grid_scratch(hipStream_t s, GridScratch **out)
         return hipSuccess;
     }
     void *p = nullptr;
-    e = hipMalloc(&p, 256);
+    e = hipMalloc(&p, sizeof(GridScratch));
     if (e != hipSuccess) return e;
     GridScratch *gs = static_cast<GridScratch *>(p);
-    e = launch_zero_scratch(gs, s);
-    if (e != hipSuccess) {
-        (void)hipFree(p);
-        return e;
-    }
     table.emplace(key, gs);
     *out = gs;
     return hipSuccess;
@@ -287,6 +282,9 @@ int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t
         return fail(FP8Q_EINVAL, "%s: C overlaps an input", fn);
     fp8q::GridScratch *gs = nullptr;
     if (amax_out) {
+        if ((M / 128) * (N / 128) > fp8q::kMaxPartials)
+            return fail(FP8Q_EUNSUPPORTED, "%s: amax_out needs at most %d output tiles of 128x128", fn,
+                        fp8q::kMaxPartials);
         hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
         if (e != hipSuccess) return hip_status(e, fn);
     }

@@ -8,17 +8,17 @@
 
 namespace fp8q {
 
-// Grid-wide reduction scratch: every block folds its magnitude max into
-// `max_bits` and takes a ticket; the last block publishes the result and puts
-// both words back to zero, so the next launch on the same stream finds them
-// zero again.  One per (device, stream); see get_grid_scratch.
+// Grid-wide reduction scratch: a kernel that reduces an amax writes one
+// partial (the canonical magnitude max of its block) per block; a one-block
+// finish kernel folds them into the output.  No atomics and no state carried
+// between launches.  One per (device, stream); see get_grid_scratch.
+constexpr int kMaxPartials = 65536;
 struct GridScratch {
-    uint32_t max_bits;
-    uint32_t ticket;
+    uint32_t part[kMaxPartials];
 };
 
 // The scratch of the calling thread's current device and stream `s`,
-// allocated (and zeroed on `s`) the first time that pair is seen.
+// allocated the first time that pair is seen.
 hipError_t get_grid_scratch(hipStream_t s, GridScratch **out);
 
 // Where a per-tensor scale comes from: exactly one pointer is non-null.
@@ -30,7 +30,7 @@ struct ScaleSrc {
 
 hipError_t launch_fill_u32(uint32_t *p, uint32_t v, hipStream_t s);
 
-hipError_t launch_zero_scratch(GridScratch *gs, hipStream_t s);
+hipError_t launch_finish_amax(const GridScratch *gs, int nparts, float *out, hipStream_t s);
 
 hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScratch *gs, hipStream_t s);
 

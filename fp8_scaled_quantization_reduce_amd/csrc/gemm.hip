@@ -2,23 +2,37 @@
 //
 // C[M][N] = (A*sA)(B*sB)^T with A [M][K], B [N][K] FP8 codes (K-contiguous),
 // fp32 accumulation in v_mfma_f32_16x16x128_f8f6f4 and a bf16 output.
-//   per-tensor: C = bf16(fl32(fl32(sA*sB) * acc))                 ("Megatron FP8",
-//               section 6: fp32 accumulate, bf16 out; section 27: one downcast
-//               of the finished dot product)
-//   block:      each 128-wide K slice is its own MFMA partial, promoted into the
-//               fp32 accumulator with the 1x128 scale of A's row and the
+//   per-tensor: C = bf16(fl32(fl32(sA*sB) * acc))   ("Megatron FP8", section 6:
+//               fp32 accumulation, bf16 output; section 27: products promoted
+//               to fp32 and summed, one downcast of the finished dot product)
+//   block:      each 128-wide K slice is its own MFMA partial, promoted into
+//               the fp32 accumulator with the 1x128 scale of A's row and the
 //               128x128 scale of B's block: acc += (sA[m,kb]*sB[n/128,kb]) * part
-// and, optionally, amax_out = max |C| over the emitted bf16 values.
+// and, optionally, the per-block magnitude max of the emitted bf16 values
+// (folded into amax_out by the finish kernel).
 //
-// Tiling: a 128x128 output tile per block of 256 lanes (four waves in 2x2, each
-// 64x64 = 4x4 MFMA tiles of 16x16), K in steps of 128 bytes.  Both operand
-// tiles (16 KiB each) are staged in LDS, double-buffered, with the 16-byte
-// chunks of each 128-byte row XOR-swizzled by the row index so that the
-// fragment reads of a wave spread over the banks.  A and B fragments are read
-// with the same lane -> K mapping, so the MFMA's internal K order does not
-// affect the dot product.  Blocks are remapped so that the tiles resident on
-// one XCD (blocks are dealt round-robin to the 8 XCDs) form contiguous groups
-// of rows and columns of C, which keeps their operand panels in that XCD's L2.
+// Tiling.  Four waves (2x2) per block; a wave owns 128 rows x (16 * kJ)
+// columns of C as 8 x kJ MFMA tiles of 16x16 (kJ = 8 per tensor: 256 fp32
+// accumulators, which live in the accumulation registers; kJ = 4 in block
+// mode, whose per-slice promotion runs on the vector ALU).  K moves in steps
+// of 128 (one MFMA K, one block-scale slice).  Operand tiles (rows x 128
+// bytes) go from global memory straight into LDS with buffer loads
+// (buffer_load_dwordx4 ... lds: no register staging) into two stages; each
+// iteration waits for its stage, reads every fragment it needs into
+// registers, then issues the loads of the next step into the other stage and
+// runs its MFMAs while they fly.  Inside a stage the eight 16-byte chunks of
+// every 128-byte row are XOR-swizzled by the row index, so the fragment reads
+// of a wave spread over the LDS banks.
+//
+// Operand order.  The MFMA is issued as (B fragment, A fragment), so its
+// 16x16 result is C^T: lane (r = lane % 16, g = lane / 16) holds C[r][4g..4g+3],
+// four consecutive columns of one row, stored as one 8-byte bf16 quad.  A and B
+// fragments use the same lane -> K mapping, so the MFMA's internal K order does
+// not affect the dot product.
+//
+// Blocks are dealt round-robin to the 8 XCDs; the tile index is remapped so
+// that each XCD works on a compact group of output tiles (4 tile rows wide),
+// whose operand panels then stay in that XCD's L2.
 #include "fp8q_device.h"
 #include "fp8q_launch.h"
 
@@ -26,24 +40,26 @@ namespace fp8q {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmThreads = 256;
-constexpr int kBM = 128, kBN = 128, kBK = 128;
+constexpr int kBM = 256, kBK = 128;
 constexpr int kXcds = 8;
-constexpr int kGroupM = 8; // tile rows per L2 group
+constexpr int kGroupM = 4; // tile rows per L2 group
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;
 
-template <int FA, int FB>
-__device__ __forceinline__ v4f mfma16x16x128(const v8i &a, const v8i &b, const v4f &c)
+__host__ __device__ constexpr int block_n(bool block_mode) { return block_mode ? 128 : 256; }
+
+template <int FX, int FY>
+__device__ __forceinline__ v4f mfma16x16x128(const v8i &x, const v8i &y, const v4f &c)
 {
-    // cbsz / blgp select the operand formats (0 = E4M3, 1 = E5M2); zero
-    // scale operands select the unscaled instruction.
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
+    // cbsz / blgp give the formats of the two operands (0 = E4M3, 1 = E5M2);
+    // zero scale operands select the unscaled instruction.
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, FX, FY, 0, 0, 0, 0);
 }
 
-// byte offset of 16-byte chunk c of row r in a [128][128] LDS tile
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// byte offset of 16-byte chunk c of row r in a [rows][128] LDS stage
+__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 4); }
 
 __device__ __forceinline__ void tile_of_block(int bid, int tilesM, int tilesN, int &tm, int &tn)
 {
@@ -59,155 +75,150 @@ __device__ __forceinline__ void tile_of_block(int bid, int tilesM, int tilesN, i
     tn = in_group / gsize;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Fill `rows` rows of a stage from a panel (buffer resource based at the
+// panel's first row): wave w loads rows 8 * (w + 4u) .. +7 for u = 0, 1, ...;
+// lane L writes LDS bytes 16L .. 16L+15 of the 1 KiB segment, i.e. physical
+// chunk L % 8 of row L / 8, which holds logical chunk (L % 8) ^ (L / 8).
+// Rows past the panel's last record read as zero; their results are never
+// stored.
+template <int kRows>
+__device__ __forceinline__ void stage_panel(__amdgpu_buffer_rsrc_t rsrc, int voff, int K, int k0, uint8_t *lds, int w)
+{
+#pragma unroll
+    for (int u = 0; u < kRows / 32; ++u) {
+        const int row = 8 * (w + 4 * u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + row * kBK), 16, voff, k0 + row * K, 0, 0);
+    }
+}
+
+// One operand fragment (16 rows x 128 K bytes): lane (r, g) reads logical
+// chunks 2g and 2g+1 of row r.
+__device__ __forceinline__ v8i read_frag(const uint8_t *lds, int r, int g)
+{
+    const uint4 lo = *reinterpret_cast<const uint4 *>(lds + swz(r, 2 * g));
+    const uint4 hi = *reinterpret_cast<const uint4 *>(lds + swz(r, 2 * g + 1));
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
 template <int FA, int FB, bool kBlock, bool kAmax>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(const uint8_t *__restrict__ A,
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint8_t *__restrict__ A,
                                                                const uint8_t *__restrict__ B,
                                                                const float *__restrict__ sA,
                                                                const float *__restrict__ sB, int M, int N, int K,
-                                                               __bf16 *__restrict__ C, GridScratch *gs,
-                                                               uint32_t *__restrict__ amax_out)
+                                                               __bf16 *__restrict__ C, GridScratch *gs)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kBM * kBK];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kBN * kBK];
-    __shared__ __attribute__((aligned(16))) float lds_sa[kBlock ? 2 : 1][kBlock ? kBM : 1];
+    constexpr int kBN = block_n(kBlock);
+    constexpr int kJ = kBN / 32; // 16-column MFMA tiles per wave
+    constexpr int kAStage = kBM * kBK, kBStage = kBN * kBK;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * (kAStage + kBStage)];
+    __shared__ __attribute__((aligned(16))) float lds_sa[2][kBlock ? kBM : 1];
     __shared__ uint32_t red[kGemmThreads / 64];
 
     int tm, tn;
-    tile_of_block(blockIdx.x, M / kBM, N / kBN, tm, tn);
+    tile_of_block(blockIdx.x, (M + kBM - 1) / kBM, (N + kBN - 1) / kBN, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, kept in a scalar register
     const int wm = w >> 1, wn = w & 1;
+    const int fr = lane & 15, fg = lane >> 4;
     const int nk = K / kBK;
     const int kblocks = K / 128;
 
-    // global -> LDS staging: lane loads rows ld_row + 32u, chunk ld_chunk
-    const int ld_row = tid >> 3, ld_chunk = tid & 7;
-    const uint8_t *Ag = A + (m0 + ld_row) * (int64_t)K + ld_chunk * 16;
-    const uint8_t *Bg = B + (n0 + ld_row) * (int64_t)K + ld_chunk * 16;
-    uint4 ra[4], rb[4];
-    float rsa = 0.f;
+    // buffer resources over this block's row panels (rows past the matrix
+    // edge are outside the record range)
+    const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBN, (int64_t)N - n0);
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * K), 0, (int)(a_rows * K), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0 * K), 0, (int)(b_rows * K), kRawBufferWord3);
+    const int voff = (lane >> 3) * K + (((lane & 7) ^ (lane >> 3)) << 4);
+    // (per-tensor mode: a one-record resource that is never read)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(kBlock ? sA + m0 * kblocks : sA), 0, kBlock ? (int)(a_rows * kblocks * 4) : 4, kRawBufferWord3);
 
-    auto gload = [&](int kt) {
-        const int64_t k0 = (int64_t)kt * kBK;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            ra[u] = *reinterpret_cast<const uint4 *>(Ag + (int64_t)(32 * u) * K + k0);
-            rb[u] = *reinterpret_cast<const uint4 *>(Bg + (int64_t)(32 * u) * K + k0);
-        }
-        if constexpr (kBlock) {
-            if (tid < kBM) rsa = sA[(m0 + tid) * kblocks + kt];
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int r = ld_row + 32 * u;
-            *reinterpret_cast<uint4 *>(&lds_a[buf][swz(r, ld_chunk)]) = ra[u];
-            *reinterpret_cast<uint4 *>(&lds_b[buf][swz(r, ld_chunk)]) = rb[u];
-        }
-        if constexpr (kBlock) {
-            if (tid < kBM) lds_sa[buf][tid] = rsa;
-        }
+    auto stage = [&](int s, int kt) {
+        uint8_t *la = lds + s * (kAStage + kBStage);
+        stage_panel<kBM>(ra, voff, K, kt * kBK, la, w);
+        stage_panel<kBN>(rb, voff, K, kt * kBK, la + kAStage, w);
+        if constexpr (kBlock)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&lds_sa[s][64 * w], 4, lane * kblocks * 4,
+                                                     (64 * w * kblocks + kt) * 4, 0, 0);
     };
 
-    v4f acc[4][4];
+    v4f acc[8][kJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < kJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    if (nk > 0) {
-        gload(0);
-        sstore(0);
-    }
-    __syncthreads();
-
-    const int fr = lane & 15, fg = lane >> 4; // fragment row within 16, K group
+    if (nk > 0) stage(0, 0);
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-
-        v8i a[4], b[4];
+        const int s = kt & 1;
+        const uint8_t *la = lds + s * (kAStage + kBStage);
+        const uint8_t *lb = la + kAStage;
+        __syncthreads(); // waits for this stage's loads (all lanes) and for every wave's reads of the other stage
+        v8i a[8], b[kJ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wm * 64 + 16 * i + fr;
-            const uint4 lo = *reinterpret_cast<const uint4 *>(&lds_a[cur][swz(r, 2 * fg)]);
-            const uint4 hi = *reinterpret_cast<const uint4 *>(&lds_a[cur][swz(r, 2 * fg + 1)]);
-            a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
+        for (int j = 0; j < kJ; ++j) b[j] = read_frag(lb, wn * (16 * kJ) + 16 * j + fr, fg);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = wn * 64 + 16 * j + fr;
-            const uint4 lo = *reinterpret_cast<const uint4 *>(&lds_b[cur][swz(r, 2 * fg)]);
-            const uint4 hi = *reinterpret_cast<const uint4 *>(&lds_b[cur][swz(r, 2 * fg + 1)]);
-            b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
-
+        for (int i = 0; i < 8; ++i) a[i] = read_frag(la, wm * 128 + 16 * i + fr, fg);
+        float wi[8];
         if constexpr (kBlock) {
-            // promote this K block's partials with the two block scales
-            const float sb = sB[(n0 / 128) * kblocks + kt];
-            v4f wsc[4];
+            const float sb = sB[((n0 + wn * 16 * kJ) / 128) * kblocks + kt];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 sa = *reinterpret_cast<const float4 *>(&lds_sa[cur][wm * 64 + 16 * i + 4 * fg]);
-                wsc[i] = v4f{sa.x * sb, sa.y * sb, sa.z * sb, sa.w * sb};
-            }
+            for (int i = 0; i < 8; ++i) wi[i] = lds_sa[s][wm * 128 + 16 * i + fr] * sb;
+        }
+        if (kt + 1 < nk) stage(s ^ 1, kt + 1);
+        if constexpr (kBlock) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const v4f part = mfma16x16x128<FA, FB>(a[i], b[j], v4f{0.f, 0.f, 0.f, 0.f});
+                for (int j = 0; j < kJ; ++j) {
+                    const v4f part = mfma16x16x128<FB, FA>(b[j], a[i], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(part[e], wsc[i][e], acc[i][j][e]);
+                    for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(part[e], wi[i], acc[i][j][e]);
                 }
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x128<FA, FB>(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < kJ; ++j) acc[i][j] = mfma16x16x128<FB, FA>(b[j], a[i], acc[i][j]);
         }
-
-        if (kt + 1 < nk) sstore(cur ^ 1);
-        __syncthreads();
     }
 
-    // epilogue: lane holds rows 4*fg + e (e = 0..3) of column fr of each 16x16 tile
+    // epilogue: lane (fr, fg) of tile (i, j) holds C[row][4 consecutive cols]
     const float alpha = kBlock ? 1.0f : (*sA) * (*sB);
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i) {
+        const int64_t row = m0 + wm * 128 + 16 * i + fr;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = n0 + wn * 64 + 16 * j + fr;
-#pragma unroll
-            for (int e = 0; e < 4; e += 2) {
-                const f32x2 v = kBlock ? f32x2{acc[i][j][e], acc[i][j][e + 1]}
-                                       : f32x2{acc[i][j][e] * alpha, acc[i][j][e + 1] * alpha};
-                const bf16x2 h = __builtin_convertvector(v, bf16x2);
-                const int64_t row = m0 + wm * 64 + 16 * i + 4 * fg + e;
-                C[row * N + col] = h[0];
-                C[(row + 1) * N + col] = h[1];
+        for (int j = 0; j < kJ; ++j) {
+            const int64_t col = n0 + wn * (16 * kJ) + 16 * j + 4 * fg;
+            const v4f v = kBlock ? acc[i][j] : acc[i][j] * alpha;
+            const bf16x4 h = __builtin_convertvector(v, bf16x4);
+            if (row < M && col < N) {
+                *reinterpret_cast<bf16x4 *>(C + row * N + col) = h;
                 if constexpr (kAmax) {
-                    const uint32_t bits = __builtin_bit_cast(uint32_t, h);
-                    m = max(m, (bits & 0x7FFFu) << 16);
-                    m = max(m, (bits >> 16 & 0x7FFFu) << 16);
+                    const uint2 bits = __builtin_bit_cast(uint2, h);
+                    m = max(m, max((bits.x & 0x7FFFu) << 16, (bits.x >> 16 & 0x7FFFu) << 16));
+                    m = max(m, max((bits.y & 0x7FFFu) << 16, (bits.y >> 16 & 0x7FFFu) << 16));
                 }
             }
         }
-    if constexpr (kAmax) {
-        // last-block finish, as in the quantization kernels
-        m = block_max_u32<kGemmThreads>(m, red);
-        if (tid == 0) {
-            atomicMax(&gs->max_bits, canonical_amax_bits(m));
-            __threadfence();
-            if (atomicAdd(&gs->ticket, 1u) == gridDim.x - 1) {
-                __threadfence();
-                const uint32_t v = atomicExch(&gs->max_bits, 0u);
-                atomicExch(&gs->ticket, 0u);
-                *amax_out = v;
-            }
-        }
     }
+    if constexpr (kAmax) {
+        m = block_max_u32<kGemmThreads>(m, red);
+        if (tid == 0) gs->part[blockIdx.x] = canonical_amax_bits(m);
+    }
+}
+
+int gemm_grid(int64_t M, int64_t N, int mode)
+{
+    const int bn = block_n(mode != 0);
+    return (int)(((M + kBM - 1) / kBM) * ((N + bn - 1) / bn));
 }
 
 template <int FA, int FB>
@@ -215,22 +226,23 @@ static hipError_t launch_gemm_t(const uint8_t *A, const float *sA, const uint8_t
                                 int64_t N, int64_t K, int mode, void *C, float *amax_out, GridScratch *gs,
                                 hipStream_t s)
 {
-    const int grid = (int)((M / kBM) * (N / kBN));
+    const int grid = gemm_grid(M, N, mode);
     __bf16 *c = reinterpret_cast<__bf16 *>(C);
-    uint32_t *am = reinterpret_cast<uint32_t *>(amax_out);
     const int m = (int)M, n = (int)N, k = (int)K;
     if (mode == 0) {
-        if (am)
-            gemm_kernel<FA, FB, false, true><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs, am);
+        if (amax_out)
+            gemm_kernel<FA, FB, false, true><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
         else
-            gemm_kernel<FA, FB, false, false><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs, am);
+            gemm_kernel<FA, FB, false, false><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
     } else {
-        if (am)
-            gemm_kernel<FA, FB, true, true><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs, am);
+        if (amax_out)
+            gemm_kernel<FA, FB, true, true><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
         else
-            gemm_kernel<FA, FB, true, false><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs, am);
+            gemm_kernel<FA, FB, true, false><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
     }
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !amax_out) return e;
+    return launch_finish_amax(gs, grid, amax_out, s);
 }
 
 hipError_t launch_gemm(const uint8_t *A, int fa, const float *sA, const uint8_t *B, int fb, const float *sB, int64_t M,

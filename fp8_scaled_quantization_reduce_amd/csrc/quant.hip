@@ -18,16 +18,18 @@
 namespace fp8q {
 
 constexpr int kThreads = 256;
-constexpr int kMaxStreamBlocks = 2048; // 8 blocks of 256 lanes per CU on 256 CUs
 
-static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-static int stream_grid(int64_t work_items, int items_per_thread)
+// Flat streaming launches: the work is cut into units of kThreads * U
+// vectors; block b takes units b, b + G, b + 2G, ... of a grid of
+// G = min(units, kMaxPartials) blocks (one unit per block at the sizes of
+// interest, so each lane issues its U loads back to back and the grid covers
+// the chip many times over).
+static int flat_grid(int64_t units)
 {
-    int64_t blocks = ceil_div(work_items, (int64_t)kThreads * items_per_thread);
-    if (blocks < 1) blocks = 1;
-    if (blocks > kMaxStreamBlocks) blocks = kMaxStreamBlocks;
-    return (int)blocks;
+    if (units < 1) return 1;
+    return (int)(units < kMaxPartials ? units : kMaxPartials);
 }
 
 template <int F>
@@ -48,98 +50,109 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t v, hipStream_t s)
     return hipGetLastError();
 }
 
-__global__ void zero_scratch_kernel(GridScratch *gs)
-{
-    if (threadIdx.x == 0 && blockIdx.x == 0) {
-        gs->max_bits = 0u;
-        gs->ticket = 0u;
-    }
-}
-
-hipError_t launch_zero_scratch(GridScratch *gs, hipStream_t s)
-{
-    zero_scratch_kernel<<<1, 64, 0, s>>>(gs);
-    return hipGetLastError();
-}
-
-// Grid-wide magnitude max without a separate initialisation launch: each
-// block folds its max into the scratch word and takes a ticket; the block
-// that draws the last ticket reads the final max, resets the scratch to zero
-// for the next launch and writes the result (every committed value is
-// already canonical, so the max is too).  Must be reached by every lane.
-__device__ __forceinline__ void grid_amax_commit(uint32_t m, GridScratch *gs, uint32_t *out)
+// One block's magnitude max -> its partial (canonical amax bits).  Every lane
+// must reach it.
+__device__ __forceinline__ void block_partial(uint32_t m, GridScratch *gs)
 {
     __shared__ uint32_t red[kThreads / 64];
     m = block_max_u32<kThreads>(m, red);
-    if (threadIdx.x == 0) {
-        atomicMax(&gs->max_bits, canonical_amax_bits(m));
-        __threadfence();
-        const uint32_t nblocks = gridDim.x * gridDim.y * gridDim.z;
-        if (atomicAdd(&gs->ticket, 1u) == nblocks - 1) {
-            __threadfence();
-            const uint32_t v = atomicExch(&gs->max_bits, 0u);
-            atomicExch(&gs->ticket, 0u);
-            *out = v;
-        }
+    if (threadIdx.x == 0) gs->part[blockIdx.x] = canonical_amax_bits(m);
+}
+
+// Fold nparts partials into the output word.  Each partial is canonical, so
+// their maximum is too.  1024 lanes with four independent loads each cover
+// the usual few thousand partials in one round trip.
+constexpr int kFinishThreads = 1024;
+
+__global__ __launch_bounds__(kFinishThreads) void finish_amax_kernel(const GridScratch *__restrict__ gs, int nparts,
+                                                                     uint32_t *__restrict__ out)
+{
+    __shared__ uint32_t red[kFinishThreads / 64];
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nparts; i += 4 * kFinishThreads) {
+        uint32_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = i + u * kFinishThreads < nparts ? gs->part[i + u * kFinishThreads] : 0u;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) m = max(m, v[u]);
     }
+    m = block_max_u32<kFinishThreads>(m, red);
+    if (threadIdx.x == 0) *out = m;
+}
+
+hipError_t launch_finish_amax(const GridScratch *gs, int nparts, float *out, hipStream_t s)
+{
+    finish_amax_kernel<<<1, kFinishThreads, 0, s>>>(gs, nparts, reinterpret_cast<uint32_t *>(out));
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ amax --
-// amax = max |x| ("Megatron FP8", section 4).  Grid-stride over 16-byte
-// vectors, four in flight per lane; the tail (< one vector) is read by the
-// first lanes of the grid.
+// amax = max |x| ("Megatron FP8", section 4).  Each lane reads U 16-byte
+// vectors of its unit, kThreads vectors apart (so every load instruction of a
+// wave covers 1 KiB contiguously); the tail of fewer than one vector is read
+// by the first lanes of block 0.
+constexpr int kAmaxU = 4;
+
 template <int DT>
-__global__ __launch_bounds__(kThreads) void amax_kernel(const void *__restrict__ x, int64_t n, GridScratch *gs,
-                                                        uint32_t *__restrict__ out)
+__global__ __launch_bounds__(kThreads) void amax_kernel(const void *__restrict__ x, int64_t n, GridScratch *gs)
 {
     constexpr int kPer = DT == kBF16 ? 8 : 4; // elements per 16-byte vector
     const int64_t nvec = n / kPer;
+    const int64_t units = ceil_div(nvec, (int64_t)kThreads * kAmaxU);
     const uint4 *__restrict__ xv = reinterpret_cast<const uint4 *>(x);
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     uint32_t m = 0;
     u16x2 m2 = {0, 0};
-    auto acc = [&](const uint4 &v) {
-        if constexpr (DT == kBF16) {
-            m2 = bf16_absmax2(m2, v.x);
-            m2 = bf16_absmax2(m2, v.y);
-            m2 = bf16_absmax2(m2, v.z);
-            m2 = bf16_absmax2(m2, v.w);
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int64_t base = unit * kThreads * kAmaxU + threadIdx.x;
+        const bool full = (unit + 1) * kThreads * kAmaxU <= nvec; // uniform: no per-load guards
+        uint4 v[kAmaxU];
+        if (full) {
+#pragma unroll
+            for (int u = 0; u < kAmaxU; ++u) v[u] = xv[base + u * kThreads];
         } else {
-            m = max(m, v.x & 0x7FFFFFFFu);
-            m = max(m, v.y & 0x7FFFFFFFu);
-            m = max(m, v.z & 0x7FFFFFFFu);
-            m = max(m, v.w & 0x7FFFFFFFu);
+#pragma unroll
+            for (int u = 0; u < kAmaxU; ++u) {
+                const int64_t i = base + u * kThreads;
+                v[u] = i < nvec ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+            }
         }
-    };
-    for (; i + 3 * stride < nvec; i += 4 * stride) {
-        const uint4 v0 = xv[i], v1 = xv[i + stride], v2 = xv[i + 2 * stride], v3 = xv[i + 3 * stride];
-        acc(v0);
-        acc(v1);
-        acc(v2);
-        acc(v3);
+#pragma unroll
+        for (int u = 0; u < kAmaxU; ++u) {
+            if constexpr (DT == kBF16) {
+                m2 = bf16_absmax2(m2, v[u].x);
+                m2 = bf16_absmax2(m2, v[u].y);
+                m2 = bf16_absmax2(m2, v[u].z);
+                m2 = bf16_absmax2(m2, v[u].w);
+            } else {
+                m = max(m, v[u].x & 0x7FFFFFFFu);
+                m = max(m, v[u].y & 0x7FFFFFFFu);
+                m = max(m, v[u].z & 0x7FFFFFFFu);
+                m = max(m, v[u].w & 0x7FFFFFFFu);
+            }
+        }
     }
-    for (; i < nvec; i += stride) acc(xv[i]);
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (t < n - nvec * kPer) {
-        const int64_t e = nvec * kPer + t;
+    if (blockIdx.x == 0 && threadIdx.x < n - nvec * kPer) {
+        const int64_t e = nvec * kPer + threadIdx.x;
         if constexpr (DT == kBF16)
             m = max(m, ((uint32_t)(reinterpret_cast<const uint16_t *>(x)[e] & 0x7FFFu)) << 16);
         else
             m = max(m, reinterpret_cast<const uint32_t *>(x)[e] & 0x7FFFFFFFu);
     }
     if constexpr (DT == kBF16) m = max(m, bf16_absmax_to_f32bits(m2));
-    grid_amax_commit(m, gs, out);
+    block_partial(m, gs);
 }
 
 hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScratch *gs, hipStream_t s)
 {
-    uint32_t *out = reinterpret_cast<uint32_t *>(amax);
+    const int64_t nvec = n / (dtype == kBF16 ? 8 : 4);
+    const int grid = flat_grid(ceil_div(nvec, (int64_t)kThreads * kAmaxU));
     if (dtype == kBF16)
-        amax_kernel<kBF16><<<stream_grid(n / 8, 4), kThreads, 0, s>>>(x, n, gs, out);
+        amax_kernel<kBF16><<<grid, kThreads, 0, s>>>(x, n, gs);
     else
-        amax_kernel<kF32><<<stream_grid(n / 4, 4), kThreads, 0, s>>>(x, n, gs, out);
-    return hipGetLastError();
+        amax_kernel<kF32><<<grid, kThreads, 0, s>>>(x, n, gs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_finish_amax(gs, grid, amax, s);
 }
 
 // ------------------------------------------------------------------ cast --
@@ -153,6 +166,7 @@ template <> struct Chunk16<kBF16> {
         a = p[0];
         b = p[1];
     }
+    __device__ __forceinline__ void zero() { a = b = make_uint4(0u, 0u, 0u, 0u); }
     __device__ __forceinline__ float get(int k) const
     {
         const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -180,6 +194,7 @@ template <> struct Chunk16<kF32> {
         v[2] = p[2];
         v[3] = p[3];
     }
+    __device__ __forceinline__ void zero() { v[0] = v[1] = v[2] = v[3] = make_uint4(0u, 0u, 0u, 0u); }
     __device__ __forceinline__ float get(int k) const
     {
         const uint4 &q = v[k >> 2];
@@ -211,12 +226,16 @@ __device__ __forceinline__ uint4 encode_chunk(const Chunk16<DT> &c, float scale)
 
 // Per-tensor cast ("Megatron FP8", section 4): q = encode(fl32(x * scale)).
 // Every lane derives the scale from the device scalar (no host round trip);
-// block 0 publishes it.  With kAmax the input's magnitude max is reduced in
-// the same pass (delayed scaling records it after the cast, section 5).
+// block 0 publishes it.  A lane encodes U chunks of 16 elements of its unit,
+// kThreads chunks apart, into one 16-byte store each.  With kAmax the input's
+// magnitude max is reduced in the same pass into the block's partial
+// (delayed scaling records it after the cast, section 5).
+constexpr int kCastU = 2;
+
 template <int F, int DT, bool kAmax>
 __global__ __launch_bounds__(kThreads) void cast_kernel(const void *__restrict__ x, int64_t n, ScaleSrc src,
                                                         uint8_t *__restrict__ q, float *scale_inv_out,
-                                                        float *scale_out, GridScratch *gs, uint32_t *amax_out)
+                                                        float *scale_out, GridScratch *gs)
 {
     const Scales sc = resolve_scales<F>(src);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -224,32 +243,34 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const void *__restrict__
         if (scale_out) *scale_out = sc.scale;
     }
     const int64_t nch = n >> 4;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t units = ceil_div(nch, (int64_t)kThreads * kCastU);
     uint4 *__restrict__ qv = reinterpret_cast<uint4 *>(q);
     uint32_t m = 0;
     u16x2 m2 = {0, 0};
-    for (; c + stride < nch; c += 2 * stride) {
-        Chunk16<DT> a, b;
-        a.load(x, c);
-        b.load(x, c + stride);
-        if constexpr (kAmax) {
-            a.absmax(m, m2);
-            b.absmax(m, m2);
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int64_t base = unit * kThreads * kCastU + threadIdx.x;
+        const bool full = (unit + 1) * kThreads * kCastU <= nch; // uniform: no per-load guards
+        Chunk16<DT> c[kCastU];
+        if (full) {
+#pragma unroll
+            for (int u = 0; u < kCastU; ++u) c[u].load(x, base + u * kThreads);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kCastU; ++u) {
+                if (base + u * kThreads < nch) c[u].load(x, base + u * kThreads);
+                else c[u].zero();
+            }
         }
-        qv[c] = encode_chunk<F, DT>(a, sc.scale);
-        qv[c + stride] = encode_chunk<F, DT>(b, sc.scale);
-    }
-    if (c < nch) {
-        Chunk16<DT> a;
-        a.load(x, c);
-        if constexpr (kAmax) a.absmax(m, m2);
-        qv[c] = encode_chunk<F, DT>(a, sc.scale);
+#pragma unroll
+        for (int u = 0; u < kCastU; ++u) {
+            if constexpr (kAmax) c[u].absmax(m, m2);
+            const uint4 o = encode_chunk<F, DT>(c[u], sc.scale);
+            if (full || base + u * kThreads < nch) qv[base + u * kThreads] = o;
+        }
     }
     // tail: fewer than 16 elements, one per lane of block 0
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (t < n - (nch << 4)) {
-        const int64_t e = (nch << 4) + t;
+    if (blockIdx.x == 0 && threadIdx.x < n - (nch << 4)) {
+        const int64_t e = (nch << 4) + threadIdx.x;
         float v;
         if constexpr (DT == kBF16)
             v = __uint_as_float(((uint32_t)reinterpret_cast<const uint16_t *>(x)[e]) << 16);
@@ -260,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const void *__restrict__
     }
     if constexpr (kAmax) {
         if constexpr (DT == kBF16) m = max(m, bf16_absmax_to_f32bits(m2));
-        grid_amax_commit(m, gs, amax_out);
+        block_partial(m, gs);
     }
 }
 
@@ -268,13 +289,14 @@ template <int F, int DT>
 static hipError_t launch_cast_t(const void *x, int64_t n, ScaleSrc src, uint8_t *q, float *scale_inv_out,
                                 float *scale_out, float *amax_out, GridScratch *gs, hipStream_t s)
 {
-    const int grid = stream_grid(n >> 4, 2);
+    const int grid = flat_grid(ceil_div(n >> 4, (int64_t)kThreads * kCastU));
     if (amax_out)
-        cast_kernel<F, DT, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs,
-                                                           reinterpret_cast<uint32_t *>(amax_out));
+        cast_kernel<F, DT, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs);
     else
-        cast_kernel<F, DT, false><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs, nullptr);
-    return hipGetLastError();
+        cast_kernel<F, DT, false><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !amax_out) return e;
+    return launch_finish_amax(gs, grid, amax_out, s);
 }
 
 hipError_t launch_cast(const void *x, int dtype, int64_t n, int fmt, ScaleSrc src, uint8_t *q, float *scale_inv_out,
@@ -302,29 +324,42 @@ __device__ __forceinline__ float2 dec2(uint32_t w)
 }
 
 // y = fl32(value(q) * scale_inv) ("Megatron FP8", section 4).  The hardware
-// decoder gives the exact value of every code.
+// decoder gives the exact value of every code.  A lane decodes U words of
+// four codes, kThreads words apart, each into one 16-byte store, so that every
+// store instruction of a wave writes 1 KiB contiguously (the output is four
+// times the input and dominates the traffic).
+constexpr int kDequantU = 2;
+
 template <int F>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__restrict__ q, int64_t n,
                                                            const float *__restrict__ scale_inv, float *__restrict__ y)
 {
     const float s = *scale_inv;
-    const int64_t nch = n >> 4;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    const uint4 *__restrict__ qv = reinterpret_cast<const uint4 *>(q);
+    const int64_t nw = n >> 2;
+    const int64_t units = ceil_div(nw, (int64_t)kThreads * kDequantU);
+    const uint32_t *__restrict__ qw = reinterpret_cast<const uint32_t *>(q);
     float4 *__restrict__ yv = reinterpret_cast<float4 *>(y);
-    for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nch; c += stride) {
-        const uint4 v = qv[c];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int64_t base = unit * kThreads * kDequantU + threadIdx.x;
+        const bool full = (unit + 1) * kThreads * kDequantU <= nw; // uniform: no per-load guards
+        uint32_t w[kDequantU];
+        if (full) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float2 lo = dec2<F, false>(w[j]);
-            const float2 hi = dec2<F, true>(w[j]);
-            yv[4 * c + j] = make_float4(lo.x * s, lo.y * s, hi.x * s, hi.y * s);
+            for (int u = 0; u < kDequantU; ++u) w[u] = qw[base + u * kThreads];
+        } else {
+#pragma unroll
+            for (int u = 0; u < kDequantU; ++u) w[u] = base + u * kThreads < nw ? qw[base + u * kThreads] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kDequantU; ++u) {
+            const float2 lo = dec2<F, false>(w[u]);
+            const float2 hi = dec2<F, true>(w[u]);
+            if (full || base + u * kThreads < nw)
+                yv[base + u * kThreads] = make_float4(lo.x * s, lo.y * s, hi.x * s, hi.y * s);
         }
     }
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (t < n - (nch << 4)) {
-        const int64_t e = (nch << 4) + t;
+    if (blockIdx.x == 0 && threadIdx.x < n - (nw << 2)) {
+        const int64_t e = (nw << 2) + threadIdx.x;
         y[e] = dec2<F, false>((uint32_t)q[e]).x * s;
     }
 }
@@ -332,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__rest
 hipError_t launch_dequant(const uint8_t *q, int fmt, int64_t n, const float *scale_inv, float *y, hipStream_t s)
 {
     if (n == 0) return hipSuccess;
-    const int grid = stream_grid(n >> 4, 2);
+    const int grid = flat_grid(ceil_div(n >> 2, (int64_t)kThreads * kDequantU));
     if (fmt == kE4M3)
         dequant_kernel<kE4M3><<<grid, kThreads, 0, s>>>(q, n, scale_inv, y);
     else
@@ -491,146 +526,166 @@ __device__ __forceinline__ void store_transposed(const uint32_t *tl, uint8_t *q_
     }
 }
 
+// One block loops over tiles t = blockIdx.x, blockIdx.x + G, ... (tile row
+// t / tiles_per_row, tile column t % tiles_per_row).
 template <int F, int DT, int kMode, bool kAmax>
 __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__ x, int64_t rows, int64_t cols,
                                                         ScaleSrc src, uint8_t *__restrict__ q_row,
                                                         uint8_t *__restrict__ q_col, float *__restrict__ s_row,
                                                         float *__restrict__ s_col, float *scale_inv_out,
-                                                        float *scale_out, GridScratch *gs, uint32_t *amax_out)
+                                                        float *scale_out, GridScratch *gs)
 {
-    __shared__ uint32_t tl[kTile * 32];            // transposed codes, 16 KiB
+    __shared__ uint32_t tl[kTile * 32]; // transposed codes, 16 KiB
     __shared__ uint32_t red[kThreads / 64];
     __shared__ uint32_t colmax[kMode == kTileBlock1x128 ? 32 * kTile : 1];
     __shared__ float colscale[kMode == kTileBlock1x128 ? kTile : 1];
 
     const int ig = threadIdx.x >> 3, jg = threadIdx.x & 7;
-    const int64_t row0 = (int64_t)blockIdx.y * kTile, col0 = (int64_t)blockIdx.x * kTile;
-    const int64_t r0 = row0 + 4 * ig, c0 = col0 + 16 * jg;
-    const bool valid = (r0 < rows) && (c0 < cols); // rows % 4 == 0, cols % 16 == 0
+    const int64_t tiles_c = ceil_div(cols, kTile), tiles = tiles_c * ceil_div(rows, kTile);
+    const int64_t brows = rows / kTile, bcols = cols / kTile; // block-scale grid (block modes)
 
-    Patch<DT> p;
-    if (valid) p.load(x, cols, r0, c0);
-    else p.zero();
-
-    uint32_t cw[4][4]; // rowwise codes
-
+    Scales sc_tensor{1.0f, 1.0f};
     if constexpr (kMode == kTilePerTensor) {
-        const Scales sc = resolve_scales<F>(src);
-        if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-            if (scale_inv_out) *scale_inv_out = sc.s;
-            if (scale_out) *scale_out = sc.scale;
+        sc_tensor = resolve_scales<F>(src);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            if (scale_inv_out) *scale_inv_out = sc_tensor.s;
+            if (scale_out) *scale_out = sc_tensor.scale;
         }
-        if constexpr (kAmax) {
+    }
+    uint32_t m_all = 0; // per-tensor fused amax
+
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const int64_t tr = t / tiles_c, tc = t - tr * tiles_c;
+        const int64_t row0 = tr * kTile, col0 = tc * kTile;
+        const int64_t r0 = row0 + 4 * ig, c0 = col0 + 16 * jg;
+        const bool valid = (r0 < rows) && (c0 < cols); // rows % 4 == 0, cols % 16 == 0
+
+        Patch<DT> p;
+        if (valid) p.load(x, cols, r0, c0);
+        else p.zero();
+
+        uint32_t cw[4][4]; // rowwise codes
+
+        if constexpr (kMode == kTilePerTensor) {
+            if constexpr (kAmax) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) m_all = max(m_all, f32_absbits(p.v[r][k]));
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    cw[r][q4] = encode4<F>(p.v[r][4 * q4], p.v[r][4 * q4 + 1], p.v[r][4 * q4 + 2],
+                                           p.v[r][4 * q4 + 3], sc_tensor.scale);
+        } else if constexpr (kMode == kTileBlock128) {
             uint32_t m = 0;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(p.v[r][k]));
-            grid_amax_commit(m, gs, amax_out);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                cw[r][q4] = encode4<F>(p.v[r][4 * q4], p.v[r][4 * q4 + 1], p.v[r][4 * q4 + 2], p.v[r][4 * q4 + 3],
-                                       sc.scale);
-    } else if constexpr (kMode == kTileBlock128) {
-        uint32_t m = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(p.v[r][k]));
-        m = block_max_u32<kThreads>(m, red);
-        const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
-        if (threadIdx.x == 0) {
-            s_row[blockIdx.y * (cols / kTile) + blockIdx.x] = sc.s;
-            if (s_col) s_col[blockIdx.x * (rows / kTile) + blockIdx.y] = sc.s;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                cw[r][q4] = encode4<F>(p.v[r][4 * q4], p.v[r][4 * q4 + 1], p.v[r][4 * q4 + 2], p.v[r][4 * q4 + 3],
-                                       sc.scale);
-    } else { // 1x128 blocks: one scale per row segment, one per column segment
-        // row segments: the 8 lanes jg = 0..7 of a row group hold the row's 128 columns
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            uint32_t m = 0;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(p.v[r][k]));
-            m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-            m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-            m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+            m = block_max_u32<kThreads>(m, red);
             const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
-            if (jg == 0) s_row[(r0 + r) * (cols / kTile) + blockIdx.x] = sc.s;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                cw[r][q4] = encode4<F>(p.v[r][4 * q4], p.v[r][4 * q4 + 1], p.v[r][4 * q4 + 2], p.v[r][4 * q4 + 3],
-                                       sc.scale);
-        }
-        // column segments: reduce each column's 128 rows through LDS
-        if (q_col) {
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                uint32_t m = 0;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) m = max(m, f32_absbits(p.v[r][k]));
-                colmax[ig * kTile + 16 * jg + k] = m;
+            if (threadIdx.x == 0) {
+                s_row[tr * bcols + tc] = sc.s;
+                if (s_col) s_col[tc * brows + tr] = sc.s;
             }
-            __syncthreads();
-            if (threadIdx.x < kTile) {
-                uint32_t m = 0;
-#pragma unroll 8
-                for (int g = 0; g < 32; ++g) m = max(m, colmax[g * kTile + threadIdx.x]);
-                const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
-                colscale[threadIdx.x] = sc.scale;
-                s_col[(col0 + threadIdx.x) * (rows / kTile) + blockIdx.y] = sc.s;
-            }
-            __syncthreads();
-        }
-    }
-
-    if (q_row && valid) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) = make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
-    }
-    if (q_col) {
-        if constexpr (kMode == kTileBlock1x128) {
-            // columnwise codes use the column-segment scales
-            uint32_t cc[4][4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int k = 4 * q4;
-                    const float *cs = colscale + 16 * jg + k;
-                    cc[r][q4] = encode4s<F>(p.v[r][k], p.v[r][k + 1], p.v[r][k + 2], p.v[r][k + 3], cs[0], cs[1],
-                                            cs[2], cs[3]);
+                for (int q4 = 0; q4 < 4; ++q4)
+                    cw[r][q4] = encode4<F>(p.v[r][4 * q4], p.v[r][4 * q4 + 1], p.v[r][4 * q4 + 2],
+                                           p.v[r][4 * q4 + 3], sc.scale);
+        } else { // 1x128 blocks: one scale per row segment, one per column segment
+            // row segments: the 8 lanes jg = 0..7 of a row group hold the row's 128 columns
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(p.v[r][k]));
+                m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+                m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+                m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+                const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
+                if (jg == 0) s_row[(r0 + r) * bcols + tc] = sc.s;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    cw[r][q4] = encode4<F>(p.v[r][4 * q4], p.v[r][4 * q4 + 1], p.v[r][4 * q4 + 2],
+                                           p.v[r][4 * q4 + 3], sc.scale);
+            }
+            // column segments: reduce each column's 128 rows through LDS
+            if (q_col) {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    uint32_t m = 0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m = max(m, f32_absbits(p.v[r][k]));
+                    colmax[ig * kTile + 16 * jg + k] = m;
                 }
-            stage_transposed(tl, cc, ig, jg);
-        } else {
-            stage_transposed(tl, cw, ig, jg);
+                __syncthreads();
+                if (threadIdx.x < kTile) {
+                    uint32_t m = 0;
+#pragma unroll 8
+                    for (int g = 0; g < 32; ++g) m = max(m, colmax[g * kTile + threadIdx.x]);
+                    const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
+                    colscale[threadIdx.x] = sc.scale;
+                    s_col[(col0 + threadIdx.x) * brows + tr] = sc.s;
+                }
+                __syncthreads();
+            }
         }
-        __syncthreads();
-        store_transposed(tl, q_col, rows, cols, row0, col0);
+
+        if (q_row && valid) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) =
+                    make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
+        }
+        if (q_col) {
+            if constexpr (kMode == kTileBlock1x128) {
+                // columnwise codes use the column-segment scales
+                uint32_t cc[4][4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int k = 4 * q4;
+                        const float *cs = colscale + 16 * jg + k;
+                        cc[r][q4] = encode4s<F>(p.v[r][k], p.v[r][k + 1], p.v[r][k + 2], p.v[r][k + 3], cs[0],
+                                                cs[1], cs[2], cs[3]);
+                    }
+                stage_transposed(tl, cc, ig, jg);
+            } else {
+                stage_transposed(tl, cw, ig, jg);
+            }
+            __syncthreads();
+            store_transposed(tl, q_col, rows, cols, row0, col0);
+        }
+        __syncthreads(); // the next tile reuses the LDS buffers
     }
+    if constexpr (kAmax) block_partial(m_all, gs);
+}
+
+static int tile_grid(int64_t rows, int64_t cols)
+{
+    return flat_grid(ceil_div(rows, kTile) * ceil_div(cols, kTile));
 }
 
 template <int F, int DT>
 static hipError_t launch_rc_t(const void *x, int64_t rows, int64_t cols, ScaleSrc src, uint8_t *q_row, uint8_t *q_col,
                               float *scale_inv_out, float *scale_out, float *amax_out, GridScratch *gs, hipStream_t s)
 {
-    const dim3 grid((unsigned)ceil_div(cols, kTile), (unsigned)ceil_div(rows, kTile));
+    const int grid = tile_grid(rows, cols);
     if (amax_out)
-        tile_kernel<F, DT, kTilePerTensor, true><<<grid, kThreads, 0, s>>>(
-            x, rows, cols, src, q_row, q_col, nullptr, nullptr, scale_inv_out, scale_out, gs,
-            reinterpret_cast<uint32_t *>(amax_out));
+        tile_kernel<F, DT, kTilePerTensor, true><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr,
+                                                                          nullptr, scale_inv_out, scale_out, gs);
     else
-        tile_kernel<F, DT, kTilePerTensor, false><<<grid, kThreads, 0, s>>>(
-            x, rows, cols, src, q_row, q_col, nullptr, nullptr, scale_inv_out, scale_out, gs, nullptr);
-    return hipGetLastError();
+        tile_kernel<F, DT, kTilePerTensor, false><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr,
+                                                                           nullptr, scale_inv_out, scale_out, nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !amax_out) return e;
+    return launch_finish_amax(gs, grid, amax_out, s);
 }
 
 hipError_t launch_rowwise_colwise(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, ScaleSrc src,
@@ -656,14 +711,14 @@ template <int F, int DT>
 static hipError_t launch_block_t(const void *x, int64_t rows, int64_t cols, int block_rows, uint8_t *q_row,
                                  float *s_row, uint8_t *q_col, float *s_col, hipStream_t s)
 {
-    const dim3 grid((unsigned)(cols / kTile), (unsigned)(rows / kTile));
+    const int grid = tile_grid(rows, cols);
     const ScaleSrc none{nullptr, nullptr, 0};
     if (block_rows == 128)
         tile_kernel<F, DT, kTileBlock128, false><<<grid, kThreads, 0, s>>>(x, rows, cols, none, q_row, q_col, s_row,
-                                                                          s_col, nullptr, nullptr, nullptr, nullptr);
+                                                                          s_col, nullptr, nullptr, nullptr);
     else
-        tile_kernel<F, DT, kTileBlock1x128, false><<<grid, kThreads, 0, s>>>(
-            x, rows, cols, none, q_row, q_col, s_row, s_col, nullptr, nullptr, nullptr, nullptr);
+        tile_kernel<F, DT, kTileBlock1x128, false><<<grid, kThreads, 0, s>>>(x, rows, cols, none, q_row, q_col,
+                                                                            s_row, s_col, nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 

@@ -11,11 +11,12 @@
  *  - All pointers are DEVICE memory owned by the caller, unless stated.  The
  *    library never copies device->host and never synchronises: each call
  *    enqueues its kernels on `stream` (a hipStream_t; NULL = the default
- *    stream) and returns.  The only device memory it allocates is a 256-byte
- *    reduction scratch per (device, stream) pair, on the first call on that
- *    pair that reduces an amax, held until the process ends.  Calls on one
- *    stream share that scratch in stream order; two host threads that enqueue
- *    on the same stream handle concurrently must serialise their calls.
+ *    stream) and returns.  The only device memory it allocates is a 256 KiB
+ *    reduction scratch (per-block partial maxima) per (device, stream) pair,
+ *    on the first call on that pair that reduces an amax, held until the
+ *    process ends.  Calls on one stream use that scratch in stream order; two
+ *    host threads that enqueue on the same stream handle concurrently must
+ *    serialise their calls.
  *  - Enum-valued arguments are passed as int32_t (values below).
  *  - Tensors are dense and row-major.  FP8 tensors are arrays of 8-bit codes
  *    (uint8_t).  bf16 tensors are arrays of 16-bit bf16 patterns.
