@@ -38,6 +38,8 @@ SIGNATURES = {
     "fp8_quantize_rowwise_colwise": [_VP, _I32, _I64, _I64, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "fp8_quantize_block": [_VP, _I32, _I64, _I64, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
     "fp8_update_scale_delayed": [_VP, _I32, _I32, _I32, _VP, _I64, _I32, _I32, _I32, _VP, _VP, _VP],
+    "fp8_quantize_delayed": [_VP, _I32, _I64, _I32, _VP, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP,
+                             _VP, _VP],
     "fp8_scaled_gemm": [_VP, _I32, _VP, _VP, _I32, _VP, _I64, _I64, _I64, _I32, _VP, _I32, _VP, _VP],
     "fp8q_last_error": [],
 }
@@ -137,6 +139,16 @@ def fp8_update_scale_delayed(hist, col, new_amax, step, fmt, margin, algo, scale
     history_len, n_cols = hist.shape
     _check(lib.fp8_update_scale_delayed(_ptr(hist), history_len, n_cols, col, _ptr(new_amax), step, fmt, margin, algo,
                                         _ptr(scale), _ptr(scale_inv), _stream(stream)))
+
+
+def fp8_quantize_delayed(x, fmt, hist, col, step, fmt_next, margin, algo, scale, scale_inv, q, q_scale_inv_out=None,
+                         amax_out=None, stream=None):
+    """One delayed-scaling step: cast with scale_inv[col], then record max|x|
+    in column col of hist and update scale/scale_inv for fmt_next."""
+    history_len, n_cols = hist.shape
+    _check(lib.fp8_quantize_delayed(_ptr(x), _dtype(x), x.numel(), fmt, _ptr(hist), history_len, n_cols, col, step,
+                                    fmt_next, margin, algo, _ptr(scale), _ptr(scale_inv), _ptr(q),
+                                    _ptr(q_scale_inv_out), _ptr(amax_out), _stream(stream)))
 
 
 def fp8_scaled_gemm(A, fa, sA, B, fb, sB, mode, C, amax_out=None, stream=None):

@@ -253,6 +253,45 @@ int fp8_update_scale_delayed(float *hist, int32_t history_len, int32_t n_cols, i
                       fn);
 }
 
+int fp8_quantize_delayed(const void *x, int32_t dtype, int64_t n, int32_t fmt, float *hist, int32_t history_len,
+                         int32_t n_cols, int32_t col, int64_t step, int32_t fmt_next, int32_t margin, int32_t algo,
+                         float *scale, float *scale_inv, uint8_t *q, float *q_scale_inv_out, float *amax_out,
+                         void *stream)
+{
+    const char *fn = "fp8_quantize_delayed";
+    if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+    if (!valid_fmt(fmt) || !valid_fmt(fmt_next)) return fail(FP8Q_EINVAL, "%s: unknown format", fn);
+    if (n < 0) return fail(FP8Q_EINVAL, "%s: negative n", fn);
+    if (algo != FP8Q_ALGO_MAX && algo != FP8Q_ALGO_MOST_RECENT)
+        return fail(FP8Q_EINVAL, "%s: unknown algo %d", fn, (int)algo);
+    if (history_len < 1 || n_cols < 1 || col < 0 || col >= n_cols)
+        return fail(FP8Q_EINVAL, "%s: need history_len >= 1 and 0 <= col < n_cols", fn);
+    if (step < 0) return fail(FP8Q_EINVAL, "%s: negative step", fn);
+    if (!hist || !scale || !scale_inv || !aligned(hist, 4) || !aligned(scale, 4) || !aligned(scale_inv, 4))
+        return fail(FP8Q_EINVAL, "%s: hist, scale, scale_inv must be 4-byte aligned pointers", fn);
+    if ((q_scale_inv_out && !aligned(q_scale_inv_out, 4)) || (amax_out && !aligned(amax_out, 4)))
+        return fail(FP8Q_EINVAL, "%s: scalar outputs must be 4-byte aligned", fn);
+    const int64_t nh = (int64_t)history_len * n_cols * 4;
+    if (overlap(hist, nh, scale, 4 * n_cols) || overlap(hist, nh, scale_inv, 4 * n_cols) ||
+        overlap(scale, 4 * n_cols, scale_inv, 4 * n_cols) || overlap(q_scale_inv_out, 4, hist, nh) ||
+        overlap(q_scale_inv_out, 4, scale, 4 * n_cols) || overlap(q_scale_inv_out, 4, scale_inv, 4 * n_cols) ||
+        overlap(amax_out, 4, hist, nh) || overlap(amax_out, 4, scale, 4 * n_cols) ||
+        overlap(amax_out, 4, scale_inv, 4 * n_cols) || (amax_out && amax_out == q_scale_inv_out))
+        return fail(FP8Q_EINVAL, "%s: state and scalar buffers overlap", fn);
+    if (n > 0) {
+        if (!x || !aligned(x, 16)) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
+        if (!q || !aligned(q, 16)) return fail(FP8Q_EINVAL, "%s: q must be a 16-byte aligned pointer", fn);
+        if (overlap(x, n * dsize(dtype), q, n)) return fail(FP8Q_EINVAL, "%s: q overlaps x", fn);
+    }
+    fp8q::GridScratch *gs = nullptr;
+    hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
+    if (e != hipSuccess) return hip_status(e, fn);
+    return hip_status(fp8q::launch_delayed_step(x, dtype, n, fmt, hist, history_len, n_cols, col, step, fmt_next, margin,
+                                                algo, scale, scale_inv, q, q_scale_inv_out, amax_out, gs,
+                                                (hipStream_t)stream),
+                      fn);
+}
+
 int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb, const float *sB,
                     int64_t M, int64_t N, int64_t K, int32_t mode, void *C, int32_t c_dtype, float *amax_out,
                     void *stream)

@@ -49,6 +49,11 @@ hipError_t launch_block(const void *x, int dtype, int64_t rows, int64_t cols, in
 hipError_t launch_delayed(float *hist, int history_len, int n_cols, int col, const float *new_amax, int64_t step,
                           int fmt, int margin, int algo, float *scale, float *scale_inv, hipStream_t s);
 
+hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, float *hist, int history_len, int n_cols,
+                               int col, int64_t step, int fmt_next, int margin, int algo, float *scale,
+                               float *scale_inv, uint8_t *q, float *q_scale_inv_out, float *amax_out, GridScratch *gs,
+                               hipStream_t s);
+
 hipError_t launch_gemm(const uint8_t *A, int fa, const float *sA, const uint8_t *B, int fb, const float *sB, int64_t M,
                        int64_t N, int64_t K, int mode, void *C, float *amax_out, GridScratch *gs, hipStream_t s);
 

@@ -104,17 +104,12 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void *__restrict__
     u16x2 m2 = {0, 0};
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int64_t base = unit * kThreads * kAmaxU + threadIdx.x;
-        const bool full = (unit + 1) * kThreads * kAmaxU <= nvec; // uniform: no per-load guards
+        // lanes past the end re-read the last vector (harmless for a max)
         uint4 v[kAmaxU];
-        if (full) {
 #pragma unroll
-            for (int u = 0; u < kAmaxU; ++u) v[u] = xv[base + u * kThreads];
-        } else {
-#pragma unroll
-            for (int u = 0; u < kAmaxU; ++u) {
-                const int64_t i = base + u * kThreads;
-                v[u] = i < nvec ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
-            }
+        for (int u = 0; u < kAmaxU; ++u) {
+            const int64_t i = base + u * kThreads;
+            v[u] = xv[i < nvec ? i : nvec - 1];
         }
 #pragma unroll
         for (int u = 0; u < kAmaxU; ++u) {
@@ -159,57 +154,36 @@ hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScr
 // Load 16 consecutive elements (one chunk) as floats.
 template <int DT> struct Chunk16;
 template <> struct Chunk16<kBF16> {
-    uint4 a, b; // 16 bf16
+    uint32_t w[8]; // 16 bf16
     __device__ __forceinline__ void load(const void *x, int64_t c)
     {
         const uint4 *p = reinterpret_cast<const uint4 *>(x) + 2 * c;
-        a = p[0];
-        b = p[1];
+        const uint4 a = p[0], b = p[1];
+        w[0] = a.x, w[1] = a.y, w[2] = a.z, w[3] = a.w, w[4] = b.x, w[5] = b.y, w[6] = b.z, w[7] = b.w;
     }
-    __device__ __forceinline__ void zero() { a = b = make_uint4(0u, 0u, 0u, 0u); }
-    __device__ __forceinline__ float get(int k) const
-    {
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        return (k & 1) ? bf16_hi(w[k >> 1]) : bf16_lo(w[k >> 1]);
-    }
+    __device__ __forceinline__ float get(int k) const { return (k & 1) ? bf16_hi(w[k >> 1]) : bf16_lo(w[k >> 1]); }
     __device__ __forceinline__ void absmax(uint32_t &, u16x2 &m2) const
     {
-        m2 = bf16_absmax2(m2, a.x);
-        m2 = bf16_absmax2(m2, a.y);
-        m2 = bf16_absmax2(m2, a.z);
-        m2 = bf16_absmax2(m2, a.w);
-        m2 = bf16_absmax2(m2, b.x);
-        m2 = bf16_absmax2(m2, b.y);
-        m2 = bf16_absmax2(m2, b.z);
-        m2 = bf16_absmax2(m2, b.w);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m2 = bf16_absmax2(m2, w[j]);
     }
 };
 template <> struct Chunk16<kF32> {
-    uint4 v[4]; // 16 floats
+    uint32_t w[16]; // 16 floats
     __device__ __forceinline__ void load(const void *x, int64_t c)
     {
         const uint4 *p = reinterpret_cast<const uint4 *>(x) + 4 * c;
-        v[0] = p[0];
-        v[1] = p[1];
-        v[2] = p[2];
-        v[3] = p[3];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 v = p[j];
+            w[4 * j] = v.x, w[4 * j + 1] = v.y, w[4 * j + 2] = v.z, w[4 * j + 3] = v.w;
+        }
     }
-    __device__ __forceinline__ void zero() { v[0] = v[1] = v[2] = v[3] = make_uint4(0u, 0u, 0u, 0u); }
-    __device__ __forceinline__ float get(int k) const
-    {
-        const uint4 &q = v[k >> 2];
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-        return __uint_as_float(w[k & 3]);
-    }
+    __device__ __forceinline__ float get(int k) const { return __uint_as_float(w[k]); }
     __device__ __forceinline__ void absmax(uint32_t &m, u16x2 &) const
     {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            m = max(m, v[j].x & 0x7FFFFFFFu);
-            m = max(m, v[j].y & 0x7FFFFFFFu);
-            m = max(m, v[j].z & 0x7FFFFFFFu);
-            m = max(m, v[j].w & 0x7FFFFFFFu);
-        }
+        for (int j = 0; j < 16; ++j) m = max(m, w[j] & 0x7FFFFFFFu);
     }
 };
 
@@ -249,23 +223,20 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const void *__restrict__
     u16x2 m2 = {0, 0};
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int64_t base = unit * kThreads * kCastU + threadIdx.x;
-        const bool full = (unit + 1) * kThreads * kCastU <= nch; // uniform: no per-load guards
+        // Lanes past the end re-read the last chunk (a valid address, so all
+        // loads are unconditional and stay in registers) and store nothing;
+        // re-reading an element does not change a max.
         Chunk16<DT> c[kCastU];
-        if (full) {
 #pragma unroll
-            for (int u = 0; u < kCastU; ++u) c[u].load(x, base + u * kThreads);
-        } else {
-#pragma unroll
-            for (int u = 0; u < kCastU; ++u) {
-                if (base + u * kThreads < nch) c[u].load(x, base + u * kThreads);
-                else c[u].zero();
-            }
+        for (int u = 0; u < kCastU; ++u) {
+            const int64_t ci = base + u * kThreads;
+            c[u].load(x, ci < nch ? ci : nch - 1);
         }
 #pragma unroll
         for (int u = 0; u < kCastU; ++u) {
             if constexpr (kAmax) c[u].absmax(m, m2);
             const uint4 o = encode_chunk<F, DT>(c[u], sc.scale);
-            if (full || base + u * kThreads < nch) qv[base + u * kThreads] = o;
+            if (base + u * kThreads < nch) qv[base + u * kThreads] = o;
         }
     }
     // tail: fewer than 16 elements, one per lane of block 0
@@ -341,21 +312,17 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__rest
     float4 *__restrict__ yv = reinterpret_cast<float4 *>(y);
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int64_t base = unit * kThreads * kDequantU + threadIdx.x;
-        const bool full = (unit + 1) * kThreads * kDequantU <= nw; // uniform: no per-load guards
         uint32_t w[kDequantU];
-        if (full) {
 #pragma unroll
-            for (int u = 0; u < kDequantU; ++u) w[u] = qw[base + u * kThreads];
-        } else {
-#pragma unroll
-            for (int u = 0; u < kDequantU; ++u) w[u] = base + u * kThreads < nw ? qw[base + u * kThreads] : 0u;
+        for (int u = 0; u < kDequantU; ++u) {
+            const int64_t i = base + u * kThreads;
+            w[u] = qw[i < nw ? i : nw - 1];
         }
 #pragma unroll
         for (int u = 0; u < kDequantU; ++u) {
             const float2 lo = dec2<F, false>(w[u]);
             const float2 hi = dec2<F, true>(w[u]);
-            if (full || base + u * kThreads < nw)
-                yv[base + u * kThreads] = make_float4(lo.x * s, lo.y * s, hi.x * s, hi.y * s);
+            if (base + u * kThreads < nw) yv[base + u * kThreads] = make_float4(lo.x * s, lo.y * s, hi.x * s, hi.y * s);
         }
     }
     if (blockIdx.x == 0 && threadIdx.x < n - (nw << 2)) {
@@ -379,27 +346,50 @@ hipError_t launch_dequant(const uint8_t *q, int fmt, int64_t n, const float *sca
 // Delayed-scaling update ("Megatron FP8", section 5): write the new amax at
 // slot step % L of column col, reduce the column (max, NaN-propagating) or take
 // the value just written, derive s = eff / FP8_MAX * 2^margin (1 when eff is
-// not > 0) and its reciprocal.  One block; L may be any length.
-__global__ __launch_bounds__(kThreads) void delayed_kernel(float *__restrict__ hist, int L, int n_cols, int col,
-                                                           const float *__restrict__ new_amax, int slot, float fmax,
-                                                           int margin, int algo, float *__restrict__ scale,
-                                                           float *__restrict__ scale_inv)
+// not > 0) and its reciprocal.  One block; L may be any length.  The new amax
+// is either read from memory or, for the fused step, reduced here from the
+// cast kernel's per-block partials (and published to amax_out).
+constexpr int kDelayedThreads = 1024;
+
+__global__ __launch_bounds__(kDelayedThreads) void delayed_kernel(float *__restrict__ hist, int L, int n_cols, int col,
+                                                                  const float *__restrict__ new_amax,
+                                                                  const GridScratch *__restrict__ gs, int nparts,
+                                                                  float *__restrict__ amax_out, int slot, float fmax,
+                                                                  int margin, int algo, float *__restrict__ scale,
+                                                                  float *__restrict__ scale_inv)
 {
-    __shared__ uint32_t red[kThreads / 64];
-    __shared__ uint32_t nan_red[kThreads / 64];
-    const float a = *new_amax;
+    __shared__ uint32_t red[kDelayedThreads / 64];
+    __shared__ uint32_t nan_red[kDelayedThreads / 64];
+    __shared__ uint32_t amax_red[kDelayedThreads / 64];
+    float a;
+    if (gs) {
+        uint32_t m = 0;
+        for (int i = threadIdx.x; i < nparts; i += 4 * kDelayedThreads) {
+            uint32_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                v[u] = i + u * kDelayedThreads < nparts ? gs->part[i + u * kDelayedThreads] : 0u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) m = max(m, v[u]);
+        }
+        m = block_max_u32<kDelayedThreads>(m, amax_red);
+        a = __uint_as_float(m);
+        if (threadIdx.x == 0 && amax_out) *amax_out = a;
+    } else {
+        a = *new_amax;
+    }
     // Largest value of the column, as an order-preserving key of the float
     // (negative values flip all bits, positive values set the sign bit).
     uint32_t key = 0;
     uint32_t saw_nan = 0;
-    for (int j = threadIdx.x; j < L; j += kThreads) {
+    for (int j = threadIdx.x; j < L; j += kDelayedThreads) {
         const float h = (j == slot) ? a : hist[(int64_t)j * n_cols + col];
         const uint32_t b = __float_as_uint(h);
         if (h != h) saw_nan = 1;
         else key = max(key, (b & 0x80000000u) ? ~b : (b | 0x80000000u));
     }
-    key = block_max_u32<kThreads>(key, red);
-    saw_nan = block_max_u32<kThreads>(saw_nan, nan_red);
+    key = block_max_u32<kDelayedThreads>(key, red);
+    saw_nan = block_max_u32<kDelayedThreads>(saw_nan, nan_red);
     if (threadIdx.x == 0) {
         hist[(int64_t)slot * n_cols + col] = a;
         float eff;
@@ -415,13 +405,44 @@ __global__ __launch_bounds__(kThreads) void delayed_kernel(float *__restrict__ h
     }
 }
 
+static float fmax_of(int fmt) { return fmt == kE4M3 ? Fmt<kE4M3>::kMax : Fmt<kE5M2>::kMax; }
+
 hipError_t launch_delayed(float *hist, int history_len, int n_cols, int col, const float *new_amax, int64_t step,
                           int fmt, int margin, int algo, float *scale, float *scale_inv, hipStream_t s)
 {
     const int slot = (int)(step % history_len);
-    const float fmax = fmt == kE4M3 ? Fmt<kE4M3>::kMax : Fmt<kE5M2>::kMax;
-    delayed_kernel<<<1, kThreads, 0, s>>>(hist, history_len, n_cols, col, new_amax, slot, fmax, margin, algo, scale,
-                                          scale_inv);
+    delayed_kernel<<<1, kDelayedThreads, 0, s>>>(hist, history_len, n_cols, col, new_amax, nullptr, 0, nullptr, slot,
+                                                 fmax_of(fmt), margin, algo, scale, scale_inv);
+    return hipGetLastError();
+}
+
+// One delayed-scaling step: cast x with the stored scale of column col
+// (scale_inv[col]), reducing the input's amax into per-block partials, then one
+// block folds the partials, publishes the amax and updates the ring and the
+// column's scales for the format of the next step.
+hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, float *hist, int history_len, int n_cols,
+                               int col, int64_t step, int fmt_next, int margin, int algo, float *scale,
+                               float *scale_inv, uint8_t *q, float *q_scale_inv_out, float *amax_out, GridScratch *gs,
+                               hipStream_t s)
+{
+    const ScaleSrc src{nullptr, scale_inv + col, 0};
+    const int grid = flat_grid(ceil_div(n >> 4, (int64_t)kThreads * kCastU));
+    if (fmt == kE4M3) {
+        if (dtype == kBF16)
+            cast_kernel<kE4M3, kBF16, true><<<grid, kThreads, 0, s>>>(x, n, src, q, q_scale_inv_out, nullptr, gs);
+        else
+            cast_kernel<kE4M3, kF32, true><<<grid, kThreads, 0, s>>>(x, n, src, q, q_scale_inv_out, nullptr, gs);
+    } else {
+        if (dtype == kBF16)
+            cast_kernel<kE5M2, kBF16, true><<<grid, kThreads, 0, s>>>(x, n, src, q, q_scale_inv_out, nullptr, gs);
+        else
+            cast_kernel<kE5M2, kF32, true><<<grid, kThreads, 0, s>>>(x, n, src, q, q_scale_inv_out, nullptr, gs);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int slot = (int)(step % history_len);
+    delayed_kernel<<<1, kDelayedThreads, 0, s>>>(hist, history_len, n_cols, col, nullptr, gs, grid, amax_out, slot,
+                                                 fmax_of(fmt_next), margin, algo, scale, scale_inv);
     return hipGetLastError();
 }
 

@@ -158,6 +158,29 @@ int fp8_update_scale_delayed(float *hist, int32_t history_len, int32_t n_cols, i
                              void *stream);
 
 /*
+ * fp8_quantize_delayed -- one delayed-scaling step ([MFP8] section 5: cast
+ * with the scale derived from the history, then record this input's amax and
+ * derive the scale for the next step).  Equivalent to
+ *   fp8_quantize_tensor(x, dtype, n, fmt, NULL, 0, &scale_inv[col], q,
+ *                       q_scale_inv_out, NULL, amax_out', stream)
+ *   fp8_update_scale_delayed(hist, history_len, n_cols, col, amax_out', step,
+ *                            fmt_next, margin, algo, scale, scale_inv, stream)
+ * with the amax handed from the cast to the update on the device (two kernel
+ * launches instead of three).
+ *   x, dtype, n, fmt   the tensor of this step and its FP8 format
+ *   hist, history_len, n_cols, col, step, margin, algo, scale, scale_inv
+ *                      the delayed-scaling state, as in fp8_update_scale_delayed
+ *   fmt_next           format whose FP8_MAX the new scale targets
+ *   q                  [n] codes
+ *   q_scale_inv_out    (nullable) receives the s this step was cast with
+ *   amax_out           (nullable) receives max |x|
+ */
+int fp8_quantize_delayed(const void *x, int32_t dtype, int64_t n, int32_t fmt, float *hist, int32_t history_len,
+                         int32_t n_cols, int32_t col, int64_t step, int32_t fmt_next, int32_t margin, int32_t algo,
+                         float *scale, float *scale_inv, uint8_t *q, float *q_scale_inv_out, float *amax_out,
+                         void *stream);
+
+/*
  * fp8_scaled_gemm -- C = (A * sA) (B * sB)^T on FP8 codes with fp32
  * accumulation ([MFP8] section 6: FP8 operands, fp32 accumulation, bf16
  * output; section 27: products promoted to fp32 and summed, one downcast of

@@ -104,6 +104,18 @@ def test_block_and_delayed_validation():
     _expect(up(BAD, 16, 1, 0, BAD + 0x100, 0, 0, 0, 0, BAD + 0x8, BAD + 0x300, S), fq.EINVAL, "overlap")
 
 
+def test_delayed_step_validation():
+    d = L.fp8_quantize_delayed
+    H, SC, SI, Q = BAD + 0x100, BAD + 0x200, BAD + 0x300, BAD + 0x10000
+    _expect(d(BAD, fq.BF16, 64, 0, H, 16, 1, 0, 0, 0, 0, 0, SC, SI, Q, None, None, S), fq.EINVAL, "overlap")
+    H = BAD + 0x40000
+    _expect(d(BAD, fq.BF16, 64, 3, H, 16, 1, 0, 0, 0, 0, 0, SC, SI, Q, None, None, S), fq.EINVAL, "format")
+    _expect(d(BAD, fq.BF16, 64, 0, H, 16, 1, 2, 0, 0, 0, 0, SC, SI, Q, None, None, S), fq.EINVAL, "col")
+    _expect(d(BAD, fq.BF16, 64, 0, H, 16, 1, 0, -1, 0, 0, 0, SC, SI, Q, None, None, S), fq.EINVAL, "step")
+    _expect(d(BAD, fq.BF16, 64, 0, H, 16, 1, 0, 0, 0, 0, 0, SC, SI, Q + 3, None, None, S), fq.EINVAL, "q must")
+    _expect(d(BAD, fq.BF16, 64, 0, H, 16, 1, 0, 0, 0, 0, 0, SC, SI, Q, SI, None, S), fq.EINVAL, "overlap")
+
+
 def test_gemm_validation():
     g = L.fp8_scaled_gemm
     A, B, C = BAD + 0x100000, BAD + 0x200000, BAD + 0x300000

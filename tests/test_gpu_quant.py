@@ -236,6 +236,35 @@ def test_delayed_32_steps_small(algo):
     _compare_delayed(got, _oracle_delayed(inputs, algo=algo))
 
 
+def _run_delayed_fused(inputs, L=16, algo=oracle.ALGO_MAX, margin=0):
+    """The same schedule through the fused one-call step."""
+    hist = torch.zeros((L, 1), dtype=torch.float32, device="cuda")
+    sc = torch.ones(1, dtype=torch.float32, device="cuda")
+    si = torch.ones(1, dtype=torch.float32, device="cuda")
+    out = []
+    for t, x in enumerate(inputs):
+        fmt = E4 if t % 2 == 0 else E5
+        fmt_next = E4 if (t + 1) % 2 == 0 else E5
+        q, qsi, am = empty_codes(x.size), scalar(-1.0), scalar(-1.0)
+        fq.fp8_quantize_delayed(to_dev(x), fmt, hist, 0, t, fmt_next, margin, algo, sc, si, q, qsi, am)
+        out.append(dict(q=host(q).reshape(x.shape), s=host(qsi)[0], amax=host(am)[0], hist=host(hist).copy(),
+                        scale=host(sc)[0], scale_inv=host(si)[0]))
+    return out
+
+
+@pytest.mark.parametrize("algo", [oracle.ALGO_MAX, oracle.ALGO_MOST_RECENT])
+def test_delayed_fused_step_32_steps(algo):
+    inputs = [workloads.delayed_step(t, 192, 336) for t in range(32)]
+    _compare_delayed(_run_delayed_fused(inputs, algo=algo), _oracle_delayed(inputs, algo=algo))
+
+
+def test_delayed_fused_step_ragged_and_nan():
+    rng = np.random.default_rng(4)
+    inputs = [workloads.to_bf16_bits(rng.standard_normal(n) * 3) for n in (1, 17, 1000003, 0, 33)]
+    inputs[2][77] = 0x7FC1  # a NaN element: amax NaN, then the ring holds NaN
+    _compare_delayed(_run_delayed_fused(inputs, L=4), _oracle_delayed(inputs, L=4))
+
+
 def test_delayed_resume_matches_straight_run():
     """32 steps straight == 16 steps, state copied to the host and back into
     fresh buffers, then 16 more steps."""
@@ -267,10 +296,13 @@ def test_delayed_nan_amax_and_long_history():
 
 def test_delayed_full_size_32_steps():
     """The full schedule: 32 steps of 8192x8192 bf16, ring of 16, alternating
-    E4M3FN / E5M2, one shared ring that wraps at step 16."""
+    E4M3FN / E5M2, one shared ring that wraps at step 16 -- through the two
+    calls and through the fused step the benchmark times."""
     inputs = workloads.parallel_map(workloads.delayed_step, range(32))
+    want = _oracle_delayed(inputs)
     got, _ = _run_delayed(inputs)
-    _compare_delayed(got, _oracle_delayed(inputs))
+    _compare_delayed(got, want)
+    _compare_delayed(_run_delayed_fused(inputs), want)
 
 
 # ---------------------------------------------------- rowwise + colwise ----
