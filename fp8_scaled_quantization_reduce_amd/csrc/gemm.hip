@@ -58,8 +58,11 @@ __device__ __forceinline__ v4f mfma16x16x128(const v8i &x, const v8i &y, const v
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, FX, FY, 0, 0, 0, 0);
 }
 
-// byte offset of 16-byte chunk c of row r in a [rows][128] LDS stage
-__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 4); }
+// Byte offset of 16-byte chunk c of row r in a [rows][128] LDS stage.  The LDS
+// serves 256 bytes (64 banks) per cycle, i.e. two 128-byte rows; XOR-ing the
+// chunk with bits 1..3 of the row gives the 16 rows read by 16 lanes of a
+// fragment 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ ((r >> 1) & 7)) << 4); }
 
 __device__ __forceinline__ void tile_of_block(int bid, int tilesM, int tilesN, int &tm, int &tn)
 {
@@ -80,9 +83,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Fill `rows` rows of a stage from a panel (buffer resource based at the
 // panel's first row): wave w loads rows 8 * (w + 4u) .. +7 for u = 0, 1, ...;
 // lane L writes LDS bytes 16L .. 16L+15 of the 1 KiB segment, i.e. physical
-// chunk L % 8 of row L / 8, which holds logical chunk (L % 8) ^ (L / 8).
-// Rows past the panel's last record read as zero; their results are never
-// stored.
+// chunk L % 8 of row 8 * (w + 4u) + L / 8, which must hold logical chunk
+// (L % 8) ^ ((row >> 1) & 7) = (L % 8) ^ ((4w + L / 16) & 7) -- the same for
+// every u, so one per-lane offset serves all loads of the wave.  Rows past
+// the panel's last record read as zero; their results are never stored.
 template <int kRows>
 __device__ __forceinline__ void stage_panel(__amdgpu_buffer_rsrc_t rsrc, int voff, int K, int k0, uint8_t *lds, int w)
 {
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint8_t *__
         __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * K), 0, (int)(a_rows * K), kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rb =
         __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0 * K), 0, (int)(b_rows * K), kRawBufferWord3);
-    const int voff = (lane >> 3) * K + (((lane & 7) ^ (lane >> 3)) << 4);
+    const int voff = (lane >> 3) * K + (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4);
     // (per-tensor mode: a one-record resource that is never read)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(kBlock ? sA + m0 * kblocks : sA), 0, kBlock ? (int)(a_rows * kblocks * 4) : 4, kRawBufferWord3);
@@ -215,6 +219,207 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint8_t *__
     }
 }
 
+// ---------------------------------------------------------------------------
+// Per-tensor kernel, pipelined.  Same 256x256 block tile and 2x2 waves of
+// 128x128, but K moves in steps of 64 bytes with v_mfma_f32_32x32x64_f8f6f4
+// (4x4 MFMA tiles of 32x32 per wave, 256 fp32 accumulators) through a ring of
+// four LDS stages of 32 KiB:
+//   - global -> LDS loads run three steps ahead of the MFMAs;
+//   - the fragments of step k+1 are read from LDS into the second register set
+//     while the MFMAs of step k run on the first;
+//   - one wave barrier per step (no memory fence: each lane waits for its own
+//     direct loads with vmcnt before the barrier).
+// LDS rows are 64 bytes (four 16-byte chunks); the chunk is XOR-ed with bits
+// 2..3 of the row so that the 16 rows read by 16 lanes hit 16 distinct bank
+// groups of the 64-bank LDS.
+constexpr int kPBK = 64;     // K bytes per pipelined step
+constexpr int kPStages = 4;  // LDS ring depth
+constexpr int kPStageBytes = 2 * kBM * kPBK;
+constexpr int kPLoads = 8;   // direct loads per lane per stage (4 for A, 4 for B)
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+template <int FX, int FY>
+__device__ __forceinline__ v16f mfma32x32x64(const v8i &x, const v8i &y, const v16f &c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, FX, FY, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ int pswz(int r, int c) { return r * kPBK + ((c ^ ((r >> 2) & 3)) << 4); }
+
+// 32 rows x 64 K bytes: lane (r = lane % 32, g = lane / 32) reads logical chunks 2g, 2g+1 of row r
+__device__ __forceinline__ v8i read_frag32(const uint8_t *lds, int r, int g)
+{
+    const uint4 lo = *reinterpret_cast<const uint4 *>(lds + pswz(r, 2 * g));
+    const uint4 hi = *reinterpret_cast<const uint4 *>(lds + pswz(r, 2 * g + 1));
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// The four ring stages are distinct LDS objects, addressed with compile-time
+// stage numbers (the step loop is unrolled by four), so the compiler can tell
+// a read of one stage from the direct loads still landing in another and does
+// not wait for those loads before reading.
+template <int FA, int FB, bool kAmax>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t *__restrict__ A,
+                                                                  const uint8_t *__restrict__ B,
+                                                                  const float *__restrict__ sA,
+                                                                  const float *__restrict__ sB, int M, int N, int K,
+                                                                  __bf16 *__restrict__ C, GridScratch *gs)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[kPStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[kPStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[kPStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[kPStageBytes];
+    __shared__ uint32_t red[kGemmThreads / 64];
+    uint8_t *const stages[4] = {st0, st1, st2, st3};
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, (M + kBM - 1) / kBM, (N + kBM - 1) / kBM, tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBM;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const int fr = lane & 31, fg = lane >> 5;
+    const int nk = K / kPBK;
+
+    const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBM, (int64_t)N - n0);
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * K), 0, (int)(a_rows * K), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0 * K), 0, (int)(b_rows * K), kRawBufferWord3);
+    // lane L of a 1 KiB load writes physical chunk L % 4 of row row0 + L / 4,
+    // which holds logical chunk (L % 4) ^ ((row >> 2) & 3) = (L % 4) ^ ((L >> 4) & 3)
+    const int voff = (lane >> 2) * K + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+
+    // wave w loads rows 64w .. 64w+63 of the A and B panels: 4 loads of 16 rows each
+    auto stage = [&](uint8_t *st, int kt) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = 64 * w + 16 * u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + row * kPBK), 16, voff,
+                                                     row * K + kt * kPBK, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = 64 * w + 16 * u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + kBM * kPBK + row * kPBK), 16, voff,
+                                                     row * K + kt * kPBK, 0, 0);
+        }
+    };
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    v8i fa0[4], fb0[4], fa1[4], fb1[4];
+    auto read_frags = [&](const uint8_t *st, v8i(&a)[4], v8i(&b)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = read_frag32(st + kBM * kPBK, wn * 128 + 32 * j + fr, fg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = read_frag32(st, wm * 128 + 32 * i + fr, fg);
+    };
+    auto mfmas = [&](const v8i(&a)[4], const v8i(&b)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x64<FB, FA>(b[j], a[i], acc[i][j]);
+    };
+    // A full step (stages k+1 .. k+3 all exist): stage k+1 must be visible,
+    // stage k+2 may still be landing.  Its 16 MFMAs are interleaved with the
+    // 16 fragment reads of step k+1 and the 8 direct loads of step k+3.
+    auto full_step = [&](int k, const uint8_t *next_st, uint8_t *load_st, const v8i(&ca)[4], const v8i(&cb)[4],
+                         v8i(&na)[4], v8i(&nb)[4]) {
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        read_frags(next_st, na, nb);
+        stage(load_st, k + 3);
+        mfmas(ca, cb);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global -> LDS load
+        }
+    };
+    // A step near the end of K, with the guards spelled out.
+    auto tail_step = [&](int k, const uint8_t *next_st, uint8_t *load_st, const v8i(&ca)[4], const v8i(&cb)[4],
+                         v8i(&na)[4], v8i(&nb)[4]) {
+        if (k >= nk) return;
+        if (k + 1 < nk) {
+            if (k + 2 < nk) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            read_frags(next_st, na, nb);
+            if (k + 3 < nk) stage(load_st, k + 3);
+        }
+        mfmas(ca, cb);
+    };
+
+    // prologue: three stages in flight, then step 0's fragments
+    if (nk > 0) stage(st0, 0);
+    if (nk > 1) stage(st1, 1);
+    if (nk > 2) stage(st2, 2);
+    if (nk > 0) {
+        if (nk >= 3) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (nk == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        read_frags(st0, fa0, fb0);
+    }
+    // steady state: four steps per iteration (stage k % 4 is static)
+    int kt = 0;
+    for (; kt + 7 <= nk; kt += 4) {
+        full_step(kt + 0, st1, st3, fa0, fb0, fa1, fb1);
+        full_step(kt + 1, st2, st0, fa1, fb1, fa0, fb0);
+        full_step(kt + 2, st3, st1, fa0, fb0, fa1, fb1);
+        full_step(kt + 3, st0, st2, fa1, fb1, fa0, fb0);
+    }
+    // at most six steps remain; kt % 4 == 0
+    tail_step(kt + 0, st1, st3, fa0, fb0, fa1, fb1);
+    tail_step(kt + 1, st2, st0, fa1, fb1, fa0, fb0);
+    tail_step(kt + 2, st3, st1, fa0, fb0, fa1, fb1);
+    tail_step(kt + 3, st0, st2, fa1, fb1, fa0, fb0);
+    tail_step(kt + 4, st1, st3, fa0, fb0, fa1, fb1);
+    tail_step(kt + 5, st2, st0, fa1, fb1, fa0, fb0);
+    (void)stages;
+
+    // epilogue: lane (fr, fg) of 32x32 tile (i, j) holds C[row][4 consecutive
+    // columns 8q + 4fg .. +3] for q = 0..3
+    const float alpha = (*sA) * (*sB);
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + wm * 128 + 32 * i + fr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t col = n0 + wn * 128 + 32 * j + 8 * q + 4 * fg;
+                const v4f v = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                  acc[i][j][4 * q + 3]} * alpha;
+                const bf16x4 h = __builtin_convertvector(v, bf16x4);
+                if (row < M && col < N) {
+                    *reinterpret_cast<bf16x4 *>(C + row * N + col) = h;
+                    if constexpr (kAmax) {
+                        const uint2 bits = __builtin_bit_cast(uint2, h);
+                        m = max(m, max((bits.x & 0x7FFFu) << 16, (bits.x >> 16 & 0x7FFFu) << 16));
+                        m = max(m, max((bits.y & 0x7FFFu) << 16, (bits.y >> 16 & 0x7FFFu) << 16));
+                    }
+                }
+            }
+        }
+    }
+    if constexpr (kAmax) {
+        m = block_max_u32<kGemmThreads>(m, red);
+        if (tid == 0) gs->part[blockIdx.x] = canonical_amax_bits(m);
+    }
+}
+
 int gemm_grid(int64_t M, int64_t N, int mode)
 {
     const int bn = block_n(mode != 0);
@@ -231,9 +436,9 @@ static hipError_t launch_gemm_t(const uint8_t *A, const float *sA, const uint8_t
     const int m = (int)M, n = (int)N, k = (int)K;
     if (mode == 0) {
         if (amax_out)
-            gemm_kernel<FA, FB, false, true><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
+            gemm_pt_kernel<FA, FB, true><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
         else
-            gemm_kernel<FA, FB, false, false><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
+            gemm_pt_kernel<FA, FB, false><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
     } else {
         if (amax_out)
             gemm_kernel<FA, FB, true, true><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
