@@ -282,6 +282,11 @@ int fp8_quantize_delayed(const void *x, int32_t dtype, int64_t n, int32_t fmt, f
         if (!x || !aligned(x, 16)) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
         if (!q || !aligned(q, 16)) return fail(FP8Q_EINVAL, "%s: q must be a 16-byte aligned pointer", fn);
         if (overlap(x, n * dsize(dtype), q, n)) return fail(FP8Q_EINVAL, "%s: q overlaps x", fn);
+        const void *state[5] = {hist, scale, scale_inv, q_scale_inv_out, amax_out};
+        const int64_t state_bytes[5] = {nh, 4 * n_cols, 4 * n_cols, 4, 4};
+        for (int i = 0; i < 5; ++i)
+            if (overlap(x, n * dsize(dtype), state[i], state_bytes[i]) || overlap(q, n, state[i], state_bytes[i]))
+                return fail(FP8Q_EINVAL, "%s: x or q overlaps the scaling state or a scalar output", fn);
     }
     fp8q::GridScratch *gs = nullptr;
     hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);

@@ -1,7 +1,7 @@
 // gemm.hip -- scaled FP8 GEMM on gfx950 matrix cores.
 //
 // C[M][N] = (A*sA)(B*sB)^T with A [M][K], B [N][K] FP8 codes (K-contiguous),
-// fp32 accumulation in v_mfma_f32_16x16x128_f8f6f4 and a bf16 output.
+// fp32 accumulation on the f8f6f4 matrix instructions and a bf16 output.
 //   per-tensor: C = bf16(fl32(fl32(sA*sB) * acc))   ("Megatron FP8", section 6:
 //               fp32 accumulation, bf16 output; section 27: products promoted
 //               to fp32 and summed, one downcast of the finished dot product)
@@ -11,22 +11,28 @@
 // and, optionally, the per-block magnitude max of the emitted bf16 values
 // (folded into amax_out by the finish kernel).
 //
-// Tiling.  Four waves (2x2) per block; a wave owns 128 rows x (16 * kJ)
-// columns of C as 8 x kJ MFMA tiles of 16x16 (kJ = 8 per tensor: 256 fp32
-// accumulators, which live in the accumulation registers; kJ = 4 in block
-// mode, whose per-slice promotion runs on the vector ALU).  K moves in steps
-// of 128 (one MFMA K, one block-scale slice).  Operand tiles (rows x 128
-// bytes) go from global memory straight into LDS with buffer loads
-// (buffer_load_dwordx4 ... lds: no register staging) into two stages; each
-// iteration waits for its stage, reads every fragment it needs into
-// registers, then issues the loads of the next step into the other stage and
-// runs its MFMAs while they fly.  Inside a stage the eight 16-byte chunks of
-// every 128-byte row are XOR-swizzled by the row index, so the fragment reads
-// of a wave spread over the LDS banks.
+// Two kernels, both with four waves (2x2) per block and operand tiles moved
+// from global memory straight into LDS by buffer loads (buffer_load_dwordx4
+// ... lds: no register staging), 16-byte chunks XOR-swizzled by row so that
+// fragment reads spread over the LDS banks:
+//
+//   gemm_pt_kernel (per-tensor): 256x256 tiles, a wave owns 128x128 of C as
+//   4x4 tiles of 32x32 (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales,
+//   256 accumulators).  K moves in steps of 64 through a ring of four LDS
+//   stages; the loop is unrolled by four so every stage index is static, and
+//   each step waits for its own stage only (the two younger stages stay in
+//   flight), reads the next step's fragments, issues the loads three steps
+//   ahead and runs its 16 MFMAs, interleaved with those reads and loads.
+//
+//   gemm_kernel (block-scaled): 256x128 tiles, a wave owns 128x64 as 8x4
+//   tiles of 16x16 (v_mfma_f32_16x16x128_f8f6f4); K moves in steps of 128
+//   (one block-scale slice) through two LDS stages, and the slice's partial
+//   is promoted on the vector ALU.
 //
 // Operand order.  The MFMA is issued as (B fragment, A fragment), so its
-// 16x16 result is C^T: lane (r = lane % 16, g = lane / 16) holds C[r][4g..4g+3],
-// four consecutive columns of one row, stored as one 8-byte bf16 quad.  A and B
+// result is C^T: in a 16x16 tile lane (r = lane % 16, g = lane / 16) holds
+// C[r][4g..4g+3], four consecutive columns of one row, stored as one 8-byte
+// bf16 quad (32x32 tiles likewise, per group of four accumulators).  A and B
 // fragments use the same lane -> K mapping, so the MFMA's internal K order does
 // not affect the dot product.
 //

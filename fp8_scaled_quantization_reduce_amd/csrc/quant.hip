@@ -60,21 +60,23 @@ __device__ __forceinline__ void block_partial(uint32_t m, GridScratch *gs)
 }
 
 // Fold nparts partials into the output word.  Each partial is canonical, so
-// their maximum is too.  1024 lanes with four independent loads each cover
-// the usual few thousand partials in one round trip.
+// their maximum is too.  1024 lanes with eight independent loads each cover
+// up to 8192 partials in one round trip.
 constexpr int kFinishThreads = 1024;
+constexpr int kFinishLoads = 8;
 
 __global__ __launch_bounds__(kFinishThreads) void finish_amax_kernel(const GridScratch *__restrict__ gs, int nparts,
                                                                      uint32_t *__restrict__ out)
 {
     __shared__ uint32_t red[kFinishThreads / 64];
     uint32_t m = 0;
-    for (int i = threadIdx.x; i < nparts; i += 4 * kFinishThreads) {
-        uint32_t v[4];
+    for (int i = threadIdx.x; i < nparts; i += kFinishLoads * kFinishThreads) {
+        uint32_t v[kFinishLoads];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = i + u * kFinishThreads < nparts ? gs->part[i + u * kFinishThreads] : 0u;
+        for (int u = 0; u < kFinishLoads; ++u)
+            v[u] = i + u * kFinishThreads < nparts ? gs->part[i + u * kFinishThreads] : 0u;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) m = max(m, v[u]);
+        for (int u = 0; u < kFinishLoads; ++u) m = max(m, v[u]);
     }
     m = block_max_u32<kFinishThreads>(m, red);
     if (threadIdx.x == 0) *out = m;
@@ -350,6 +352,17 @@ hipError_t launch_dequant(const uint8_t *q, int fmt, int64_t n, const float *sca
 // is either read from memory or, for the fused step, reduced here from the
 // cast kernel's per-block partials (and published to amax_out).
 constexpr int kDelayedThreads = 1024;
+constexpr int kDelayedLoads = 8; // partial loads in flight per lane
+
+// Order-preserving key of a float for an unsigned max (negative values flip
+// all bits, positive values set the sign bit); every NaN maps above +inf, so
+// a NaN anywhere in the column wins the max.
+__device__ __forceinline__ uint32_t order_key(float h)
+{
+    const uint32_t b = __float_as_uint(h);
+    if (h != h) return 0xFFFFFFFFu;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
 
 __global__ __launch_bounds__(kDelayedThreads) void delayed_kernel(float *__restrict__ hist, int L, int n_cols, int col,
                                                                   const float *__restrict__ new_amax,
@@ -358,47 +371,52 @@ __global__ __launch_bounds__(kDelayedThreads) void delayed_kernel(float *__restr
                                                                   int margin, int algo, float *__restrict__ scale,
                                                                   float *__restrict__ scale_inv)
 {
-    __shared__ uint32_t red[kDelayedThreads / 64];
-    __shared__ uint32_t nan_red[kDelayedThreads / 64];
-    __shared__ uint32_t amax_red[kDelayedThreads / 64];
-    float a;
+    __shared__ uint32_t red_a[kDelayedThreads / 64];
+    __shared__ uint32_t red_k[kDelayedThreads / 64];
+    const int tid = threadIdx.x;
+    // The lane's first history entry is loaded before the partials so that
+    // both round trips overlap.
+    const bool h0_valid = tid < L && tid != slot;
+    const float h0 = h0_valid ? hist[(int64_t)tid * n_cols + col] : 0.0f;
+    uint32_t m = 0;
     if (gs) {
-        uint32_t m = 0;
-        for (int i = threadIdx.x; i < nparts; i += 4 * kDelayedThreads) {
-            uint32_t v[4];
+        for (int i = tid; i < nparts; i += kDelayedLoads * kDelayedThreads) {
+            uint32_t v[kDelayedLoads];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < kDelayedLoads; ++u)
                 v[u] = i + u * kDelayedThreads < nparts ? gs->part[i + u * kDelayedThreads] : 0u;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) m = max(m, v[u]);
+            for (int u = 0; u < kDelayedLoads; ++u) m = max(m, v[u]);
         }
-        m = block_max_u32<kDelayedThreads>(m, amax_red);
-        a = __uint_as_float(m);
-        if (threadIdx.x == 0 && amax_out) *amax_out = a;
-    } else {
-        a = *new_amax;
     }
-    // Largest value of the column, as an order-preserving key of the float
-    // (negative values flip all bits, positive values set the sign bit).
-    uint32_t key = 0;
-    uint32_t saw_nan = 0;
-    for (int j = threadIdx.x; j < L; j += kDelayedThreads) {
-        const float h = (j == slot) ? a : hist[(int64_t)j * n_cols + col];
-        const uint32_t b = __float_as_uint(h);
-        if (h != h) saw_nan = 1;
-        else key = max(key, (b & 0x80000000u) ? ~b : (b | 0x80000000u));
+    // largest entry of the column other than the slot being overwritten
+    uint32_t key = h0_valid ? order_key(h0) : 0u;
+    for (int j = tid + kDelayedThreads; j < L; j += kDelayedThreads)
+        if (j != slot) key = max(key, order_key(hist[(int64_t)j * n_cols + col]));
+    // one exchange for both maxima
+    m = wave_max_u32(m);
+    key = wave_max_u32(key);
+    if ((tid & 63) == 0) {
+        red_a[tid >> 6] = m;
+        red_k[tid >> 6] = key;
     }
-    key = block_max_u32<kDelayedThreads>(key, red);
-    saw_nan = block_max_u32<kDelayedThreads>(saw_nan, nan_red);
-    if (threadIdx.x == 0) {
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+        for (int w = 1; w < kDelayedThreads / 64; ++w) {
+            m = max(m, red_a[w]);
+            key = max(key, red_k[w]);
+        }
+        const float a = gs ? __uint_as_float(m) : *new_amax;
+        if (gs && amax_out) *amax_out = a;
         hist[(int64_t)slot * n_cols + col] = a;
+        key = max(key, order_key(a));
         float eff;
-        if (algo == 0) {
-            const uint32_t b = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
-            eff = saw_nan ? __uint_as_float(kCanonicalNaN) : __uint_as_float(b);
-        } else {
+        if (algo == 0)
+            eff = key == 0xFFFFFFFFu ? __uint_as_float(kCanonicalNaN)
+                                     : __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+        else
             eff = a;
-        }
         const float s = (eff > 0.0f) ? ldexpf(eff / fmax, margin) : 1.0f;
         scale_inv[col] = s;
         scale[col] = 1.0f / s;

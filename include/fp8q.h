@@ -174,6 +174,8 @@ int fp8_update_scale_delayed(float *hist, int32_t history_len, int32_t n_cols, i
  *   q                  [n] codes
  *   q_scale_inv_out    (nullable) receives the s this step was cast with
  *   amax_out           (nullable) receives max |x|
+ * Errors: the checks of both calls above, plus FP8Q_EINVAL when x or q
+ * overlaps hist, scale, scale_inv or a scalar output.
  */
 int fp8_quantize_delayed(const void *x, int32_t dtype, int64_t n, int32_t fmt, float *hist, int32_t history_len,
                          int32_t n_cols, int32_t col, int64_t step, int32_t fmt_next, int32_t margin, int32_t algo,

@@ -106,8 +106,12 @@ def test_block_and_delayed_validation():
 
 def test_delayed_step_validation():
     d = L.fp8_quantize_delayed
-    H, SC, SI, Q = BAD + 0x100, BAD + 0x200, BAD + 0x300, BAD + 0x10000
+    H, SC, SI, Q = BAD + 0x40, BAD + 0x200, BAD + 0x300, BAD + 0x10000
+    # the history ring inside x (128 bytes of bf16), then inside q
     _expect(d(BAD, fq.BF16, 64, 0, H, 16, 1, 0, 0, 0, 0, 0, SC, SI, Q, None, None, S), fq.EINVAL, "overlap")
+    _expect(d(BAD, fq.BF16, 64, 0, Q + 16, 4, 1, 0, 0, 0, 0, 0, SC, SI, Q, None, None, S), fq.EINVAL, "overlap")
+    _expect(d(BAD, fq.BF16, 64, 0, BAD + 0x400, 16, 1, 0, 0, 0, 0, 0, BAD + 0x400, SI, Q, None, None, S),
+            fq.EINVAL, "overlap")
     H = BAD + 0x40000
     _expect(d(BAD, fq.BF16, 64, 3, H, 16, 1, 0, 0, 0, 0, 0, SC, SI, Q, None, None, S), fq.EINVAL, "format")
     _expect(d(BAD, fq.BF16, 64, 0, H, 16, 1, 2, 0, 0, 0, 0, SC, SI, Q, None, None, S), fq.EINVAL, "col")
