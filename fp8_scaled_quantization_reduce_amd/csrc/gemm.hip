@@ -11,7 +11,7 @@
 // and, optionally, the per-block magnitude max of the emitted bf16 values
 // (folded into amax_out by the finish kernel).
 //
-// Two kernels, both with four waves (2x2) per block and operand tiles moved
+// Two kernels, both with 256x256 block tiles and operand tiles moved
 // from global memory straight into LDS by buffer loads (buffer_load_dwordx4
 // ... lds: no register staging), 16-byte chunks XOR-swizzled by row so that
 // fragment reads spread over the LDS banks:
@@ -24,10 +24,10 @@
 //   flight), reads the next step's fragments, issues the loads three steps
 //   ahead and runs its 16 MFMAs, interleaved with those reads and loads.
 //
-//   gemm_kernel (block-scaled): 256x128 tiles, a wave owns 128x64 as 8x4
-//   tiles of 16x16 (v_mfma_f32_16x16x128_f8f6f4); K moves in steps of 128
-//   (one block-scale slice) through two LDS stages, and the slice's partial
-//   is promoted on the vector ALU.
+//   gemm_bs_kernel (block-scaled): 256x256 tiles and eight waves of 64x128,
+//   each as 4x8 tiles of 16x16 (v_mfma_f32_16x16x128_f8f6f4); K moves in
+//   steps of 128 (one block-scale slice) through two LDS stages, and each
+//   slice's partial is promoted on the vector ALU.
 //
 // Operand order.  The MFMA is issued as (B fragment, A fragment), so its
 // result is C^T: in a 16x16 tile lane (r = lane % 16, g = lane / 16) holds
@@ -53,8 +53,6 @@ constexpr int kBM = 256, kBK = 128;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4; // tile rows per L2 group
 constexpr uint32_t kRawBufferWord3 = 0x00020000u;
-
-__host__ __device__ constexpr int block_n(bool block_mode) { return block_mode ? 128 : 256; }
 
 template <int FX, int FY>
 __device__ __forceinline__ v4f mfma16x16x128(const v8i &x, const v8i &y, const v4f &c)
@@ -86,23 +84,6 @@ __device__ __forceinline__ void tile_of_block(int bid, int tilesM, int tilesN, i
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Fill `rows` rows of a stage from a panel (buffer resource based at the
-// panel's first row): wave w loads rows 8 * (w + 4u) .. +7 for u = 0, 1, ...;
-// lane L writes LDS bytes 16L .. 16L+15 of the 1 KiB segment, i.e. physical
-// chunk L % 8 of row 8 * (w + 4u) + L / 8, which must hold logical chunk
-// (L % 8) ^ ((row >> 1) & 7) = (L % 8) ^ ((4w + L / 16) & 7) -- the same for
-// every u, so one per-lane offset serves all loads of the wave.  Rows past
-// the panel's last record read as zero; their results are never stored.
-template <int kRows>
-__device__ __forceinline__ void stage_panel(__amdgpu_buffer_rsrc_t rsrc, int voff, int K, int k0, uint8_t *lds, int w)
-{
-#pragma unroll
-    for (int u = 0; u < kRows / 32; ++u) {
-        const int row = 8 * (w + 4 * u);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + row * kBK), 16, voff, k0 + row * K, 0, 0);
-    }
-}
-
 // One operand fragment (16 rows x 128 K bytes): lane (r, g) reads logical
 // chunks 2g and 2g+1 of row r.
 __device__ __forceinline__ v8i read_frag(const uint8_t *lds, int r, int g)
@@ -112,122 +93,9 @@ __device__ __forceinline__ v8i read_frag(const uint8_t *lds, int r, int g)
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <int FA, int FB, bool kBlock, bool kAmax>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(const uint8_t *__restrict__ A,
-                                                               const uint8_t *__restrict__ B,
-                                                               const float *__restrict__ sA,
-                                                               const float *__restrict__ sB, int M, int N, int K,
-                                                               __bf16 *__restrict__ C, GridScratch *gs)
-{
-    constexpr int kBN = block_n(kBlock);
-    constexpr int kJ = kBN / 32; // 16-column MFMA tiles per wave
-    constexpr int kAStage = kBM * kBK, kBStage = kBN * kBK;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * (kAStage + kBStage)];
-    __shared__ __attribute__((aligned(16))) float lds_sa[2][kBlock ? kBM : 1];
-    __shared__ uint32_t red[kGemmThreads / 64];
-
-    int tm, tn;
-    tile_of_block(blockIdx.x, (M + kBM - 1) / kBM, (N + kBN - 1) / kBN, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, kept in a scalar register
-    const int wm = w >> 1, wn = w & 1;
-    const int fr = lane & 15, fg = lane >> 4;
-    const int nk = K / kBK;
-    const int kblocks = K / 128;
-
-    // buffer resources over this block's row panels (rows past the matrix
-    // edge are outside the record range)
-    const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBN, (int64_t)N - n0);
-    const __amdgpu_buffer_rsrc_t ra =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * K), 0, (int)(a_rows * K), kRawBufferWord3);
-    const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0 * K), 0, (int)(b_rows * K), kRawBufferWord3);
-    const int voff = (lane >> 3) * K + (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4);
-    // (per-tensor mode: a one-record resource that is never read)
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(kBlock ? sA + m0 * kblocks : sA), 0, kBlock ? (int)(a_rows * kblocks * 4) : 4, kRawBufferWord3);
-
-    auto stage = [&](int s, int kt) {
-        uint8_t *la = lds + s * (kAStage + kBStage);
-        stage_panel<kBM>(ra, voff, K, kt * kBK, la, w);
-        stage_panel<kBN>(rb, voff, K, kt * kBK, la + kAStage, w);
-        if constexpr (kBlock)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)&lds_sa[s][64 * w], 4, lane * kblocks * 4,
-                                                     (64 * w * kblocks + kt) * 4, 0, 0);
-    };
-
-    v4f acc[8][kJ];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < kJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    if (nk > 0) stage(0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int s = kt & 1;
-        const uint8_t *la = lds + s * (kAStage + kBStage);
-        const uint8_t *lb = la + kAStage;
-        __syncthreads(); // waits for this stage's loads (all lanes) and for every wave's reads of the other stage
-        v8i a[8], b[kJ];
-#pragma unroll
-        for (int j = 0; j < kJ; ++j) b[j] = read_frag(lb, wn * (16 * kJ) + 16 * j + fr, fg);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = read_frag(la, wm * 128 + 16 * i + fr, fg);
-        float wi[8];
-        if constexpr (kBlock) {
-            const float sb = sB[((n0 + wn * 16 * kJ) / 128) * kblocks + kt];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) wi[i] = lds_sa[s][wm * 128 + 16 * i + fr] * sb;
-        }
-        if (kt + 1 < nk) stage(s ^ 1, kt + 1);
-        if constexpr (kBlock) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < kJ; ++j) {
-                    const v4f part = mfma16x16x128<FB, FA>(b[j], a[i], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(part[e], wi[i], acc[i][j][e]);
-                }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < kJ; ++j) acc[i][j] = mfma16x16x128<FB, FA>(b[j], a[i], acc[i][j]);
-        }
-    }
-
-    // epilogue: lane (fr, fg) of tile (i, j) holds C[row][4 consecutive cols]
-    const float alpha = kBlock ? 1.0f : (*sA) * (*sB);
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t row = m0 + wm * 128 + 16 * i + fr;
-#pragma unroll
-        for (int j = 0; j < kJ; ++j) {
-            const int64_t col = n0 + wn * (16 * kJ) + 16 * j + 4 * fg;
-            const v4f v = kBlock ? acc[i][j] : acc[i][j] * alpha;
-            const bf16x4 h = __builtin_convertvector(v, bf16x4);
-            if (row < M && col < N) {
-                *reinterpret_cast<bf16x4 *>(C + row * N + col) = h;
-                if constexpr (kAmax) {
-                    const uint2 bits = __builtin_bit_cast(uint2, h);
-                    m = max(m, max((bits.x & 0x7FFFu) << 16, (bits.x >> 16 & 0x7FFFu) << 16));
-                    m = max(m, max((bits.y & 0x7FFFu) << 16, (bits.y >> 16 & 0x7FFFu) << 16));
-                }
-            }
-        }
-    }
-    if constexpr (kAmax) {
-        m = block_max_u32<kGemmThreads>(m, red);
-        if (tid == 0) gs->part[blockIdx.x] = canonical_amax_bits(m);
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Per-tensor kernel, pipelined.  Same 256x256 block tile and 2x2 waves of
-// 128x128, but K moves in steps of 64 bytes with v_mfma_f32_32x32x64_f8f6f4
+// Per-tensor kernel, pipelined.  256x256 block tile and 2x2 waves of
+// 128x128; K moves in steps of 64 bytes with v_mfma_f32_32x32x64_f8f6f4
 // (4x4 MFMA tiles of 32x32 per wave, 256 fp32 accumulators) through a ring of
 // four LDS stages of 32 KiB:
 //   - global -> LDS loads run three steps ahead of the MFMAs;
@@ -426,10 +294,174 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Block-scaled kernel.  256x256 block tile, eight waves (4 x 2) of 64x128, each
+// as 4 x 8 tiles of 16x16.  One K step is one 128-wide scale slice and one
+// v_mfma_f32_16x16x128_f8f6f4 per tile, started from zero, so its result is
+// exactly that slice's partial product; it is promoted at once,
+//   acc = fma(part, fl32(sA[row][kb] * sB[col block][kb]), acc),
+// with the accumulators in ordinary vector registers (128 per lane; the
+// two-waves-per-SIMD budget is 256).  The slice's A rows and B rows (2 x 32
+// KiB) and the 256 row scales of A (1 KiB) go straight into LDS; two stages,
+// the next slice's loads in flight during this one's MFMAs.
+constexpr int kBSThreads = 512;
+constexpr int kBSStageBytes = 2 * kBM * kBK;
+
+template <int FA, int FB, bool kAmax>
+__global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *__restrict__ A,
+                                                                const uint8_t *__restrict__ B,
+                                                                const float *__restrict__ sA,
+                                                                const float *__restrict__ sB, int M, int N, int K,
+                                                                __bf16 *__restrict__ C, GridScratch *gs)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[kBSStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[kBSStageBytes];
+    __shared__ __attribute__((aligned(16))) float sa0[kBM];
+    __shared__ __attribute__((aligned(16))) float sa1[kBM];
+    __shared__ uint32_t red[kBSThreads / 64];
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, (M + kBM - 1) / kBM, (N + kBM - 1) / kBM, tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBM;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const int fr = lane & 15, fg = lane >> 4;
+    const int kblocks = K / kBK;
+
+    const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBM, (int64_t)N - n0);
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * K), 0, (int)(a_rows * K), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0 * K), 0, (int)(b_rows * K), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)(sA + m0 * kblocks), 0,
+                                                                        (int)(a_rows * kblocks * 4), kRawBufferWord3);
+    // lane L of a 1 KiB load writes physical chunk L % 8 of row 8(w + 8u) + L / 8,
+    // which holds logical chunk (L % 8) ^ ((row >> 1) & 7) = (L % 8) ^ ((4w + L / 16) & 7)
+    const int voff = (lane >> 3) * K + (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4);
+    // the wave's 128 columns lie in one 128-column scale block (clamped for the
+    // half tile past N, whose results are never stored)
+    const int nb = min((int)((n0 + wn * 128) / 128), N / 128 - 1);
+    const float *__restrict__ sbp = sB + (int64_t)nb * kblocks;
+
+    auto stage = [&](uint8_t *st, float *sa, int kb) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = 8 * (w + 8 * u);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + row * kBK), 16, voff, kb * kBK + row * K,
+                                                     0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = 8 * (w + 8 * u);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + kBM * kBK + row * kBK), 16, voff,
+                                                     kb * kBK + row * K, 0, 0);
+        }
+        if (w < 4)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(sa + 64 * w), 4, lane * kblocks * 4,
+                                                     (64 * w * kblocks + kb) * 4, 0, 0);
+    };
+
+    v4f acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // Column tile j's MFMAs run while tile j-1's partials are promoted and
+    // tile j+1's B fragment is read.  Empty asm statements pin that order (the
+    // compiler would otherwise issue all 32 MFMAs first and spill their 128
+    // partial registers): the one on the B fragment keeps tile j's MFMAs
+    // below it, the one on the promoted accumulators keeps tile j-1's FMAs
+    // above the next tile's.
+    auto compute = [&](const uint8_t *st, const float *sa, float sb) {
+        const uint8_t *lb = st + kBM * kBK;
+        v8i a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = read_frag(st, wm * 64 + 16 * i + fr, fg);
+        float wi[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wi[i] = sa[wm * 64 + 16 * i + fr] * sb;
+        v8i b = read_frag(lb, wn * 128 + fr, fg);
+        v4f prev[4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            asm volatile("" : "+v"(b));
+            v8i bn;
+            if (j + 1 < 8) bn = read_frag(lb, wn * 128 + 16 * (j + 1) + fr, fg);
+            v4f cur[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cur[i] = mfma16x16x128<FB, FA>(b, a[i], v4f{0.f, 0.f, 0.f, 0.f});
+            if (j > 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[i][j - 1][e] = __builtin_fmaf(prev[i][e], wi[i], acc[i][j - 1][e]);
+                asm volatile("" : "+v"(acc[0][j - 1]), "+v"(acc[1][j - 1]), "+v"(acc[2][j - 1]),
+                             "+v"(acc[3][j - 1]));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) prev[i] = cur[i];
+            if (j + 1 < 8) b = bn;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][7][e] = __builtin_fmaf(prev[i][e], wi[i], acc[i][7][e]);
+        asm volatile("" : "+v"(acc[0][7]), "+v"(acc[1][7]), "+v"(acc[2][7]), "+v"(acc[3][7]));
+    };
+
+    if (kblocks > 0) stage(st0, sa0, 0);
+    float sb_cur = kblocks > 0 ? sbp[0] : 0.0f;
+    for (int kb = 0; kb < kblocks; kb += 2) {
+        // slice kb in stage 0: wait for its loads (every lane), and for every
+        // wave to be done with stage 1 before refilling it
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (kb + 1 < kblocks) stage(st1, sa1, kb + 1);
+        float sb_next = kb + 1 < kblocks ? sbp[kb + 1] : 0.0f;
+        compute(st0, sa0, sb_cur);
+        sb_cur = sb_next;
+        if (kb + 1 >= kblocks) break;
+        // slice kb + 1 in stage 1
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (kb + 2 < kblocks) stage(st0, sa0, kb + 2);
+        sb_next = kb + 2 < kblocks ? sbp[kb + 2] : 0.0f;
+        compute(st1, sa1, sb_cur);
+        sb_cur = sb_next;
+    }
+
+    // epilogue: lane (fr, fg) of tile (i, j) holds C[row][4 consecutive cols]
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + wm * 64 + 16 * i + fr;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t col = n0 + wn * 128 + 16 * j + 4 * fg;
+            const bf16x4 h = __builtin_convertvector(acc[i][j], bf16x4);
+            if (row < M && col < N) {
+                *reinterpret_cast<bf16x4 *>(C + row * N + col) = h;
+                if constexpr (kAmax) {
+                    const uint2 bits = __builtin_bit_cast(uint2, h);
+                    m = max(m, max((bits.x & 0x7FFFu) << 16, (bits.x >> 16 & 0x7FFFu) << 16));
+                    m = max(m, max((bits.y & 0x7FFFu) << 16, (bits.y >> 16 & 0x7FFFu) << 16));
+                }
+            }
+        }
+    }
+    if constexpr (kAmax) {
+        m = block_max_u32<kBSThreads>(m, red);
+        if (tid == 0) gs->part[blockIdx.x] = canonical_amax_bits(m);
+    }
+}
+
 int gemm_grid(int64_t M, int64_t N, int mode)
 {
-    const int bn = block_n(mode != 0);
-    return (int)(((M + kBM - 1) / kBM) * ((N + bn - 1) / bn));
+    (void)mode;
+    return (int)(((M + kBM - 1) / kBM) * ((N + kBM - 1) / kBM));
 }
 
 template <int FA, int FB>
@@ -447,9 +479,9 @@ static hipError_t launch_gemm_t(const uint8_t *A, const float *sA, const uint8_t
             gemm_pt_kernel<FA, FB, false><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
     } else {
         if (amax_out)
-            gemm_kernel<FA, FB, true, true><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
+            gemm_bs_kernel<FA, FB, true><<<grid, kBSThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
         else
-            gemm_kernel<FA, FB, true, false><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
+            gemm_bs_kernel<FA, FB, false><<<grid, kBSThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !amax_out) return e;
