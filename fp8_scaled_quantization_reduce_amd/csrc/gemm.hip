@@ -94,22 +94,28 @@ __device__ __forceinline__ v8i read_frag(const uint8_t *lds, int r, int g)
 }
 
 // ---------------------------------------------------------------------------
-// Per-tensor kernel, pipelined.  256x256 block tile and 2x2 waves of
-// 128x128; K moves in steps of 64 bytes with v_mfma_f32_32x32x64_f8f6f4
-// (4x4 MFMA tiles of 32x32 per wave, 256 fp32 accumulators) through a ring of
-// four LDS stages of 32 KiB:
-//   - global -> LDS loads run three steps ahead of the MFMAs;
-//   - the fragments of step k+1 are read from LDS into the second register set
-//     while the MFMAs of step k run on the first;
-//   - one wave barrier per step (no memory fence: each lane waits for its own
-//     direct loads with vmcnt before the barrier).
-// LDS rows are 64 bytes (four 16-byte chunks); the chunk is XOR-ed with bits
-// 2..3 of the row so that the 16 rows read by 16 lanes hit 16 distinct bank
-// groups of the 64-bank LDS.
-constexpr int kPBK = 64;     // K bytes per pipelined step
-constexpr int kPStages = 4;  // LDS ring depth
-constexpr int kPStageBytes = 2 * kBM * kPBK;
-constexpr int kPLoads = 8;   // direct loads per lane per stage (4 for A, 4 for B)
+// Per-tensor kernel.  256x256 block tile, 2x2 waves of 128x128 as 4x4 tiles
+// of v_mfma_f32_32x32x64_f8f6f4 (256 fp32 accumulators per lane).  K moves in
+// slices of 128 through two LDS stages of 64 KiB; every direct load moves 8
+// rows x 128 bytes (whole 128-byte rows fetch about 1.6x faster from L2 than
+// 64-byte half rows).  A slice is two half steps of 64 K, each 16 MFMAs per
+// wave, and the one barrier per slice sits between them:
+//   half 0: MFMAs on the slice's first-half fragments while the second-half
+//           fragments are read from LDS;
+//   sync:   wait for this lane's loads of the next slice and the LDS reads,
+//           then barrier: the next slice is in LDS and nobody reads this
+//           slice's stage any more;
+//   half 1: the loads of the slice after next go into this stage, while the
+//           MFMAs run on the second-half fragments and the next slice's
+//           first-half fragments are read.
+// So LDS reads always overlap MFMAs, and the loads have a whole slice of
+// MFMAs to land.
+constexpr int kPTStageBytes = 2 * kBM * kBK;
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8).  Issued through the builtin rather than inline asm so
+// that the compiler's own wait insertion knows what has been waited for.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | (7 << 4) | ((lgkm & 0xF) << 8) | ((vm >> 4) << 14); }
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -119,20 +125,18 @@ __device__ __forceinline__ v16f mfma32x32x64(const v8i &x, const v8i &y, const v
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, FX, FY, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ int pswz(int r, int c) { return r * kPBK + ((c ^ ((r >> 2) & 3)) << 4); }
-
-// 32 rows x 64 K bytes: lane (r = lane % 32, g = lane / 32) reads logical chunks 2g, 2g+1 of row r
-__device__ __forceinline__ v8i read_frag32(const uint8_t *lds, int r, int g)
+// 32 rows x 64 K bytes of half step h: lane (r = lane % 32, g = lane / 32)
+// reads logical chunks 4h + 2g and 4h + 2g + 1 of row r (same swizzle as above)
+__device__ __forceinline__ v8i read_frag32(const uint8_t *lds, int r, int g, int h)
 {
-    const uint4 lo = *reinterpret_cast<const uint4 *>(lds + pswz(r, 2 * g));
-    const uint4 hi = *reinterpret_cast<const uint4 *>(lds + pswz(r, 2 * g + 1));
+    const uint4 lo = *reinterpret_cast<const uint4 *>(lds + swz(r, 4 * h + 2 * g));
+    const uint4 hi = *reinterpret_cast<const uint4 *>(lds + swz(r, 4 * h + 2 * g + 1));
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// The four ring stages are distinct LDS objects, addressed with compile-time
-// stage numbers (the step loop is unrolled by four), so the compiler can tell
-// a read of one stage from the direct loads still landing in another and does
-// not wait for those loads before reading.
+// The two stages are distinct LDS objects addressed with compile-time stage
+// numbers (the slice loop is unrolled by two), so the compiler can tell a
+// read of one stage from the direct loads landing in the other.
 template <int FA, int FB, bool kAmax>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t *__restrict__ A,
                                                                   const uint8_t *__restrict__ B,
@@ -140,12 +144,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
                                                                   const float *__restrict__ sB, int M, int N, int K,
                                                                   __bf16 *__restrict__ C, GridScratch *gs)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[kPStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[kPStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t st2[kPStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t st3[kPStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[kPTStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[kPTStageBytes];
     __shared__ uint32_t red[kGemmThreads / 64];
-    uint8_t *const stages[4] = {st0, st1, st2, st3};
 
     int tm, tn;
     tile_of_block(blockIdx.x, (M + kBM - 1) / kBM, (N + kBM - 1) / kBM, tm, tn);
@@ -154,30 +155,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w >> 1, wn = w & 1;
     const int fr = lane & 31, fg = lane >> 5;
-    const int nk = K / kPBK;
+    const int nk = K / kBK;
 
     const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBM, (int64_t)N - n0);
     const __amdgpu_buffer_rsrc_t ra =
         __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * K), 0, (int)(a_rows * K), kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rb =
         __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0 * K), 0, (int)(b_rows * K), kRawBufferWord3);
-    // lane L of a 1 KiB load writes physical chunk L % 4 of row row0 + L / 4,
-    // which holds logical chunk (L % 4) ^ ((row >> 2) & 3) = (L % 4) ^ ((L >> 4) & 3)
-    const int voff = (lane >> 2) * K + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+    // lane L of a 1 KiB load writes physical chunk L % 8 of row 8(w + 4u) + L / 8,
+    // which holds logical chunk (L % 8) ^ ((row >> 1) & 7) = (L % 8) ^ ((4w + L / 16) & 7)
+    const int voff = (lane >> 3) * K + (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4);
 
-    // wave w loads rows 64w .. 64w+63 of the A and B panels: 4 loads of 16 rows each
-    auto stage = [&](uint8_t *st, int kt) {
+    // wave w loads rows 8(w + 4u), u = 0..7, of both panels: 16 loads of 1 KiB
+    auto stage = [&](uint8_t *st, int kb) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int row = 64 * w + 16 * u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + row * kPBK), 16, voff,
-                                                     row * K + kt * kPBK, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int row = 64 * w + 16 * u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + kBM * kPBK + row * kPBK), 16, voff,
-                                                     row * K + kt * kPBK, 0, 0);
+        for (int u = 0; u < 8; ++u) {
+            const int row = 8 * (w + 4 * u);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + row * kBK), 16, voff, row * K + kb * kBK,
+                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + kBM * kBK + row * kBK), 16, voff,
+                                                     row * K + kb * kBK, 0, 0);
         }
     };
 
@@ -189,12 +186,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    v8i fa0[4], fb0[4], fa1[4], fb1[4];
-    auto read_frags = [&](const uint8_t *st, v8i(&a)[4], v8i(&b)[4]) {
+    v8i fa0[4], fb0[4], fa1[4], fb1[4]; // first-half and second-half fragments
+    auto read_frags = [&](const uint8_t *st, int h, v8i(&a)[4], v8i(&b)[4]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = read_frag32(st + kBM * kPBK, wn * 128 + 32 * j + fr, fg);
+        for (int j = 0; j < 4; ++j) b[j] = read_frag32(st + kBM * kBK, wn * 128 + 32 * j + fr, fg, h);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = read_frag32(st, wm * 128 + 32 * i + fr, fg);
+        for (int i = 0; i < 4; ++i) a[i] = read_frag32(st, wm * 128 + 32 * i + fr, fg, h);
     };
     auto mfmas = [&](const v8i(&a)[4], const v8i(&b)[4]) {
 #pragma unroll
@@ -202,65 +199,61 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x64<FB, FA>(b[j], a[i], acc[i][j]);
     };
-    // A full step (stages k+1 .. k+3 all exist): stage k+1 must be visible,
-    // stage k+2 may still be landing.  Its 16 MFMAs are interleaved with the
-    // 16 fragment reads of step k+1 and the 8 direct loads of step k+3.
-    auto full_step = [&](int k, const uint8_t *next_st, uint8_t *load_st, const v8i(&ca)[4], const v8i(&cb)[4],
-                         v8i(&na)[4], v8i(&nb)[4]) {
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        read_frags(next_st, na, nb);
-        stage(load_st, k + 3);
-        mfmas(ca, cb);
+
+    // One slice in stage `cur` (the next one in `nxt`).  `full` = the slices
+    // kb + 1 and kb + 2 both exist (no guards).
+    auto slice = [&](int kb, const uint8_t *cur, uint8_t *nxt_load, const uint8_t *nxt, bool full) {
+        // half 0
+        mfmas(fa0, fb0);
+        read_frags(cur, 1, fa1, fb1);
+        if (full) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global -> LDS load
+            for (int t = 0; t < 16; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // LDS read
+            }
         }
-    };
-    // A step near the end of K, with the guards spelled out.
-    auto tail_step = [&](int k, const uint8_t *next_st, uint8_t *load_st, const v8i(&ca)[4], const v8i(&cb)[4],
-                         v8i(&na)[4], v8i(&nb)[4]) {
-        if (k >= nk) return;
-        if (k + 1 < nk) {
-            if (k + 2 < nk) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            read_frags(next_st, na, nb);
-            if (k + 3 < nk) stage(load_st, k + 3);
+        // sync: the next slice landed (this lane's loads, then every wave's)
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // half 1
+        if (full || kb + 2 < nk) stage(const_cast<uint8_t *>(cur), kb + 2);
+        mfmas(fa1, fb1);
+        if (full || kb + 1 < nk) read_frags(nxt, 0, fa0, fb0);
+        if (full) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global -> LDS load
+            }
         }
-        mfmas(ca, cb);
+        (void)nxt_load;
     };
 
-    // prologue: three stages in flight, then step 0's fragments
-    if (nk > 0) stage(st0, 0);
-    if (nk > 1) stage(st1, 1);
-    if (nk > 2) stage(st2, 2);
+    // prologue: slices 0 and 1 in flight, slice 0's first-half fragments.
+    // Both stages are always filled (for K = 128 the second load reads bytes
+    // of the panel that are never used; rows past the record read zero): with
+    // an unconditional pair the compiler's wait insertion keeps the two stages
+    // apart and puts no full wait at the top of the loop.
     if (nk > 0) {
-        if (nk >= 3) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else if (nk == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        stage(st0, 0);
+        stage(st1, 1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(16, 15));
         __builtin_amdgcn_s_barrier();
-        read_frags(st0, fa0, fb0);
+        asm volatile("" ::: "memory");
+        read_frags(st0, 0, fa0, fb0);
     }
-    // steady state: four steps per iteration (stage k % 4 is static)
-    int kt = 0;
-    for (; kt + 7 <= nk; kt += 4) {
-        full_step(kt + 0, st1, st3, fa0, fb0, fa1, fb1);
-        full_step(kt + 1, st2, st0, fa1, fb1, fa0, fb0);
-        full_step(kt + 2, st3, st1, fa0, fb0, fa1, fb1);
-        full_step(kt + 3, st0, st2, fa1, fb1, fa0, fb0);
+    int kb = 0;
+    for (; kb + 4 <= nk; kb += 2) {
+        slice(kb, st0, st0, st1, true);
+        slice(kb + 1, st1, st1, st0, true);
     }
-    // at most six steps remain; kt % 4 == 0
-    tail_step(kt + 0, st1, st3, fa0, fb0, fa1, fb1);
-    tail_step(kt + 1, st2, st0, fa1, fb1, fa0, fb0);
-    tail_step(kt + 2, st3, st1, fa0, fb0, fa1, fb1);
-    tail_step(kt + 3, st0, st2, fa1, fb1, fa0, fb0);
-    tail_step(kt + 4, st1, st3, fa0, fb0, fa1, fb1);
-    tail_step(kt + 5, st2, st0, fa1, fb1, fa0, fb0);
-    (void)stages;
+    // at most three slices remain; kb is even
+    if (kb < nk) slice(kb, st0, st0, st1, false);
+    if (kb + 1 < nk) slice(kb + 1, st1, st1, st0, false);
+    if (kb + 2 < nk) slice(kb + 2, st0, st0, st1, false);
 
     // epilogue: lane (fr, fg) of 32x32 tile (i, j) holds C[row][4 consecutive
     // columns 8q + 4fg .. +3] for q = 0..3
@@ -368,30 +361,38 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Column tile j's MFMAs run while tile j-1's partials are promoted and
-    // tile j+1's B fragment is read.  Empty asm statements pin that order (the
-    // compiler would otherwise issue all 32 MFMAs first and spill their 128
-    // partial registers): the one on the B fragment keeps tile j's MFMAs
-    // below it, the one on the promoted accumulators keeps tile j-1's FMAs
-    // above the next tile's.
-    auto compute = [&](const uint8_t *st, const float *sa, float sb) {
-        const uint8_t *lb = st + kBM * kBK;
-        v8i a[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = read_frag(st, wm * 64 + 16 * i + fr, fg);
-        float wi[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wi[i] = sa[wm * 64 + 16 * i + fr] * sb;
-        v8i b = read_frag(lb, wn * 128 + fr, fg);
+    // One slice (stage `cur`, its row scales in `sac`; the next slice already
+    // in flight to `nxt` / `san`).  Column tile j's MFMAs run while tile
+    // j-1's partials are promoted and tile j+1's B fragment is read.  Once
+    // the last fragment of `cur` is in registers (before tile 7), every lane
+    // waits for its own loads of the next slice and the block meets at the
+    // one barrier of the slice; then the slice after next is loaded into
+    // `cur`, and tile 7's MFMAs overlap the reads of the next slice's A
+    // fragments, first B fragment and row scales.  Empty asm statements pin
+    // this order (the compiler would otherwise issue all 32 MFMAs first and
+    // spill their 128 partial registers): the one on the B fragment keeps
+    // tile j's MFMAs below it, the one on the promoted accumulators keeps
+    // tile j-1's FMAs above the next tile's.
+    v8i a[4], b;
+    float wi[4];
+    float sb_next = 0.0f;
+    auto slice = [&](int kb, uint8_t *cur, float *sac, const uint8_t *nxt, const float *san, bool full) {
+        const uint8_t *lb = cur + kBM * kBK;
         v4f prev[4];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             asm volatile("" : "+v"(b));
             v8i bn;
             if (j + 1 < 8) bn = read_frag(lb, wn * 128 + 16 * (j + 1) + fr, fg);
-            v4f cur[4];
+            if (j == 7) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                if (full || kb + 2 < kblocks) stage(cur, sac, kb + 2);
+            }
+            v4f cur_p[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) cur[i] = mfma16x16x128<FB, FA>(b, a[i], v4f{0.f, 0.f, 0.f, 0.f});
+            for (int i = 0; i < 4; ++i) cur_p[i] = mfma16x16x128<FB, FA>(b, a[i], v4f{0.f, 0.f, 0.f, 0.f});
             if (j > 0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -402,36 +403,53 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
                              "+v"(acc[3][j - 1]));
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) prev[i] = cur[i];
+            for (int i = 0; i < 4; ++i) prev[i] = cur_p[i];
             if (j + 1 < 8) b = bn;
         }
+        // tile 7's promotion with this slice's weights, then the next slice's
+        // fragments and weights
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[i][7][e] = __builtin_fmaf(prev[i][e], wi[i], acc[i][7][e]);
         asm volatile("" : "+v"(acc[0][7]), "+v"(acc[1][7]), "+v"(acc[2][7]), "+v"(acc[3][7]));
+        if (full || kb + 1 < kblocks) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = read_frag(nxt, wm * 64 + 16 * i + fr, fg);
+            b = read_frag(nxt + kBM * kBK, wn * 128 + fr, fg);
+            const float sb = sb_next;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wi[i] = san[wm * 64 + 16 * i + fr] * sb;
+            sb_next = (full || kb + 2 < kblocks) ? sbp[kb + 2] : 0.0f;
+        }
     };
 
-    if (kblocks > 0) stage(st0, sa0, 0);
-    float sb_cur = kblocks > 0 ? sbp[0] : 0.0f;
-    for (int kb = 0; kb < kblocks; kb += 2) {
-        // slice kb in stage 0: wait for its loads (every lane), and for every
-        // wave to be done with stage 1 before refilling it
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (kb + 1 < kblocks) stage(st1, sa1, kb + 1);
-        float sb_next = kb + 1 < kblocks ? sbp[kb + 1] : 0.0f;
-        compute(st0, sa0, sb_cur);
-        sb_cur = sb_next;
-        if (kb + 1 >= kblocks) break;
-        // slice kb + 1 in stage 1
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (kb + 2 < kblocks) stage(st0, sa0, kb + 2);
-        sb_next = kb + 2 < kblocks ? sbp[kb + 2] : 0.0f;
-        compute(st1, sa1, sb_cur);
-        sb_cur = sb_next;
+    // prologue: slices 0 and 1 in flight (both stages always filled, see the
+    // per-tensor kernel), slice 0's fragments and weights
+    if (kblocks > 0) {
+        stage(st0, sa0, 0);
+        stage(st1, sa1, 1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = read_frag(st0, wm * 64 + 16 * i + fr, fg);
+        b = read_frag(st0 + kBM * kBK, wn * 128 + fr, fg);
+        const float sb = sbp[0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wi[i] = sa0[wm * 64 + 16 * i + fr] * sb;
+        sb_next = kblocks > 1 ? sbp[1] : 0.0f;
     }
+    // steady state: slices kb + 2 and kb + 3 exist (no guards)
+    int kb = 0;
+    for (; kb + 4 <= kblocks; kb += 2) {
+        slice(kb, st0, sa0, st1, sa1, true);
+        slice(kb + 1, st1, sa1, st0, sa0, true);
+    }
+    // at most three slices remain; kb is even
+    if (kb < kblocks) slice(kb, st0, sa0, st1, sa1, false);
+    if (kb + 1 < kblocks) slice(kb + 1, st1, sa1, st0, sa0, false);
+    if (kb + 2 < kblocks) slice(kb + 2, st0, sa0, st1, sa1, false);
 
     // epilogue: lane (fr, fg) of tile (i, j) holds C[row][4 consecutive cols]
     uint32_t m = 0;

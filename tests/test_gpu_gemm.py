@@ -105,7 +105,7 @@ def _block_operands(rng, M, N, K, fa, fb, a_std=1.0, b_std=0.02):
 
 
 @pytest.mark.parametrize("fa,fb", [(E4, E4), (E5, E4)])
-@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (256, 384, 512), (384, 256, 1280)])
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (128, 384, 256), (256, 384, 512), (256, 256, 640), (384, 256, 1280)])
 def test_gemm_block_parity(fa, fb, M, N, K):
     rng = np.random.default_rng(M + 2 * N + 3 * K + fa)
     qa, sa, qb, sb = _block_operands(rng, M, N, K, fa, fb)
