@@ -494,38 +494,29 @@ __device__ __forceinline__ void transpose4x4(const uint32_t d0, const uint32_t d
     e[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
 }
 
-// dword address in the transposed LDS tile of (tile column j, row dword d)
-__device__ __forceinline__ int tlds_addr(int j, int d) { return j * 32 + ((d + 8 * (j >> 4)) & 31); }
+// dword address in the transposed LDS tile of (tile column j, row dword d).
+// A column is 32 dwords, so two columns fill the 64 banks.  The rotation by 8
+// dwords per 16 columns spreads the 8 lanes jg = 0..7 of one staging write
+// over 32 banks; swapping the two columns of a pair when bit 6 of j is set
+// puts lanes jg >= 4 on the other 32, so the 64 lanes of a write hit 64
+// distinct banks.  Every 16-byte read stays contiguous.
+__device__ __forceinline__ int tlds_addr(int j, int d)
+{
+    return (j ^ ((j >> 6) & 1)) * 32 + ((d + 8 * (j >> 4)) & 31);
+}
 
-// A lane's 4 rows x 16 columns of input as floats.
-template <int DT> struct Patch {
-    float v[4][16];
+// A lane's 4 rows x 16 columns of input as raw 16-byte vectors.
+template <int DT> struct RawPatch {
+    static constexpr int kVec = DT == kBF16 ? 2 : 4; // 16-byte vectors per row
+    uint4 w[4][kVec];
     __device__ __forceinline__ void load(const void *x, int64_t ld, int64_t r0, int64_t c0)
     {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            if constexpr (DT == kBF16) {
-                const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) +
-                                                                 (r0 + r) * ld + c0);
-                const uint4 a = p[0], b = p[1];
-                const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(x) +
+                                                             ((r0 + r) * ld + c0) * (DT == kBF16 ? 2 : 4));
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    v[r][2 * k] = bf16_lo(w[k]);
-                    v[r][2 * k + 1] = bf16_hi(w[k]);
-                }
-            } else {
-                const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) +
-                                                                   (r0 + r) * ld + c0);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float4 f = p[k];
-                    v[r][4 * k] = f.x;
-                    v[r][4 * k + 1] = f.y;
-                    v[r][4 * k + 2] = f.z;
-                    v[r][4 * k + 3] = f.w;
-                }
-            }
+            for (int k = 0; k < kVec; ++k) w[r][k] = p[k];
         }
     }
     __device__ __forceinline__ void zero()
@@ -533,9 +524,41 @@ template <int DT> struct Patch {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int k = 0; k < 16; ++k) v[r][k] = 0.0f;
+            for (int k = 0; k < kVec; ++k) w[r][k] = make_uint4(0, 0, 0, 0);
     }
 };
+
+// Hide a raw patch's words from the optimiser, so that floats derived from
+// it before this point are recomputed after it instead of being kept live.
+template <int DT> __device__ __forceinline__ void opaque(RawPatch<DT> &p)
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int k = 0; k < RawPatch<DT>::kVec; ++k) {
+            uint32_t a = p.w[r][k].x, b = p.w[r][k].y, c = p.w[r][k].z, d = p.w[r][k].w;
+            asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+            p.w[r][k] = make_uint4(a, b, c, d);
+        }
+}
+
+// Element (r, k) of a raw patch as a float (k is a compile-time constant in
+// every use, so this is one shift or mask for bf16 and nothing for fp32; the
+// floats are recomputed where needed rather than kept across the barriers).
+template <int DT>
+__device__ __forceinline__ float patch_elem(const RawPatch<DT> &p, int r, int k)
+{
+    if constexpr (DT == kBF16) {
+        const uint4 a = p.w[r][k >> 3];
+        const int e = (k & 7) >> 1;
+        const uint32_t w = e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
+        return (k & 1) ? bf16_hi(w) : bf16_lo(w);
+    } else {
+        const uint4 a = p.w[r][k >> 2];
+        const int e = k & 3;
+        return __uint_as_float(e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w);
+    }
+}
 
 // Store the lane's 4x16 codes (cw[r][0..3] = row r, 16 codes) transposed into LDS.
 __device__ __forceinline__ void stage_transposed(uint32_t *tl, const uint32_t cw[4][4], int ig, int jg)
@@ -576,7 +599,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
 {
     __shared__ uint32_t tl[kTile * 32]; // transposed codes, 16 KiB
     __shared__ uint32_t red[kThreads / 64];
-    __shared__ uint32_t colmax[kMode == kTileBlock1x128 ? 32 * kTile : 1];
+    __shared__ uint32_t colmax[kMode == kTileBlock1x128 ? 4 * kTile : 1]; // per wave, per tile column
     __shared__ float colscale[kMode == kTileBlock1x128 ? kTile : 1];
 
     const int ig = threadIdx.x >> 3, jg = threadIdx.x & 7;
@@ -593,15 +616,23 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
     }
     uint32_t m_all = 0; // per-tensor fused amax
 
+    // The lane's patch of tile t (rows % 4 == 0 and cols % 16 == 0, so a patch
+    // is either whole or entirely outside the matrix).
+    auto load_patch = [&](int64_t t, RawPatch<DT> &raw) {
+        const int64_t tr = t / tiles_c, tc = t - tr * tiles_c;
+        const int64_t r0 = tr * kTile + 4 * ig, c0 = tc * kTile + 16 * jg;
+        if (r0 < rows && c0 < cols) raw.load(x, cols, r0, c0);
+        else raw.zero();
+    };
     for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
         const int64_t tr = t / tiles_c, tc = t - tr * tiles_c;
         const int64_t row0 = tr * kTile, col0 = tc * kTile;
         const int64_t r0 = row0 + 4 * ig, c0 = col0 + 16 * jg;
-        const bool valid = (r0 < rows) && (c0 < cols); // rows % 4 == 0, cols % 16 == 0
+        const bool valid = (r0 < rows) && (c0 < cols);
 
-        Patch<DT> p;
-        if (valid) p.load(x, cols, r0, c0);
-        else p.zero();
+        RawPatch<DT> p;
+        load_patch(t, p);
+#define PV(r, k) patch_elem<DT>(p, (r), (k))
 
         uint32_t cw[4][4]; // rowwise codes
 
@@ -610,21 +641,22 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int k = 0; k < 16; ++k) m_all = max(m_all, f32_absbits(p.v[r][k]));
+                    for (int k = 0; k < 16; ++k) m_all = max(m_all, f32_absbits(PV(r, k)));
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
-                    cw[r][q4] = encode4<F>(p.v[r][4 * q4], p.v[r][4 * q4 + 1], p.v[r][4 * q4 + 2],
-                                           p.v[r][4 * q4 + 3], sc_tensor.scale);
+                    cw[r][q4] = encode4<F>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
+                                           PV(r, 4 * q4 + 3), sc_tensor.scale);
         } else if constexpr (kMode == kTileBlock128) {
             uint32_t m = 0;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(p.v[r][k]));
+                for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(PV(r, k)));
             m = block_max_u32<kThreads>(m, red);
+            opaque(p);
             const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
             if (threadIdx.x == 0) {
                 s_row[tr * bcols + tc] = sc.s;
@@ -634,15 +666,15 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
-                    cw[r][q4] = encode4<F>(p.v[r][4 * q4], p.v[r][4 * q4 + 1], p.v[r][4 * q4 + 2],
-                                           p.v[r][4 * q4 + 3], sc.scale);
+                    cw[r][q4] = encode4<F>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
+                                           PV(r, 4 * q4 + 3), sc.scale);
         } else { // 1x128 blocks: one scale per row segment, one per column segment
             // row segments: the 8 lanes jg = 0..7 of a row group hold the row's 128 columns
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 uint32_t m = 0;
 #pragma unroll
-                for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(p.v[r][k]));
+                for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(PV(r, k)));
                 m = max(m, (uint32_t)__shfl_xor((int)m, 1));
                 m = max(m, (uint32_t)__shfl_xor((int)m, 2));
                 m = max(m, (uint32_t)__shfl_xor((int)m, 4));
@@ -650,23 +682,40 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 if (jg == 0) s_row[(r0 + r) * bcols + tc] = sc.s;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
-                    cw[r][q4] = encode4<F>(p.v[r][4 * q4], p.v[r][4 * q4 + 1], p.v[r][4 * q4 + 2],
-                                           p.v[r][4 * q4 + 3], sc.scale);
+                    cw[r][q4] = encode4<F>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
+                                           PV(r, 4 * q4 + 3), sc.scale);
+                // stored now: the rowwise codes need not stay live through the column phase
+                if (q_row && valid)
+                    *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) =
+                        make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
             }
-            // column segments: reduce each column's 128 rows through LDS
+            opaque(p);
+            // column segments: a column's 128 rows are 4 rows in each of 32
+            // lanes; the 8 of them in one wave (lane bits 3..5) are reduced
+            // with cross-lane moves, the 4 waves through LDS
             if (q_col) {
+                const int wv = threadIdx.x >> 6;
+                uint32_t cm[16];
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
                     uint32_t m = 0;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) m = max(m, f32_absbits(p.v[r][k]));
-                    colmax[ig * kTile + 16 * jg + k] = m;
+                    for (int r = 0; r < 4; ++r) m = max(m, f32_absbits(PV(r, k)));
+                    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xF, 0xF, false)); // lane ^ 8
+                    m = max(m, (uint32_t)__builtin_amdgcn_ds_swizzle((int)m, 0x401F));                    // lane ^ 16
+                    m = max(m, (uint32_t)__shfl_xor((int)m, 32));                                         // lane ^ 32
+                    cm[k] = m;
+                }
+                if ((threadIdx.x & 63) < 8) {
+                    uint4 *dst = reinterpret_cast<uint4 *>(colmax + wv * kTile + 16 * jg);
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        dst[q4] = make_uint4(cm[4 * q4], cm[4 * q4 + 1], cm[4 * q4 + 2], cm[4 * q4 + 3]);
                 }
                 __syncthreads();
                 if (threadIdx.x < kTile) {
-                    uint32_t m = 0;
-#pragma unroll 8
-                    for (int g = 0; g < 32; ++g) m = max(m, colmax[g * kTile + threadIdx.x]);
+                    const uint32_t m = max(max(colmax[threadIdx.x], colmax[kTile + threadIdx.x]),
+                                           max(colmax[2 * kTile + threadIdx.x], colmax[3 * kTile + threadIdx.x]));
                     const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
                     colscale[threadIdx.x] = sc.scale;
                     s_col[(col0 + threadIdx.x) * brows + tr] = sc.s;
@@ -675,7 +724,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
             }
         }
 
-        if (q_row && valid) {
+        if (kMode != kTileBlock1x128 && q_row && valid) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) =
@@ -684,6 +733,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
         if (q_col) {
             if constexpr (kMode == kTileBlock1x128) {
                 // columnwise codes use the column-segment scales
+                opaque(p);
                 uint32_t cc[4][4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -691,7 +741,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     for (int q4 = 0; q4 < 4; ++q4) {
                         const int k = 4 * q4;
                         const float *cs = colscale + 16 * jg + k;
-                        cc[r][q4] = encode4s<F>(p.v[r][k], p.v[r][k + 1], p.v[r][k + 2], p.v[r][k + 3], cs[0],
+                        cc[r][q4] = encode4s<F>(PV(r, k), PV(r, k + 1), PV(r, k + 2), PV(r, k + 3), cs[0],
                                                 cs[1], cs[2], cs[3]);
                     }
                 stage_transposed(tl, cc, ig, jg);
@@ -702,6 +752,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
             store_transposed(tl, q_col, rows, cols, row0, col0);
         }
         __syncthreads(); // the next tile reuses the LDS buffers
+#undef PV
     }
     if constexpr (kAmax) block_partial(m_all, gs);
 }
