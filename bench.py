@@ -37,7 +37,7 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0
 # FETCH_SIZE and WRITE_SIZE counters of the current kernels scaled by the
 # factors a plain copy gives (profiles/delayed_step_8192x8192_bf16_hbm_traffic.md);
 # set back to None whenever either kernel changes, until the counters are taken again.
-TRAFFIC_BYTES_PER_STEP = 201700704
+TRAFFIC_BYTES_PER_STEP = 201704131
 
 
 def parse():
@@ -108,8 +108,11 @@ def main():
     host_inputs = workloads.parallel_map(workloads.delayed_step, range(T), workers=16)
     xs = [to_dev(h) for h in host_inputs]
     print("# inputs ready in %.1fs" % (time.time() - t0), file=sys.stderr, flush=True)
-    qbufs = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(2)]
-    qsi = [torch.empty(1, device=dev) for _ in range(2)]
+    # eight output buffers (512 MiB) in rotation, so that the 256 MB
+    # last-level cache cannot hold a step's codes until they are overwritten
+    NQ = 8
+    qbufs = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(NQ)]
+    qsi = [torch.empty(1, device=dev) for _ in range(NQ)]
     am = torch.empty(1, device=dev)
     hist = torch.zeros((16, 1), device=dev)
     sc = torch.ones(1, device=dev)
@@ -120,8 +123,8 @@ def main():
         fmt_next = E4 if (t + 1) % 2 == 0 else E5
         # cast with the stored scale + fused amax (one kernel), then the
         # partial fold and ring update (one one-block kernel)
-        fq.fp8_quantize_delayed(xs[t % T], fmt, hist, 0, t, fmt_next, 0, fq.ALGO_MAX, sc, si, qbufs[t % 2],
-                                qsi[t % 2], am, stream=stream)
+        fq.fp8_quantize_delayed(xs[t % T], fmt, hist, 0, t, fmt_next, 0, fq.ALGO_MAX, sc, si, qbufs[t % NQ],
+                                qsi[t % NQ], am, stream=stream)
 
     t = 0
     for _ in range(args.warmup):
@@ -162,7 +165,7 @@ def main():
         "data": "synthetic (seeded numpy generators, resident in HBM)",
         "config": {"workload": "delayed scaling, 32 steps of 8192x8192 bf16, E4M3FN/E5M2 alternating, "
                                "amax history 16 (max), fused input amax",
-                   "tensor": [rows, cols], "history_len": 16, "distinct_inputs": T,
+                   "tensor": [rows, cols], "history_len": 16, "distinct_inputs": T, "distinct_outputs": NQ,
                    "bytes_per_step": bytes_per_step, "host_wall_s": round(wall, 4)},
         "roofline": {"kernel": "fp8_quantize_delayed: cast_kernel (fused amax) + delayed_kernel",
                      "bound": "hbm", "achieved": round(achieved, 1),
@@ -203,7 +206,9 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream):
     E4, E5 = fq.E4M3FN, fq.E5M2
     am = torch.empty(1, device=dev)
     si = torch.empty(1, device=dev)
-    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    # outputs rotate over sets totalling at least 512 MiB, like the inputs, so
+    # that the last-level cache cannot absorb the writes
+    qs8 = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(8)]
 
     def gbs(nbytes, ms):
         g = nbytes / (ms * 1e-3) / 1e9
@@ -217,43 +222,46 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream):
     # a1+a2+a3 current scaling: amax pass + cast pass (5 B/elem)
     def current(i):
         fq.fp8_amax(xs[i], am, stream=stream)
-        fq.fp8_quantize_tensor(xs[i], E4, q, amax_in=am, margin=0, scale_inv_out=si, stream=stream)
+        fq.fp8_quantize_tensor(xs[i], E4, qs8[i % 8], amax_in=am, margin=0, scale_inv_out=si, stream=stream)
     ms = _time(torch, stream, current, 20, rotate=len(xs))
     out["current_scaling_amax+cast_bf16_8192x8192"] = gbs(5 * n, ms)
 
     # a4 dequantize 8192^2 codes -> fp32 (1 + 4 B/elem)
-    y = torch.empty(n, dtype=torch.float32, device=dev)
-    qs = [torch.randint(0, 256, (n,), dtype=torch.uint8, device=dev) for _ in range(3)]
-    ms = _time(torch, stream, lambda i: fq.fp8_dequantize(qs[i], E4, si, y, stream=stream), 20, rotate=3)
+    ys = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(2)]
+    for c in qs8:
+        c.random_(0, 256)
+    ms = _time(torch, stream, lambda i: fq.fp8_dequantize(qs8[i], E4, si, ys[i % 2], stream=stream), 20, rotate=8)
     out["dequantize_8192x8192_to_fp32"] = gbs(5 * n, ms)
 
     # a7 rowwise + columnwise per-tensor cast 8192^2 bf16 (2 + 1 + 1 B/elem)
-    qr = torch.empty((8192, 8192), dtype=torch.uint8, device=dev)
-    qc = torch.empty((8192, 8192), dtype=torch.uint8, device=dev)
+    qr = [q.view(8192, 8192) for q in qs8[:4]]
+    qc = [q.view(8192, 8192) for q in qs8[4:]]
     sc1 = torch.full((1,), 0.01, device=dev)
     x2 = [x.view(8192, 8192) for x in xs]
     ms = _time(torch, stream, lambda i: fq.fp8_quantize_rowwise_colwise(
-        x2[i], E4, q_row=qr, q_col=qc, scale_inv_in=sc1, stream=stream), 20, rotate=len(xs))
+        x2[i], E4, q_row=qr[i % 4], q_col=qc[i % 4], scale_inv_in=sc1, stream=stream), 20, rotate=len(xs))
     out["rowwise_colwise_bf16_8192x8192"] = gbs(4 * n, ms)
 
     # a8 block quantization of the 7168x4096 weight (128x128) and the
     # 4096x7168 activation (1x128), both with their columnwise copies
     W = torch.randn((7168, 4096), device=dev, generator=torch.Generator(device=dev).manual_seed(1)) * 0.02
     Ws = [(W * (1 + 0.01 * k)).to(torch.bfloat16) for k in range(10)]
-    qw, qwt = torch.empty((7168, 4096), dtype=torch.uint8, device=dev), torch.empty((4096, 7168), dtype=torch.uint8, device=dev)
+    qw = [torch.empty((7168, 4096), dtype=torch.uint8, device=dev) for _ in range(10)]
+    qwt = [torch.empty((4096, 7168), dtype=torch.uint8, device=dev) for _ in range(10)]
     sw, swt = torch.empty((56, 32), device=dev), torch.empty((32, 56), device=dev)
-    ms = _time(torch, stream, lambda i: fq.fp8_quantize_block(Ws[i], E4, 128, qw, sw, qwt, swt, stream=stream),
+    ms = _time(torch, stream, lambda i: fq.fp8_quantize_block(Ws[i], E4, 128, qw[i], sw, qwt[i], swt, stream=stream),
                20, rotate=len(Ws))
     nW = 7168 * 4096
     out["block128x128_bf16_7168x4096_with_colwise"] = gbs(4 * nW + 2 * 4 * (nW // 16384), ms)
     X = torch.randn((4096, 7168), device=dev, generator=torch.Generator(device=dev).manual_seed(2))
     Xs = [(X * (1 + 0.01 * k)).to(torch.bfloat16) for k in range(10)]
-    qx, qxt = torch.empty((4096, 7168), dtype=torch.uint8, device=dev), torch.empty((7168, 4096), dtype=torch.uint8, device=dev)
+    qx = [q.view(4096, 7168) for q in qw]
+    qxt = [q.view(7168, 4096) for q in qwt]
     sx, sxt = torch.empty((4096, 56), device=dev), torch.empty((7168, 32), device=dev)
-    ms = _time(torch, stream, lambda i: fq.fp8_quantize_block(Xs[i], E4, 1, qx, sx, qxt, sxt, stream=stream),
+    ms = _time(torch, stream, lambda i: fq.fp8_quantize_block(Xs[i], E4, 1, qx[i], sx, qxt[i], sxt, stream=stream),
                20, rotate=len(Xs))
     out["block1x128_bf16_4096x7168_with_colwise"] = gbs(4 * nW + 4 * (nW // 128) * 2, ms)
-    del Ws, Xs, W, X
+    del Ws, Xs, W, X, qw, qwt, qx, qxt, qs8, qr, qc, ys
 
     def tflops(flop, ms):
         tf = flop / (ms * 1e-3) / 1e12
