@@ -29,7 +29,7 @@ import numpy as np
 E4M3FN, E5M2 = 0, 1
 F32, BF16 = 0, 1
 ALGO_MAX, ALGO_MOST_RECENT = 0, 1
-PER_TENSOR, BLOCK_1x128_128x128 = 0, 1
+PER_TENSOR, BLOCK_1x128_128x128, BLOCK_1x128_1x128 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fp8_oracle.c")
@@ -249,34 +249,61 @@ def decode_codes(q: np.ndarray, fmt: int) -> np.ndarray:
     return out
 
 
+def _block_weight(sA, sB, mode, M, N, kb):
+    """Weight of slice kb for every (m, n): sA[m,kb] * sB[., kb] with B's
+    scale taken per 128-row block (128x128) or per row (1x128)."""
+    sA = np.asarray(sA, dtype=np.float64)
+    sB = np.asarray(sB, dtype=np.float64)
+    rows_of_b = np.arange(N) // 128 if mode == BLOCK_1x128_128x128 else np.arange(N)
+    return sA[:, kb][:, None] * sB[rows_of_b, kb][None, :]
+
+
 def gemm_reference(A: np.ndarray, fa: int, sA, B: np.ndarray, fb: int, sB, mode: int = PER_TENSOR) -> np.ndarray:
     """float64 reference of C = (A*sA)(B*sB)^T for FP8 codes A [M][K], B [N][K].
 
     Per tensor: sA, sB are the two dequant scales and
     R = sA*sB * sum_k val(A[m,k]) val(B[n,k]).
-    Block: sA [M][K/128] (1x128 blocks of A), sB [N/128][K/128] (128x128 blocks
-    of B), and each 128-wide slice of K is summed on its own and weighted by
-    its two block scales:
-    R = sum_kb sA[m,kb] sB[n//128,kb] sum_{k in kb} val(A[m,k]) val(B[n,k]).
+    Block: sA [M][K/128] (1x128 blocks of A) and each 128-wide slice of K is
+    summed on its own and weighted by the slice's two block scales,
+    R = sum_kb sA[m,kb] sB[.,kb] sum_{k in kb} val(A[m,k]) val(B[n,k]),
+    where sB is [N/128][K/128] (128x128 blocks of B, indexed by n // 128) or
+    [N][K/128] (1x128 blocks of B, indexed by n: the weight-gradient GEMM,
+    whose operands are both the transposed, token-contiguous copies).
 
     "Megatron FP8", section 27: products are promoted and summed at full
     precision and only the finished dot product is rounded to the output type;
-    section 6: fp32 accumulation, bf16 output.  Here the sums are float64, in
-    which every E4M3 x E4M3 sum at these sizes is exact."""
+    section 6: fp32 accumulation, bf16 output for fprop/dgrad and fp32 output
+    for wgrad.  Here the sums are float64, in which every E4M3 x E4M3 sum at
+    these sizes is exact."""
     a = decode_codes(A, fa)
     b = decode_codes(B, fb)
     if mode == PER_TENSOR:
         return (a @ b.T) * (float(np.float32(sA)) * float(np.float32(sB)))
     M, K = a.shape
     N = b.shape[0]
-    sA = np.asarray(sA, dtype=np.float64)
-    sB = np.asarray(sB, dtype=np.float64)
     R = np.zeros((M, N), dtype=np.float64)
-    row_block_of_n = np.arange(N) // 128
     for kb in range(K // 128):
         part = a[:, kb * 128:(kb + 1) * 128] @ b[:, kb * 128:(kb + 1) * 128].T
-        R += part * sA[:, kb][:, None] * sB[row_block_of_n, kb][None, :]
+        R += part * _block_weight(sA, sB, mode, M, N, kb)
     return R
+
+
+def gemm_abs_sum(A: np.ndarray, fa: int, sA, B: np.ndarray, fb: int, sB, mode: int = PER_TENSOR) -> np.ndarray:
+    """S[m,n] = the same weighted sum over |val(A[m,k]) val(B[n,k])| and |weights|
+    (float64): the scale of rounding error for an fp32 result.  Summing n
+    terms in fp32, in any order, is off by at most (n - 1) * 2^-24 * S to first
+    order (the standard bound for recursive summation)."""
+    a = np.abs(decode_codes(A, fa))
+    b = np.abs(decode_codes(B, fb))
+    if mode == PER_TENSOR:
+        return (a @ b.T) * abs(float(np.float32(sA)) * float(np.float32(sB)))
+    M, K = a.shape
+    N = b.shape[0]
+    S = np.zeros((M, N), dtype=np.float64)
+    for kb in range(K // 128):
+        part = a[:, kb * 128:(kb + 1) * 128] @ b[:, kb * 128:(kb + 1) * 128].T
+        S += part * np.abs(_block_weight(sA, sB, mode, M, N, kb))
+    return S
 
 
 def gemm_reference_entries(A: np.ndarray, fa: int, sA, B: np.ndarray, fb: int, sB, rows, cols,
@@ -297,8 +324,9 @@ def gemm_reference_entries(A: np.ndarray, fa: int, sA, B: np.ndarray, fb: int, s
             out[i] = float(np.dot(av, bv)) * (float(np.float32(sA)) * float(np.float32(sB)))
         else:
             acc = 0.0
+            nb = n // 128 if mode == BLOCK_1x128_128x128 else n
             for kb in range(K // 128):
                 sl = slice(kb * 128, (kb + 1) * 128)
-                acc += float(np.dot(av[sl], bv[sl])) * float(sA[m, kb]) * float(sB[n // 128, kb])
+                acc += float(np.dot(av[sl], bv[sl])) * float(sA[m, kb]) * float(sB[nb, kb])
             out[i] = acc
     return out

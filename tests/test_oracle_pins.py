@@ -395,8 +395,10 @@ def _brute_gemm(A, fa, sA, B, fb, sB, mode):
                 w = ta[A[m, k]] * tb[B[n, k]]
                 if mode == oracle.PER_TENSOR:
                     acc += w
-                else:
+                elif mode == oracle.BLOCK_1x128_128x128:
                     acc += w * sA[m, k // 128] * sB[n // 128, k // 128]
+                else:
+                    acc += w * sA[m, k // 128] * sB[n, k // 128]
             R[m, n] = acc * (float(sA) * float(sB) if mode == oracle.PER_TENSOR else 1.0)
     return R
 
@@ -432,6 +434,58 @@ def test_gemm_reference_brute_force_block():
     assert np.allclose(R, ref, rtol=1e-12, atol=1e-300)
     ent = oracle.gemm_reference_entries(A, E5, sA, B, E4, sB, [2, 0], [255, 129], oracle.BLOCK_1x128_128x128)
     assert np.allclose(ent, ref[[2, 0], [255, 129]], rtol=1e-12, atol=0)
+
+
+def test_gemm_reference_brute_force_block_1x128_both():
+    """The weight-gradient layout: both operands carry 1x128 scales, B's per row."""
+    rng = np.random.default_rng(34)
+    M, N, K = 4, 6, 384
+    A = _random_codes(rng, (M, K), E5)
+    B = _random_codes(rng, (N, K), E4)
+    sA = np.float32(rng.uniform(0.1, 2, (M, K // 128)))
+    sB = np.float32(rng.uniform(0.1, 2, (N, K // 128)))
+    R = oracle.gemm_reference(A, E5, sA, B, E4, sB, oracle.BLOCK_1x128_1x128)
+    ref = _brute_gemm(A, E5, sA, B, E4, sB, oracle.BLOCK_1x128_1x128)
+    assert np.allclose(R, ref, rtol=1e-12, atol=1e-300)
+    ent = oracle.gemm_reference_entries(A, E5, sA, B, E4, sB, [3, 0], [5, 1], oracle.BLOCK_1x128_1x128)
+    assert np.allclose(ent, ref[[3, 0], [5, 1]], rtol=1e-12, atol=0)
+    # B's 1x128 scales that are equal within each 128-row group reduce to the 128x128 rule
+    N2 = 256
+    B2 = _random_codes(rng, (N2, K), E4)
+    sB_blk = np.float32(rng.uniform(0.1, 2, (N2 // 128, K // 128)))
+    sB_rows = np.repeat(sB_blk, 128, axis=0)
+    assert np.array_equal(oracle.gemm_reference(A, E5, sA, B2, E4, sB_rows, oracle.BLOCK_1x128_1x128),
+                          oracle.gemm_reference(A, E5, sA, B2, E4, sB_blk, oracle.BLOCK_1x128_128x128))
+
+
+def test_gemm_abs_sum_bounds_the_result():
+    """S >= |R| everywhere, S == R when every term is non-negative, and S is the
+    brute-force sum of absolute terms."""
+    rng = np.random.default_rng(35)
+    M, N, K = 3, 5, 256
+    A = _random_codes(rng, (M, K), E4)
+    B = _random_codes(rng, (N, K), E5)
+    sA = np.float32(rng.uniform(-2, 2, (M, K // 128)))
+    sB = np.float32(rng.uniform(-2, 2, (N, K // 128)))
+    for mode, a_s, b_s in ((oracle.PER_TENSOR, np.float32(-0.5), np.float32(3.0)),
+                           (oracle.BLOCK_1x128_1x128, sA, sB)):
+        R = oracle.gemm_reference(A, E4, a_s, B, E5, b_s, mode)
+        S = oracle.gemm_abs_sum(A, E4, a_s, B, E5, b_s, mode)
+        assert np.all(S >= np.abs(R) * (1 - 1e-12))
+        ta, tb = np.abs(oracle.decode_table(E4)), np.abs(oracle.decode_table(E5))
+        m, n = 2, 4
+        terms = ta[A[m]] * tb[B[n]]
+        if mode == oracle.PER_TENSOR:
+            brute = terms.sum() * abs(float(a_s) * float(b_s))
+        else:
+            brute = sum(terms[kb * 128:(kb + 1) * 128].sum() * abs(float(a_s[m, kb]) * float(b_s[n, kb]))
+                        for kb in range(K // 128))
+        assert np.isclose(S[m, n], brute, rtol=1e-12)
+    Ap = A & 0x7F
+    Bp = B & 0x7F
+    Rp = oracle.gemm_reference(Ap, E4, np.abs(sA), Bp, E5, np.abs(sB), oracle.BLOCK_1x128_1x128)
+    Sp = oracle.gemm_abs_sum(Ap, E4, np.abs(sA), Bp, E5, np.abs(sB), oracle.BLOCK_1x128_1x128)
+    assert np.allclose(Rp, Sp, rtol=1e-12)
 
 
 def test_gemm_reference_exact_special_cases():
