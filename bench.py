@@ -16,7 +16,8 @@ uses that same per-step duration.
 
 Every other row of the hot path (amax, current scaling, dequantize, rowwise +
 columnwise, 128x128 and 1x128 block quantization, per-tensor and block-scaled
-GEMMs) is timed at its own workload size and reported under "rows".
+GEMMs, and the fp32-output weight-gradient GEMM) is timed at its own workload
+size and reported under "rows".
 
 The CPU oracle is timed on the host cores on a bounded sample of the same
 workload ("cpu_baseline").
@@ -311,6 +312,18 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream):
     ms = _time(torch, stream, lambda i: fq.fp8_scaled_gemm(dYq, E5, sdy, Wtq, E4, swt, fq.BLOCK_1x128_128x128, dX,
                                                             cam, stream=stream), 10)
     out["gemm_block_dgrad_4096x4096x14336"] = tflops(2 * 4096 * 4096 * 14336, ms)
+    del dYq, Wtq, Xq, Wq, Y, dX
+
+    # next: weight gradient dW = dY^T X, fp32 out, both operands the
+    # token-contiguous (columnwise) copies with 1x128 scales along the tokens
+    dYt = codes((14336, 4096), E5)
+    Xt = codes((4096, 4096), E4)
+    sdyt = torch.rand((14336, 32), device=dev, generator=g) + 0.5
+    sxt = torch.rand((4096, 32), device=dev, generator=g) + 0.5
+    dW = torch.empty((14336, 4096), dtype=torch.float32, device=dev)
+    ms = _time(torch, stream, lambda i: fq.fp8_scaled_gemm(dYt, E5, sdyt, Xt, E4, sxt, fq.BLOCK_1x128_1x128, dW,
+                                                            cam, stream=stream), 10)
+    out["gemm_block_wgrad_14336x4096x4096_fp32out"] = tflops(2 * 14336 * 4096 * 4096, ms)
     return out
 
 

@@ -23,7 +23,7 @@ import torch
 E4M3FN, E5M2 = 0, 1
 F32, BF16 = 0, 1
 ALGO_MAX, ALGO_MOST_RECENT = 0, 1
-PER_TENSOR, BLOCK_1x128_128x128 = 0, 1
+PER_TENSOR, BLOCK_1x128_128x128, BLOCK_1x128_1x128 = 0, 1, 2
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -152,12 +152,10 @@ def fp8_quantize_delayed(x, fmt, hist, col, step, fmt_next, margin, algo, scale,
 
 
 def fp8_scaled_gemm(A, fa, sA, B, fb, sB, mode, C, amax_out=None, stream=None):
-    """C = (A*sA)(B*sB)^T, A [M][K], B [N][K] codes, C [M][N] bf16."""
+    """C = (A*sA)(B*sB)^T, A [M][K], B [N][K] codes, C [M][N] bfloat16 or float32."""
     M, K = A.shape
     N = B.shape[0]
     if B.shape[1] != K or tuple(C.shape) != (M, N):
         raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape), tuple(C.shape)))
-    if C.dtype != torch.bfloat16:
-        raise TypeError("C must be bfloat16")
-    _check(lib.fp8_scaled_gemm(_ptr(A), fa, _ptr(sA), _ptr(B), fb, _ptr(sB), M, N, K, mode, _ptr(C), BF16,
+    _check(lib.fp8_scaled_gemm(_ptr(A), fa, _ptr(sA), _ptr(B), fb, _ptr(sB), M, N, K, mode, _ptr(C), _dtype(C),
                                _ptr(amax_out), _stream(stream)))

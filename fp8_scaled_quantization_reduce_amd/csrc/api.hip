@@ -303,10 +303,9 @@ int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t
 {
     const char *fn = "fp8_scaled_gemm";
     if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(FP8Q_EINVAL, "%s: unknown operand format", fn);
-    if (mode != FP8Q_PER_TENSOR && mode != FP8Q_BLOCK_1x128_128x128)
+    if (mode != FP8Q_PER_TENSOR && mode != FP8Q_BLOCK_1x128_128x128 && mode != FP8Q_BLOCK_1x128_1x128)
         return fail(FP8Q_EINVAL, "%s: unknown scaling mode %d", fn, (int)mode);
     if (!valid_dtype(c_dtype)) return fail(FP8Q_EINVAL, "%s: unknown output dtype %d", fn, (int)c_dtype);
-    if (c_dtype != FP8Q_BF16) return fail(FP8Q_EUNSUPPORTED, "%s: only bf16 output is implemented", fn);
     if (M < 0 || N < 0 || K < 0) return fail(FP8Q_EINVAL, "%s: negative shape", fn);
     if (M % 128 || N % 128 || K % 128) return fail(FP8Q_EUNSUPPORTED, "%s: M, N, K must be multiples of 128", fn);
     if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31)
@@ -322,7 +321,8 @@ int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t
     if (!C || !aligned(C, 16)) return fail(FP8Q_EINVAL, "%s: C must be a 16-byte aligned pointer", fn);
     if (K > 0 && (!A || !B || !aligned(A, 16) || !aligned(B, 16)))
         return fail(FP8Q_EINVAL, "%s: A and B must be 16-byte aligned pointers", fn);
-    if (overlap(C, M * N * 2, A, M * K) || overlap(C, M * N * 2, B, N * K) || overlap(C, M * N * 2, amax_out, 4))
+    const int64_t c_bytes = M * N * dsize(c_dtype);
+    if (overlap(C, c_bytes, A, M * K) || overlap(C, c_bytes, B, N * K) || overlap(C, c_bytes, amax_out, 4))
         return fail(FP8Q_EINVAL, "%s: C overlaps an input", fn);
     fp8q::GridScratch *gs = nullptr;
     if (amax_out) {
@@ -332,8 +332,8 @@ int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t
         hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
         if (e != hipSuccess) return hip_status(e, fn);
     }
-    return hip_status(fp8q::launch_gemm(A, fa, sA, B, fb, sB, M, N, K, mode, C, amax_out, gs, (hipStream_t)stream),
-                      fn);
+    return hip_status(
+        fp8q::launch_gemm(A, fa, sA, B, fb, sB, M, N, K, mode, C, c_dtype, amax_out, gs, (hipStream_t)stream), fn);
 }
 
 } // extern "C"

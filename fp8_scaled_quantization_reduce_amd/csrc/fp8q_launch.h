@@ -55,6 +55,7 @@ hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, flo
                                hipStream_t s);
 
 hipError_t launch_gemm(const uint8_t *A, int fa, const float *sA, const uint8_t *B, int fb, const float *sB, int64_t M,
-                       int64_t N, int64_t K, int mode, void *C, float *amax_out, GridScratch *gs, hipStream_t s);
+                       int64_t N, int64_t K, int mode, void *C, int c_dtype, float *amax_out, GridScratch *gs,
+                       hipStream_t s);
 
 } // namespace fp8q

@@ -96,6 +96,28 @@ __device__ __forceinline__ v8i read_frag(const uint8_t *lds, int r, int g)
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
+// Store four consecutive outputs of one row of C (bf16, round to nearest even,
+// or fp32 as is) and fold their magnitudes into m (canonicalised later).
+template <bool kF32, bool kAmax>
+__device__ __forceinline__ void store_out4(void *C, int64_t idx, const v4f &v, uint32_t &m)
+{
+    if constexpr (kF32) {
+        *reinterpret_cast<v4f *>(reinterpret_cast<float *>(C) + idx) = v;
+        if constexpr (kAmax) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = max(m, __float_as_uint(v[e]) & 0x7FFFFFFFu);
+        }
+    } else {
+        const bf16x4 h = __builtin_convertvector(v, bf16x4);
+        *reinterpret_cast<bf16x4 *>(reinterpret_cast<__bf16 *>(C) + idx) = h;
+        if constexpr (kAmax) {
+            const uint2 bits = __builtin_bit_cast(uint2, h);
+            m = max(m, max((bits.x & 0x7FFFu) << 16, (bits.x >> 16 & 0x7FFFu) << 16));
+            m = max(m, max((bits.y & 0x7FFFu) << 16, (bits.y >> 16 & 0x7FFFu) << 16));
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Per-tensor kernel.  256x256 block tile, 2x2 waves of 128x128 as 4x4 tiles
 // of v_mfma_f32_32x32x64_f8f6f4 (256 fp32 accumulators per lane).  K moves in
@@ -140,12 +162,12 @@ __device__ __forceinline__ v8i read_frag32(const uint8_t *lds, int r, int g, int
 // The two stages are distinct LDS objects addressed with compile-time stage
 // numbers (the slice loop is unrolled by two), so the compiler can tell a
 // read of one stage from the direct loads landing in the other.
-template <int FA, int FB, bool kAmax>
+template <int FA, int FB, bool kAmax, bool kF32>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t *__restrict__ A,
                                                                   const uint8_t *__restrict__ B,
                                                                   const float *__restrict__ sA,
                                                                   const float *__restrict__ sB, int M, int N, int K,
-                                                                  __bf16 *__restrict__ C, GridScratch *gs)
+                                                                  void *__restrict__ C, GridScratch *gs)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t st0[kPTStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[kPTStageBytes];
@@ -272,15 +294,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
                 const int64_t col = n0 + wn * 128 + 32 * j + 8 * q + 4 * fg;
                 const v4f v = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                   acc[i][j][4 * q + 3]} * alpha;
-                const bf16x4 h = __builtin_convertvector(v, bf16x4);
-                if (row < M && col < N) {
-                    *reinterpret_cast<bf16x4 *>(C + row * N + col) = h;
-                    if constexpr (kAmax) {
-                        const uint2 bits = __builtin_bit_cast(uint2, h);
-                        m = max(m, max((bits.x & 0x7FFFu) << 16, (bits.x >> 16 & 0x7FFFu) << 16));
-                        m = max(m, max((bits.y & 0x7FFFu) << 16, (bits.y >> 16 & 0x7FFFu) << 16));
-                    }
-                }
+                if (row < M && col < N) store_out4<kF32, kAmax>(C, row * N + col, v, m);
             }
         }
     }
@@ -303,17 +317,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
 constexpr int kBSThreads = 512;
 constexpr int kBSStageBytes = 2 * kBM * kBK;
 
-template <int FA, int FB, bool kAmax>
+template <int FA, int FB, bool kAmax, bool kF32, bool kRowB>
 __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *__restrict__ A,
                                                                 const uint8_t *__restrict__ B,
                                                                 const float *__restrict__ sA,
                                                                 const float *__restrict__ sB, int M, int N, int K,
-                                                                __bf16 *__restrict__ C, GridScratch *gs)
+                                                                void *__restrict__ C, GridScratch *gs)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t st0[kBSStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[kBSStageBytes];
     __shared__ __attribute__((aligned(16))) float sa0[kBM];
     __shared__ __attribute__((aligned(16))) float sa1[kBM];
+    __shared__ __attribute__((aligned(16))) float sb0[kRowB ? kBM : 4]; // B's row scales (1x128 B)
+    __shared__ __attribute__((aligned(16))) float sb1[kRowB ? kBM : 4];
     __shared__ uint32_t red[kBSThreads / 64];
 
     int tm, tn;
@@ -335,12 +351,15 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
     // lane L of a 1 KiB load writes physical chunk L % 8 of row 8(w + 8u) + L / 8,
     // which holds logical chunk (L % 8) ^ ((row >> 1) & 7) = (L % 8) ^ ((4w + L / 16) & 7)
     const int voff = (lane >> 3) * K + (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4);
-    // the wave's 128 columns lie in one 128-column scale block (clamped for the
-    // half tile past N, whose results are never stored)
+    // 128x128 B: the wave's 128 columns lie in one 128-column scale block
+    // (clamped for the half tile past N, whose results are never stored).
+    // 1x128 B: one scale per row of B (column of C), staged like A's.
     const int nb = min((int)((n0 + wn * 128) / 128), N / 128 - 1);
     const float *__restrict__ sbp = sB + (int64_t)nb * kblocks;
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(sB + (kRowB ? n0 * kblocks : 0)), 0, kRowB ? (int)(b_rows * kblocks * 4) : 4, kRawBufferWord3);
 
-    auto stage = [&](uint8_t *st, float *sa, int kb) {
+    auto stage = [&](uint8_t *st, float *sa, float *sbr, int kb) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int row = 8 * (w + 8 * u);
@@ -356,6 +375,9 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
         if (w < 4)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(sa + 64 * w), 4, lane * kblocks * 4,
                                                      (64 * w * kblocks + kb) * 4, 0, 0);
+        else if (kRowB)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(sbr + 64 * (w - 4)), 4, lane * kblocks * 4,
+                                                     (64 * (w - 4) * kblocks + kb) * 4, 0, 0);
     };
 
     v4f acc[4][8];
@@ -376,83 +398,103 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
     // spill their 128 partial registers): the one on the B fragment keeps
     // tile j's MFMAs below it, the one on the promoted accumulators keeps
     // tile j-1's FMAs above the next tile's.
+    // Weights: 128x128 B: wi[i] = fl32(sA[row i] * sB[block]); 1x128 B:
+    // fl32(sA[row i] * sB[col]) per element, from sai[i] and the tile's four
+    // column scales, read from LDS just before the tile's MFMAs are issued
+    // (tile 7's before the slice's barrier, after which the stage is reloaded).
     v8i a[4], b;
-    float wi[4];
+    float wi[4], sai[4];
     float sb_next = 0.0f;
-    auto slice = [&](int kb, uint8_t *cur, float *sac, const uint8_t *nxt, const float *san, bool full) {
+    auto promote = [&](int j, const v4f (&part)[4], const v4f &sbj) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float wgt = kRowB ? sai[i] * sbj[e] : wi[i];
+                acc[i][j][e] = __builtin_fmaf(part[i][e], wgt, acc[i][j][e]);
+            }
+        asm volatile("" : "+v"(acc[0][j]), "+v"(acc[1][j]), "+v"(acc[2][j]), "+v"(acc[3][j]));
+    };
+    auto slice = [&](int kb, uint8_t *cur, float *sac, float *sbc, const uint8_t *nxt, const float *san,
+                     bool full) {
         const uint8_t *lb = cur + kBM * kBK;
+        const float *sbw = sbc + wn * 128 + 4 * fg; // this lane's column scales, tile 0
         v4f prev[4];
+        v4f sb7 = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             asm volatile("" : "+v"(b));
             v8i bn;
             if (j + 1 < 8) bn = read_frag(lb, wn * 128 + 16 * (j + 1) + fr, fg);
+            v4f sbj = v4f{0.f, 0.f, 0.f, 0.f}; // tile j-1's column scales
+            if constexpr (kRowB) {
+                if (j > 0) sbj = *reinterpret_cast<const v4f *>(sbw + 16 * (j - 1));
+                if (j == 7) sb7 = *reinterpret_cast<const v4f *>(sbw + 16 * 7);
+            }
             if (j == 7) {
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
-                if (full || kb + 2 < kblocks) stage(cur, sac, kb + 2);
+                if (full || kb + 2 < kblocks) stage(cur, sac, sbc, kb + 2);
             }
             v4f cur_p[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) cur_p[i] = mfma16x16x128<FB, FA>(b, a[i], v4f{0.f, 0.f, 0.f, 0.f});
-            if (j > 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc[i][j - 1][e] = __builtin_fmaf(prev[i][e], wi[i], acc[i][j - 1][e]);
-                asm volatile("" : "+v"(acc[0][j - 1]), "+v"(acc[1][j - 1]), "+v"(acc[2][j - 1]),
-                             "+v"(acc[3][j - 1]));
-            }
+            if (j > 0) promote(j - 1, prev, sbj);
 #pragma unroll
             for (int i = 0; i < 4; ++i) prev[i] = cur_p[i];
             if (j + 1 < 8) b = bn;
         }
         // tile 7's promotion with this slice's weights, then the next slice's
         // fragments and weights
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][7][e] = __builtin_fmaf(prev[i][e], wi[i], acc[i][7][e]);
-        asm volatile("" : "+v"(acc[0][7]), "+v"(acc[1][7]), "+v"(acc[2][7]), "+v"(acc[3][7]));
+        promote(7, prev, sb7);
         if (full || kb + 1 < kblocks) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i] = read_frag(nxt, wm * 64 + 16 * i + fr, fg);
             b = read_frag(nxt + kBM * kBK, wn * 128 + fr, fg);
-            const float sb = sb_next;
+            if constexpr (kRowB) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wi[i] = san[wm * 64 + 16 * i + fr] * sb;
-            sb_next = (full || kb + 2 < kblocks) ? sbp[kb + 2] : 0.0f;
+                for (int i = 0; i < 4; ++i) sai[i] = san[wm * 64 + 16 * i + fr];
+            } else {
+                const float sb = sb_next;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wi[i] = san[wm * 64 + 16 * i + fr] * sb;
+                sb_next = (full || kb + 2 < kblocks) ? sbp[kb + 2] : 0.0f;
+            }
         }
     };
 
     // prologue: slices 0 and 1 in flight (both stages always filled, see the
     // per-tensor kernel), slice 0's fragments and weights
     if (kblocks > 0) {
-        stage(st0, sa0, 0);
-        stage(st1, sa1, 1);
+        stage(st0, sa0, sb0, 0);
+        stage(st1, sa1, sb1, 1);
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[i] = read_frag(st0, wm * 64 + 16 * i + fr, fg);
         b = read_frag(st0 + kBM * kBK, wn * 128 + fr, fg);
-        const float sb = sbp[0];
+        if constexpr (kRowB) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wi[i] = sa0[wm * 64 + 16 * i + fr] * sb;
-        sb_next = kblocks > 1 ? sbp[1] : 0.0f;
+            for (int i = 0; i < 4; ++i) sai[i] = sa0[wm * 64 + 16 * i + fr];
+        } else {
+            const float sb = sbp[0];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wi[i] = sa0[wm * 64 + 16 * i + fr] * sb;
+            sb_next = kblocks > 1 ? sbp[1] : 0.0f;
+        }
     }
     // steady state: slices kb + 2 and kb + 3 exist (no guards)
     int kb = 0;
     for (; kb + 4 <= kblocks; kb += 2) {
-        slice(kb, st0, sa0, st1, sa1, true);
-        slice(kb + 1, st1, sa1, st0, sa0, true);
+        slice(kb, st0, sa0, sb0, st1, sa1, true);
+        slice(kb + 1, st1, sa1, sb1, st0, sa0, true);
     }
     // at most three slices remain; kb is even
-    if (kb < kblocks) slice(kb, st0, sa0, st1, sa1, false);
-    if (kb + 1 < kblocks) slice(kb + 1, st1, sa1, st0, sa0, false);
-    if (kb + 2 < kblocks) slice(kb + 2, st0, sa0, st1, sa1, false);
+    if (kb < kblocks) slice(kb, st0, sa0, sb0, st1, sa1, false);
+    if (kb + 1 < kblocks) slice(kb + 1, st1, sa1, sb1, st0, sa0, false);
+    if (kb + 2 < kblocks) slice(kb + 2, st0, sa0, sb0, st1, sa1, false);
 
     // epilogue: lane (fr, fg) of tile (i, j) holds C[row][4 consecutive cols]
     uint32_t m = 0;
@@ -462,15 +504,7 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int64_t col = n0 + wn * 128 + 16 * j + 4 * fg;
-            const bf16x4 h = __builtin_convertvector(acc[i][j], bf16x4);
-            if (row < M && col < N) {
-                *reinterpret_cast<bf16x4 *>(C + row * N + col) = h;
-                if constexpr (kAmax) {
-                    const uint2 bits = __builtin_bit_cast(uint2, h);
-                    m = max(m, max((bits.x & 0x7FFFu) << 16, (bits.x >> 16 & 0x7FFFu) << 16));
-                    m = max(m, max((bits.y & 0x7FFFu) << 16, (bits.y >> 16 & 0x7FFFu) << 16));
-                }
-            }
+            if (row < M && col < N) store_out4<kF32, kAmax>(C, row * N + col, acc[i][j], m);
         }
     }
     if constexpr (kAmax) {
@@ -485,40 +519,54 @@ int gemm_grid(int64_t M, int64_t N, int mode)
     return (int)(((M + kBM - 1) / kBM) * ((N + kBM - 1) / kBM));
 }
 
-template <int FA, int FB>
+template <int FA, int FB, bool kF32>
 static hipError_t launch_gemm_t(const uint8_t *A, const float *sA, const uint8_t *B, const float *sB, int64_t M,
                                 int64_t N, int64_t K, int mode, void *C, float *amax_out, GridScratch *gs,
                                 hipStream_t s)
 {
     const int grid = gemm_grid(M, N, mode);
-    __bf16 *c = reinterpret_cast<__bf16 *>(C);
     const int m = (int)M, n = (int)N, k = (int)K;
     if (mode == 0) {
         if (amax_out)
-            gemm_pt_kernel<FA, FB, true><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
+            gemm_pt_kernel<FA, FB, true, kF32><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
         else
-            gemm_pt_kernel<FA, FB, false><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
+            gemm_pt_kernel<FA, FB, false, kF32><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
+    } else if (mode == 1) {
+        if (amax_out)
+            gemm_bs_kernel<FA, FB, true, kF32, false><<<grid, kBSThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
+        else
+            gemm_bs_kernel<FA, FB, false, kF32, false><<<grid, kBSThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
     } else {
         if (amax_out)
-            gemm_bs_kernel<FA, FB, true><<<grid, kBSThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
+            gemm_bs_kernel<FA, FB, true, kF32, true><<<grid, kBSThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
         else
-            gemm_bs_kernel<FA, FB, false><<<grid, kBSThreads, 0, s>>>(A, B, sA, sB, m, n, k, c, gs);
+            gemm_bs_kernel<FA, FB, false, kF32, true><<<grid, kBSThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !amax_out) return e;
     return launch_finish_amax(gs, grid, amax_out, s);
 }
 
+template <int FA, int FB>
+static hipError_t launch_gemm_f(const uint8_t *A, const float *sA, const uint8_t *B, const float *sB, int64_t M,
+                                int64_t N, int64_t K, int mode, void *C, int c_dtype, float *amax_out,
+                                GridScratch *gs, hipStream_t s)
+{
+    if (c_dtype == kF32) return launch_gemm_t<FA, FB, true>(A, sA, B, sB, M, N, K, mode, C, amax_out, gs, s);
+    return launch_gemm_t<FA, FB, false>(A, sA, B, sB, M, N, K, mode, C, amax_out, gs, s);
+}
+
 hipError_t launch_gemm(const uint8_t *A, int fa, const float *sA, const uint8_t *B, int fb, const float *sB, int64_t M,
-                       int64_t N, int64_t K, int mode, void *C, float *amax_out, GridScratch *gs, hipStream_t s)
+                       int64_t N, int64_t K, int mode, void *C, int c_dtype, float *amax_out, GridScratch *gs,
+                       hipStream_t s)
 {
     if (fa == kE4M3 && fb == kE4M3)
-        return launch_gemm_t<kE4M3, kE4M3>(A, sA, B, sB, M, N, K, mode, C, amax_out, gs, s);
+        return launch_gemm_f<kE4M3, kE4M3>(A, sA, B, sB, M, N, K, mode, C, c_dtype, amax_out, gs, s);
     if (fa == kE5M2 && fb == kE4M3)
-        return launch_gemm_t<kE5M2, kE4M3>(A, sA, B, sB, M, N, K, mode, C, amax_out, gs, s);
+        return launch_gemm_f<kE5M2, kE4M3>(A, sA, B, sB, M, N, K, mode, C, c_dtype, amax_out, gs, s);
     if (fa == kE4M3 && fb == kE5M2)
-        return launch_gemm_t<kE4M3, kE5M2>(A, sA, B, sB, M, N, K, mode, C, amax_out, gs, s);
-    return launch_gemm_t<kE5M2, kE5M2>(A, sA, B, sB, M, N, K, mode, C, amax_out, gs, s);
+        return launch_gemm_f<kE4M3, kE5M2>(A, sA, B, sB, M, N, K, mode, C, c_dtype, amax_out, gs, s);
+    return launch_gemm_f<kE5M2, kE5M2>(A, sA, B, sB, M, N, K, mode, C, c_dtype, amax_out, gs, s);
 }
 
 } // namespace fp8q

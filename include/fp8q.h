@@ -62,6 +62,7 @@ extern "C" {
 /* GEMM scaling modes */
 #define FP8Q_PER_TENSOR 0
 #define FP8Q_BLOCK_1x128_128x128 1
+#define FP8Q_BLOCK_1x128_1x128 2
 
 /*
  * fp8_amax -- *amax = max_i |x_i| over n elements ([MFP8] section 4, the
@@ -184,17 +185,23 @@ int fp8_quantize_delayed(const void *x, int32_t dtype, int64_t n, int32_t fmt, f
 
 /*
  * fp8_scaled_gemm -- C = (A * sA) (B * sB)^T on FP8 codes with fp32
- * accumulation ([MFP8] section 6: FP8 operands, fp32 accumulation, bf16
- * output; section 27: products promoted to fp32 and summed, one downcast of
- * the finished dot product).
+ * accumulation ([MFP8] section 6: FP8 operands and fp32 accumulation, bf16
+ * output for fprop and dgrad, fp32 output for wgrad = dY^T X; section 27:
+ * products promoted to fp32 and summed, one downcast of the finished dot
+ * product).
  *   A [M][K] codes of format fa, B [N][K] codes of format fb (both
- *   K-contiguous), C [M][N] output of type c_dtype (FP8Q_BF16).
+ *   K-contiguous), C [M][N] output of type c_dtype (FP8Q_BF16 or FP8Q_F32).
  *   mode FP8Q_PER_TENSOR: sA, sB point to one float each (dequant scales);
- *        C = bf16(fl32(fl32(sA*sB) * acc)).
+ *        C = out(fl32(fl32(sA*sB) * acc)).
  *   mode FP8Q_BLOCK_1x128_128x128: sA [M][K/128] (1x128 blocks of A),
  *        sB [N/128][K/128] (128x128 blocks of B); each 128-wide K slice is
- *        accumulated separately and added as acc += sA[m,kb]*sB[n/128,kb]*part.
- *   amax_out (nullable) receives max |C| over the emitted bf16 values.
+ *        accumulated separately and added as
+ *        acc = fma(part, fl32(sA[m,kb]*sB[n/128,kb]), acc); C = out(acc).
+ *   mode FP8Q_BLOCK_1x128_1x128: as above with sB [N][K/128] (1x128 blocks
+ *        of B, one scale per row of B and K slice), the weight gradient from
+ *        the transposed (token-contiguous) copies of dY and X.
+ *   out() is bf16 round-to-nearest-even or the fp32 value itself.
+ *   amax_out (nullable) receives max |C| over the emitted values.
  * M, N, K must be multiples of 128 (FP8Q_EUNSUPPORTED otherwise).
  */
 int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb, const float *sB,

@@ -7,6 +7,7 @@ import re
 
 import pytest
 
+import oracle
 from conftest import ROOT
 
 fq = pytest.importorskip("fp8_scaled_quantization_reduce_amd")
@@ -42,7 +43,8 @@ def test_enum_values_match_header():
     assert int(defs["FP8Q_F32"]) == fq.F32 and int(defs["FP8Q_BF16"]) == fq.BF16
     assert int(defs["FP8Q_EINVAL"]) == fq.EINVAL and int(defs["FP8Q_EUNSUPPORTED"]) == fq.EUNSUPPORTED
     assert int(defs["FP8Q_PER_TENSOR"]) == fq.PER_TENSOR
-    assert int(defs["FP8Q_BLOCK_1x128_128x128"]) == fq.BLOCK_1x128_128x128
+    assert int(defs["FP8Q_BLOCK_1x128_128x128"]) == fq.BLOCK_1x128_128x128 == oracle.BLOCK_1x128_128x128
+    assert int(defs["FP8Q_BLOCK_1x128_1x128"]) == fq.BLOCK_1x128_1x128 == oracle.BLOCK_1x128_1x128
 
 
 def _expect(status, code, fragment):
@@ -123,7 +125,10 @@ def test_delayed_step_validation():
 def test_gemm_validation():
     g = L.fp8_scaled_gemm
     A, B, C = BAD + 0x100000, BAD + 0x200000, BAD + 0x300000
-    _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 0, C, fq.F32, None, S), fq.EUNSUPPORTED, "bf16")
+    _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 0, C, 7, None, S), fq.EINVAL, "dtype")
+    _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 3, C, fq.F32, None, S), fq.EINVAL, "mode")
+    # an fp32 C of 128x128 spans 64 KiB: one that starts 32 KiB before B overlaps it
+    _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 2, B - 0x8000, fq.F32, None, S), fq.EINVAL, "overlaps")
     _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 100, 128, 0, C, fq.BF16, None, S), fq.EUNSUPPORTED, "multiples")
     _expect(g(A, 2, BAD, B, 0, BAD + 4, 128, 128, 128, 0, C, fq.BF16, None, S), fq.EINVAL, "format")
     _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 5, C, fq.BF16, None, S), fq.EINVAL, "mode")

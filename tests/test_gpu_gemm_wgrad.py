@@ -1,0 +1,158 @@
+"""GPU parity of the weight-gradient GEMM: fp32 output ("Megatron FP8",
+section 6: dW = dY^T X with fp32 accumulation and fp32 output) in every
+scaling mode, including 1x128 scales on both operands (the transposed,
+token-contiguous copies of dY and X).
+
+Bar for fp32 output, element by element, with R the float64 oracle and S the
+same weighted sum over absolute terms (oracle.gemm_abs_sum):
+    |C - R| <= (2^-11 + (K + K/128 + 2) * 2^-24) * S,
+and, as for every GEMM, |C - R| <= 1e-2 * max |R|.  The second term of the
+first bound is fp32 summation (n - 1 roundings of at most 2^-24 of the running
+magnitude: one per product, one per slice promotion, one for the output
+scale).  The first is the FP8 matrix instruction's own adder: it sums the
+products of one instruction with fewer bits than an fp32 add chain, measured on
+random codes at up to 2^-12.7 * S for one 128-wide slice (2^-19.4 * S on codes of
+Gaussian data), so 2^-11 leaves a 3x margin.  Exact cases (small integers,
+power-of-two scales) must match bit for bit, and the output amax must equal
+max |C| over the emitted values."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import f32_bits, host, scalar, to_dev
+
+pytestmark = pytest.mark.gpu
+
+fq = pytest.importorskip("fp8_scaled_quantization_reduce_amd")
+E4, E5 = oracle.E4M3FN, oracle.E5M2
+MODES = (oracle.PER_TENSOR, oracle.BLOCK_1x128_128x128, oracle.BLOCK_1x128_1x128)
+
+
+def _gpu_gemm_f32(A, fa, sA, B, fb, sB, mode):
+    M, N = A.shape[0], B.shape[0]
+    C = torch.full((M, N), 12345.0, dtype=torch.float32, device="cuda")
+    am = scalar(-1.0)
+    sa = to_dev(np.ascontiguousarray(np.float32(sA).reshape(-1)))
+    sb = to_dev(np.ascontiguousarray(np.float32(sB).reshape(-1)))
+    fq.fp8_scaled_gemm(to_dev(A), fa, sa, to_dev(B), fb, sb, mode, C, am)
+    return host(C), host(am)[0]
+
+
+MFMA_ADDER = 2.0 ** -11
+
+
+def _bound(A, fa, sA, B, fb, sB, mode):
+    K = A.shape[1]
+    return (MFMA_ADDER + (K + K // 128 + 2) * 2.0 ** -24) * oracle.gemm_abs_sum(A, fa, sA, B, fb, sB, mode)
+
+
+def _check(C, amax, A, fa, sA, B, fb, sB, mode):
+    R = oracle.gemm_reference(A, fa, sA, B, fb, sB, mode)
+    err = np.abs(C.astype(np.float64) - R)
+    bound = _bound(A, fa, sA, B, fb, sB, mode)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), (worst, err[worst], bound[worst])
+    assert np.max(err) <= 1e-2 * np.max(np.abs(R))
+    assert f32_bits(amax) == f32_bits(np.max(np.abs(C)))
+
+
+def _random_codes(rng, shape, fmt):
+    c = rng.integers(0, 256, shape).astype(np.uint8)
+    bad = ~np.isfinite(oracle.decode_table(fmt)[c])
+    c[bad] = 0x38
+    return c
+
+
+def _scales(rng, mode, M, N, K):
+    if mode == oracle.PER_TENSOR:
+        return np.float32(rng.uniform(0.5, 2)), np.float32(rng.uniform(1e-3, 1e-2))
+    sA = np.float32(rng.uniform(0.5, 2, (M, K // 128)))
+    nb = N // 128 if mode == oracle.BLOCK_1x128_128x128 else N
+    return sA, np.float32(rng.uniform(1e-3, 1e-2, (nb, K // 128)))
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("fa,fb", [(E5, E4), (E4, E4)])
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (384, 256, 640), (256, 512, 1536)])
+def test_fp32_output_parity(mode, fa, fb, M, N, K):
+    rng = np.random.default_rng(M + 3 * N + 5 * K + 7 * mode + fa)
+    A = _random_codes(rng, (M, K), fa)
+    B = _random_codes(rng, (N, K), fb)
+    sA, sB = _scales(rng, mode, M, N, K)
+    C, am = _gpu_gemm_f32(A, fa, sA, B, fb, sB, mode)
+    _check(C, am, A, fa, sA, B, fb, sB, mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_fp32_output_exact_small_integers(mode):
+    """Integers in [-4, 4] with power-of-two scales: every partial sum and
+    weight is exact in fp32, so C equals the oracle bit for bit."""
+    rng = np.random.default_rng(11 + mode)
+    M, N, K = 256, 384, 512
+    va = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    vb = rng.integers(-4, 5, (N, K)).astype(np.float32)
+    A, B = oracle.encode(E4, va), oracle.encode(E5, vb)
+    if mode == oracle.PER_TENSOR:
+        sA, sB = np.float32(0.25), np.float32(8.0)
+    else:
+        sA = np.float32(2.0 ** rng.integers(-3, 4, (M, K // 128)))
+        nb = N // 128 if mode == oracle.BLOCK_1x128_128x128 else N
+        sB = np.float32(2.0 ** rng.integers(-3, 4, (nb, K // 128)))
+    C, am = _gpu_gemm_f32(A, E4, sA, B, E5, sB, mode)
+    R = oracle.gemm_reference(A, E4, sA, B, E5, sB, mode)
+    assert np.array_equal(C, R.astype(np.float32))
+    assert f32_bits(am) == f32_bits(np.max(np.abs(C)))
+
+
+def test_wgrad_from_columnwise_copies():
+    """The full weight-gradient recipe at a small size: dY (E5M2) and X (E4M3)
+    are block-quantized by the oracle with their 1x128 columnwise copies, and
+    dW = dY^T X consumes those copies (A = dY^T [Nout][T], B = X^T [Kin][T])."""
+    rng = np.random.default_rng(21)
+    T, Nout, Kin = 512, 384, 256
+    dy = workloads.to_bf16_bits(rng.standard_normal((T, Nout)) * 1e-3)
+    x = workloads.to_bf16_bits(rng.standard_normal((T, Kin)))
+    _, _, dyt, s_dyt = oracle.quantize_block(dy, E5, 1)
+    _, _, xt, s_xt = oracle.quantize_block(x, E4, 1)
+    assert dyt.shape == (Nout, T) and s_dyt.shape == (Nout, T // 128)
+    C, am = _gpu_gemm_f32(dyt, E5, s_dyt, xt, E4, s_xt, fq.BLOCK_1x128_1x128)
+    _check(C, am, dyt, E5, s_dyt, xt, E4, s_xt, oracle.BLOCK_1x128_1x128)
+
+
+def test_bf16_output_with_row_scaled_b():
+    """The 1x128 x 1x128 mode also emits bf16 (tolerance of the bf16 tests)."""
+    rng = np.random.default_rng(23)
+    M, N, K = 256, 384, 384
+    A, B = _random_codes(rng, (M, K), E5), _random_codes(rng, (N, K), E4)
+    sA, sB = _scales(rng, oracle.BLOCK_1x128_1x128, M, N, K)
+    C = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    am = scalar(-1.0)
+    fq.fp8_scaled_gemm(to_dev(A), E5, to_dev(sA.reshape(-1)), to_dev(B), E4, to_dev(sB.reshape(-1)),
+                       fq.BLOCK_1x128_1x128, C, am)
+    Cf = host(C.float())
+    R = oracle.gemm_reference(A, E5, sA, B, E4, sB, oracle.BLOCK_1x128_1x128)
+    assert np.max(np.abs(Cf - R)) <= 1e-2 * np.max(np.abs(R))
+    assert f32_bits(host(am)[0]) == f32_bits(np.max(np.abs(Cf)))
+
+
+def test_wgrad_full_size_sampled():
+    """dW for the MLP block's weight [14336][4096] over 4096 tokens, in the
+    launch configuration the benchmark times, checked at sampled entries."""
+    rng = np.random.default_rng(29)
+    M, N, K = 14336, 4096, 4096
+    A = _random_codes(rng, (M, K), E5)
+    B = _random_codes(rng, (N, K), E4)
+    sA, sB = _scales(rng, oracle.BLOCK_1x128_1x128, M, N, K)
+    C, am = _gpu_gemm_f32(A, E5, sA, B, E4, sB, fq.BLOCK_1x128_1x128)
+    rows = rng.integers(0, M, 48)
+    cols = rng.integers(0, N, 48)
+    rows[:4] = [0, M - 1, 0, M - 1]
+    cols[:4] = [0, N - 1, N - 1, 0]
+    R = oracle.gemm_reference_entries(A, E5, sA, B, E4, sB, rows, cols, oracle.BLOCK_1x128_1x128)
+    for i, (m, n) in enumerate(zip(rows, cols)):
+        S = oracle.gemm_abs_sum(A[m:m + 1], E5, sA[m:m + 1], B[n:n + 1], E4, sB[n:n + 1],
+                                oracle.BLOCK_1x128_1x128)[0, 0]
+        assert abs(float(C[m, n]) - R[i]) <= (MFMA_ADDER + (K + K // 128 + 2) * 2.0 ** -24) * S, (m, n)
+    assert f32_bits(am) == f32_bits(np.max(np.abs(C)))
