@@ -29,7 +29,7 @@ import numpy as np
 E4M3FN, E5M2 = 0, 1
 F32, BF16 = 0, 1
 ALGO_MAX, ALGO_MOST_RECENT = 0, 1
-PER_TENSOR, BLOCK_1x128_128x128, BLOCK_1x128_1x128 = 0, 1, 2
+PER_TENSOR, BLOCK_1x128_128x128, BLOCK_1x128_1x128, MXFP8 = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fp8_oracle.c")
@@ -76,6 +76,7 @@ def _load():
             lib.orc_transpose.argtypes = [vp, i64, i64, i64, vp]
             lib.orc_delayed_update.argtypes = [vp, i32, i32, i32, f32, i64, i32, i32, i32, vp, vp]
             lib.orc_decode_buffer.argtypes = [vp, i32, i64, vp]
+            lib.orc_quantize_mx.argtypes = [vp, i32, i64, i64, i32, vp, vp]
             lib.orc_num_threads.restype = i32
             _lib = lib
     return _lib
@@ -241,12 +242,46 @@ def delayed_update(hist: np.ndarray, col: int, new_amax, step: int, fmt: int, ma
 
 
 # -------------------------------------------------------------------- GEMM ---
+def quantize_mx(x: np.ndarray, fmt: int):
+    """MXFP8 of a 2-D tensor along its rows ("Megatron FP8", sections 10 and 16:
+    32 consecutive elements share one E8M0 power-of-two scale): returns
+    (codes [rows][cols], scale bytes [rows][cols/32]).  See orc_quantize_mx for
+    the shared-exponent rule."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    q = np.empty((rows, cols), dtype=np.uint8)
+    sc = np.empty((rows, cols // 32), dtype=np.uint8)
+    _load().orc_quantize_mx(_ptr(x), _dtype_of(x), rows, cols, fmt, _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def quantize_mx_colwise(x: np.ndarray, fmt: int):
+    """The columnwise MXFP8 copy: the same rule applied to x^T (blocks of 32
+    consecutive rows of one column), as [cols][rows] codes and [cols][rows/32]
+    scale bytes."""
+    return quantize_mx(np.ascontiguousarray(np.asarray(x).T), fmt)
+
+
+def e8m0_value(b) -> np.ndarray:
+    """float64 value of E8M0 scale bytes: 2^(b - 127), NaN for 255."""
+    b = np.asarray(b).astype(np.int64)
+    v = np.ldexp(1.0, b - 127)
+    return np.where(b == 255, np.nan, v)
+
+
 def decode_codes(q: np.ndarray, fmt: int) -> np.ndarray:
     """float64 values of a code buffer."""
     q = np.ascontiguousarray(q, dtype=np.uint8)
     out = np.empty(q.shape, dtype=np.float64)
     _load().orc_decode_buffer(_ptr(q), fmt, q.size, _ptr(out))
     return out
+
+
+def _mx_scaled(v: np.ndarray, scale_bytes) -> np.ndarray:
+    """Element values times their block's E8M0 scale (32 per scale, along K)."""
+    return v * np.repeat(e8m0_value(scale_bytes), 32, axis=1)
 
 
 def _block_weight(sA, sB, mode, M, N, kb):
@@ -269,6 +304,8 @@ def gemm_reference(A: np.ndarray, fa: int, sA, B: np.ndarray, fb: int, sB, mode:
     where sB is [N/128][K/128] (128x128 blocks of B, indexed by n // 128) or
     [N][K/128] (1x128 blocks of B, indexed by n: the weight-gradient GEMM,
     whose operands are both the transposed, token-contiguous copies).
+    MXFP8: sA [M][K/32] and sB [N][K/32] are E8M0 bytes and every element is
+    multiplied by its block's power of two before the products are summed.
 
     "Megatron FP8", section 27: products are promoted and summed at full
     precision and only the finished dot product is rounded to the output type;
@@ -279,6 +316,8 @@ def gemm_reference(A: np.ndarray, fa: int, sA, B: np.ndarray, fb: int, sB, mode:
     b = decode_codes(B, fb)
     if mode == PER_TENSOR:
         return (a @ b.T) * (float(np.float32(sA)) * float(np.float32(sB)))
+    if mode == MXFP8:
+        return _mx_scaled(a, sA) @ _mx_scaled(b, sB).T
     M, K = a.shape
     N = b.shape[0]
     R = np.zeros((M, N), dtype=np.float64)
@@ -297,6 +336,8 @@ def gemm_abs_sum(A: np.ndarray, fa: int, sA, B: np.ndarray, fb: int, sB, mode: i
     b = np.abs(decode_codes(B, fb))
     if mode == PER_TENSOR:
         return (a @ b.T) * abs(float(np.float32(sA)) * float(np.float32(sB)))
+    if mode == MXFP8:
+        return _mx_scaled(a, sA) @ _mx_scaled(b, sB).T
     M, K = a.shape
     N = b.shape[0]
     S = np.zeros((M, N), dtype=np.float64)
@@ -322,6 +363,10 @@ def gemm_reference_entries(A: np.ndarray, fa: int, sA, B: np.ndarray, fb: int, s
         bv = tb[B[n]]
         if mode == PER_TENSOR:
             out[i] = float(np.dot(av, bv)) * (float(np.float32(sA)) * float(np.float32(sB)))
+        elif mode == MXFP8:
+            ea = np.repeat(e8m0_value(sA[m]), 32)
+            eb = np.repeat(e8m0_value(sB[n]), 32)
+            out[i] = float(np.dot(av * ea, bv * eb))
         else:
             acc = 0.0
             nb = n // 128 if mode == BLOCK_1x128_128x128 else n

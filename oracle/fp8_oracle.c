@@ -317,6 +317,55 @@ void orc_delayed_update(float *hist, int history_len, int n_cols, int col, float
     scale[col] = 1.0f / s;
 }
 
+/* MXFP8 ([MFP8] sections 10 and 16; the OCP Microscaling format the pages
+ * name): every 32 consecutive elements of a row share one E8M0 scale, a
+ * power of two 2^(b - 127) stored as the byte b (0..254; 255 is NaN), and each
+ * element is an E4M3FN or E5M2 code.  The pages do not spell out how the
+ * shared exponent is chosen; the reading here is the OCP rule: the largest
+ * power of two not above the block's amax, divided by the format's largest
+ * power of two (2^8 for E4M3FN, 2^15 for E5M2), so that the block's largest
+ * element lands in the format's top binade:
+ *   e = floor(log2(amax)) - emax, clamped to [-127, 127]; b = e + 127;
+ *   q = encode(fl32(x * 2^-e)).
+ * An all-zero block takes e = -127.  A NaN amax gives b = 255 and NaN codes
+ * (x times NaN).  An infinite amax clamps e to 127. */
+void orc_quantize_mx(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t *q, uint8_t *scales)
+{
+    const int emax = fmt == ORC_E4M3FN ? 8 : 15;
+    const int64_t nblk = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t bj = 0; bj < nblk; ++bj) {
+            const int64_t j0 = bj * 32;
+            float a = 0.0f;
+            int saw_nan = 0;
+            for (int64_t j = j0; j < j0 + 32; ++j) {
+                const float v = load_elem(x, dtype, i * cols + j);
+                if (isnan(v)) saw_nan = 1;
+                else if (fabsf(v) > a) a = fabsf(v);
+            }
+            int e;
+            float mult;
+            if (saw_nan) {
+                scales[i * nblk + bj] = 255;
+                mult = canonical_nan();
+            } else {
+                if (a == 0.0f) e = -127;
+                else if (isinf(a)) e = 127;
+                else {
+                    e = ilogbf(a) - emax; /* floor(log2(a)), subnormal a included */
+                    if (e < -127) e = -127;
+                    if (e > 127) e = 127;
+                }
+                scales[i * nblk + bj] = (uint8_t)(e + 127);
+                mult = ldexpf(1.0f, -e); /* exact: 2^-127 .. 2^127 */
+            }
+            for (int64_t j = j0; j < j0 + 32; ++j)
+                q[i * cols + j] = encode_product(fmt, load_elem(x, dtype, i * cols + j), mult);
+        }
+    }
+}
+
 /* Decode a whole code buffer to binary64 (the GEMM reference's operands). */
 void orc_decode_buffer(const uint8_t *q, int fmt, int64_t n, double *out)
 {

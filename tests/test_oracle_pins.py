@@ -513,3 +513,104 @@ def test_nan_product_sign_rule():
     assert list(oracle.quantize(x, E4, np.float32(0.0))) == [0x7F, 0xFF, 0x00, 0xFF, 0x7F, 0x80]
     assert list(oracle.quantize(x, E5, nan)) == [0x7F, 0xFF, 0x7F, 0xFF, 0x7F, 0xFF]
     assert list(oracle.quantize(x, E4, np.float32(-1.0))) == [0xFE, 0x7E, 0xB8, 0x7F, 0xFF, 0x40]
+
+
+# ---------------------------------------------------------------- MXFP8 pins --
+def test_e8m0_scale_values():
+    """E8M0 ("Megatron FP8", sections 10 and 16): an unsigned exponent byte, no
+    mantissa, no sign; powers of two from 2^-127 to 2^127; 255 is NaN."""
+    v = oracle.e8m0_value(np.arange(256))
+    assert v[0] == 2.0 ** -127 and v[127] == 1.0 and v[254] == 2.0 ** 127
+    assert np.isnan(v[255])
+    assert np.all(v[1:255] == 2 * v[0:254])
+
+
+def test_mx_scale_overhead_page_example():
+    """Section 16's count: 1,048,576 FP8 elements carry 32,768 scale bytes
+    (one per 32), 1,081,344 bytes in all (3.125% metadata)."""
+    x = np.float32(np.random.default_rng(40).standard_normal((1024, 1024)))
+    q, sc = oracle.quantize_mx(x, E4)
+    assert q.size == 1048576 and sc.size == 32768 and q.nbytes + sc.nbytes == 1081344
+
+
+@pytest.mark.parametrize("fmt,emax,mbits", [(E4, 8, 3), (E5, 15, 2)])
+def test_mx_block_max_in_top_binade_and_error_bound(fmt, emax, mbits):
+    """Every block's largest element lands in the format's top binade
+    [2^emax, 2^(emax+1)) after scaling (so the block uses the format's whole
+    range), and every element reconstructs within half a unit in the last place
+    of its binade (2^-(m+1) relative, section 24's bound), or saturates at
+    FP8_MAX, which only the top binade's values above FP8_MAX do."""
+    rng = np.random.default_rng(41 + fmt)
+    x64 = rng.standard_normal((64, 256)) * np.exp(rng.uniform(-20, 20, (64, 1)))
+    x = np.float32(x64)
+    q, sc = oracle.quantize_mx(x, fmt)
+    tab = oracle.decode_table(fmt)
+    fmax = oracle.fmax(fmt)
+    e = sc.astype(np.int64) - 127
+    xs = x.astype(np.float64) * np.ldexp(1.0, -np.repeat(e, 32, axis=1))  # exact scaled values
+    blk_max = np.abs(xs).reshape(64, 8, 32).max(axis=2)
+    assert np.all((blk_max >= 2.0 ** emax) & (blk_max < 2.0 ** (emax + 1)))
+    dec = tab[q]
+    sat = np.abs(xs) > fmax
+    assert np.all(np.abs(dec[sat]) == fmax)
+    normal = (~sat) & (np.abs(xs) >= 2.0 ** (1 - (7 if fmt == E4 else 15)))
+    binade = np.ldexp(1.0, np.floor(np.log2(np.abs(xs[normal]))).astype(int))
+    assert np.all(np.abs(dec[normal] - xs[normal]) <= binade * 2.0 ** -(mbits + 1))
+    sub = (~sat) & ~normal
+    step = 2.0 ** ((1 - (7 if fmt == E4 else 15)) - mbits)
+    assert np.all(np.abs(dec[sub] - xs[sub]) <= step / 2)
+
+
+def test_mx_special_blocks():
+    """All-zero block: scale 2^-127 (byte 0), codes 0.  A block of one power of
+    two 2^k: scale 2^(k - emax), every code the format's 2^emax (0x78 in both
+    formats).  A NaN in the block: NaN scale byte and NaN codes."""
+    x = np.zeros((3, 64), np.float32)
+    x[1, :32] = 2.0 ** 5
+    x[1, 32:] = -(2.0 ** -30)
+    x[2, :32] = np.float32(1.5)
+    x[2, 7] = np.nan
+    for fmt, emax in ((E4, 8), (E5, 15)):
+        q, sc = oracle.quantize_mx(x, fmt)
+        assert list(sc[0]) == [0, 0] and not q[0].any()
+        assert sc[1, 0] == 5 - emax + 127 and np.all(q[1, :32] == 0x78)
+        assert sc[1, 1] == -30 - emax + 127 and np.all(q[1, 32:] == 0xF8)
+        assert sc[2, 0] == 255 and np.all((q[2, :32] & 0x7F) == 0x7F)
+
+
+def test_mx_colwise_is_rowwise_of_transpose():
+    x = np.float32(np.random.default_rng(42).standard_normal((64, 96)))
+    qc, sc = oracle.quantize_mx_colwise(x, E5)
+    qt, st = oracle.quantize_mx(np.ascontiguousarray(x.T), E5)
+    assert np.array_equal(qc, qt) and np.array_equal(sc, st) and qc.shape == (96, 64)
+
+
+def test_gemm_reference_mx():
+    """MXFP8 GEMM: unit scales (byte 127) reduce to the unscaled product;
+    brute force on a tiny case; a power-of-two scale on one block of A scales
+    exactly that block's contribution."""
+    rng = np.random.default_rng(43)
+    M, N, K = 3, 4, 96
+    A = _random_codes(rng, (M, K), E4)
+    B = _random_codes(rng, (N, K), E5)
+    ones_a = np.full((M, K // 32), 127, np.uint8)
+    ones_b = np.full((N, K // 32), 127, np.uint8)
+    R1 = oracle.gemm_reference(A, E4, ones_a, B, E5, ones_b, oracle.MXFP8)
+    assert np.array_equal(R1, oracle.gemm_reference(A, E4, 1.0, B, E5, 1.0))
+    sa = rng.integers(110, 140, (M, K // 32)).astype(np.uint8)
+    sb = rng.integers(110, 140, (N, K // 32)).astype(np.uint8)
+    R = oracle.gemm_reference(A, E4, sa, B, E5, sb, oracle.MXFP8)
+    ta, tb = oracle.decode_table(E4), oracle.decode_table(E5)
+    for m in range(M):
+        for n in range(N):
+            ref = sum(ta[A[m, k]] * 2.0 ** (int(sa[m, k // 32]) - 127) * tb[B[n, k]] * 2.0 ** (int(sb[n, k // 32]) - 127)
+                      for k in range(K))
+            assert np.isclose(R[m, n], ref, rtol=1e-12, atol=0)
+    ent = oracle.gemm_reference_entries(A, E4, sa, B, E5, sb, [2, 0], [3, 1], oracle.MXFP8)
+    assert np.allclose(ent, R[[2, 0], [3, 1]], rtol=1e-12, atol=0)
+    sa2 = sa.copy()
+    sa2[1, 2] += 3
+    R2 = oracle.gemm_reference(A, E4, sa2, B, E5, sb, oracle.MXFP8)
+    part = oracle.gemm_reference(A[:, 64:96], E4, sa[:, 2:3], B[:, 64:96], E5, sb[:, 2:3], oracle.MXFP8)
+    assert np.allclose(R2[1] - R[1], 7 * part[1], rtol=1e-12, atol=1e-300)
+    assert np.array_equal(R2[[0, 2]], R[[0, 2]])
