@@ -23,7 +23,7 @@ import torch
 E4M3FN, E5M2 = 0, 1
 F32, BF16 = 0, 1
 ALGO_MAX, ALGO_MOST_RECENT = 0, 1
-PER_TENSOR, BLOCK_1x128_128x128, BLOCK_1x128_1x128 = 0, 1, 2
+PER_TENSOR, BLOCK_1x128_128x128, BLOCK_1x128_1x128, MXFP8 = 0, 1, 2, 3
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

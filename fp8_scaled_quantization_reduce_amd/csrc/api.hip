@@ -303,7 +303,8 @@ int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t
 {
     const char *fn = "fp8_scaled_gemm";
     if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(FP8Q_EINVAL, "%s: unknown operand format", fn);
-    if (mode != FP8Q_PER_TENSOR && mode != FP8Q_BLOCK_1x128_128x128 && mode != FP8Q_BLOCK_1x128_1x128)
+    if (mode != FP8Q_PER_TENSOR && mode != FP8Q_BLOCK_1x128_128x128 && mode != FP8Q_BLOCK_1x128_1x128 &&
+        mode != FP8Q_MXFP8)
         return fail(FP8Q_EINVAL, "%s: unknown scaling mode %d", fn, (int)mode);
     if (!valid_dtype(c_dtype)) return fail(FP8Q_EINVAL, "%s: unknown output dtype %d", fn, (int)c_dtype);
     if (M < 0 || N < 0 || K < 0) return fail(FP8Q_EINVAL, "%s: negative shape", fn);

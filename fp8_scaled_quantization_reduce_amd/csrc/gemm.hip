@@ -159,10 +159,29 @@ __device__ __forceinline__ v8i read_frag32(const uint8_t *lds, int r, int g, int
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
+// MXFP8 layout of the same 32 rows x 64 K bytes.  The scaled instruction's
+// K order puts bytes 0..15 of lane (r, g) at K 16g .. 16g+15 of the half step
+// and bytes 16..31 at K 32 + 16g .. 32 + 16g + 15, and takes the scale of K
+// block b (32 elements) of row r from lane r + 32b (measured on the MI355X with
+// unit codes and one scaled lane at a time).  So lane (r, g) reads logical
+// chunks 4h + g and 4h + 2 + g, and supplies the scale of block 2h + g.
+__device__ __forceinline__ v8i read_frag32_mx(const uint8_t *lds, int r, int g, int h)
+{
+    const uint4 lo = *reinterpret_cast<const uint4 *>(lds + swz(r, 4 * h + g));
+    const uint4 hi = *reinterpret_cast<const uint4 *>(lds + swz(r, 4 * h + 2 + g));
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
 // The two stages are distinct LDS objects addressed with compile-time stage
 // numbers (the slice loop is unrolled by two), so the compiler can tell a
 // read of one stage from the direct loads landing in the other.
-template <int FA, int FB, bool kAmax, bool kF32>
+// With kMX (MXFP8), sA and sB point to E8M0 scale bytes, [M][K/32] and
+// [N][K/32]: every 32-element K block of a row carries a power of two that the
+// matrix instruction applies itself (v_mfma_scale_f32_32x32x64_f8f6f4 takes one
+// scale byte per lane, for the 32 K bytes that lane holds).  Each stage also
+// carries the slice's four scale bytes of every A and B row (one dword per row,
+// loaded straight into LDS with the codes).
+template <int FA, int FB, bool kAmax, bool kF32, bool kMX>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t *__restrict__ A,
                                                                   const uint8_t *__restrict__ B,
                                                                   const float *__restrict__ sA,
@@ -171,7 +190,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
 {
     __shared__ __attribute__((aligned(1024))) uint8_t st0[kPTStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[kPTStageBytes];
+    __shared__ __attribute__((aligned(16))) uint32_t sx0[kMX ? 2 * kBM : 1]; // A rows' then B rows' scale dwords
+    __shared__ __attribute__((aligned(16))) uint32_t sx1[kMX ? 2 * kBM : 1];
     __shared__ uint32_t red[kGemmThreads / 64];
+    constexpr int kStageLoads = kMX ? 18 : 16; // direct loads per lane per stage
 
     int tm, tn;
     tile_of_block(blockIdx.x, (M + kBM - 1) / kBM, (N + kBM - 1) / kBM, tm, tn);
@@ -191,8 +213,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     // which holds logical chunk (L % 8) ^ ((row >> 1) & 7) = (L % 8) ^ ((4w + L / 16) & 7)
     const int voff = (lane >> 3) * K + (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4);
 
+    // MXFP8 scale rows: K/32 bytes per row; the slice's 4 bytes are one dword
+    const int kx = K / 32;
+    const __amdgpu_buffer_rsrc_t rxa = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(reinterpret_cast<const uint8_t *>(sA) + (kMX ? m0 * kx : 0)), 0, kMX ? (int)(a_rows * kx) : 4,
+        kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rxb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(reinterpret_cast<const uint8_t *>(sB) + (kMX ? n0 * kx : 0)), 0, kMX ? (int)(b_rows * kx) : 4,
+        kRawBufferWord3);
+
     // wave w loads rows 8(w + 4u), u = 0..7, of both panels: 16 loads of 1 KiB
-    auto stage = [&](uint8_t *st, int kb) {
+    // (and, MXFP8, the scale dwords of rows 64w .. 64w+63 of both panels)
+    auto stage = [&](uint8_t *st, uint32_t *sx, int kb) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int row = 8 * (w + 4 * u);
@@ -200,6 +232,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
                                                      0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + kBM * kBK + row * kBK), 16, voff,
                                                      row * K + kb * kBK, 0, 0);
+        }
+        if constexpr (kMX) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxa, (lds_void *)(sx + 64 * w), 4, lane * kx,
+                                                     64 * w * kx + 4 * kb, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxb, (lds_void *)(sx + kBM + 64 * w), 4, lane * kx,
+                                                     64 * w * kx + 4 * kb, 0, 0);
         }
     };
 
@@ -212,24 +250,53 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     v8i fa0[4], fb0[4], fa1[4], fb1[4]; // first-half and second-half fragments
+    // MXFP8: the scale dwords of the lane's A rows (i) and B rows (j) for the
+    // current slice and the next one, pre-shifted by 8 * fg bytes so that byte
+    // 0 is the scale of this lane's K block in half 0 and byte 2 in half 1
+    uint32_t xa0[4], xb0[4], xa1[4], xb1[4];
     auto read_frags = [&](const uint8_t *st, int h, v8i(&a)[4], v8i(&b)[4]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = read_frag32(st + kBM * kBK, wn * 128 + 32 * j + fr, fg, h);
+        for (int j = 0; j < 4; ++j)
+            b[j] = kMX ? read_frag32_mx(st + kBM * kBK, wn * 128 + 32 * j + fr, fg, h)
+                       : read_frag32(st + kBM * kBK, wn * 128 + 32 * j + fr, fg, h);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = read_frag32(st, wm * 128 + 32 * i + fr, fg, h);
+        for (int i = 0; i < 4; ++i)
+            a[i] = kMX ? read_frag32_mx(st, wm * 128 + 32 * i + fr, fg, h) : read_frag32(st, wm * 128 + 32 * i + fr, fg, h);
     };
-    auto mfmas = [&](const v8i(&a)[4], const v8i(&b)[4]) {
+    auto read_scales = [&](const uint32_t *sx, uint32_t(&xa)[4], uint32_t(&xb)[4]) {
+        if constexpr (kMX) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xa[i] = sx[wm * 128 + 32 * i + fr] >> (8 * fg);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xb[j] = sx[kBM + wn * 128 + 32 * j + fr] >> (8 * fg);
+        }
+    };
+    // half h of the slice whose scale dwords are xa / xb
+    auto mfmas = [&](const v8i(&a)[4], const v8i(&b)[4], const uint32_t(&xa)[4], const uint32_t(&xb)[4], int h) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x64<FB, FA>(b[j], a[i], acc[i][j]);
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (kMX) {
+                    if (h == 0)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], FB, FA, 0,
+                                                                                    (int)xb[j], 0, (int)xa[i]);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], FB, FA, 2,
+                                                                                    (int)xb[j], 2, (int)xa[i]);
+                } else {
+                    acc[i][j] = mfma32x32x64<FB, FA>(b[j], a[i], acc[i][j]);
+                }
+            }
     };
 
     // One slice in stage `cur` (the next one in `nxt`).  `full` = the slices
     // kb + 1 and kb + 2 both exist (no guards).
-    auto slice = [&](int kb, const uint8_t *cur, uint8_t *nxt_load, const uint8_t *nxt, bool full) {
+    auto slice = [&](int kb, uint8_t *cur, uint32_t *sxc, const uint8_t *nxt, const uint32_t *sxn,
+                     const uint32_t(&xa)[4], const uint32_t(&xb)[4], uint32_t(&xan)[4], uint32_t(&xbn)[4],
+                     bool full) {
         // half 0
-        mfmas(fa0, fb0);
+        mfmas(fa0, fb0, xa, xb, 0);
         read_frags(cur, 1, fa1, fb1);
         if (full) {
 #pragma unroll
@@ -243,9 +310,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         // half 1
-        if (full || kb + 2 < nk) stage(const_cast<uint8_t *>(cur), kb + 2);
-        mfmas(fa1, fb1);
-        if (full || kb + 1 < nk) read_frags(nxt, 0, fa0, fb0);
+        if (full || kb + 2 < nk) stage(cur, sxc, kb + 2);
+        mfmas(fa1, fb1, xa, xb, 1);
+        if (full || kb + 1 < nk) {
+            read_frags(nxt, 0, fa0, fb0);
+            read_scales(sxn, xan, xbn);
+        }
         if (full) {
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
@@ -254,7 +324,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global -> LDS load
             }
         }
-        (void)nxt_load;
     };
 
     // prologue: slices 0 and 1 in flight, slice 0's first-half fragments.
@@ -263,26 +332,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     // an unconditional pair the compiler's wait insertion keeps the two stages
     // apart and puts no full wait at the top of the loop.
     if (nk > 0) {
-        stage(st0, 0);
-        stage(st1, 1);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(16, 15));
+        stage(st0, sx0, 0);
+        stage(st1, sx1, 1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(kStageLoads, 15));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         read_frags(st0, 0, fa0, fb0);
+        read_scales(sx0, xa0, xb0);
     }
     int kb = 0;
     for (; kb + 4 <= nk; kb += 2) {
-        slice(kb, st0, st0, st1, true);
-        slice(kb + 1, st1, st1, st0, true);
+        slice(kb, st0, sx0, st1, sx1, xa0, xb0, xa1, xb1, true);
+        slice(kb + 1, st1, sx1, st0, sx0, xa1, xb1, xa0, xb0, true);
     }
     // at most three slices remain; kb is even
-    if (kb < nk) slice(kb, st0, st0, st1, false);
-    if (kb + 1 < nk) slice(kb + 1, st1, st1, st0, false);
-    if (kb + 2 < nk) slice(kb + 2, st0, st0, st1, false);
+    if (kb < nk) slice(kb, st0, sx0, st1, sx1, xa0, xb0, xa1, xb1, false);
+    if (kb + 1 < nk) slice(kb + 1, st1, sx1, st0, sx0, xa1, xb1, xa0, xb0, false);
+    if (kb + 2 < nk) slice(kb + 2, st0, sx0, st1, sx1, xa0, xb0, xa1, xb1, false);
 
     // epilogue: lane (fr, fg) of 32x32 tile (i, j) holds C[row][4 consecutive
     // columns 8q + 4fg .. +3] for q = 0..3
-    const float alpha = (*sA) * (*sB);
+    const float alpha = kMX ? 1.0f : (*sA) * (*sB);
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -528,9 +598,14 @@ static hipError_t launch_gemm_t(const uint8_t *A, const float *sA, const uint8_t
     const int m = (int)M, n = (int)N, k = (int)K;
     if (mode == 0) {
         if (amax_out)
-            gemm_pt_kernel<FA, FB, true, kF32><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
+            gemm_pt_kernel<FA, FB, true, kF32, false><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
         else
-            gemm_pt_kernel<FA, FB, false, kF32><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
+            gemm_pt_kernel<FA, FB, false, kF32, false><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
+    } else if (mode == 3) {
+        if (amax_out)
+            gemm_pt_kernel<FA, FB, true, kF32, true><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
+        else
+            gemm_pt_kernel<FA, FB, false, kF32, true><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
     } else if (mode == 1) {
         if (amax_out)
             gemm_bs_kernel<FA, FB, true, kF32, false><<<grid, kBSThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);

@@ -63,6 +63,7 @@ extern "C" {
 #define FP8Q_PER_TENSOR 0
 #define FP8Q_BLOCK_1x128_128x128 1
 #define FP8Q_BLOCK_1x128_1x128 2
+#define FP8Q_MXFP8 3
 
 /*
  * fp8_amax -- *amax = max_i |x_i| over n elements ([MFP8] section 4, the
@@ -200,6 +201,11 @@ int fp8_quantize_delayed(const void *x, int32_t dtype, int64_t n, int32_t fmt, f
  *   mode FP8Q_BLOCK_1x128_1x128: as above with sB [N][K/128] (1x128 blocks
  *        of B, one scale per row of B and K slice), the weight gradient from
  *        the transposed (token-contiguous) copies of dY and X.
+ *   mode FP8Q_MXFP8 ([MFP8] sections 10 and 16): sA [M][K/32] and sB
+ *        [N][K/32] are E8M0 scale bytes (const uint8_t data passed through the
+ *        float pointers), one per 32-element block along K; every element is
+ *        multiplied by 2^(byte - 127) of its block (by the matrix instruction
+ *        itself) and C = out(acc).
  *   out() is bf16 round-to-nearest-even or the fp32 value itself.
  *   amax_out (nullable) receives max |C| over the emitted values.
  * M, N, K must be multiples of 128 (FP8Q_EUNSUPPORTED otherwise).

@@ -45,6 +45,7 @@ def test_enum_values_match_header():
     assert int(defs["FP8Q_PER_TENSOR"]) == fq.PER_TENSOR
     assert int(defs["FP8Q_BLOCK_1x128_128x128"]) == fq.BLOCK_1x128_128x128 == oracle.BLOCK_1x128_128x128
     assert int(defs["FP8Q_BLOCK_1x128_1x128"]) == fq.BLOCK_1x128_1x128 == oracle.BLOCK_1x128_1x128
+    assert int(defs["FP8Q_MXFP8"]) == fq.MXFP8 == oracle.MXFP8
 
 
 def _expect(status, code, fragment):
@@ -126,7 +127,7 @@ def test_gemm_validation():
     g = L.fp8_scaled_gemm
     A, B, C = BAD + 0x100000, BAD + 0x200000, BAD + 0x300000
     _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 0, C, 7, None, S), fq.EINVAL, "dtype")
-    _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 3, C, fq.F32, None, S), fq.EINVAL, "mode")
+    _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 4, C, fq.F32, None, S), fq.EINVAL, "mode")
     # an fp32 C of 128x128 spans 64 KiB: one that starts 32 KiB before B overlaps it
     _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 2, B - 0x8000, fq.F32, None, S), fq.EINVAL, "overlaps")
     _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 100, 128, 0, C, fq.BF16, None, S), fq.EUNSUPPORTED, "multiples")

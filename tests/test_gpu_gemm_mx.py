@@ -1,0 +1,78 @@
+"""GPU parity of the MXFP8 GEMM ("Megatron FP8", sections 10 and 16: 1x32
+blocks along K with E8M0 power-of-two scales, applied by the matrix
+instruction).  Operands and scale bytes come from the oracle.  Bars: the fp32
+bound of the weight-gradient tests (the scales are powers of two, so every
+weighted term is exact and the only errors are the instruction's adder and
+fp32 summation), 1e-2 * max |R| for bf16, bit-exact small-integer cases, and
+amax == max |C|."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import f32_bits, host, scalar, to_dev
+
+pytestmark = pytest.mark.gpu
+
+fq = pytest.importorskip("fp8_scaled_quantization_reduce_amd")
+E4, E5 = oracle.E4M3FN, oracle.E5M2
+MFMA_ADDER = 2.0 ** -11
+
+
+def _gemm(A, fa, sA, B, fb, sB, dtype):
+    M, N = A.shape[0], B.shape[0]
+    C = torch.full((M, N), 3.0, dtype=dtype, device="cuda")
+    am = scalar(-1.0)
+    fq.fp8_scaled_gemm(to_dev(A), fa, to_dev(np.ascontiguousarray(sA)), to_dev(B), fb,
+                       to_dev(np.ascontiguousarray(sB)), fq.MXFP8, C, am)
+    return host(C.float()), host(am)[0]
+
+
+def _mx_operands(rng, M, N, K, fa, fb):
+    xa = workloads.to_bf16_bits(rng.standard_normal((M, K)) * np.exp(rng.uniform(-4, 4, (M, 1))))
+    xb = workloads.to_bf16_bits(rng.standard_normal((N, K)) * np.exp(rng.uniform(-4, 4, (N, K // 32))).repeat(32, 1))
+    qa, sa = oracle.quantize_mx(xa, fa)
+    qb, sb = oracle.quantize_mx(xb, fb)
+    return qa, sa, qb, sb
+
+
+@pytest.mark.parametrize("fa,fb", [(E4, E4), (E5, E4), (E4, E5), (E5, E5)])
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (384, 256, 640), (256, 512, 1536)])
+def test_mx_gemm_fp32_parity(fa, fb, M, N, K):
+    rng = np.random.default_rng(M + 7 * N + 3 * K + 11 * fa + fb)
+    qa, sa, qb, sb = _mx_operands(rng, M, N, K, fa, fb)
+    C, am = _gemm(qa, fa, sa, qb, fb, sb, torch.float32)
+    R = oracle.gemm_reference(qa, fa, sa, qb, fb, sb, oracle.MXFP8)
+    S = oracle.gemm_abs_sum(qa, fa, sa, qb, fb, sb, oracle.MXFP8)
+    err = np.abs(C.astype(np.float64) - R)
+    bound = (MFMA_ADDER + (K + 2) * 2.0 ** -24) * S
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), (worst, err[worst], bound[worst])
+    assert f32_bits(am) == f32_bits(np.max(np.abs(C)))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (512, 384, 1024)])
+def test_mx_gemm_bf16_parity(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    qa, sa, qb, sb = _mx_operands(rng, M, N, K, E4, E4)
+    C, am = _gemm(qa, E4, sa, qb, E4, sb, torch.bfloat16)
+    R = oracle.gemm_reference(qa, E4, sa, qb, E4, sb, oracle.MXFP8)
+    assert np.max(np.abs(C - R)) <= 1e-2 * np.max(np.abs(R))
+    assert f32_bits(am) == f32_bits(np.max(np.abs(C)))
+
+
+def test_mx_gemm_scales_apply_per_32_block_exactly():
+    """Unit codes with a different power-of-two scale on every 32-element block
+    of A and B: every product and sum is exact, so C must equal the oracle bit
+    for bit; a wrong block-to-lane assignment of the scales would not."""
+    rng = np.random.default_rng(5)
+    M, N, K = 256, 256, 512
+    va = rng.integers(-1, 2, (M, K)).astype(np.float32)
+    vb = rng.integers(-1, 2, (N, K)).astype(np.float32)
+    A, B = oracle.encode(E4, va), oracle.encode(E4, vb)
+    sa = rng.integers(124, 131, (M, K // 32)).astype(np.uint8)
+    sb = rng.integers(124, 131, (N, K // 32)).astype(np.uint8)
+    C, am = _gemm(A, E4, sa, B, E4, sb, torch.float32)
+    R = oracle.gemm_reference(A, E4, sa, B, E4, sb, oracle.MXFP8)
+    assert np.array_equal(C, R.astype(np.float32))
