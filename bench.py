@@ -16,8 +16,9 @@ uses that same per-step duration.
 
 Every other row of the hot path (amax, current scaling, dequantize, rowwise +
 columnwise, 128x128 and 1x128 block quantization, per-tensor and block-scaled
-GEMMs, and the fp32-output weight-gradient GEMM) is timed at its own workload
-size and reported under "rows".
+GEMMs, and the next rows: the fp32-output weight-gradient GEMM, MXFP8
+quantization and the MXFP8 GEMM) is timed at its own workload size and
+reported under "rows".
 
 The CPU oracle is timed on the host cores on a bounded sample of the same
 workload ("cpu_baseline").
@@ -262,7 +263,14 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream):
     ms = _time(torch, stream, lambda i: fq.fp8_quantize_block(Xs[i], E4, 1, qx[i], sx, qxt[i], sxt, stream=stream),
                20, rotate=len(Xs))
     out["block1x128_bf16_4096x7168_with_colwise"] = gbs(4 * nW + 4 * (nW // 128) * 2, ms)
-    del Ws, Xs, W, X, qw, qwt, qx, qxt, qs8, qr, qc, ys
+    # next: MXFP8 quantization of 8192^2 bf16 with the columnwise copy
+    # (2 + 1 + 1 B/elem + 2 scale bytes per 32 elements)
+    sm = [torch.empty((8192, 256), dtype=torch.uint8, device=dev) for _ in range(4)]
+    smt = [torch.empty((8192, 256), dtype=torch.uint8, device=dev) for _ in range(4)]
+    ms = _time(torch, stream, lambda i: fq.fp8_quantize_mx(x2[i], E4, qr[i % 4], sm[i % 4], qc[i % 4], smt[i % 4],
+                                                           stream=stream), 20, rotate=len(xs))
+    out["mxfp8_bf16_8192x8192_with_colwise"] = gbs(4 * n + 2 * n // 32, ms)
+    del Ws, Xs, W, X, qw, qwt, qx, qxt, qs8, qr, qc, ys, sm, smt
 
     def tflops(flop, ms):
         tf = flop / (ms * 1e-3) / 1e12
@@ -324,6 +332,24 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream):
     ms = _time(torch, stream, lambda i: fq.fp8_scaled_gemm(dYt, E5, sdyt, Xt, E4, sxt, fq.BLOCK_1x128_1x128, dW,
                                                             cam, stream=stream), 10)
     out["gemm_block_wgrad_14336x4096x4096_fp32out"] = tflops(2 * 14336 * 4096 * 4096, ms)
+    del dYt, Xt, dW
+
+    # next: MXFP8 GEMM 8192^3 (E8M0 scales per 32 along K, applied by the
+    # matrix instruction), operands from the library's MXFP8 quantization
+    def mx_codes(shape):
+        x = torch.randn(shape, device=dev, generator=g).to(torch.bfloat16)
+        c = torch.empty(shape, dtype=torch.uint8, device=dev)
+        e = torch.empty((shape[0], shape[1] // 32), dtype=torch.uint8, device=dev)
+        fq.fp8_quantize_mx(x, E4, c, e, stream=stream)
+        del x
+        return c, e
+
+    Am, sAm = mx_codes((8192, 8192))
+    Bm, sBm = mx_codes((8192, 8192))
+    Cm = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+    ms = _time(torch, stream, lambda i: fq.fp8_scaled_gemm(Am, E4, sAm, Bm, E4, sBm, fq.MXFP8, Cm, cam,
+                                                            stream=stream), 10)
+    out["gemm_mxfp8_e4m3_8192x8192x8192"] = tflops(2 * 8192 ** 3, ms)
     return out
 
 

@@ -6,7 +6,7 @@ the names of the C entry points in ``include/fp8q.h`` and only marshal torch
 tensors (device memory) and the current HIP stream into them.  Every step of
 the computation runs in the library's HIP kernels; there is no Python or CPU
 fallback.  Importing the package fails if the library has not been built
-(``python -m fp8_scaled_quantization_reduce_amd.build``).
+(``python fp8_scaled_quantization_reduce_amd/build.py``).
 
 Tensor conventions: high-precision inputs are ``torch.float32`` or
 ``torch.bfloat16``; FP8 codes are ``torch.uint8``; scalars (amax, scales) are
@@ -37,6 +37,7 @@ SIGNATURES = {
     "fp8_dequantize": [_VP, _I32, _I64, _VP, _VP, _VP],
     "fp8_quantize_rowwise_colwise": [_VP, _I32, _I64, _I64, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "fp8_quantize_block": [_VP, _I32, _I64, _I64, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
+    "fp8_quantize_mx": [_VP, _I32, _I64, _I64, _I32, _VP, _VP, _VP, _VP, _VP],
     "fp8_update_scale_delayed": [_VP, _I32, _I32, _I32, _VP, _I64, _I32, _I32, _I32, _VP, _VP, _VP],
     "fp8_quantize_delayed": [_VP, _I32, _I64, _I32, _VP, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP,
                              _VP, _VP],
@@ -54,7 +55,7 @@ class Fp8qError(RuntimeError):
 def _load_library():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libfp8q.so is not built (%s); build it with "
-                          "`python -m fp8_scaled_quantization_reduce_amd.build`" % LIB_PATH)
+                          "`python fp8_scaled_quantization_reduce_amd/build.py`" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     for name, argtypes in SIGNATURES.items():
         fn = getattr(lib, name)
@@ -132,6 +133,14 @@ def fp8_quantize_block(x, fmt, block_rows, q_row, s_row, q_col=None, s_col=None,
     rows, cols = x.shape
     _check(lib.fp8_quantize_block(_ptr(x), _dtype(x), rows, cols, fmt, block_rows, _ptr(q_row), _ptr(s_row),
                                   _ptr(q_col), _ptr(s_col), _stream(stream)))
+
+
+def fp8_quantize_mx(x, fmt, q_row, s_row, q_col=None, s_col=None, stream=None):
+    """MXFP8: 1x32 blocks along the rows with E8M0 scale bytes (uint8 tensors),
+    optionally the columnwise copy (the same rule on x^T)."""
+    rows, cols = x.shape
+    _check(lib.fp8_quantize_mx(_ptr(x), _dtype(x), rows, cols, fmt, _ptr(q_row), _ptr(s_row), _ptr(q_col),
+                               _ptr(s_col), _stream(stream)))
 
 
 def fp8_update_scale_delayed(hist, col, new_amax, step, fmt, margin, algo, scale, scale_inv, stream=None):

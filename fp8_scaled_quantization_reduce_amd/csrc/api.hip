@@ -229,6 +229,33 @@ int fp8_quantize_block(const void *x, int32_t dtype, int64_t rows, int64_t cols,
                       fn);
 }
 
+int fp8_quantize_mx(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt, uint8_t *q_row,
+                    uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, void *stream)
+{
+    const char *fn = "fp8_quantize_mx";
+    if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+    if (!valid_fmt(fmt)) return fail(FP8Q_EINVAL, "%s: unknown format %d", fn, (int)fmt);
+    if (rows < 0 || cols < 0) return fail(FP8Q_EINVAL, "%s: negative shape", fn);
+    if (rows % 128 || cols % 128) return fail(FP8Q_EUNSUPPORTED, "%s: rows and cols must be multiples of 128", fn);
+    if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 31)
+        return fail(FP8Q_EUNSUPPORTED, "%s: a dimension exceeds 2^31", fn);
+    if ((q_col == nullptr) != (s_col == nullptr)) return fail(FP8Q_EINVAL, "%s: give both q_col and s_col or neither", fn);
+    const int64_t n = rows * cols;
+    if (n == 0) return ok();
+    if (!x || !aligned(x, 16)) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
+    if (!q_row || !aligned(q_row, 16) || !s_row)
+        return fail(FP8Q_EINVAL, "%s: q_row must be a 16-byte aligned pointer and s_row non-null", fn);
+    if (q_col && !aligned(q_col, 16)) return fail(FP8Q_EINVAL, "%s: q_col misaligned", fn);
+    const int64_t ns = n / 32; // scale bytes of either layout
+    const int64_t nx = n * dsize(dtype);
+    if (overlap(x, nx, q_row, n) || overlap(x, nx, q_col, n) || overlap(q_row, n, q_col, n) ||
+        overlap(s_row, ns, s_col, ns) || overlap(q_row, n, s_row, ns) || overlap(q_col, n, s_col, ns) ||
+        overlap(q_row, n, s_col, ns) || overlap(q_col, n, s_row, ns) || overlap(x, nx, s_row, ns) ||
+        overlap(x, nx, s_col, ns))
+        return fail(FP8Q_EINVAL, "%s: buffers overlap", fn);
+    return hip_status(fp8q::launch_mx(x, dtype, rows, cols, fmt, q_row, s_row, q_col, s_col, (hipStream_t)stream), fn);
+}
+
 int fp8_update_scale_delayed(float *hist, int32_t history_len, int32_t n_cols, int32_t col, const float *new_amax,
                              int64_t step, int32_t fmt, int32_t margin, int32_t algo, float *scale, float *scale_inv,
                              void *stream)

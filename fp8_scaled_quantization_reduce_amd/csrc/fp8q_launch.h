@@ -46,6 +46,9 @@ hipError_t launch_rowwise_colwise(const void *x, int dtype, int64_t rows, int64_
 hipError_t launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int block_rows, uint8_t *q_row,
                         float *s_row, uint8_t *q_col, float *s_col, hipStream_t s);
 
+hipError_t launch_mx(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t *q_row, uint8_t *s_row,
+                     uint8_t *q_col, uint8_t *s_col, hipStream_t s);
+
 hipError_t launch_delayed(float *hist, int history_len, int n_cols, int col, const float *new_amax, int64_t step,
                           int fmt, int margin, int algo, float *scale, float *scale_inv, hipStream_t s);
 

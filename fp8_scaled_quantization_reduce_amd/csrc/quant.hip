@@ -475,7 +475,35 @@ hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, flo
 // four consecutive rows; the dwords land in LDS as a [128 col][128 row] byte
 // tile, rotated by 8 dwords per 16 columns so that the writes of a wave spread
 // over all banks while every 16-byte read stays contiguous.
-enum TileMode { kTilePerTensor = 0, kTileBlock128 = 1, kTileBlock1x128 = 2 };
+enum TileMode { kTilePerTensor = 0, kTileBlock128 = 1, kTileBlock1x128 = 2, kTileMX = 3 };
+
+// MXFP8 shared scale of one 32-element block from its magnitude max (float
+// bits, NaN above 0x7F800000): e = floor(log2(amax)) - emax clamped to
+// [-127, 127] (emax = 8 for E4M3FN, 15 for E5M2; 0 gives -127, Inf gives 127),
+// the E8M0 byte e + 127 (255 for NaN) and the exact multiplier 2^-e.
+struct MxScale {
+    float mult;
+    uint32_t byte;
+};
+
+template <int F> __device__ __forceinline__ MxScale mx_scale(uint32_t abits)
+{
+    constexpr int emax = F == kE4M3 ? 8 : 15;
+    if (abits > kInfBits) return {__uint_as_float(kCanonicalNaN), 255u};
+    int e;
+    if (abits == 0) {
+        e = -127;
+    } else if (abits == kInfBits) {
+        e = 127;
+    } else {
+        const int biased = (int)(abits >> 23);
+        const int fl = biased ? biased - 127 : (31 - __builtin_clz(abits)) - 149; // floor(log2)
+        e = min(max(fl - emax, -127), 127);
+    }
+    // 2^-e: a normal float for -e >= -126, the subnormal 2^-127 for e = 127
+    const uint32_t mbits = e < 127 ? (uint32_t)(127 - e) << 23 : 0x00400000u;
+    return {__uint_as_float(mbits), (uint32_t)(e + 127)};
+}
 
 constexpr int kTile = 128;
 
@@ -593,10 +621,15 @@ __device__ __forceinline__ void store_transposed(const uint32_t *tl, uint8_t *q_
 template <int F, int DT, int kMode, bool kAmax>
 __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__ x, int64_t rows, int64_t cols,
                                                         ScaleSrc src, uint8_t *__restrict__ q_row,
-                                                        uint8_t *__restrict__ q_col, float *__restrict__ s_row,
-                                                        float *__restrict__ s_col, float *scale_inv_out,
+                                                        uint8_t *__restrict__ q_col, void *__restrict__ s_row_p,
+                                                        void *__restrict__ s_col_p, float *scale_inv_out,
                                                         float *scale_out, GridScratch *gs)
 {
+    // block scales: fp32 (128x128, 1x128) or E8M0 bytes (MXFP8)
+    float *__restrict__ s_row = reinterpret_cast<float *>(s_row_p);
+    float *__restrict__ s_col = reinterpret_cast<float *>(s_col_p);
+    uint8_t *__restrict__ e_row = reinterpret_cast<uint8_t *>(s_row_p);
+    uint8_t *__restrict__ e_col = reinterpret_cast<uint8_t *>(s_col_p);
     __shared__ uint32_t tl[kTile * 32]; // transposed codes, 16 KiB
     __shared__ uint32_t red[kThreads / 64];
     __shared__ uint32_t colmax[kMode == kTileBlock1x128 ? 4 * kTile : 1]; // per wave, per tile column
@@ -668,6 +701,59 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 for (int q4 = 0; q4 < 4; ++q4)
                     cw[r][q4] = encode4<F>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
                                            PV(r, 4 * q4 + 3), sc.scale);
+        } else if constexpr (kMode == kTileMX) {
+            // MXFP8: 1x32 row blocks are two lanes (jg = 2b, 2b + 1) of a row;
+            // 32x1 column blocks are the 8 lanes of one wave sharing jg (the
+            // wave holds rows 32w .. 32w+31 of the tile), so no block scale
+            // leaves its wave
+            const int64_t xrow = cols / 32, xcol = rows / 32;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(PV(r, k)));
+                m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false)); // lane ^ 1
+                const MxScale ms = mx_scale<F>(m);
+                if ((jg & 1) == 0 && valid) e_row[(r0 + r) * xrow + (c0 >> 5)] = (uint8_t)ms.byte;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    cw[r][q4] = encode4<F>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
+                                           PV(r, 4 * q4 + 3), ms.mult);
+                if (q_row && valid)
+                    *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) =
+                        make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
+            }
+            if (q_col) {
+                opaque(p);
+                float cm[16];
+                uint32_t cb[16];
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    uint32_t m = 0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m = max(m, f32_absbits(PV(r, k)));
+                    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xF, 0xF, false)); // lane ^ 8
+                    m = max(m, (uint32_t)__builtin_amdgcn_ds_swizzle((int)m, 0x401F));                    // lane ^ 16
+                    m = max(m, (uint32_t)__shfl_xor((int)m, 32));                                         // lane ^ 32
+                    const MxScale ms = mx_scale<F>(m);
+                    cm[k] = ms.mult;
+                    cb[k] = ms.byte;
+                }
+                if ((threadIdx.x & 63) < 8 && valid) {
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) e_col[(c0 + k) * xcol + (r0 >> 5)] = (uint8_t)cb[k];
+                }
+                uint32_t cc[4][4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int k = 4 * q4;
+                        cc[r][q4] = encode4s<F>(PV(r, k), PV(r, k + 1), PV(r, k + 2), PV(r, k + 3), cm[k],
+                                                cm[k + 1], cm[k + 2], cm[k + 3]);
+                    }
+                stage_transposed(tl, cc, ig, jg);
+            }
         } else { // 1x128 blocks: one scale per row segment, one per column segment
             // row segments: the 8 lanes jg = 0..7 of a row group hold the row's 128 columns
 #pragma unroll
@@ -724,7 +810,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
             }
         }
 
-        if (kMode != kTileBlock1x128 && q_row && valid) {
+        if (kMode != kTileBlock1x128 && kMode != kTileMX && q_row && valid) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) =
@@ -745,7 +831,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                                                 cs[1], cs[2], cs[3]);
                     }
                 stage_transposed(tl, cc, ig, jg);
-            } else {
+            } else if constexpr (kMode != kTileMX) { // (MXFP8 staged its own column codes above)
                 stage_transposed(tl, cw, ig, jg);
             }
             __syncthreads();
@@ -810,6 +896,28 @@ static hipError_t launch_block_t(const void *x, int64_t rows, int64_t cols, int 
         tile_kernel<F, DT, kTileBlock1x128, false><<<grid, kThreads, 0, s>>>(x, rows, cols, none, q_row, q_col,
                                                                             s_row, s_col, nullptr, nullptr, nullptr);
     return hipGetLastError();
+}
+
+template <int F, int DT>
+static hipError_t launch_mx_t(const void *x, int64_t rows, int64_t cols, uint8_t *q_row, uint8_t *s_row,
+                              uint8_t *q_col, uint8_t *s_col, hipStream_t s)
+{
+    const ScaleSrc none{nullptr, nullptr, 0};
+    tile_kernel<F, DT, kTileMX, false><<<tile_grid(rows, cols), kThreads, 0, s>>>(
+        x, rows, cols, none, q_row, q_col, s_row, s_col, nullptr, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t *q_row, uint8_t *s_row,
+                     uint8_t *q_col, uint8_t *s_col, hipStream_t s)
+{
+    if (rows == 0 || cols == 0) return hipSuccess;
+    if (fmt == kE4M3) {
+        if (dtype == kBF16) return launch_mx_t<kE4M3, kBF16>(x, rows, cols, q_row, s_row, q_col, s_col, s);
+        return launch_mx_t<kE4M3, kF32>(x, rows, cols, q_row, s_row, q_col, s_col, s);
+    }
+    if (dtype == kBF16) return launch_mx_t<kE5M2, kBF16>(x, rows, cols, q_row, s_row, q_col, s_col, s);
+    return launch_mx_t<kE5M2, kF32>(x, rows, cols, q_row, s_row, q_col, s_col, s);
 }
 
 hipError_t launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int block_rows, uint8_t *q_row,

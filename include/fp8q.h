@@ -140,6 +140,27 @@ int fp8_quantize_block(const void *x, int32_t dtype, int64_t rows, int64_t cols,
                        uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col, void *stream);
 
 /*
+ * fp8_quantize_mx -- MXFP8 quantization ([MFP8] section 16: 32 consecutive
+ * elements share one E8M0 scale, 8 exponent bits, no mantissa or sign,
+ * 2^-127 .. 2^127; section 10: the finest-grained recipe).  The pages leave
+ * the choice of the shared exponent open; this library takes the OCP
+ * Microscaling rule: for a block with magnitude max a,
+ *   e = floor(log2(a)) - emax (emax = 8 for E4M3FN, 15 for E5M2), clamped to
+ *   [-127, 127]; an all-zero block takes e = -127, an infinite a e = 127;
+ *   the scale byte is e + 127 (255, NaN, when the block holds a NaN) and each
+ *   element is encoded from fl32(x * 2^-e) like every other cast (saturating,
+ *   round to nearest even; a NaN block's elements become NaN codes).
+ *   x      [rows][cols] of `dtype`; rows, cols multiples of 128
+ *   q_row  [rows][cols] codes; s_row [rows][cols/32] scale bytes (blocks of 32
+ *          consecutive columns of a row: the K-contiguous operand of the
+ *          FP8Q_MXFP8 GEMM)
+ *   q_col, s_col (nullable, both or neither): the columnwise copy, the same
+ *          rule applied to x^T: q_col [cols][rows], s_col [cols][rows/32].
+ */
+int fp8_quantize_mx(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt, uint8_t *q_row,
+                    uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, void *stream);
+
+/*
  * fp8_update_scale_delayed -- delayed-scaling state update ([MFP8] section 5,
  * the amax-history ring and the fp8_meta update).
  *   hist       [history_len][n_cols] float history, column `col` is updated

@@ -123,6 +123,16 @@ def test_delayed_step_validation():
     _expect(d(BAD, fq.BF16, 64, 0, H, 16, 1, 0, 0, 0, 0, 0, SC, SI, Q, SI, None, S), fq.EINVAL, "overlap")
 
 
+def test_mx_validation():
+    m = L.fp8_quantize_mx
+    Q, SR = BAD + 0x100000, BAD + 0x200000
+    _expect(m(BAD, fq.BF16, 128, 128, 2, Q, SR, None, None, S), fq.EINVAL, "format")
+    _expect(m(BAD, fq.BF16, 128, 96, 0, Q, SR, None, None, S), fq.EUNSUPPORTED, "multiples")
+    _expect(m(BAD, fq.BF16, 128, 128, 0, Q, SR, Q + 0x10000, None, S), fq.EINVAL, "both")
+    _expect(m(BAD, fq.BF16, 128, 128, 0, Q + 1, SR, None, None, S), fq.EINVAL, "16-byte")
+    _expect(m(BAD, fq.BF16, 128, 128, 0, Q, Q + 0x100, None, None, S), fq.EINVAL, "overlap")
+
+
 def test_gemm_validation():
     g = L.fp8_scaled_gemm
     A, B, C = BAD + 0x100000, BAD + 0x200000, BAD + 0x300000
