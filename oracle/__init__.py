@@ -30,6 +30,7 @@ E4M3FN, E5M2 = 0, 1
 F32, BF16 = 0, 1
 ALGO_MAX, ALGO_MOST_RECENT = 0, 1
 PER_TENSOR, BLOCK_1x128_128x128, BLOCK_1x128_1x128, MXFP8 = 0, 1, 2, 3
+ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fp8_oracle.c")
@@ -375,3 +376,57 @@ def gemm_reference_entries(A: np.ndarray, fa: int, sA, B: np.ndarray, fb: int, s
                 acc += float(np.dot(av[sl], bv[sl])) * float(sA[m, kb]) * float(sB[nb, kb])
             out[i] = acc
     return out
+
+
+# ------------------------------------------------------------ GEMM epilogue ---
+# "Megatron FP8", section 6: bias addition and an activation (ReLU, GELU) can
+# be folded into the FP8 GEMM's epilogue, as Transformer Engine does for the
+# MLP's bias + GELU, so the intermediate never makes a bf16 round trip;
+# section 4: a tensor that is cast to FP8 records its amax for the next
+# scaling decision.  The pages name the fusions but not their arithmetic; the
+# readings taken here: bias is one value per output column (per output
+# feature), added to the finished GEMM value; GELU is the exact form
+# x * Phi(x) (Phi the standard normal CDF), not an approximation of it; ReLU
+# maps values below zero to zero and keeps NaN; an FP8 output is the
+# per-tensor cast (section 4) of the float32 result with a given dequant scale,
+# and its amax is taken over the values before that cast.
+
+
+def gelu(v) -> np.ndarray:
+    """float64 GELU, x * Phi(x) = x/2 * erfc(-x / sqrt 2).  erfc (a library
+    special function) keeps the relative accuracy of Phi for large negative x,
+    where 1 + erf(x / sqrt 2) would cancel."""
+    from scipy.special import erfc
+    v = np.asarray(v, dtype=np.float64)
+    return 0.5 * v * erfc(-v / np.sqrt(2.0))
+
+
+def relu(v) -> np.ndarray:
+    """x for x >= 0 (and for NaN, and -0.0), else 0."""
+    v = np.asarray(v, dtype=np.float64)
+    return np.where(v < 0, 0.0, v)
+
+
+def epilogue_reference(R: np.ndarray, bias=None, act: int = ACT_NONE) -> np.ndarray:
+    """float64 y[m, n] = act(R[m, n] + bias[n]) for a GEMM result R [M][N]
+    and a bias of one value per output column (None: no bias)."""
+    y = np.asarray(R, dtype=np.float64)
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64).reshape(1, -1)
+    if act == ACT_RELU:
+        return relu(y)
+    if act == ACT_GELU:
+        return gelu(y)
+    if act != ACT_NONE:
+        raise ValueError("unknown activation %r" % act)
+    return y
+
+
+def epilogue_fp8_codes(y: np.ndarray, fmt: int, out_scale_inv):
+    """FP8 output of the epilogue: the values rounded to float32, then the
+    per-tensor cast with dequant scale s = out_scale_inv (codes of
+    fl32(fl32(y) * fl32(1/s))).  Returns (codes, amax), the amax being
+    max |fl32(y)| over the values before the cast."""
+    y32 = np.asarray(y, dtype=np.float64).astype(np.float32)
+    return quantize(y32, fmt, reciprocal(out_scale_inv)), amax(y32)
+

@@ -614,3 +614,92 @@ def test_gemm_reference_mx():
     part = oracle.gemm_reference(A[:, 64:96], E4, sa[:, 2:3], B[:, 64:96], E5, sb[:, 2:3], oracle.MXFP8)
     assert np.allclose(R2[1] - R[1], 7 * part[1], rtol=1e-12, atol=1e-300)
     assert np.array_equal(R2[[0, 2]], R[[0, 2]])
+
+
+# ---------------------------------------------------------- GEMM epilogue ----
+# Standard normal CDF values as printed in statistical tables (and the erf(1)
+# constant); GELU(x) = x * Phi(x).
+PHI_TABLE = [(0.0, 0.5), (1.0, 0.8413447460685429), (-1.0, 0.15865525393145707), (2.0, 0.9772498680518208),
+             (3.0, 0.9986501019683699), (-3.0, 0.0013498980316301035), (1.959963984540054, 0.975)]
+ERF_1 = 0.8427007929497149
+
+
+def test_gelu_tabulated_values():
+    """A wrong sign inside Phi gives GELU(1) = 0.159, a missing 1/sqrt 2 gives
+    0.921; both fail here."""
+    for x, phi in PHI_TABLE:
+        assert math.isclose(float(oracle.gelu(x)), x * phi, rel_tol=1e-12, abs_tol=1e-300), x
+
+
+def test_gelu_invariants_and_tails():
+    x = np.linspace(-8, 8, 4001)
+    g = oracle.gelu(x)
+    # x Phi(x) - (-x) Phi(-x) = x (Phi(x) + Phi(-x)) = x
+    assert np.allclose(g - oracle.gelu(-x), x, rtol=0, atol=1e-14)
+    # the minimum is about -0.17, near x = -0.75
+    i = int(np.argmin(g))
+    assert -0.1701 < g[i] < -0.1699 and -0.76 < x[i] < -0.74
+    assert oracle.gelu(40.0) == 40.0 and oracle.gelu(0.0) == 0.0
+    # far left tail: x Phi(x) ~ phi(x) (1 - 1/x^2 + ...) (Mills ratio)
+    t = -10.0
+    mills = math.exp(-t * t / 2) / math.sqrt(2 * math.pi) * (1 - 1 / t ** 2 + 3 / t ** 4 - 15 / t ** 6)
+    assert math.isclose(float(oracle.gelu(t)), -mills, rel_tol=1e-4)
+    assert np.isnan(oracle.gelu(np.nan)) and np.isnan(oracle.gelu(-np.inf))
+    assert oracle.gelu(np.inf) == np.inf
+
+
+def test_gelu_slope_bound():
+    """The slope Phi(x) + x phi(x) peaks at x = sqrt 2 at
+    Phi(sqrt 2) + sqrt 2 phi(sqrt 2) = (1 + erf 1)/2 + e^-1 / sqrt(pi) ~ 1.1289
+    and bottoms at -0.1289 (x = -sqrt 2): the factor by which GELU can grow an
+    error of its argument (the GPU tests use 1.13)."""
+    peak = (1 + ERF_1) / 2 + math.exp(-1) / math.sqrt(math.pi)
+    x = np.linspace(-10, 10, 400001)
+    d = np.diff(oracle.gelu(x)) / np.diff(x)
+    assert abs(d.max() - peak) < 1e-6 and abs(d.min() - (1 - peak)) < 1e-6
+    assert peak < 1.13
+
+
+def test_relu_and_epilogue_composition():
+    v = np.array([-1.0, -0.0, 0.0, 2.5, np.nan])
+    r = oracle.relu(v)
+    assert r[0] == 0 and not np.signbit(r[0]) and np.signbit(r[1]) and r[3] == 2.5 and np.isnan(r[4])
+    # bias is per output column: R [2][3] + bias [3]
+    R = np.array([[1.0, -2.0, 3.0], [-4.0, 5.0, -6.0]])
+    b = np.array([0.5, 1.0, 10.0])
+    assert np.array_equal(oracle.epilogue_reference(R, b), [[1.5, -1.0, 13.0], [-3.5, 6.0, 4.0]])
+    assert np.array_equal(oracle.epilogue_reference(R, b, oracle.ACT_RELU), [[1.5, 0.0, 13.0], [0.0, 6.0, 4.0]])
+    with pytest.raises(ValueError):
+        oracle.epilogue_reference(R, np.ones(2))
+    # the activation applies after the bias
+    g = oracle.epilogue_reference(np.array([[-1.0]]), np.array([2.0]), oracle.ACT_GELU)
+    assert math.isclose(float(g[0, 0]), 0.8413447460685429, rel_tol=1e-12)
+
+
+def test_epilogue_gemm_brute_force():
+    """GEMM + bias + GELU on a tiny case by loops over the decode table."""
+    rng = np.random.default_rng(71)
+    M, N, K = 3, 5, 128
+    A = rng.integers(0, 0x7F, (M, K)).astype(np.uint8)
+    B = rng.integers(0, 0x7B, (N, K)).astype(np.uint8) | 0x80 * rng.integers(0, 2, (N, K)).astype(np.uint8)
+    sA, sB = np.float32(0.37), np.float32(0.011)
+    bias = rng.standard_normal(N)
+    y = oracle.epilogue_reference(oracle.gemm_reference(A, E4, sA, B, E5, sB), bias, oracle.ACT_GELU)
+    for m in range(M):
+        for n in range(N):
+            acc = sum(oracle.decode(E4, int(A[m, k])) * oracle.decode(E5, int(B[n, k])) for k in range(K))
+            v = acc * float(sA) * float(sB) + bias[n]
+            want = v * 0.5 * (1 + math.erf(v / math.sqrt(2)))
+            assert math.isclose(y[m, n], want, rel_tol=1e-12, abs_tol=1e-15)
+
+
+def test_epilogue_fp8_output_codes():
+    """FP8 output with dequant scale s = 2: the values are multiplied by
+    fl32(1/2) = 0.5 and cast: 1 -> 0.5 (0x30), 896 -> 448 (0x7E), -3 -> -1.5
+    (0xBC), 2000 -> 1000 saturates to 448; the amax is taken before the cast."""
+    q, am = oracle.epilogue_fp8_codes(np.array([[1.0, 896.0, -3.0, 2000.0]]), E4, 2.0)
+    assert q.tolist() == [[0x30, 0x7E, 0xBC, 0x7E]] and am == 2000.0
+    # E5M2: 57344 is the largest finite value, and 1000 * 0.5 = 500 lies
+    # between 448 and 512 (step 64 in [256, 512)): 512 is nearer
+    q, am = oracle.epilogue_fp8_codes(np.array([[1000.0, -0.25]]), E5, 2.0)
+    assert [oracle.decode(E5, int(c)) for c in q[0]] == [512.0, -0.125]
