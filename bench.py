@@ -320,7 +320,23 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream):
     ms = _time(torch, stream, lambda i: fq.fp8_scaled_gemm(dYq, E5, sdy, Wtq, E4, swt, fq.BLOCK_1x128_128x128, dX,
                                                             cam, stream=stream), 10)
     out["gemm_block_dgrad_4096x4096x14336"] = tflops(2 * 4096 * 4096 * 14336, ms)
-    del dYq, Wtq, Xq, Wq, Y, dX
+    del dYq, Wtq, dX
+
+    # next: the MLP's first projection with its epilogue fused, per-tensor
+    # E4M3 x E4M3, H = GELU(X W^T + b) cast to E4M3 codes with a given output
+    # scale and the pre-cast amax; beside it the same GEMM with a plain bf16
+    # output (the difference is the epilogue's cost)
+    bias = torch.randn(14336, device=dev, generator=g) * 0.5
+    s_h = torch.full((1,), 6.0 / 448, device=dev)
+    H = torch.empty((4096, 14336), dtype=torch.uint8, device=dev)
+    ms = _time(torch, stream, lambda i: fq.fp8_scaled_gemm(Xq, E4, s1, Wq, E4, s1, fq.PER_TENSOR, Y, cam,
+                                                            stream=stream), 10)
+    out["gemm_per_tensor_fc1_4096x14336x4096_bf16"] = tflops(2 * 4096 * 14336 * 4096, ms)
+    ms = _time(torch, stream, lambda i: fq.fp8_scaled_gemm_fused(Xq, E4, s1, Wq, E4, s1, fq.PER_TENSOR, H, bias=bias,
+                                                                  act=fq.ACT_GELU, out_fmt=E4, c_scale_inv=s_h,
+                                                                  amax_out=cam, stream=stream), 10)
+    out["gemm_fused_bias_gelu_e4m3out_4096x14336x4096"] = tflops(2 * 4096 * 14336 * 4096, ms)
+    del Xq, Wq, Y, H, bias
 
     # next: weight gradient dW = dY^T X, fp32 out, both operands the
     # token-contiguous (columnwise) copies with 1x128 scales along the tokens

@@ -24,6 +24,8 @@ E4M3FN, E5M2 = 0, 1
 F32, BF16 = 0, 1
 ALGO_MAX, ALGO_MOST_RECENT = 0, 1
 PER_TENSOR, BLOCK_1x128_128x128, BLOCK_1x128_1x128, MXFP8 = 0, 1, 2, 3
+OUT_E4M3FN, OUT_E5M2 = 2, 3
+ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +44,8 @@ SIGNATURES = {
     "fp8_quantize_delayed": [_VP, _I32, _I64, _I32, _VP, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _VP, _VP, _VP, _VP,
                              _VP, _VP],
     "fp8_scaled_gemm": [_VP, _I32, _VP, _VP, _I32, _VP, _I64, _I64, _I64, _I32, _VP, _I32, _VP, _VP],
+    "fp8_scaled_gemm_fused": [_VP, _I32, _VP, _VP, _I32, _VP, _I64, _I64, _I64, _I32, _VP, _I32, _VP, _I32, _VP, _VP,
+                              _VP],
     "fp8q_last_error": [],
 }
 
@@ -168,3 +172,23 @@ def fp8_scaled_gemm(A, fa, sA, B, fb, sB, mode, C, amax_out=None, stream=None):
         raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape), tuple(C.shape)))
     _check(lib.fp8_scaled_gemm(_ptr(A), fa, _ptr(sA), _ptr(B), fb, _ptr(sB), M, N, K, mode, _ptr(C), _dtype(C),
                                _ptr(amax_out), _stream(stream)))
+
+
+def fp8_scaled_gemm_fused(A, fa, sA, B, fb, sB, mode, C, *, bias=None, act=ACT_NONE, out_fmt=None,
+                          c_scale_inv=None, amax_out=None, stream=None):
+    """C = out(act((A*sA)(B*sB)^T + bias)); C bfloat16 / float32, or uint8
+    codes of out_fmt (E4M3FN / E5M2) cast with the dequant scale c_scale_inv."""
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape), tuple(C.shape)))
+    if C.dtype == torch.uint8:
+        if out_fmt not in (E4M3FN, E5M2):
+            raise ValueError("a uint8 C needs out_fmt E4M3FN or E5M2")
+        c_type = OUT_E4M3FN if out_fmt == E4M3FN else OUT_E5M2
+    else:
+        c_type = _dtype(C)
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N):
+        raise ValueError("bias must be float32 with N elements")
+    _check(lib.fp8_scaled_gemm_fused(_ptr(A), fa, _ptr(sA), _ptr(B), fb, _ptr(sB), M, N, K, mode, _ptr(bias), act,
+                                     _ptr(C), c_type, _ptr(c_scale_inv), _ptr(amax_out), _stream(stream)))

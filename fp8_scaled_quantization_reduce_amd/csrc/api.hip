@@ -324,16 +324,21 @@ int fp8_quantize_delayed(const void *x, int32_t dtype, int64_t n, int32_t fmt, f
                       fn);
 }
 
-int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb, const float *sB,
-                    int64_t M, int64_t N, int64_t K, int32_t mode, void *C, int32_t c_dtype, float *amax_out,
-                    void *stream)
+} // extern "C"
+
+// Shared body of the two GEMM entry points.  c_type: FP8Q_F32, FP8Q_BF16,
+// FP8Q_OUT_E4M3FN or FP8Q_OUT_E5M2 (the last two only from the fused call).
+static int scaled_gemm(const char *fn, const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb,
+                       const float *sB, int64_t M, int64_t N, int64_t K, int32_t mode, const float *bias, int32_t act,
+                       void *C, int32_t c_type, const float *c_scale_inv, float *amax_out, void *stream)
 {
-    const char *fn = "fp8_scaled_gemm";
     if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(FP8Q_EINVAL, "%s: unknown operand format", fn);
     if (mode != FP8Q_PER_TENSOR && mode != FP8Q_BLOCK_1x128_128x128 && mode != FP8Q_BLOCK_1x128_1x128 &&
         mode != FP8Q_MXFP8)
         return fail(FP8Q_EINVAL, "%s: unknown scaling mode %d", fn, (int)mode);
-    if (!valid_dtype(c_dtype)) return fail(FP8Q_EINVAL, "%s: unknown output dtype %d", fn, (int)c_dtype);
+    if (act != FP8Q_ACT_NONE && act != FP8Q_ACT_RELU && act != FP8Q_ACT_GELU)
+        return fail(FP8Q_EINVAL, "%s: unknown activation %d", fn, (int)act);
+    const bool fp8_out = c_type == FP8Q_OUT_E4M3FN || c_type == FP8Q_OUT_E5M2;
     if (M < 0 || N < 0 || K < 0) return fail(FP8Q_EINVAL, "%s: negative shape", fn);
     if (M % 128 || N % 128 || K % 128) return fail(FP8Q_EUNSUPPORTED, "%s: M, N, K must be multiples of 128", fn);
     if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31)
@@ -341,6 +346,10 @@ int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t
     if (!sA || !sB || !aligned(sA, 4) || !aligned(sB, 4))
         return fail(FP8Q_EINVAL, "%s: sA and sB must be 4-byte aligned pointers", fn);
     if (amax_out && !aligned(amax_out, 4)) return fail(FP8Q_EINVAL, "%s: amax_out misaligned", fn);
+    if (fp8_out && (!c_scale_inv || !aligned(c_scale_inv, 4)))
+        return fail(FP8Q_EINVAL, "%s: an FP8 output needs a 4-byte aligned c_scale_inv", fn);
+    if (!fp8_out && c_scale_inv) return fail(FP8Q_EINVAL, "%s: c_scale_inv is only for an FP8 output", fn);
+    if (bias && !aligned(bias, 16)) return fail(FP8Q_EINVAL, "%s: bias must be 16-byte aligned", fn);
     if (M == 0 || N == 0) {
         if (amax_out) return hip_status(fp8q::launch_fill_u32(reinterpret_cast<uint32_t *>(amax_out), 0u,
                                                               (hipStream_t)stream), fn);
@@ -349,9 +358,12 @@ int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t
     if (!C || !aligned(C, 16)) return fail(FP8Q_EINVAL, "%s: C must be a 16-byte aligned pointer", fn);
     if (K > 0 && (!A || !B || !aligned(A, 16) || !aligned(B, 16)))
         return fail(FP8Q_EINVAL, "%s: A and B must be 16-byte aligned pointers", fn);
-    const int64_t c_bytes = M * N * dsize(c_dtype);
-    if (overlap(C, c_bytes, A, M * K) || overlap(C, c_bytes, B, N * K) || overlap(C, c_bytes, amax_out, 4))
+    const int64_t c_bytes = M * N * (fp8_out ? 1 : dsize(c_type));
+    if (overlap(C, c_bytes, A, M * K) || overlap(C, c_bytes, B, N * K) || overlap(C, c_bytes, amax_out, 4) ||
+        overlap(C, c_bytes, bias, 4 * N) || overlap(C, c_bytes, c_scale_inv, 4))
         return fail(FP8Q_EINVAL, "%s: C overlaps an input", fn);
+    if (overlap(amax_out, 4, bias, 4 * N) || overlap(amax_out, 4, c_scale_inv, 4))
+        return fail(FP8Q_EINVAL, "%s: amax_out overlaps an input", fn);
     fp8q::GridScratch *gs = nullptr;
     if (amax_out) {
         if ((M / 128) * (N / 128) > fp8q::kMaxPartials)
@@ -360,8 +372,34 @@ int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t
         hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
         if (e != hipSuccess) return hip_status(e, fn);
     }
-    return hip_status(
-        fp8q::launch_gemm(A, fa, sA, B, fb, sB, M, N, K, mode, C, c_dtype, amax_out, gs, (hipStream_t)stream), fn);
+    // kernel output kinds: 0 bf16, 1 fp32, 2 E4M3FN codes, 3 E5M2 codes
+    const int out_kind = c_type == FP8Q_BF16 ? 0 : c_type == FP8Q_F32 ? 1 : c_type == FP8Q_OUT_E4M3FN ? 2 : 3;
+    return hip_status(fp8q::launch_gemm(A, fa, sA, B, fb, sB, M, N, K, mode, C, out_kind, bias, act, c_scale_inv,
+                                        amax_out, gs, (hipStream_t)stream),
+                      fn);
+}
+
+extern "C" {
+
+int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb, const float *sB,
+                    int64_t M, int64_t N, int64_t K, int32_t mode, void *C, int32_t c_dtype, float *amax_out,
+                    void *stream)
+{
+    const char *fn = "fp8_scaled_gemm";
+    if (!valid_dtype(c_dtype)) return fail(FP8Q_EINVAL, "%s: unknown output dtype %d", fn, (int)c_dtype);
+    return scaled_gemm(fn, A, fa, sA, B, fb, sB, M, N, K, mode, nullptr, FP8Q_ACT_NONE, C, c_dtype, nullptr, amax_out,
+                       stream);
+}
+
+int fp8_scaled_gemm_fused(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb,
+                          const float *sB, int64_t M, int64_t N, int64_t K, int32_t mode, const float *bias,
+                          int32_t act, void *C, int32_t c_type, const float *c_scale_inv, float *amax_out,
+                          void *stream)
+{
+    const char *fn = "fp8_scaled_gemm_fused";
+    if (!valid_dtype(c_type) && c_type != FP8Q_OUT_E4M3FN && c_type != FP8Q_OUT_E5M2)
+        return fail(FP8Q_EINVAL, "%s: unknown output type %d", fn, (int)c_type);
+    return scaled_gemm(fn, A, fa, sA, B, fb, sB, M, N, K, mode, bias, act, C, c_type, c_scale_inv, amax_out, stream);
 }
 
 } // extern "C"

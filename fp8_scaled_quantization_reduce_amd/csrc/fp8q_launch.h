@@ -57,8 +57,10 @@ hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, flo
                                float *scale_inv, uint8_t *q, float *q_scale_inv_out, float *amax_out, GridScratch *gs,
                                hipStream_t s);
 
+// out_kind: 0 bf16, 1 fp32, 2 E4M3FN codes, 3 E5M2 codes (cast with
+// 1 / *out_scale_inv); act: 0 none, 1 ReLU, 2 GELU; bias [N] fp32 or null.
 hipError_t launch_gemm(const uint8_t *A, int fa, const float *sA, const uint8_t *B, int fb, const float *sB, int64_t M,
-                       int64_t N, int64_t K, int mode, void *C, int c_dtype, float *amax_out, GridScratch *gs,
-                       hipStream_t s);
+                       int64_t N, int64_t K, int mode, void *C, int out_kind, const float *bias, int act,
+                       const float *out_scale_inv, float *amax_out, GridScratch *gs, hipStream_t s);
 
 } // namespace fp8q

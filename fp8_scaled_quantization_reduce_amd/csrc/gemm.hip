@@ -1,647 +1,19 @@
-// gemm.hip -- scaled FP8 GEMM on gfx950 matrix cores.
-//
-// C[M][N] = (A*sA)(B*sB)^T with A [M][K], B [N][K] FP8 codes (K-contiguous),
-// fp32 accumulation on the f8f6f4 matrix instructions and a bf16 output.
-//   per-tensor: C = bf16(fl32(fl32(sA*sB) * acc))   ("Megatron FP8", section 6:
-//               fp32 accumulation, bf16 output; section 27: products promoted
-//               to fp32 and summed, one downcast of the finished dot product)
-//   block:      each 128-wide K slice is its own MFMA partial, promoted into
-//               the fp32 accumulator with the 1x128 scale of A's row and the
-//               128x128 scale of B's block: acc += (sA[m,kb]*sB[n/128,kb]) * part
-// and, optionally, the per-block magnitude max of the emitted bf16 values
-// (folded into amax_out by the finish kernel).
-//
-// Two kernels, both with 256x256 block tiles and operand tiles moved
-// from global memory straight into LDS by buffer loads (buffer_load_dwordx4
-// ... lds: no register staging), 16-byte chunks XOR-swizzled by row so that
-// fragment reads spread over the LDS banks:
-//
-//   gemm_pt_kernel (per-tensor): 256x256 tiles, a wave owns 128x128 of C as
-//   4x4 tiles of 32x32 (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales,
-//   256 accumulators).  K moves in steps of 64 through a ring of four LDS
-//   stages; the loop is unrolled by four so every stage index is static, and
-//   each step waits for its own stage only (the two younger stages stay in
-//   flight), reads the next step's fragments, issues the loads three steps
-//   ahead and runs its 16 MFMAs, interleaved with those reads and loads.
-//
-//   gemm_bs_kernel (block-scaled): 256x256 tiles and eight waves of 64x128,
-//   each as 4x8 tiles of 16x16 (v_mfma_f32_16x16x128_f8f6f4); K moves in
-//   steps of 128 (one block-scale slice) through two LDS stages, and each
-//   slice's partial is promoted on the vector ALU.
-//
-// Operand order.  The MFMA is issued as (B fragment, A fragment), so its
-// result is C^T: in a 16x16 tile lane (r = lane % 16, g = lane / 16) holds
-// C[r][4g..4g+3], four consecutive columns of one row, stored as one 8-byte
-// bf16 quad (32x32 tiles likewise, per group of four accumulators).  A and B
-// fragments use the same lane -> K mapping, so the MFMA's internal K order does
-// not affect the dot product.
-//
-// Blocks are dealt round-robin to the 8 XCDs; the tile index is remapped so
-// that each XCD works on a compact group of output tiles (4 tile rows wide),
-// whose operand panels then stay in that XCD's L2.
+// gemm.hip -- dispatch of a scaled-GEMM launch to the translation unit of its
+// operand-format pair (the kernels are in gemm_kernels.h).
 #include "fp8q_device.h"
-#include "fp8q_launch.h"
+#include "gemm_pairs.h"
 
 namespace fp8q {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kGemmThreads = 256;
-constexpr int kBM = 256, kBK = 128;
-constexpr int kXcds = 8;
-constexpr int kGroupM = 4; // tile rows per L2 group
-constexpr uint32_t kRawBufferWord3 = 0x00020000u;
-
-template <int FX, int FY>
-__device__ __forceinline__ v4f mfma16x16x128(const v8i &x, const v8i &y, const v4f &c)
-{
-    // cbsz / blgp give the formats of the two operands (0 = E4M3, 1 = E5M2);
-    // zero scale operands select the unscaled instruction.
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, FX, FY, 0, 0, 0, 0);
-}
-
-// Byte offset of 16-byte chunk c of row r in a [rows][128] LDS stage.  The LDS
-// serves 256 bytes (64 banks) per cycle, i.e. two 128-byte rows; XOR-ing the
-// chunk with bits 1..3 of the row gives the 16 rows read by 16 lanes of a
-// fragment 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ ((r >> 1) & 7)) << 4); }
-
-__device__ __forceinline__ void tile_of_block(int bid, int tilesM, int tilesN, int &tm, int &tn)
-{
-    const int ntiles = tilesM * tilesN;
-    int t = bid;
-    if (ntiles % kXcds == 0) t = (bid % kXcds) * (ntiles / kXcds) + bid / kXcds;
-    const int per_group = kGroupM * tilesN;
-    const int group = t / per_group;
-    const int first_m = group * kGroupM;
-    const int gsize = min(tilesM - first_m, kGroupM);
-    const int in_group = t - group * per_group;
-    tm = first_m + in_group % gsize;
-    tn = in_group / gsize;
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// One operand fragment (16 rows x 128 K bytes): lane (r, g) reads logical
-// chunks g and g + 4 of row r.  (Chunks 2g and 2g + 1 would be the same K
-// bytes in another order, but then lanes r and r + 16 of one read hit the same
-// banks: measured, that read pattern runs at 0.6x the speed with half of the
-// LDS cycles lost to bank conflicts.)
-__device__ __forceinline__ v8i read_frag(const uint8_t *lds, int r, int g)
-{
-    const uint4 lo = *reinterpret_cast<const uint4 *>(lds + swz(r, g));
-    const uint4 hi = *reinterpret_cast<const uint4 *>(lds + swz(r, g + 4));
-    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
-// Store four consecutive outputs of one row of C (bf16, round to nearest even,
-// or fp32 as is) and fold their magnitudes into m (canonicalised later).
-template <bool kF32, bool kAmax>
-__device__ __forceinline__ void store_out4(void *C, int64_t idx, const v4f &v, uint32_t &m)
-{
-    if constexpr (kF32) {
-        *reinterpret_cast<v4f *>(reinterpret_cast<float *>(C) + idx) = v;
-        if constexpr (kAmax) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m = max(m, __float_as_uint(v[e]) & 0x7FFFFFFFu);
-        }
-    } else {
-        const bf16x4 h = __builtin_convertvector(v, bf16x4);
-        *reinterpret_cast<bf16x4 *>(reinterpret_cast<__bf16 *>(C) + idx) = h;
-        if constexpr (kAmax) {
-            const uint2 bits = __builtin_bit_cast(uint2, h);
-            m = max(m, max((bits.x & 0x7FFFu) << 16, (bits.x >> 16 & 0x7FFFu) << 16));
-            m = max(m, max((bits.y & 0x7FFFu) << 16, (bits.y >> 16 & 0x7FFFu) << 16));
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Per-tensor kernel.  256x256 block tile, 2x2 waves of 128x128 as 4x4 tiles
-// of v_mfma_f32_32x32x64_f8f6f4 (256 fp32 accumulators per lane).  K moves in
-// slices of 128 through two LDS stages of 64 KiB; every direct load moves 8
-// rows x 128 bytes (whole 128-byte rows fetch about 1.6x faster from L2 than
-// 64-byte half rows).  A slice is two half steps of 64 K, each 16 MFMAs per
-// wave, and the one barrier per slice sits between them:
-//   half 0: MFMAs on the slice's first-half fragments while the second-half
-//           fragments are read from LDS;
-//   sync:   wait for this lane's loads of the next slice and the LDS reads,
-//           then barrier: the next slice is in LDS and nobody reads this
-//           slice's stage any more;
-//   half 1: the loads of the slice after next go into this stage, while the
-//           MFMAs run on the second-half fragments and the next slice's
-//           first-half fragments are read.
-// So LDS reads always overlap MFMAs, and the loads have a whole slice of
-// MFMAs to land.
-constexpr int kPTStageBytes = 2 * kBM * kBK;
-
-// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
-// 6:4, lgkmcnt in 11:8).  Issued through the builtin rather than inline asm so
-// that the compiler's own wait insertion knows what has been waited for.
-constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 0xF) | (7 << 4) | ((lgkm & 0xF) << 8) | ((vm >> 4) << 14); }
-
-typedef float v16f __attribute__((ext_vector_type(16)));
-
-template <int FX, int FY>
-__device__ __forceinline__ v16f mfma32x32x64(const v8i &x, const v8i &y, const v16f &c)
-{
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, FX, FY, 0, 0, 0, 0);
-}
-
-// 32 rows x 64 K bytes of half step h: lane (r = lane % 32, g = lane / 32)
-// reads logical chunks 4h + 2g and 4h + 2g + 1 of row r (same swizzle as above)
-__device__ __forceinline__ v8i read_frag32(const uint8_t *lds, int r, int g, int h)
-{
-    const uint4 lo = *reinterpret_cast<const uint4 *>(lds + swz(r, 4 * h + 2 * g));
-    const uint4 hi = *reinterpret_cast<const uint4 *>(lds + swz(r, 4 * h + 2 * g + 1));
-    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
-// MXFP8 layout of the same 32 rows x 64 K bytes.  The scaled instruction's
-// K order puts bytes 0..15 of lane (r, g) at K 16g .. 16g+15 of the half step
-// and bytes 16..31 at K 32 + 16g .. 32 + 16g + 15, and takes the scale of K
-// block b (32 elements) of row r from lane r + 32b (measured on the MI355X with
-// unit codes and one scaled lane at a time).  So lane (r, g) reads logical
-// chunks 4h + g and 4h + 2 + g, and supplies the scale of block 2h + g.
-__device__ __forceinline__ v8i read_frag32_mx(const uint8_t *lds, int r, int g, int h)
-{
-    const uint4 lo = *reinterpret_cast<const uint4 *>(lds + swz(r, 4 * h + g));
-    const uint4 hi = *reinterpret_cast<const uint4 *>(lds + swz(r, 4 * h + 2 + g));
-    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
-// The two stages are distinct LDS objects addressed with compile-time stage
-// numbers (the slice loop is unrolled by two), so the compiler can tell a
-// read of one stage from the direct loads landing in the other.
-// With kMX (MXFP8), sA and sB point to E8M0 scale bytes, [M][K/32] and
-// [N][K/32]: every 32-element K block of a row carries a power of two that the
-// matrix instruction applies itself (v_mfma_scale_f32_32x32x64_f8f6f4 takes one
-// scale byte per lane, for the 32 K bytes that lane holds).  Each stage also
-// carries the slice's four scale bytes of every A and B row (one dword per row,
-// loaded straight into LDS with the codes).
-template <int FA, int FB, bool kAmax, bool kF32, bool kMX>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t *__restrict__ A,
-                                                                  const uint8_t *__restrict__ B,
-                                                                  const float *__restrict__ sA,
-                                                                  const float *__restrict__ sB, int M, int N, int K,
-                                                                  void *__restrict__ C, GridScratch *gs)
-{
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[kPTStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[kPTStageBytes];
-    __shared__ __attribute__((aligned(16))) uint32_t sx0[kMX ? 2 * kBM : 1]; // A rows' then B rows' scale dwords
-    __shared__ __attribute__((aligned(16))) uint32_t sx1[kMX ? 2 * kBM : 1];
-    __shared__ uint32_t red[kGemmThreads / 64];
-    constexpr int kStageLoads = kMX ? 18 : 16; // direct loads per lane per stage
-
-    int tm, tn;
-    tile_of_block(blockIdx.x, (M + kBM - 1) / kBM, (N + kBM - 1) / kBM, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBM;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = w >> 1, wn = w & 1;
-    const int fr = lane & 31, fg = lane >> 5;
-    const int nk = K / kBK;
-
-    const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBM, (int64_t)N - n0);
-    const __amdgpu_buffer_rsrc_t ra =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * K), 0, (int)(a_rows * K), kRawBufferWord3);
-    const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0 * K), 0, (int)(b_rows * K), kRawBufferWord3);
-    // lane L of a 1 KiB load writes physical chunk L % 8 of row 8(w + 4u) + L / 8,
-    // which holds logical chunk (L % 8) ^ ((row >> 1) & 7) = (L % 8) ^ ((4w + L / 16) & 7)
-    const int voff = (lane >> 3) * K + (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4);
-
-    // MXFP8 scale rows: K/32 bytes per row; the slice's 4 bytes are one dword
-    const int kx = K / 32;
-    const __amdgpu_buffer_rsrc_t rxa = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(reinterpret_cast<const uint8_t *>(sA) + (kMX ? m0 * kx : 0)), 0, kMX ? (int)(a_rows * kx) : 4,
-        kRawBufferWord3);
-    const __amdgpu_buffer_rsrc_t rxb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(reinterpret_cast<const uint8_t *>(sB) + (kMX ? n0 * kx : 0)), 0, kMX ? (int)(b_rows * kx) : 4,
-        kRawBufferWord3);
-
-    // wave w loads rows 8(w + 4u), u = 0..7, of both panels: 16 loads of 1 KiB
-    // (and, MXFP8, the scale dwords of rows 64w .. 64w+63 of both panels)
-    auto stage = [&](uint8_t *st, uint32_t *sx, int kb) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int row = 8 * (w + 4 * u);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + row * kBK), 16, voff, row * K + kb * kBK,
-                                                     0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + kBM * kBK + row * kBK), 16, voff,
-                                                     row * K + kb * kBK, 0, 0);
-        }
-        if constexpr (kMX) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxa, (lds_void *)(sx + 64 * w), 4, lane * kx,
-                                                     64 * w * kx + 4 * kb, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxb, (lds_void *)(sx + kBM + 64 * w), 4, lane * kx,
-                                                     64 * w * kx + 4 * kb, 0, 0);
-        }
-    };
-
-    v16f acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-    v8i fa0[4], fb0[4], fa1[4], fb1[4]; // first-half and second-half fragments
-    // MXFP8: the scale dwords of the lane's A rows (i) and B rows (j) for the
-    // current slice and the next one, pre-shifted by 8 * fg bytes so that byte
-    // 0 is the scale of this lane's K block in half 0 and byte 2 in half 1
-    uint32_t xa0[4], xb0[4], xa1[4], xb1[4];
-    auto read_frags = [&](const uint8_t *st, int h, v8i(&a)[4], v8i(&b)[4]) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            b[j] = kMX ? read_frag32_mx(st + kBM * kBK, wn * 128 + 32 * j + fr, fg, h)
-                       : read_frag32(st + kBM * kBK, wn * 128 + 32 * j + fr, fg, h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a[i] = kMX ? read_frag32_mx(st, wm * 128 + 32 * i + fr, fg, h) : read_frag32(st, wm * 128 + 32 * i + fr, fg, h);
-    };
-    auto read_scales = [&](const uint32_t *sx, uint32_t(&xa)[4], uint32_t(&xb)[4]) {
-        if constexpr (kMX) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xa[i] = sx[wm * 128 + 32 * i + fr] >> (8 * fg);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) xb[j] = sx[kBM + wn * 128 + 32 * j + fr] >> (8 * fg);
-        }
-    };
-    // half h of the slice whose scale dwords are xa / xb
-    auto mfmas = [&](const v8i(&a)[4], const v8i(&b)[4], const uint32_t(&xa)[4], const uint32_t(&xb)[4], int h) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (kMX) {
-                    if (h == 0)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], FB, FA, 0,
-                                                                                    (int)xb[j], 0, (int)xa[i]);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], FB, FA, 2,
-                                                                                    (int)xb[j], 2, (int)xa[i]);
-                } else {
-                    acc[i][j] = mfma32x32x64<FB, FA>(b[j], a[i], acc[i][j]);
-                }
-            }
-    };
-
-    // One slice in stage `cur` (the next one in `nxt`).  `full` = the slices
-    // kb + 1 and kb + 2 both exist (no guards).
-    auto slice = [&](int kb, uint8_t *cur, uint32_t *sxc, const uint8_t *nxt, const uint32_t *sxn,
-                     const uint32_t(&xa)[4], const uint32_t(&xb)[4], uint32_t(&xan)[4], uint32_t(&xbn)[4],
-                     bool full) {
-        // half 0
-        mfmas(fa0, fb0, xa, xb, 0);
-        read_frags(cur, 1, fa1, fb1);
-        if (full) {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // LDS read
-            }
-        }
-        // sync: the next slice landed (this lane's loads, then every wave's)
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        // half 1
-        if (full || kb + 2 < nk) stage(cur, sxc, kb + 2);
-        mfmas(fa1, fb1, xa, xb, 1);
-        if (full || kb + 1 < nk) {
-            read_frags(nxt, 0, fa0, fb0);
-            read_scales(sxn, xan, xbn);
-        }
-        if (full) {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global -> LDS load
-            }
-        }
-    };
-
-    // prologue: slices 0 and 1 in flight, slice 0's first-half fragments.
-    // Both stages are always filled (for K = 128 the second load reads bytes
-    // of the panel that are never used; rows past the record read zero): with
-    // an unconditional pair the compiler's wait insertion keeps the two stages
-    // apart and puts no full wait at the top of the loop.
-    if (nk > 0) {
-        stage(st0, sx0, 0);
-        stage(st1, sx1, 1);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(kStageLoads, 15));
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        read_frags(st0, 0, fa0, fb0);
-        read_scales(sx0, xa0, xb0);
-    }
-    int kb = 0;
-    for (; kb + 4 <= nk; kb += 2) {
-        slice(kb, st0, sx0, st1, sx1, xa0, xb0, xa1, xb1, true);
-        slice(kb + 1, st1, sx1, st0, sx0, xa1, xb1, xa0, xb0, true);
-    }
-    // at most three slices remain; kb is even
-    if (kb < nk) slice(kb, st0, sx0, st1, sx1, xa0, xb0, xa1, xb1, false);
-    if (kb + 1 < nk) slice(kb + 1, st1, sx1, st0, sx0, xa1, xb1, xa0, xb0, false);
-    if (kb + 2 < nk) slice(kb + 2, st0, sx0, st1, sx1, xa0, xb0, xa1, xb1, false);
-
-    // epilogue: lane (fr, fg) of 32x32 tile (i, j) holds C[row][4 consecutive
-    // columns 8q + 4fg .. +3] for q = 0..3
-    const float alpha = kMX ? 1.0f : (*sA) * (*sB);
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t row = m0 + wm * 128 + 32 * i + fr;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t col = n0 + wn * 128 + 32 * j + 8 * q + 4 * fg;
-                const v4f v = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                  acc[i][j][4 * q + 3]} * alpha;
-                if (row < M && col < N) store_out4<kF32, kAmax>(C, row * N + col, v, m);
-            }
-        }
-    }
-    if constexpr (kAmax) {
-        m = block_max_u32<kGemmThreads>(m, red);
-        if (tid == 0) gs->part[blockIdx.x] = canonical_amax_bits(m);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Block-scaled kernel.  256x256 block tile, eight waves (4 x 2) of 64x128, each
-// as 4 x 8 tiles of 16x16.  One K step is one 128-wide scale slice and one
-// v_mfma_f32_16x16x128_f8f6f4 per tile, started from zero, so its result is
-// exactly that slice's partial product; it is promoted at once,
-//   acc = fma(part, fl32(sA[row][kb] * sB[col block][kb]), acc),
-// with the accumulators in ordinary vector registers (128 per lane; the
-// two-waves-per-SIMD budget is 256).  The slice's A rows and B rows (2 x 32
-// KiB) and the 256 row scales of A (1 KiB) go straight into LDS; two stages,
-// the next slice's loads in flight during this one's MFMAs.
-constexpr int kBSThreads = 512;
-constexpr int kBSStageBytes = 2 * kBM * kBK;
-
-template <int FA, int FB, bool kAmax, bool kF32, bool kRowB>
-__global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *__restrict__ A,
-                                                                const uint8_t *__restrict__ B,
-                                                                const float *__restrict__ sA,
-                                                                const float *__restrict__ sB, int M, int N, int K,
-                                                                void *__restrict__ C, GridScratch *gs)
-{
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[kBSStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[kBSStageBytes];
-    __shared__ __attribute__((aligned(16))) float sa0[kBM];
-    __shared__ __attribute__((aligned(16))) float sa1[kBM];
-    __shared__ __attribute__((aligned(16))) float sb0[kRowB ? kBM : 4]; // B's row scales (1x128 B)
-    __shared__ __attribute__((aligned(16))) float sb1[kRowB ? kBM : 4];
-    __shared__ uint32_t red[kBSThreads / 64];
-
-    int tm, tn;
-    tile_of_block(blockIdx.x, (M + kBM - 1) / kBM, (N + kBM - 1) / kBM, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBM;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = w >> 1, wn = w & 1;
-    const int fr = lane & 15, fg = lane >> 4;
-    const int kblocks = K / kBK;
-
-    const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBM, (int64_t)N - n0);
-    const __amdgpu_buffer_rsrc_t ra =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * K), 0, (int)(a_rows * K), kRawBufferWord3);
-    const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0 * K), 0, (int)(b_rows * K), kRawBufferWord3);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)(sA + m0 * kblocks), 0,
-                                                                        (int)(a_rows * kblocks * 4), kRawBufferWord3);
-    // lane L of a 1 KiB load writes physical chunk L % 8 of row 8(w + 8u) + L / 8,
-    // which holds logical chunk (L % 8) ^ ((row >> 1) & 7) = (L % 8) ^ ((4w + L / 16) & 7)
-    const int voff = (lane >> 3) * K + (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4);
-    // 128x128 B: the wave's 128 columns lie in one 128-column scale block
-    // (clamped for the half tile past N, whose results are never stored).
-    // 1x128 B: one scale per row of B (column of C), staged like A's.
-    const int nb = min((int)((n0 + wn * 128) / 128), N / 128 - 1);
-    const float *__restrict__ sbp = sB + (int64_t)nb * kblocks;
-    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(sB + (kRowB ? n0 * kblocks : 0)), 0, kRowB ? (int)(b_rows * kblocks * 4) : 4, kRawBufferWord3);
-
-    auto stage = [&](uint8_t *st, float *sa, float *sbr, int kb) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int row = 8 * (w + 8 * u);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + row * kBK), 16, voff, kb * kBK + row * K,
-                                                     0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int row = 8 * (w + 8 * u);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + kBM * kBK + row * kBK), 16, voff,
-                                                     kb * kBK + row * K, 0, 0);
-        }
-        if (w < 4)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(sa + 64 * w), 4, lane * kblocks * 4,
-                                                     (64 * w * kblocks + kb) * 4, 0, 0);
-        else if (kRowB)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(sbr + 64 * (w - 4)), 4, lane * kblocks * 4,
-                                                     (64 * (w - 4) * kblocks + kb) * 4, 0, 0);
-    };
-
-    v4f acc[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // One slice (stage `cur`, its row scales in `sac`; the next slice already
-    // in flight to `nxt` / `san`).  Column tile j's MFMAs run while tile
-    // j-1's partials are promoted and tile j+1's B fragment is read.  Once
-    // the last fragment of `cur` is in registers (before tile 7), every lane
-    // waits for its own loads of the next slice and the block meets at the
-    // one barrier of the slice; then the slice after next is loaded into
-    // `cur`, and tile 7's MFMAs overlap the reads of the next slice's A
-    // fragments, first B fragment and row scales.  Empty asm statements pin
-    // this order (the compiler would otherwise issue all 32 MFMAs first and
-    // spill their 128 partial registers): the one on the B fragment keeps
-    // tile j's MFMAs below it, the one on the promoted accumulators keeps
-    // tile j-1's FMAs above the next tile's.
-    // Weights: 128x128 B: wi[i] = fl32(sA[row i] * sB[block]); 1x128 B:
-    // fl32(sA[row i] * sB[col]) per element, from sai[i] and the tile's four
-    // column scales, read from LDS just before the tile's MFMAs are issued
-    // (tile 7's before the slice's barrier, after which the stage is reloaded).
-    v8i a[4], b;
-    float wi[4], sai[4];
-    float sb_next = 0.0f;
-    auto promote = [&](int j, const v4f (&part)[4], const v4f &sbj) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float wgt = kRowB ? sai[i] * sbj[e] : wi[i];
-                acc[i][j][e] = __builtin_fmaf(part[i][e], wgt, acc[i][j][e]);
-            }
-        asm volatile("" : "+v"(acc[0][j]), "+v"(acc[1][j]), "+v"(acc[2][j]), "+v"(acc[3][j]));
-    };
-    auto slice = [&](int kb, uint8_t *cur, float *sac, float *sbc, const uint8_t *nxt, const float *san,
-                     bool full) {
-        const uint8_t *lb = cur + kBM * kBK;
-        const float *sbw = sbc + wn * 128 + 4 * fg; // this lane's column scales, tile 0
-        v4f prev[4];
-        v4f sb7 = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            asm volatile("" : "+v"(b));
-            v8i bn;
-            if (j + 1 < 8) bn = read_frag(lb, wn * 128 + 16 * (j + 1) + fr, fg);
-            v4f sbj = v4f{0.f, 0.f, 0.f, 0.f}; // tile j-1's column scales
-            if constexpr (kRowB) {
-                if (j > 0) sbj = *reinterpret_cast<const v4f *>(sbw + 16 * (j - 1));
-                if (j == 7) sb7 = *reinterpret_cast<const v4f *>(sbw + 16 * 7);
-            }
-            if (j == 7) {
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-                __builtin_amdgcn_s_barrier();
-                asm volatile("" ::: "memory");
-                if (full || kb + 2 < kblocks) stage(cur, sac, sbc, kb + 2);
-            }
-            v4f cur_p[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) cur_p[i] = mfma16x16x128<FB, FA>(b, a[i], v4f{0.f, 0.f, 0.f, 0.f});
-            if (j > 0) promote(j - 1, prev, sbj);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) prev[i] = cur_p[i];
-            if (j + 1 < 8) b = bn;
-        }
-        // tile 7's promotion with this slice's weights, then the next slice's
-        // fragments and weights
-        promote(7, prev, sb7);
-        if (full || kb + 1 < kblocks) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = read_frag(nxt, wm * 64 + 16 * i + fr, fg);
-            b = read_frag(nxt + kBM * kBK, wn * 128 + fr, fg);
-            if constexpr (kRowB) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sai[i] = san[wm * 64 + 16 * i + fr];
-            } else {
-                const float sb = sb_next;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) wi[i] = san[wm * 64 + 16 * i + fr] * sb;
-                sb_next = (full || kb + 2 < kblocks) ? sbp[kb + 2] : 0.0f;
-            }
-        }
-    };
-
-    // prologue: slices 0 and 1 in flight (both stages always filled, see the
-    // per-tensor kernel), slice 0's fragments and weights
-    if (kblocks > 0) {
-        stage(st0, sa0, sb0, 0);
-        stage(st1, sa1, sb1, 1);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = read_frag(st0, wm * 64 + 16 * i + fr, fg);
-        b = read_frag(st0 + kBM * kBK, wn * 128 + fr, fg);
-        if constexpr (kRowB) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sai[i] = sa0[wm * 64 + 16 * i + fr];
-        } else {
-            const float sb = sbp[0];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wi[i] = sa0[wm * 64 + 16 * i + fr] * sb;
-            sb_next = kblocks > 1 ? sbp[1] : 0.0f;
-        }
-    }
-    // steady state: slices kb + 2 and kb + 3 exist (no guards)
-    int kb = 0;
-    for (; kb + 4 <= kblocks; kb += 2) {
-        slice(kb, st0, sa0, sb0, st1, sa1, true);
-        slice(kb + 1, st1, sa1, sb1, st0, sa0, true);
-    }
-    // at most three slices remain; kb is even
-    if (kb < kblocks) slice(kb, st0, sa0, sb0, st1, sa1, false);
-    if (kb + 1 < kblocks) slice(kb + 1, st1, sa1, sb1, st0, sa0, false);
-    if (kb + 2 < kblocks) slice(kb + 2, st0, sa0, sb0, st1, sa1, false);
-
-    // epilogue: lane (fr, fg) of tile (i, j) holds C[row][4 consecutive cols]
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t row = m0 + wm * 64 + 16 * i + fr;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t col = n0 + wn * 128 + 16 * j + 4 * fg;
-            if (row < M && col < N) store_out4<kF32, kAmax>(C, row * N + col, acc[i][j], m);
-        }
-    }
-    if constexpr (kAmax) {
-        m = block_max_u32<kBSThreads>(m, red);
-        if (tid == 0) gs->part[blockIdx.x] = canonical_amax_bits(m);
-    }
-}
-
-int gemm_grid(int64_t M, int64_t N, int mode)
-{
-    (void)mode;
-    return (int)(((M + kBM - 1) / kBM) * ((N + kBM - 1) / kBM));
-}
-
-template <int FA, int FB, bool kF32>
-static hipError_t launch_gemm_t(const uint8_t *A, const float *sA, const uint8_t *B, const float *sB, int64_t M,
-                                int64_t N, int64_t K, int mode, void *C, float *amax_out, GridScratch *gs,
-                                hipStream_t s)
-{
-    const int grid = gemm_grid(M, N, mode);
-    const int m = (int)M, n = (int)N, k = (int)K;
-    if (mode == 0) {
-        if (amax_out)
-            gemm_pt_kernel<FA, FB, true, kF32, false><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
-        else
-            gemm_pt_kernel<FA, FB, false, kF32, false><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
-    } else if (mode == 3) {
-        if (amax_out)
-            gemm_pt_kernel<FA, FB, true, kF32, true><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
-        else
-            gemm_pt_kernel<FA, FB, false, kF32, true><<<grid, kGemmThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
-    } else if (mode == 1) {
-        if (amax_out)
-            gemm_bs_kernel<FA, FB, true, kF32, false><<<grid, kBSThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
-        else
-            gemm_bs_kernel<FA, FB, false, kF32, false><<<grid, kBSThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
-    } else {
-        if (amax_out)
-            gemm_bs_kernel<FA, FB, true, kF32, true><<<grid, kBSThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
-        else
-            gemm_bs_kernel<FA, FB, false, kF32, true><<<grid, kBSThreads, 0, s>>>(A, B, sA, sB, m, n, k, C, gs);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !amax_out) return e;
-    return launch_finish_amax(gs, grid, amax_out, s);
-}
-
-template <int FA, int FB>
-static hipError_t launch_gemm_f(const uint8_t *A, const float *sA, const uint8_t *B, const float *sB, int64_t M,
-                                int64_t N, int64_t K, int mode, void *C, int c_dtype, float *amax_out,
-                                GridScratch *gs, hipStream_t s)
-{
-    if (c_dtype == kF32) return launch_gemm_t<FA, FB, true>(A, sA, B, sB, M, N, K, mode, C, amax_out, gs, s);
-    return launch_gemm_t<FA, FB, false>(A, sA, B, sB, M, N, K, mode, C, amax_out, gs, s);
-}
-
 hipError_t launch_gemm(const uint8_t *A, int fa, const float *sA, const uint8_t *B, int fb, const float *sB, int64_t M,
-                       int64_t N, int64_t K, int mode, void *C, int c_dtype, float *amax_out, GridScratch *gs,
-                       hipStream_t s)
+                       int64_t N, int64_t K, int mode, void *C, int out_kind, const float *bias, int act,
+                       const float *out_scale_inv, float *amax_out, GridScratch *gs, hipStream_t s)
 {
-    if (fa == kE4M3 && fb == kE4M3)
-        return launch_gemm_f<kE4M3, kE4M3>(A, sA, B, sB, M, N, K, mode, C, c_dtype, amax_out, gs, s);
-    if (fa == kE5M2 && fb == kE4M3)
-        return launch_gemm_f<kE5M2, kE4M3>(A, sA, B, sB, M, N, K, mode, C, c_dtype, amax_out, gs, s);
-    if (fa == kE4M3 && fb == kE5M2)
-        return launch_gemm_f<kE4M3, kE5M2>(A, sA, B, sB, M, N, K, mode, C, c_dtype, amax_out, gs, s);
-    return launch_gemm_f<kE5M2, kE5M2>(A, sA, B, sB, M, N, K, mode, C, c_dtype, amax_out, gs, s);
+    const GemmArgs a{A, B, sA, sB, M, N, K, mode, C, out_kind, bias, act, out_scale_inv, amax_out, gs, s};
+    if (fa == kE4M3 && fb == kE4M3) return launch_gemm_e4m3_e4m3(a);
+    if (fa == kE5M2 && fb == kE4M3) return launch_gemm_e5m2_e4m3(a);
+    if (fa == kE4M3 && fb == kE5M2) return launch_gemm_e4m3_e5m2(a);
+    return launch_gemm_e5m2_e5m2(a);
 }
 
 } // namespace fp8q

@@ -65,6 +65,16 @@ extern "C" {
 #define FP8Q_BLOCK_1x128_1x128 2
 #define FP8Q_MXFP8 3
 
+/* output types of fp8_scaled_gemm_fused beyond FP8Q_F32 / FP8Q_BF16: FP8
+ * codes of the named format */
+#define FP8Q_OUT_E4M3FN 2
+#define FP8Q_OUT_E5M2 3
+
+/* epilogue activations, [MFP8] section 6 */
+#define FP8Q_ACT_NONE 0
+#define FP8Q_ACT_RELU 1
+#define FP8Q_ACT_GELU 2
+
 /*
  * fp8_amax -- *amax = max_i |x_i| over n elements ([MFP8] section 4, the
  * amax of compute_fp8_scale; section 11, tensor_amax).
@@ -234,6 +244,36 @@ int fp8_quantize_delayed(const void *x, int32_t dtype, int64_t n, int32_t fmt, f
 int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb, const float *sB,
                     int64_t M, int64_t N, int64_t K, int32_t mode, void *C, int32_t c_dtype, float *amax_out,
                     void *stream);
+
+/*
+ * fp8_scaled_gemm_fused -- fp8_scaled_gemm with the epilogue fusions of
+ * [MFP8] section 6 (bias addition and an activation folded into the GEMM
+ * epilogue, so the intermediate never makes a bf16 round trip through
+ * memory) and an FP8 output cast with a given scale, whose amax feeds the
+ * next scaling decision ([MFP8] section 4: amax of the high-precision tensor
+ * recorded for delayed scaling; section 5: the history update).
+ *   A, fa, sA, B, fb, sB, M, N, K, mode: as fp8_scaled_gemm; v[m,n] is the
+ *   value fp8_scaled_gemm would round to its output type (fp32).
+ *   bias (nullable): fp32 [N], 16-byte aligned; added along the rows:
+ *        y = act(v[m,n] + bias[n]) in binary32.
+ *   act: FP8Q_ACT_NONE; FP8Q_ACT_RELU (y < 0 -> 0, NaN kept);
+ *        FP8Q_ACT_GELU, the exact form v * Phi(v), Phi the standard normal
+ *        CDF (not the tanh approximation), evaluated in binary32 to within
+ *        2^-21 |v| of v * Phi(v); +inf maps to +inf, -inf and NaN to NaN.
+ *   C [M][N] of type c_type: FP8Q_BF16 (round to nearest even), FP8Q_F32, or
+ *        FP8Q_OUT_E4M3FN / FP8Q_OUT_E5M2: codes of fl32(y * fl32(1/s)) with
+ *        s = *c_scale_inv (the output's dequant scale, 4-byte aligned float,
+ *        required for and only for FP8 outputs), saturating RNE cast.
+ *   amax_out (nullable): max |C| over the emitted values for bf16 / fp32
+ *        output, max |y| over the values before the cast for FP8 output.
+ * Errors: those of fp8_scaled_gemm; FP8Q_EINVAL for an unknown c_type or
+ * act, a missing or stray c_scale_inv, a misaligned bias, or C or amax_out
+ * overlapping bias or c_scale_inv.
+ */
+int fp8_scaled_gemm_fused(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb,
+                          const float *sB, int64_t M, int64_t N, int64_t K, int32_t mode, const float *bias,
+                          int32_t act, void *C, int32_t c_type, const float *c_scale_inv, float *amax_out,
+                          void *stream);
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char *fp8q_last_error(void);

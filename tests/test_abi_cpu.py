@@ -46,6 +46,10 @@ def test_enum_values_match_header():
     assert int(defs["FP8Q_BLOCK_1x128_128x128"]) == fq.BLOCK_1x128_128x128 == oracle.BLOCK_1x128_128x128
     assert int(defs["FP8Q_BLOCK_1x128_1x128"]) == fq.BLOCK_1x128_1x128 == oracle.BLOCK_1x128_1x128
     assert int(defs["FP8Q_MXFP8"]) == fq.MXFP8 == oracle.MXFP8
+    assert int(defs["FP8Q_OUT_E4M3FN"]) == fq.OUT_E4M3FN and int(defs["FP8Q_OUT_E5M2"]) == fq.OUT_E5M2
+    assert int(defs["FP8Q_ACT_NONE"]) == fq.ACT_NONE == oracle.ACT_NONE
+    assert int(defs["FP8Q_ACT_RELU"]) == fq.ACT_RELU == oracle.ACT_RELU
+    assert int(defs["FP8Q_ACT_GELU"]) == fq.ACT_GELU == oracle.ACT_GELU
 
 
 def _expect(status, code, fragment):
@@ -146,6 +150,30 @@ def test_gemm_validation():
     _expect(g(A, 0, None, B, 0, BAD + 4, 128, 128, 128, 0, C, fq.BF16, None, S), fq.EINVAL, "sA")
     _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 0, A + 64, fq.BF16, None, S), fq.EINVAL, "overlaps")
     _expect(g(A + 8, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 0, C, fq.BF16, None, S), fq.EINVAL, "16-byte")
+
+
+def test_gemm_fused_validation():
+    g = L.fp8_scaled_gemm_fused
+    A, B, C, SI, BIAS = BAD + 0x100000, BAD + 0x200000, BAD + 0x300000, BAD + 0x8, BAD + 0x400000
+    E4OUT = fq.OUT_E4M3FN
+
+    def call(bias=None, act=0, c=C, c_type=fq.BF16, si=None, amax=None, mode=0):
+        return g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, mode, bias, act, c, c_type, si, amax, S)
+
+    _expect(call(act=3), fq.EINVAL, "activation")
+    _expect(call(c_type=4), fq.EINVAL, "output type")
+    _expect(call(c_type=E4OUT), fq.EINVAL, "c_scale_inv")
+    _expect(call(c_type=E4OUT, si=SI + 2), fq.EINVAL, "c_scale_inv")
+    _expect(call(si=SI), fq.EINVAL, "only for an FP8")
+    _expect(call(bias=BIAS + 4), fq.EINVAL, "bias")
+    _expect(call(mode=4), fq.EINVAL, "mode")
+    # an FP8 C of 128x128 spans 16 KiB: a bias 8 KiB in overlaps it
+    _expect(call(bias=C + 0x2000, c_type=E4OUT, si=SI), fq.EINVAL, "overlaps")
+    _expect(call(c_type=E4OUT, si=C + 0x3000), fq.EINVAL, "overlaps")
+    _expect(call(bias=BIAS, amax=BIAS + 0x100), fq.EINVAL, "amax_out overlaps")
+    _expect(call(c_type=E4OUT, si=SI, amax=SI), fq.EINVAL, "amax_out overlaps")
+    # the plain entry point does not take the fused output types
+    _expect(L.fp8_scaled_gemm(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 0, C, E4OUT, None, S), fq.EINVAL, "dtype")
 
 
 def test_last_error_is_thread_local_string():
