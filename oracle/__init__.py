@@ -430,3 +430,92 @@ def epilogue_fp8_codes(y: np.ndarray, fmt: int, out_scale_inv):
     y32 = np.asarray(y, dtype=np.float64).astype(np.float32)
     return quantize(y32, fmt, reciprocal(out_scale_inv)), amax(y32)
 
+
+
+# ---------------------------------------- per-direction quantization, stats ---
+COLSRC_ORIGINAL, COLSRC_ROWWISE_DEQUANTIZED = 0, 1
+
+
+def _as_f32(x: np.ndarray) -> np.ndarray:
+    """float32 values of a bf16 (uint16 bit patterns) or float32 tensor."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32)
+    return x.astype(np.float32)
+
+
+def quantize_hybrid(x: np.ndarray, row_fmt: int, col_fmt: int, col_source: int, *, amax_in=None,
+                    row_margin: int = 0, col_margin: int = 0, row_scale_inv_in=None, col_scale_inv_in=None):
+    """Per-direction ("hybrid") per-tensor quantization of a 2-D tensor
+    ("[Pytorch][Common] Hybrid quantization #2817": the rowwise and the
+    columnwise copies may use different formats and scaling recipes; the
+    columnwise copy is quantized from the original input, or from the
+    dequantized rowwise values).
+
+    Each direction is a per-tensor quantizer of its own source: the rowwise
+    source is x, the columnwise source is x (original) or
+    x' = dequantize(q_row) (rowwise_dequantized).  With ``amax_in`` (current
+    scaling) each direction takes the amax of its own source -- amax_in for x,
+    max |x'| for x' -- with its own format and margin; otherwise the two given
+    dequant scales are used.  Returns dict(q_row [R][C], q_col [C][R],
+    row_scale_inv, col_scale_inv)."""
+    if (amax_in is None) == (row_scale_inv_in is None or col_scale_inv_in is None):
+        raise ValueError("exactly one of amax_in / the pair of given scales")
+    xf = np.ascontiguousarray(_as_f32(x))
+    if amax_in is not None:
+        s_r, sc_r = current_scale(amax_in, row_fmt, row_margin)
+    else:
+        s_r = np.float32(row_scale_inv_in)
+        sc_r = reciprocal(s_r)
+    q_row = quantize(xf, row_fmt, sc_r)
+    if col_source == COLSRC_ORIGINAL:
+        src = xf
+        col_amax = amax_in
+    elif col_source == COLSRC_ROWWISE_DEQUANTIZED:
+        src = dequantize(q_row, row_fmt, s_r)
+        col_amax = None if amax_in is None else amax(src)
+    else:
+        raise ValueError("unknown columnwise source %r" % col_source)
+    if amax_in is not None:
+        s_c, sc_c = current_scale(col_amax, col_fmt, col_margin)
+    else:
+        s_c = np.float32(col_scale_inv_in)
+        sc_c = reciprocal(s_c)
+    q_col = transpose(quantize(np.ascontiguousarray(src), col_fmt, sc_c))
+    return dict(q_row=q_row, q_col=q_col, row_scale_inv=s_r, col_scale_inv=s_c)
+
+
+def cast_stats(x: np.ndarray, fmt: int, scale_inv) -> np.ndarray:
+    """Diagnostics of a per-tensor cast with dequant scale s ("Megatron FP8",
+    section 24: per-tensor amax, scale, overflow and underflow counts of every
+    cast).  With y = fl32(x * fl32(1/s)) and c its code, returns uint64
+    [overflows, underflows, nans, nonzeros]:
+      overflows  -- x not NaN and |y| > FP8_MAX (the cast saturates them);
+      underflows -- x finite and nonzero, and c is a zero code;
+      nans       -- x is NaN;
+      nonzeros   -- x not NaN and x != 0 (the population underflows are
+                    counted against)."""
+    xf = np.ascontiguousarray(_as_f32(x))
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = xf * reciprocal(scale_inv)
+    c = encode(fmt, y)
+    nan = np.isnan(xf)
+    nonzero = ~nan & (xf != 0)
+    over = ~nan & (np.abs(y) > fmax(fmt))
+    under = nonzero & np.isfinite(xf) & ((c & 0x7F) == 0)
+    return np.array([over.sum(), under.sum(), nan.sum(), nonzero.sum()], dtype=np.uint64)
+
+
+def quantize_error_feedback(g: np.ndarray, residual: np.ndarray, fmt: int, scale_inv):
+    """One step of FP8 quantization with error feedback ("Megatron FP8",
+    section 25: quantize g + residual, send the codes, keep what the cast lost
+    for the next step):
+      v = fl32(g + residual),  q = codes of fl32(v * fl32(1/s)),
+      residual' = fl32(v - fl32(value(q) * s)),
+    and the amax of v (what delayed scaling records for the next scale).
+    Returns (q, residual', amax_v)."""
+    v = (_as_f32(g) + np.asarray(residual, dtype=np.float32)).astype(np.float32)
+    q = quantize(np.ascontiguousarray(v), fmt, reciprocal(scale_inv))
+    with np.errstate(invalid="ignore"):
+        r = (v - dequantize(q, fmt, scale_inv)).astype(np.float32)
+    return q, r, amax(np.ascontiguousarray(v))

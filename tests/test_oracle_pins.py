@@ -703,3 +703,126 @@ def test_epilogue_fp8_output_codes():
     # between 448 and 512 (step 64 in [256, 512)): 512 is nearer
     q, am = oracle.epilogue_fp8_codes(np.array([[1000.0, -0.25]]), E5, 2.0)
     assert [oracle.decode(E5, int(c)) for c in q[0]] == [512.0, -0.125]
+
+
+# ------------------------------------ per-direction quantization, diagnostics ----
+def test_hybrid_same_format_is_rowwise_colwise():
+    """One format, one scale, columnwise from the original: the hybrid
+    quantizer reduces to the rowwise + columnwise cast (pinned above)."""
+    x = workloads.delayed_step(3, 256, 384)
+    am = oracle.amax(x)
+    for fmt in (E4, E5):
+        h = oracle.quantize_hybrid(x, fmt, fmt, oracle.COLSRC_ORIGINAL, amax_in=am, row_margin=1, col_margin=1)
+        s, sc = oracle.current_scale(am, fmt, 1)
+        q_row, q_col = oracle.quantize_rowwise_colwise(x, fmt, sc)
+        assert np.array_equal(h["q_row"], q_row) and np.array_equal(h["q_col"], q_col)
+        assert f32_bits(h["row_scale_inv"]) == f32_bits(s) == f32_bits(h["col_scale_inv"])
+
+
+def test_hybrid_cross_format_directions_are_independent():
+    """E4M3 rows and E5M2 columns from the original: each copy is the
+    per-tensor cast of x (resp. x^T) in its own format, with its own margin."""
+    x = workloads.block_act(128, 256, seed=4)
+    am = oracle.amax(x)
+    h = oracle.quantize_hybrid(x, E4, E5, oracle.COLSRC_ORIGINAL, amax_in=am, row_margin=0, col_margin=2)
+    r = oracle.quantize_tensor(x, E4, amax_in=am, margin=0)
+    c = oracle.quantize_tensor(oracle.transpose(x), E5, amax_in=am, margin=2)
+    assert np.array_equal(h["q_row"], r["q"]) and np.array_equal(h["q_col"], c["q"])
+
+
+def test_hybrid_rowwise_dequantized_is_idempotent_in_one_format():
+    """Quantize, dequantize, quantize again with the same format and scale
+    gives the same codes (the FP8 grid is far coarser than one fp32 rounding
+    of value * s * (1/s)), so with equal given scales q_col = q_row^T; with a
+    coarser column format it equals the E5M2 cast of the dequantized values,
+    which differs from the cast of the original somewhere."""
+    x = workloads.delayed_step(5, 128, 256)
+    for s in (np.float32(0.3), np.float32(1 / 448), np.float32(2.0 ** -9)):
+        h = oracle.quantize_hybrid(x, E4, E4, oracle.COLSRC_ROWWISE_DEQUANTIZED, row_scale_inv_in=s,
+                                   col_scale_inv_in=s)
+        assert np.array_equal(h["q_col"], oracle.transpose(h["q_row"]))
+    s = np.float32(oracle.amax(x) / 448)
+    d = oracle.quantize_hybrid(x, E4, E5, oracle.COLSRC_ROWWISE_DEQUANTIZED, row_scale_inv_in=s, col_scale_inv_in=s)
+    o = oracle.quantize_hybrid(x, E4, E5, oracle.COLSRC_ORIGINAL, row_scale_inv_in=s, col_scale_inv_in=s)
+    assert np.array_equal(d["q_row"], o["q_row"])
+    xd = oracle.dequantize(d["q_row"], E4, s)
+    assert np.array_equal(d["q_col"], oracle.transpose(oracle.quantize(xd, E5, oracle.reciprocal(s))))
+    assert not np.array_equal(d["q_col"], o["q_col"])
+
+
+def test_hybrid_dequantized_source_takes_its_own_amax():
+    """Current scaling of the columnwise copy from the dequantized rowwise
+    values uses max |x'|: with margin 2 the rowwise cast maps the largest
+    element to 448 / 4 = 112 (exact in E4M3), so max |x'| = fl32(112 * s_r)."""
+    x = np.float32([[3.0, -7.25, 0.5, 1.0] * 4] * 16)
+    h = oracle.quantize_hybrid(x, E4, E5, oracle.COLSRC_ROWWISE_DEQUANTIZED, amax_in=np.float32(7.25),
+                               row_margin=2, col_margin=0)
+    s_r = np.float32(np.float32(7.25 / 448) * 4)
+    assert f32_bits(h["row_scale_inv"]) == f32_bits(s_r)
+    amax_d = np.float32(np.float32(112.0) * s_r)
+    assert f32_bits(h["col_scale_inv"]) == f32_bits(np.float32(amax_d / np.float32(57344)))
+
+
+def test_cast_stats_hand_cases():
+    """E4M3 with s = 1: 449, 500 and +inf exceed 448 (3 overflows; -448 does
+    not); 2^-10 (a tie, to the even zero) and 3e-4 become zero codes while
+    2^-10 * 1.1 rounds up to 2^-9 (2 underflows); one NaN; 0 and -0 are not
+    counted as nonzero."""
+    x = np.float32([0.0, -0.0, 449, 500, -448, np.inf, 2.0 ** -10, 3e-4, 1.1 * 2.0 ** -10, np.nan, 1.0, -2.5])
+    st = oracle.cast_stats(x, E4, 1.0)
+    assert st.tolist() == [3, 2, 1, 9]
+    # E5M2 reaches 57344 and 2^-16: with s = 1/64 the values are multiplied by 64
+    st = oracle.cast_stats(np.float32([900.0, 896.0, 2.0 ** -23, 2.0 ** -22]), E5, 1 / 64)
+    assert st.tolist() == [1, 1, 0, 4]
+
+
+def test_cast_stats_counts_against_the_encoder():
+    """On every bf16 pattern at three scales: overflows are the products
+    (formed in float64, exact, and rounded once to float32) beyond FP8_MAX,
+    and underflows the nonzero finite inputs that the pinned cast maps to a
+    zero code."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    xf = oracle._as_f32(bits)
+    for fmt in (E4, E5):
+        for s in (1.0, 1e-3, 37.5):
+            st = oracle.cast_stats(bits, fmt, s)
+            with np.errstate(over="ignore", invalid="ignore"):
+                y = np.float32(xf.astype(np.float64) * float(oracle.reciprocal(s)))
+            fin = np.isfinite(xf)
+            assert st[2] == np.isnan(xf).sum()
+            assert st[0] == (~np.isnan(xf) & (np.abs(y) > oracle.fmax(fmt))).sum()
+            zero_code = (oracle.quantize(bits, fmt, oracle.reciprocal(s)) & 0x7F) == 0
+            assert st[1] == (fin & (xf != 0) & zero_code).sum()
+
+
+def _fp8_ulp(y: np.ndarray, fmt: int) -> np.ndarray:
+    """Spacing of the FP8 grid at |y| from the bit layout (bias, mantissa bits)."""
+    bias, mbits = (7, 3) if fmt == E4 else (15, 2)
+    e = np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -40)))
+    return 2.0 ** (np.maximum(e, 1 - bias) - mbits)
+
+
+def test_error_feedback_telescopes_and_stays_below_half_a_step():
+    """"Megatron FP8", section 25: with the residual carried over, the sum of
+    what was sent plus the last residual equals the sum of the inputs (up to
+    the fp32 roundings of v and of the residual, one ulp of |v| each per
+    step), and each residual is at most half an FP8 step of its value."""
+    rng = np.random.default_rng(3)
+    n, T, s = 4096, 24, np.float32(2.0 ** -12)
+    r = np.zeros(n, np.float32)
+    sent = np.zeros(n, np.float64)
+    total = np.zeros(n, np.float64)
+    slack = np.zeros(n, np.float64)
+    for t in range(T):
+        g = workloads.to_bf16_bits(rng.standard_normal(n) * 1e-3 * (1 + t % 3))
+        q, r_new, am = oracle.quantize_error_feedback(g, r, E5, s)
+        v = oracle._as_f32(g).astype(np.float64) + r.astype(np.float64)
+        assert am == np.float32(np.max(np.abs(np.float32(v))))
+        dq = oracle.dequantize(q, E5, s).astype(np.float64)
+        y = np.float32(v) * float(oracle.reciprocal(s))
+        assert np.all(np.abs(r_new) <= 0.5 * _fp8_ulp(y, E5) * float(s) * (1 + 2.0 ** -20))
+        sent += dq
+        total += oracle._as_f32(g)
+        slack += 2.0 ** -23 * np.abs(v)
+        r = r_new
+    assert np.all(np.abs(sent + r - total) <= 2 * slack)
