@@ -26,6 +26,7 @@ ALGO_MAX, ALGO_MOST_RECENT = 0, 1
 PER_TENSOR, BLOCK_1x128_128x128, BLOCK_1x128_1x128, MXFP8 = 0, 1, 2, 3
 OUT_E4M3FN, OUT_E5M2 = 2, 3
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
+COLSRC_ORIGINAL, COLSRC_ROWWISE_DEQUANTIZED = 0, 1
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -46,6 +47,10 @@ SIGNATURES = {
     "fp8_scaled_gemm": [_VP, _I32, _VP, _VP, _I32, _VP, _I64, _I64, _I64, _I32, _VP, _I32, _VP, _VP],
     "fp8_scaled_gemm_fused": [_VP, _I32, _VP, _VP, _I32, _VP, _I64, _I64, _I64, _I32, _VP, _I32, _VP, _I32, _VP, _VP,
                               _VP],
+    "fp8_quantize_hybrid": [_VP, _I32, _I64, _I64, _I32, _I32, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
+                            _VP, _VP],
+    "fp8_cast_stats": [_VP, _I32, _I64, _I32, _VP, _VP, _VP],
+    "fp8_quantize_error_feedback": [_VP, _I32, _VP, _I64, _I32, _VP, _VP, _VP, _VP],
     "fp8q_last_error": [],
 }
 
@@ -192,3 +197,31 @@ def fp8_scaled_gemm_fused(A, fa, sA, B, fb, sB, mode, C, *, bias=None, act=ACT_N
         raise ValueError("bias must be float32 with N elements")
     _check(lib.fp8_scaled_gemm_fused(_ptr(A), fa, _ptr(sA), _ptr(B), fb, _ptr(sB), M, N, K, mode, _ptr(bias), act,
                                      _ptr(C), c_type, _ptr(c_scale_inv), _ptr(amax_out), _stream(stream)))
+
+
+def fp8_quantize_hybrid(x, row_fmt, col_fmt, col_source, *, q_row=None, q_col=None, amax_in=None, row_margin=0,
+                        col_margin=0, row_scale_inv_in=None, col_scale_inv_in=None, row_scale_inv_out=None,
+                        col_scale_inv_out=None, amax_out=None, stream=None):
+    """Per-direction per-tensor cast: rowwise codes in row_fmt, columnwise
+    (transposed) codes in col_fmt from x or from the dequantized rows."""
+    rows, cols = x.shape
+    _check(lib.fp8_quantize_hybrid(_ptr(x), _dtype(x), rows, cols, row_fmt, col_fmt, col_source, _ptr(amax_in),
+                                   row_margin, col_margin, _ptr(row_scale_inv_in), _ptr(col_scale_inv_in),
+                                   _ptr(q_row), _ptr(q_col), _ptr(row_scale_inv_out), _ptr(col_scale_inv_out),
+                                   _ptr(amax_out), _stream(stream)))
+
+
+def fp8_cast_stats(x, fmt, scale_inv, stats, stream=None):
+    """stats (int64 [4] on the device) = overflows, underflows, NaNs,
+    nonzeros of the cast of x with dequant scale scale_inv."""
+    if stats.dtype not in (torch.int64, torch.uint64) or stats.numel() != 4:
+        raise ValueError("stats must be a 4-element 64-bit integer tensor")
+    _check(lib.fp8_cast_stats(_ptr(x), _dtype(x), x.numel(), fmt, _ptr(scale_inv), _ptr(stats), _stream(stream)))
+
+
+def fp8_quantize_error_feedback(g, residual, fmt, scale_inv, q, amax_out=None, stream=None):
+    """q = cast(g + residual); residual <- (g + residual) - dequant(q), in place."""
+    if residual.dtype != torch.float32 or residual.numel() != g.numel():
+        raise ValueError("residual must be float32 with g's element count")
+    _check(lib.fp8_quantize_error_feedback(_ptr(g), _dtype(g), _ptr(residual), g.numel(), fmt, _ptr(scale_inv),
+                                           _ptr(q), _ptr(amax_out), _stream(stream)))

@@ -324,6 +324,116 @@ int fp8_quantize_delayed(const void *x, int32_t dtype, int64_t n, int32_t fmt, f
                       fn);
 }
 
+int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t row_fmt, int32_t col_fmt,
+                        int32_t col_source, const float *amax_in, int32_t row_margin, int32_t col_margin,
+                        const float *row_scale_inv_in, const float *col_scale_inv_in, uint8_t *q_row, uint8_t *q_col,
+                        float *row_scale_inv_out, float *col_scale_inv_out, float *amax_out, void *stream)
+{
+    const char *fn = "fp8_quantize_hybrid";
+    if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+    if (!valid_fmt(row_fmt) || !valid_fmt(col_fmt)) return fail(FP8Q_EINVAL, "%s: unknown format", fn);
+    if (col_source != FP8Q_COLSRC_ORIGINAL && col_source != FP8Q_COLSRC_ROWWISE_DEQUANTIZED)
+        return fail(FP8Q_EINVAL, "%s: unknown columnwise source %d", fn, (int)col_source);
+    if (rows < 0 || cols < 0) return fail(FP8Q_EINVAL, "%s: negative shape", fn);
+    if (rows % 16 || cols % 16) return fail(FP8Q_EUNSUPPORTED, "%s: rows and cols must be multiples of 16", fn);
+    if (rows * cols > 0 && !q_row && !q_col)
+        return fail(FP8Q_EINVAL, "%s: at least one of q_row / q_col is needed", fn);
+    if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 31)
+        return fail(FP8Q_EUNSUPPORTED, "%s: a dimension exceeds 2^31", fn);
+    const bool given = row_scale_inv_in || col_scale_inv_in;
+    if (amax_in ? given : !(row_scale_inv_in && col_scale_inv_in))
+        return fail(FP8Q_EINVAL, "%s: give either amax_in or both row_scale_inv_in and col_scale_inv_in", fn);
+    const float *ins[3] = {amax_in, row_scale_inv_in, col_scale_inv_in};
+    const float *outs[3] = {row_scale_inv_out, col_scale_inv_out, amax_out};
+    for (const float *p : ins)
+        if (p && !aligned(p, 4)) return fail(FP8Q_EINVAL, "%s: scale input not 4-byte aligned", fn);
+    for (int i = 0; i < 3; ++i) {
+        if (!outs[i]) continue;
+        if (!aligned(outs[i], 4)) return fail(FP8Q_EINVAL, "%s: scalar output not 4-byte aligned", fn);
+        for (const float *p : ins)
+            if (outs[i] == p) return fail(FP8Q_EINVAL, "%s: a scalar output aliases a scale input", fn);
+        for (int j = 0; j < i; ++j)
+            if (outs[j] == outs[i]) return fail(FP8Q_EINVAL, "%s: scalar outputs alias each other", fn);
+    }
+    const int64_t n = rows * cols;
+    if (n > 0) {
+        if (!x || !aligned(x, 16)) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
+        if ((q_row && !aligned(q_row, 16)) || (q_col && !aligned(q_col, 16)))
+            return fail(FP8Q_EINVAL, "%s: q_row / q_col must be 16-byte aligned", fn);
+        if (overlap(x, n * dsize(dtype), q_row, n) || overlap(x, n * dsize(dtype), q_col, n) ||
+            overlap(q_row, n, q_col, n))
+            return fail(FP8Q_EINVAL, "%s: output buffers overlap", fn);
+        for (const float *p : ins)
+            if (overlap(q_row, n, p, 4) || overlap(q_col, n, p, 4))
+                return fail(FP8Q_EINVAL, "%s: an output buffer overlaps a scale input", fn);
+        for (const float *p : outs)
+            if (overlap(x, n * dsize(dtype), p, 4) || overlap(q_row, n, p, 4) || overlap(q_col, n, p, 4))
+                return fail(FP8Q_EINVAL, "%s: a scalar output overlaps x or the codes", fn);
+    }
+    fp8q::GridScratch *gs = nullptr;
+    if (amax_out) {
+        hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
+        if (e != hipSuccess) return hip_status(e, fn);
+    }
+    const fp8q::ScaleSrc src{amax_in, row_scale_inv_in, (int)row_margin};
+    const fp8q::ScaleSrc src_col{amax_in, col_scale_inv_in, (int)col_margin};
+    return hip_status(fp8q::launch_hybrid(x, dtype, rows, cols, row_fmt, col_fmt, col_source, src, src_col, q_row,
+                                          q_col, row_scale_inv_out, col_scale_inv_out, amax_out, gs,
+                                          (hipStream_t)stream),
+                      fn);
+}
+
+int fp8_cast_stats(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *scale_inv, uint64_t *stats,
+                   void *stream)
+{
+    const char *fn = "fp8_cast_stats";
+    if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+    if (!valid_fmt(fmt)) return fail(FP8Q_EINVAL, "%s: unknown format %d", fn, (int)fmt);
+    if (n < 0) return fail(FP8Q_EINVAL, "%s: negative n", fn);
+    if (!scale_inv || !aligned(scale_inv, 4)) return fail(FP8Q_EINVAL, "%s: scale_inv must be 4-byte aligned", fn);
+    if (!stats || !aligned(stats, 8)) return fail(FP8Q_EINVAL, "%s: stats must be an 8-byte aligned pointer", fn);
+    if (overlap(stats, 32, scale_inv, 4)) return fail(FP8Q_EINVAL, "%s: stats overlaps scale_inv", fn);
+    if (n > 0) {
+        if (!x || !aligned(x, 16)) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
+        if (overlap(x, n * dsize(dtype), stats, 32)) return fail(FP8Q_EINVAL, "%s: stats overlaps x", fn);
+    }
+    fp8q::GridScratch *gs = nullptr;
+    hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
+    if (e != hipSuccess) return hip_status(e, fn);
+    return hip_status(fp8q::launch_cast_stats(x, dtype, n, fmt, scale_inv, stats, gs, (hipStream_t)stream), fn);
+}
+
+int fp8_quantize_error_feedback(const void *g, int32_t dtype, float *residual, int64_t n, int32_t fmt,
+                                const float *scale_inv, uint8_t *q, float *amax_out, void *stream)
+{
+    const char *fn = "fp8_quantize_error_feedback";
+    if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+    if (!valid_fmt(fmt)) return fail(FP8Q_EINVAL, "%s: unknown format %d", fn, (int)fmt);
+    if (n < 0) return fail(FP8Q_EINVAL, "%s: negative n", fn);
+    if (!scale_inv || !aligned(scale_inv, 4)) return fail(FP8Q_EINVAL, "%s: scale_inv must be 4-byte aligned", fn);
+    if (amax_out && (!aligned(amax_out, 4) || amax_out == scale_inv))
+        return fail(FP8Q_EINVAL, "%s: amax_out misaligned or aliasing scale_inv", fn);
+    if (n > 0) {
+        if (!g || !aligned(g, 16)) return fail(FP8Q_EINVAL, "%s: g must be a 16-byte aligned pointer", fn);
+        if (!residual || !aligned(residual, 16))
+            return fail(FP8Q_EINVAL, "%s: residual must be a 16-byte aligned pointer", fn);
+        if (!q || !aligned(q, 16)) return fail(FP8Q_EINVAL, "%s: q must be a 16-byte aligned pointer", fn);
+        const int64_t ng = n * dsize(dtype);
+        if (overlap(g, ng, residual, 4 * n) || overlap(g, ng, q, n) || overlap(residual, 4 * n, q, n))
+            return fail(FP8Q_EINVAL, "%s: g, residual and q overlap", fn);
+        if (overlap(g, ng, scale_inv, 4) || overlap(residual, 4 * n, scale_inv, 4) || overlap(q, n, scale_inv, 4) ||
+            overlap(g, ng, amax_out, 4) || overlap(residual, 4 * n, amax_out, 4) || overlap(q, n, amax_out, 4))
+            return fail(FP8Q_EINVAL, "%s: a tensor overlaps scale_inv or amax_out", fn);
+    }
+    fp8q::GridScratch *gs = nullptr;
+    if (amax_out) {
+        hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
+        if (e != hipSuccess) return hip_status(e, fn);
+    }
+    return hip_status(
+        fp8q::launch_error_feedback(g, dtype, residual, n, fmt, scale_inv, q, amax_out, gs, (hipStream_t)stream), fn);
+}
+
 } // extern "C"
 
 // Shared body of the two GEMM entry points.  c_type: FP8Q_F32, FP8Q_BF16,

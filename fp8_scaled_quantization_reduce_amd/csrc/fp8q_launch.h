@@ -12,9 +12,12 @@ namespace fp8q {
 // partial (the canonical magnitude max of its block) per block; a one-block
 // finish kernel folds them into the output.  No atomics and no state carried
 // between launches.  One per (device, stream); see get_grid_scratch.
+// The cast statistics keep four per-block counts the same way.
 constexpr int kMaxPartials = 65536;
+constexpr int kStats = 4; // overflows, underflows, NaNs, nonzeros
 struct GridScratch {
     uint32_t part[kMaxPartials];
+    uint32_t cnt[kStats][kMaxPartials];
 };
 
 // The scratch of the calling thread's current device and stream `s`,
@@ -48,6 +51,19 @@ hipError_t launch_block(const void *x, int dtype, int64_t rows, int64_t cols, in
 
 hipError_t launch_mx(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t *q_row, uint8_t *s_row,
                      uint8_t *q_col, uint8_t *s_col, hipStream_t s);
+
+hipError_t launch_hybrid(const void *x, int dtype, int64_t rows, int64_t cols, int row_fmt, int col_fmt,
+                         int col_source, ScaleSrc src, ScaleSrc src_col, uint8_t *q_row, uint8_t *q_col,
+                         float *row_scale_inv_out, float *col_scale_inv_out, float *amax_out, GridScratch *gs,
+                         hipStream_t s);
+
+// stats[0..3] (uint64): overflows, underflows, NaNs, nonzeros of the cast of
+// x with dequant scale *scale_inv.
+hipError_t launch_cast_stats(const void *x, int dtype, int64_t n, int fmt, const float *scale_inv, uint64_t *stats,
+                             GridScratch *gs, hipStream_t s);
+
+hipError_t launch_error_feedback(const void *g, int dtype, float *residual, int64_t n, int fmt,
+                                 const float *scale_inv, uint8_t *q, float *amax_out, GridScratch *gs, hipStream_t s);
 
 hipError_t launch_delayed(float *hist, int history_len, int n_cols, int col, const float *new_amax, int64_t step,
                           int fmt, int margin, int algo, float *scale, float *scale_inv, hipStream_t s);

@@ -155,6 +155,9 @@ __device__ __forceinline__ void store_out4(void *C, int64_t idx, int64_t col, v4
                                            float out_scale)
 {
     if constexpr (kFuse) {
+        // v is already rounded to binary32; the bias add rounds once more (no
+        // fused multiply-add with the scale that formed v)
+#pragma clang fp contract(off)
         if (epi.bias) v += *reinterpret_cast<const v4f *>(epi.bias + col);
         if (epi.act == kActRelu) {
 #pragma unroll

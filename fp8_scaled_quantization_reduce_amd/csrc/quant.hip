@@ -344,6 +344,235 @@ hipError_t launch_dequant(const uint8_t *q, int fmt, int64_t n, const float *sca
     return hipGetLastError();
 }
 
+// --------------------------------------------------------- cast statistics --
+// Diagnostics of a per-tensor cast ("Megatron FP8", section 24: per-tensor
+// overflow and underflow counts next to amax and scale).  With
+// y = fl32(x * fl32(1/s)):
+//   overflow  -- x not NaN and |y| > FP8_MAX (the cast saturates it);
+//   underflow -- x finite and nonzero and its code a zero code, i.e. |y| at
+//                most half the smallest subnormal (the tie rounds to the even
+//                zero): |y| <= 2^-10 (E4M3FN) or 2^-17 (E5M2);
+//   NaN, and nonzero (not NaN, x != 0).
+// A read-only stream like the amax; each block writes four partial counts and
+// a one-block kernel sums them into 64-bit totals.
+template <int F> struct Tiny;
+template <> struct Tiny<kE4M3> { static constexpr float kHalfMinSub = 0x1p-10f; };
+template <> struct Tiny<kE5M2> { static constexpr float kHalfMinSub = 0x1p-17f; };
+
+template <int F>
+__device__ __forceinline__ void stat1(float v, float scale, uint32_t c[kStats])
+{
+    const float y = fabsf(v * scale);
+    const bool nan = v != v;
+    const bool nz = !nan && v != 0.0f;
+    c[0] += (!nan && y > Fmt<F>::kMax) ? 1u : 0u;
+    c[1] += (nz && fabsf(v) != __builtin_inff() && y <= Tiny<F>::kHalfMinSub) ? 1u : 0u;
+    c[2] += nan ? 1u : 0u;
+    c[3] += nz ? 1u : 0u;
+}
+
+__device__ __forceinline__ void block_counts(uint32_t c[kStats], GridScratch *gs)
+{
+    __shared__ uint32_t red[kStats][kThreads / 64];
+#pragma unroll
+    for (int k = 0; k < kStats; ++k) {
+        uint32_t v = c[k];
+        // wave sum with DPP row shifts and broadcasts, like wave_max_u32
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+        if ((threadIdx.x & 63) == 63) red[k][threadIdx.x >> 6] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < kStats) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) t += red[threadIdx.x][w];
+        gs->cnt[threadIdx.x][blockIdx.x] = t;
+    }
+}
+
+constexpr int kStatsU = 4;
+
+template <int F, int DT>
+__global__ __launch_bounds__(kThreads) void cast_stats_kernel(const void *__restrict__ x, int64_t n,
+                                                              const float *__restrict__ scale_inv, GridScratch *gs)
+{
+    const float scale = 1.0f / *scale_inv;
+    const int64_t nch = n >> 4;
+    const int64_t units = ceil_div(nch, (int64_t)kThreads * kStatsU);
+    uint32_t c[kStats] = {0, 0, 0, 0};
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int64_t base = unit * kThreads * kStatsU + threadIdx.x;
+        Chunk16<DT> ch[kStatsU];
+#pragma unroll
+        for (int u = 0; u < kStatsU; ++u) {
+            const int64_t ci = base + u * kThreads;
+            ch[u].load(x, ci < nch ? ci : nch - 1);
+        }
+#pragma unroll
+        for (int u = 0; u < kStatsU; ++u) {
+            if (base + u * kThreads < nch) { // (counts, unlike a max, must not see a chunk twice)
+#pragma unroll
+                for (int k = 0; k < 16; ++k) stat1<F>(ch[u].get(k), scale, c);
+            }
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x < n - (nch << 4)) {
+        const int64_t e = (nch << 4) + threadIdx.x;
+        float v;
+        if constexpr (DT == kBF16)
+            v = __uint_as_float(((uint32_t)reinterpret_cast<const uint16_t *>(x)[e]) << 16);
+        else
+            v = reinterpret_cast<const float *>(x)[e];
+        stat1<F>(v, scale, c);
+    }
+    block_counts(c, gs);
+}
+
+constexpr int kStatsFinishThreads = 1024;
+
+__global__ __launch_bounds__(kStatsFinishThreads) void finish_stats_kernel(const GridScratch *__restrict__ gs,
+                                                                           int nparts, uint64_t *__restrict__ out)
+{
+    __shared__ uint64_t red[kStats][kStatsFinishThreads / 64];
+    uint64_t t[kStats] = {0, 0, 0, 0};
+    for (int i = threadIdx.x; i < nparts; i += kStatsFinishThreads) {
+#pragma unroll
+        for (int k = 0; k < kStats; ++k) t[k] += gs->cnt[k][i];
+    }
+#pragma unroll
+    for (int k = 0; k < kStats; ++k) {
+        uint64_t v = t[k];
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+        if ((threadIdx.x & 63) == 0) red[k][threadIdx.x >> 6] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < kStats) {
+        uint64_t v = 0;
+        for (int w = 0; w < kStatsFinishThreads / 64; ++w) v += red[threadIdx.x][w];
+        out[threadIdx.x] = v;
+    }
+}
+
+hipError_t launch_cast_stats(const void *x, int dtype, int64_t n, int fmt, const float *scale_inv, uint64_t *stats,
+                             GridScratch *gs, hipStream_t s)
+{
+    const int grid = flat_grid(ceil_div(n >> 4, (int64_t)kThreads * kStatsU));
+    if (fmt == kE4M3) {
+        if (dtype == kBF16) cast_stats_kernel<kE4M3, kBF16><<<grid, kThreads, 0, s>>>(x, n, scale_inv, gs);
+        else cast_stats_kernel<kE4M3, kF32><<<grid, kThreads, 0, s>>>(x, n, scale_inv, gs);
+    } else {
+        if (dtype == kBF16) cast_stats_kernel<kE5M2, kBF16><<<grid, kThreads, 0, s>>>(x, n, scale_inv, gs);
+        else cast_stats_kernel<kE5M2, kF32><<<grid, kThreads, 0, s>>>(x, n, scale_inv, gs);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    finish_stats_kernel<<<1, kStatsFinishThreads, 0, s>>>(gs, grid, stats);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------- error feedback --
+// One step of FP8 quantization with error feedback ("Megatron FP8", section
+// 25): v = fl32(g + r), q = encode(fl32(v * fl32(1/s))), and the residual
+// keeps what the cast lost, r = fl32(v - fl32(value(q) * s)), for the next
+// step; the amax of v is reduced in the same pass (delayed scaling records it).
+// A lane handles U chunks of 16 elements: the residual is read and written by
+// the same lane, so the in-place update needs no synchronisation.
+constexpr int kEfU = 2;
+
+template <int F, int DT>
+__global__ __launch_bounds__(kThreads) void error_feedback_kernel(const void *__restrict__ g,
+                                                                  float *__restrict__ residual, int64_t n,
+                                                                  const float *__restrict__ scale_inv,
+                                                                  uint8_t *__restrict__ q, GridScratch *gs,
+                                                                  bool amax)
+{
+    // v - value * s is rounded twice (product, then difference), as defined:
+    // no fused multiply-add
+#pragma clang fp contract(off)
+    const float s = *scale_inv;
+    const float scale = 1.0f / s;
+    const int64_t nch = n >> 4;
+    const int64_t units = ceil_div(nch, (int64_t)kThreads * kEfU);
+    float4 *__restrict__ rv = reinterpret_cast<float4 *>(residual);
+    uint4 *__restrict__ qv = reinterpret_cast<uint4 *>(q);
+    uint32_t m = 0;
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int64_t base = unit * kThreads * kEfU + threadIdx.x;
+        Chunk16<DT> ch[kEfU];
+        float4 r[kEfU][4];
+#pragma unroll
+        for (int u = 0; u < kEfU; ++u) {
+            const int64_t ci = base + u * kThreads;
+            const int64_t cc = ci < nch ? ci : nch - 1;
+            ch[u].load(g, cc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r[u][j] = rv[4 * cc + j];
+        }
+#pragma unroll
+        for (int u = 0; u < kEfU; ++u) {
+            float v[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[4 * j] = ch[u].get(4 * j) + r[u][j].x;
+                v[4 * j + 1] = ch[u].get(4 * j + 1) + r[u][j].y;
+                v[4 * j + 2] = ch[u].get(4 * j + 2) + r[u][j].z;
+                v[4 * j + 3] = ch[u].get(4 * j + 3) + r[u][j].w;
+            }
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[j] = encode4<F>(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], scale);
+            if (base + u * kThreads < nch) {
+                const int64_t ci = base + u * kThreads;
+                qv[ci] = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float2 lo = dec2<F, false>(w[j]), hi = dec2<F, true>(w[j]);
+                    rv[4 * ci + j] = make_float4(v[4 * j] - lo.x * s, v[4 * j + 1] - lo.y * s,
+                                                 v[4 * j + 2] - hi.x * s, v[4 * j + 3] - hi.y * s);
+                }
+#pragma unroll
+                for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(v[k]));
+            }
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x < n - (nch << 4)) {
+        const int64_t e = (nch << 4) + threadIdx.x;
+        float gv;
+        if constexpr (DT == kBF16)
+            gv = __uint_as_float(((uint32_t)reinterpret_cast<const uint16_t *>(g)[e]) << 16);
+        else
+            gv = reinterpret_cast<const float *>(g)[e];
+        const float v = gv + residual[e];
+        const uint32_t c = encode1<F>(v, scale);
+        q[e] = (uint8_t)c;
+        residual[e] = v - dec2<F, false>(c).x * s;
+        m = max(m, f32_absbits(v));
+    }
+    if (amax) block_partial(m, gs);
+}
+
+hipError_t launch_error_feedback(const void *g, int dtype, float *residual, int64_t n, int fmt,
+                                 const float *scale_inv, uint8_t *q, float *amax_out, GridScratch *gs, hipStream_t s)
+{
+    const int grid = flat_grid(ceil_div(n >> 4, (int64_t)kThreads * kEfU));
+    const bool am = amax_out != nullptr;
+    if (fmt == kE4M3) {
+        if (dtype == kBF16) error_feedback_kernel<kE4M3, kBF16><<<grid, kThreads, 0, s>>>(g, residual, n, scale_inv, q, gs, am);
+        else error_feedback_kernel<kE4M3, kF32><<<grid, kThreads, 0, s>>>(g, residual, n, scale_inv, q, gs, am);
+    } else {
+        if (dtype == kBF16) error_feedback_kernel<kE5M2, kBF16><<<grid, kThreads, 0, s>>>(g, residual, n, scale_inv, q, gs, am);
+        else error_feedback_kernel<kE5M2, kF32><<<grid, kThreads, 0, s>>>(g, residual, n, scale_inv, q, gs, am);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !am) return e;
+    return launch_finish_amax(gs, grid, amax_out, s);
+}
+
 // --------------------------------------------------------------- delayed --
 // Delayed-scaling update ("Megatron FP8", section 5): write the new amax at
 // slot step % L of column col, reduce the column (max, NaN-propagating) or take
@@ -475,7 +704,10 @@ hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, flo
 // four consecutive rows; the dwords land in LDS as a [128 col][128 row] byte
 // tile, rotated by 8 dwords per 16 columns so that the writes of a wave spread
 // over all banks while every 16-byte read stays contiguous.
-enum TileMode { kTilePerTensor = 0, kTileBlock128 = 1, kTileBlock1x128 = 2, kTileMX = 3 };
+// kTileHybrid + colF + 2 * dequantized_source: per-direction per-tensor
+// quantization (row codes in format F, column codes in format colF with their
+// own scale, from x or from the dequantized row codes).
+enum TileMode { kTilePerTensor = 0, kTileBlock128 = 1, kTileBlock1x128 = 2, kTileMX = 3, kTileHybrid = 4 };
 
 // MXFP8 shared scale of one 32-element block from its magnitude max (float
 // bits, NaN above 0x7F800000): e = floor(log2(amax)) - emax clamped to
@@ -623,8 +855,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                                                         ScaleSrc src, uint8_t *__restrict__ q_row,
                                                         uint8_t *__restrict__ q_col, void *__restrict__ s_row_p,
                                                         void *__restrict__ s_col_p, float *scale_inv_out,
-                                                        float *scale_out, GridScratch *gs)
+                                                        float *scale_out, GridScratch *gs, ScaleSrc src_col,
+                                                        float *col_scale_inv_out)
 {
+    constexpr bool kHybrid = kMode >= kTileHybrid;
+    constexpr int FC = kHybrid ? ((kMode - kTileHybrid) & 1) : F; // format of the column codes
+    constexpr bool kDeq = kHybrid && ((kMode - kTileHybrid) >> 1); // columns from the dequantized rows
     // block scales: fp32 (128x128, 1x128) or E8M0 bytes (MXFP8)
     float *__restrict__ s_row = reinterpret_cast<float *>(s_row_p);
     float *__restrict__ s_col = reinterpret_cast<float *>(s_col_p);
@@ -639,13 +875,24 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
     const int64_t tiles_c = ceil_div(cols, kTile), tiles = tiles_c * ceil_div(rows, kTile);
     const int64_t brows = rows / kTile, bcols = cols / kTile; // block-scale grid (block modes)
 
-    Scales sc_tensor{1.0f, 1.0f};
-    if constexpr (kMode == kTilePerTensor) {
+    Scales sc_tensor{1.0f, 1.0f}, sc_col{1.0f, 1.0f};
+    if constexpr (kMode == kTilePerTensor || kHybrid) {
         sc_tensor = resolve_scales<F>(src);
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             if (scale_inv_out) *scale_inv_out = sc_tensor.s;
             if (scale_out) *scale_out = sc_tensor.scale;
         }
+    }
+    if constexpr (kHybrid) {
+        if (kDeq && src_col.amax_in) {
+            // current scaling of the dequantized rows: their amax is the
+            // image of amax(x) under the (monotone) cast and dequantization
+            const uint32_t c = encode1<F>(*src_col.amax_in, sc_tensor.scale);
+            sc_col = current_scales(dec2<F, false>(c).x * sc_tensor.s, Fmt<FC>::kMax, src_col.margin);
+        } else {
+            sc_col = resolve_scales<FC>(src_col);
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0 && col_scale_inv_out) *col_scale_inv_out = sc_col.s;
     }
     uint32_t m_all = 0; // per-tensor fused amax
 
@@ -669,7 +916,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
 
         uint32_t cw[4][4]; // rowwise codes
 
-        if constexpr (kMode == kTilePerTensor) {
+        if constexpr (kMode == kTilePerTensor || kHybrid) {
             if constexpr (kAmax) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -831,6 +1078,39 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                                                 cs[1], cs[2], cs[3]);
                     }
                 stage_transposed(tl, cc, ig, jg);
+            } else if constexpr (kHybrid) {
+                // column codes in their own format and scale, from x or from
+                // x' = fl32(value(row code) * s_row)
+                uint32_t cc[4][4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        if constexpr (kDeq) {
+                            const uint32_t w = cw[r][q4];
+                            const float2 lo = dec2<F, false>(w), hi = dec2<F, true>(w);
+                            const float sr = sc_tensor.s;
+                            const float d0 = lo.x * sr, d1 = lo.y * sr, d2 = hi.x * sr, d3 = hi.y * sr;
+                            uint32_t c = encode4<FC>(d0, d1, d2, d3, sc_col.scale);
+                            // a NaN row code stays NaN with the sign of its code (the
+                            // decoder's NaN carries no sign of its own); rare path
+                            if (__builtin_expect((d0 != d0) | (d1 != d1) | (d2 != d2) | (d3 != d3), 0)) {
+                                const uint32_t flip =
+                                    ((__float_as_uint(sr) ^ __float_as_uint(sc_col.scale)) >> 24) & 0x80u;
+                                const float d[4] = {d0, d1, d2, d3};
+#pragma unroll
+                                for (int b = 0; b < 4; ++b)
+                                    if (d[b] != d[b])
+                                        c = (c & ~(0xFFu << (8 * b))) |
+                                            ((0x7Fu | (((w >> (8 * b)) & 0x80u) ^ flip)) << (8 * b));
+                            }
+                            cc[r][q4] = c;
+                        } else {
+                            cc[r][q4] = encode4<FC>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
+                                                    PV(r, 4 * q4 + 3), sc_col.scale);
+                        }
+                    }
+                stage_transposed(tl, cc, ig, jg);
             } else if constexpr (kMode != kTileMX) { // (MXFP8 staged its own column codes above)
                 stage_transposed(tl, cw, ig, jg);
             }
@@ -855,10 +1135,12 @@ static hipError_t launch_rc_t(const void *x, int64_t rows, int64_t cols, ScaleSr
     const int grid = tile_grid(rows, cols);
     if (amax_out)
         tile_kernel<F, DT, kTilePerTensor, true><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr,
-                                                                          nullptr, scale_inv_out, scale_out, gs);
+                                                                          nullptr, scale_inv_out, scale_out, gs,
+                                                                          ScaleSrc{}, nullptr);
     else
         tile_kernel<F, DT, kTilePerTensor, false><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr,
-                                                                           nullptr, scale_inv_out, scale_out, nullptr);
+                                                                           nullptr, scale_inv_out, scale_out, nullptr,
+                                                                           ScaleSrc{}, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !amax_out) return e;
     return launch_finish_amax(gs, grid, amax_out, s);
@@ -883,6 +1165,63 @@ hipError_t launch_rowwise_colwise(const void *x, int dtype, int64_t rows, int64_
     return launch_rc_t<kE5M2, kF32>(x, rows, cols, src, q_row, q_col, scale_inv_out, scale_out, amax_out, gs, s);
 }
 
+template <int F, int DT, int kMode>
+static hipError_t launch_hybrid_m(const void *x, int64_t rows, int64_t cols, ScaleSrc src, ScaleSrc src_col,
+                                  uint8_t *q_row, uint8_t *q_col, float *row_scale_inv_out, float *col_scale_inv_out,
+                                  float *amax_out, GridScratch *gs, hipStream_t s)
+{
+    const int grid = tile_grid(rows, cols);
+    if (amax_out)
+        tile_kernel<F, DT, kMode, true><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr, nullptr,
+                                                                 row_scale_inv_out, nullptr, gs, src_col,
+                                                                 col_scale_inv_out);
+    else
+        tile_kernel<F, DT, kMode, false><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr, nullptr,
+                                                                  row_scale_inv_out, nullptr, nullptr, src_col,
+                                                                  col_scale_inv_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !amax_out) return e;
+    return launch_finish_amax(gs, grid, amax_out, s);
+}
+
+template <int F, int DT>
+static hipError_t launch_hybrid_t(const void *x, int64_t rows, int64_t cols, int col_fmt, int col_source, ScaleSrc src,
+                                  ScaleSrc src_col, uint8_t *q_row, uint8_t *q_col, float *row_scale_inv_out,
+                                  float *col_scale_inv_out, float *amax_out, GridScratch *gs, hipStream_t s)
+{
+    const int mode = kTileHybrid + col_fmt + 2 * col_source;
+#define FP8Q_HYBRID(M)                                                                                              \
+    case M:                                                                                                         \
+        return launch_hybrid_m<F, DT, M>(x, rows, cols, src, src_col, q_row, q_col, row_scale_inv_out,              \
+                                         col_scale_inv_out, amax_out, gs, s)
+    switch (mode) {
+        FP8Q_HYBRID(kTileHybrid);
+        FP8Q_HYBRID(kTileHybrid + 1);
+        FP8Q_HYBRID(kTileHybrid + 2);
+        FP8Q_HYBRID(kTileHybrid + 3);
+    }
+#undef FP8Q_HYBRID
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_hybrid(const void *x, int dtype, int64_t rows, int64_t cols, int row_fmt, int col_fmt,
+                         int col_source, ScaleSrc src, ScaleSrc src_col, uint8_t *q_row, uint8_t *q_col,
+                         float *row_scale_inv_out, float *col_scale_inv_out, float *amax_out, GridScratch *gs,
+                         hipStream_t s)
+{
+    // an empty tensor still publishes both scales and an amax of 0: the grid
+    // is one block with no tiles to visit
+#define FP8Q_ARGS x, rows, cols, col_fmt, col_source, src, src_col, q_row, q_col, row_scale_inv_out, col_scale_inv_out, \
+                  amax_out, gs, s
+    if (row_fmt == kE4M3) {
+        if (dtype == kBF16) return launch_hybrid_t<kE4M3, kBF16>(FP8Q_ARGS);
+        return launch_hybrid_t<kE4M3, kF32>(FP8Q_ARGS);
+    }
+    if (dtype == kBF16) return launch_hybrid_t<kE5M2, kBF16>(FP8Q_ARGS);
+    return launch_hybrid_t<kE5M2, kF32>(FP8Q_ARGS);
+#undef FP8Q_ARGS
+}
+
 template <int F, int DT>
 static hipError_t launch_block_t(const void *x, int64_t rows, int64_t cols, int block_rows, uint8_t *q_row,
                                  float *s_row, uint8_t *q_col, float *s_col, hipStream_t s)
@@ -891,10 +1230,12 @@ static hipError_t launch_block_t(const void *x, int64_t rows, int64_t cols, int 
     const ScaleSrc none{nullptr, nullptr, 0};
     if (block_rows == 128)
         tile_kernel<F, DT, kTileBlock128, false><<<grid, kThreads, 0, s>>>(x, rows, cols, none, q_row, q_col, s_row,
-                                                                          s_col, nullptr, nullptr, nullptr);
+                                                                          s_col, nullptr, nullptr, nullptr, none,
+                                                                          nullptr);
     else
         tile_kernel<F, DT, kTileBlock1x128, false><<<grid, kThreads, 0, s>>>(x, rows, cols, none, q_row, q_col,
-                                                                            s_row, s_col, nullptr, nullptr, nullptr);
+                                                                            s_row, s_col, nullptr, nullptr, nullptr,
+                                                                            none, nullptr);
     return hipGetLastError();
 }
 
@@ -904,7 +1245,7 @@ static hipError_t launch_mx_t(const void *x, int64_t rows, int64_t cols, uint8_t
 {
     const ScaleSrc none{nullptr, nullptr, 0};
     tile_kernel<F, DT, kTileMX, false><<<tile_grid(rows, cols), kThreads, 0, s>>>(
-        x, rows, cols, none, q_row, q_col, s_row, s_col, nullptr, nullptr, nullptr);
+        x, rows, cols, none, q_row, q_col, s_row, s_col, nullptr, nullptr, nullptr, none, nullptr);
     return hipGetLastError();
 }
 

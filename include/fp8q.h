@@ -11,8 +11,8 @@
  *  - All pointers are DEVICE memory owned by the caller, unless stated.  The
  *    library never copies device->host and never synchronises: each call
  *    enqueues its kernels on `stream` (a hipStream_t; NULL = the default
- *    stream) and returns.  The only device memory it allocates is a 256 KiB
- *    reduction scratch (per-block partial maxima) per (device, stream) pair,
+ *    stream) and returns.  The only device memory it allocates is a 1.25 MiB
+ *    reduction scratch (per-block partial maxima and counts) per (device, stream) pair,
  *    on the first call on that pair that reduces an amax, held until the
  *    process ends.  Calls on one stream use that scratch in stream order; two
  *    host threads that enqueue on the same stream handle concurrently must
@@ -69,6 +69,10 @@ extern "C" {
  * codes of the named format */
 #define FP8Q_OUT_E4M3FN 2
 #define FP8Q_OUT_E5M2 3
+
+/* source of the columnwise copy in fp8_quantize_hybrid, [HYBRID] */
+#define FP8Q_COLSRC_ORIGINAL 0
+#define FP8Q_COLSRC_ROWWISE_DEQUANTIZED 1
 
 /* epilogue activations, [MFP8] section 6 */
 #define FP8Q_ACT_NONE 0
@@ -274,6 +278,66 @@ int fp8_scaled_gemm_fused(const uint8_t *A, int32_t fa, const float *sA, const u
                           const float *sB, int64_t M, int64_t N, int64_t K, int32_t mode, const float *bias,
                           int32_t act, void *C, int32_t c_type, const float *c_scale_inv, float *amax_out,
                           void *stream);
+
+/*
+ * fp8_quantize_hybrid -- per-direction ("hybrid") per-tensor quantization of
+ * a 2-D tensor ([HYBRID]: the rowwise and the columnwise copies may use
+ * different formats and scaling recipes; the columnwise copy is quantized
+ * from the original input or from the dequantized rowwise values).
+ *   x [rows][cols] of dtype; q_row [rows][cols] codes of row_fmt,
+ *   q_col [cols][rows] codes of col_fmt (either may be NULL, not both unless
+ *   the tensor is empty; with the dequantized source the row codes are formed
+ *   even when q_row is NULL).  An empty tensor still publishes both scales
+ *   and an amax of 0.
+ *   col_source FP8Q_COLSRC_ORIGINAL: q_col = cast of x^T;
+ *              FP8Q_COLSRC_ROWWISE_DEQUANTIZED: q_col = cast of x'^T with
+ *              x' = fl32(value(q_row) * s_row).
+ *   Scales, exactly one way:
+ *     amax_in (= max |x|): current scaling per direction of its own source,
+ *       s_row from amax_in with row_fmt and row_margin; s_col from amax_in
+ *       (original source) or from max |x'| (which the cast maps exactly from
+ *       amax_in, so no second pass) with col_fmt and col_margin;
+ *     row_scale_inv_in and col_scale_inv_in: the two given dequant scales
+ *       (delayed scaling, one history per direction).
+ *   Each direction casts with fl32(1/s) like fp8_quantize_tensor.
+ *   row_scale_inv_out, col_scale_inv_out, amax_out (nullable): the scales
+ *   used and max |x| (fused).
+ * rows, cols: multiples of 16 (FP8Q_EUNSUPPORTED otherwise).
+ * Errors: FP8Q_EINVAL for unknown enums, a wrong combination of scale
+ * inputs, misalignment, or overlapping buffers (scalar outputs may not alias
+ * inputs or each other).
+ */
+int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t row_fmt, int32_t col_fmt,
+                        int32_t col_source, const float *amax_in, int32_t row_margin, int32_t col_margin,
+                        const float *row_scale_inv_in, const float *col_scale_inv_in, uint8_t *q_row, uint8_t *q_col,
+                        float *row_scale_inv_out, float *col_scale_inv_out, float *amax_out, void *stream);
+
+/*
+ * fp8_cast_stats -- diagnostics of the per-tensor cast of x with dequant
+ * scale *scale_inv ([MFP8] section 24: per-tensor overflow and underflow
+ * counts reported next to amax and scale).  With y = fl32(x * fl32(1/s)):
+ *   stats[0] overflows:  x not NaN and |y| > FP8_MAX (saturated by the cast);
+ *   stats[1] underflows: x finite and nonzero whose code is a zero code;
+ *   stats[2] NaNs;  stats[3] nonzeros (x not NaN and x != 0).
+ * stats: device uint64_t[4], 8-byte aligned.  x is read once (no codes are
+ * written).
+ */
+int fp8_cast_stats(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *scale_inv, uint64_t *stats,
+                   void *stream);
+
+/*
+ * fp8_quantize_error_feedback -- one step of FP8 quantization with error
+ * feedback ([MFP8] section 25: quantize g plus the carried residual, keep what
+ * the cast lost for the next step, so the sum of what is sent tracks the sum
+ * of the inputs):
+ *   v = fl32(g + residual);  q = codes of fl32(v * fl32(1/s)), s = *scale_inv;
+ *   residual <- fl32(v - fl32(value(q) * s))   (in place);
+ *   amax_out (nullable) <- max |v| (for the next delayed-scaling update).
+ * g: n elements of dtype; residual: fp32 [n], 16-byte aligned, read and
+ * written; q: n codes of fmt.
+ */
+int fp8_quantize_error_feedback(const void *g, int32_t dtype, float *residual, int64_t n, int32_t fmt,
+                                const float *scale_inv, uint8_t *q, float *amax_out, void *stream);
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char *fp8q_last_error(void);

@@ -50,6 +50,9 @@ def test_enum_values_match_header():
     assert int(defs["FP8Q_ACT_NONE"]) == fq.ACT_NONE == oracle.ACT_NONE
     assert int(defs["FP8Q_ACT_RELU"]) == fq.ACT_RELU == oracle.ACT_RELU
     assert int(defs["FP8Q_ACT_GELU"]) == fq.ACT_GELU == oracle.ACT_GELU
+    assert int(defs["FP8Q_COLSRC_ORIGINAL"]) == fq.COLSRC_ORIGINAL == oracle.COLSRC_ORIGINAL
+    assert int(defs["FP8Q_COLSRC_ROWWISE_DEQUANTIZED"]) == fq.COLSRC_ROWWISE_DEQUANTIZED \
+        == oracle.COLSRC_ROWWISE_DEQUANTIZED
 
 
 def _expect(status, code, fragment):
@@ -174,6 +177,55 @@ def test_gemm_fused_validation():
     _expect(call(c_type=E4OUT, si=SI, amax=SI), fq.EINVAL, "amax_out overlaps")
     # the plain entry point does not take the fused output types
     _expect(L.fp8_scaled_gemm(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 0, C, E4OUT, None, S), fq.EINVAL, "dtype")
+
+
+def test_hybrid_validation():
+    h = L.fp8_quantize_hybrid
+    X, QR, QC, A, SR, SC = BAD, BAD + 0x100000, BAD + 0x200000, BAD + 0x300000, BAD + 0x300010, BAD + 0x300020
+
+    def call(dtype=fq.BF16, rows=128, cols=128, rf=0, cf=1, src=0, amax=A, rsi=None, csi=None, qr=QR, qc=QC,
+             rso=None, cso=None, ao=None):
+        return h(X, dtype, rows, cols, rf, cf, src, amax, 0, 0, rsi, csi, qr, qc, rso, cso, ao, S)
+
+    _expect(call(dtype=5), fq.EINVAL, "dtype")
+    _expect(call(rf=2), fq.EINVAL, "format")
+    _expect(call(cf=7), fq.EINVAL, "format")
+    _expect(call(src=2), fq.EINVAL, "columnwise source")
+    _expect(call(rows=24), fq.EUNSUPPORTED, "multiples of 16")
+    _expect(call(qr=None, qc=None), fq.EINVAL, "at least one")
+    _expect(call(amax=None), fq.EINVAL, "either amax_in")
+    _expect(call(rsi=SR), fq.EINVAL, "either amax_in")
+    _expect(call(amax=None, rsi=SR), fq.EINVAL, "either amax_in")
+    _expect(call(amax=A + 2), fq.EINVAL, "aligned")
+    _expect(call(rso=A), fq.EINVAL, "aliases")
+    _expect(call(amax=None, rsi=SR, csi=SC, cso=SC), fq.EINVAL, "aliases")
+    _expect(call(rso=SR + 0x100, cso=SR + 0x100), fq.EINVAL, "alias each other")
+    _expect(call(qc=QR + 0x10), fq.EINVAL, "overlap")
+    _expect(call(qr=X + 0x40), fq.EINVAL, "overlap")
+    _expect(call(amax=QR + 0x40), fq.EINVAL, "overlaps a scale input")
+    _expect(call(ao=QC + 0x40), fq.EINVAL, "overlaps x or the codes")
+
+
+def test_stats_and_error_feedback_validation():
+    st = L.fp8_cast_stats
+    _expect(st(BAD, 3, 64, 0, BAD + 0x1000, BAD + 0x2000, S), fq.EINVAL, "dtype")
+    _expect(st(BAD, 0, 64, 2, BAD + 0x1000, BAD + 0x2000, S), fq.EINVAL, "format")
+    _expect(st(BAD, 0, -1, 0, BAD + 0x1000, BAD + 0x2000, S), fq.EINVAL, "negative")
+    _expect(st(BAD, 0, 64, 0, None, BAD + 0x2000, S), fq.EINVAL, "scale_inv")
+    _expect(st(BAD, 0, 64, 0, BAD + 0x1000, BAD + 0x2004, S), fq.EINVAL, "8-byte")
+    _expect(st(BAD, 0, 64, 0, BAD + 0x1000, BAD + 0xFF8, S), fq.EINVAL, "overlaps scale_inv")
+    _expect(st(BAD, 0, 64, 0, BAD + 0x1000, BAD + 0x80, S), fq.EINVAL, "overlaps x")
+    _expect(st(BAD + 4, 0, 64, 0, BAD + 0x1000, BAD + 0x2000, S), fq.EINVAL, "16-byte")
+    ef = L.fp8_quantize_error_feedback
+    G, R, Q, SI, AM = BAD, BAD + 0x10000, BAD + 0x20000, BAD + 0x30000, BAD + 0x30010
+    _expect(ef(G, 0, R, 64, 2, SI, Q, None, S), fq.EINVAL, "format")
+    _expect(ef(G, 0, R, 64, 0, None, Q, None, S), fq.EINVAL, "scale_inv")
+    _expect(ef(G, 0, R, 64, 0, SI, Q, SI, S), fq.EINVAL, "aliasing")
+    _expect(ef(G, 0, R + 8, 64, 0, SI, Q, None, S), fq.EINVAL, "residual")
+    _expect(ef(G, 0, G + 0x80, 64, 0, SI, Q, None, S), fq.EINVAL, "overlap")
+    _expect(ef(G, 0, R, 64, 0, SI, R + 0x40, None, S), fq.EINVAL, "overlap")
+    _expect(ef(G, 0, R, 64, 0, R + 0x20, Q, None, S), fq.EINVAL, "overlaps scale_inv")
+    _expect(ef(G, 0, R, 64, 0, SI, Q, Q + 0x8, S), fq.EINVAL, "overlaps scale_inv or amax_out")
 
 
 def test_last_error_is_thread_local_string():
