@@ -270,7 +270,32 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream):
     ms = _time(torch, stream, lambda i: fq.fp8_quantize_mx(x2[i], E4, qr[i % 4], sm[i % 4], qc[i % 4], smt[i % 4],
                                                            stream=stream), 20, rotate=len(xs))
     out["mxfp8_bf16_8192x8192_with_colwise"] = gbs(4 * n + 2 * n // 32, ms)
-    del Ws, Xs, W, X, qw, qwt, qx, qxt, qs8, qr, qc, ys, sm, smt
+
+    # next: per-direction quantization of 8192^2 bf16, E4M3 rows and E5M2
+    # columns from the dequantized rows, current scaling per direction
+    # (2 + 1 + 1 B/elem)
+    fq.fp8_amax(x2[0], am, stream=stream)
+    rsi, csi = torch.empty(1, device=dev), torch.empty(1, device=dev)
+    ms = _time(torch, stream, lambda i: fq.fp8_quantize_hybrid(
+        x2[i], E4, E5, fq.COLSRC_ROWWISE_DEQUANTIZED, q_row=qr[i % 4], q_col=qc[i % 4], amax_in=am,
+        row_scale_inv_out=rsi, col_scale_inv_out=csi, stream=stream), 20, rotate=len(xs))
+    out["hybrid_e4m3_rows_e5m2_cols_dequantized_bf16_8192x8192"] = gbs(4 * n, ms)
+
+    # next: cast statistics (overflow / underflow counts) of 8192^2 bf16
+    # under a given scale (2 B/elem read)
+    st = torch.empty(4, dtype=torch.int64, device=dev)
+    ms = _time(torch, stream, lambda i: fq.fp8_cast_stats(xs[i], E4, sc1, st, stream=stream), 20, rotate=len(xs))
+    out["cast_stats_bf16_8192x8192"] = gbs(2 * n, ms)
+
+    # next: error-feedback quantization of a 64 Mi-element bf16 gradient to
+    # E5M2 with its fp32 residual updated in place (2 + 4 + 1 + 4 B/elem)
+    del ys
+    res = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(2)]
+    s_ef = torch.full((1,), 2.0 ** -16, device=dev)
+    ms = _time(torch, stream, lambda i: fq.fp8_quantize_error_feedback(xs[i], res[i % 2], E5, s_ef, qs8[i % 8], am,
+                                                                       stream=stream), 20, rotate=len(xs))
+    out["error_feedback_bf16_to_e5m2_64Mi"] = gbs(11 * n, ms)
+    del Ws, Xs, W, X, qw, qwt, qx, qxt, qs8, qr, qc, sm, smt, res
 
     def tflops(flop, ms):
         tf = flop / (ms * 1e-3) / 1e12
