@@ -451,8 +451,13 @@ static int scaled_gemm(const char *fn, const uint8_t *A, int32_t fa, const float
     const bool fp8_out = c_type == FP8Q_OUT_E4M3FN || c_type == FP8Q_OUT_E5M2;
     if (M < 0 || N < 0 || K < 0) return fail(FP8Q_EINVAL, "%s: negative shape", fn);
     if (M % 128 || N % 128 || K % 128) return fail(FP8Q_EUNSUPPORTED, "%s: M, N, K must be multiples of 128", fn);
-    if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31)
+    if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31)
         return fail(FP8Q_EUNSUPPORTED, "%s: a dimension exceeds 2^31", fn);
+    // a block's operand panel (256 rows of K bytes) is addressed with 32-bit
+    // buffer offsets, and the grid is one block per 256x256 output tile
+    if (K > (int64_t)1 << 22) return fail(FP8Q_EUNSUPPORTED, "%s: K exceeds 2^22", fn);
+    if ((M / 256 + 1) * (N / 256 + 1) > (int64_t)INT32_MAX)
+        return fail(FP8Q_EUNSUPPORTED, "%s: more than 2^31 output tiles", fn);
     if (!sA || !sB || !aligned(sA, 4) || !aligned(sB, 4))
         return fail(FP8Q_EINVAL, "%s: sA and sB must be 4-byte aligned pointers", fn);
     if (amax_out && !aligned(amax_out, 4)) return fail(FP8Q_EINVAL, "%s: amax_out misaligned", fn);

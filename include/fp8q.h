@@ -243,7 +243,8 @@ int fp8_quantize_delayed(const void *x, int32_t dtype, int64_t n, int32_t fmt, f
  *        itself) and C = out(acc).
  *   out() is bf16 round-to-nearest-even or the fp32 value itself.
  *   amax_out (nullable) receives max |C| over the emitted values.
- * M, N, K must be multiples of 128 (FP8Q_EUNSUPPORTED otherwise).
+ * M, N, K must be multiples of 128, K at most 2^22 and M, N at most 2^31
+ * (FP8Q_EUNSUPPORTED otherwise).
  */
 int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb, const float *sB,
                     int64_t M, int64_t N, int64_t K, int32_t mode, void *C, int32_t c_dtype, float *amax_out,

@@ -153,6 +153,8 @@ def test_gemm_validation():
     _expect(g(A, 0, None, B, 0, BAD + 4, 128, 128, 128, 0, C, fq.BF16, None, S), fq.EINVAL, "sA")
     _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 0, A + 64, fq.BF16, None, S), fq.EINVAL, "overlaps")
     _expect(g(A + 8, 0, BAD, B, 0, BAD + 4, 128, 128, 128, 0, C, fq.BF16, None, S), fq.EINVAL, "16-byte")
+    _expect(g(A, 0, BAD, B, 0, BAD + 4, 128, 128, (1 << 22) + 128, 0, C, fq.BF16, None, S), fq.EUNSUPPORTED, "2^22")
+    _expect(g(A, 0, BAD, B, 0, BAD + 4, 1 << 31, 1 << 31, 128, 0, C, fq.BF16, None, S), fq.EUNSUPPORTED, "tiles")
 
 
 def test_gemm_fused_validation():
