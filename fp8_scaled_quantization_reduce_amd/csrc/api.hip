@@ -243,8 +243,9 @@ int fp8_quantize_mx(const void *x, int32_t dtype, int64_t rows, int64_t cols, in
     const int64_t n = rows * cols;
     if (n == 0) return ok();
     if (!x || !aligned(x, 16)) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
-    if (!q_row || !aligned(q_row, 16) || !s_row)
-        return fail(FP8Q_EINVAL, "%s: q_row must be a 16-byte aligned pointer and s_row non-null", fn);
+    if (!q_row || !aligned(q_row, 16) || !s_row || !aligned(s_row, 4))
+        return fail(FP8Q_EINVAL, "%s: q_row must be a 16-byte aligned pointer and s_row 4-byte aligned", fn);
+    if (s_col && !aligned(s_col, 4)) return fail(FP8Q_EINVAL, "%s: s_col must be 4-byte aligned", fn);
     if (q_col && !aligned(q_col, 16)) return fail(FP8Q_EINVAL, "%s: q_col misaligned", fn);
     const int64_t ns = n / 32; // scale bytes of either layout
     const int64_t nx = n * dsize(dtype);

@@ -870,6 +870,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
     __shared__ uint32_t red[kThreads / 64];
     __shared__ uint32_t colmax[kMode == kTileBlock1x128 ? 4 * kTile : 1]; // per wave, per tile column
     __shared__ float colscale[kMode == kTileBlock1x128 ? kTile : 1];
+    __shared__ uint32_t ecol[kMode == kTileMX ? kTile : 1]; // MXFP8: a tile column's 4 scale bytes
 
     const int ig = threadIdx.x >> 3, jg = threadIdx.x & 7;
     const int64_t tiles_c = ceil_div(cols, kTile), tiles = tiles_c * ceil_div(rows, kTile);
@@ -953,7 +954,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
             // 32x1 column blocks are the 8 lanes of one wave sharing jg (the
             // wave holds rows 32w .. 32w+31 of the tile), so no block scale
             // leaves its wave
-            const int64_t xrow = cols / 32, xcol = rows / 32;
+            const int64_t xrow = cols / 32;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 uint32_t m = 0;
@@ -961,7 +962,15 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(PV(r, k)));
                 m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false)); // lane ^ 1
                 const MxScale ms = mx_scale<F>(m);
-                if ((jg & 1) == 0 && valid) e_row[(r0 + r) * xrow + (c0 >> 5)] = (uint8_t)ms.byte;
+                // the row's 4 scale bytes of this tile sit in lanes jg = 0, 2, 4, 6:
+                // gather them into lane jg = 0 (row_shl:n reads lane + n) for one
+                // 4-byte store instead of four byte stores
+                const uint32_t b1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ms.byte, 0x102, 0xF, 0xF, false);
+                const uint32_t b2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ms.byte, 0x104, 0xF, 0xF, false);
+                const uint32_t b3 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ms.byte, 0x106, 0xF, 0xF, false);
+                if (jg == 0 && valid)
+                    *reinterpret_cast<uint32_t *>(e_row + (r0 + r) * xrow + (col0 >> 5)) =
+                        ms.byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
                     cw[r][q4] = encode4<F>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
@@ -986,9 +995,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     cm[k] = ms.mult;
                     cb[k] = ms.byte;
                 }
-                if ((threadIdx.x & 63) < 8 && valid) {
+                // a tile column's 4 scale bytes (one per wave) meet in LDS and
+                // leave as one 4-byte store after the barrier below
+                if ((threadIdx.x & 63) < 8) {
+                    uint8_t *eb = reinterpret_cast<uint8_t *>(ecol);
 #pragma unroll
-                    for (int k = 0; k < 16; ++k) e_col[(c0 + k) * xcol + (r0 >> 5)] = (uint8_t)cb[k];
+                    for (int k = 0; k < 16; ++k) eb[(16 * jg + k) * 4 + (threadIdx.x >> 6)] = (uint8_t)cb[k];
                 }
                 uint32_t cc[4][4];
 #pragma unroll
@@ -1116,6 +1128,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
             }
             __syncthreads();
             store_transposed(tl, q_col, rows, cols, row0, col0);
+            if constexpr (kMode == kTileMX) {
+                const int64_t xcol = rows / 32;
+                if (threadIdx.x < kTile && col0 + threadIdx.x < cols)
+                    *reinterpret_cast<uint32_t *>(e_col + (col0 + threadIdx.x) * xcol + (row0 >> 5)) =
+                        ecol[threadIdx.x];
+            }
         }
         __syncthreads(); // the next tile reuses the LDS buffers
 #undef PV

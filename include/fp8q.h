@@ -170,6 +170,7 @@ int fp8_quantize_block(const void *x, int32_t dtype, int64_t rows, int64_t cols,
  *          FP8Q_MXFP8 GEMM)
  *   q_col, s_col (nullable, both or neither): the columnwise copy, the same
  *          rule applied to x^T: q_col [cols][rows], s_col [cols][rows/32].
+ *   Code buffers 16-byte aligned, scale buffers 4-byte aligned.
  */
 int fp8_quantize_mx(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt, uint8_t *q_row,
                     uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, void *stream);
