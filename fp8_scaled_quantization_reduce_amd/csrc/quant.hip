@@ -353,31 +353,73 @@ hipError_t launch_dequant(const uint8_t *q, int fmt, int64_t n, const float *sca
 //                most half the smallest subnormal (the tie rounds to the even
 //                zero): |y| <= 2^-10 (E4M3FN) or 2^-17 (E5M2);
 //   NaN, and nonzero (not NaN, x != 0).
+// |y| is monotone in |x|, so the classes are intervals of the magnitude bits
+// m of x: zero, underflow (0, U], normal, overflow (O, inf], NaN above inf,
+// with U and O found once per lane by bisection over the bit patterns (the
+// largest magnitude whose product stays at or below the limit).  A lane
+// counts m > T for T = 0, U, O, inf and the four counts follow by
+// differences.  bf16 magnitudes are 16-bit, two to a register, counted with
+// packed 16-bit saturating subtracts (min(m - T, 1)); fp32 magnitudes take
+// the sign of T - m.
 // A read-only stream like the amax; each block writes four partial counts and
 // a one-block kernel sums them into 64-bit totals.
 template <int F> struct Tiny;
 template <> struct Tiny<kE4M3> { static constexpr float kHalfMinSub = 0x1p-10f; };
 template <> struct Tiny<kE5M2> { static constexpr float kHalfMinSub = 0x1p-17f; };
 
-template <int F>
-__device__ __forceinline__ void stat1(float v, float scale, uint32_t c[kStats])
+// Largest magnitude bits m in [0, 0x7F800000] with |fl32(m * scale)| <= limit
+// (0 when even the smallest nonzero magnitude exceeds it).  The answer lies
+// within a few patterns of limit / |scale|: a short walk from there, checked
+// at both ends, and a bisection only if the walk does not settle (every
+// block runs this once, so it must cost far less than its stream).
+__device__ __forceinline__ bool within(uint32_t m, float scale, float limit)
 {
-    const float y = fabsf(v * scale);
-    const bool nan = v != v;
-    const bool nz = !nan && v != 0.0f;
-    c[0] += (!nan && y > Fmt<F>::kMax) ? 1u : 0u;
-    c[1] += (nz && fabsf(v) != __builtin_inff() && y <= Tiny<F>::kHalfMinSub) ? 1u : 0u;
-    c[2] += nan ? 1u : 0u;
-    c[3] += nz ? 1u : 0u;
+    return fabsf(__uint_as_float(m) * scale) <= limit;
 }
 
-__device__ __forceinline__ void block_counts(uint32_t c[kStats], GridScratch *gs)
+__device__ __forceinline__ uint32_t last_magnitude_within(float scale, float limit)
+{
+    uint32_t c = min(f32_absbits(limit / scale), kInfBits);
+#pragma unroll
+    for (int i = 0; i < 4 && c < kInfBits && within(c + 1, scale, limit); ++i) ++c;
+#pragma unroll
+    for (int i = 0; i < 4 && c > 0 && !within(c, scale, limit); ++i) --c;
+    if ((c == 0 || within(c, scale, limit)) && (c == kInfBits || !within(c + 1, scale, limit))) return c;
+    uint32_t lo = 0, hi = kInfBits;
+    if (within(hi, scale, limit)) return hi;
+    while (hi - lo > 1) {
+        const uint32_t mid = lo + ((hi - lo) >> 1);
+        if (within(mid, scale, limit)) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Thresholds T[0..3] = 0, U, O, inf (magnitude bits).
+template <int F> __device__ __forceinline__ void stat_thresholds(float scale, uint32_t T[kStats])
+{
+    T[0] = 0;
+    T[3] = kInfBits;
+    if (scale != scale) { // NaN products: neither overflow nor underflow
+        T[1] = 0;
+        T[2] = kInfBits;
+    } else {
+        T[1] = last_magnitude_within(scale, Tiny<F>::kHalfMinSub);
+        // with a zero scale inf * 0 is NaN: nothing overflows
+        T[2] = scale == 0.0f ? kInfBits : last_magnitude_within(scale, Fmt<F>::kMax);
+    }
+}
+
+// Per-block counts of m > T[k] -> partials of (overflows, underflows, NaNs,
+// nonzeros).
+__device__ __forceinline__ void block_counts(const uint32_t g[kStats], GridScratch *gs)
 {
     __shared__ uint32_t red[kStats][kThreads / 64];
+    const uint32_t c[kStats] = {g[2] - g[3], g[0] - g[1], g[3], g[0] - g[3]};
 #pragma unroll
     for (int k = 0; k < kStats; ++k) {
         uint32_t v = c[k];
-        // wave sum with DPP row shifts and broadcasts, like wave_max_u32
+        // wave sum with DPP row shifts and broadcasts (total in lane 63)
         v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);
         v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);
         v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);
@@ -395,16 +437,42 @@ __device__ __forceinline__ void block_counts(uint32_t c[kStats], GridScratch *gs
     }
 }
 
+// Add the counts m > T[k] of one chunk to g.
+__device__ __forceinline__ void chunk_counts(const Chunk16<kBF16> &c, const uint32_t T[kStats], uint32_t g[kStats])
+{
+    // 16-bit magnitudes: m16 << 16 > T  <=>  m16 > T >> 16, and with both
+    // below 2^15 that is the sign bit of the 16-bit difference T16 - m16
+#pragma unroll
+    for (int k = 0; k < kStats; ++k) {
+        const u16x2 t = {(unsigned short)(T[k] >> 16), (unsigned short)(T[k] >> 16)};
+        u16x2 acc = {0, 0};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += (u16x2)((t - as_u16x2(c.w[j] & 0x7FFF7FFFu)) >> (unsigned short)15);
+        g[k] += (uint32_t)acc.x + (uint32_t)acc.y;
+    }
+}
+
+__device__ __forceinline__ void chunk_counts(const Chunk16<kF32> &c, const uint32_t T[kStats], uint32_t g[kStats])
+{
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t m = c.w[j] & 0x7FFFFFFFu;
+#pragma unroll
+        for (int k = 0; k < kStats; ++k) g[k] += (T[k] - m) >> 31; // m, T < 2^31
+    }
+}
+
 constexpr int kStatsU = 4;
 
 template <int F, int DT>
 __global__ __launch_bounds__(kThreads) void cast_stats_kernel(const void *__restrict__ x, int64_t n,
                                                               const float *__restrict__ scale_inv, GridScratch *gs)
 {
-    const float scale = 1.0f / *scale_inv;
+    uint32_t T[kStats];
+    stat_thresholds<F>(1.0f / *scale_inv, T);
     const int64_t nch = n >> 4;
     const int64_t units = ceil_div(nch, (int64_t)kThreads * kStatsU);
-    uint32_t c[kStats] = {0, 0, 0, 0};
+    uint32_t g[kStats] = {0, 0, 0, 0};
     for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int64_t base = unit * kThreads * kStatsU + threadIdx.x;
         Chunk16<DT> ch[kStatsU];
@@ -414,23 +482,20 @@ __global__ __launch_bounds__(kThreads) void cast_stats_kernel(const void *__rest
             ch[u].load(x, ci < nch ? ci : nch - 1);
         }
 #pragma unroll
-        for (int u = 0; u < kStatsU; ++u) {
-            if (base + u * kThreads < nch) { // (counts, unlike a max, must not see a chunk twice)
-#pragma unroll
-                for (int k = 0; k < 16; ++k) stat1<F>(ch[u].get(k), scale, c);
-            }
-        }
+        for (int u = 0; u < kStatsU; ++u) // counts, unlike a max, must not see a chunk twice
+            if (base + u * kThreads < nch) chunk_counts(ch[u], T, g);
     }
     if (blockIdx.x == 0 && threadIdx.x < n - (nch << 4)) {
         const int64_t e = (nch << 4) + threadIdx.x;
-        float v;
+        uint32_t m;
         if constexpr (DT == kBF16)
-            v = __uint_as_float(((uint32_t)reinterpret_cast<const uint16_t *>(x)[e]) << 16);
+            m = ((uint32_t)reinterpret_cast<const uint16_t *>(x)[e] & 0x7FFFu) << 16;
         else
-            v = reinterpret_cast<const float *>(x)[e];
-        stat1<F>(v, scale, c);
+            m = reinterpret_cast<const uint32_t *>(x)[e] & 0x7FFFFFFFu;
+#pragma unroll
+        for (int k = 0; k < kStats; ++k) g[k] += m > T[k] ? 1u : 0u;
     }
-    block_counts(c, gs);
+    block_counts(g, gs);
 }
 
 constexpr int kStatsFinishThreads = 1024;

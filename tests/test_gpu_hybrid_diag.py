@@ -113,7 +113,7 @@ def _stats_gpu(x, fmt, s):
 
 
 @pytest.mark.parametrize("fmt", [E4, E5])
-@pytest.mark.parametrize("s", [1.0, 1e-3, 37.5, 2.0 ** -20])
+@pytest.mark.parametrize("s", [1.0, 1e-3, 37.5, 2.0 ** -20, 3e-38, 1e38, np.inf, 0.0, np.nan, -2.5])
 def test_cast_stats_every_bf16_pattern(fmt, s):
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     assert np.array_equal(_stats_gpu(bits, fmt, s), oracle.cast_stats(bits, fmt, s))
