@@ -57,8 +57,10 @@ __device__ __forceinline__ uint32_t nan_code(float x, float scale)
 }
 
 // Four elements x[k] times their scales s[k] -> one dword of four codes
-// (byte k = code of x[k] * s[k]).
-template <int F>
+// (byte k = code of x[k] * s[k]).  kRepair = false is for callers that have
+// shown no product can be NaN (no NaN input, every scale finite and nonzero):
+// it skips the NaN test.
+template <int F, bool kRepair = true>
 __device__ __forceinline__ uint32_t encode4s(float x0, float x1, float x2, float x3, float s0, float s1, float s2,
                                              float s3)
 {
@@ -66,6 +68,7 @@ __device__ __forceinline__ uint32_t encode4s(float x0, float x1, float x2, float
     int r = cvt2<F, false>(y0, y1, 0);
     r = cvt2<F, true>(y2, y3, r);
     uint32_t c = (uint32_t)r;
+    if constexpr (!kRepair) return c;
     // NaN products are rare: one compare per element, a branch per dword.
     const bool any_nan = (y0 != y0) | (y1 != y1) | (y2 != y2) | (y3 != y3);
     if (__builtin_expect(any_nan, 0)) {
@@ -78,11 +81,14 @@ __device__ __forceinline__ uint32_t encode4s(float x0, float x1, float x2, float
 }
 
 // Four elements with one scale.
-template <int F>
+template <int F, bool kRepair = true>
 __device__ __forceinline__ uint32_t encode4(float x0, float x1, float x2, float x3, float scale)
 {
-    return encode4s<F>(x0, x1, x2, x3, scale, scale, scale, scale);
+    return encode4s<F, kRepair>(x0, x1, x2, x3, scale, scale, scale, scale);
 }
+
+// A scale with which no finite input gives a NaN product.
+__device__ __forceinline__ bool finite_nonzero(float s) { return fabsf(s) < __builtin_inff() && s != 0.0f; }
 
 // One element -> its code byte.
 template <int F>

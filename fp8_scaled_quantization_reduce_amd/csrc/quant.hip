@@ -885,6 +885,60 @@ __device__ __forceinline__ float patch_elem(const RawPatch<DT> &p, int r, int k)
     }
 }
 
+// Magnitude maxima (fp32 bit patterns, NaN above 0x7F800000) of the lane's
+// 4 x 16 patch: per row of 16 elements and per column of 4.  bf16 words hold
+// two elements, maximised together with packed 16-bit operations.
+template <int DT> __device__ __forceinline__ uint32_t patch_word(const RawPatch<DT> &p, int r, int j)
+{
+    const uint4 a = p.w[r][j >> 2];
+    const int e = j & 3;
+    return e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
+}
+
+template <int DT> __device__ __forceinline__ void patch_row_max(const RawPatch<DT> &p, uint32_t row[4])
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if constexpr (DT == kBF16) {
+            u16x2 m = as_u16x2(patch_word<DT>(p, r, 0) & 0x7FFF7FFFu);
+#pragma unroll
+            for (int j = 1; j < 8; ++j) m = __builtin_elementwise_max(m, as_u16x2(patch_word<DT>(p, r, j) & 0x7FFF7FFFu));
+            row[r] = bf16_absmax_to_f32bits(m);
+        } else {
+            uint32_t m = 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) m = max(m, patch_word<DT>(p, r, j) & 0x7FFFFFFFu);
+            row[r] = m;
+        }
+    }
+}
+
+template <int DT> __device__ __forceinline__ void patch_col_max(const RawPatch<DT> &p, uint32_t col[16])
+{
+    if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { // word j holds columns 2j (low half) and 2j + 1
+            u16x2 m = as_u16x2(patch_word<DT>(p, 0, j) & 0x7FFF7FFFu);
+#pragma unroll
+            for (int r = 1; r < 4; ++r) m = __builtin_elementwise_max(m, as_u16x2(patch_word<DT>(p, r, j) & 0x7FFF7FFFu));
+            col[2 * j] = (uint32_t)m.x << 16;
+            col[2 * j + 1] = (uint32_t)m.y << 16;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m = max(m, patch_word<DT>(p, r, k) & 0x7FFFFFFFu);
+            col[k] = m;
+        }
+    }
+}
+
+template <bool B> struct Rep {
+    static constexpr bool value = B;
+};
+
 // Store the lane's 4x16 codes (cw[r][0..3] = row r, 16 codes) transposed into LDS.
 __device__ __forceinline__ void stage_transposed(uint32_t *tl, const uint32_t cw[4][4], int ig, int jg)
 {
@@ -936,6 +990,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
     __shared__ uint32_t colmax[kMode == kTileBlock1x128 ? 4 * kTile : 1]; // per wave, per tile column
     __shared__ float colscale[kMode == kTileBlock1x128 ? kTile : 1];
     __shared__ uint32_t ecol[kMode == kTileMX ? kTile : 1]; // MXFP8: a tile column's 4 scale bytes
+    __shared__ uint32_t colbad; // 1x128: some column scale of the tile is NaN, infinite or zero
 
     const int ig = threadIdx.x >> 3, jg = threadIdx.x & 7;
     const int64_t tiles_c = ceil_div(cols, kTile), tiles = tiles_c * ceil_div(rows, kTile);
@@ -981,50 +1036,60 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
 #define PV(r, k) patch_elem<DT>(p, (r), (k))
 
         uint32_t cw[4][4]; // rowwise codes
-
-        if constexpr (kMode == kTilePerTensor || kHybrid) {
-            if constexpr (kAmax) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int k = 0; k < 16; ++k) m_all = max(m_all, f32_absbits(PV(r, k)));
-            }
+        // Encodes of the lane's 4 x 16 patch; kR selects the NaN-repairing
+        // encode, needed only when some product can be NaN (a NaN input, or a
+        // scale that is NaN, infinite or zero).  Every mode encodes with the
+        // short form and, in that rare case alone, encodes again with repair
+        // (one unconditional path keeps the two from sharing registers).
+        auto enc_rows = [&](auto rep, float scale) {
+            constexpr bool kR = decltype(rep)::value;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
-                    cw[r][q4] = encode4<F>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
-                                           PV(r, 4 * q4 + 3), sc_tensor.scale);
+                    cw[r][q4] = encode4<F, kR>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2), PV(r, 4 * q4 + 3),
+                                               scale);
+        };
+
+        if constexpr (kMode == kTilePerTensor || kHybrid) {
+            uint32_t rm[4];
+            patch_row_max<DT>(p, rm);
+            const uint32_t pmax = max(max(rm[0], rm[1]), max(rm[2], rm[3]));
+            if constexpr (kAmax) m_all = max(m_all, pmax);
+            enc_rows(Rep<false>{}, sc_tensor.scale);
+            if (!(pmax <= kInfBits && finite_nonzero(sc_tensor.scale))) {
+                opaque(p);
+                enc_rows(Rep<true>{}, sc_tensor.scale);
+            }
         } else if constexpr (kMode == kTileBlock128) {
-            uint32_t m = 0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(PV(r, k)));
+            uint32_t rm[4];
+            patch_row_max<DT>(p, rm);
+            uint32_t m = max(max(rm[0], rm[1]), max(rm[2], rm[3]));
             m = block_max_u32<kThreads>(m, red);
-            opaque(p);
             const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
             if (threadIdx.x == 0) {
                 s_row[tr * bcols + tc] = sc.s;
                 if (s_col) s_col[tc * brows + tr] = sc.s;
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    cw[r][q4] = encode4<F>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
-                                           PV(r, 4 * q4 + 3), sc.scale);
+            // the block scale is uniform: finite and nonzero exactly when the
+            // block holds no NaN or infinity
+            enc_rows(Rep<false>{}, sc.scale);
+            if (!finite_nonzero(sc.scale)) {
+                opaque(p);
+                enc_rows(Rep<true>{}, sc.scale);
+            }
         } else if constexpr (kMode == kTileMX) {
             // MXFP8: 1x32 row blocks are two lanes (jg = 2b, 2b + 1) of a row;
             // 32x1 column blocks are the 8 lanes of one wave sharing jg (the
             // wave holds rows 32w .. 32w+31 of the tile), so no block scale
-            // leaves its wave
+            // leaves its wave.  A block's multiplier is a finite, nonzero power
+            // of two unless the block holds a NaN.
             const int64_t xrow = cols / 32;
+            uint32_t rm[4];
+            patch_row_max<DT>(p, rm);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                uint32_t m = 0;
-#pragma unroll
-                for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(PV(r, k)));
+                uint32_t m = rm[r];
                 m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false)); // lane ^ 1
                 const MxScale ms = mx_scale<F>(m);
                 // the row's 4 scale bytes of this tile sit in lanes jg = 0, 2, 4, 6:
@@ -1038,24 +1103,32 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                         ms.byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
-                    cw[r][q4] = encode4<F>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
-                                           PV(r, 4 * q4 + 3), ms.mult);
+                    cw[r][q4] = encode4<F, false>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
+                                                  PV(r, 4 * q4 + 3), ms.mult);
+                if (m > kInfBits) {
+                    opaque(p);
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        cw[r][q4] = encode4<F, true>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
+                                                     PV(r, 4 * q4 + 3), ms.mult);
+                }
                 if (q_row && valid)
                     *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) =
                         make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
             }
             if (q_col) {
                 opaque(p);
+                uint32_t cmax[16];
+                patch_col_max<DT>(p, cmax);
                 float cm[16];
-                uint32_t cb[16];
+                uint32_t cb[16], worst = 0;
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
-                    uint32_t m = 0;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) m = max(m, f32_absbits(PV(r, k)));
+                    uint32_t m = cmax[k];
                     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xF, 0xF, false)); // lane ^ 8
                     m = max(m, (uint32_t)__builtin_amdgcn_ds_swizzle((int)m, 0x401F));                    // lane ^ 16
                     m = max(m, (uint32_t)__shfl_xor((int)m, 32));                                         // lane ^ 32
+                    worst = max(worst, m);
                     const MxScale ms = mx_scale<F>(m);
                     cm[k] = ms.mult;
                     cb[k] = ms.byte;
@@ -1068,32 +1141,47 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     for (int k = 0; k < 16; ++k) eb[(16 * jg + k) * 4 + (threadIdx.x >> 6)] = (uint8_t)cb[k];
                 }
                 uint32_t cc[4][4];
+                auto enc_cols = [&](auto rep) {
+                    constexpr bool kR = decltype(rep)::value;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+                    for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const int k = 4 * q4;
-                        cc[r][q4] = encode4s<F>(PV(r, k), PV(r, k + 1), PV(r, k + 2), PV(r, k + 3), cm[k],
-                                                cm[k + 1], cm[k + 2], cm[k + 3]);
-                    }
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const int k = 4 * q4;
+                            cc[r][q4] = encode4s<F, kR>(PV(r, k), PV(r, k + 1), PV(r, k + 2), PV(r, k + 3), cm[k],
+                                                        cm[k + 1], cm[k + 2], cm[k + 3]);
+                        }
+                };
+                enc_cols(Rep<false>{});
+                if (worst > kInfBits) {
+                    opaque(p);
+                    enc_cols(Rep<true>{});
+                }
                 stage_transposed(tl, cc, ig, jg);
             }
         } else { // 1x128 blocks: one scale per row segment, one per column segment
             // row segments: the 8 lanes jg = 0..7 of a row group hold the row's 128 columns
+            uint32_t rm[4];
+            patch_row_max<DT>(p, rm);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                uint32_t m = 0;
-#pragma unroll
-                for (int k = 0; k < 16; ++k) m = max(m, f32_absbits(PV(r, k)));
-                m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-                m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+                uint32_t m = rm[r];
+                m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false)); // lane ^ 1
+                m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false)); // lane ^ 2
                 m = max(m, (uint32_t)__shfl_xor((int)m, 4));
                 const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
                 if (jg == 0) s_row[(r0 + r) * bcols + tc] = sc.s;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
-                    cw[r][q4] = encode4<F>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
-                                           PV(r, 4 * q4 + 3), sc.scale);
+                    cw[r][q4] = encode4<F, false>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
+                                                  PV(r, 4 * q4 + 3), sc.scale);
+                if (!finite_nonzero(sc.scale)) {
+                    opaque(p);
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        cw[r][q4] = encode4<F, true>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
+                                                     PV(r, 4 * q4 + 3), sc.scale);
+                }
                 // stored now: the rowwise codes need not stay live through the column phase
                 if (q_row && valid)
                     *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) =
@@ -1106,11 +1194,10 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
             if (q_col) {
                 const int wv = threadIdx.x >> 6;
                 uint32_t cm[16];
+                patch_col_max<DT>(p, cm);
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
-                    uint32_t m = 0;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) m = max(m, f32_absbits(PV(r, k)));
+                    uint32_t m = cm[k];
                     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xF, 0xF, false)); // lane ^ 8
                     m = max(m, (uint32_t)__builtin_amdgcn_ds_swizzle((int)m, 0x401F));                    // lane ^ 16
                     m = max(m, (uint32_t)__shfl_xor((int)m, 32));                                         // lane ^ 32
@@ -1122,6 +1209,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     for (int q4 = 0; q4 < 4; ++q4)
                         dst[q4] = make_uint4(cm[4 * q4], cm[4 * q4 + 1], cm[4 * q4 + 2], cm[4 * q4 + 3]);
                 }
+                if (threadIdx.x == 0) colbad = 0;
                 __syncthreads();
                 if (threadIdx.x < kTile) {
                     const uint32_t m = max(max(colmax[threadIdx.x], colmax[kTile + threadIdx.x]),
@@ -1129,6 +1217,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
                     colscale[threadIdx.x] = sc.scale;
                     s_col[(col0 + threadIdx.x) * brows + tr] = sc.s;
+                    if (!finite_nonzero(sc.scale)) colbad = 1;
                 }
                 __syncthreads();
             }
@@ -1145,48 +1234,75 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 // columnwise codes use the column-segment scales
                 opaque(p);
                 uint32_t cc[4][4];
+                auto enc_cols = [&](auto rep) {
+                    constexpr bool kR = decltype(rep)::value;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+                    for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const int k = 4 * q4;
-                        const float *cs = colscale + 16 * jg + k;
-                        cc[r][q4] = encode4s<F>(PV(r, k), PV(r, k + 1), PV(r, k + 2), PV(r, k + 3), cs[0],
-                                                cs[1], cs[2], cs[3]);
-                    }
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const int k = 4 * q4;
+                            const float *cs = colscale + 16 * jg + k;
+                            cc[r][q4] = encode4s<F, kR>(PV(r, k), PV(r, k + 1), PV(r, k + 2), PV(r, k + 3), cs[0],
+                                                        cs[1], cs[2], cs[3]);
+                        }
+                };
+                enc_cols(Rep<false>{});
+                if (colbad != 0) {
+                    opaque(p);
+                    enc_cols(Rep<true>{});
+                }
                 stage_transposed(tl, cc, ig, jg);
             } else if constexpr (kHybrid) {
                 // column codes in their own format and scale, from x or from
                 // x' = fl32(value(row code) * s_row)
+                uint32_t rm[4];
+                patch_row_max<DT>(p, rm);
+                const bool clean = max(max(rm[0], rm[1]), max(rm[2], rm[3])) <= kInfBits &&
+                                   finite_nonzero(sc_tensor.scale) && finite_nonzero(sc_col.scale) &&
+                                   (!kDeq || finite_nonzero(sc_tensor.s));
                 uint32_t cc[4][4];
+                auto enc_cols = [&](auto rep) {
+                    constexpr bool kR = decltype(rep)::value;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+                    for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        if constexpr (kDeq) {
-                            const uint32_t w = cw[r][q4];
-                            const float2 lo = dec2<F, false>(w), hi = dec2<F, true>(w);
-                            const float sr = sc_tensor.s;
-                            const float d0 = lo.x * sr, d1 = lo.y * sr, d2 = hi.x * sr, d3 = hi.y * sr;
-                            uint32_t c = encode4<FC>(d0, d1, d2, d3, sc_col.scale);
-                            // a NaN row code stays NaN with the sign of its code (the
-                            // decoder's NaN carries no sign of its own); rare path
-                            if (__builtin_expect((d0 != d0) | (d1 != d1) | (d2 != d2) | (d3 != d3), 0)) {
-                                const uint32_t flip =
-                                    ((__float_as_uint(sr) ^ __float_as_uint(sc_col.scale)) >> 24) & 0x80u;
-                                const float d[4] = {d0, d1, d2, d3};
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            if constexpr (kDeq) {
+                                const uint32_t w = cw[r][q4];
+                                const float2 lo = dec2<F, false>(w), hi = dec2<F, true>(w);
+                                const float sr = sc_tensor.s;
+                                const float d0 = lo.x * sr, d1 = lo.y * sr, d2 = hi.x * sr, d3 = hi.y * sr;
+                                uint32_t c = encode4<FC, kR>(d0, d1, d2, d3, sc_col.scale);
+                                if constexpr (kR) {
+                                    // a NaN row code stays NaN with the sign of its code
+                                    // (the decoder's NaN carries no sign of its own)
+                                    if (__builtin_expect((d0 != d0) | (d1 != d1) | (d2 != d2) | (d3 != d3), 0)) {
+                                        const uint32_t flip =
+                                            ((__float_as_uint(sr) ^ __float_as_uint(sc_col.scale)) >> 24) & 0x80u;
+                                        const float d[4] = {d0, d1, d2, d3};
 #pragma unroll
-                                for (int b = 0; b < 4; ++b)
-                                    if (d[b] != d[b])
-                                        c = (c & ~(0xFFu << (8 * b))) |
-                                            ((0x7Fu | (((w >> (8 * b)) & 0x80u) ^ flip)) << (8 * b));
+                                        for (int b = 0; b < 4; ++b)
+                                            if (d[b] != d[b])
+                                                c = (c & ~(0xFFu << (8 * b))) |
+                                                    ((0x7Fu | (((w >> (8 * b)) & 0x80u) ^ flip)) << (8 * b));
+                                    }
+                                }
+                                cc[r][q4] = c;
+                            } else {
+                                cc[r][q4] = encode4<FC, kR>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
+                                                            PV(r, 4 * q4 + 3), sc_col.scale);
                             }
-                            cc[r][q4] = c;
-                        } else {
-                            cc[r][q4] = encode4<FC>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
-                                                    PV(r, 4 * q4 + 3), sc_col.scale);
                         }
-                    }
+                };
+                enc_cols(Rep<false>{});
+                if (!clean) {
+                    opaque(p);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) asm volatile("" : "+v"(cw[r][q4]));
+                    enc_cols(Rep<true>{});
+                }
                 stage_transposed(tl, cc, ig, jg);
             } else if constexpr (kMode != kTileMX) { // (MXFP8 staged its own column codes above)
                 stage_transposed(tl, cw, ig, jg);
