@@ -10,7 +10,7 @@
 #include <mutex>
 #include <utility>
 
-#include "../../include/fp8q.h"
+#include "fp8q.h"
 #include "fp8q_launch.h"
 
 namespace {
