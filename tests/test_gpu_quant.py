@@ -327,6 +327,23 @@ def test_rowwise_colwise_parity(fmt, shape, dt):
     assert same_f32(host(si)[0], s_ref) and same_f32(host(sc)[0], sc_ref) and same_f32(host(am)[0], a)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("s", [0.37, 0.0, np.inf, np.nan, -2.0])
+def test_rowwise_colwise_specials_and_edge_scales(dt, s):
+    """NaN, infinities and zeros in the input under ordinary and degenerate
+    given scales (0 and inf make inf * 0 and 0 * inf products NaN): every
+    code, including NaN codes and their signs, equals the oracle's."""
+    rows, cols = 144, 272
+    v = np.random.default_rng(4).standard_normal((rows, cols)) * 50
+    v[3, 5], v[77, 200], v[143, 271], v[10, 10], v[11, 11] = np.nan, np.inf, -np.inf, 0.0, -0.0
+    x = v.astype(np.float32) if dt == "f32" else workloads.to_bf16_bits(v)
+    qr, qc = empty_codes((rows, cols)), empty_codes((cols, rows))
+    fq.fp8_quantize_rowwise_colwise(to_dev(x), E4, q_row=qr, q_col=qc, scale_inv_in=scalar(s))
+    qr_ref, qc_ref = oracle.quantize_rowwise_colwise(x, E4, oracle.reciprocal(np.float32(s)))
+    assert np.array_equal(host(qr), qr_ref), first_mismatches(host(qr), qr_ref)
+    assert np.array_equal(host(qc), qc_ref), first_mismatches(host(qc), qc_ref)
+
+
 def test_rowwise_colwise_full_size_given_scale():
     x = workloads.delayed_step(9)
     rows, cols = x.shape
@@ -380,9 +397,8 @@ def test_block_small(block_rows, fmt, dt):
     v[:128, :128] = 0.0  # an all-zero block
     v[200, 3] = np.inf
     v[300, 130] = -np.inf
+    v[140, 140] = np.nan
     x = v.astype(np.float32) if dt == "f32" else workloads.to_bf16_bits(v)
-    if dt == "f32":
-        x[140, 140] = np.nan
     _check_block(x, fmt, block_rows)
 
 
