@@ -39,7 +39,7 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0
 # FETCH_SIZE and WRITE_SIZE counters of the current kernels scaled by the
 # factors a plain copy gives (profiles/delayed_step_8192x8192_bf16_hbm_traffic.md);
 # set back to None whenever either kernel changes, until the counters are taken again.
-TRAFFIC_BYTES_PER_STEP = 201713706
+TRAFFIC_BYTES_PER_STEP = 201712694
 
 
 def parse():
@@ -82,7 +82,7 @@ def main():
         copy_calibration(args.copy_mib)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 

@@ -43,7 +43,7 @@ extern "C" {
 /* status codes */
 #define FP8Q_OK 0
 #define FP8Q_EINVAL 1      /* bad pointer, size, alignment or enum value */
-#define FP8Q_EUNSUPPORTED 2 /* valid request this build does not implement */
+#define FP8Q_EUNSUPPORTED 2 /* valid request the library does not implement */
 #define FP8Q_EHIP 3        /* the HIP runtime reported an error */
 
 /* FP8 formats, [MFP8] section 2.  E4M3FN: bias 7, max 448, no Inf, NaN only
