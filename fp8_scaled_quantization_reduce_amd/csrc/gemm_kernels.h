@@ -74,11 +74,10 @@ __device__ __forceinline__ v4f mfma16x16x128(const v8i &x, const v8i &y, const v
 // fragment 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int r, int c) { return r * kBK + ((c ^ ((r >> 1) & 7)) << 4); }
 
-__device__ __forceinline__ void tile_of_block(int bid, int tilesM, int tilesN, int &tm, int &tn)
+// Tile t of the grouped order: groups of kGroupM tile rows, walked column by
+// column inside a group.
+__device__ __forceinline__ void group_tile(int t, int tilesM, int tilesN, int &tm, int &tn)
 {
-    const int ntiles = tilesM * tilesN;
-    int t = bid;
-    if (ntiles % kXcds == 0) t = (bid % kXcds) * (ntiles / kXcds) + bid / kXcds;
     const int per_group = kGroupM * tilesN;
     const int group = t / per_group;
     const int first_m = group * kGroupM;
@@ -86,6 +85,15 @@ __device__ __forceinline__ void tile_of_block(int bid, int tilesM, int tilesN, i
     const int in_group = t - group * per_group;
     tm = first_m + in_group % gsize;
     tn = in_group / gsize;
+}
+
+// Block bid of a grid of n blocks -> its index in the grouped order, dealt so
+// that each XCD gets a contiguous run (blocks go to XCD bid mod 8).
+__device__ __forceinline__ int xcd_order(int bid, int n) { return n % kXcds ? bid : (bid % kXcds) * (n / kXcds) + bid / kXcds; }
+
+__device__ __forceinline__ void tile_of_block(int bid, int tilesM, int tilesN, int &tm, int &tn)
+{
+    group_tile(xcd_order(bid, tilesM * tilesN), tilesM, tilesN, tm, tn);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -462,13 +470,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
 constexpr int kBSThreads = 512;
 constexpr int kBSStageBytes = 2 * kBM * kBK;
 
-template <int FA, int FB, bool kAmax, int kOut, bool kFuse, bool kRowB>
+// kBN = 256: the block computes a 256x256 tile, grid block b -> grouped tile
+// xcd_order(b, n_main).  kBN = 128: half a tile (the wave tiles are 64x64),
+// grid block b -> the half b & 1 of grouped tile tile_base + b / 2; the
+// launcher uses it for a last, partly empty wave of tiles, which then runs as
+// a full wave of half tiles.  Each block's amax partial goes to part[b].
+template <int FA, int FB, bool kAmax, int kOut, bool kFuse, bool kRowB, int kBN>
 __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *__restrict__ A,
                                                                 const uint8_t *__restrict__ B,
                                                                 const float *__restrict__ sA,
                                                                 const float *__restrict__ sB, int M, int N, int K,
-                                                                void *__restrict__ C, Epi epi, GridScratch *gs)
+                                                                void *__restrict__ C, Epi epi, uint32_t *part,
+                                                                int tile_base, int n_main)
 {
+    constexpr int kWN = kBN / 2; // a wave's columns
+    constexpr int kTJ = kWN / 16; // its 16-wide column tiles
     __shared__ __attribute__((aligned(1024))) uint8_t st0[kBSStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[kBSStageBytes];
     __shared__ __attribute__((aligned(16))) float sa0[kBM];
@@ -478,15 +494,17 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
     __shared__ uint32_t red[kBSThreads / 64];
 
     int tm, tn;
-    tile_of_block(blockIdx.x, (M + kBM - 1) / kBM, (N + kBM - 1) / kBM, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBM;
+    const int tilesM = (M + kBM - 1) / kBM, tilesN = (N + kBM - 1) / kBM;
+    if constexpr (kBN == kBM) group_tile(xcd_order(blockIdx.x, n_main), tilesM, tilesN, tm, tn);
+    else group_tile(tile_base + (int)(blockIdx.x >> 1), tilesM, tilesN, tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBM + (kBN == kBM ? 0 : (blockIdx.x & 1) * kBN);
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w >> 1, wn = w & 1;
     const int fr = lane & 15, fg = lane >> 4;
     const int kblocks = K / kBK;
 
-    const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBM, (int64_t)N - n0);
+    const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBN, (int64_t)N - n0);
     const __amdgpu_buffer_rsrc_t ra =
         __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * K), 0, (int)(a_rows * K), kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rb =
@@ -499,7 +517,7 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
     // 128x128 B: the wave's 128 columns lie in one 128-column scale block
     // (clamped for the half tile past N, whose results are never stored).
     // 1x128 B: one scale per row of B (column of C), staged like A's.
-    const int nb = min((int)((n0 + wn * 128) / 128), N / 128 - 1);
+    const int nb = min((int)((n0 + wn * kWN) / 128), N / 128 - 1);
     const float *__restrict__ sbp = sB + (int64_t)nb * kblocks;
     const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(sB + (kRowB ? n0 * kblocks : 0)), 0, kRowB ? (int)(b_rows * kblocks * 4) : 4, kRawBufferWord3);
@@ -512,7 +530,7 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
                                                      0, 0);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kBN / 64; ++u) {
             const int row = 8 * (w + 8 * u);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + kBM * kBK + row * kBK), 16, voff,
                                                      kb * kBK + row * K, 0, 0);
@@ -520,16 +538,16 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
         if (w < 4)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(sa + 64 * w), 4, lane * kblocks * 4,
                                                      (64 * w * kblocks + kb) * 4, 0, 0);
-        else if (kRowB)
+        else if (kRowB && (w - 4) * 64 < kBN)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(sbr + 64 * (w - 4)), 4, lane * kblocks * 4,
                                                      (64 * (w - 4) * kblocks + kb) * 4, 0, 0);
     };
 
-    v4f acc[4][8];
+    v4f acc[4][kTJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < kTJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     // One slice (stage `cur`, its row scales in `sac`; the next slice already
     // in flight to `nxt` / `san`).  Column tile j's MFMAs run while tile
@@ -563,20 +581,20 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
     auto slice = [&](int kb, uint8_t *cur, float *sac, float *sbc, const uint8_t *nxt, const float *san,
                      bool full) {
         const uint8_t *lb = cur + kBM * kBK;
-        const float *sbw = sbc + wn * 128 + 4 * fg; // this lane's column scales, tile 0
+        const float *sbw = sbc + wn * kWN + 4 * fg; // this lane's column scales, tile 0
         v4f prev[4];
         v4f sb7 = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kTJ; ++j) {
             asm volatile("" : "+v"(b));
             v8i bn;
-            if (j + 1 < 8) bn = read_frag(lb, wn * 128 + 16 * (j + 1) + fr, fg);
+            if (j + 1 < kTJ) bn = read_frag(lb, wn * kWN + 16 * (j + 1) + fr, fg);
             v4f sbj = v4f{0.f, 0.f, 0.f, 0.f}; // tile j-1's column scales
             if constexpr (kRowB) {
                 if (j > 0) sbj = *reinterpret_cast<const v4f *>(sbw + 16 * (j - 1));
-                if (j == 7) sb7 = *reinterpret_cast<const v4f *>(sbw + 16 * 7);
+                if (j == kTJ - 1) sb7 = *reinterpret_cast<const v4f *>(sbw + 16 * (kTJ - 1));
             }
-            if (j == 7) {
+            if (j == kTJ - 1) {
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
@@ -588,15 +606,15 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
             if (j > 0) promote(j - 1, prev, sbj);
 #pragma unroll
             for (int i = 0; i < 4; ++i) prev[i] = cur_p[i];
-            if (j + 1 < 8) b = bn;
+            if (j + 1 < kTJ) b = bn;
         }
-        // tile 7's promotion with this slice's weights, then the next slice's
-        // fragments and weights
-        promote(7, prev, sb7);
+        // the last tile's promotion with this slice's weights, then the next
+        // slice's fragments and weights
+        promote(kTJ - 1, prev, sb7);
         if (full || kb + 1 < kblocks) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i] = read_frag(nxt, wm * 64 + 16 * i + fr, fg);
-            b = read_frag(nxt + kBM * kBK, wn * 128 + fr, fg);
+            b = read_frag(nxt + kBM * kBK, wn * kWN + fr, fg);
             if constexpr (kRowB) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sai[i] = san[wm * 64 + 16 * i + fr];
@@ -619,7 +637,7 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[i] = read_frag(st0, wm * 64 + 16 * i + fr, fg);
-        b = read_frag(st0 + kBM * kBK, wn * 128 + fr, fg);
+        b = read_frag(st0 + kBM * kBK, wn * kWN + fr, fg);
         if constexpr (kRowB) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) sai[i] = sa0[wm * 64 + 16 * i + fr];
@@ -648,14 +666,14 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
     for (int i = 0; i < 4; ++i) {
         const int64_t row = m0 + wm * 64 + 16 * i + fr;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t col = n0 + wn * 128 + 16 * j + 4 * fg;
+        for (int j = 0; j < kTJ; ++j) {
+            const int64_t col = n0 + wn * kWN + 16 * j + 4 * fg;
             if (row < M && col < N) store_out4<kOut, kAmax, kFuse>(C, row * N + col, col, acc[i][j], m, epi, out_scale);
         }
     }
     if constexpr (kAmax) {
         m = block_max_u32<kBSThreads>(m, red);
-        if (tid == 0) gs->part[blockIdx.x] = canonical_amax_bits(m);
+        if (tid == 0) part[blockIdx.x] = canonical_amax_bits(m);
     }
 }
 
@@ -664,26 +682,52 @@ inline int gemm_grid(int64_t M, int64_t N) { return (int)(((M + kBM - 1) / kBM) 
 template <int FA, int FB, int kOut, bool kFuse>
 hipError_t launch_gemm_epi(const GemmArgs &a)
 {
-    const int grid = gemm_grid(a.M, a.N);
     const int m = (int)a.M, n = (int)a.N, k = (int)a.K;
     const Epi epi{a.bias, a.act, a.out_scale_inv};
-#define FP8Q_GEMM_LAUNCH(KERNEL, THREADS, FLAG)                                                                     \
-    do {                                                                                                            \
-        if (a.amax_out)                                                                                             \
-            KERNEL<FA, FB, true, kOut, kFuse, FLAG>                                                                 \
-                <<<grid, THREADS, 0, a.stream>>>(a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, a.gs);                    \
-        else                                                                                                        \
-            KERNEL<FA, FB, false, kOut, kFuse, FLAG>                                                                \
-                <<<grid, THREADS, 0, a.stream>>>(a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, a.gs);                    \
-    } while (0)
-    if (a.mode == 0) FP8Q_GEMM_LAUNCH(gemm_pt_kernel, kGemmThreads, false);
-    else if (a.mode == 3) FP8Q_GEMM_LAUNCH(gemm_pt_kernel, kGemmThreads, true);
-    else if (a.mode == 1) FP8Q_GEMM_LAUNCH(gemm_bs_kernel, kBSThreads, false);
-    else FP8Q_GEMM_LAUNCH(gemm_bs_kernel, kBSThreads, true);
-#undef FP8Q_GEMM_LAUNCH
+    int parts = gemm_grid(a.M, a.N);
+    if (a.mode == 0 || a.mode == 3) {
+        const int grid = parts;
+#define FP8Q_PT_LAUNCH(FLAG)                                                                                        \
+        do {                                                                                                        \
+            if (a.amax_out)                                                                                         \
+                gemm_pt_kernel<FA, FB, true, kOut, kFuse, FLAG>                                                     \
+                    <<<grid, kGemmThreads, 0, a.stream>>>(a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, a.gs);           \
+            else                                                                                                    \
+                gemm_pt_kernel<FA, FB, false, kOut, kFuse, FLAG>                                                    \
+                    <<<grid, kGemmThreads, 0, a.stream>>>(a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, a.gs);           \
+        } while (0)
+        if (a.mode == 0) FP8Q_PT_LAUNCH(false);
+        else FP8Q_PT_LAUNCH(true);
+#undef FP8Q_PT_LAUNCH
+    } else {
+        // A last wave of tiles at most half full runs as a full wave of half
+        // tiles (256x128), launched after the full tiles.
+        const int tiles = parts, r = a.cus > 0 ? tiles % a.cus : 0;
+        const int n_main = (r > 0 && 2 * r <= a.cus) ? tiles - r : tiles;
+        const int n_half = 2 * (tiles - n_main);
+        uint32_t *part = a.gs ? a.gs->part : nullptr;
+#define FP8Q_BS_LAUNCH(ROWB, BN, GRID, PART, BASE)                                                                  \
+        do {                                                                                                        \
+            if (a.amax_out)                                                                                         \
+                gemm_bs_kernel<FA, FB, true, kOut, kFuse, ROWB, BN><<<GRID, kBSThreads, 0, a.stream>>>(             \
+                    a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, PART, BASE, n_main);                                   \
+            else                                                                                                    \
+                gemm_bs_kernel<FA, FB, false, kOut, kFuse, ROWB, BN><<<GRID, kBSThreads, 0, a.stream>>>(            \
+                    a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, PART, BASE, n_main);                                   \
+        } while (0)
+        if (a.mode == 1) {
+            if (n_main > 0) FP8Q_BS_LAUNCH(false, kBM, n_main, part, 0);
+            if (n_half > 0) FP8Q_BS_LAUNCH(false, kBM / 2, n_half, part ? part + n_main : nullptr, n_main);
+        } else {
+            if (n_main > 0) FP8Q_BS_LAUNCH(true, kBM, n_main, part, 0);
+            if (n_half > 0) FP8Q_BS_LAUNCH(true, kBM / 2, n_half, part ? part + n_main : nullptr, n_main);
+        }
+#undef FP8Q_BS_LAUNCH
+        parts = n_main + n_half;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.amax_out) return e;
-    return launch_finish_amax(a.gs, grid, a.amax_out, a.stream);
+    return launch_finish_amax(a.gs, parts, a.amax_out, a.stream);
 }
 
 // Every output kind and epilogue of one operand-format pair.  The plain

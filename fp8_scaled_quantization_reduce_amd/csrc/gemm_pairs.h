@@ -23,6 +23,7 @@ struct GemmArgs {
     float *amax_out;            // or null
     GridScratch *gs;
     hipStream_t stream;
+    int cus; // compute units of the device (tile-wave accounting)
 };
 
 hipError_t launch_gemm_e4m3_e4m3(const GemmArgs &a);

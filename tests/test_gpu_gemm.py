@@ -186,3 +186,21 @@ def test_gemm_block_full_size_mlp():
     _sampled_check(C, am, qx, E4, sx, qw, E4, sw, mode, n=1024, seed=1)
     C, am = _gpu_gemm(qdy, E5, sdy, qwt, E4, swt, mode)
     _sampled_check(C, am, qdy, E5, sdy, qwt, E4, swt, mode, n=1024, seed=2)
+
+
+@pytest.mark.parametrize("mode", [fq.BLOCK_1x128_128x128, fq.BLOCK_1x128_1x128])
+@pytest.mark.parametrize("M,N,K", [(4352, 4096, 256), (3072, 3072, 256), (256, 384, 256), (4352, 3968, 384)])
+def test_gemm_block_last_wave_of_half_tiles(mode, M, N, K):
+    """The block-scaled GEMM runs a last wave of tiles that is at most half
+    full as a wave of 256x128 half tiles (a second launch): 17x16 tiles leave
+    16 (both launches), 12x12 leave 144 (no split), 1x2 are all half tiles (the
+    second half of the last tile lies past N), 17x16 with N = 3968 ends in a
+    half-empty tile column.  Every case is checked in full against the
+    oracle, with the output amax over all of C."""
+    rng = np.random.default_rng(M + N + K + mode)
+    xa = workloads.to_bf16_bits(rng.standard_normal((M, K)) * np.exp(rng.uniform(-2, 2, (M, 1))))
+    xb = workloads.to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
+    qa, sa, _, _ = oracle.quantize_block(xa, E4, 1)
+    qb, sb, _, _ = oracle.quantize_block(xb, E4, 128 if mode == fq.BLOCK_1x128_128x128 else 1)
+    C, am = _gpu_gemm(qa, E4, sa, qb, E4, sb, mode)
+    _check_tol_and_amax(C, am, oracle.gemm_reference(qa, E4, sa, qb, E4, sb, mode))
