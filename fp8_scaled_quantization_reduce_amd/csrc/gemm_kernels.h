@@ -263,30 +263,39 @@ __device__ __forceinline__ v8i read_frag32_mx(const uint8_t *lds, int r, int g, 
 // scale byte per lane, for the 32 K bytes that lane holds).  Each stage also
 // carries the slice's four scale bytes of every A and B row (one dword per row,
 // loaded straight into LDS with the codes).
-template <int FA, int FB, bool kAmax, int kOut, bool kFuse, bool kMX>
+// kBN = 256: a 256x256 tile per block (grid block b -> grouped tile
+// xcd_order(b, n_main)); kBN = 128: half a tile, wave tiles 128x64 (grid
+// block b -> half b & 1 of grouped tile tile_base + b / 2), for a last wave of
+// tiles that is at most half full.  Each block's amax partial goes to part[b].
+template <int FA, int FB, bool kAmax, int kOut, bool kFuse, bool kMX, int kBN>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t *__restrict__ A,
                                                                   const uint8_t *__restrict__ B,
                                                                   const float *__restrict__ sA,
                                                                   const float *__restrict__ sB, int M, int N, int K,
-                                                                  void *__restrict__ C, Epi epi, GridScratch *gs)
+                                                                  void *__restrict__ C, Epi epi, uint32_t *part,
+                                                                  int tile_base, int n_main)
 {
+    constexpr int kWN = kBN / 2;  // a wave's columns
+    constexpr int kTJ = kWN / 32; // its 32-wide column tiles
     __shared__ __attribute__((aligned(1024))) uint8_t st0[kPTStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[kPTStageBytes];
     __shared__ __attribute__((aligned(16))) uint32_t sx0[kMX ? 2 * kBM : 1]; // A rows' then B rows' scale dwords
     __shared__ __attribute__((aligned(16))) uint32_t sx1[kMX ? 2 * kBM : 1];
     __shared__ uint32_t red[kGemmThreads / 64];
-    constexpr int kStageLoads = kMX ? 18 : 16; // direct loads per lane per stage
+    constexpr int kStageLoads = 8 + kBN / 32 + (kMX ? 2 : 0); // direct loads per lane per stage
 
     int tm, tn;
-    tile_of_block(blockIdx.x, (M + kBM - 1) / kBM, (N + kBM - 1) / kBM, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBM;
+    const int tilesM = (M + kBM - 1) / kBM, tilesN = (N + kBM - 1) / kBM;
+    if constexpr (kBN == kBM) group_tile(xcd_order(blockIdx.x, n_main), tilesM, tilesN, tm, tn);
+    else group_tile(tile_base + (int)(blockIdx.x >> 1), tilesM, tilesN, tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBM + (kBN == kBM ? 0 : (blockIdx.x & 1) * kBN);
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w >> 1, wn = w & 1;
     const int fr = lane & 31, fg = lane >> 5;
     const int nk = K / kBK;
 
-    const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBM, (int64_t)N - n0);
+    const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBN, (int64_t)N - n0);
     const __amdgpu_buffer_rsrc_t ra =
         __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * K), 0, (int)(a_rows * K), kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rb =
@@ -304,16 +313,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
         (void *)(reinterpret_cast<const uint8_t *>(sB) + (kMX ? n0 * kx : 0)), 0, kMX ? (int)(b_rows * kx) : 4,
         kRawBufferWord3);
 
-    // wave w loads rows 8(w + 4u), u = 0..7, of both panels: 16 loads of 1 KiB
-    // (and, MXFP8, the scale dwords of rows 64w .. 64w+63 of both panels)
+    // wave w loads rows 8(w + 4u), u = 0..7, of the A panel and u < kBN / 32
+    // of the B panel (16 or 12 loads of 1 KiB), and, MXFP8, the scale dwords
+    // of rows 64w .. 64w+63 of both panels (rows past the B panel read zero)
     auto stage = [&](uint8_t *st, uint32_t *sx, int kb) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int row = 8 * (w + 4 * u);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + row * kBK), 16, voff, row * K + kb * kBK,
                                                      0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + kBM * kBK + row * kBK), 16, voff,
-                                                     row * K + kb * kBK, 0, 0);
+            if (u < kBN / 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + kBM * kBK + row * kBK), 16, voff,
+                                                         row * K + kb * kBK, 0, 0);
         }
         if constexpr (kMX) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rxa, (lds_void *)(sx + 64 * w), 4, lane * kx,
@@ -323,42 +334,42 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
         }
     };
 
-    v16f acc[4][4];
+    v16f acc[4][kTJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kTJ; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    v8i fa0[4], fb0[4], fa1[4], fb1[4]; // first-half and second-half fragments
+    v8i fa0[4], fb0[kTJ], fa1[4], fb1[kTJ]; // first-half and second-half fragments
     // MXFP8: the scale dwords of the lane's A rows (i) and B rows (j) for the
     // current slice and the next one, pre-shifted by 8 * fg bytes so that byte
     // 0 is the scale of this lane's K block in half 0 and byte 2 in half 1
-    uint32_t xa0[4], xb0[4], xa1[4], xb1[4];
-    auto read_frags = [&](const uint8_t *st, int h, v8i(&a)[4], v8i(&b)[4]) {
+    uint32_t xa0[4], xb0[kTJ], xa1[4], xb1[kTJ];
+    auto read_frags = [&](const uint8_t *st, int h, v8i(&a)[4], v8i(&b)[kTJ]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            b[j] = kMX ? read_frag32_mx(st + kBM * kBK, wn * 128 + 32 * j + fr, fg, h)
-                       : read_frag32(st + kBM * kBK, wn * 128 + 32 * j + fr, fg, h);
+        for (int j = 0; j < kTJ; ++j)
+            b[j] = kMX ? read_frag32_mx(st + kBM * kBK, wn * kWN + 32 * j + fr, fg, h)
+                       : read_frag32(st + kBM * kBK, wn * kWN + 32 * j + fr, fg, h);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             a[i] = kMX ? read_frag32_mx(st, wm * 128 + 32 * i + fr, fg, h) : read_frag32(st, wm * 128 + 32 * i + fr, fg, h);
     };
-    auto read_scales = [&](const uint32_t *sx, uint32_t(&xa)[4], uint32_t(&xb)[4]) {
+    auto read_scales = [&](const uint32_t *sx, uint32_t(&xa)[4], uint32_t(&xb)[kTJ]) {
         if constexpr (kMX) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) xa[i] = sx[wm * 128 + 32 * i + fr] >> (8 * fg);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xb[j] = sx[kBM + wn * 128 + 32 * j + fr] >> (8 * fg);
+            for (int j = 0; j < kTJ; ++j) xb[j] = sx[kBM + wn * kWN + 32 * j + fr] >> (8 * fg);
         }
     };
     // half h of the slice whose scale dwords are xa / xb
-    auto mfmas = [&](const v8i(&a)[4], const v8i(&b)[4], const uint32_t(&xa)[4], const uint32_t(&xb)[4], int h) {
+    auto mfmas = [&](const v8i(&a)[4], const v8i(&b)[kTJ], const uint32_t(&xa)[4], const uint32_t(&xb)[kTJ], int h) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < kTJ; ++j) {
                 if constexpr (kMX) {
                     if (h == 0)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], FB, FA, 0,
@@ -375,14 +386,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     // One slice in stage `cur` (the next one in `nxt`).  `full` = the slices
     // kb + 1 and kb + 2 both exist (no guards).
     auto slice = [&](int kb, uint8_t *cur, uint32_t *sxc, const uint8_t *nxt, const uint32_t *sxn,
-                     const uint32_t(&xa)[4], const uint32_t(&xb)[4], uint32_t(&xan)[4], uint32_t(&xbn)[4],
+                     const uint32_t(&xa)[4], const uint32_t(&xb)[kTJ], uint32_t(&xan)[4], uint32_t(&xbn)[kTJ],
                      bool full) {
         // half 0
         mfmas(fa0, fb0, xa, xb, 0);
         read_frags(cur, 1, fa1, fb1);
         if (full) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
+            for (int t = 0; t < 4 * kTJ; ++t) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // LDS read
             }
@@ -400,7 +411,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
         }
         if (full) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
+            for (int t = 0; t < 4 * kTJ; ++t) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // LDS read
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global -> LDS load
@@ -441,10 +452,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     for (int i = 0; i < 4; ++i) {
         const int64_t row = m0 + wm * 128 + 32 * i + fr;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kTJ; ++j) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t col = n0 + wn * 128 + 32 * j + 8 * q + 4 * fg;
+                const int64_t col = n0 + wn * kWN + 32 * j + 8 * q + 4 * fg;
                 const v4f v = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                   acc[i][j][4 * q + 3]} * alpha;
                 if (row < M && col < N) store_out4<kOut, kAmax, kFuse>(C, row * N + col, col, v, m, epi, out_scale);
@@ -453,7 +464,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     }
     if constexpr (kAmax) {
         m = block_max_u32<kGemmThreads>(m, red);
-        if (tid == 0) gs->part[blockIdx.x] = canonical_amax_bits(m);
+        if (tid == 0) part[blockIdx.x] = canonical_amax_bits(m);
     }
 }
 
@@ -684,28 +695,33 @@ hipError_t launch_gemm_epi(const GemmArgs &a)
 {
     const int m = (int)a.M, n = (int)a.N, k = (int)a.K;
     const Epi epi{a.bias, a.act, a.out_scale_inv};
-    int parts = gemm_grid(a.M, a.N);
+    // A last wave of tiles that is at most half full runs as a full wave of
+    // half tiles (256x128), launched after the full tiles.
+    const int tiles = gemm_grid(a.M, a.N), r = a.cus > 0 ? tiles % a.cus : 0;
+    const int n_main = (r > 0 && 2 * r <= a.cus) ? tiles - r : tiles;
+    const int n_half = 2 * (tiles - n_main);
+    uint32_t *part = a.gs ? a.gs->part : nullptr;
+    uint32_t *part_half = part ? part + n_main : nullptr;
+    const int parts = n_main + n_half;
     if (a.mode == 0 || a.mode == 3) {
-        const int grid = parts;
-#define FP8Q_PT_LAUNCH(FLAG)                                                                                        \
+#define FP8Q_PT_LAUNCH(FLAG, BN, GRID, PART, BASE)                                                                  \
         do {                                                                                                        \
             if (a.amax_out)                                                                                         \
-                gemm_pt_kernel<FA, FB, true, kOut, kFuse, FLAG>                                                     \
-                    <<<grid, kGemmThreads, 0, a.stream>>>(a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, a.gs);           \
+                gemm_pt_kernel<FA, FB, true, kOut, kFuse, FLAG, BN><<<GRID, kGemmThreads, 0, a.stream>>>(           \
+                    a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, PART, BASE, n_main);                                   \
             else                                                                                                    \
-                gemm_pt_kernel<FA, FB, false, kOut, kFuse, FLAG>                                                    \
-                    <<<grid, kGemmThreads, 0, a.stream>>>(a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, a.gs);           \
+                gemm_pt_kernel<FA, FB, false, kOut, kFuse, FLAG, BN><<<GRID, kGemmThreads, 0, a.stream>>>(          \
+                    a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, PART, BASE, n_main);                                   \
         } while (0)
-        if (a.mode == 0) FP8Q_PT_LAUNCH(false);
-        else FP8Q_PT_LAUNCH(true);
+        if (a.mode == 0) {
+            if (n_main > 0) FP8Q_PT_LAUNCH(false, kBM, n_main, part, 0);
+            if (n_half > 0) FP8Q_PT_LAUNCH(false, kBM / 2, n_half, part_half, n_main);
+        } else {
+            if (n_main > 0) FP8Q_PT_LAUNCH(true, kBM, n_main, part, 0);
+            if (n_half > 0) FP8Q_PT_LAUNCH(true, kBM / 2, n_half, part_half, n_main);
+        }
 #undef FP8Q_PT_LAUNCH
     } else {
-        // A last wave of tiles at most half full runs as a full wave of half
-        // tiles (256x128), launched after the full tiles.
-        const int tiles = parts, r = a.cus > 0 ? tiles % a.cus : 0;
-        const int n_main = (r > 0 && 2 * r <= a.cus) ? tiles - r : tiles;
-        const int n_half = 2 * (tiles - n_main);
-        uint32_t *part = a.gs ? a.gs->part : nullptr;
 #define FP8Q_BS_LAUNCH(ROWB, BN, GRID, PART, BASE)                                                                  \
         do {                                                                                                        \
             if (a.amax_out)                                                                                         \
@@ -717,13 +733,12 @@ hipError_t launch_gemm_epi(const GemmArgs &a)
         } while (0)
         if (a.mode == 1) {
             if (n_main > 0) FP8Q_BS_LAUNCH(false, kBM, n_main, part, 0);
-            if (n_half > 0) FP8Q_BS_LAUNCH(false, kBM / 2, n_half, part ? part + n_main : nullptr, n_main);
+            if (n_half > 0) FP8Q_BS_LAUNCH(false, kBM / 2, n_half, part_half, n_main);
         } else {
             if (n_main > 0) FP8Q_BS_LAUNCH(true, kBM, n_main, part, 0);
-            if (n_half > 0) FP8Q_BS_LAUNCH(true, kBM / 2, n_half, part ? part + n_main : nullptr, n_main);
+            if (n_half > 0) FP8Q_BS_LAUNCH(true, kBM / 2, n_half, part_half, n_main);
         }
 #undef FP8Q_BS_LAUNCH
-        parts = n_main + n_half;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.amax_out) return e;

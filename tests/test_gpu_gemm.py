@@ -28,9 +28,10 @@ def _gpu_gemm(A, fa, sA, B, fb, sB, mode):
     M, N = A.shape[0], B.shape[0]
     C = torch.full((M, N), 12345.0, dtype=torch.bfloat16, device="cuda")
     am = scalar(-1.0)
-    sa = to_dev(np.ascontiguousarray(np.float32(sA).reshape(-1)))
-    sb = to_dev(np.ascontiguousarray(np.float32(sB).reshape(-1)))
-    fq.fp8_scaled_gemm(to_dev(A), fa, sa, to_dev(B), fb, sb, mode, C, am)
+    def scales(s):  # E8M0 bytes (MXFP8) pass through; everything else is fp32
+        s = np.asarray(s)
+        return to_dev(np.ascontiguousarray((s if s.dtype == np.uint8 else np.float32(s)).reshape(-1)))
+    fq.fp8_scaled_gemm(to_dev(A), fa, scales(sA), to_dev(B), fb, scales(sB), mode, C, am)
     return bf16_to_f32(host(C)), host(am)[0]
 
 
@@ -202,5 +203,24 @@ def test_gemm_block_last_wave_of_half_tiles(mode, M, N, K):
     xb = workloads.to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
     qa, sa, _, _ = oracle.quantize_block(xa, E4, 1)
     qb, sb, _, _ = oracle.quantize_block(xb, E4, 128 if mode == fq.BLOCK_1x128_128x128 else 1)
+    C, am = _gpu_gemm(qa, E4, sa, qb, E4, sb, mode)
+    _check_tol_and_amax(C, am, oracle.gemm_reference(qa, E4, sa, qb, E4, sb, mode))
+
+
+@pytest.mark.parametrize("mode", [fq.PER_TENSOR, fq.MXFP8])
+@pytest.mark.parametrize("M,N,K", [(4352, 4096, 256), (256, 384, 256), (4352, 3968, 384)])
+def test_gemm_per_tensor_and_mx_last_wave_of_half_tiles(mode, M, N, K):
+    """The per-tensor / MXFP8 kernel's last wave of half tiles (see the
+    block-scaled test above), against the full float64 oracle."""
+    rng = np.random.default_rng(M + 2 * N + K + mode)
+    xa = workloads.to_bf16_bits(rng.standard_normal((M, K)))
+    xb = workloads.to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
+    if mode == fq.MXFP8:
+        qa, sa = oracle.quantize_mx(xa, E4)
+        qb, sb = oracle.quantize_mx(xb, E4)
+    else:
+        ra = oracle.quantize_tensor(xa, E4, amax_in=oracle.amax(xa))
+        rb = oracle.quantize_tensor(xb, E4, amax_in=oracle.amax(xb))
+        qa, sa, qb, sb = ra["q"], ra["scale_inv"], rb["q"], rb["scale_inv"]
     C, am = _gpu_gemm(qa, E4, sa, qb, E4, sb, mode)
     _check_tol_and_amax(C, am, oracle.gemm_reference(qa, E4, sa, qb, E4, sb, mode))
