@@ -15,7 +15,8 @@
 //   MXFP8:      the E8M0 block scales are applied by the matrix instruction
 // The epilogue writes bf16 (RNE), fp32 or FP8 codes of act(v + bias), and
 // optionally the per-block magnitude max of what it emits (folded into
-// amax_out by the finish kernel).
+// amax_out by the finish kernel).  Plain bf16 results go through the LDS
+// stages (free once the K loop is done) and leave as whole row pieces.
 //
 // Two kernels, both with 256x256 block tiles and operand tiles moved from
 // global memory straight into LDS by buffer loads (no register staging),
@@ -199,6 +200,35 @@ __device__ __forceinline__ void store_out4(void *C, int64_t idx, int64_t col, v4
         }
     }
 }
+
+// bf16 results of one wave staged through LDS: kRows x kCols values, rows of
+// kCols * 2 bytes whose 16-byte chunks are XOR-swizzled by the row, so that
+// the 8-byte writes of the matrix-instruction layout and the 16-byte row reads
+// both spread over the banks.  Stored back as whole row pieces: each store
+// instruction writes 64 / NC rows of kCols * 2 contiguous bytes, instead of
+// 16 or 8 bytes in each of 32 or 16 rows.
+template <int kRows, int kCols> struct EpiStage {
+    static constexpr int kPitch = kCols * 2, kNC = kPitch / 16, kRowsPerPass = 64 / kNC;
+    __device__ static __forceinline__ int addr(int r, int c) { return r * kPitch + ((c ^ (r & (kNC - 1))) << 4); }
+    // value quad (4 bf16) at row r, columns 4h .. 4h + 3
+    __device__ static __forceinline__ void put(uint8_t *ep, int r, int h, bf16x4 v)
+    {
+        *reinterpret_cast<bf16x4 *>(ep + addr(r, h >> 1) + 8 * (h & 1)) = v;
+    }
+    // the wave's rows to C (row0, col0: the sub-tile's origin in C)
+    __device__ static __forceinline__ void store(const uint8_t *ep, void *C, int64_t N, int64_t row0, int64_t col0,
+                                                 int lane)
+    {
+        const int c = lane % kNC, rr = lane / kNC;
+        __bf16 *Cb = reinterpret_cast<__bf16 *>(C);
+#pragma unroll 4
+        for (int s = 0; s < kRows / kRowsPerPass; ++s) {
+            const int r = s * kRowsPerPass + rr;
+            const uint4 v = *reinterpret_cast<const uint4 *>(ep + addr(r, c));
+            *reinterpret_cast<uint4 *>(Cb + (row0 + r) * N + col0 + 8 * c) = v;
+        }
+    }
+};
 
 // ---------------------------------------------------------------------------
 // Per-tensor kernel.  256x256 block tile, 2x2 waves of 128x128 as 4x4 tiles
@@ -448,17 +478,48 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     const float alpha = kMX ? 1.0f : (*sA) * (*sB);
     const float out_scale = kOut >= kOutE4M3 ? 1.0f / *epi.out_si : 0.0f;
     uint32_t m = 0;
+    if constexpr (kOut == kOutBF16 && !kFuse) {
+        // M and N are multiples of 128: a wave's sub-tile is wholly inside C
+        // or wholly outside
+        typedef EpiStage<128, kWN> ES;
+        const int64_t wrow0 = m0 + wm * 128, wcol0 = n0 + wn * kWN;
+        const bool inside = wrow0 < M && wcol0 < N;
+        uint8_t *ep = (w < 2 ? st0 : st1) + (w & 1) * (128 * ES::kPitch);
+        __syncthreads(); // no wave reads the stages any more
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t row = m0 + wm * 128 + 32 * i + fr;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < kTJ; ++j) {
+            for (int j = 0; j < kTJ; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t col = n0 + wn * kWN + 32 * j + 8 * q + 4 * fg;
-                const v4f v = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                  acc[i][j][4 * q + 3]} * alpha;
-                if (row < M && col < N) store_out4<kOut, kAmax, kFuse>(C, row * N + col, col, v, m, epi, out_scale);
+                for (int q = 0; q < 4; ++q) {
+                    const v4f v = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                      acc[i][j][4 * q + 3]} * alpha;
+                    const bf16x4 h = __builtin_convertvector(v, bf16x4);
+                    if constexpr (kAmax) {
+                        const uint2 bits = __builtin_bit_cast(uint2, h);
+                        m = max(m, max((bits.x & 0x7FFFu) << 16, (bits.x >> 16 & 0x7FFFu) << 16));
+                        m = max(m, max((bits.y & 0x7FFFu) << 16, (bits.y >> 16 & 0x7FFFu) << 16));
+                    }
+                    ES::put(ep, 32 * i + fr, 8 * j + 2 * q + fg, h);
+                }
+        if (!inside) m = 0;
+        __syncthreads();
+        if (inside) ES::store(ep, C, N, wrow0, wcol0, lane);
+    } else {
+        // fp32, FP8 and fused outputs: straight from the accumulators
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = m0 + wm * 128 + 32 * i + fr;
+#pragma unroll
+            for (int j = 0; j < kTJ; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t col = n0 + wn * kWN + 32 * j + 8 * q + 4 * fg;
+                    const v4f v = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                      acc[i][j][4 * q + 3]} * alpha;
+                    if (row < M && col < N)
+                        store_out4<kOut, kAmax, kFuse>(C, row * N + col, col, v, m, epi, out_scale);
+                }
             }
         }
     }
@@ -673,13 +734,40 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
     // epilogue: lane (fr, fg) of tile (i, j) holds C[row][4 consecutive cols]
     const float out_scale = kOut >= kOutE4M3 ? 1.0f / *epi.out_si : 0.0f;
     uint32_t m = 0;
+    if constexpr (kOut == kOutBF16 && !kFuse) {
+        // bf16 through LDS, as in the per-tensor kernel (64-row wave slabs are
+        // likewise wholly inside or outside C)
+        typedef EpiStage<64, kWN> ES;
+        const int64_t wrow0 = m0 + wm * 64, wcol0 = n0 + wn * kWN;
+        const bool inside = wrow0 < M && wcol0 < N;
+        uint8_t *ep = (w < 4 ? st0 : st1) + (w & 3) * (64 * ES::kPitch);
+        __syncthreads(); // no wave reads the stages any more
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t row = m0 + wm * 64 + 16 * i + fr;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < kTJ; ++j) {
-            const int64_t col = n0 + wn * kWN + 16 * j + 4 * fg;
-            if (row < M && col < N) store_out4<kOut, kAmax, kFuse>(C, row * N + col, col, acc[i][j], m, epi, out_scale);
+            for (int j = 0; j < kTJ; ++j) {
+                const bf16x4 h = __builtin_convertvector(acc[i][j], bf16x4);
+                if constexpr (kAmax) {
+                    const uint2 bits = __builtin_bit_cast(uint2, h);
+                    m = max(m, max((bits.x & 0x7FFFu) << 16, (bits.x >> 16 & 0x7FFFu) << 16));
+                    m = max(m, max((bits.y & 0x7FFFu) << 16, (bits.y >> 16 & 0x7FFFu) << 16));
+                }
+                ES::put(ep, 16 * i + fr, 4 * j + fg, h);
+            }
+        if (!inside) m = 0;
+        __syncthreads();
+        if (inside) ES::store(ep, C, N, wrow0, wcol0, lane);
+    } else {
+        // fp32, FP8 and fused outputs: straight from the accumulators
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = m0 + wm * 64 + 16 * i + fr;
+#pragma unroll
+            for (int j = 0; j < kTJ; ++j) {
+                const int64_t col = n0 + wn * kWN + 16 * j + 4 * fg;
+                if (row < M && col < N)
+                    store_out4<kOut, kAmax, kFuse>(C, row * N + col, col, acc[i][j], m, epi, out_scale);
+            }
         }
     }
     if constexpr (kAmax) {
