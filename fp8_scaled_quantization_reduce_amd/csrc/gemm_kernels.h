@@ -15,8 +15,8 @@
 //   MXFP8:      the E8M0 block scales are applied by the matrix instruction
 // The epilogue writes bf16 (RNE), fp32 or FP8 codes of act(v + bias), and
 // optionally the per-block magnitude max of what it emits (folded into
-// amax_out by the finish kernel).  Plain bf16 results go through the LDS
-// stages (free once the K loop is done) and leave as whole row pieces.
+// amax_out by the finish kernel).  Results go through the LDS stages (free
+// once the K loop is done) and leave as whole row pieces.
 //
 // Two kernels, both with 256x256 block tiles and operand tiles moved from
 // global memory straight into LDS by buffer loads (no register staging),
@@ -156,12 +156,13 @@ struct Epi {
     const float *out_si; // the output's dequant scale s (FP8 output only)
 };
 
-// Apply the epilogue to four consecutive outputs of one row of C, store them
-// and fold their magnitudes into m (canonicalised later): for bf16 and fp32
-// outputs the emitted values, for FP8 outputs the values y before the cast.
+// Apply the epilogue to four consecutive outputs of one row of C (starting at
+// column col) and return their bytes packed from the low end (bf16: 8, fp32:
+// 16, FP8: 4), folding their magnitudes into m (canonicalised later): for bf16
+// and fp32 outputs the emitted values, for FP8 outputs the values y before the
+// cast.
 template <int kOut, bool kAmax, bool kFuse>
-__device__ __forceinline__ void store_out4(void *C, int64_t idx, int64_t col, v4f v, uint32_t &m, const Epi &epi,
-                                           float out_scale)
+__device__ __forceinline__ uint4 pack_out4(int64_t col, v4f v, uint32_t &m, const Epi &epi, float out_scale)
 {
     if constexpr (kFuse) {
         // v is already rounded to binary32; the bias add rounds once more (no
@@ -177,55 +178,64 @@ __device__ __forceinline__ void store_out4(void *C, int64_t idx, int64_t col, v4
         }
     }
     if constexpr (kOut == kOutF32) {
-        *reinterpret_cast<v4f *>(reinterpret_cast<float *>(C) + idx) = v;
         if constexpr (kAmax) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) m = max(m, __float_as_uint(v[e]) & 0x7FFFFFFFu);
         }
+        return __builtin_bit_cast(uint4, v);
     } else if constexpr (kOut == kOutBF16) {
-        const bf16x4 h = __builtin_convertvector(v, bf16x4);
-        *reinterpret_cast<bf16x4 *>(reinterpret_cast<__bf16 *>(C) + idx) = h;
+        const uint2 bits = __builtin_bit_cast(uint2, __builtin_convertvector(v, bf16x4));
         if constexpr (kAmax) {
-            const uint2 bits = __builtin_bit_cast(uint2, h);
             m = max(m, max((bits.x & 0x7FFFu) << 16, (bits.x >> 16 & 0x7FFFu) << 16));
             m = max(m, max((bits.y & 0x7FFFu) << 16, (bits.y >> 16 & 0x7FFFu) << 16));
         }
+        return make_uint4(bits.x, bits.y, 0u, 0u);
     } else {
         constexpr int F = kOut == kOutE4M3 ? kE4M3 : kE5M2;
-        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(C) + idx) =
-            encode4<F>(v[0], v[1], v[2], v[3], out_scale);
         if constexpr (kAmax) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) m = max(m, __float_as_uint(v[e]) & 0x7FFFFFFFu);
         }
+        return make_uint4(encode4<F>(v[0], v[1], v[2], v[3], out_scale), 0u, 0u, 0u);
     }
 }
 
-// bf16 results of one wave staged through LDS: kRows x kCols values, rows of
-// kCols * 2 bytes whose 16-byte chunks are XOR-swizzled by the row, so that
-// the 8-byte writes of the matrix-instruction layout and the 16-byte row reads
-// both spread over the banks.  Stored back as whole row pieces: each store
-// instruction writes 64 / NC rows of kCols * 2 contiguous bytes, instead of
-// 16 or 8 bytes in each of 32 or 16 rows.
-template <int kRows, int kCols> struct EpiStage {
-    static constexpr int kPitch = kCols * 2, kNC = kPitch / 16, kRowsPerPass = 64 / kNC;
+template <int kOut> constexpr int out_bytes() { return kOut == kOutF32 ? 4 : kOut == kOutBF16 ? 2 : 1; }
+
+// A wave's output tile staged through LDS (the operand stages, free once the K
+// loop is done) and stored as whole row pieces.  The matrix-instruction
+// layout leaves each lane four consecutive values of one row, so a direct
+// store instruction would write 4 to 16 bytes into each of 16 or 32 rows;
+// from LDS each store instruction writes 16 bytes per lane along rows of
+// kCols * kB contiguous bytes.  Rows are kCols * kB bytes whose 16-byte chunks
+// are XOR-swizzled by the row, so that both the quad writes and the row reads
+// spread over the banks.  A pass holds kPassRows rows (the whole wave tile
+// unless fp32 does not fit the wave's share of the stages).
+template <int kCols, int kB, int kRows, int kBudget> struct EpiStage {
+    static constexpr int kPitch = kCols * kB, kNC = kPitch / 16, kRowsPerStore = 64 / kNC;
+    static constexpr int kPassRows = kRows * kPitch <= kBudget ? kRows : kBudget / kPitch;
+    static constexpr int kPasses = kRows / kPassRows;
     __device__ static __forceinline__ int addr(int r, int c) { return r * kPitch + ((c ^ (r & (kNC - 1))) << 4); }
-    // value quad (4 bf16) at row r, columns 4h .. 4h + 3
-    __device__ static __forceinline__ void put(uint8_t *ep, int r, int h, bf16x4 v)
+    // packed bytes of quad h (columns 4h .. 4h + 3) of row r
+    __device__ static __forceinline__ void put(uint8_t *ep, int r, int h, uint4 bits)
     {
-        *reinterpret_cast<bf16x4 *>(ep + addr(r, h >> 1) + 8 * (h & 1)) = v;
+        const int o = 4 * h * kB;
+        uint8_t *p = ep + addr(r, o >> 4) + (o & 15);
+        if constexpr (kB == 4) *reinterpret_cast<uint4 *>(p) = bits;
+        else if constexpr (kB == 2) *reinterpret_cast<uint2 *>(p) = make_uint2(bits.x, bits.y);
+        else *reinterpret_cast<uint32_t *>(p) = bits.x;
     }
-    // the wave's rows to C (row0, col0: the sub-tile's origin in C)
+    // kPassRows rows to C [.][N] (elements of kB bytes), from row0, col0
     __device__ static __forceinline__ void store(const uint8_t *ep, void *C, int64_t N, int64_t row0, int64_t col0,
                                                  int lane)
     {
         const int c = lane % kNC, rr = lane / kNC;
-        __bf16 *Cb = reinterpret_cast<__bf16 *>(C);
+        uint8_t *Cb = reinterpret_cast<uint8_t *>(C);
 #pragma unroll 4
-        for (int s = 0; s < kRows / kRowsPerPass; ++s) {
-            const int r = s * kRowsPerPass + rr;
+        for (int s = 0; s < kPassRows / kRowsPerStore; ++s) {
+            const int r = s * kRowsPerStore + rr;
             const uint4 v = *reinterpret_cast<const uint4 *>(ep + addr(r, c));
-            *reinterpret_cast<uint4 *>(Cb + (row0 + r) * N + col0 + 8 * c) = v;
+            *reinterpret_cast<uint4 *>(Cb + ((row0 + r) * N + col0) * kB + 16 * c) = v;
         }
     }
 };
@@ -478,49 +488,34 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     const float alpha = kMX ? 1.0f : (*sA) * (*sB);
     const float out_scale = kOut >= kOutE4M3 ? 1.0f / *epi.out_si : 0.0f;
     uint32_t m = 0;
-    if constexpr (kOut == kOutBF16 && !kFuse) {
+    {
         // M and N are multiples of 128: a wave's sub-tile is wholly inside C
-        // or wholly outside
-        typedef EpiStage<128, kWN> ES;
+        // or wholly outside.  Two waves share each 64 KiB stage.
+        typedef EpiStage<kWN, out_bytes<kOut>(), 128, kPTStageBytes / 2> ES;
         const int64_t wrow0 = m0 + wm * 128, wcol0 = n0 + wn * kWN;
         const bool inside = wrow0 < M && wcol0 < N;
-        uint8_t *ep = (w < 2 ? st0 : st1) + (w & 1) * (128 * ES::kPitch);
-        __syncthreads(); // no wave reads the stages any more
+        uint8_t *ep = (w < 2 ? st0 : st1) + (w & 1) * (kPTStageBytes / 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int ps = 0; ps < ES::kPasses; ++ps) {
+            __syncthreads(); // the stages (then the previous pass) are no longer read
+            if (inside) {
 #pragma unroll
-            for (int j = 0; j < kTJ; ++j)
+                for (int i = 0; i < 4; ++i) {
+                    if ((32 * i) / ES::kPassRows != ps) continue;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const v4f v = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                      acc[i][j][4 * q + 3]} * alpha;
-                    const bf16x4 h = __builtin_convertvector(v, bf16x4);
-                    if constexpr (kAmax) {
-                        const uint2 bits = __builtin_bit_cast(uint2, h);
-                        m = max(m, max((bits.x & 0x7FFFu) << 16, (bits.x >> 16 & 0x7FFFu) << 16));
-                        m = max(m, max((bits.y & 0x7FFFu) << 16, (bits.y >> 16 & 0x7FFFu) << 16));
-                    }
-                    ES::put(ep, 32 * i + fr, 8 * j + 2 * q + fg, h);
-                }
-        if (!inside) m = 0;
-        __syncthreads();
-        if (inside) ES::store(ep, C, N, wrow0, wcol0, lane);
-    } else {
-        // fp32, FP8 and fused outputs: straight from the accumulators
+                    for (int j = 0; j < kTJ; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t row = m0 + wm * 128 + 32 * i + fr;
-#pragma unroll
-            for (int j = 0; j < kTJ; ++j) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t col = n0 + wn * kWN + 32 * j + 8 * q + 4 * fg;
-                    const v4f v = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                      acc[i][j][4 * q + 3]} * alpha;
-                    if (row < M && col < N)
-                        store_out4<kOut, kAmax, kFuse>(C, row * N + col, col, v, m, epi, out_scale);
+                        for (int q = 0; q < 4; ++q) {
+                            const v4f v = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                              acc[i][j][4 * q + 3]} * alpha;
+                            const uint4 bits =
+                                pack_out4<kOut, kAmax, kFuse>(wcol0 + 32 * j + 8 * q + 4 * fg, v, m, epi, out_scale);
+                            ES::put(ep, 32 * i + fr - ps * ES::kPassRows, 8 * j + 2 * q + fg, bits);
+                        }
                 }
             }
+            __syncthreads();
+            if (inside) ES::store(ep, C, N, wrow0 + ps * ES::kPassRows, wcol0, lane);
         }
     }
     if constexpr (kAmax) {
@@ -734,40 +729,30 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
     // epilogue: lane (fr, fg) of tile (i, j) holds C[row][4 consecutive cols]
     const float out_scale = kOut >= kOutE4M3 ? 1.0f / *epi.out_si : 0.0f;
     uint32_t m = 0;
-    if constexpr (kOut == kOutBF16 && !kFuse) {
-        // bf16 through LDS, as in the per-tensor kernel (64-row wave slabs are
-        // likewise wholly inside or outside C)
-        typedef EpiStage<64, kWN> ES;
+    {
+        // staged as in the per-tensor kernel: 64-row wave slabs are likewise
+        // wholly inside or outside C; four waves share each 64 KiB stage
+        typedef EpiStage<kWN, out_bytes<kOut>(), 64, kBSStageBytes / 4> ES;
         const int64_t wrow0 = m0 + wm * 64, wcol0 = n0 + wn * kWN;
         const bool inside = wrow0 < M && wcol0 < N;
-        uint8_t *ep = (w < 4 ? st0 : st1) + (w & 3) * (64 * ES::kPitch);
-        __syncthreads(); // no wave reads the stages any more
+        uint8_t *ep = (w < 4 ? st0 : st1) + (w & 3) * (kBSStageBytes / 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int ps = 0; ps < ES::kPasses; ++ps) {
+            __syncthreads(); // the stages (then the previous pass) are no longer read
+            if (inside) {
 #pragma unroll
-            for (int j = 0; j < kTJ; ++j) {
-                const bf16x4 h = __builtin_convertvector(acc[i][j], bf16x4);
-                if constexpr (kAmax) {
-                    const uint2 bits = __builtin_bit_cast(uint2, h);
-                    m = max(m, max((bits.x & 0x7FFFu) << 16, (bits.x >> 16 & 0x7FFFu) << 16));
-                    m = max(m, max((bits.y & 0x7FFFu) << 16, (bits.y >> 16 & 0x7FFFu) << 16));
+                for (int i = 0; i < 4; ++i) {
+                    if ((16 * i) / ES::kPassRows != ps) continue;
+#pragma unroll
+                    for (int j = 0; j < kTJ; ++j) {
+                        const uint4 bits =
+                            pack_out4<kOut, kAmax, kFuse>(wcol0 + 16 * j + 4 * fg, acc[i][j], m, epi, out_scale);
+                        ES::put(ep, 16 * i + fr - ps * ES::kPassRows, 4 * j + fg, bits);
+                    }
                 }
-                ES::put(ep, 16 * i + fr, 4 * j + fg, h);
             }
-        if (!inside) m = 0;
-        __syncthreads();
-        if (inside) ES::store(ep, C, N, wrow0, wcol0, lane);
-    } else {
-        // fp32, FP8 and fused outputs: straight from the accumulators
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t row = m0 + wm * 64 + 16 * i + fr;
-#pragma unroll
-            for (int j = 0; j < kTJ; ++j) {
-                const int64_t col = n0 + wn * kWN + 16 * j + 4 * fg;
-                if (row < M && col < N)
-                    store_out4<kOut, kAmax, kFuse>(C, row * N + col, col, acc[i][j], m, epi, out_scale);
-            }
+            __syncthreads();
+            if (inside) ES::store(ep, C, N, wrow0 + ps * ES::kPassRows, wcol0, lane);
         }
     }
     if constexpr (kAmax) {
