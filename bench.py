@@ -301,6 +301,12 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream):
     st = torch.empty(4, dtype=torch.int64, device=dev)
     ms = _time(torch, stream, lambda i: fq.fp8_cast_stats(xs[i], E4, sc1, st, stream=stream), 20, rotate=len(xs))
     out["cast_stats_bf16_8192x8192"] = gbs(2 * n, ms)
+    # next: the same counts fused into the cast (given scale, E4M3 codes):
+    # 2 B read + 1 B written per element, against 3 B + 2 B for a cast
+    # followed by the separate statistics pass
+    ms = _time(torch, stream, lambda i: fq.fp8_quantize_tensor_stats(xs[i], E4, qs8[i % 8], st, scale_inv_in=sc1,
+                                                                      stream=stream), 20, rotate=len(xs))
+    out["cast_with_fused_stats_bf16_8192x8192"] = gbs(3 * n, ms)
 
     # next: error-feedback quantization of a 64 Mi-element bf16 gradient to
     # E5M2 with its fp32 residual updated in place (2 + 4 + 1 + 4 B/elem)

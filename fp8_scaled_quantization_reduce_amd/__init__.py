@@ -37,6 +37,7 @@ _VP, _I32, _I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 SIGNATURES = {
     "fp8_amax": [_VP, _I32, _I64, _VP, _VP],
     "fp8_quantize_tensor": [_VP, _I32, _I64, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP],
+    "fp8_quantize_tensor_stats": [_VP, _I32, _I64, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "fp8_dequantize": [_VP, _I32, _I64, _VP, _VP, _VP],
     "fp8_quantize_rowwise_colwise": [_VP, _I32, _I64, _I64, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP],
     "fp8_quantize_block": [_VP, _I32, _I64, _I64, _I32, _I32, _VP, _VP, _VP, _VP, _VP],
@@ -121,6 +122,17 @@ def fp8_quantize_tensor(x, fmt, q, *, amax_in=None, margin=0, scale_inv_in=None,
     """Per-tensor scaled cast; exactly one of amax_in / scale_inv_in."""
     _check(lib.fp8_quantize_tensor(_ptr(x), _dtype(x), x.numel(), fmt, _ptr(amax_in), margin, _ptr(scale_inv_in),
                                    _ptr(q), _ptr(scale_inv_out), _ptr(scale_out), _ptr(amax_out), _stream(stream)))
+
+
+def fp8_quantize_tensor_stats(x, fmt, q, stats, *, amax_in=None, margin=0, scale_inv_in=None, scale_inv_out=None,
+                              scale_out=None, amax_out=None, stream=None):
+    """fp8_quantize_tensor that also writes the cast's counts to stats (int64
+    [4] on the device: overflows, underflows, NaNs, nonzeros) in the same pass."""
+    if stats.dtype not in (torch.int64, torch.uint64) or stats.numel() != 4:
+        raise ValueError("stats must be a 4-element 64-bit integer tensor")
+    _check(lib.fp8_quantize_tensor_stats(_ptr(x), _dtype(x), x.numel(), fmt, _ptr(amax_in), margin,
+                                         _ptr(scale_inv_in), _ptr(q), _ptr(scale_inv_out), _ptr(scale_out),
+                                         _ptr(amax_out), _ptr(stats), _stream(stream)))
 
 
 def fp8_dequantize(q, fmt, scale_inv, y, stream=None):

@@ -125,29 +125,55 @@ int fp8_amax(const void *x, int32_t dtype, int64_t n, float *amax, void *stream)
     return hip_status(fp8q::launch_amax(x, dtype, n, amax, gs, (hipStream_t)stream), fn);
 }
 
-int fp8_quantize_tensor(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *amax_in, int32_t margin,
-                        const float *scale_inv_in, uint8_t *q, float *scale_inv_out, float *scale_out,
-                        float *amax_out, void *stream)
+// fp8_quantize_tensor and, with stats, fp8_quantize_tensor_stats
+static int quantize_tensor(const char *fn, const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *amax_in,
+                           int32_t margin, const float *scale_inv_in, uint8_t *q, float *scale_inv_out,
+                           float *scale_out, float *amax_out, uint64_t *stats, void *stream)
 {
-    const char *fn = "fp8_quantize_tensor";
     if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
     if (!valid_fmt(fmt)) return fail(FP8Q_EINVAL, "%s: unknown format %d", fn, (int)fmt);
     if (n < 0) return fail(FP8Q_EINVAL, "%s: negative n", fn);
     int st = check_scale_src(fn, amax_in, scale_inv_in, scale_inv_out, scale_out, amax_out);
     if (st) return st;
+    if (stats) {
+        const float *scalars[4] = {amax_in ? amax_in : scale_inv_in, scale_inv_out, scale_out, amax_out};
+        if (!aligned(stats, 8)) return fail(FP8Q_EINVAL, "%s: stats must be an 8-byte aligned pointer", fn);
+        for (const float *p : scalars)
+            if (overlap(stats, 32, p, p ? 4 : 0)) return fail(FP8Q_EINVAL, "%s: stats overlaps a scalar", fn);
+    }
     if (n > 0) {
         if (!x || !aligned(x, 16)) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
         if (!q || !aligned(q, 16)) return fail(FP8Q_EINVAL, "%s: q must be a 16-byte aligned pointer", fn);
         if (overlap(x, n * dsize(dtype), q, n)) return fail(FP8Q_EINVAL, "%s: q overlaps x", fn);
+        if (stats && (overlap(x, n * dsize(dtype), stats, 32) || overlap(q, n, stats, 32)))
+            return fail(FP8Q_EINVAL, "%s: stats overlaps x or q", fn);
     }
     fp8q::GridScratch *gs = nullptr;
-    if (amax_out) {
+    if (amax_out || stats) {
         hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
         if (e != hipSuccess) return hip_status(e, fn);
     }
     return hip_status(fp8q::launch_cast(x, dtype, n, fmt, make_src(amax_in, margin, scale_inv_in), q, scale_inv_out,
-                                        scale_out, amax_out, gs, (hipStream_t)stream),
+                                        scale_out, amax_out, stats, gs, (hipStream_t)stream),
                       fn);
+}
+
+int fp8_quantize_tensor(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *amax_in, int32_t margin,
+                        const float *scale_inv_in, uint8_t *q, float *scale_inv_out, float *scale_out,
+                        float *amax_out, void *stream)
+{
+    return quantize_tensor("fp8_quantize_tensor", x, dtype, n, fmt, amax_in, margin, scale_inv_in, q, scale_inv_out,
+                           scale_out, amax_out, nullptr, stream);
+}
+
+int fp8_quantize_tensor_stats(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *amax_in,
+                              int32_t margin, const float *scale_inv_in, uint8_t *q, float *scale_inv_out,
+                              float *scale_out, float *amax_out, uint64_t *stats, void *stream)
+{
+    const char *fn = "fp8_quantize_tensor_stats";
+    if (!stats) return fail(FP8Q_EINVAL, "%s: stats must be given", fn);
+    return quantize_tensor(fn, x, dtype, n, fmt, amax_in, margin, scale_inv_in, q, scale_inv_out, scale_out, amax_out,
+                           stats, stream);
 }
 
 int fp8_dequantize(const uint8_t *q, int32_t fmt, int64_t n, const float *scale_inv, float *y, void *stream)

@@ -37,8 +37,9 @@ hipError_t launch_finish_amax(const GridScratch *gs, int nparts, float *out, hip
 
 hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScratch *gs, hipStream_t s);
 
+// stats (nullable): uint64[4] counts of the cast, reduced in the same pass
 hipError_t launch_cast(const void *x, int dtype, int64_t n, int fmt, ScaleSrc src, uint8_t *q, float *scale_inv_out,
-                       float *scale_out, float *amax_out, GridScratch *gs, hipStream_t s);
+                       float *scale_out, float *amax_out, uint64_t *stats, GridScratch *gs, hipStream_t s);
 
 hipError_t launch_dequant(const uint8_t *q, int fmt, int64_t n, const float *scale_inv, float *y, hipStream_t s);
 

@@ -201,152 +201,6 @@ __device__ __forceinline__ uint4 encode_chunk(const Chunk16<DT> &c, float scale)
     return o;
 }
 
-// Per-tensor cast ("Megatron FP8", section 4): q = encode(fl32(x * scale)).
-// Every lane derives the scale from the device scalar (no host round trip);
-// block 0 publishes it.  A lane encodes U chunks of 16 elements of its unit,
-// kThreads chunks apart, into one 16-byte store each.  With kAmax the input's
-// magnitude max is reduced in the same pass into the block's partial
-// (delayed scaling records it after the cast, section 5).
-constexpr int kCastU = 2;
-
-template <int F, int DT, bool kAmax>
-__global__ __launch_bounds__(kThreads) void cast_kernel(const void *__restrict__ x, int64_t n, ScaleSrc src,
-                                                        uint8_t *__restrict__ q, float *scale_inv_out,
-                                                        float *scale_out, GridScratch *gs)
-{
-    const Scales sc = resolve_scales<F>(src);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        if (scale_inv_out) *scale_inv_out = sc.s;
-        if (scale_out) *scale_out = sc.scale;
-    }
-    const int64_t nch = n >> 4;
-    const int64_t units = ceil_div(nch, (int64_t)kThreads * kCastU);
-    uint4 *__restrict__ qv = reinterpret_cast<uint4 *>(q);
-    uint32_t m = 0;
-    u16x2 m2 = {0, 0};
-    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
-        const int64_t base = unit * kThreads * kCastU + threadIdx.x;
-        // Lanes past the end re-read the last chunk (a valid address, so all
-        // loads are unconditional and stay in registers) and store nothing;
-        // re-reading an element does not change a max.
-        Chunk16<DT> c[kCastU];
-#pragma unroll
-        for (int u = 0; u < kCastU; ++u) {
-            const int64_t ci = base + u * kThreads;
-            c[u].load(x, ci < nch ? ci : nch - 1);
-        }
-#pragma unroll
-        for (int u = 0; u < kCastU; ++u) {
-            if constexpr (kAmax) c[u].absmax(m, m2);
-            const uint4 o = encode_chunk<F, DT>(c[u], sc.scale);
-            if (base + u * kThreads < nch) st_stream(qv + base + u * kThreads, o);
-        }
-    }
-    // tail: fewer than 16 elements, one per lane of block 0
-    if (blockIdx.x == 0 && threadIdx.x < n - (nch << 4)) {
-        const int64_t e = (nch << 4) + threadIdx.x;
-        float v;
-        if constexpr (DT == kBF16)
-            v = __uint_as_float(((uint32_t)reinterpret_cast<const uint16_t *>(x)[e]) << 16);
-        else
-            v = reinterpret_cast<const float *>(x)[e];
-        if constexpr (kAmax) m = max(m, f32_absbits(v));
-        q[e] = (uint8_t)encode1<F>(v, sc.scale);
-    }
-    if constexpr (kAmax) {
-        if constexpr (DT == kBF16) m = max(m, bf16_absmax_to_f32bits(m2));
-        block_partial(m, gs);
-    }
-}
-
-template <int F, int DT>
-static hipError_t launch_cast_t(const void *x, int64_t n, ScaleSrc src, uint8_t *q, float *scale_inv_out,
-                                float *scale_out, float *amax_out, GridScratch *gs, hipStream_t s)
-{
-    const int grid = flat_grid(ceil_div(n >> 4, (int64_t)kThreads * kCastU));
-    if (amax_out)
-        cast_kernel<F, DT, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs);
-    else
-        cast_kernel<F, DT, false><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, nullptr);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !amax_out) return e;
-    return launch_finish_amax(gs, grid, amax_out, s);
-}
-
-hipError_t launch_cast(const void *x, int dtype, int64_t n, int fmt, ScaleSrc src, uint8_t *q, float *scale_inv_out,
-                       float *scale_out, float *amax_out, GridScratch *gs, hipStream_t s)
-{
-    if (fmt == kE4M3) {
-        if (dtype == kBF16) return launch_cast_t<kE4M3, kBF16>(x, n, src, q, scale_inv_out, scale_out, amax_out, gs, s);
-        return launch_cast_t<kE4M3, kF32>(x, n, src, q, scale_inv_out, scale_out, amax_out, gs, s);
-    }
-    if (dtype == kBF16) return launch_cast_t<kE5M2, kBF16>(x, n, src, q, scale_inv_out, scale_out, amax_out, gs, s);
-    return launch_cast_t<kE5M2, kF32>(x, n, src, q, scale_inv_out, scale_out, amax_out, gs, s);
-}
-
-// --------------------------------------------------------------- dequant --
-template <int F, bool kHi>
-__device__ __forceinline__ float2 dec2(uint32_t w)
-{
-    typedef float v2f __attribute__((ext_vector_type(2)));
-    v2f r;
-    if constexpr (F == kE4M3)
-        r = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHi);
-    else
-        r = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, kHi);
-    return make_float2(r.x, r.y);
-}
-
-// y = fl32(value(q) * scale_inv) ("Megatron FP8", section 4).  The hardware
-// decoder gives the exact value of every code.  A lane decodes U words of
-// four codes, kThreads words apart, each into one 16-byte store, so that every
-// store instruction of a wave writes 1 KiB contiguously (the output is four
-// times the input and dominates the traffic).
-constexpr int kDequantU = 2;
-
-template <int F>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__restrict__ q, int64_t n,
-                                                           const float *__restrict__ scale_inv, float *__restrict__ y)
-{
-    const float s = *scale_inv;
-    const int64_t nw = n >> 2;
-    const int64_t units = ceil_div(nw, (int64_t)kThreads * kDequantU);
-    const uint32_t *__restrict__ qw = reinterpret_cast<const uint32_t *>(q);
-    float4 *__restrict__ yv = reinterpret_cast<float4 *>(y);
-    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
-        const int64_t base = unit * kThreads * kDequantU + threadIdx.x;
-        uint32_t w[kDequantU];
-#pragma unroll
-        for (int u = 0; u < kDequantU; ++u) {
-            const int64_t i = base + u * kThreads;
-            w[u] = ld_stream_u32(qw + (i < nw ? i : nw - 1));
-        }
-#pragma unroll
-        for (int u = 0; u < kDequantU; ++u) {
-            const float2 lo = dec2<F, false>(w[u]);
-            const float2 hi = dec2<F, true>(w[u]);
-            if (base + u * kThreads < nw)
-                st_stream(yv + base + u * kThreads, make_uint4(__float_as_uint(lo.x * s), __float_as_uint(lo.y * s),
-                                                               __float_as_uint(hi.x * s), __float_as_uint(hi.y * s)));
-        }
-    }
-    if (blockIdx.x == 0 && threadIdx.x < n - (nw << 2)) {
-        const int64_t e = (nw << 2) + threadIdx.x;
-        y[e] = dec2<F, false>((uint32_t)q[e]).x * s;
-    }
-}
-
-hipError_t launch_dequant(const uint8_t *q, int fmt, int64_t n, const float *scale_inv, float *y, hipStream_t s)
-{
-    if (n == 0) return hipSuccess;
-    const int grid = flat_grid(ceil_div(n >> 2, (int64_t)kThreads * kDequantU));
-    if (fmt == kE4M3)
-        dequant_kernel<kE4M3><<<grid, kThreads, 0, s>>>(q, n, scale_inv, y);
-    else
-        dequant_kernel<kE5M2><<<grid, kThreads, 0, s>>>(q, n, scale_inv, y);
-    return hipGetLastError();
-}
-
 // --------------------------------------------------------- cast statistics --
 // Diagnostics of a per-tensor cast ("Megatron FP8", section 24: per-tensor
 // overflow and underflow counts next to amax and scale).  With
@@ -364,8 +218,9 @@ hipError_t launch_dequant(const uint8_t *q, int fmt, int64_t n, const float *sca
 // differences.  bf16 magnitudes are 16-bit, two to a register, counted with
 // packed 16-bit saturating subtracts (min(m - T, 1)); fp32 magnitudes take
 // the sign of T - m.
-// A read-only stream like the amax; each block writes four partial counts and
-// a one-block kernel sums them into 64-bit totals.
+// fp8_cast_stats is a read-only stream like the amax, and the cast can count
+// in its own pass; either way each block writes four partial counts and a
+// one-block kernel sums them into 64-bit totals.
 template <int F> struct Tiny;
 template <> struct Tiny<kE4M3> { static constexpr float kHalfMinSub = 0x1p-10f; };
 template <> struct Tiny<kE5M2> { static constexpr float kHalfMinSub = 0x1p-17f; };
@@ -465,6 +320,175 @@ __device__ __forceinline__ void chunk_counts(const Chunk16<kF32> &c, const uint3
     }
 }
 
+// Per-tensor cast ("Megatron FP8", section 4): q = encode(fl32(x * scale)).
+// Every lane derives the scale from the device scalar (no host round trip);
+// block 0 publishes it.  A lane encodes U chunks of 16 elements of its unit,
+// kThreads chunks apart, into one 16-byte store each.  With kAmax the input's
+// magnitude max is reduced in the same pass into the block's partial
+// (delayed scaling records it after the cast, section 5).  With kCount the
+// same pass counts the cast's overflows, underflows, NaNs and nonzeros
+// (section 24) against the scale it casts with.
+constexpr int kCastU = 2;
+
+template <int F, int DT, bool kAmax, bool kCount = false>
+__global__ __launch_bounds__(kThreads) void cast_kernel(const void *__restrict__ x, int64_t n, ScaleSrc src,
+                                                        uint8_t *__restrict__ q, float *scale_inv_out,
+                                                        float *scale_out, GridScratch *gs)
+{
+    const Scales sc = resolve_scales<F>(src);
+    uint32_t T[kStats], g[kStats] = {0, 0, 0, 0};
+    if constexpr (kCount) stat_thresholds<F>(sc.scale, T);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (scale_inv_out) *scale_inv_out = sc.s;
+        if (scale_out) *scale_out = sc.scale;
+    }
+    const int64_t nch = n >> 4;
+    const int64_t units = ceil_div(nch, (int64_t)kThreads * kCastU);
+    uint4 *__restrict__ qv = reinterpret_cast<uint4 *>(q);
+    uint32_t m = 0;
+    u16x2 m2 = {0, 0};
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int64_t base = unit * kThreads * kCastU + threadIdx.x;
+        // Lanes past the end re-read the last chunk (a valid address, so all
+        // loads are unconditional and stay in registers) and store nothing;
+        // re-reading an element does not change a max.
+        Chunk16<DT> c[kCastU];
+#pragma unroll
+        for (int u = 0; u < kCastU; ++u) {
+            const int64_t ci = base + u * kThreads;
+            c[u].load(x, ci < nch ? ci : nch - 1);
+        }
+#pragma unroll
+        for (int u = 0; u < kCastU; ++u) {
+            if constexpr (kAmax) c[u].absmax(m, m2);
+            const uint4 o = encode_chunk<F, DT>(c[u], sc.scale);
+            if (base + u * kThreads < nch) {
+                st_stream(qv + base + u * kThreads, o);
+                if constexpr (kCount) chunk_counts(c[u], T, g); // a re-read chunk must not count twice
+            }
+        }
+    }
+    // tail: fewer than 16 elements, one per lane of block 0
+    if (blockIdx.x == 0 && threadIdx.x < n - (nch << 4)) {
+        const int64_t e = (nch << 4) + threadIdx.x;
+        float v;
+        if constexpr (DT == kBF16)
+            v = __uint_as_float(((uint32_t)reinterpret_cast<const uint16_t *>(x)[e]) << 16);
+        else
+            v = reinterpret_cast<const float *>(x)[e];
+        if constexpr (kAmax) m = max(m, f32_absbits(v));
+        q[e] = (uint8_t)encode1<F>(v, sc.scale);
+        if constexpr (kCount) {
+#pragma unroll
+            for (int k = 0; k < kStats; ++k) g[k] += f32_absbits(v) > T[k] ? 1u : 0u;
+        }
+    }
+    if constexpr (kAmax) {
+        if constexpr (DT == kBF16) m = max(m, bf16_absmax_to_f32bits(m2));
+        block_partial(m, gs);
+    }
+    if constexpr (kCount) block_counts(g, gs);
+}
+
+static hipError_t launch_finish_stats(const GridScratch *gs, int nparts, uint64_t *stats, hipStream_t s);
+
+template <int F, int DT>
+static hipError_t launch_cast_t(const void *x, int64_t n, ScaleSrc src, uint8_t *q, float *scale_inv_out,
+                                float *scale_out, float *amax_out, uint64_t *stats, GridScratch *gs, hipStream_t s)
+{
+    const int grid = flat_grid(ceil_div(n >> 4, (int64_t)kThreads * kCastU));
+    if (stats) {
+        if (amax_out)
+            cast_kernel<F, DT, true, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs);
+        else
+            cast_kernel<F, DT, false, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs);
+    } else if (amax_out) {
+        cast_kernel<F, DT, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs);
+    } else {
+        cast_kernel<F, DT, false><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, nullptr);
+    }
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && amax_out) e = launch_finish_amax(gs, grid, amax_out, s);
+    if (e == hipSuccess && stats) e = launch_finish_stats(gs, grid, stats, s);
+    return e;
+}
+
+hipError_t launch_cast(const void *x, int dtype, int64_t n, int fmt, ScaleSrc src, uint8_t *q, float *scale_inv_out,
+                       float *scale_out, float *amax_out, uint64_t *stats, GridScratch *gs, hipStream_t s)
+{
+    if (fmt == kE4M3) {
+        if (dtype == kBF16)
+            return launch_cast_t<kE4M3, kBF16>(x, n, src, q, scale_inv_out, scale_out, amax_out, stats, gs, s);
+        return launch_cast_t<kE4M3, kF32>(x, n, src, q, scale_inv_out, scale_out, amax_out, stats, gs, s);
+    }
+    if (dtype == kBF16)
+        return launch_cast_t<kE5M2, kBF16>(x, n, src, q, scale_inv_out, scale_out, amax_out, stats, gs, s);
+    return launch_cast_t<kE5M2, kF32>(x, n, src, q, scale_inv_out, scale_out, amax_out, stats, gs, s);
+}
+
+// --------------------------------------------------------------- dequant --
+template <int F, bool kHi>
+__device__ __forceinline__ float2 dec2(uint32_t w)
+{
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    v2f r;
+    if constexpr (F == kE4M3)
+        r = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHi);
+    else
+        r = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, kHi);
+    return make_float2(r.x, r.y);
+}
+
+// y = fl32(value(q) * scale_inv) ("Megatron FP8", section 4).  The hardware
+// decoder gives the exact value of every code.  A lane decodes U words of
+// four codes, kThreads words apart, each into one 16-byte store, so that every
+// store instruction of a wave writes 1 KiB contiguously (the output is four
+// times the input and dominates the traffic).
+constexpr int kDequantU = 2;
+
+template <int F>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__restrict__ q, int64_t n,
+                                                           const float *__restrict__ scale_inv, float *__restrict__ y)
+{
+    const float s = *scale_inv;
+    const int64_t nw = n >> 2;
+    const int64_t units = ceil_div(nw, (int64_t)kThreads * kDequantU);
+    const uint32_t *__restrict__ qw = reinterpret_cast<const uint32_t *>(q);
+    float4 *__restrict__ yv = reinterpret_cast<float4 *>(y);
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int64_t base = unit * kThreads * kDequantU + threadIdx.x;
+        uint32_t w[kDequantU];
+#pragma unroll
+        for (int u = 0; u < kDequantU; ++u) {
+            const int64_t i = base + u * kThreads;
+            w[u] = ld_stream_u32(qw + (i < nw ? i : nw - 1));
+        }
+#pragma unroll
+        for (int u = 0; u < kDequantU; ++u) {
+            const float2 lo = dec2<F, false>(w[u]);
+            const float2 hi = dec2<F, true>(w[u]);
+            if (base + u * kThreads < nw)
+                st_stream(yv + base + u * kThreads, make_uint4(__float_as_uint(lo.x * s), __float_as_uint(lo.y * s),
+                                                               __float_as_uint(hi.x * s), __float_as_uint(hi.y * s)));
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x < n - (nw << 2)) {
+        const int64_t e = (nw << 2) + threadIdx.x;
+        y[e] = dec2<F, false>((uint32_t)q[e]).x * s;
+    }
+}
+
+hipError_t launch_dequant(const uint8_t *q, int fmt, int64_t n, const float *scale_inv, float *y, hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    const int grid = flat_grid(ceil_div(n >> 2, (int64_t)kThreads * kDequantU));
+    if (fmt == kE4M3)
+        dequant_kernel<kE4M3><<<grid, kThreads, 0, s>>>(q, n, scale_inv, y);
+    else
+        dequant_kernel<kE5M2><<<grid, kThreads, 0, s>>>(q, n, scale_inv, y);
+    return hipGetLastError();
+}
+
 constexpr int kStatsU = 4;
 
 template <int F, int DT>
@@ -539,7 +563,12 @@ hipError_t launch_cast_stats(const void *x, int dtype, int64_t n, int fmt, const
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    finish_stats_kernel<<<1, kStatsFinishThreads, 0, s>>>(gs, grid, stats);
+    return launch_finish_stats(gs, grid, stats, s);
+}
+
+static hipError_t launch_finish_stats(const GridScratch *gs, int nparts, uint64_t *stats, hipStream_t s)
+{
+    finish_stats_kernel<<<1, kStatsFinishThreads, 0, s>>>(gs, nparts, stats);
     return hipGetLastError();
 }
 
@@ -1356,7 +1385,7 @@ hipError_t launch_rowwise_colwise(const void *x, int dtype, int64_t rows, int64_
 {
     if (rows == 0 || cols == 0) {
         // still publish the scales and an amax of 0
-        return launch_cast(x, dtype, 0, fmt, src, nullptr, scale_inv_out, scale_out, amax_out, gs, s);
+        return launch_cast(x, dtype, 0, fmt, src, nullptr, scale_inv_out, scale_out, amax_out, nullptr, gs, s);
     }
     if (fmt == kE4M3) {
         if (dtype == kBF16)

@@ -109,6 +109,23 @@ int fp8_quantize_tensor(const void *x, int32_t dtype, int64_t n, int32_t fmt, co
                         float *scale_out, float *amax_out, void *stream);
 
 /*
+ * fp8_quantize_tensor_stats -- fp8_quantize_tensor that also counts, in the
+ * same pass over x, what the cast did ([MFP8] section 24: per-tensor
+ * overflow and underflow counts reported next to amax and scale; the counts
+ * of fp8_cast_stats, taken against the scale s this call casts with, so that
+ * monitoring a cast costs no second read of x):
+ *   stats[0] overflows (x not NaN and |fl32(x * fl32(1/s))| > FP8_MAX),
+ *   stats[1] underflows (x finite and nonzero with a zero code),
+ *   stats[2] NaNs, stats[3] nonzeros (x not NaN and x != 0).
+ *   stats  device uint64_t[4], 8-byte aligned, required; overwritten.
+ * Every other argument, and every error, as in fp8_quantize_tensor; plus
+ * FP8Q_EINVAL when stats is null, misaligned, or overlaps x, q or a scalar.
+ */
+int fp8_quantize_tensor_stats(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *amax_in,
+                              int32_t margin, const float *scale_inv_in, uint8_t *q, float *scale_inv_out,
+                              float *scale_out, float *amax_out, uint64_t *stats, void *stream);
+
+/*
  * fp8_dequantize -- y_i = fl32(value(q_i) * *scale_inv) ([MFP8] section 4: the
  * cached inverse makes dequantization one element multiply; section 23:
  * reconstruction = fp8 value times scale).  With scale_inv = 1 over the 256
