@@ -87,6 +87,19 @@ def test_quantize_tensor_validation():
             fq.EINVAL, "aligned")
 
 
+def test_quantize_tensor_stats_validation():
+    q, st, am = BAD + 0x10000, BAD + 0x20000, BAD + 0x800
+    f = L.fp8_quantize_tensor_stats
+    _expect(f(BAD, fq.BF16, 64, 0, am, 0, None, q, None, None, None, None, S), fq.EINVAL, "stats must be given")
+    _expect(f(BAD, fq.BF16, 64, 0, am, 0, None, q, None, None, None, st + 4, S), fq.EINVAL, "8-byte")
+    _expect(f(BAD, fq.BF16, 64, 0, am, 0, None, q, None, None, None, am - 8, S), fq.EINVAL, "stats overlaps a scalar")
+    _expect(f(BAD, fq.BF16, 64, 0, am, 0, None, q, None, None, None, BAD + 64, S), fq.EINVAL, "stats overlaps x")
+    _expect(f(BAD, fq.BF16, 64, 0, am, 0, None, q, None, None, None, q + 32, S), fq.EINVAL, "stats overlaps x or q")
+    # the checks of fp8_quantize_tensor come first, under this call's name
+    _expect(f(BAD, fq.BF16, 64, 5, am, 0, None, q, None, None, None, st, S), fq.EINVAL, "fp8_quantize_tensor_stats")
+    _expect(f(BAD, fq.BF16, 64, 0, None, 0, None, q, None, None, None, st, S), fq.EINVAL, "exactly one")
+
+
 def test_dequant_and_rowwise_colwise_validation():
     _expect(L.fp8_dequantize(BAD, 3, 16, BAD + 0x800, BAD + 0x1000, S), fq.EINVAL, "format")
     _expect(L.fp8_dequantize(BAD, 0, 16, None, BAD + 0x1000, S), fq.EINVAL, "scale_inv")
