@@ -212,12 +212,12 @@ __device__ __forceinline__ uint4 encode_chunk(const Chunk16<DT> &c, float scale)
 //   NaN, and nonzero (not NaN, x != 0).
 // |y| is monotone in |x|, so the classes are intervals of the magnitude bits
 // m of x: zero, underflow (0, U], normal, overflow (O, inf], NaN above inf,
-// with U and O found once per lane by bisection over the bit patterns (the
-// largest magnitude whose product stays at or below the limit).  A lane
-// counts m > T for T = 0, U, O, inf and the four counts follow by
-// differences.  bf16 magnitudes are 16-bit, two to a register, counted with
-// packed 16-bit saturating subtracts (min(m - T, 1)); fp32 magnitudes take
-// the sign of T - m.
+// with U and O the largest magnitudes whose products stay at or below the
+// limits (found per block by a short walk from limit / scale, a bisection over
+// the bit patterns only if the walk does not settle).  A lane counts m > T
+// for T = 0, U, O, inf and the four counts follow by differences.  bf16
+// magnitudes are 16-bit, two to a register, and m > T is the sign bit of the
+// packed 16-bit difference T - m; fp32 magnitudes take the sign of T - m.
 // fp8_cast_stats is a read-only stream like the amax, and the cast can count
 // in its own pass; either way each block writes four partial counts and a
 // one-block kernel sums them into 64-bit totals.
