@@ -83,3 +83,45 @@ def test_delayed_scaling_on_two_streams():
             oracle.delayed_update(hist, 0, r["amax"], t, fmt_next, 0, oracle.ALGO_MAX, sc, si)
         assert np.array_equal(f32_bits(host(d["hist"])), f32_bits(hist))
         assert f32_bits(host(d["si"])[0]) == f32_bits(si[0]) and f32_bits(host(d["sc"])[0]) == f32_bits(sc[0])
+
+
+def test_gemms_with_output_amax_on_two_streams():
+    """Per-tensor and block-scaled GEMMs with an output amax (block partials in
+    the stream's scratch, then a finish kernel) launched alternately on two
+    streams: each C is within the GEMM tolerance of the float64 reference and
+    each amax is max |C| of its own output."""
+    dev = "cuda"
+    M, N, K = 512, 768, 1024
+    cases = []
+    for seeds in ((11, 12), (13, 14)):
+        a, b = workloads.gemm_pair(M, N, K, seeds=seeds)
+        qa = oracle.quantize_block(a, E4, 1)
+        qb = oracle.quantize_block(b, E4, 128)
+        cases.append(dict(A=qa[0], sA=qa[1], B=qb[0], sB=qb[1]))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for k in range(2):
+        c = cases[k]
+        with torch.cuda.stream(streams[k]):
+            outs.append(dict(A=to_dev(c["A"]), sA=to_dev(c["sA"]), B=to_dev(c["B"]), sB=to_dev(c["sB"]),
+                             one=torch.ones(1, device=dev),
+                             Cb=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                             Cp=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                             ab=torch.full((1,), -1.0, device=dev), ap=torch.full((1,), -1.0, device=dev)))
+    torch.cuda.synchronize()
+    for _ in range(6):
+        for k in range(2):
+            o, s = outs[k], streams[k]
+            fq.fp8_scaled_gemm(o["A"], E4, o["sA"], o["B"], E4, o["sB"], fq.BLOCK_1x128_128x128, o["Cb"], o["ab"],
+                               stream=s)
+            fq.fp8_scaled_gemm(o["A"], E4, o["one"], o["B"], E4, o["one"], fq.PER_TENSOR, o["Cp"], o["ap"],
+                               stream=s)
+    torch.cuda.synchronize()
+    for k in range(2):
+        c, o = cases[k], outs[k]
+        for C, am, R in ((o["Cb"], o["ab"], oracle.gemm_reference(c["A"], E4, c["sA"], c["B"], E4, c["sB"],
+                                                                    oracle.BLOCK_1x128_128x128)),
+                         (o["Cp"], o["ap"], oracle.gemm_reference(c["A"], E4, 1.0, c["B"], E4, 1.0))):
+            cf = C.float().cpu().numpy()
+            assert np.max(np.abs(cf - R)) <= 1e-2 * np.max(np.abs(R))
+            assert host(am)[0] == np.max(np.abs(cf))
