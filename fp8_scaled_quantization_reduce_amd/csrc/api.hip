@@ -3,15 +3,40 @@
 // Host-side validation happens before any HIP call, so argument errors are
 // reported without touching the device; valid calls only enqueue kernels on
 // the caller's stream.  Messages for the last error are thread-local.
+//
+// Reduction scratch.  Calls that reduce over a grid (an amax, the cast
+// statistics) fold per-block partials in a small scratch slot and finish with
+// a one-block kernel that reads the slot and leaves it zero.  The slots are
+// one device global, `scratch` below: kScratchSlots slots of 3 KiB on every
+// device the library runs on, held until the process ends.  The library never
+// allocates device memory.  Each stream that runs a reducing call gets a slot
+// of its own on first use (a host-side table, no device work), so calls on
+// different streams never share partials; a host mutex per slot is held while
+// one call enqueues its kernels, so calls from several host threads on one
+// stream cannot interleave their partials.  A device with more than
+// kScratchSlots such streams returns FP8Q_EUNSUPPORTED.
+//
+// FP8Q_DEBUG (environment, read once): when set to a non-empty value other
+// than "0", every call prints one line to stderr -- the entry point, its sizes
+// and formats, the stream and scratch slot, and the status with its message.
+// The line is written after the kernels are enqueued; it never waits for the
+// device.
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <thread>
 #include <utility>
 
 #include "fp8q.h"
 #include "fp8q_launch.h"
+
+// Every device's reduction scratch (zero-initialised when the code object is
+// loaded on the device).  Host code never takes this name as a device
+// address: the address on the current device comes from hipGetSymbolAddress.
+static __device__ __align__(256) fp8q::GridScratch scratch[fp8q::kScratchSlots];
 
 namespace {
 
@@ -37,6 +62,138 @@ int hip_status(hipError_t e, const char *what)
     if (e != hipSuccess) return fail(FP8Q_EHIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
 }
+
+bool debug_enabled()
+{
+    static const bool on = [] {
+        const char *v = std::getenv("FP8Q_DEBUG");
+        return v && v[0] && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+// ------------------------------------------------------ scratch slots ----
+constexpr int kMaxDevices = 64;
+
+struct Slot {
+    std::mutex mu;      // held across the launches of one call
+    bool dirty = false; // a failed call may have left partials in the slot
+};
+
+struct StreamKey {
+    hipStream_t s;
+    std::thread::id thread; // only for the per-thread default stream, whose handle is shared
+    bool operator<(const StreamKey &o) const { return s != o.s ? s < o.s : thread < o.thread; }
+};
+
+struct DeviceScratch {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    fp8q::GridScratch *base = nullptr; // address of `scratch` on this device
+    Slot slots[fp8q::kScratchSlots];
+    std::map<StreamKey, int> slot_of; // guarded by g_table_mu
+};
+
+DeviceScratch g_devices[kMaxDevices];
+std::mutex g_table_mu;
+
+// The scratch slot of the current device and stream `s`, locked for the
+// duration of one call.
+class ScratchLease {
+public:
+    // FP8Q_OK, or an error status with its message set
+    int acquire(const char *fn, hipStream_t s)
+    {
+        int dev = -1;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_status(e, fn);
+        if (dev < 0 || dev >= kMaxDevices) return fail(FP8Q_EUNSUPPORTED, "%s: device %d out of range", fn, dev);
+        DeviceScratch &d = g_devices[dev];
+        // once per device, with that device current
+        std::call_once(d.once, [&d] { d.err = hipGetSymbolAddress((void **)&d.base, HIP_SYMBOL(scratch)); });
+        if (d.err != hipSuccess) return hip_status(d.err, fn);
+        int idx;
+        {
+            std::lock_guard<std::mutex> lock(g_table_mu);
+            const StreamKey key{s, s == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id()};
+            auto it = d.slot_of.find(key);
+            if (it != d.slot_of.end()) {
+                idx = it->second;
+            } else {
+                if ((int)d.slot_of.size() >= fp8q::kScratchSlots)
+                    return fail(FP8Q_EUNSUPPORTED,
+                                "%s: more than %d streams on device %d have run reducing calls (scratch slots)", fn,
+                                fp8q::kScratchSlots, dev);
+                idx = (int)d.slot_of.size();
+                d.slot_of.emplace(key, idx);
+            }
+        }
+        slot_ = &d.slots[idx];
+        lock_ = std::unique_lock<std::mutex>(slot_->mu);
+        index_ = idx;
+        gs = d.base + idx;
+        if (slot_->dirty) {
+            e = fp8q::launch_clear_scratch(gs, s);
+            if (e != hipSuccess) return hip_status(e, fn);
+            slot_->dirty = false;
+        }
+        return FP8Q_OK;
+    }
+    // record the outcome of the call's launches
+    int settle(int status)
+    {
+        if (slot_ && status != FP8Q_OK) slot_->dirty = true;
+        return status;
+    }
+    int index() const { return index_; }
+    fp8q::GridScratch *gs = nullptr;
+
+private:
+    Slot *slot_ = nullptr;
+    int index_ = -1;
+    std::unique_lock<std::mutex> lock_;
+};
+
+// One entry-point call: its optional scratch lease and its debug line.
+class Call {
+public:
+    Call(const char *fn, void *stream) : fn_(fn), stream_(stream) { args_[0] = '\0'; }
+    ~Call()
+    {
+        if (!debug_enabled()) return;
+        std::fprintf(stderr, "fp8q: %s(%s) stream=%p slot=%d -> %d%s%s\n", fn_, args_, stream_, lease_.index(),
+                     status_, status_ ? " " : "", status_ ? g_err : "");
+        std::fflush(stderr);
+    }
+    // sizes and formats for the debug line (formatted only when it is on)
+    void args(const char *fmt, ...)
+    {
+        if (!debug_enabled()) return;
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(args_, sizeof(args_), fmt, ap);
+        va_end(ap);
+    }
+    int scratch(fp8q::GridScratch **gs)
+    {
+        const int st = lease_.acquire(fn_, (hipStream_t)stream_);
+        *gs = st == FP8Q_OK ? lease_.gs : nullptr;
+        return st;
+    }
+    int ret(int status)
+    {
+        status_ = lease_.settle(status);
+        return status_;
+    }
+    int launched(hipError_t e) { return ret(hip_status(e, fn_)); }
+
+private:
+    const char *fn_;
+    void *stream_;
+    char args_[192];
+    int status_ = FP8Q_OK;
+    ScratchLease lease_;
+};
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool valid_fmt(int32_t f) { return f == FP8Q_E4M3FN || f == FP8Q_E5M2; }
@@ -77,41 +234,9 @@ fp8q::ScaleSrc make_src(const float *amax_in, int32_t margin, const float *scale
 
 } // namespace
 
-namespace fp8q {
+extern "C" const char *fp8q_last_error(void) { return g_err; }
 
-// One reduction scratch per (device, stream): calls on one stream run in
-// order, so they can share it; different streams never do.  Allocated on the
-// first call that needs it and held until the process ends.
-hipError_t get_grid_scratch(hipStream_t s, GridScratch **out)
-{
-    static std::mutex mu;
-    static std::map<std::pair<int, hipStream_t>, GridScratch *> table;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(mu);
-    const auto key = std::make_pair(dev, s);
-    auto it = table.find(key);
-    if (it != table.end()) {
-        *out = it->second;
-        return hipSuccess;
-    }
-    void *p = nullptr;
-    e = hipMalloc(&p, sizeof(GridScratch));
-    if (e != hipSuccess) return e;
-    GridScratch *gs = static_cast<GridScratch *>(p);
-    table.emplace(key, gs);
-    *out = gs;
-    return hipSuccess;
-}
-
-} // namespace fp8q
-
-extern "C" {
-
-const char *fp8q_last_error(void) { return g_err; }
-
-int fp8_amax(const void *x, int32_t dtype, int64_t n, float *amax, void *stream)
+static int fp8_amax_impl(Call &c, const void *x, int32_t dtype, int64_t n, float *amax, void *stream)
 {
     const char *fn = "fp8_amax";
     if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
@@ -120,15 +245,22 @@ int fp8_amax(const void *x, int32_t dtype, int64_t n, float *amax, void *stream)
     if (n > 0 && (!x || !aligned(x, 16))) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
     if (overlap(x, n * dsize(dtype), amax, 4)) return fail(FP8Q_EINVAL, "%s: amax overlaps x", fn);
     fp8q::GridScratch *gs = nullptr;
-    hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
-    if (e != hipSuccess) return hip_status(e, fn);
+    const int st = c.scratch(&gs);
+    if (st) return st;
     return hip_status(fp8q::launch_amax(x, dtype, n, amax, gs, (hipStream_t)stream), fn);
 }
 
+extern "C" int fp8_amax(const void *x, int32_t dtype, int64_t n, float *amax, void *stream)
+{
+    Call c("fp8_amax", stream);
+    c.args("dtype=%lld n=%lld", (long long)dtype, (long long)n);
+    return c.ret(fp8_amax_impl(c, x, dtype, n, amax, stream));
+}
+
 // fp8_quantize_tensor and, with stats, fp8_quantize_tensor_stats
-static int quantize_tensor(const char *fn, const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *amax_in,
-                           int32_t margin, const float *scale_inv_in, uint8_t *q, float *scale_inv_out,
-                           float *scale_out, float *amax_out, uint64_t *stats, void *stream)
+static int quantize_tensor(Call &c, const char *fn, const void *x, int32_t dtype, int64_t n, int32_t fmt,
+                           const float *amax_in, int32_t margin, const float *scale_inv_in, uint8_t *q,
+                           float *scale_inv_out, float *scale_out, float *amax_out, uint64_t *stats, void *stream)
 {
     if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
     if (!valid_fmt(fmt)) return fail(FP8Q_EINVAL, "%s: unknown format %d", fn, (int)fmt);
@@ -150,33 +282,52 @@ static int quantize_tensor(const char *fn, const void *x, int32_t dtype, int64_t
     }
     fp8q::GridScratch *gs = nullptr;
     if (amax_out || stats) {
-        hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
-        if (e != hipSuccess) return hip_status(e, fn);
+        const int st = c.scratch(&gs);
+        if (st) return st;
     }
     return hip_status(fp8q::launch_cast(x, dtype, n, fmt, make_src(amax_in, margin, scale_inv_in), q, scale_inv_out,
                                         scale_out, amax_out, stats, gs, (hipStream_t)stream),
                       fn);
 }
 
-int fp8_quantize_tensor(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *amax_in, int32_t margin,
-                        const float *scale_inv_in, uint8_t *q, float *scale_inv_out, float *scale_out,
-                        float *amax_out, void *stream)
+static int fp8_quantize_tensor_impl(Call &c, const void *x, int32_t dtype, int64_t n, int32_t fmt,
+                                    const float *amax_in, int32_t margin, const float *scale_inv_in, uint8_t *q,
+                                    float *scale_inv_out, float *scale_out, float *amax_out, void *stream)
 {
-    return quantize_tensor("fp8_quantize_tensor", x, dtype, n, fmt, amax_in, margin, scale_inv_in, q, scale_inv_out,
+    return quantize_tensor(c, "fp8_quantize_tensor", x, dtype, n, fmt, amax_in, margin, scale_inv_in, q, scale_inv_out,
                            scale_out, amax_out, nullptr, stream);
 }
 
-int fp8_quantize_tensor_stats(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *amax_in,
-                              int32_t margin, const float *scale_inv_in, uint8_t *q, float *scale_inv_out,
-                              float *scale_out, float *amax_out, uint64_t *stats, void *stream)
+extern "C" int fp8_quantize_tensor(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *amax_in,
+                                   int32_t margin, const float *scale_inv_in, uint8_t *q, float *scale_inv_out,
+                                   float *scale_out, float *amax_out, void *stream)
+{
+    Call c("fp8_quantize_tensor", stream);
+    c.args("dtype=%lld n=%lld fmt=%lld margin=%lld", (long long)dtype, (long long)n, (long long)fmt, (long long)margin);
+    return c.ret(fp8_quantize_tensor_impl(c, x, dtype, n, fmt, amax_in, margin, scale_inv_in, q, scale_inv_out, scale_out, amax_out, stream));
+}
+
+static int fp8_quantize_tensor_stats_impl(Call &c, const void *x, int32_t dtype, int64_t n, int32_t fmt,
+                                          const float *amax_in, int32_t margin, const float *scale_inv_in, uint8_t *q,
+                                          float *scale_inv_out, float *scale_out, float *amax_out, uint64_t *stats,
+                                          void *stream)
 {
     const char *fn = "fp8_quantize_tensor_stats";
     if (!stats) return fail(FP8Q_EINVAL, "%s: stats must be given", fn);
-    return quantize_tensor(fn, x, dtype, n, fmt, amax_in, margin, scale_inv_in, q, scale_inv_out, scale_out, amax_out,
+    return quantize_tensor(c, fn, x, dtype, n, fmt, amax_in, margin, scale_inv_in, q, scale_inv_out, scale_out, amax_out,
                            stats, stream);
 }
 
-int fp8_dequantize(const uint8_t *q, int32_t fmt, int64_t n, const float *scale_inv, float *y, void *stream)
+extern "C" int fp8_quantize_tensor_stats(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *amax_in,
+                                         int32_t margin, const float *scale_inv_in, uint8_t *q, float *scale_inv_out,
+                                         float *scale_out, float *amax_out, uint64_t *stats, void *stream)
+{
+    Call c("fp8_quantize_tensor_stats", stream);
+    c.args("dtype=%lld n=%lld fmt=%lld margin=%lld", (long long)dtype, (long long)n, (long long)fmt, (long long)margin);
+    return c.ret(fp8_quantize_tensor_stats_impl(c, x, dtype, n, fmt, amax_in, margin, scale_inv_in, q, scale_inv_out, scale_out, amax_out, stats, stream));
+}
+
+static int fp8_dequantize_impl(Call &c, const uint8_t *q, int32_t fmt, int64_t n, const float *scale_inv, float *y, void *stream)
 {
     const char *fn = "fp8_dequantize";
     if (!valid_fmt(fmt)) return fail(FP8Q_EINVAL, "%s: unknown format %d", fn, (int)fmt);
@@ -190,10 +341,17 @@ int fp8_dequantize(const uint8_t *q, int32_t fmt, int64_t n, const float *scale_
     return hip_status(fp8q::launch_dequant(q, fmt, n, scale_inv, y, (hipStream_t)stream), fn);
 }
 
-int fp8_quantize_rowwise_colwise(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt,
-                                 const float *amax_in, int32_t margin, const float *scale_inv_in, uint8_t *q_row,
-                                 uint8_t *q_col, float *scale_inv_out, float *scale_out, float *amax_out,
-                                 void *stream)
+extern "C" int fp8_dequantize(const uint8_t *q, int32_t fmt, int64_t n, const float *scale_inv, float *y, void *stream)
+{
+    Call c("fp8_dequantize", stream);
+    c.args("fmt=%lld n=%lld", (long long)fmt, (long long)n);
+    return c.ret(fp8_dequantize_impl(c, q, fmt, n, scale_inv, y, stream));
+}
+
+static int fp8_quantize_rowwise_colwise_impl(Call &c, const void *x, int32_t dtype, int64_t rows, int64_t cols,
+                                             int32_t fmt, const float *amax_in, int32_t margin,
+                                             const float *scale_inv_in, uint8_t *q_row, uint8_t *q_col,
+                                             float *scale_inv_out, float *scale_out, float *amax_out, void *stream)
 {
     const char *fn = "fp8_quantize_rowwise_colwise";
     if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
@@ -216,8 +374,8 @@ int fp8_quantize_rowwise_colwise(const void *x, int32_t dtype, int64_t rows, int
     }
     fp8q::GridScratch *gs = nullptr;
     if (amax_out) {
-        hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
-        if (e != hipSuccess) return hip_status(e, fn);
+        const int st = c.scratch(&gs);
+        if (st) return st;
     }
     return hip_status(fp8q::launch_rowwise_colwise(x, dtype, rows, cols, fmt, make_src(amax_in, margin, scale_inv_in),
                                                    q_row, q_col, scale_inv_out, scale_out, amax_out, gs,
@@ -225,8 +383,19 @@ int fp8_quantize_rowwise_colwise(const void *x, int32_t dtype, int64_t rows, int
                       fn);
 }
 
-int fp8_quantize_block(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt, int32_t block_rows,
-                       uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col, void *stream)
+extern "C" int fp8_quantize_rowwise_colwise(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt,
+                                            const float *amax_in, int32_t margin, const float *scale_inv_in,
+                                            uint8_t *q_row, uint8_t *q_col, float *scale_inv_out, float *scale_out,
+                                            float *amax_out, void *stream)
+{
+    Call c("fp8_quantize_rowwise_colwise", stream);
+    c.args("dtype=%lld rows=%lld cols=%lld fmt=%lld margin=%lld", (long long)dtype, (long long)rows, (long long)cols, (long long)fmt, (long long)margin);
+    return c.ret(fp8_quantize_rowwise_colwise_impl(c, x, dtype, rows, cols, fmt, amax_in, margin, scale_inv_in, q_row, q_col, scale_inv_out, scale_out, amax_out, stream));
+}
+
+static int fp8_quantize_block_impl(Call &c, const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt,
+                                   int32_t block_rows, uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col,
+                                   void *stream)
 {
     const char *fn = "fp8_quantize_block";
     if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
@@ -255,8 +424,17 @@ int fp8_quantize_block(const void *x, int32_t dtype, int64_t rows, int64_t cols,
                       fn);
 }
 
-int fp8_quantize_mx(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt, uint8_t *q_row,
-                    uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, void *stream)
+extern "C" int fp8_quantize_block(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt,
+                                  int32_t block_rows, uint8_t *q_row, float *s_row, uint8_t *q_col, float *s_col,
+                                  void *stream)
+{
+    Call c("fp8_quantize_block", stream);
+    c.args("dtype=%lld rows=%lld cols=%lld fmt=%lld block_rows=%lld", (long long)dtype, (long long)rows, (long long)cols, (long long)fmt, (long long)block_rows);
+    return c.ret(fp8_quantize_block_impl(c, x, dtype, rows, cols, fmt, block_rows, q_row, s_row, q_col, s_col, stream));
+}
+
+static int fp8_quantize_mx_impl(Call &c, const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt,
+                                uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, void *stream)
 {
     const char *fn = "fp8_quantize_mx";
     if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
@@ -283,9 +461,17 @@ int fp8_quantize_mx(const void *x, int32_t dtype, int64_t rows, int64_t cols, in
     return hip_status(fp8q::launch_mx(x, dtype, rows, cols, fmt, q_row, s_row, q_col, s_col, (hipStream_t)stream), fn);
 }
 
-int fp8_update_scale_delayed(float *hist, int32_t history_len, int32_t n_cols, int32_t col, const float *new_amax,
-                             int64_t step, int32_t fmt, int32_t margin, int32_t algo, float *scale, float *scale_inv,
-                             void *stream)
+extern "C" int fp8_quantize_mx(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t fmt, uint8_t *q_row,
+                               uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, void *stream)
+{
+    Call c("fp8_quantize_mx", stream);
+    c.args("dtype=%lld rows=%lld cols=%lld fmt=%lld", (long long)dtype, (long long)rows, (long long)cols, (long long)fmt);
+    return c.ret(fp8_quantize_mx_impl(c, x, dtype, rows, cols, fmt, q_row, s_row, q_col, s_col, stream));
+}
+
+static int fp8_update_scale_delayed_impl(Call &c, float *hist, int32_t history_len, int32_t n_cols, int32_t col,
+                                         const float *new_amax, int64_t step, int32_t fmt, int32_t margin,
+                                         int32_t algo, float *scale, float *scale_inv, void *stream)
 {
     const char *fn = "fp8_update_scale_delayed";
     if (!valid_fmt(fmt)) return fail(FP8Q_EINVAL, "%s: unknown format %d", fn, (int)fmt);
@@ -307,10 +493,19 @@ int fp8_update_scale_delayed(float *hist, int32_t history_len, int32_t n_cols, i
                       fn);
 }
 
-int fp8_quantize_delayed(const void *x, int32_t dtype, int64_t n, int32_t fmt, float *hist, int32_t history_len,
-                         int32_t n_cols, int32_t col, int64_t step, int32_t fmt_next, int32_t margin, int32_t algo,
-                         float *scale, float *scale_inv, uint8_t *q, float *q_scale_inv_out, float *amax_out,
-                         void *stream)
+extern "C" int fp8_update_scale_delayed(float *hist, int32_t history_len, int32_t n_cols, int32_t col,
+                                        const float *new_amax, int64_t step, int32_t fmt, int32_t margin,
+                                        int32_t algo, float *scale, float *scale_inv, void *stream)
+{
+    Call c("fp8_update_scale_delayed", stream);
+    c.args("history_len=%lld n_cols=%lld col=%lld step=%lld fmt=%lld margin=%lld algo=%lld", (long long)history_len, (long long)n_cols, (long long)col, (long long)step, (long long)fmt, (long long)margin, (long long)algo);
+    return c.ret(fp8_update_scale_delayed_impl(c, hist, history_len, n_cols, col, new_amax, step, fmt, margin, algo, scale, scale_inv, stream));
+}
+
+static int fp8_quantize_delayed_impl(Call &c, const void *x, int32_t dtype, int64_t n, int32_t fmt, float *hist,
+                                     int32_t history_len, int32_t n_cols, int32_t col, int64_t step, int32_t fmt_next,
+                                     int32_t margin, int32_t algo, float *scale, float *scale_inv, uint8_t *q,
+                                     float *q_scale_inv_out, float *amax_out, void *stream)
 {
     const char *fn = "fp8_quantize_delayed";
     if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
@@ -343,18 +538,29 @@ int fp8_quantize_delayed(const void *x, int32_t dtype, int64_t n, int32_t fmt, f
                 return fail(FP8Q_EINVAL, "%s: x or q overlaps the scaling state or a scalar output", fn);
     }
     fp8q::GridScratch *gs = nullptr;
-    hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
-    if (e != hipSuccess) return hip_status(e, fn);
+    const int st = c.scratch(&gs);
+    if (st) return st;
     return hip_status(fp8q::launch_delayed_step(x, dtype, n, fmt, hist, history_len, n_cols, col, step, fmt_next, margin,
                                                 algo, scale, scale_inv, q, q_scale_inv_out, amax_out, gs,
                                                 (hipStream_t)stream),
                       fn);
 }
 
-int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t row_fmt, int32_t col_fmt,
-                        int32_t col_source, const float *amax_in, int32_t row_margin, int32_t col_margin,
-                        const float *row_scale_inv_in, const float *col_scale_inv_in, uint8_t *q_row, uint8_t *q_col,
-                        float *row_scale_inv_out, float *col_scale_inv_out, float *amax_out, void *stream)
+extern "C" int fp8_quantize_delayed(const void *x, int32_t dtype, int64_t n, int32_t fmt, float *hist,
+                                    int32_t history_len, int32_t n_cols, int32_t col, int64_t step, int32_t fmt_next,
+                                    int32_t margin, int32_t algo, float *scale, float *scale_inv, uint8_t *q,
+                                    float *q_scale_inv_out, float *amax_out, void *stream)
+{
+    Call c("fp8_quantize_delayed", stream);
+    c.args("dtype=%lld n=%lld fmt=%lld history_len=%lld n_cols=%lld col=%lld step=%lld fmt_next=%lld margin=%lld algo=%lld", (long long)dtype, (long long)n, (long long)fmt, (long long)history_len, (long long)n_cols, (long long)col, (long long)step, (long long)fmt_next, (long long)margin, (long long)algo);
+    return c.ret(fp8_quantize_delayed_impl(c, x, dtype, n, fmt, hist, history_len, n_cols, col, step, fmt_next, margin, algo, scale, scale_inv, q, q_scale_inv_out, amax_out, stream));
+}
+
+static int fp8_quantize_hybrid_impl(Call &c, const void *x, int32_t dtype, int64_t rows, int64_t cols,
+                                    int32_t row_fmt, int32_t col_fmt, int32_t col_source, const float *amax_in,
+                                    int32_t row_margin, int32_t col_margin, const float *row_scale_inv_in,
+                                    const float *col_scale_inv_in, uint8_t *q_row, uint8_t *q_col,
+                                    float *row_scale_inv_out, float *col_scale_inv_out, float *amax_out, void *stream)
 {
     const char *fn = "fp8_quantize_hybrid";
     if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
@@ -399,8 +605,8 @@ int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, int64_t cols
     }
     fp8q::GridScratch *gs = nullptr;
     if (amax_out) {
-        hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
-        if (e != hipSuccess) return hip_status(e, fn);
+        const int st = c.scratch(&gs);
+        if (st) return st;
     }
     const fp8q::ScaleSrc src{amax_in, row_scale_inv_in, (int)row_margin};
     const fp8q::ScaleSrc src_col{amax_in, col_scale_inv_in, (int)col_margin};
@@ -410,8 +616,19 @@ int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, int64_t cols
                       fn);
 }
 
-int fp8_cast_stats(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *scale_inv, uint64_t *stats,
-                   void *stream)
+extern "C" int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t row_fmt,
+                                   int32_t col_fmt, int32_t col_source, const float *amax_in, int32_t row_margin,
+                                   int32_t col_margin, const float *row_scale_inv_in, const float *col_scale_inv_in,
+                                   uint8_t *q_row, uint8_t *q_col, float *row_scale_inv_out, float *col_scale_inv_out,
+                                   float *amax_out, void *stream)
+{
+    Call c("fp8_quantize_hybrid", stream);
+    c.args("dtype=%lld rows=%lld cols=%lld row_fmt=%lld col_fmt=%lld col_source=%lld row_margin=%lld col_margin=%lld", (long long)dtype, (long long)rows, (long long)cols, (long long)row_fmt, (long long)col_fmt, (long long)col_source, (long long)row_margin, (long long)col_margin);
+    return c.ret(fp8_quantize_hybrid_impl(c, x, dtype, rows, cols, row_fmt, col_fmt, col_source, amax_in, row_margin, col_margin, row_scale_inv_in, col_scale_inv_in, q_row, q_col, row_scale_inv_out, col_scale_inv_out, amax_out, stream));
+}
+
+static int fp8_cast_stats_impl(Call &c, const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *scale_inv,
+                               uint64_t *stats, void *stream)
 {
     const char *fn = "fp8_cast_stats";
     if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
@@ -425,13 +642,22 @@ int fp8_cast_stats(const void *x, int32_t dtype, int64_t n, int32_t fmt, const f
         if (overlap(x, n * dsize(dtype), stats, 32)) return fail(FP8Q_EINVAL, "%s: stats overlaps x", fn);
     }
     fp8q::GridScratch *gs = nullptr;
-    hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
-    if (e != hipSuccess) return hip_status(e, fn);
+    const int st = c.scratch(&gs);
+    if (st) return st;
     return hip_status(fp8q::launch_cast_stats(x, dtype, n, fmt, scale_inv, stats, gs, (hipStream_t)stream), fn);
 }
 
-int fp8_quantize_error_feedback(const void *g, int32_t dtype, float *residual, int64_t n, int32_t fmt,
-                                const float *scale_inv, uint8_t *q, float *amax_out, void *stream)
+extern "C" int fp8_cast_stats(const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *scale_inv,
+                              uint64_t *stats, void *stream)
+{
+    Call c("fp8_cast_stats", stream);
+    c.args("dtype=%lld n=%lld fmt=%lld", (long long)dtype, (long long)n, (long long)fmt);
+    return c.ret(fp8_cast_stats_impl(c, x, dtype, n, fmt, scale_inv, stats, stream));
+}
+
+static int fp8_quantize_error_feedback_impl(Call &c, const void *g, int32_t dtype, float *residual, int64_t n,
+                                            int32_t fmt, const float *scale_inv, uint8_t *q, float *amax_out,
+                                            void *stream)
 {
     const char *fn = "fp8_quantize_error_feedback";
     if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
@@ -454,20 +680,26 @@ int fp8_quantize_error_feedback(const void *g, int32_t dtype, float *residual, i
     }
     fp8q::GridScratch *gs = nullptr;
     if (amax_out) {
-        hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
-        if (e != hipSuccess) return hip_status(e, fn);
+        const int st = c.scratch(&gs);
+        if (st) return st;
     }
     return hip_status(
         fp8q::launch_error_feedback(g, dtype, residual, n, fmt, scale_inv, q, amax_out, gs, (hipStream_t)stream), fn);
 }
 
-} // extern "C"
+extern "C" int fp8_quantize_error_feedback(const void *g, int32_t dtype, float *residual, int64_t n, int32_t fmt,
+                                           const float *scale_inv, uint8_t *q, float *amax_out, void *stream)
+{
+    Call c("fp8_quantize_error_feedback", stream);
+    c.args("dtype=%lld n=%lld fmt=%lld", (long long)dtype, (long long)n, (long long)fmt);
+    return c.ret(fp8_quantize_error_feedback_impl(c, g, dtype, residual, n, fmt, scale_inv, q, amax_out, stream));
+}
 
 // Shared body of the two GEMM entry points.  c_type: FP8Q_F32, FP8Q_BF16,
 // FP8Q_OUT_E4M3FN or FP8Q_OUT_E5M2 (the last two only from the fused call).
-static int scaled_gemm(const char *fn, const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb,
-                       const float *sB, int64_t M, int64_t N, int64_t K, int32_t mode, const float *bias, int32_t act,
-                       void *C, int32_t c_type, const float *c_scale_inv, float *amax_out, void *stream)
+static int scaled_gemm(Call &c, const char *fn, const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B,
+                       int32_t fb, const float *sB, int64_t M, int64_t N, int64_t K, int32_t mode, const float *bias,
+                       int32_t act, void *C, int32_t c_type, const float *c_scale_inv, float *amax_out, void *stream)
 {
     if (!valid_fmt(fa) || !valid_fmt(fb)) return fail(FP8Q_EINVAL, "%s: unknown operand format", fn);
     if (mode != FP8Q_PER_TENSOR && mode != FP8Q_BLOCK_1x128_128x128 && mode != FP8Q_BLOCK_1x128_1x128 &&
@@ -508,11 +740,8 @@ static int scaled_gemm(const char *fn, const uint8_t *A, int32_t fa, const float
         return fail(FP8Q_EINVAL, "%s: amax_out overlaps an input", fn);
     fp8q::GridScratch *gs = nullptr;
     if (amax_out) {
-        if ((M / 128) * (N / 128) > fp8q::kMaxPartials)
-            return fail(FP8Q_EUNSUPPORTED, "%s: amax_out needs at most %d output tiles of 128x128", fn,
-                        fp8q::kMaxPartials);
-        hipError_t e = fp8q::get_grid_scratch((hipStream_t)stream, &gs);
-        if (e != hipSuccess) return hip_status(e, fn);
+        const int st = c.scratch(&gs);
+        if (st) return st;
     }
     // kernel output kinds: 0 bf16, 1 fp32, 2 E4M3FN codes, 3 E5M2 codes
     const int out_kind = c_type == FP8Q_BF16 ? 0 : c_type == FP8Q_F32 ? 1 : c_type == FP8Q_OUT_E4M3FN ? 2 : 3;
@@ -521,27 +750,43 @@ static int scaled_gemm(const char *fn, const uint8_t *A, int32_t fa, const float
                       fn);
 }
 
-extern "C" {
-
-int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb, const float *sB,
-                    int64_t M, int64_t N, int64_t K, int32_t mode, void *C, int32_t c_dtype, float *amax_out,
-                    void *stream)
+static int fp8_scaled_gemm_impl(Call &c, const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb,
+                                const float *sB, int64_t M, int64_t N, int64_t K, int32_t mode, void *C,
+                                int32_t c_dtype, float *amax_out, void *stream)
 {
     const char *fn = "fp8_scaled_gemm";
     if (!valid_dtype(c_dtype)) return fail(FP8Q_EINVAL, "%s: unknown output dtype %d", fn, (int)c_dtype);
-    return scaled_gemm(fn, A, fa, sA, B, fb, sB, M, N, K, mode, nullptr, FP8Q_ACT_NONE, C, c_dtype, nullptr, amax_out,
+    return scaled_gemm(c, fn, A, fa, sA, B, fb, sB, M, N, K, mode, nullptr, FP8Q_ACT_NONE, C, c_dtype, nullptr, amax_out,
                        stream);
 }
 
-int fp8_scaled_gemm_fused(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb,
-                          const float *sB, int64_t M, int64_t N, int64_t K, int32_t mode, const float *bias,
-                          int32_t act, void *C, int32_t c_type, const float *c_scale_inv, float *amax_out,
-                          void *stream)
+extern "C" int fp8_scaled_gemm(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb,
+                               const float *sB, int64_t M, int64_t N, int64_t K, int32_t mode, void *C,
+                               int32_t c_dtype, float *amax_out, void *stream)
+{
+    Call c("fp8_scaled_gemm", stream);
+    c.args("fa=%lld fb=%lld M=%lld N=%lld K=%lld mode=%lld c_dtype=%lld", (long long)fa, (long long)fb, (long long)M, (long long)N, (long long)K, (long long)mode, (long long)c_dtype);
+    return c.ret(fp8_scaled_gemm_impl(c, A, fa, sA, B, fb, sB, M, N, K, mode, C, c_dtype, amax_out, stream));
+}
+
+static int fp8_scaled_gemm_fused_impl(Call &c, const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B,
+                                      int32_t fb, const float *sB, int64_t M, int64_t N, int64_t K, int32_t mode,
+                                      const float *bias, int32_t act, void *C, int32_t c_type,
+                                      const float *c_scale_inv, float *amax_out, void *stream)
 {
     const char *fn = "fp8_scaled_gemm_fused";
     if (!valid_dtype(c_type) && c_type != FP8Q_OUT_E4M3FN && c_type != FP8Q_OUT_E5M2)
         return fail(FP8Q_EINVAL, "%s: unknown output type %d", fn, (int)c_type);
-    return scaled_gemm(fn, A, fa, sA, B, fb, sB, M, N, K, mode, bias, act, C, c_type, c_scale_inv, amax_out, stream);
+    return scaled_gemm(c, fn, A, fa, sA, B, fb, sB, M, N, K, mode, bias, act, C, c_type, c_scale_inv, amax_out, stream);
 }
 
-} // extern "C"
+extern "C" int fp8_scaled_gemm_fused(const uint8_t *A, int32_t fa, const float *sA, const uint8_t *B, int32_t fb,
+                                     const float *sB, int64_t M, int64_t N, int64_t K, int32_t mode,
+                                     const float *bias, int32_t act, void *C, int32_t c_type,
+                                     const float *c_scale_inv, float *amax_out, void *stream)
+{
+    Call c("fp8_scaled_gemm_fused", stream);
+    c.args("fa=%lld fb=%lld M=%lld N=%lld K=%lld mode=%lld act=%lld c_type=%lld", (long long)fa, (long long)fb, (long long)M, (long long)N, (long long)K, (long long)mode, (long long)act, (long long)c_type);
+    return c.ret(fp8_scaled_gemm_fused_impl(c, A, fa, sA, B, fb, sB, M, N, K, mode, bias, act, C, c_type, c_scale_inv, amax_out, stream));
+}
+

@@ -8,21 +8,32 @@
 
 namespace fp8q {
 
-// Grid-wide reduction scratch: a kernel that reduces an amax writes one
-// partial (the canonical magnitude max of its block) per block; a one-block
-// finish kernel folds them into the output.  No atomics and no state carried
-// between launches.  One per (device, stream); see get_grid_scratch.
-// The cast statistics keep four per-block counts the same way.
-constexpr int kMaxPartials = 65536;
+// Grid-wide reduction scratch.  A kernel that reduces an amax folds each
+// block's magnitude max into part[block % kParts] with an unsigned atomic max
+// (the canonical magnitude bits of non-negative values order like the values,
+// and the canonical NaN sorts above +inf); the cast statistics add each
+// block's four counts into cnt[k][block % kCntParts].  One small kernel then
+// reads every slot, writes the result and puts the slot back to zero, so a
+// scratch is all zeros between calls (it starts zeroed, as a device global).
+// The grid size is not limited by the scratch.
+constexpr int kParts = 256;
+constexpr int kCntParts = 64;
 constexpr int kStats = 4; // overflows, underflows, NaNs, nonzeros
 struct GridScratch {
-    uint32_t part[kMaxPartials];
-    uint32_t cnt[kStats][kMaxPartials];
+    uint32_t part[kParts];
+    unsigned long long cnt[kStats][kCntParts];
 };
+static_assert(sizeof(GridScratch) == 3072, "one scratch slot is 3 KiB");
 
-// The scratch of the calling thread's current device and stream `s`,
-// allocated the first time that pair is seen.
-hipError_t get_grid_scratch(hipStream_t s, GridScratch **out);
+// Flat launches keep at most this many blocks (larger inputs are covered by
+// grid-stride loops).
+constexpr int kMaxGrid = 65536;
+
+// Scratch slots per device: one per stream that has run a reducing call.
+constexpr int kScratchSlots = 64;
+
+// Enqueue the zeroing of one scratch slot (after a failed call left it dirty).
+hipError_t launch_clear_scratch(GridScratch *gs, hipStream_t s);
 
 // Where a per-tensor scale comes from: exactly one pointer is non-null.
 struct ScaleSrc {
@@ -33,7 +44,7 @@ struct ScaleSrc {
 
 hipError_t launch_fill_u32(uint32_t *p, uint32_t v, hipStream_t s);
 
-hipError_t launch_finish_amax(const GridScratch *gs, int nparts, float *out, hipStream_t s);
+hipError_t launch_finish_amax(GridScratch *gs, float *out, hipStream_t s);
 
 hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScratch *gs, hipStream_t s);
 

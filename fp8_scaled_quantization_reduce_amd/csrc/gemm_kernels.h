@@ -306,7 +306,8 @@ __device__ __forceinline__ v8i read_frag32_mx(const uint8_t *lds, int r, int g, 
 // kBN = 256: a 256x256 tile per block (grid block b -> grouped tile
 // xcd_order(b, n_main)); kBN = 128: half a tile, wave tiles 128x64 (grid
 // block b -> half b & 1 of grouped tile tile_base + b / 2), for a last wave of
-// tiles that is at most half full.  Each block's amax partial goes to part[b].
+// tiles that is at most half full.  Each block's amax partial is folded into
+// part[b % kParts] (an atomic max; the finish kernel reads and clears it).
 template <int FA, int FB, bool kAmax, int kOut, bool kFuse, bool kMX, int kBN>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t *__restrict__ A,
                                                                   const uint8_t *__restrict__ B,
@@ -520,7 +521,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     }
     if constexpr (kAmax) {
         m = block_max_u32<kGemmThreads>(m, red);
-        if (tid == 0) part[blockIdx.x] = canonical_amax_bits(m);
+        if (tid == 0) atomicMax(&part[blockIdx.x % kParts], canonical_amax_bits(m));
     }
 }
 
@@ -541,7 +542,8 @@ constexpr int kBSStageBytes = 2 * kBM * kBK;
 // xcd_order(b, n_main).  kBN = 128: half a tile (the wave tiles are 64x64),
 // grid block b -> the half b & 1 of grouped tile tile_base + b / 2; the
 // launcher uses it for a last, partly empty wave of tiles, which then runs as
-// a full wave of half tiles.  Each block's amax partial goes to part[b].
+// a full wave of half tiles.  Each block's amax partial is folded into
+// part[b % kParts].
 template <int FA, int FB, bool kAmax, int kOut, bool kFuse, bool kRowB, int kBN>
 __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *__restrict__ A,
                                                                 const uint8_t *__restrict__ B,
@@ -757,7 +759,7 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
     }
     if constexpr (kAmax) {
         m = block_max_u32<kBSThreads>(m, red);
-        if (tid == 0) part[blockIdx.x] = canonical_amax_bits(m);
+        if (tid == 0) atomicMax(&part[blockIdx.x % kParts], canonical_amax_bits(m));
     }
 }
 
@@ -774,8 +776,7 @@ hipError_t launch_gemm_epi(const GemmArgs &a)
     const int n_main = (r > 0 && 2 * r <= a.cus) ? tiles - r : tiles;
     const int n_half = 2 * (tiles - n_main);
     uint32_t *part = a.gs ? a.gs->part : nullptr;
-    uint32_t *part_half = part ? part + n_main : nullptr;
-    const int parts = n_main + n_half;
+    uint32_t *part_half = part;
     if (a.mode == 0 || a.mode == 3) {
 #define FP8Q_PT_LAUNCH(FLAG, BN, GRID, PART, BASE)                                                                  \
         do {                                                                                                        \
@@ -815,7 +816,7 @@ hipError_t launch_gemm_epi(const GemmArgs &a)
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.amax_out) return e;
-    return launch_finish_amax(a.gs, parts, a.amax_out, a.stream);
+    return launch_finish_amax(a.gs, a.amax_out, a.stream);
 }
 
 // Every output kind and epilogue of one operand-format pair.  The plain

@@ -23,13 +23,13 @@ __host__ __device__ static inline int64_t ceil_div(int64_t a, int64_t b) { retur
 
 // Flat streaming launches: the work is cut into units of kThreads * U
 // vectors; block b takes units b, b + G, b + 2G, ... of a grid of
-// G = min(units, kMaxPartials) blocks (one unit per block at the sizes of
+// G = min(units, kMaxGrid) blocks (one unit per block at the sizes of
 // interest, so each lane issues its U loads back to back and the grid covers
 // the chip many times over).
 static int flat_grid(int64_t units)
 {
     if (units < 1) return 1;
-    return (int)(units < kMaxPartials ? units : kMaxPartials);
+    return (int)(units < kMaxGrid ? units : kMaxGrid);
 }
 
 template <int F>
@@ -50,41 +50,43 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t v, hipStream_t s)
     return hipGetLastError();
 }
 
-// One block's magnitude max -> its partial (canonical amax bits).  Every lane
-// must reach it.
+// One block's magnitude max -> the atomic max of its partial slot (canonical
+// amax bits, so the slot's maximum is canonical too).  Every lane must reach
+// it.  The atomic returns nothing, so the block does not wait for it.
 __device__ __forceinline__ void block_partial(uint32_t m, GridScratch *gs)
 {
     __shared__ uint32_t red[kThreads / 64];
     m = block_max_u32<kThreads>(m, red);
-    if (threadIdx.x == 0) gs->part[blockIdx.x] = canonical_amax_bits(m);
+    if (threadIdx.x == 0) atomicMax(&gs->part[blockIdx.x % kParts], canonical_amax_bits(m));
 }
 
-// Fold nparts partials into the output word.  Each partial is canonical, so
-// their maximum is too.  1024 lanes with eight independent loads each cover
-// up to 8192 partials in one round trip.
-constexpr int kFinishThreads = 1024;
-constexpr int kFinishLoads = 8;
+// Read partial slot i and put it back to zero (one round trip).
+__device__ __forceinline__ uint32_t take_partial(GridScratch *gs, int i) { return atomicExch(&gs->part[i], 0u); }
 
-__global__ __launch_bounds__(kFinishThreads) void finish_amax_kernel(const GridScratch *__restrict__ gs, int nparts,
-                                                                     uint32_t *__restrict__ out)
+// Fold the kParts partial slots into the output word, leaving them zero.
+__global__ __launch_bounds__(kParts) void finish_amax_kernel(GridScratch *__restrict__ gs, uint32_t *__restrict__ out)
 {
-    __shared__ uint32_t red[kFinishThreads / 64];
-    uint32_t m = 0;
-    for (int i = threadIdx.x; i < nparts; i += kFinishLoads * kFinishThreads) {
-        uint32_t v[kFinishLoads];
-#pragma unroll
-        for (int u = 0; u < kFinishLoads; ++u)
-            v[u] = i + u * kFinishThreads < nparts ? gs->part[i + u * kFinishThreads] : 0u;
-#pragma unroll
-        for (int u = 0; u < kFinishLoads; ++u) m = max(m, v[u]);
-    }
-    m = block_max_u32<kFinishThreads>(m, red);
+    __shared__ uint32_t red[kParts / 64];
+    const uint32_t m = block_max_u32<kParts>(take_partial(gs, threadIdx.x), red);
     if (threadIdx.x == 0) *out = m;
 }
 
-hipError_t launch_finish_amax(const GridScratch *gs, int nparts, float *out, hipStream_t s)
+hipError_t launch_finish_amax(GridScratch *gs, float *out, hipStream_t s)
 {
-    finish_amax_kernel<<<1, kFinishThreads, 0, s>>>(gs, nparts, reinterpret_cast<uint32_t *>(out));
+    finish_amax_kernel<<<1, kParts, 0, s>>>(gs, reinterpret_cast<uint32_t *>(out));
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kParts) void clear_scratch_kernel(GridScratch *__restrict__ gs)
+{
+    gs->part[threadIdx.x] = 0u;
+    if (threadIdx.x < kStats * kCntParts) gs->cnt[threadIdx.x / kCntParts][threadIdx.x % kCntParts] = 0ull;
+}
+
+hipError_t launch_clear_scratch(GridScratch *gs, hipStream_t s)
+{
+    static_assert(kStats * kCntParts <= kParts, "one lane per slot");
+    clear_scratch_kernel<<<1, kParts, 0, s>>>(gs);
     return hipGetLastError();
 }
 
@@ -149,7 +151,7 @@ hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScr
         amax_kernel<kF32><<<grid, kThreads, 0, s>>>(x, n, gs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_finish_amax(gs, grid, amax, s);
+    return launch_finish_amax(gs, amax, s);
 }
 
 // ------------------------------------------------------------------ cast --
@@ -291,7 +293,7 @@ __device__ __forceinline__ void block_counts(const uint32_t g[kStats], GridScrat
         uint32_t t = 0;
 #pragma unroll
         for (int w = 0; w < kThreads / 64; ++w) t += red[threadIdx.x][w];
-        gs->cnt[threadIdx.x][blockIdx.x] = t;
+        if (t) atomicAdd(&gs->cnt[threadIdx.x][blockIdx.x % kCntParts], (unsigned long long)t);
     }
 }
 
@@ -390,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const void *__restrict__
     if constexpr (kCount) block_counts(g, gs);
 }
 
-static hipError_t launch_finish_stats(const GridScratch *gs, int nparts, uint64_t *stats, hipStream_t s);
+static hipError_t launch_finish_stats(GridScratch *gs, uint64_t *stats, hipStream_t s);
 
 template <int F, int DT>
 static hipError_t launch_cast_t(const void *x, int64_t n, ScaleSrc src, uint8_t *q, float *scale_inv_out,
@@ -408,8 +410,8 @@ static hipError_t launch_cast_t(const void *x, int64_t n, ScaleSrc src, uint8_t 
         cast_kernel<F, DT, false><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, nullptr);
     }
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && amax_out) e = launch_finish_amax(gs, grid, amax_out, s);
-    if (e == hipSuccess && stats) e = launch_finish_stats(gs, grid, stats, s);
+    if (e == hipSuccess && amax_out) e = launch_finish_amax(gs, amax_out, s);
+    if (e == hipSuccess && stats) e = launch_finish_stats(gs, stats, s);
     return e;
 }
 
@@ -525,29 +527,16 @@ __global__ __launch_bounds__(kThreads) void cast_stats_kernel(const void *__rest
     block_counts(g, gs);
 }
 
-constexpr int kStatsFinishThreads = 1024;
-
-__global__ __launch_bounds__(kStatsFinishThreads) void finish_stats_kernel(const GridScratch *__restrict__ gs,
-                                                                           int nparts, uint64_t *__restrict__ out)
+// One wave per statistic: lane i takes count slot i (and zeroes it), the
+// wave sums them into the 64-bit total.
+__global__ __launch_bounds__(kStats * kCntParts) void finish_stats_kernel(GridScratch *__restrict__ gs,
+                                                                          uint64_t *__restrict__ out)
 {
-    __shared__ uint64_t red[kStats][kStatsFinishThreads / 64];
-    uint64_t t[kStats] = {0, 0, 0, 0};
-    for (int i = threadIdx.x; i < nparts; i += kStatsFinishThreads) {
-#pragma unroll
-        for (int k = 0; k < kStats; ++k) t[k] += gs->cnt[k][i];
-    }
-#pragma unroll
-    for (int k = 0; k < kStats; ++k) {
-        uint64_t v = t[k];
-        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-        if ((threadIdx.x & 63) == 0) red[k][threadIdx.x >> 6] = v;
-    }
-    __syncthreads();
-    if (threadIdx.x < kStats) {
-        uint64_t v = 0;
-        for (int w = 0; w < kStatsFinishThreads / 64; ++w) v += red[threadIdx.x][w];
-        out[threadIdx.x] = v;
-    }
+    static_assert(kCntParts == 64, "one wave per statistic");
+    const int k = threadIdx.x >> 6;
+    uint64_t v = atomicExch(&gs->cnt[k][threadIdx.x & 63], 0ull);
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0) out[k] = v;
 }
 
 hipError_t launch_cast_stats(const void *x, int dtype, int64_t n, int fmt, const float *scale_inv, uint64_t *stats,
@@ -563,12 +552,12 @@ hipError_t launch_cast_stats(const void *x, int dtype, int64_t n, int fmt, const
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_finish_stats(gs, grid, stats, s);
+    return launch_finish_stats(gs, stats, s);
 }
 
-static hipError_t launch_finish_stats(const GridScratch *gs, int nparts, uint64_t *stats, hipStream_t s)
+static hipError_t launch_finish_stats(GridScratch *gs, uint64_t *stats, hipStream_t s)
 {
-    finish_stats_kernel<<<1, kStatsFinishThreads, 0, s>>>(gs, nparts, stats);
+    finish_stats_kernel<<<1, kStats * kCntParts, 0, s>>>(gs, stats);
     return hipGetLastError();
 }
 
@@ -669,7 +658,7 @@ hipError_t launch_error_feedback(const void *g, int dtype, float *residual, int6
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !am) return e;
-    return launch_finish_amax(gs, grid, amax_out, s);
+    return launch_finish_amax(gs, amax_out, s);
 }
 
 // --------------------------------------------------------------- delayed --
@@ -678,9 +667,9 @@ hipError_t launch_error_feedback(const void *g, int dtype, float *residual, int6
 // the value just written, derive s = eff / FP8_MAX * 2^margin (1 when eff is
 // not > 0) and its reciprocal.  One block; L may be any length.  The new amax
 // is either read from memory or, for the fused step, reduced here from the
-// cast kernel's per-block partials (and published to amax_out).
-constexpr int kDelayedThreads = 1024;
-constexpr int kDelayedLoads = 8; // partial loads in flight per lane
+// cast kernel's partial slots (which it leaves zero) and published to
+// amax_out.
+constexpr int kDelayedThreads = kParts; // one partial slot per lane
 
 // Order-preserving key of a float for an unsigned max (negative values flip
 // all bits, positive values set the sign bit); every NaN maps above +inf, so
@@ -694,7 +683,7 @@ __device__ __forceinline__ uint32_t order_key(float h)
 
 __global__ __launch_bounds__(kDelayedThreads) void delayed_kernel(float *__restrict__ hist, int L, int n_cols, int col,
                                                                   const float *__restrict__ new_amax,
-                                                                  const GridScratch *__restrict__ gs, int nparts,
+                                                                  GridScratch *__restrict__ gs,
                                                                   float *__restrict__ amax_out, int slot, float fmax,
                                                                   int margin, int algo, float *__restrict__ scale,
                                                                   float *__restrict__ scale_inv)
@@ -706,23 +695,13 @@ __global__ __launch_bounds__(kDelayedThreads) void delayed_kernel(float *__restr
     // both round trips overlap.
     const bool h0_valid = tid < L && tid != slot;
     const float h0 = h0_valid ? hist[(int64_t)tid * n_cols + col] : 0.0f;
-    uint32_t m = 0;
-    if (gs) {
-        for (int i = tid; i < nparts; i += kDelayedLoads * kDelayedThreads) {
-            uint32_t v[kDelayedLoads];
-#pragma unroll
-            for (int u = 0; u < kDelayedLoads; ++u)
-                v[u] = i + u * kDelayedThreads < nparts ? gs->part[i + u * kDelayedThreads] : 0u;
-#pragma unroll
-            for (int u = 0; u < kDelayedLoads; ++u) m = max(m, v[u]);
-        }
-    }
+    const uint32_t m0 = gs ? take_partial(gs, tid) : 0u;
     // largest entry of the column other than the slot being overwritten
     uint32_t key = h0_valid ? order_key(h0) : 0u;
     for (int j = tid + kDelayedThreads; j < L; j += kDelayedThreads)
         if (j != slot) key = max(key, order_key(hist[(int64_t)j * n_cols + col]));
     // one exchange for both maxima
-    m = wave_max_u32(m);
+    uint32_t m = wave_max_u32(m0);
     key = wave_max_u32(key);
     if ((tid & 63) == 0) {
         red_a[tid >> 6] = m;
@@ -757,15 +736,15 @@ hipError_t launch_delayed(float *hist, int history_len, int n_cols, int col, con
                           int fmt, int margin, int algo, float *scale, float *scale_inv, hipStream_t s)
 {
     const int slot = (int)(step % history_len);
-    delayed_kernel<<<1, kDelayedThreads, 0, s>>>(hist, history_len, n_cols, col, new_amax, nullptr, 0, nullptr, slot,
+    delayed_kernel<<<1, kDelayedThreads, 0, s>>>(hist, history_len, n_cols, col, new_amax, nullptr, nullptr, slot,
                                                  fmax_of(fmt), margin, algo, scale, scale_inv);
     return hipGetLastError();
 }
 
 // One delayed-scaling step: cast x with the stored scale of column col
 // (scale_inv[col]), reducing the input's amax into per-block partials, then one
-// block folds the partials, publishes the amax and updates the ring and the
-// column's scales for the format of the next step.
+// block folds the partial slots, publishes the amax and updates the ring and
+// the column's scales for the format of the next step.
 hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, float *hist, int history_len, int n_cols,
                                int col, int64_t step, int fmt_next, int margin, int algo, float *scale,
                                float *scale_inv, uint8_t *q, float *q_scale_inv_out, float *amax_out, GridScratch *gs,
@@ -787,7 +766,7 @@ hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, flo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int slot = (int)(step % history_len);
-    delayed_kernel<<<1, kDelayedThreads, 0, s>>>(hist, history_len, n_cols, col, nullptr, gs, grid, amax_out, slot,
+    delayed_kernel<<<1, kDelayedThreads, 0, s>>>(hist, history_len, n_cols, col, nullptr, gs, amax_out, slot,
                                                  fmax_of(fmt_next), margin, algo, scale, scale_inv);
     return hipGetLastError();
 }
@@ -1376,7 +1355,7 @@ static hipError_t launch_rc_t(const void *x, int64_t rows, int64_t cols, ScaleSr
                                                                            ScaleSrc{}, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !amax_out) return e;
-    return launch_finish_amax(gs, grid, amax_out, s);
+    return launch_finish_amax(gs, amax_out, s);
 }
 
 hipError_t launch_rowwise_colwise(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, ScaleSrc src,
@@ -1414,7 +1393,7 @@ static hipError_t launch_hybrid_m(const void *x, int64_t rows, int64_t cols, Sca
                                                                   col_scale_inv_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !amax_out) return e;
-    return launch_finish_amax(gs, grid, amax_out, s);
+    return launch_finish_amax(gs, amax_out, s);
 }
 
 template <int F, int DT>

@@ -11,12 +11,23 @@
  *  - All pointers are DEVICE memory owned by the caller, unless stated.  The
  *    library never copies device->host and never synchronises: each call
  *    enqueues its kernels on `stream` (a hipStream_t; NULL = the default
- *    stream) and returns.  The only device memory it allocates is a 1.25 MiB
- *    reduction scratch (per-block partial maxima and counts) per (device, stream) pair,
- *    on the first call on that pair that reduces an amax, held until the
- *    process ends.  Calls on one stream use that scratch in stream order; two
- *    host threads that enqueue on the same stream handle concurrently must
- *    serialise their calls.
+ *    stream) and returns.
+ *  - The library never allocates device memory.  Calls that reduce over the
+ *    whole grid (an amax, the cast statistics) keep per-block partials in a
+ *    reduction scratch that is a device global of the library: 64 slots of
+ *    3 KiB on each device, created with the library's code object on that
+ *    device and held until the process ends.  Each stream gets a slot of its
+ *    own the first time it runs such a call (a host-side table; no device
+ *    work), so calls on different streams never share partials.  The slot is
+ *    all zeros between calls: the call's last kernel reads it and clears it.
+ *    While one call enqueues its kernels it holds a host lock on its slot, so
+ *    host threads that share a stream are safe.  A device on which more than
+ *    64 streams have run reducing calls returns FP8Q_EUNSUPPORTED.
+ *  - FP8Q_DEBUG set in the environment (to anything but "" or "0") makes every
+ *    call print one line to stderr: the entry point, its integer arguments,
+ *    the stream, the scratch slot and the returned status and message.  The
+ *    line is printed after the kernels are enqueued and never waits for the
+ *    device.
  *  - Enum-valued arguments are passed as int32_t (values below).
  *  - Tensors are dense and row-major.  FP8 tensors are arrays of 8-bit codes
  *    (uint8_t).  bf16 tensors are arrays of 16-bit bf16 patterns.
@@ -25,7 +36,8 @@
  *  - Errors: arguments are validated on the host before any HIP call.  A
  *    non-zero status is returned and a message is kept for
  *    fp8q_last_error() (thread-local).  Nothing is written on error.  A
- *    launch failure reported by the runtime returns FP8Q_EHIP.
+ *    launch failure reported by the runtime returns FP8Q_EHIP, as does a
+ *    valid call made where no device is usable (the message says why).
  *  - Numerics: scales, amaxes and the scaled values are binary32 with
  *    round-to-nearest-even.  The FP8 cast saturates to +-FP8_MAX and rounds to
  *    nearest, ties to even.  NaN is kept: a NaN product x*scale becomes code

@@ -247,3 +247,89 @@ def test_last_error_is_thread_local_string():
     L.fp8_amax(BAD, 9, 16, BAD, S)
     msg = fq.last_error()
     assert isinstance(msg, str) and msg.startswith("fp8_amax")
+
+
+# --------------------------------------------------------- lifecycle ------
+# The library allocates no device memory: its reduction scratch is one device
+# global of fixed size (64 slots of 3 KiB per device), whose address on the
+# current device comes from hipGetSymbolAddress.  Both facts are visible in the
+# built library without a GPU.
+ALLOCATORS = ("hipMalloc", "hipFree", "hipHostMalloc", "hipHostFree", "hipExtMallocWithFlags", "hipMallocAsync",
+              "hipFreeAsync", "hipMallocManaged", "hipMallocPitch", "hipMalloc3D", "hipMallocArray",
+              "hipMemPoolCreate", "hipMemCreate", "hipMemAddressReserve")
+SCRATCH_SLOTS, SLOT_BYTES = 64, 3072
+
+
+def _nm(*flags):
+    import subprocess
+    out = subprocess.run(["nm", *flags, fq.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    return out.splitlines()
+
+
+def test_library_never_allocates_device_memory():
+    imported = {line.split()[-1].split("@")[0] for line in _nm("-D", "--undefined-only") if line.strip()}
+    hip = sorted(s for s in imported if s.startswith("hip"))
+    assert hip, "the library should import the HIP runtime"
+    bad = [s for s in hip if s.startswith(ALLOCATORS)]
+    assert not bad, bad
+    assert "hipGetSymbolAddress" in imported
+
+
+def test_reduction_scratch_is_a_fixed_device_global():
+    rows = [line.split() for line in _nm("-S", "--defined-only")]
+    sizes = [int(r[1], 16) for r in rows if len(r) == 4 and r[3] in ("scratch", "_ZL7scratch")]
+    assert sizes == [SCRATCH_SLOTS * SLOT_BYTES], sizes
+
+
+def test_header_states_the_scratch_lifecycle():
+    text = " ".join(" ".join(re.sub(r"^\s*\*\s?", "", ln) for ln in open(HEADER).read().splitlines()).split())
+    assert "never allocates device memory" in text
+    assert "%d slots of %d KiB" % (SCRATCH_SLOTS, SLOT_BYTES // 1024) in text
+    assert "more than %d streams" % SCRATCH_SLOTS in text
+
+
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the error path of a machine without a GPU")
+def test_valid_calls_without_a_device_return_ehip():
+    """Valid arguments (fake, never dereferenced device addresses) where no
+    device is usable: the call reports the runtime's error instead of
+    crashing or silently doing nothing."""
+    calls = [
+        ("fp8_amax", lambda: L.fp8_amax(BAD, fq.BF16, 64, BAD + 0x1000, S)),
+        ("fp8_quantize_tensor", lambda: L.fp8_quantize_tensor(BAD, fq.BF16, 64, 0, BAD + 0x800, 0, None,
+                                                              BAD + 0x10000, None, None, None, S)),
+        ("fp8_dequantize", lambda: L.fp8_dequantize(BAD, 0, 64, BAD + 0x800, BAD + 0x1000, S)),
+        ("fp8_quantize_block", lambda: L.fp8_quantize_block(BAD, fq.BF16, 128, 128, 0, 128, BAD + 0x100000,
+                                                            BAD + 0x200000, None, None, S)),
+        ("fp8_update_scale_delayed", lambda: L.fp8_update_scale_delayed(BAD, 16, 1, 0, BAD + 0x100, 0, 0, 0, 0,
+                                                                        BAD + 0x200, BAD + 0x300, S)),
+        ("fp8_scaled_gemm", lambda: L.fp8_scaled_gemm(BAD + 0x100000, 0, BAD, BAD + 0x200000, 0, BAD + 4, 128, 128,
+                                                      128, 0, BAD + 0x300000, fq.BF16, None, S)),
+    ]
+    for name, call in calls:
+        status = call()
+        msg = fq.last_error()
+        assert status == fq.EHIP, (name, status, msg)
+        assert msg.startswith(name + ":") and len(msg) > len(name) + 3, msg
+
+
+def test_debug_log_lines():
+    """FP8Q_DEBUG prints one stderr line per call with the entry point, its
+    integer arguments and the status; without it nothing is printed."""
+    import subprocess
+    import sys
+    code = ("import fp8_scaled_quantization_reduce_amd as fq\n"
+            "fq.lib.fp8_amax(0x1000, 9, 16, 0x1000, None)\n"
+            "fq.lib.fp8_dequantize(0x1000, 0, 64, 0x2000, 0x3000, None)\n")
+    env = dict(os.environ, PYTHONPATH=ROOT)
+    on = subprocess.run([sys.executable, "-c", code], env=dict(env, FP8Q_DEBUG="1"), capture_output=True, text=True)
+    lines = [x for x in on.stderr.splitlines() if x.startswith("fp8q: ")]
+    assert len(lines) == 2, on.stderr
+    assert lines[0].startswith("fp8q: fp8_amax(dtype=9 n=16)") and "-> 1 fp8_amax: unknown dtype 9" in lines[0]
+    assert lines[1].startswith("fp8q: fp8_dequantize(fmt=0 n=64)")
+    off = subprocess.run([sys.executable, "-c", code], env=dict(env, FP8Q_DEBUG="0"), capture_output=True, text=True)
+    assert "fp8q: " not in off.stderr

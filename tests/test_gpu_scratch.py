@@ -1,0 +1,138 @@
+"""The reduction scratch is left empty by every call, and calls from several
+host threads on one stream keep their partials apart.
+
+Each reducing entry point runs twice in a row on one stream, first on a large
+input with a large amax (or many counts), then on a smaller input with a
+smaller amax: the second result must equal the oracle's for the second input
+alone, which fails if partials of the first call were left in the slot.
+Expected values come from the oracle."""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import f32_bits, host, scalar, to_dev
+
+pytestmark = pytest.mark.gpu
+
+fq = pytest.importorskip("fp8_scaled_quantization_reduce_amd")
+E4, E5 = oracle.E4M3FN, oracle.E5M2
+
+
+def _pair(shape_big=(2048, 4096), shape_small=(384, 256), seed=0):
+    rng = np.random.default_rng(seed)
+    big = workloads.to_bf16_bits(rng.standard_normal(shape_big) * 100.0)
+    small = workloads.to_bf16_bits(rng.standard_normal(shape_small) * 0.5)
+    assert oracle.amax(small) < oracle.amax(big)
+    return big, small
+
+
+def test_amax_twice():
+    big, small = _pair()
+    for x in (big, small):
+        am = scalar(-1.0)
+        fq.fp8_amax(to_dev(x), am)
+        assert f32_bits(host(am)[0]) == f32_bits(oracle.amax(x))
+
+
+def test_cast_with_amax_and_stats_twice():
+    big, small = _pair(seed=1)
+    for x in (big, small):
+        xd = to_dev(x)
+        q = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+        am, st = scalar(-1.0), torch.full((4,), -1, dtype=torch.int64, device="cuda")
+        si = scalar(0.25)
+        fq.fp8_quantize_tensor_stats(xd, E4, q, st, scale_inv_in=si, amax_out=am)
+        assert np.array_equal(host(q), oracle.quantize(x, E4, oracle.reciprocal(np.float32(0.25))).ravel())
+        assert f32_bits(host(am)[0]) == f32_bits(oracle.amax(x))
+        assert np.array_equal(host(st), oracle.cast_stats(x, E4, np.float32(0.25)).astype(np.int64))
+        st2 = torch.full((4,), -1, dtype=torch.int64, device="cuda")
+        fq.fp8_cast_stats(xd, E5, si, st2)
+        assert np.array_equal(host(st2), oracle.cast_stats(x, E5, np.float32(0.25)).astype(np.int64))
+
+
+def test_rowwise_colwise_hybrid_and_error_feedback_twice():
+    big, small = _pair(seed=2)
+    for x in (big, small):
+        xd = to_dev(x)
+        rows, cols = x.shape
+        qr = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+        qc = torch.empty((cols, rows), dtype=torch.uint8, device="cuda")
+        am = scalar(-1.0)
+        fq.fp8_quantize_rowwise_colwise(xd, E4, q_row=qr, q_col=qc, scale_inv_in=scalar(2.0), amax_out=am)
+        assert f32_bits(host(am)[0]) == f32_bits(oracle.amax(x))
+        am2 = scalar(-1.0)
+        fq.fp8_quantize_hybrid(xd, E4, E5, fq.COLSRC_ORIGINAL, q_row=qr, q_col=qc, row_scale_inv_in=scalar(2.0),
+                               col_scale_inv_in=scalar(4.0), amax_out=am2)
+        assert f32_bits(host(am2)[0]) == f32_bits(oracle.amax(x))
+        res = torch.zeros(x.size, dtype=torch.float32, device="cuda")
+        q = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+        am3 = scalar(-1.0)
+        fq.fp8_quantize_error_feedback(xd, res, E4, scalar(1.0), q, amax_out=am3)
+        assert f32_bits(host(am3)[0]) == f32_bits(oracle.amax(x))
+
+
+def test_delayed_step_twice():
+    big, small = _pair(seed=3)
+    hist = torch.zeros((4, 1), dtype=torch.float32, device="cuda")
+    scale, scale_inv = scalar(1.0), scalar(1.0)
+    ref_hist = np.zeros((4, 1), np.float32)
+    for step, x in enumerate((big, small)):
+        q = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+        am = scalar(-1.0)
+        fq.fp8_quantize_delayed(to_dev(x), E4, hist, 0, step, E4, 0, fq.ALGO_MOST_RECENT, scale, scale_inv, q,
+                                amax_out=am)
+        ref_hist[step, 0] = oracle.amax(x)
+        assert f32_bits(host(am)[0]) == f32_bits(oracle.amax(x))
+        assert np.array_equal(f32_bits(host(hist)), f32_bits(ref_hist))
+
+
+def test_gemm_amax_twice():
+    rng = np.random.default_rng(4)
+    for M, N, K, std in ((1024, 1024, 256, 1.0), (256, 384, 128, 0.01)):
+        xa = workloads.to_bf16_bits(rng.standard_normal((M, K)) * std)
+        xb = workloads.to_bf16_bits(rng.standard_normal((N, K)))
+        ra = oracle.quantize_tensor(xa, E4, amax_in=oracle.amax(xa))
+        rb = oracle.quantize_tensor(xb, E4, amax_in=oracle.amax(xb))
+        C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        am = scalar(-1.0)
+        fq.fp8_scaled_gemm(to_dev(ra["q"]), E4, to_dev(np.float32([ra["scale_inv"]])), to_dev(rb["q"]), E4,
+                           to_dev(np.float32([rb["scale_inv"]])), fq.PER_TENSOR, C, am)
+        assert f32_bits(host(am)[0]) == f32_bits(np.max(np.abs(host(C))))
+
+
+def test_threads_sharing_one_stream():
+    """Four host threads enqueue amax and cast-with-amax calls on the same
+    stream at once; every call's result is its own input's amax."""
+    rng = np.random.default_rng(5)
+    inputs = [workloads.to_bf16_bits(rng.standard_normal(1 << 16) * (10.0 ** k)) for k in range(4)]
+    want = [oracle.amax(x) for x in inputs]
+    dev_in = [to_dev(x) for x in inputs]
+    calls = 64
+    outs = [torch.full((calls, 2), -1.0, dtype=torch.float32, device="cuda") for _ in inputs]
+    qs = [torch.empty(1 << 16, dtype=torch.uint8, device="cuda") for _ in inputs]
+    one = scalar(1.0)
+    stream = torch.cuda.current_stream()
+    errors = []
+
+    def work(t):
+        try:
+            for i in range(calls):
+                fq.fp8_amax(dev_in[t], outs[t][i, 0:1], stream=stream)
+                fq.fp8_quantize_tensor(dev_in[t], E4, qs[t], scale_inv_in=one, amax_out=outs[t][i, 1:2],
+                                       stream=stream)
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(len(inputs))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for t in range(len(inputs)):
+        got = f32_bits(host(outs[t]))
+        assert np.all(got == f32_bits(want[t])), (t, np.unique(got))
