@@ -125,11 +125,12 @@ def _ptr(t, name="tensor"):
     if t is None:
         return None
     _tensor(t, name)
-    if not t.is_cuda:
+    dev = t.get_device()  # -1 for host tensors
+    if dev < 0:
         raise ValueError("%s must be a GPU tensor (device %s)" % (name, t.device))
-    if t.device.index != torch.cuda.current_device():
-        raise ValueError("%s is on %s but the current device is cuda:%d" % (name, t.device,
-                                                                          torch.cuda.current_device()))
+    if dev != torch.cuda.current_device():
+        raise ValueError("%s is on cuda:%d but the current device is cuda:%d" % (name, dev,
+                                                                               torch.cuda.current_device()))
     return t.data_ptr()
 
 

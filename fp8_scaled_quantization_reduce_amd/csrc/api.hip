@@ -7,7 +7,7 @@
 // Reduction scratch.  Calls that reduce over a grid (an amax, the cast
 // statistics) fold per-block partials in a small scratch slot and finish with
 // a one-block kernel that reads the slot and leaves it zero.  The slots are
-// one device global, `scratch` below: kScratchSlots slots of 3 KiB on every
+// one device global, `scratch` below: kScratchSlots slots of 6 KiB on every
 // device the library runs on, held until the process ends.  The library never
 // allocates device memory.  Each stream that runs a reducing call gets a slot
 // of its own on first use (a host-side table, no device work), so calls on

@@ -8,26 +8,32 @@
 
 namespace fp8q {
 
-// Grid-wide reduction scratch.  A kernel that reduces an amax folds each
-// block's magnitude max into part[block % kParts] with an unsigned atomic max
-// (the canonical magnitude bits of non-negative values order like the values,
-// and the canonical NaN sorts above +inf); the cast statistics add each
-// block's four counts into cnt[k][block % kCntParts].  One small kernel then
-// reads every slot, writes the result and puts the slot back to zero, so a
-// scratch is all zeros between calls (it starts zeroed, as a device global).
-// The grid size is not limited by the scratch.
-constexpr int kParts = 256;
+// Grid-wide reduction scratch.  A flat or tile kernel that reduces an amax
+// runs at most kParts blocks (grid-stride loops cover larger inputs) and
+// block b stores its canonical magnitude max to part[b]; a GEMM block folds
+// its max into part[b % kParts] with an unsigned atomic max (the canonical
+// magnitude bits order like the values, and the canonical NaN sorts above
+// +inf).  The cast statistics add each block's four counts into
+// cnt[k][b % kCntParts].  One small kernel then reads the slots the call used,
+// writes the result and puts them back to zero, so a scratch is all zeros
+// between calls (it starts zeroed, as a device global).
+#ifndef FP8Q_REDUCE_GRID
+#define FP8Q_REDUCE_GRID 1024
+#endif
+constexpr int kParts = FP8Q_REDUCE_GRID;
 constexpr int kCntParts = 64;
 constexpr int kStats = 4; // overflows, underflows, NaNs, nonzeros
 struct GridScratch {
     uint32_t part[kParts];
     unsigned long long cnt[kStats][kCntParts];
 };
-static_assert(sizeof(GridScratch) == 3072, "one scratch slot is 3 KiB");
+static_assert(kParts % 256 == 0 && sizeof(GridScratch) == 4 * kParts + 2048, "scratch layout");
 
-// Flat launches keep at most this many blocks (larger inputs are covered by
-// grid-stride loops).
-constexpr int kMaxGrid = 65536;
+// Flat launches that reduce nothing keep at most this many blocks.
+#ifndef FP8Q_MAX_GRID
+#define FP8Q_MAX_GRID 65536
+#endif
+constexpr int kMaxGrid = FP8Q_MAX_GRID;
 
 // Scratch slots per device: one per stream that has run a reducing call.
 constexpr int kScratchSlots = 64;
@@ -44,7 +50,8 @@ struct ScaleSrc {
 
 hipError_t launch_fill_u32(uint32_t *p, uint32_t v, hipStream_t s);
 
-hipError_t launch_finish_amax(GridScratch *gs, float *out, hipStream_t s);
+// Fold part[0 .. nparts) into *out and clear those slots.
+hipError_t launch_finish_amax(GridScratch *gs, int nparts, float *out, hipStream_t s);
 
 hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScratch *gs, hipStream_t s);
 

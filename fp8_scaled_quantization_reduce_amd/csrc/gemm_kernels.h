@@ -816,7 +816,9 @@ hipError_t launch_gemm_epi(const GemmArgs &a)
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.amax_out) return e;
-    return launch_finish_amax(a.gs, a.amax_out, a.stream);
+    // blocks b of both launches folded into part[b % kParts]
+    return launch_finish_amax(a.gs, n_main > kParts || n_half > kParts ? kParts : (n_main > n_half ? n_main : n_half),
+                              a.amax_out, a.stream);
 }
 
 // Every output kind and epilogue of one operand-format pair.  The plain

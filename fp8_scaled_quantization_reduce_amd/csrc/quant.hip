@@ -32,6 +32,20 @@ static int flat_grid(int64_t units)
     return (int)(units < kMaxGrid ? units : kMaxGrid);
 }
 
+// The grid of a launch that reduces into the scratch: one partial slot per
+// block, at most `cap` <= kParts blocks.  Fewer, longer-lived blocks make the
+// finish kernel's read-and-clear pass short; measured on the MI355X over
+// 8192x8192 bf16, a 1024-block cast with fused amax takes 38.8 us against
+// 40.2 us at 2048 blocks and 46.8 us at 8192, and the read-only amax pass is
+// fastest at 512 blocks (22.4 us, 23.2 us at 1024), where each lane still has
+// four 16-byte loads in flight per unit.
+static int reduce_grid(int64_t units, int cap = kParts)
+{
+    if (units < 1) return 1;
+    return (int)(units < cap ? units : cap);
+}
+constexpr int kAmaxGrid = kParts / 2;
+
 template <int F>
 __device__ __forceinline__ Scales resolve_scales(const ScaleSrc &src)
 {
@@ -50,43 +64,55 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t v, hipStream_t s)
     return hipGetLastError();
 }
 
-// One block's magnitude max -> the atomic max of its partial slot (canonical
-// amax bits, so the slot's maximum is canonical too).  Every lane must reach
-// it.  The atomic returns nothing, so the block does not wait for it.
+// One block's magnitude max -> its partial slot (canonical amax bits).  Every
+// lane must reach it.  The launch has at most kParts blocks.
 __device__ __forceinline__ void block_partial(uint32_t m, GridScratch *gs)
 {
     __shared__ uint32_t red[kThreads / 64];
     m = block_max_u32<kThreads>(m, red);
-    if (threadIdx.x == 0) atomicMax(&gs->part[blockIdx.x % kParts], canonical_amax_bits(m));
+    if (threadIdx.x == 0) gs->part[blockIdx.x] = canonical_amax_bits(m);
 }
 
 // Read partial slot i and put it back to zero (one round trip).
 __device__ __forceinline__ uint32_t take_partial(GridScratch *gs, int i) { return atomicExch(&gs->part[i], 0u); }
 
-// Fold the kParts partial slots into the output word, leaving them zero.
-__global__ __launch_bounds__(kParts) void finish_amax_kernel(GridScratch *__restrict__ gs, uint32_t *__restrict__ out)
+// Max of partial slots [0, nparts), which it leaves zero; kThreads lanes with
+// up to kParts / kThreads exchanges in flight each.  Every lane gets the result.
+__device__ __forceinline__ uint32_t take_partials(GridScratch *gs, int nparts)
 {
-    __shared__ uint32_t red[kParts / 64];
-    const uint32_t m = block_max_u32<kParts>(take_partial(gs, threadIdx.x), red);
+    __shared__ uint32_t red[kThreads / 64];
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < kParts / kThreads; ++u) {
+        const int i = threadIdx.x + u * kThreads;
+        if (i < nparts) m = max(m, take_partial(gs, i));
+    }
+    return block_max_u32<kThreads>(m, red);
+}
+
+__global__ __launch_bounds__(kThreads) void finish_amax_kernel(GridScratch *__restrict__ gs, int nparts,
+                                                               uint32_t *__restrict__ out)
+{
+    const uint32_t m = take_partials(gs, nparts);
     if (threadIdx.x == 0) *out = m;
 }
 
-hipError_t launch_finish_amax(GridScratch *gs, float *out, hipStream_t s)
+hipError_t launch_finish_amax(GridScratch *gs, int nparts, float *out, hipStream_t s)
 {
-    finish_amax_kernel<<<1, kParts, 0, s>>>(gs, reinterpret_cast<uint32_t *>(out));
+    finish_amax_kernel<<<1, kThreads, 0, s>>>(gs, nparts, reinterpret_cast<uint32_t *>(out));
     return hipGetLastError();
 }
 
-__global__ __launch_bounds__(kParts) void clear_scratch_kernel(GridScratch *__restrict__ gs)
+__global__ __launch_bounds__(kThreads) void clear_scratch_kernel(GridScratch *__restrict__ gs)
 {
-    gs->part[threadIdx.x] = 0u;
+    for (int i = threadIdx.x; i < kParts; i += kThreads) gs->part[i] = 0u;
     if (threadIdx.x < kStats * kCntParts) gs->cnt[threadIdx.x / kCntParts][threadIdx.x % kCntParts] = 0ull;
 }
 
 hipError_t launch_clear_scratch(GridScratch *gs, hipStream_t s)
 {
-    static_assert(kStats * kCntParts <= kParts, "one lane per slot");
-    clear_scratch_kernel<<<1, kParts, 0, s>>>(gs);
+    static_assert(kStats * kCntParts <= kThreads, "one lane per count slot");
+    clear_scratch_kernel<<<1, kThreads, 0, s>>>(gs);
     return hipGetLastError();
 }
 
@@ -95,7 +121,10 @@ hipError_t launch_clear_scratch(GridScratch *gs, hipStream_t s)
 // vectors of its unit, kThreads vectors apart (so every load instruction of a
 // wave covers 1 KiB contiguously); the tail of fewer than one vector is read
 // by the first lanes of block 0.
-constexpr int kAmaxU = 4;
+#ifndef FP8Q_AMAX_U
+#define FP8Q_AMAX_U 4
+#endif
+constexpr int kAmaxU = FP8Q_AMAX_U;
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const void *__restrict__ x, int64_t n, GridScratch *gs)
@@ -144,14 +173,14 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void *__restrict__
 hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScratch *gs, hipStream_t s)
 {
     const int64_t nvec = n / (dtype == kBF16 ? 8 : 4);
-    const int grid = flat_grid(ceil_div(nvec, (int64_t)kThreads * kAmaxU));
+    const int grid = reduce_grid(ceil_div(nvec, (int64_t)kThreads * kAmaxU), kAmaxGrid);
     if (dtype == kBF16)
         amax_kernel<kBF16><<<grid, kThreads, 0, s>>>(x, n, gs);
     else
         amax_kernel<kF32><<<grid, kThreads, 0, s>>>(x, n, gs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_finish_amax(gs, amax, s);
+    return launch_finish_amax(gs, grid, amax, s);
 }
 
 // ------------------------------------------------------------------ cast --
@@ -330,7 +359,10 @@ __device__ __forceinline__ void chunk_counts(const Chunk16<kF32> &c, const uint3
 // (delayed scaling records it after the cast, section 5).  With kCount the
 // same pass counts the cast's overflows, underflows, NaNs and nonzeros
 // (section 24) against the scale it casts with.
-constexpr int kCastU = 2;
+#ifndef FP8Q_CAST_U
+#define FP8Q_CAST_U 2
+#endif
+constexpr int kCastU = FP8Q_CAST_U;
 
 template <int F, int DT, bool kAmax, bool kCount = false>
 __global__ __launch_bounds__(kThreads) void cast_kernel(const void *__restrict__ x, int64_t n, ScaleSrc src,
@@ -398,7 +430,8 @@ template <int F, int DT>
 static hipError_t launch_cast_t(const void *x, int64_t n, ScaleSrc src, uint8_t *q, float *scale_inv_out,
                                 float *scale_out, float *amax_out, uint64_t *stats, GridScratch *gs, hipStream_t s)
 {
-    const int grid = flat_grid(ceil_div(n >> 4, (int64_t)kThreads * kCastU));
+    const int64_t units = ceil_div(n >> 4, (int64_t)kThreads * kCastU);
+    const int grid = (amax_out || stats) ? reduce_grid(units) : flat_grid(units);
     if (stats) {
         if (amax_out)
             cast_kernel<F, DT, true, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs);
@@ -410,7 +443,7 @@ static hipError_t launch_cast_t(const void *x, int64_t n, ScaleSrc src, uint8_t 
         cast_kernel<F, DT, false><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, nullptr);
     }
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && amax_out) e = launch_finish_amax(gs, amax_out, s);
+    if (e == hipSuccess && amax_out) e = launch_finish_amax(gs, grid, amax_out, s);
     if (e == hipSuccess && stats) e = launch_finish_stats(gs, stats, s);
     return e;
 }
@@ -542,7 +575,7 @@ __global__ __launch_bounds__(kStats * kCntParts) void finish_stats_kernel(GridSc
 hipError_t launch_cast_stats(const void *x, int dtype, int64_t n, int fmt, const float *scale_inv, uint64_t *stats,
                              GridScratch *gs, hipStream_t s)
 {
-    const int grid = flat_grid(ceil_div(n >> 4, (int64_t)kThreads * kStatsU));
+    const int grid = reduce_grid(ceil_div(n >> 4, (int64_t)kThreads * kStatsU));
     if (fmt == kE4M3) {
         if (dtype == kBF16) cast_stats_kernel<kE4M3, kBF16><<<grid, kThreads, 0, s>>>(x, n, scale_inv, gs);
         else cast_stats_kernel<kE4M3, kF32><<<grid, kThreads, 0, s>>>(x, n, scale_inv, gs);
@@ -647,8 +680,9 @@ __global__ __launch_bounds__(kThreads) void error_feedback_kernel(const void *__
 hipError_t launch_error_feedback(const void *g, int dtype, float *residual, int64_t n, int fmt,
                                  const float *scale_inv, uint8_t *q, float *amax_out, GridScratch *gs, hipStream_t s)
 {
-    const int grid = flat_grid(ceil_div(n >> 4, (int64_t)kThreads * kEfU));
     const bool am = amax_out != nullptr;
+    const int64_t units = ceil_div(n >> 4, (int64_t)kThreads * kEfU);
+    const int grid = am ? reduce_grid(units) : flat_grid(units);
     if (fmt == kE4M3) {
         if (dtype == kBF16) error_feedback_kernel<kE4M3, kBF16><<<grid, kThreads, 0, s>>>(g, residual, n, scale_inv, q, gs, am);
         else error_feedback_kernel<kE4M3, kF32><<<grid, kThreads, 0, s>>>(g, residual, n, scale_inv, q, gs, am);
@@ -658,7 +692,7 @@ hipError_t launch_error_feedback(const void *g, int dtype, float *residual, int6
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !am) return e;
-    return launch_finish_amax(gs, amax_out, s);
+    return launch_finish_amax(gs, grid, amax_out, s);
 }
 
 // --------------------------------------------------------------- delayed --
@@ -669,7 +703,7 @@ hipError_t launch_error_feedback(const void *g, int dtype, float *residual, int6
 // is either read from memory or, for the fused step, reduced here from the
 // cast kernel's partial slots (which it leaves zero) and published to
 // amax_out.
-constexpr int kDelayedThreads = kParts; // one partial slot per lane
+constexpr int kDelayedThreads = 256;
 
 // Order-preserving key of a float for an unsigned max (negative values flip
 // all bits, positive values set the sign bit); every NaN maps above +inf, so
@@ -683,7 +717,7 @@ __device__ __forceinline__ uint32_t order_key(float h)
 
 __global__ __launch_bounds__(kDelayedThreads) void delayed_kernel(float *__restrict__ hist, int L, int n_cols, int col,
                                                                   const float *__restrict__ new_amax,
-                                                                  GridScratch *__restrict__ gs,
+                                                                  GridScratch *__restrict__ gs, int nparts,
                                                                   float *__restrict__ amax_out, int slot, float fmax,
                                                                   int margin, int algo, float *__restrict__ scale,
                                                                   float *__restrict__ scale_inv)
@@ -695,7 +729,11 @@ __global__ __launch_bounds__(kDelayedThreads) void delayed_kernel(float *__restr
     // both round trips overlap.
     const bool h0_valid = tid < L && tid != slot;
     const float h0 = h0_valid ? hist[(int64_t)tid * n_cols + col] : 0.0f;
-    const uint32_t m0 = gs ? take_partial(gs, tid) : 0u;
+    uint32_t m0 = 0;
+    if (gs)
+#pragma unroll
+        for (int u = 0; u < kParts / kDelayedThreads; ++u)
+            if (tid + u * kDelayedThreads < nparts) m0 = max(m0, take_partial(gs, tid + u * kDelayedThreads));
     // largest entry of the column other than the slot being overwritten
     uint32_t key = h0_valid ? order_key(h0) : 0u;
     for (int j = tid + kDelayedThreads; j < L; j += kDelayedThreads)
@@ -736,7 +774,7 @@ hipError_t launch_delayed(float *hist, int history_len, int n_cols, int col, con
                           int fmt, int margin, int algo, float *scale, float *scale_inv, hipStream_t s)
 {
     const int slot = (int)(step % history_len);
-    delayed_kernel<<<1, kDelayedThreads, 0, s>>>(hist, history_len, n_cols, col, new_amax, nullptr, nullptr, slot,
+    delayed_kernel<<<1, kDelayedThreads, 0, s>>>(hist, history_len, n_cols, col, new_amax, nullptr, 0, nullptr, slot,
                                                  fmax_of(fmt), margin, algo, scale, scale_inv);
     return hipGetLastError();
 }
@@ -751,7 +789,7 @@ hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, flo
                                hipStream_t s)
 {
     const ScaleSrc src{nullptr, scale_inv + col, 0};
-    const int grid = flat_grid(ceil_div(n >> 4, (int64_t)kThreads * kCastU));
+    const int grid = reduce_grid(ceil_div(n >> 4, (int64_t)kThreads * kCastU));
     if (fmt == kE4M3) {
         if (dtype == kBF16)
             cast_kernel<kE4M3, kBF16, true><<<grid, kThreads, 0, s>>>(x, n, src, q, q_scale_inv_out, nullptr, gs);
@@ -766,7 +804,7 @@ hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, flo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int slot = (int)(step % history_len);
-    delayed_kernel<<<1, kDelayedThreads, 0, s>>>(hist, history_len, n_cols, col, nullptr, gs, amax_out, slot,
+    delayed_kernel<<<1, kDelayedThreads, 0, s>>>(hist, history_len, n_cols, col, nullptr, gs, grid, amax_out, slot,
                                                  fmax_of(fmt_next), margin, algo, scale, scale_inv);
     return hipGetLastError();
 }
@@ -1335,16 +1373,17 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
     if constexpr (kAmax) block_partial(m_all, gs);
 }
 
-static int tile_grid(int64_t rows, int64_t cols)
+static int tile_grid(int64_t rows, int64_t cols, bool reduce = false)
 {
-    return flat_grid(ceil_div(rows, kTile) * ceil_div(cols, kTile));
+    const int64_t tiles = ceil_div(rows, kTile) * ceil_div(cols, kTile);
+    return reduce ? reduce_grid(tiles) : flat_grid(tiles);
 }
 
 template <int F, int DT>
 static hipError_t launch_rc_t(const void *x, int64_t rows, int64_t cols, ScaleSrc src, uint8_t *q_row, uint8_t *q_col,
                               float *scale_inv_out, float *scale_out, float *amax_out, GridScratch *gs, hipStream_t s)
 {
-    const int grid = tile_grid(rows, cols);
+    const int grid = tile_grid(rows, cols, amax_out != nullptr);
     if (amax_out)
         tile_kernel<F, DT, kTilePerTensor, true><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr,
                                                                           nullptr, scale_inv_out, scale_out, gs,
@@ -1355,7 +1394,7 @@ static hipError_t launch_rc_t(const void *x, int64_t rows, int64_t cols, ScaleSr
                                                                            ScaleSrc{}, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !amax_out) return e;
-    return launch_finish_amax(gs, amax_out, s);
+    return launch_finish_amax(gs, grid, amax_out, s);
 }
 
 hipError_t launch_rowwise_colwise(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, ScaleSrc src,
@@ -1382,7 +1421,7 @@ static hipError_t launch_hybrid_m(const void *x, int64_t rows, int64_t cols, Sca
                                   uint8_t *q_row, uint8_t *q_col, float *row_scale_inv_out, float *col_scale_inv_out,
                                   float *amax_out, GridScratch *gs, hipStream_t s)
 {
-    const int grid = tile_grid(rows, cols);
+    const int grid = tile_grid(rows, cols, amax_out != nullptr);
     if (amax_out)
         tile_kernel<F, DT, kMode, true><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr, nullptr,
                                                                  row_scale_inv_out, nullptr, gs, src_col,
@@ -1393,7 +1432,7 @@ static hipError_t launch_hybrid_m(const void *x, int64_t rows, int64_t cols, Sca
                                                                   col_scale_inv_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !amax_out) return e;
-    return launch_finish_amax(gs, amax_out, s);
+    return launch_finish_amax(gs, grid, amax_out, s);
 }
 
 template <int F, int DT>

@@ -15,7 +15,7 @@
  *  - The library never allocates device memory.  Calls that reduce over the
  *    whole grid (an amax, the cast statistics) keep per-block partials in a
  *    reduction scratch that is a device global of the library: 64 slots of
- *    3 KiB on each device, created with the library's code object on that
+ *    6 KiB on each device, created with the library's code object on that
  *    device and held until the process ends.  Each stream gets a slot of its
  *    own the first time it runs such a call (a host-side table; no device
  *    work), so calls on different streams never share partials.  The slot is

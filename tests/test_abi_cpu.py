@@ -251,13 +251,13 @@ def test_last_error_is_thread_local_string():
 
 # --------------------------------------------------------- lifecycle ------
 # The library allocates no device memory: its reduction scratch is one device
-# global of fixed size (64 slots of 3 KiB per device), whose address on the
+# global of fixed size (64 slots of 6 KiB per device), whose address on the
 # current device comes from hipGetSymbolAddress.  Both facts are visible in the
 # built library without a GPU.
 ALLOCATORS = ("hipMalloc", "hipFree", "hipHostMalloc", "hipHostFree", "hipExtMallocWithFlags", "hipMallocAsync",
               "hipFreeAsync", "hipMallocManaged", "hipMallocPitch", "hipMalloc3D", "hipMallocArray",
               "hipMemPoolCreate", "hipMemCreate", "hipMemAddressReserve")
-SCRATCH_SLOTS, SLOT_BYTES = 64, 3072
+SCRATCH_SLOTS, SLOT_BYTES = 64, 6144
 
 
 def _nm(*flags):
