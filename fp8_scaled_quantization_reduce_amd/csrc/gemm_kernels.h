@@ -763,6 +763,328 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
     }
 }
 
+// ---------------------------------------------------------------------------
+// Block-scaled kernel with a ping-pong schedule (the launch of full 256x256
+// tiles).  The same tiles, operand stages and arithmetic as gemm_bs_kernel:
+// eight waves of 64x128 (4 x 8 tiles of 16x16, one v_mfma_f32_16x16x128 per
+// tile per 128-wide K slice, started from zero, promoted at once by
+// acc = fma(part, weight, acc)).  What differs is the order of work.  The
+// waves form two groups, X (waves 0-3) and Y (waves 4-7), one wave of each on
+// every SIMD, and a slice runs as four phases separated by barriers: in each
+// phase one group computes half of its slice (16 MFMAs, each followed by the
+// promotion of the tile two before it) from fragments already in registers,
+// while the other group reads its next fragments from LDS, finishes the
+// promotion of its last two tiles and (group X) issues global loads.  So
+// every SIMD always has one wave feeding its matrix pipe while the other
+// waits on memory, instead of both waves stalling together at one barrier
+// per slice (measured on the MI355X: two waves that each interleave four
+// promotion FMAs per MFMA keep the pipe ~94% busy; the lockstep schedule
+// kept it 46% busy).
+//
+// Memory: two 64 KiB stages (A rows 0..255, B rows 0..255 of one slice) plus
+// per-stage scales.  Group X alone loads, in two groups per slice: group 1
+// (A, the B rows 0..63 and 128..191 that X and Y read first, the A row scales
+// and B's scales) once the stage's previous A and first-half B reads are
+// over, group 2 (B rows 64..127 and 192..255) once its second-half reads are
+// over, each six phases before it is read.  Every X wave issues the same
+// loads in the same order, so one vmcnt threshold at the end of each X
+// compute phase (G1 + G2 younger loads outstanding) proves that the data the
+// next phases read has landed.
+template <int kv> struct PhaseC {
+    static constexpr int value = kv;
+};
+
+template <int FA, int FB, bool kAmax, int kOut, bool kFuse, bool kRowB>
+__global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_pp_kernel(const uint8_t *__restrict__ A,
+                                                                   const uint8_t *__restrict__ B,
+                                                                   const float *__restrict__ sA,
+                                                                   const float *__restrict__ sB, int M, int N, int K,
+                                                                   void *__restrict__ C, Epi epi, uint32_t *part,
+                                                                   int n_main)
+{
+    // One LDS object per stage (the compiler's wait insertion tells the direct
+    // loads into different objects apart, so a read of one stage never waits
+    // for the loads landing in the other; within a stage the loads that a
+    // read does not need were issued four phases earlier).  Stage layout:
+    //   A      rows 0..255 of the tile (32 KiB)
+    //   B0     the B rows each wave reads first: tile rows 0..63 (group X)
+    //          then 128..191 (group Y) (16 KiB)
+    //   B1     the B rows each wave reads second: 64..127, then 192..255
+    //   SA     the slice's 256 A row scales
+    //   SB0    1x128 B: the scales of B0's rows; 128x128 B: the tile's two
+    //          block scales at [0], [1] (each loading wave writes a 64-float copy)
+    //   SB1    1x128 B: the scales of B1's rows
+    // B row n of the tile is row (n >> 7) * 64 + (n & 63) of B0 (n & 64 == 0)
+    // or B1.  Rows are 128 bytes with 16-byte chunks XOR-swizzled by row.
+    constexpr int kAB = kBM * kBK, kB2 = kBM / 2 * kBK; // code bytes of A, of B0 / B1
+    constexpr int oB0 = kAB, oB1 = kAB + kB2, oSA = kAB + 2 * kB2, oSB0 = oSA + 4 * kBM, oSB1 = oSB0 + 4 * kBM;
+    constexpr int kStage = oSB1 + 2 * kBM;
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[kStage];
+    __shared__ uint32_t red[kBSThreads / 64];
+    constexpr int G1 = 7;              // loads per wave in group 1
+    constexpr int G2 = kRowB ? 3 : 2;  // and in group 2
+    constexpr int kVm = G1 + G2;       // younger loads allowed at the end of every phase
+    auto fptr = [](uint8_t *st, int off) { return reinterpret_cast<float *>(st + off); };
+
+    int tm, tn;
+    const int tilesM = (M + kBM - 1) / kBM, tilesN = (N + kBM - 1) / kBM;
+    group_tile(xcd_order(blockIdx.x, n_main), tilesM, tilesN, tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBM;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool gx = w < 4;
+    const int wm = w & 3, wn = w >> 2; // rows 64 wm .., columns 128 wn .. of the tile
+    const int fr = lane & 15, fg = lane >> 4;
+    const int kblocks = K / kBK;
+
+    const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBM, (int64_t)N - n0);
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * K), 0, (int)(a_rows * K), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0 * K), 0, (int)(b_rows * K), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)(sA + m0 * kblocks), 0,
+                                                                        (int)(a_rows * kblocks * 4), kRawBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsb =
+        kRowB ? __builtin_amdgcn_make_buffer_rsrc((void *)(sB + n0 * kblocks), 0, (int)(b_rows * kblocks * 4),
+                                                  kRawBufferWord3)
+              : __builtin_amdgcn_make_buffer_rsrc((void *)sB, 0, (int)((N / 128) * kblocks * 4), kRawBufferWord3);
+    // Every wave loads an eighth of each region: rows 8(w + 8u) + L / 8; lane L
+    // writes physical chunk L % 8 of its row, which holds logical chunk
+    // (L % 8) ^ ((row >> 1) & 7) = (L % 8) ^ ((4 w + L / 16) & 7)
+    const int voff = (lane >> 3) * K + (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4);
+    // 128x128 B: lanes 0 and 1 fetch the scales of the tile's two column
+    // blocks (clamped inside B for a tile column past N, whose results are
+    // never stored), the other lanes repeat them
+    const int sb_voff = kRowB ? lane * kblocks * 4 : min((int)(n0 / 128) + (lane & 1), N / 128 - 1) * kblocks * 4;
+
+    // A: rows 8(w + 8u), u = 0..3; B half h: LDS rows 8(w + 8u), u = 0..1,
+    // holding tile rows (LDS row >> 6) * 128 + 64 h + (LDS row & 63)
+    auto load_a = [&](uint8_t *dst, int kb) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int row = 8 * (w + 8 * u);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(dst + row * kBK), 16, voff, row * K + kb * kBK,
+                                                     0, 0);
+        }
+    };
+    auto load_b = [&](uint8_t *dst, int h, int kb) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int row = 8 * (w + 8 * u);
+            const int trow = (row >> 6) * 128 + 64 * h + (row & 63);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(dst + row * kBK), 16, voff, trow * K + kb * kBK,
+                                                     0, 0);
+        }
+    };
+    // 1x128 B: the scales of half h's LDS rows 64 (w & 1) .. + 63 (the other
+    // waves repeat waves 0 and 1, writing the same values)
+    auto load_sb_rows = [&](float *dst, int h, int kb) {
+        const int lrow = 64 * (w & 1), trow = 128 * (w & 1) + 64 * h;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(dst + lrow), 4, sb_voff, (trow * kblocks + kb) * 4,
+                                                 0, 0);
+    };
+    // group 1 of slice kb: A, B's first half, and one scale load per wave
+    // (waves 0-3: A row scales 64 w ..; waves 4-7: B's first-half scales)
+    auto load_g1 = [&](uint8_t *st, int kb) {
+        load_a(st, kb);
+        load_b(st + oB0, 0, kb);
+        if (w < 4)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(st + oSA + 4 * 64 * w), 4, lane * kblocks * 4,
+                                                     (64 * w * kblocks + kb) * 4, 0, 0);
+        else if constexpr (kRowB)
+            load_sb_rows(fptr(st, oSB0), 0, kb);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(st + oSB0 + 4 * 64 * (w - 4)), 4, sb_voff,
+                                                     kb * 4, 0, 0);
+    };
+    // group 2 of slice kb: B's second half (and its 1x128 scales)
+    auto load_g2 = [&](uint8_t *st, int kb) {
+        load_b(st + oB1, 1, kb);
+        if constexpr (kRowB) load_sb_rows(fptr(st, oSB1), 1, kb);
+    };
+
+    v4f acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    v8i a[4], b[4];   // the slice's A fragments, the half's B fragments
+    float wi[4];      // 128x128 B: weight of row i; 1x128 B: sA of row i
+    v4f sbq[4];       // 1x128 B: the half's column scales, per 16-column tile
+    v4f pr[3];        // MFMA results awaiting promotion (tile t in pr[t % 3])
+
+    // weight of tile (i, column tile jj of the half) for element e
+    auto weight = [&](int i, int jj, int e) { return kRowB ? wi[i] * sbq[jj][e] : wi[i]; };
+    // promote tile t (t = 4 jj + i) of half h
+    auto promote = [&](auto hc, int t) {
+        constexpr int h = decltype(hc)::value;
+        const int i = t & 3, jj = t >> 2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc[i][4 * h + jj][e] = __builtin_fmaf(pr[t % 3][e], weight(i, jj, e), acc[i][4 * h + jj][e]);
+        // keeps these FMAs in their phase (ordered with the phase boundary's
+        // volatile statements)
+        asm volatile("" : "+v"(acc[i][4 * h + jj]));
+    };
+    // compute phase of half h: MFMA of tile t, then the promotion of tile t - 2
+    // (its result has landed); tiles 14 and 15 are promoted by the next phase
+    auto compute = [&](auto hc) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            pr[t % 3] = mfma16x16x128<FB, FA>(b[t >> 2], a[t & 3], v4f{0.f, 0.f, 0.f, 0.f});
+            if (t >= 2) promote(hc, t - 2);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+            if (t >= 2) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0); // promotion FMAs
+        }
+    };
+    auto tail = [&](auto hc) {
+        promote(hc, 14);
+        promote(hc, 15);
+    };
+    auto read_a = [&](const uint8_t *st) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = read_frag(st, wm * 64 + 16 * i + fr, fg);
+    };
+    auto read_b = [&](const uint8_t *st) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) b[jj] = read_frag(st, wn * 64 + 16 * jj + fr, fg);
+    };
+    // the slice's weights (with the first half) and the half's 1x128 column scales
+    auto read_scales = [&](const float *ssa_, const float *ssbh, int h) {
+        if (h == 0) {
+            if constexpr (kRowB) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wi[i] = ssa_[wm * 64 + 16 * i + fr];
+            } else {
+                const float sb = ssbh[wn];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wi[i] = ssa_[wm * 64 + 16 * i + fr] * sb;
+            }
+        }
+        if constexpr (kRowB) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                sbq[jj] = *reinterpret_cast<const v4f *>(ssbh + wn * 64 + 16 * jj + 4 * fg);
+        }
+    };
+    // Phase boundaries.  The scheduling barriers keep every instruction on
+    // its side (matrix and vector instructions touch no memory, so a memory
+    // fence alone would let them drift across the barrier into the other
+    // phase); the end of a read phase waits for its LDS reads, the end of a
+    // compute phase for the loads the next phases read.
+    auto phase_end = [&](auto wc) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(decltype(wc)::value);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto sync_lds = [&]() { phase_end(PhaseC<waitcnt_imm(kVm, 0)>{}); };
+    auto sync = [&]() { phase_end(PhaseC<waitcnt_imm(kVm, 15)>{}); };
+    using H0 = PhaseC<0>;
+    using H1 = PhaseC<1>;
+
+    // One slice (stage cur, the other stage nxt): four operations, one per
+    // phase, each ending at a barrier after the wave has waited for all but
+    // its kVm youngest loads.  Group X runs the operations one phase ahead of
+    // group Y, so in every phase one group computes while the other reads.
+    // Each wave loads in its read phases: in M0 its share of group 2 of the
+    // next slice into nxt (both groups have read nxt's second-half B by then),
+    // in M1 its share of group 1 of slice kb + 2 into cur (both have read its A
+    // and first-half B).  Data is read at least five phases after it was
+    // requested, and every wave issues the same loads in every slice (loads
+    // past the last slice read bytes that are never used, or zeros past the
+    // panel), so the one threshold holds in every phase.
+    auto slice = [&](int kb, uint8_t *cur, uint8_t *nxt) {
+        read_a(cur); // M0: A and the first half's B fragments, the slice's weights
+        read_b(cur + oB0);
+        tail(H1{});
+        read_scales(fptr(cur, oSA), fptr(cur, oSB0), 0);
+        load_g2(nxt, kb + 1);
+        sync_lds();
+        compute(H0{}); // C0
+        sync();
+        read_b(cur + oB1); // M1
+        tail(H0{});
+        read_scales(fptr(cur, oSA), fptr(cur, oSB1), 1);
+        load_g1(cur, kb + 2);
+        sync_lds();
+        compute(H1{}); // C1
+        sync();
+    };
+
+    // prologue: groups 1 and 2 of slice 0 and group 1 of slice 1 (slice 0's
+    // first read phase loads group 2 of slice 1), then slice 0's group 1 landed
+    if (kblocks > 0) {
+        load_g1(st0, 0);
+        load_g2(st0, 0);
+        load_g1(st1, 1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(G2 + G1, 15));
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // nothing to promote yet: zero partials and weights make the first
+    // tail a no-op
+#pragma unroll
+    for (int q = 0; q < 3; ++q) pr[q] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        wi[i] = 0.0f;
+        sbq[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    if (!gx) sync(); // group Y starts one phase later
+    int kb = 0;
+    for (; kb + 1 < kblocks; kb += 2) {
+        slice(kb, st0, st1);
+        slice(kb + 1, st1, st0);
+    }
+    if (kb < kblocks) slice(kb, st0, st1);
+    if (gx) sync(); // and ends one phase later
+    tail(H1{});
+    // the loads of the slices past the end must land before the stages are reused
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    // epilogue: lane (fr, fg) of tile (i, j) holds C[row][4 consecutive cols];
+    // each wave stages its 64x128 results in 16 KiB of the freed stages
+    const float out_scale = kOut >= kOutE4M3 ? 1.0f / *epi.out_si : 0.0f;
+    uint32_t m = 0;
+    {
+        typedef EpiStage<128, out_bytes<kOut>(), 64, kB2> ES;
+        const int64_t wrow0 = m0 + wm * 64, wcol0 = n0 + wn * 128;
+        const bool inside = wrow0 < M && wcol0 < N;
+        uint8_t *ep = (w < 4 ? st0 : st1) + (w & 3) * kB2;
+#pragma unroll
+        for (int ps = 0; ps < ES::kPasses; ++ps) {
+            __syncthreads(); // the stages (then the previous pass) are no longer read
+            if (inside) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if ((16 * i) / ES::kPassRows != ps) continue;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const uint4 bits =
+                            pack_out4<kOut, kAmax, kFuse>(wcol0 + 16 * j + 4 * fg, acc[i][j], m, epi, out_scale);
+                        ES::put(ep, 16 * i + fr - ps * ES::kPassRows, 4 * j + fg, bits);
+                    }
+                }
+            }
+            __syncthreads();
+            if (inside) ES::store(ep, C, N, wrow0 + ps * ES::kPassRows, wcol0, lane);
+        }
+    }
+    if constexpr (kAmax) {
+        m = block_max_u32<kBSThreads>(m, red);
+        if (tid == 0) atomicMax(&part[blockIdx.x % kParts], canonical_amax_bits(m));
+    }
+}
+
 inline int gemm_grid(int64_t M, int64_t N) { return (int)(((M + kBM - 1) / kBM) * ((N + kBM - 1) / kBM)); }
 
 template <int FA, int FB, int kOut, bool kFuse>
@@ -805,13 +1127,23 @@ hipError_t launch_gemm_epi(const GemmArgs &a)
                 gemm_bs_kernel<FA, FB, false, kOut, kFuse, ROWB, BN><<<GRID, kBSThreads, 0, a.stream>>>(            \
                     a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, PART, BASE, n_main);                                   \
         } while (0)
+#define FP8Q_BS_PP_LAUNCH(ROWB)                                                                                     \
+        do {                                                                                                        \
+            if (a.amax_out)                                                                                         \
+                gemm_bs_pp_kernel<FA, FB, true, kOut, kFuse, ROWB><<<n_main, kBSThreads, 0, a.stream>>>(            \
+                    a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, part, n_main);                                         \
+            else                                                                                                    \
+                gemm_bs_pp_kernel<FA, FB, false, kOut, kFuse, ROWB><<<n_main, kBSThreads, 0, a.stream>>>(           \
+                    a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, part, n_main);                                         \
+        } while (0)
         if (a.mode == 1) {
-            if (n_main > 0) FP8Q_BS_LAUNCH(false, kBM, n_main, part, 0);
+            if (n_main > 0) FP8Q_BS_PP_LAUNCH(false);
             if (n_half > 0) FP8Q_BS_LAUNCH(false, kBM / 2, n_half, part_half, n_main);
         } else {
-            if (n_main > 0) FP8Q_BS_LAUNCH(true, kBM, n_main, part, 0);
+            if (n_main > 0) FP8Q_BS_PP_LAUNCH(true);
             if (n_half > 0) FP8Q_BS_LAUNCH(true, kBM / 2, n_half, part_half, n_main);
         }
+#undef FP8Q_BS_PP_LAUNCH
 #undef FP8Q_BS_LAUNCH
     }
     hipError_t e = hipGetLastError();
