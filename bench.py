@@ -22,8 +22,7 @@ rows) is timed at its own workload size under "rows": the median and the
 back-to-back launches between two events, taken after 150 ms of untimed
 launches of the same call.  Memory-bound rows report GB/s against the 8 TB/s
 peak and against a device copy measured in the same run; GEMM rows report
-TFLOP/s against the 5.0 PFLOP/s FP8 peak and against that peak scaled to the
-graphics clock sampled while the row ran.  Each row carries the CPU oracle's
+TFLOP/s against the 5.0 PFLOP/s FP8 peak.  Each row carries the CPU oracle's
 rate on the same workload ("cpu"), a baseline only.
 
 The CPU oracle's delayed-scaling schedule is the headline's "cpu_baseline".
@@ -32,7 +31,6 @@ import argparse
 import json
 import os
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +39,6 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 FP8_MFMA_PEAK_TFLOPS = 5000.0
-MFMA_PEAK_SCLK_MHZ = 2400.0  # the clock the 5.0 PFLOP/s figure assumes (256 CUs x 8192 FP8 flop/clk)
 # HBM bytes of one delayed step (cast_kernel + delayed_kernel), from the
 # FETCH_SIZE and WRITE_SIZE counters scaled by the factors a plain copy gives
 # (profiles/delayed_step_8192x8192_bf16_hbm_traffic.md); None whenever either
@@ -93,87 +90,6 @@ def copy_calibration(mib, reps=4):
                       "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
-# ----------------------------------------------------------------- clock ----
-class ClockSampler:
-    """Samples the GPU's graphics clock (MHz) from a host thread while a row
-    runs, through the AMD SMI library when it is importable, else the sysfs
-    DPM table; reports nothing when neither can be read."""
-
-    def __init__(self, period_s=0.005):
-        self.period = period_s
-        self.read = None
-        self.source = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            handle = amdsmi.amdsmi_get_processor_handles()[0]
-
-            def read_xcds():
-                # the current clock of every XCD (each has its own graphics
-                # clock domain); entries of 0xFFFF are unused slots
-                clks = amdsmi.amdsmi_get_gpu_metrics_info(handle)["current_gfxclks"]
-                v = [float(c) for c in clks if isinstance(c, (int, float)) and 0 < c < 0xFFFF]
-                if not v:
-                    raise ValueError("no per-XCD clocks")
-                return sum(v) / len(v)
-
-            def read_clk():
-                return float(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"])
-            try:
-                read_xcds()
-                self.read, self.source = read_xcds, "amdsmi gpu metrics, mean of the XCDs' current graphics clocks"
-            except Exception:
-                read_clk()
-                self.read, self.source = read_clk, "amdsmi graphics clock"
-        except Exception:
-            self.read = self._sysfs_reader()
-        self.samples = []
-        self._stop = threading.Event()
-        self._thread = None
-
-    def _sysfs_reader(self):
-        import glob
-        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-            def read_dpm(path=path):
-                for line in open(path):
-                    if line.strip().endswith("*"):
-                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
-                raise ValueError("no current level")
-            try:
-                read_dpm()
-            except Exception:
-                continue
-            self.source = "sysfs pp_dpm_sclk (" + path + ")"
-            return read_dpm
-        return None
-
-    def _loop(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append(self.read())
-            except Exception:
-                pass
-            self._stop.wait(self.period)
-
-    def start(self):
-        self.samples = []
-        if self.read is None:
-            return
-        self._stop.clear()
-        self._thread = threading.Thread(target=self._loop, daemon=True)
-        self._thread.start()
-
-    def stop(self):
-        if self._thread is not None:
-            self._stop.set()
-            self._thread.join()
-            self._thread = None
-        if not self.samples:
-            return None
-        s = sorted(self.samples)
-        return {"mean_mhz": round(sum(s) / len(s), 1), "min_mhz": s[0], "max_mhz": s[-1], "n": len(s)}
-
-
 # ---------------------------------------------------------------- timing ----
 def _pct(values, q):
     s = sorted(values)
@@ -183,11 +99,10 @@ def _pct(values, q):
     return s[lo] + (s[hi] - s[lo]) * (pos - lo)
 
 
-def time_launches(torch, stream, fn, per_sample, rotate=1, samples=SAMPLES, clock=None):
+def time_launches(torch, stream, fn, per_sample, rotate=1, samples=SAMPLES):
     """ms per launch of fn(i): after WARM_S seconds of untimed launches,
     `samples` samples of `per_sample` back-to-back launches, each sample
-    between two events on `stream`.  Returns median, p10, p90 and the clock
-    sampled meanwhile."""
+    between two events on `stream`.  Returns median, p10 and p90."""
     i, t0 = 0, time.perf_counter()
     while True:
         fn(i % rotate)
@@ -198,8 +113,6 @@ def time_launches(torch, stream, fn, per_sample, rotate=1, samples=SAMPLES, cloc
                 break
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(samples + 1)]
-    if clock:
-        clock.start()
     ev[0].record(stream)
     for k in range(samples):
         for _ in range(per_sample):
@@ -207,10 +120,9 @@ def time_launches(torch, stream, fn, per_sample, rotate=1, samples=SAMPLES, cloc
             i += 1
         ev[k + 1].record(stream)
     torch.cuda.synchronize()
-    sclk = clock.stop() if clock else None
     ms = [ev[k].elapsed_time(ev[k + 1]) / per_sample for k in range(samples)]
     return {"ms": round(_pct(ms, 0.5), 5), "ms_p10": round(_pct(ms, 0.1), 5), "ms_p90": round(_pct(ms, 0.9), 5),
-            "samples": samples, "launches_per_sample": per_sample, "sclk": sclk}
+            "samples": samples, "launches_per_sample": per_sample}
 
 
 def cpu_rate(fn, units, unit, budget_s=3.0, reps=3):
@@ -268,7 +180,6 @@ def main():
     dev = "cuda"
     stream = torch.cuda.current_stream()
     E4, E5 = fq.E4M3FN, fq.E5M2
-    clock = ClockSampler()
 
     def to_dev(a):
         if a.dtype == np.uint16:
@@ -296,15 +207,14 @@ def main():
         "data": "synthetic (seeded numpy generators, resident in HBM)",
     }
     if args.headline:
-        result.update(headline(args, fq, torch, xs, stream, clock, n))
+        result.update(headline(args, fq, torch, xs, stream, n))
 
     # -------------------------------------------------------- every row ----
     only = set(x for x in args.only.split(",") if x)
     if args.rows:
-        out, ceiling = time_rows(fq, torch, np, workloads, to_dev, xs, stream, clock, only, args.cpu_baseline)
+        out, ceiling = time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, args.cpu_baseline)
         result["rows"] = out
         result["copy_ceiling"] = ceiling
-    result["clock_source"] = clock.source
 
     # ------------------------------------------------------ CPU baseline ----
     if args.cpu_baseline and args.headline:
@@ -313,7 +223,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def headline(args, fq, torch, xs, stream, clock, n):
+def headline(args, fq, torch, xs, stream, n):
     dev = "cuda"
     E4, E5 = fq.E4M3FN, fq.E5M2
     T = len(xs)
@@ -346,7 +256,6 @@ def headline(args, fq, torch, xs, stream, clock, n):
     # costs the GPU several microseconds per step on its own.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    clock.start()
     wall0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
@@ -354,7 +263,6 @@ def headline(args, fq, torch, xs, stream, clock, n):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    sclk = clock.stop()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
     bytes_per_step = 3 * n
@@ -369,7 +277,7 @@ def headline(args, fq, torch, xs, stream, clock, n):
                                "amax history 16 (max), fused input amax",
                    "tensor": [rows, cols], "history_len": 16, "distinct_inputs": T, "distinct_outputs": NQ,
                    "bytes_per_step": bytes_per_step, "host_wall_s": round(wall, 4),
-                   "step_ms_p10_p50_p90": [spread["ms_p10"], spread["ms"], spread["ms_p90"]], "sclk": sclk},
+                   "step_ms_p10_p50_p90": [spread["ms_p10"], spread["ms"], spread["ms_p90"]]},
         "roofline": {"kernel": "fp8_quantize_delayed: cast_kernel (fused amax) + delayed_kernel",
                      "bound": "hbm", "achieved": round(value, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
@@ -378,7 +286,7 @@ def headline(args, fq, torch, xs, stream, clock, n):
     }
 
 
-def time_rows(fq, torch, np, workloads, to_dev, xs, stream, clock, only, with_cpu):
+def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
     """Every row of the path at its own workload.  Returns (rows, copy ceiling)."""
     import oracle
     dev = "cuda"
@@ -415,10 +323,6 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, clock, only, with_cp
         tf = flop / (t["ms"] * 1e-3) / 1e12
         row = dict(t)
         row.update({"TFLOP/s": round(tf, 1), "frac_mfma": round(tf / FP8_MFMA_PEAK_TFLOPS, 4), "flop": int(flop)})
-        if t.get("sclk"):
-            peak = FP8_MFMA_PEAK_TFLOPS * t["sclk"]["mean_mhz"] / MFMA_PEAK_SCLK_MHZ
-            row["mfma_peak_at_sclk_tflops"] = round(peak, 1)
-            row["frac_mfma_at_sclk"] = round(tf / peak, 4)
         if cpu is not None:
             row["cpu"] = cpu
         out[name] = row
@@ -665,7 +569,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, clock, only, with_cp
         B = codes((8192, 8192), E4)
         C = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
         t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm(A, E4, s1, B, E4, s1, fq.PER_TENSOR, C, cam,
-                                                                       stream=stream), 4, clock=clock)
+                                                                       stream=stream), 4)
         mfma(name, 2 * 8192 ** 3, t, gemm_cpu(8192, 8192, 8192, oracle.E4M3FN, oracle.E4M3FN, oracle.PER_TENSOR, 512))
         del A, B, C
 
@@ -682,7 +586,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, clock, only, with_cp
         sx = torch.rand((4096, 32), device=dev, generator=g) + 0.5
         sw = torch.rand((112, 32), device=dev, generator=g) + 0.5
         t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm(Xq, E4, sx, Wq, E4, sw, fq.BLOCK_1x128_128x128,
-                                                                       Y, cam, stream=stream), 4, clock=clock)
+                                                                       Y, cam, stream=stream), 4)
         mfma(name, 2 * 4096 * 14336 * 4096, t,
              gemm_cpu(4096, 14336, 4096, oracle.E4M3FN, oracle.E4M3FN, oracle.BLOCK_1x128_128x128, 256))
     name = "gemm_block_dgrad_4096x4096x14336"
@@ -694,7 +598,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, clock, only, with_cp
         dX = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
         t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm(dYq, E5, sdy, Wtq, E4, swt,
                                                                        fq.BLOCK_1x128_128x128, dX, cam,
-                                                                       stream=stream), 4, clock=clock)
+                                                                       stream=stream), 4)
         mfma(name, 2 * 4096 * 4096 * 14336, t,
              gemm_cpu(4096, 4096, 14336, oracle.E5M2, oracle.E4M3FN, oracle.BLOCK_1x128_128x128, 256))
         del dYq, Wtq, dX
@@ -709,12 +613,12 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, clock, only, with_cp
         H = torch.empty((4096, 14336), dtype=torch.uint8, device=dev)
         if want(names_fc1[0]):
             t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm(Xq, E4, s1, Wq, E4, s1, fq.PER_TENSOR, Y,
-                                                                           cam, stream=stream), 4, clock=clock)
+                                                                           cam, stream=stream), 4)
             mfma(names_fc1[0], 2 * 4096 * 14336 * 4096, t)
         if want(names_fc1[1]):
             t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm_fused(
                 Xq, E4, s1, Wq, E4, s1, fq.PER_TENSOR, H, bias=bias, act=fq.ACT_GELU, out_fmt=E4, c_scale_inv=s_h,
-                amax_out=cam, stream=stream), 4, clock=clock)
+                amax_out=cam, stream=stream), 4)
             mfma(names_fc1[1], 2 * 4096 * 14336 * 4096, t)
         del H, bias
     del Xq, Wq
@@ -730,7 +634,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, clock, only, with_cp
         dW = torch.empty((14336, 4096), dtype=torch.float32, device=dev)
         t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm(dYt, E5, sdyt, Xt, E4, sxt,
                                                                        fq.BLOCK_1x128_1x128, dW, cam, stream=stream),
-                          4, clock=clock)
+                          4)
         mfma(name, 2 * 14336 * 4096 * 4096, t,
              gemm_cpu(14336, 4096, 4096, oracle.E5M2, oracle.E4M3FN, oracle.BLOCK_1x128_1x128, 512))
         del dYt, Xt, dW
@@ -751,7 +655,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, clock, only, with_cp
         Bm, sBm = mx_codes((8192, 8192))
         Cm = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
         t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm(Am, E4, sAm, Bm, E4, sBm, fq.MXFP8, Cm, cam,
-                                                                       stream=stream), 4, clock=clock)
+                                                                       stream=stream), 4)
         mfma(name, 2 * 8192 ** 3, t, gemm_cpu(8192, 8192, 8192, oracle.E4M3FN, oracle.E4M3FN, oracle.MXFP8, 512))
     return out, ceiling
 
