@@ -22,7 +22,10 @@ rows) is timed at its own workload size under "rows": the median and the
 back-to-back launches between two events, taken after 150 ms of untimed
 launches of the same call.  Memory-bound rows report GB/s against the 8 TB/s
 peak and against a device copy measured in the same run; GEMM rows report
-TFLOP/s against the 5.0 PFLOP/s FP8 peak.  Each row carries the CPU oracle's
+TFLOP/s against the 5.0 PFLOP/s FP8 peak and against that peak scaled to
+the graphics clock the row runs at ("sclk": measured on the device by the
+library's clock monitor, which shares CUs with an untimed batch of the same
+launches right after the timed samples).  Each row carries the CPU oracle's
 rate on the same workload ("cpu"), a baseline only.
 
 The CPU oracle's delayed-scaling schedule is the headline's "cpu_baseline".
@@ -39,6 +42,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 FP8_MFMA_PEAK_TFLOPS = 5000.0
+MFMA_PEAK_SCLK_MHZ = 2400.0  # the clock the 5.0 PFLOP/s figure assumes (256 CUs x 8192 FP8 flop/clk)
 # HBM bytes of one delayed step (cast_kernel + delayed_kernel), from the
 # FETCH_SIZE and WRITE_SIZE counters scaled by the factors a plain copy gives
 # (profiles/delayed_step_8192x8192_bf16_hbm_traffic.md); None whenever either
@@ -99,10 +103,39 @@ def _pct(values, q):
     return s[lo] + (s[hi] - s[lo]) * (pos - lo)
 
 
-def time_launches(torch, stream, fn, per_sample, rotate=1, samples=SAMPLES):
+_SIDE = []
+
+
+def measure_clock(torch, fq, fn, rotate, ms_per_launch, target_ms=30.0):
+    """Graphics clock (MHz, per XCD) while fn runs back to back: an untimed
+    batch of about target_ms of launches on the current stream, measured by the
+    library's clock monitor, which runs on a side stream (default priority)
+    on CUs it shares with the batch until a stop word, set on the current
+    stream behind the batch, ends it.  None when the monitor did not see the
+    stop word."""
+    if not _SIDE:
+        _SIDE.append(torch.cuda.Stream())
+    out = torch.zeros(3 * fq.CLOCK_BLOCKS + 1, dtype=torch.int64, device="cuda")
+    stop = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    fq.fp8q_clock_monitor(out, stop, stream=_SIDE[0])
+    for i in range(max(8, int(target_ms / max(ms_per_launch, 1e-3)))):
+        fn(i % rotate)
+    stop.fill_(1)
+    torch.cuda.synchronize()
+    mhz = fq.clock_mhz(out.cpu().tolist())
+    if not mhz:
+        return None
+    v = list(mhz.values())
+    return {"mean_mhz": round(sum(v) / len(v), 1), "min_mhz": round(min(v), 1), "max_mhz": round(max(v), 1),
+            "xcds": len(v)}
+
+
+def time_launches(torch, stream, fn, per_sample, rotate=1, samples=SAMPLES, fq=None):
     """ms per launch of fn(i): after WARM_S seconds of untimed launches,
     `samples` samples of `per_sample` back-to-back launches, each sample
-    between two events on `stream`.  Returns median, p10 and p90."""
+    between two events on `stream`.  Returns median, p10 and p90, and (given
+    the library module fq) the graphics clock of a further untimed batch."""
     i, t0 = 0, time.perf_counter()
     while True:
         fn(i % rotate)
@@ -121,8 +154,11 @@ def time_launches(torch, stream, fn, per_sample, rotate=1, samples=SAMPLES):
         ev[k + 1].record(stream)
     torch.cuda.synchronize()
     ms = [ev[k].elapsed_time(ev[k + 1]) / per_sample for k in range(samples)]
-    return {"ms": round(_pct(ms, 0.5), 5), "ms_p10": round(_pct(ms, 0.1), 5), "ms_p90": round(_pct(ms, 0.9), 5),
-            "samples": samples, "launches_per_sample": per_sample}
+    r = {"ms": round(_pct(ms, 0.5), 5), "ms_p10": round(_pct(ms, 0.1), 5), "ms_p90": round(_pct(ms, 0.9), 5),
+         "samples": samples, "launches_per_sample": per_sample}
+    if fq is not None:
+        r["sclk"] = measure_clock(torch, fq, lambda j: fn((i + j) % rotate), rotate, r["ms"])
+    return r
 
 
 def cpu_rate(fn, units, unit, budget_s=3.0, reps=3):
@@ -269,7 +305,7 @@ def headline(args, fq, torch, xs, stream, n):
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     # the spread of the step time: 50 samples of 8 steps each, after the
     # timed region (the state machine just continues)
-    spread = time_launches(torch, stream, step, 8)
+    spread = time_launches(torch, stream, step, 8, fq=fq)
     return {
         "value": round(value, 1),
         "ms_per_step": round(ms_per_step, 5),
@@ -277,7 +313,8 @@ def headline(args, fq, torch, xs, stream, n):
                                "amax history 16 (max), fused input amax",
                    "tensor": [rows, cols], "history_len": 16, "distinct_inputs": T, "distinct_outputs": NQ,
                    "bytes_per_step": bytes_per_step, "host_wall_s": round(wall, 4),
-                   "step_ms_p10_p50_p90": [spread["ms_p10"], spread["ms"], spread["ms_p90"]]},
+                   "step_ms_p10_p50_p90": [spread["ms_p10"], spread["ms"], spread["ms_p90"]],
+                   "sclk": spread.get("sclk")},
         "roofline": {"kernel": "fp8_quantize_delayed: cast_kernel (fused amax) + delayed_kernel",
                      "bound": "hbm", "achieved": round(value, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
@@ -298,6 +335,10 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
 
     def want(name):
         return not only or name in only
+
+    def timed(fn, per_sample, rotate=1):
+        # every row also reports the graphics clock of an untimed batch
+        return time_launches(torch, stream, fn, per_sample, rotate, fq=fq)
 
     # the device copy ceiling of this run: torch's copy of 128 MiB buffers,
     # eight pairs in rotation (2 GiB), read + written bytes per second
@@ -323,6 +364,11 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
         tf = flop / (t["ms"] * 1e-3) / 1e12
         row = dict(t)
         row.update({"TFLOP/s": round(tf, 1), "frac_mfma": round(tf / FP8_MFMA_PEAK_TFLOPS, 4), "flop": int(flop)})
+        if t.get("sclk"):
+            # the FP8 peak scales with the graphics clock the row ran at
+            peak = FP8_MFMA_PEAK_TFLOPS * t["sclk"]["mean_mhz"] / MFMA_PEAK_SCLK_MHZ
+            row["mfma_peak_at_sclk_tflops"] = round(peak, 1)
+            row["frac_mfma_at_sclk"] = round(tf / peak, 4)
         if cpu is not None:
             row["cpu"] = cpu
         out[name] = row
@@ -353,7 +399,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
             fq.fp8_amax(x1, am, stream=stream)
             fq.fp8_quantize_tensor(x1, E4, q1, amax_in=am, margin=1, scale_inv_out=s1o, stream=stream)
             fq.fp8_dequantize(q1, E4, s1o, y1, stream=stream)
-        t = time_launches(torch, stream, cfg1, 16)
+        t = timed(cfg1, 16)
 
         def cfg1_cpu():
             r = oracle.quantize_tensor(x1h, oracle.E4M3FN, amax_in=oracle.amax(x1h), margin=1)
@@ -363,7 +409,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
         codes = torch.arange(256, dtype=torch.int32, device=dev).to(torch.uint8)
         one = torch.ones(1, device=dev)
         tab = torch.empty(256, device=dev)
-        t = time_launches(torch, stream, lambda i: fq.fp8_dequantize(codes, i % 2, one, tab, stream=stream), 16)
+        t = timed(lambda i: fq.fp8_dequantize(codes, i % 2, one, tab, stream=stream), 16)
         out["decode_tables_256_codes"] = dict(t, note="dequantize of the 256 codes with scale 1, alternating formats")
 
     # outputs rotate over sets totalling at least 512 MiB, like the inputs, so
@@ -373,7 +419,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
     # a1 amax over bf16 8192^2 (2 B/elem)
     name = "amax_bf16_8192x8192"
     if want(name):
-        t = time_launches(torch, stream, lambda i: fq.fp8_amax(xs[i], am, stream=stream), 16, rotate=len(xs))
+        t = timed(lambda i: fq.fp8_amax(xs[i], am, stream=stream), 16, rotate=len(xs))
         hbm(name, 2 * n, t, cpu(lambda: oracle.amax(host_x()), 2 * n / 1e9, "GB/s"))
 
     # a1+a2+a3 current scaling: amax pass + cast pass (5 B/elem)
@@ -382,7 +428,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
         def current(i):
             fq.fp8_amax(xs[i], am, stream=stream)
             fq.fp8_quantize_tensor(xs[i], E4, qs8[i % 8], amax_in=am, margin=0, scale_inv_out=si, stream=stream)
-        t = time_launches(torch, stream, current, 8, rotate=len(xs))
+        t = timed(current, 8, rotate=len(xs))
         hbm(name, 5 * n, t, cpu(lambda: oracle.quantize_tensor(host_x(), oracle.E4M3FN, amax_in=oracle.amax(host_x())),
                                 5 * n / 1e9, "GB/s"))
 
@@ -390,7 +436,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
     sc1 = torch.full((1,), 0.01, device=dev)
     name = "cast_given_scale_bf16_8192x8192"
     if want(name):
-        t = time_launches(torch, stream, lambda i: fq.fp8_quantize_tensor(xs[i], E4, qs8[i % 8], scale_inv_in=sc1,
+        t = timed(lambda i: fq.fp8_quantize_tensor(xs[i], E4, qs8[i % 8], scale_inv_in=sc1,
                                                                           stream=stream), 16, rotate=len(xs))
         hbm(name, 3 * n, t, cpu(lambda: oracle.quantize(host_x(), oracle.E4M3FN, np.float32(100.0)), 3 * n / 1e9,
                                 "GB/s"))
@@ -402,7 +448,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
         for c in qs8:
             c.random_(0, 256)
         si.fill_(0.01)
-        t = time_launches(torch, stream, lambda i: fq.fp8_dequantize(qs8[i], E4, si, ys[i % 2], stream=stream), 16,
+        t = timed(lambda i: fq.fp8_dequantize(qs8[i], E4, si, ys[i % 2], stream=stream), 16,
                           rotate=8)
         hq = np.random.default_rng(0).integers(0, 256, n, dtype=np.uint8)
         hbm(name, 5 * n, t, cpu(lambda: oracle.dequantize(hq, oracle.E4M3FN, np.float32(0.01)), 5 * n / 1e9, "GB/s"))
@@ -414,7 +460,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
     x2 = [x.view(8192, 8192) for x in xs]
     name = "rowwise_colwise_bf16_8192x8192"
     if want(name):
-        t = time_launches(torch, stream, lambda i: fq.fp8_quantize_rowwise_colwise(
+        t = timed(lambda i: fq.fp8_quantize_rowwise_colwise(
             x2[i], E4, q_row=qr[i % 4], q_col=qc[i % 4], scale_inv_in=sc1, stream=stream), 16, rotate=len(xs))
         hbm(name, 4 * n, t, cpu(lambda: oracle.quantize_rowwise_colwise(host_x(), oracle.E4M3FN, np.float32(100.0)),
                                 4 * n / 1e9, "GB/s"))
@@ -432,7 +478,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
             Ws = [(W * (1 + 0.01 * k)).to(torch.bfloat16) for k in range(10)]
             del W
             sw, swt = torch.empty((56, 32), device=dev), torch.empty((32, 56), device=dev)
-            t = time_launches(torch, stream, lambda i: fq.fp8_quantize_block(Ws[i], E4, 128, qw[i], sw, qwt[i], swt,
+            t = timed(lambda i: fq.fp8_quantize_block(Ws[i], E4, 128, qw[i], sw, qwt[i], swt,
                                                                              stream=stream), 16, rotate=len(Ws))
             hw = workloads.block_weight() if with_cpu else None
             hbm(name_w, 4 * nW + 2 * 4 * (nW // 16384), t,
@@ -445,7 +491,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
             qx = [q.view(4096, 7168) for q in qw]
             qxt = [q.view(7168, 4096) for q in qwt]
             sx, sxt = torch.empty((4096, 56), device=dev), torch.empty((7168, 32), device=dev)
-            t = time_launches(torch, stream, lambda i: fq.fp8_quantize_block(Xs[i], E4, 1, qx[i], sx, qxt[i], sxt,
+            t = timed(lambda i: fq.fp8_quantize_block(Xs[i], E4, 1, qx[i], sx, qxt[i], sxt,
                                                                              stream=stream), 16, rotate=len(Xs))
             ha = workloads.block_act() if with_cpu else None
             hbm(name_x, 4 * nW + 4 * (nW // 128) * 2, t,
@@ -459,7 +505,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
     if want(name):
         sm = [torch.empty((8192, 256), dtype=torch.uint8, device=dev) for _ in range(4)]
         smt = [torch.empty((8192, 256), dtype=torch.uint8, device=dev) for _ in range(4)]
-        t = time_launches(torch, stream, lambda i: fq.fp8_quantize_mx(x2[i], E4, qr[i % 4], sm[i % 4], qc[i % 4],
+        t = timed(lambda i: fq.fp8_quantize_mx(x2[i], E4, qr[i % 4], sm[i % 4], qc[i % 4],
                                                                       smt[i % 4], stream=stream), 16, rotate=len(xs))
 
         def mx_cpu():
@@ -475,7 +521,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
     if want(name):
         fq.fp8_amax(x2[0], am, stream=stream)
         rsi, csi = torch.empty(1, device=dev), torch.empty(1, device=dev)
-        t = time_launches(torch, stream, lambda i: fq.fp8_quantize_hybrid(
+        t = timed(lambda i: fq.fp8_quantize_hybrid(
             x2[i], E4, E5, fq.COLSRC_ROWWISE_DEQUANTIZED, q_row=qr[i % 4], q_col=qc[i % 4], amax_in=am,
             row_scale_inv_out=rsi, col_scale_inv_out=csi, stream=stream), 16, rotate=len(xs))
 
@@ -491,13 +537,13 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
     st = torch.empty(4, dtype=torch.int64, device=dev)
     name = "cast_stats_bf16_8192x8192"
     if want(name):
-        t = time_launches(torch, stream, lambda i: fq.fp8_cast_stats(xs[i], E4, sc1, st, stream=stream), 16,
+        t = timed(lambda i: fq.fp8_cast_stats(xs[i], E4, sc1, st, stream=stream), 16,
                           rotate=len(xs))
         hbm(name, 2 * n, t, cpu(lambda: oracle.cast_stats(host_x(), oracle.E4M3FN, np.float32(0.01)), 2 * n / 1e9,
                                 "GB/s"))
     name = "cast_with_fused_stats_bf16_8192x8192"
     if want(name):
-        t = time_launches(torch, stream, lambda i: fq.fp8_quantize_tensor_stats(xs[i], E4, qs8[i % 8], st,
+        t = timed(lambda i: fq.fp8_quantize_tensor_stats(xs[i], E4, qs8[i % 8], st,
                                                                                 scale_inv_in=sc1, stream=stream),
                           16, rotate=len(xs))
 
@@ -512,7 +558,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
     if want(name):
         res = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(2)]
         s_ef = torch.full((1,), 2.0 ** -16, device=dev)
-        t = time_launches(torch, stream, lambda i: fq.fp8_quantize_error_feedback(xs[i], res[i % 2], E5, s_ef,
+        t = timed(lambda i: fq.fp8_quantize_error_feedback(xs[i], res[i % 2], E5, s_ef,
                                                                                   qs8[i % 8], am, stream=stream),
                           8, rotate=len(xs))
         hres = np.zeros(n, np.float32) if with_cpu else None
@@ -568,7 +614,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
         A = codes((8192, 8192), E4)
         B = codes((8192, 8192), E4)
         C = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
-        t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm(A, E4, s1, B, E4, s1, fq.PER_TENSOR, C, cam,
+        t = timed(lambda i: fq.fp8_scaled_gemm(A, E4, s1, B, E4, s1, fq.PER_TENSOR, C, cam,
                                                                        stream=stream), 4)
         mfma(name, 2 * 8192 ** 3, t, gemm_cpu(8192, 8192, 8192, oracle.E4M3FN, oracle.E4M3FN, oracle.PER_TENSOR, 512))
         del A, B, C
@@ -585,7 +631,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
     if want(name):
         sx = torch.rand((4096, 32), device=dev, generator=g) + 0.5
         sw = torch.rand((112, 32), device=dev, generator=g) + 0.5
-        t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm(Xq, E4, sx, Wq, E4, sw, fq.BLOCK_1x128_128x128,
+        t = timed(lambda i: fq.fp8_scaled_gemm(Xq, E4, sx, Wq, E4, sw, fq.BLOCK_1x128_128x128,
                                                                        Y, cam, stream=stream), 4)
         mfma(name, 2 * 4096 * 14336 * 4096, t,
              gemm_cpu(4096, 14336, 4096, oracle.E4M3FN, oracle.E4M3FN, oracle.BLOCK_1x128_128x128, 256))
@@ -596,7 +642,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
         sdy = torch.rand((4096, 112), device=dev, generator=g) + 0.5
         swt = torch.rand((32, 112), device=dev, generator=g) + 0.5
         dX = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
-        t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm(dYq, E5, sdy, Wtq, E4, swt,
+        t = timed(lambda i: fq.fp8_scaled_gemm(dYq, E5, sdy, Wtq, E4, swt,
                                                                        fq.BLOCK_1x128_128x128, dX, cam,
                                                                        stream=stream), 4)
         mfma(name, 2 * 4096 * 4096 * 14336, t,
@@ -612,11 +658,11 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
         s_h = torch.full((1,), 6.0 / 448, device=dev)
         H = torch.empty((4096, 14336), dtype=torch.uint8, device=dev)
         if want(names_fc1[0]):
-            t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm(Xq, E4, s1, Wq, E4, s1, fq.PER_TENSOR, Y,
+            t = timed(lambda i: fq.fp8_scaled_gemm(Xq, E4, s1, Wq, E4, s1, fq.PER_TENSOR, Y,
                                                                            cam, stream=stream), 4)
             mfma(names_fc1[0], 2 * 4096 * 14336 * 4096, t)
         if want(names_fc1[1]):
-            t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm_fused(
+            t = timed(lambda i: fq.fp8_scaled_gemm_fused(
                 Xq, E4, s1, Wq, E4, s1, fq.PER_TENSOR, H, bias=bias, act=fq.ACT_GELU, out_fmt=E4, c_scale_inv=s_h,
                 amax_out=cam, stream=stream), 4)
             mfma(names_fc1[1], 2 * 4096 * 14336 * 4096, t)
@@ -632,7 +678,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
         sdyt = torch.rand((14336, 32), device=dev, generator=g) + 0.5
         sxt = torch.rand((4096, 32), device=dev, generator=g) + 0.5
         dW = torch.empty((14336, 4096), dtype=torch.float32, device=dev)
-        t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm(dYt, E5, sdyt, Xt, E4, sxt,
+        t = timed(lambda i: fq.fp8_scaled_gemm(dYt, E5, sdyt, Xt, E4, sxt,
                                                                        fq.BLOCK_1x128_1x128, dW, cam, stream=stream),
                           4)
         mfma(name, 2 * 14336 * 4096 * 4096, t,
@@ -654,7 +700,7 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
         Am, sAm = mx_codes((8192, 8192))
         Bm, sBm = mx_codes((8192, 8192))
         Cm = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
-        t = time_launches(torch, stream, lambda i: fq.fp8_scaled_gemm(Am, E4, sAm, Bm, E4, sBm, fq.MXFP8, Cm, cam,
+        t = timed(lambda i: fq.fp8_scaled_gemm(Am, E4, sAm, Bm, E4, sBm, fq.MXFP8, Cm, cam,
                                                                        stream=stream), 4)
         mfma(name, 2 * 8192 ** 3, t, gemm_cpu(8192, 8192, 8192, oracle.E4M3FN, oracle.E4M3FN, oracle.MXFP8, 512))
     return out, ceiling

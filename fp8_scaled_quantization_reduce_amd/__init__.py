@@ -52,6 +52,7 @@ SIGNATURES = {
                             _VP, _VP],
     "fp8_cast_stats": [_VP, _I32, _I64, _I32, _VP, _VP, _VP],
     "fp8_quantize_error_feedback": [_VP, _I32, _VP, _I64, _I32, _VP, _VP, _VP, _VP],
+    "fp8q_clock_monitor": [_VP, _VP, _VP],
     "fp8q_last_error": [],
 }
 
@@ -387,3 +388,33 @@ def fp8_quantize_error_feedback(g, residual, fmt, scale_inv, q, amax_out=None, s
     _check(lib.fp8_quantize_error_feedback(_ptr(g, "g"), _dtype(g), _ptr(residual, "residual"), g.numel(), fmt,
                                            _ptr(scale_inv, "scale_inv"), _ptr(q, "q"), _ptr(amax_out, "amax_out"),
                                            _stream(stream)))
+
+
+CLOCK_BLOCKS = 8
+CLOCK_MONITOR_SECONDS = 2
+
+
+def fp8q_clock_monitor(out, stop, stream=None):
+    """Enqueue the clock monitor (a measurement aid): out (int64 [25] on the
+    device) receives, per block b, the XCD id, the shader-clock cycles and
+    the constant-rate ticks from the kernel's start until stop (int32 [1] on
+    the device) becomes nonzero; out[24] = the constant rate in kHz."""
+    _need(out, "out", _STATS, 3 * CLOCK_BLOCKS + 1)
+    _need(stop, "stop", (torch.int32,), 1)
+    _check(lib.fp8q_clock_monitor(_ptr(out, "out"), _ptr(stop, "stop"), _stream(stream)))
+
+
+def clock_mhz(sample):
+    """{xcd: MHz} from a host copy of a clock-monitor output (an XCD measured
+    by several blocks keeps their mean); None for a monitor that ran into its
+    time limit instead of seeing stop."""
+    khz = int(sample[3 * CLOCK_BLOCKS])
+    if khz <= 0:
+        return None
+    acc = {}
+    for b in range(CLOCK_BLOCKS):
+        cycles, ticks = int(sample[3 * b + 1]), int(sample[3 * b + 2])
+        if ticks >= khz * 1000 * CLOCK_MONITOR_SECONDS or cycles <= 0 or ticks <= 0:
+            return None
+        acc.setdefault(int(sample[3 * b]), []).append(cycles / (ticks / (khz * 1e3)) / 1e6)
+    return {x: sum(v) / len(v) for x, v in sorted(acc.items())}

@@ -236,6 +236,22 @@ fp8q::ScaleSrc make_src(const float *amax_in, int32_t margin, const float *scale
 
 extern "C" const char *fp8q_last_error(void) { return g_err; }
 
+static int fp8q_clock_monitor_impl(uint64_t *out, const uint32_t *stop, void *stream)
+{
+    const char *fn = "fp8q_clock_monitor";
+    if (!out || !aligned(out, 8)) return fail(FP8Q_EINVAL, "%s: out must be an 8-byte aligned pointer", fn);
+    if (!stop || !aligned(stop, 4)) return fail(FP8Q_EINVAL, "%s: stop must be a 4-byte aligned pointer", fn);
+    if (overlap(out, 8 * (3 * fp8q::kClockBlocks + 1), stop, 4))
+        return fail(FP8Q_EINVAL, "%s: stop overlaps out", fn);
+    return hip_status(fp8q::launch_clock_monitor(out, stop, (hipStream_t)stream), fn);
+}
+
+extern "C" int fp8q_clock_monitor(uint64_t *out, const uint32_t *stop, void *stream)
+{
+    Call c("fp8q_clock_monitor", stream);
+    return c.ret(fp8q_clock_monitor_impl(out, stop, stream));
+}
+
 static int fp8_amax_impl(Call &c, const void *x, int32_t dtype, int64_t n, float *amax, void *stream)
 {
     const char *fn = "fp8_amax";

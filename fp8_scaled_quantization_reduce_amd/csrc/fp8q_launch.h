@@ -41,6 +41,15 @@ constexpr int kScratchSlots = 64;
 // Enqueue the zeroing of one scratch slot (after a failed call left it dirty).
 hipError_t launch_clear_scratch(GridScratch *gs, hipStream_t s);
 
+// Graphics clock of the CUs that run kClockBlocks one-wave blocks next to
+// other work (consecutive blocks start on consecutive XCDs), from when the
+// kernel starts until *stop is nonzero (at most kClockMonitorSeconds):
+// out[3 b + 0, 1, 2] = XCD id, shader-clock cycles, constant-rate ticks of
+// block b; out[3 kClockBlocks] = the constant rate in kHz.
+constexpr int kClockBlocks = 8;
+constexpr int kClockMonitorSeconds = 2;
+hipError_t launch_clock_monitor(uint64_t *out, const uint32_t *stop, hipStream_t s);
+
 // Where a per-tensor scale comes from: exactly one pointer is non-null.
 struct ScaleSrc {
     const float *amax_in;      // current scaling from this amax

@@ -116,6 +116,46 @@ hipError_t launch_clear_scratch(GridScratch *gs, hipStream_t s)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------- clock monitor --
+// One wave per block measures the graphics clock of the CU it shares with
+// other work: it reads the shader-clock counter (s_memtime, counts the CU's
+// clock) and the constant-rate counter (s_memrealtime), then polls the stop
+// word with agent-scope loads (which see a store made by a kernel that has
+// finished on any XCD), sleeping briefly between polls, until the word is
+// nonzero or `max_ticks` constant-rate ticks have passed (so the loop always
+// ends), and reads both counters again.  Lanes 0, 1, 2 store the XCD id
+// (HW_REG_XCC_ID bits 3:0) and the two deltas; block 0's lane 3 stores the
+// constant rate in kHz.  Stores are per-lane vector stores.
+__global__ __launch_bounds__(64) void clock_monitor_kernel(uint64_t *__restrict__ out, const uint32_t *stop,
+                                                           uint64_t wall_khz, uint64_t max_ticks)
+{
+    const uint64_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20);
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        if (__builtin_amdgcn_s_memrealtime() - r0 >= max_ticks) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    const int lane = threadIdx.x;
+    const uint64_t v = lane == 0 ? xcc : lane == 1 ? t1 - t0 : lane == 2 ? r1 - r0 : wall_khz;
+    if (lane < 3 || (lane == 3 && blockIdx.x == 0)) out[lane < 3 ? 3 * blockIdx.x + lane : 3 * kClockBlocks] = v;
+}
+
+hipError_t launch_clock_monitor(uint64_t *out, const uint32_t *stop, hipStream_t s)
+{
+    int dev = 0, khz = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (e != hipSuccess) return e;
+    if (khz <= 0) return hipErrorInvalidValue;
+    // at most kClockMonitorSeconds of the constant-rate counter
+    clock_monitor_kernel<<<kClockBlocks, 64, 0, s>>>(out, stop, (uint64_t)khz,
+                                                     (uint64_t)khz * 1000 * kClockMonitorSeconds);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ amax --
 // amax = max |x| ("Megatron FP8", section 4).  Each lane reads U 16-byte
 // vectors of its unit, kThreads vectors apart (so every load instruction of a

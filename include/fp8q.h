@@ -370,6 +370,28 @@ int fp8_cast_stats(const void *x, int32_t dtype, int64_t n, int32_t fmt, const f
 int fp8_quantize_error_feedback(const void *g, int32_t dtype, float *residual, int64_t n, int32_t fmt,
                                 const float *scale_inv, uint8_t *q, float *amax_out, void *stream);
 
+/*
+ * fp8q_clock_monitor -- a measurement aid, not a step of the method: the
+ * graphics clock that other work runs at.  Enqueues on `stream` one kernel of
+ * 8 one-wave blocks (consecutive blocks start on consecutive XCDs; each needs
+ * only a few registers, so it shares a CU with the work being measured).
+ * Each block counts its CU's shader-clock cycles and the chip's constant-rate
+ * ticks from its start until *stop is nonzero, or 2 seconds of the constant
+ * counter, whichever comes first.  cycles / (ticks / rate) is the CU's average
+ * clock over that interval.  Use: zero *stop, enqueue this on a side stream,
+ * enqueue the work on another stream, then make *stop nonzero from a kernel
+ * on the work's stream (the blocks read it with agent-scope loads) and
+ * synchronize.
+ * out: device uint64[25], 8-byte aligned, written when the kernel ends:
+ *   out[3 b + 0] XCD id of block b (b = 0..7), out[3 b + 1] shader-clock
+ *   cycles, out[3 b + 2] constant-rate ticks, out[24] the constant rate in
+ *   kHz.
+ * stop: device uint32, 4-byte aligned, read only.
+ * Errors: FP8Q_EINVAL for a null, misaligned or overlapping pointer;
+ * FP8Q_EHIP from the launch.  Uses no scratch.
+ */
+int fp8q_clock_monitor(uint64_t *out, const uint32_t *stop, void *stream);
+
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char *fp8q_last_error(void);
 
