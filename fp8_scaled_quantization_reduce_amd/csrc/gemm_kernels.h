@@ -300,9 +300,12 @@ __device__ __forceinline__ v8i read_frag32_mx(const uint8_t *lds, int r, int g, 
 // With kMX (MXFP8), sA and sB point to E8M0 scale bytes, [M][K/32] and
 // [N][K/32]: every 32-element K block of a row carries a power of two that the
 // matrix instruction applies itself (v_mfma_scale_f32_32x32x64_f8f6f4 takes one
-// scale byte per lane, for the 32 K bytes that lane holds).  Each stage also
-// carries the slice's four scale bytes of every A and B row (one dword per row,
-// loaded straight into LDS with the codes).
+// scale byte per lane, for the 32 K bytes that lane holds).  The scales come
+// in groups of four slices: 16 bytes of every A and B row, loaded straight
+// into LDS ([row][4 dwords], two groups in flight) by loads in which four
+// lanes cover one row's 16 bytes, so each load touches 16 rows instead of 64
+// (a load per slice of one scale dword per row, 64 rows apart in memory, kept
+// the address unit busy and the slice's wait long).
 // kBN = 256: a 256x256 tile per block (grid block b -> grouped tile
 // xcd_order(b, n_main)); kBN = 128: half a tile, wave tiles 128x64 (grid
 // block b -> half b & 1 of grouped tile tile_base + b / 2), for a last wave of
@@ -320,10 +323,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     constexpr int kTJ = kWN / 32; // its 32-wide column tiles
     __shared__ __attribute__((aligned(1024))) uint8_t st0[kPTStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[kPTStageBytes];
-    __shared__ __attribute__((aligned(16))) uint32_t sx0[kMX ? 2 * kBM : 1]; // A rows' then B rows' scale dwords
-    __shared__ __attribute__((aligned(16))) uint32_t sx1[kMX ? 2 * kBM : 1];
+    // MXFP8: the scale dwords of an even and of an odd group of four slices
+    // (two LDS objects, like the stages), each A rows' then B rows' [row][4]
+    constexpr int kSxGroup = 2 * kBM * 4;
+    __shared__ __attribute__((aligned(16))) uint32_t sxe[kMX ? kSxGroup : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t sxo[kMX ? kSxGroup : 1];
     __shared__ uint32_t red[kGemmThreads / 64];
-    constexpr int kStageLoads = 8 + kBN / 32 + (kMX ? 2 : 0); // direct loads per lane per stage
+    constexpr int kStageLoads = 8 + kBN / 32; // direct loads per lane per stage
 
     int tm, tn;
     const int tilesM = (M + kBM - 1) / kBM, tilesN = (N + kBM - 1) / kBM;
@@ -355,9 +361,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
         kRawBufferWord3);
 
     // wave w loads rows 8(w + 4u), u = 0..7, of the A panel and u < kBN / 32
-    // of the B panel (16 or 12 loads of 1 KiB), and, MXFP8, the scale dwords
-    // of rows 64w .. 64w+63 of both panels (rows past the B panel read zero)
-    auto stage = [&](uint8_t *st, uint32_t *sx, int kb) {
+    // of the B panel (16 or 12 loads of 1 KiB)
+    auto stage = [&](uint8_t *st, int kb) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int row = 8 * (w + 4 * u);
@@ -367,12 +372,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + kBM * kBK + row * kBK), 16, voff,
                                                          row * K + kb * kBK, 0, 0);
         }
-        if constexpr (kMX) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxa, (lds_void *)(sx + 64 * w), 4, lane * kx,
-                                                     64 * w * kx + 4 * kb, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxb, (lds_void *)(sx + kBM + 64 * w), 4, lane * kx,
-                                                     64 * w * kx + 4 * kb, 0, 0);
+    };
+    // MXFP8 scale group g (slices 4g .. 4g+3) into sxe (g even) or sxo (g odd):
+    // wave w loads rows 64w .. 64w+63 of both panels, 16 rows per load, lane L
+    // the dword L % 4 of row L / 4 (bytes past a panel read zero; bytes past a
+    // row's last slice, of groups past the last one too, are never read)
+    const int sx_voff = (lane >> 2) * kx + 4 * (lane & 3);
+    constexpr int kScaleGroupLoads = 8; // loads per lane per scale group
+    auto scale_group_to = [&](uint32_t *dst, int g) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = 64 * w + 16 * q;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxa, (lds_void *)(dst + 4 * row), 4, sx_voff, row * kx + 16 * g,
+                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxb, (lds_void *)(dst + 4 * (kBM + row)), 4, sx_voff,
+                                                     row * kx + 16 * g, 0, 0);
         }
+    };
+    auto scale_group = [&](int g, bool odd) {
+        if constexpr (kMX) scale_group_to(odd ? sxo : sxe, g);
     };
 
     v16f acc[4][kTJ];
@@ -397,13 +415,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
         for (int i = 0; i < 4; ++i)
             a[i] = kMX ? read_frag32_mx(st, wm * 128 + 32 * i + fr, fg, h) : read_frag32(st, wm * 128 + 32 * i + fr, fg, h);
     };
-    auto read_scales = [&](const uint32_t *sx, uint32_t(&xa)[4], uint32_t(&xb)[kTJ]) {
-        if constexpr (kMX) {
+    // the scale dwords of slice kb (group kb / 4, dword kb % 4 of each row)
+    auto read_scales_from = [&](const uint32_t *sx, uint32_t(&xa)[4], uint32_t(&xb)[kTJ]) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xa[i] = sx[wm * 128 + 32 * i + fr] >> (8 * fg);
+        for (int i = 0; i < 4; ++i) xa[i] = sx[4 * (wm * 128 + 32 * i + fr)] >> (8 * fg);
 #pragma unroll
-            for (int j = 0; j < kTJ; ++j) xb[j] = sx[kBM + wn * kWN + 32 * j + fr] >> (8 * fg);
-        }
+        for (int j = 0; j < kTJ; ++j) xb[j] = sx[4 * (kBM + wn * kWN + 32 * j + fr)] >> (8 * fg);
+    };
+    // (odd: the group of slice kb is odd, so its dwords are in sxo)
+    auto read_scales = [&](int kb, bool odd, uint32_t(&xa)[4], uint32_t(&xb)[kTJ]) {
+        if constexpr (kMX) read_scales_from((odd ? sxo : sxe) + (kb & 3), xa, xb);
     };
     // half h of the slice whose scale dwords are xa / xb
     auto mfmas = [&](const v8i(&a)[4], const v8i(&b)[kTJ], const uint32_t(&xa)[4], const uint32_t(&xb)[kTJ], int h) {
@@ -426,9 +447,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
 
     // One slice in stage `cur` (the next one in `nxt`).  `full` = the slices
     // kb + 1 and kb + 2 both exist (no guards).
-    auto slice = [&](int kb, uint8_t *cur, uint32_t *sxc, const uint8_t *nxt, const uint32_t *sxn,
-                     const uint32_t(&xa)[4], const uint32_t(&xb)[kTJ], uint32_t(&xan)[4], uint32_t(&xbn)[kTJ],
-                     bool full) {
+    // MXFP8: slice kb = 8t + p has a fixed place p in the unrolled loop.  At
+    // p = 0 and 4 (the first slice of group g) it loads group g + 1 at its end
+    // (into the object group g is not in).  Those loads are then the youngest
+    // of the wave, and the wait of the next slice (p = 1, 5) lets them stay in
+    // flight; that slice reads only group g's object, so the compiler's wait
+    // insertion keeps the two apart.  The slice after it issues loads of its
+    // own, so its wait (like every other) is a full one: the group has about
+    // a slice and a half to arrive instead of half a slice.
+    auto slice = [&](int kb, int p, uint8_t *cur, const uint8_t *nxt, const uint32_t(&xa)[4],
+                     const uint32_t(&xb)[kTJ], uint32_t(&xan)[4], uint32_t(&xbn)[kTJ], bool full) {
+        const bool issue = kMX && (p & 3) == 0, relaxed = kMX && (p & 3) == 1;
         // half 0
         mfmas(fa0, fb0, xa, xb, 0);
         read_frags(cur, 1, fa1, fb1);
@@ -439,17 +468,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // LDS read
             }
         }
-        // sync: the next slice landed (this lane's loads, then every wave's)
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        // sync: the next slice landed (this lane's loads, then every wave's).
+        // MXFP8: the scale group issued at the end of the previous slice (the
+        // youngest kScaleGroupLoads loads) may stay in flight through this wait.
+        if (relaxed)
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(kScaleGroupLoads, 0));
+        else
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        // half 1
-        if (full || kb + 2 < nk) stage(cur, sxc, kb + 2);
+        // half 1: the next slice's scales first, while no direct load is in
+        // flight (the scale buffers are one LDS object whose group is chosen
+        // at run time, and the compiler's wait insertion would otherwise hold
+        // the reads for the stage loads issued below)
+        if (full || kb + 1 < nk) read_scales(kb + 1, (((p + 1) >> 2) & 1) != 0, xan, xbn);
+        if (full || kb + 2 < nk) stage(cur, kb + 2);
         mfmas(fa1, fb1, xa, xb, 1);
-        if (full || kb + 1 < nk) {
-            read_frags(nxt, 0, fa0, fb0);
-            read_scales(sxn, xan, xbn);
-        }
+        if (full || kb + 1 < nk) read_frags(nxt, 0, fa0, fb0);
         if (full) {
 #pragma unroll
             for (int t = 0; t < 4 * kTJ; ++t) {
@@ -458,6 +493,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global -> LDS load
             }
         }
+        // MXFP8: at the first slice of group g, group g + 1 goes into the
+        // object whose last reads (slice 4g - 1's scales, read during slice
+        // 4g - 2) every wave finished before this slice's barrier; its first
+        // reader is slice 4g + 3, after full waits.  Loaded also past the last
+        // group (reading zeros or unused bytes), so that the relaxed wait of
+        // the next slice holds in every tile.
+        if (issue) scale_group((kb >> 2) + 1, ((p >> 2) & 1) == 0);
     };
 
     // prologue: slices 0 and 1 in flight, slice 0's first-half fragments.
@@ -466,23 +508,49 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     // an unconditional pair the compiler's wait insertion keeps the two stages
     // apart and puts no full wait at the top of the loop.
     if (nk > 0) {
-        stage(st0, sx0, 0);
-        stage(st1, sx1, 1);
+        scale_group(0, false);
+        stage(st0, 0);
+        stage(st1, 1);
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(kStageLoads, 15));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         read_frags(st0, 0, fa0, fb0);
-        read_scales(sx0, xa0, xb0);
+        read_scales(0, false, xa0, xb0);
     }
     int kb = 0;
-    for (; kb + 4 <= nk; kb += 2) {
-        slice(kb, st0, sx0, st1, sx1, xa0, xb0, xa1, xb1, true);
-        slice(kb + 1, st1, sx1, st0, sx0, xa1, xb1, xa0, xb0, true);
+    if constexpr (kMX) {
+        // eight slices per trip, so that every slice's place, and with it its
+        // wait and the scale object it reads, is fixed at compile time
+        for (; kb + 10 <= nk; kb += 8) {
+            slice(kb, 0, st0, st1, xa0, xb0, xa1, xb1, true);
+            slice(kb + 1, 1, st1, st0, xa1, xb1, xa0, xb0, true);
+            slice(kb + 2, 2, st0, st1, xa0, xb0, xa1, xb1, true);
+            slice(kb + 3, 3, st1, st0, xa1, xb1, xa0, xb0, true);
+            slice(kb + 4, 4, st0, st1, xa0, xb0, xa1, xb1, true);
+            slice(kb + 5, 5, st1, st0, xa1, xb1, xa0, xb0, true);
+            slice(kb + 6, 6, st0, st1, xa0, xb0, xa1, xb1, true);
+            slice(kb + 7, 7, st1, st0, xa1, xb1, xa0, xb0, true);
+        }
+        // at most nine slices remain; kb % 8 == 0
+        if (kb < nk) slice(kb, 0, st0, st1, xa0, xb0, xa1, xb1, false);
+        if (kb + 1 < nk) slice(kb + 1, 1, st1, st0, xa1, xb1, xa0, xb0, false);
+        if (kb + 2 < nk) slice(kb + 2, 2, st0, st1, xa0, xb0, xa1, xb1, false);
+        if (kb + 3 < nk) slice(kb + 3, 3, st1, st0, xa1, xb1, xa0, xb0, false);
+        if (kb + 4 < nk) slice(kb + 4, 4, st0, st1, xa0, xb0, xa1, xb1, false);
+        if (kb + 5 < nk) slice(kb + 5, 5, st1, st0, xa1, xb1, xa0, xb0, false);
+        if (kb + 6 < nk) slice(kb + 6, 6, st0, st1, xa0, xb0, xa1, xb1, false);
+        if (kb + 7 < nk) slice(kb + 7, 7, st1, st0, xa1, xb1, xa0, xb0, false);
+        if (kb + 8 < nk) slice(kb + 8, 0, st0, st1, xa0, xb0, xa1, xb1, false);
+    } else {
+        for (; kb + 4 <= nk; kb += 2) {
+            slice(kb, 0, st0, st1, xa0, xb0, xa1, xb1, true);
+            slice(kb + 1, 1, st1, st0, xa1, xb1, xa0, xb0, true);
+        }
+        // at most three slices remain; kb is even
+        if (kb < nk) slice(kb, 0, st0, st1, xa0, xb0, xa1, xb1, false);
+        if (kb + 1 < nk) slice(kb + 1, 1, st1, st0, xa1, xb1, xa0, xb0, false);
+        if (kb + 2 < nk) slice(kb + 2, 0, st0, st1, xa0, xb0, xa1, xb1, false);
     }
-    // at most three slices remain; kb is even
-    if (kb < nk) slice(kb, st0, sx0, st1, sx1, xa0, xb0, xa1, xb1, false);
-    if (kb + 1 < nk) slice(kb + 1, st1, sx1, st0, sx0, xa1, xb1, xa0, xb0, false);
-    if (kb + 2 < nk) slice(kb + 2, st0, sx0, st1, sx1, xa0, xb0, xa1, xb1, false);
 
     // epilogue: lane (fr, fg) of 32x32 tile (i, j) holds C[row][4 consecutive
     // columns 8q + 4fg .. +3] for q = 0..3

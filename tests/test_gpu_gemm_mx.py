@@ -38,7 +38,10 @@ def _mx_operands(rng, M, N, K, fa, fb):
 
 
 @pytest.mark.parametrize("fa,fb", [(E4, E4), (E5, E4), (E4, E5), (E5, E5)])
-@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (384, 256, 640), (256, 512, 1536)])
+# K / 128 = 1, 5, 9, 12, 17, 18 slices: every place of a slice in the
+# kernel's eight-slice loop and its tail, groups of four slices cut short
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (384, 256, 640), (256, 256, 1152), (256, 512, 1536),
+                                   (128, 384, 2176), (256, 128, 2304)])
 def test_mx_gemm_fp32_parity(fa, fb, M, N, K):
     rng = np.random.default_rng(M + 7 * N + 3 * K + 11 * fa + fb)
     qa, sa, qb, sb = _mx_operands(rng, M, N, K, fa, fb)
