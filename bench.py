@@ -66,6 +66,9 @@ def parse():
     p.add_argument("--rows", type=int, default=1, help="also time every row of the path (1) or not (0)")
     p.add_argument("--only", default="", help="comma-separated row names: time only these rows")
     p.add_argument("--headline", type=int, default=1, help="time the headline delayed-scaling steps (1) or not (0)")
+    p.add_argument("--clock", type=int, default=1,
+                   help="measure each row's graphics clock with the clock monitor (1) or not (0: for counter "
+                        "collection, which runs kernels one at a time, so the monitor would only time out)")
     p.add_argument("--cpu-baseline", type=int, default=1)
     p.add_argument("--cpu-seconds", type=float, default=6.0)
     p.add_argument("--copy-mib", type=int, default=0,
@@ -104,6 +107,7 @@ def _pct(values, q):
 
 
 _SIDE = []
+CLOCK = [True]
 
 
 def measure_clock(torch, fq, fn, rotate, ms_per_launch, target_ms=30.0):
@@ -156,7 +160,7 @@ def time_launches(torch, stream, fn, per_sample, rotate=1, samples=SAMPLES, fq=N
     ms = [ev[k].elapsed_time(ev[k + 1]) / per_sample for k in range(samples)]
     r = {"ms": round(_pct(ms, 0.5), 5), "ms_p10": round(_pct(ms, 0.1), 5), "ms_p90": round(_pct(ms, 0.9), 5),
          "samples": samples, "launches_per_sample": per_sample}
-    if fq is not None:
+    if fq is not None and CLOCK[0]:
         r["sclk"] = measure_clock(torch, fq, lambda j: fn((i + j) % rotate), rotate, r["ms"])
     return r
 
@@ -198,6 +202,7 @@ def cpu_model():
 
 def main():
     args = parse()
+    CLOCK[0] = bool(args.clock)
     if args.copy_mib:
         copy_calibration(args.copy_mib)
         return

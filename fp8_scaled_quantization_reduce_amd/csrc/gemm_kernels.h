@@ -325,7 +325,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     __shared__ __attribute__((aligned(1024))) uint8_t st1[kPTStageBytes];
     // MXFP8: the scale dwords of an even and of an odd group of four slices
     // (two LDS objects, like the stages), each A rows' then B rows' [row][4]
-    constexpr int kSxGroup = 2 * kBM * 4;
+    // with one dword of padding after every 16 rows: row r's dword d sits at
+    // 4 r + r / 16 + d, so the 32 rows a scale read touches (fr = 0..31) fall
+    // in 32 different banks
+    constexpr int kSxGroup = 2 * kBM * 4 + 2 * kBM / 16;
     __shared__ __attribute__((aligned(16))) uint32_t sxe[kMX ? kSxGroup : 1];
     __shared__ __attribute__((aligned(16))) uint32_t sxo[kMX ? kSxGroup : 1];
     __shared__ uint32_t red[kGemmThreads / 64];
@@ -374,18 +377,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
         }
     };
     // MXFP8 scale group g (slices 4g .. 4g+3) into sxe (g even) or sxo (g odd):
-    // wave w loads rows 64w .. 64w+63 of both panels, 16 rows per load, lane L
-    // the dword L % 4 of row L / 4 (bytes past a panel read zero; bytes past a
-    // row's last slice, of groups past the last one too, are never read)
+    // wave w loads rows 64w .. 64w+63 of both panels, 16 rows per load (one
+    // padded run of 64 dwords), lane L the dword L % 4 of row L / 4 (bytes past
+    // a panel read zero; bytes past a row's last slice, of groups past the last
+    // one too, are never read)
     const int sx_voff = (lane >> 2) * kx + 4 * (lane & 3);
     constexpr int kScaleGroupLoads = 8; // loads per lane per scale group
+    auto sx_pos = [](int r) { return 4 * r + (r >> 4); };
     auto scale_group_to = [&](uint32_t *dst, int g) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int row = 64 * w + 16 * q;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxa, (lds_void *)(dst + 4 * row), 4, sx_voff, row * kx + 16 * g,
-                                                     0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxb, (lds_void *)(dst + 4 * (kBM + row)), 4, sx_voff,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxa, (lds_void *)(dst + sx_pos(row)), 4, sx_voff,
+                                                     row * kx + 16 * g, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxb, (lds_void *)(dst + sx_pos(kBM + row)), 4, sx_voff,
                                                      row * kx + 16 * g, 0, 0);
         }
     };
@@ -418,9 +423,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
     // the scale dwords of slice kb (group kb / 4, dword kb % 4 of each row)
     auto read_scales_from = [&](const uint32_t *sx, uint32_t(&xa)[4], uint32_t(&xb)[kTJ]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xa[i] = sx[4 * (wm * 128 + 32 * i + fr)] >> (8 * fg);
+        for (int i = 0; i < 4; ++i) xa[i] = sx[sx_pos(wm * 128 + 32 * i + fr)] >> (8 * fg);
 #pragma unroll
-        for (int j = 0; j < kTJ; ++j) xb[j] = sx[4 * (kBM + wn * kWN + 32 * j + fr)] >> (8 * fg);
+        for (int j = 0; j < kTJ; ++j) xb[j] = sx[sx_pos(kBM + wn * kWN + 32 * j + fr)] >> (8 * fg);
     };
     // (odd: the group of slice kb is odd, so its dwords are in sxo)
     auto read_scales = [&](int kb, bool odd, uint32_t(&xa)[4], uint32_t(&xb)[kTJ]) {
