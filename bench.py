@@ -45,9 +45,9 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0
 MFMA_PEAK_SCLK_MHZ = 2400.0  # the clock the 5.0 PFLOP/s figure assumes (256 CUs x 8192 FP8 flop/clk)
 # HBM bytes of one delayed step (cast_kernel + delayed_kernel), from the
 # FETCH_SIZE and WRITE_SIZE counters scaled by the factors a plain copy gives
-# (profiles/delayed_step_8192x8192_bf16_hbm_traffic.md); None whenever either
-# kernel has changed since the counters were taken.
-TRAFFIC_BYTES_PER_STEP = None
+# (profiles/hbm_traffic_bench_kernels.md); None whenever either kernel has
+# changed since the counters were taken.
+TRAFFIC_BYTES_PER_STEP = 201714296
 
 # Seconds of untimed launches before each row is timed.  The GPU's clocks
 # take tens of milliseconds of sustained matrix work to settle: measured on
