@@ -476,12 +476,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
         // sync: the next slice landed (this lane's loads, then every wave's).
         // MXFP8: the scale group issued at the end of the previous slice (the
         // youngest kScaleGroupLoads loads) may stay in flight through this wait.
+        // (scheduling barriers keep every matrix instruction on its side of the
+        // slice barrier; the scheduler otherwise moves some across it, and in
+        // the MXFP8 eight-slice loop the halves lose their balance)
+        __builtin_amdgcn_sched_barrier(0);
         if (relaxed)
             __builtin_amdgcn_s_waitcnt(waitcnt_imm(kScaleGroupLoads, 0));
         else
             __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         // half 1: the next slice's scales first, while no direct load is in
         // flight (the scale buffers are one LDS object whose group is chosen
         // at run time, and the compiler's wait insertion would otherwise hold
