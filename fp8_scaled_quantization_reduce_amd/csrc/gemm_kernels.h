@@ -855,19 +855,19 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
 // promotion of its last two tiles and (group X) issues global loads.  So
 // every SIMD always has one wave feeding its matrix pipe while the other
 // waits on memory, instead of both waves stalling together at one barrier
-// per slice (measured on the MI355X: two waves that each interleave four
-// promotion FMAs per MFMA keep the pipe ~94% busy; the lockstep schedule
-// kept it 46% busy).
+// per slice (measured on the MI355X, fprop 4096x14336x4096: the matrix pipes
+// are busy 0.62 of the active cycles, against 0.46 with the lockstep
+// schedule).
 //
 // Memory: two 64 KiB stages (A rows 0..255, B rows 0..255 of one slice) plus
-// per-stage scales.  Group X alone loads, in two groups per slice: group 1
-// (A, the B rows 0..63 and 128..191 that X and Y read first, the A row scales
-// and B's scales) once the stage's previous A and first-half B reads are
-// over, group 2 (B rows 64..127 and 192..255) once its second-half reads are
-// over, each six phases before it is read.  Every X wave issues the same
-// loads in the same order, so one vmcnt threshold at the end of each X
-// compute phase (G1 + G2 younger loads outstanding) proves that the data the
-// next phases read has landed.
+// per-stage scales.  Every wave loads an eighth of each, in two groups per
+// slice, each in one of its read phases: group 1 (A, the B rows 0..63 and
+// 128..191 that both groups read first, the A row scales and B's scales) once
+// the stage's previous A and first-half B reads are over, group 2 (B rows
+// 64..127 and 192..255) once its second-half reads are over, at least five
+// phases before they are read.  Every wave issues the same loads in the same
+// order, so one vmcnt threshold at the end of every phase (G1 + G2 younger
+// loads outstanding) proves that the data the next phases read has landed.
 template <int kv> struct PhaseC {
     static constexpr int value = kv;
 };
