@@ -27,10 +27,11 @@
 //   tiles of 32x32 (v_mfma_scale_f32_32x32x64_f8f6f4, 256 accumulators); K
 //   moves in slices of 128 through two LDS stages.
 //
-//   gemm_bs_kernel (block-scaled): eight waves of 64x128, each as 4x8 tiles
-//   of 16x16 (v_mfma_f32_16x16x128_f8f6f4); K moves in steps of 128 (one
-//   block-scale slice) through two LDS stages, and each slice's partial is
-//   promoted on the vector ALU.
+//   gemm_bs_pp_kernel (block-scaled): eight waves of 64x128, each as 4x8
+//   tiles of 16x16 (v_mfma_f32_16x16x128_f8f6f4), in two groups that take
+//   turns at the matrix pipes; K moves in steps of 128 (one block-scale slice)
+//   through two LDS stages, and each slice's partial is promoted on the
+//   vector ALU.
 //
 // Operand order.  The MFMA is issued as (B fragment, A fragment), so its
 // result is C^T: in a 16x16 tile lane (r = lane % 16, g = lane / 16) holds
@@ -604,42 +605,81 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_pt_kernel(const uint8_t 
 }
 
 // ---------------------------------------------------------------------------
-// Block-scaled kernel.  256x256 block tile, eight waves (4 x 2) of 64x128, each
-// as 4 x 8 tiles of 16x16.  One K step is one 128-wide scale slice and one
-// v_mfma_f32_16x16x128_f8f6f4 per tile, started from zero, so its result is
-// exactly that slice's partial product; it is promoted at once,
-//   acc = fma(part, fl32(sA[row][kb] * sB[col block][kb]), acc),
-// with the accumulators in ordinary vector registers (128 per lane; the
-// two-waves-per-SIMD budget is 256).  The slice's A rows and B rows (2 x 32
-// KiB) and the 256 row scales of A (1 KiB) go straight into LDS; two stages,
-// the next slice's loads in flight during this one's MFMAs.
+// Block-scaled kernel.  A 256 x kBN block tile (kBN = 256; 128 for the half
+// tiles of a last, partly empty round), eight waves (4 x 2) of 64 x kBN/2,
+// each as 4 x kBN/32 tiles of 16x16.  One K step is one 128-wide scale slice
+// and one v_mfma_f32_16x16x128_f8f6f4 per tile, started from zero, so its
+// result is exactly that slice's partial product; it is promoted at once,
+//   acc = fma(part, fl32(sA[row][kb] * sB[col block or col][kb]), acc),
+// with the accumulators in ordinary vector registers (the vector ALU cannot
+// operate on AGPRs; 128 per lane for full tiles, within the budget of two
+// waves per SIMD).
+//
+// Ping-pong schedule.  The waves form two groups, X (waves 0-3) and Y (waves
+// 4-7), one wave of each on every SIMD, and a slice runs as four phases
+// separated by barriers: in each phase one group computes half of its slice
+// (its first or second kBN/64 column tiles: the MFMAs, each followed by the
+// promotion of the tile two before it) from fragments already in registers,
+// while the other group reads its next fragments from LDS, finishes the
+// promotion of its last two tiles and issues global loads.  So every SIMD
+// always has one wave feeding its matrix pipe while the other waits on
+// memory, instead of both waves stalling together at one barrier per slice
+// (measured on the MI355X, fprop 4096x14336x4096: the matrix pipes are busy
+// 0.62 of the active cycles, against 0.46 with that lockstep schedule).
+//
+// Memory: two stages (A rows 0..255 and B rows 0..kBN-1 of one slice) plus
+// per-stage scales.  Every wave loads an eighth of each, in two groups per
+// slice, each in one of its read phases: group 1 (A, the B rows that both
+// groups read first, the A row scales and B's scales) once the stage's
+// previous A and first-half B reads are over, group 2 (the B rows read
+// second) once its second-half reads are over, at least five phases before
+// they are read.  Every wave issues the same loads in the same order, so one
+// vmcnt threshold at the end of every phase (G1 + G2 younger loads
+// outstanding) proves that the data the next phases read has landed.
 constexpr int kBSThreads = 512;
-constexpr int kBSStageBytes = 2 * kBM * kBK;
 
-// kBN = 256: the block computes a 256x256 tile, grid block b -> grouped tile
-// xcd_order(b, n_main).  kBN = 128: half a tile (the wave tiles are 64x64),
-// grid block b -> the half b & 1 of grouped tile tile_base + b / 2; the
-// launcher uses it for a last, partly empty wave of tiles, which then runs as
-// a full wave of half tiles.  Each block's amax partial is folded into
-// part[b % kParts].
+template <int kv> struct PhaseC {
+    static constexpr int value = kv;
+};
+
 template <int FA, int FB, bool kAmax, int kOut, bool kFuse, bool kRowB, int kBN>
-__global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *__restrict__ A,
-                                                                const uint8_t *__restrict__ B,
-                                                                const float *__restrict__ sA,
-                                                                const float *__restrict__ sB, int M, int N, int K,
-                                                                void *__restrict__ C, Epi epi, uint32_t *part,
-                                                                int tile_base, int n_main)
+__global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_pp_kernel(const uint8_t *__restrict__ A,
+                                                                   const uint8_t *__restrict__ B,
+                                                                   const float *__restrict__ sA,
+                                                                   const float *__restrict__ sB, int M, int N, int K,
+                                                                   void *__restrict__ C, Epi epi, uint32_t *part,
+                                                                   int tile_base, int n_main)
 {
-    constexpr int kWN = kBN / 2; // a wave's columns
-    constexpr int kTJ = kWN / 16; // its 16-wide column tiles
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[kBSStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[kBSStageBytes];
-    __shared__ __attribute__((aligned(16))) float sa0[kBM];
-    __shared__ __attribute__((aligned(16))) float sa1[kBM];
-    __shared__ __attribute__((aligned(16))) float sb0[kRowB ? kBM : 4]; // B's row scales (1x128 B)
-    __shared__ __attribute__((aligned(16))) float sb1[kRowB ? kBM : 4];
+    // One LDS object per stage (the compiler's wait insertion tells the direct
+    // loads into different objects apart, so a read of one stage never waits
+    // for the loads landing in the other; within a stage the loads that a
+    // read does not need were issued four phases earlier).  Stage layout:
+    //   A      rows 0..255 of the tile (32 KiB)
+    //   B0     the B rows each wave reads first: tile rows 0..Q-1 (group X)
+    //          then 2Q..3Q-1 (group Y), Q = kBN / 4 (2Q rows)
+    //   B1     the B rows each wave reads second: Q..2Q-1, then 3Q..4Q-1
+    //   SA     the slice's 256 A row scales
+    //   SB0    1x128 B: the scales of B0's rows; 128x128 B: the block scales
+    //          of the tile's column blocks at [0], [1] (each loading wave
+    //          writes a 64-float copy)
+    //   SB1    1x128 B: the scales of B1's rows
+    // B row n of the tile is row (n / 2Q) * Q + n % Q of B0 (n % 2Q < Q) or
+    // B1.  Rows are 128 bytes with 16-byte chunks XOR-swizzled by row.
+    constexpr int kQ = kBN / 4, kJT = kQ / 16;         // a half's columns and 16-wide column tiles
+    constexpr int kAB = kBM * kBK, kB2 = 2 * kQ * kBK; // code bytes of A, of B0 / B1
+    constexpr int oB0 = kAB, oB1 = kAB + kB2, oSA = kAB + 2 * kB2, oSB0 = oSA + 4 * kBM, oSB1 = oSB0 + 4 * kBM;
+    constexpr int kStage = oSB1 + 2 * kBM;
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[kStage];
     __shared__ uint32_t red[kBSThreads / 64];
+    constexpr int kBL = kBN / 128;         // loads per wave of one B half
+    constexpr int G1 = 4 + kBL + 1;        // loads per wave in group 1
+    constexpr int G2 = kBL + (kRowB ? 1 : 0); // and in group 2
+    constexpr int kVm = G1 + G2;           // younger loads allowed at the end of every phase
+    auto fptr = [](uint8_t *st, int off) { return reinterpret_cast<float *>(st + off); };
 
+    // kBN = 256: grid block b -> grouped tile xcd_order(b, n_main).  kBN =
+    // 128: half b & 1 (columns 128 (b & 1) ..) of grouped tile tile_base + b / 2
     int tm, tn;
     const int tilesM = (M + kBM - 1) / kBM, tilesN = (N + kBM - 1) / kBM;
     if constexpr (kBN == kBM) group_tile(xcd_order(blockIdx.x, n_main), tilesM, tilesN, tm, tn);
@@ -647,276 +687,12 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_kernel(const uint8_t *_
     const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBM + (kBN == kBM ? 0 : (blockIdx.x & 1) * kBN);
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = w >> 1, wn = w & 1;
+    const bool gx = w < 4;
+    const int wm = w & 3, wn = w >> 2; // rows 64 wm .., columns 2Q wn .. of the tile
     const int fr = lane & 15, fg = lane >> 4;
     const int kblocks = K / kBK;
 
     const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBN, (int64_t)N - n0);
-    const __amdgpu_buffer_rsrc_t ra =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * K), 0, (int)(a_rows * K), kRawBufferWord3);
-    const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(B + n0 * K), 0, (int)(b_rows * K), kRawBufferWord3);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)(sA + m0 * kblocks), 0,
-                                                                        (int)(a_rows * kblocks * 4), kRawBufferWord3);
-    // lane L of a 1 KiB load writes physical chunk L % 8 of row 8(w + 8u) + L / 8,
-    // which holds logical chunk (L % 8) ^ ((row >> 1) & 7) = (L % 8) ^ ((4w + L / 16) & 7)
-    const int voff = (lane >> 3) * K + (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4);
-    // 128x128 B: the wave's 128 columns lie in one 128-column scale block
-    // (clamped for the half tile past N, whose results are never stored).
-    // 1x128 B: one scale per row of B (column of C), staged like A's.
-    const int nb = min((int)((n0 + wn * kWN) / 128), N / 128 - 1);
-    const float *__restrict__ sbp = sB + (int64_t)nb * kblocks;
-    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(sB + (kRowB ? n0 * kblocks : 0)), 0, kRowB ? (int)(b_rows * kblocks * 4) : 4, kRawBufferWord3);
-
-    auto stage = [&](uint8_t *st, float *sa, float *sbr, int kb) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int row = 8 * (w + 8 * u);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(st + row * kBK), 16, voff, kb * kBK + row * K,
-                                                     0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < kBN / 64; ++u) {
-            const int row = 8 * (w + 8 * u);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(st + kBM * kBK + row * kBK), 16, voff,
-                                                     kb * kBK + row * K, 0, 0);
-        }
-        if (w < 4)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(sa + 64 * w), 4, lane * kblocks * 4,
-                                                     (64 * w * kblocks + kb) * 4, 0, 0);
-        else if (kRowB && (w - 4) * 64 < kBN)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(sbr + 64 * (w - 4)), 4, lane * kblocks * 4,
-                                                     (64 * (w - 4) * kblocks + kb) * 4, 0, 0);
-    };
-
-    v4f acc[4][kTJ];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < kTJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // One slice (stage `cur`, its row scales in `sac`; the next slice already
-    // in flight to `nxt` / `san`).  Column tile j's MFMAs run while tile
-    // j-1's partials are promoted and tile j+1's B fragment is read.  Once
-    // the last fragment of `cur` is in registers (before tile 7), every lane
-    // waits for its own loads of the next slice and the block meets at the
-    // one barrier of the slice; then the slice after next is loaded into
-    // `cur`, and tile 7's MFMAs overlap the reads of the next slice's A
-    // fragments, first B fragment and row scales.  Empty asm statements pin
-    // this order (the compiler would otherwise issue all 32 MFMAs first and
-    // spill their 128 partial registers): the one on the B fragment keeps
-    // tile j's MFMAs below it, the one on the promoted accumulators keeps
-    // tile j-1's FMAs above the next tile's.
-    // Weights: 128x128 B: wi[i] = fl32(sA[row i] * sB[block]); 1x128 B:
-    // fl32(sA[row i] * sB[col]) per element, from sai[i] and the tile's four
-    // column scales, read from LDS just before the tile's MFMAs are issued
-    // (tile 7's before the slice's barrier, after which the stage is reloaded).
-    v8i a[4], b;
-    float wi[4], sai[4];
-    float sb_next = 0.0f;
-    auto promote = [&](int j, const v4f (&part)[4], const v4f &sbj) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float wgt = kRowB ? sai[i] * sbj[e] : wi[i];
-                acc[i][j][e] = __builtin_fmaf(part[i][e], wgt, acc[i][j][e]);
-            }
-        asm volatile("" : "+v"(acc[0][j]), "+v"(acc[1][j]), "+v"(acc[2][j]), "+v"(acc[3][j]));
-    };
-    auto slice = [&](int kb, uint8_t *cur, float *sac, float *sbc, const uint8_t *nxt, const float *san,
-                     bool full) {
-        const uint8_t *lb = cur + kBM * kBK;
-        const float *sbw = sbc + wn * kWN + 4 * fg; // this lane's column scales, tile 0
-        v4f prev[4];
-        v4f sb7 = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < kTJ; ++j) {
-            asm volatile("" : "+v"(b));
-            v8i bn;
-            if (j + 1 < kTJ) bn = read_frag(lb, wn * kWN + 16 * (j + 1) + fr, fg);
-            v4f sbj = v4f{0.f, 0.f, 0.f, 0.f}; // tile j-1's column scales
-            if constexpr (kRowB) {
-                if (j > 0) sbj = *reinterpret_cast<const v4f *>(sbw + 16 * (j - 1));
-                if (j == kTJ - 1) sb7 = *reinterpret_cast<const v4f *>(sbw + 16 * (kTJ - 1));
-            }
-            if (j == kTJ - 1) {
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-                __builtin_amdgcn_s_barrier();
-                asm volatile("" ::: "memory");
-                if (full || kb + 2 < kblocks) stage(cur, sac, sbc, kb + 2);
-            }
-            v4f cur_p[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) cur_p[i] = mfma16x16x128<FB, FA>(b, a[i], v4f{0.f, 0.f, 0.f, 0.f});
-            if (j > 0) promote(j - 1, prev, sbj);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) prev[i] = cur_p[i];
-            if (j + 1 < kTJ) b = bn;
-        }
-        // the last tile's promotion with this slice's weights, then the next
-        // slice's fragments and weights
-        promote(kTJ - 1, prev, sb7);
-        if (full || kb + 1 < kblocks) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = read_frag(nxt, wm * 64 + 16 * i + fr, fg);
-            b = read_frag(nxt + kBM * kBK, wn * kWN + fr, fg);
-            if constexpr (kRowB) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sai[i] = san[wm * 64 + 16 * i + fr];
-            } else {
-                const float sb = sb_next;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) wi[i] = san[wm * 64 + 16 * i + fr] * sb;
-                sb_next = (full || kb + 2 < kblocks) ? sbp[kb + 2] : 0.0f;
-            }
-        }
-    };
-
-    // prologue: slices 0 and 1 in flight (both stages always filled, see the
-    // per-tensor kernel), slice 0's fragments and weights
-    if (kblocks > 0) {
-        stage(st0, sa0, sb0, 0);
-        stage(st1, sa1, sb1, 1);
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = read_frag(st0, wm * 64 + 16 * i + fr, fg);
-        b = read_frag(st0 + kBM * kBK, wn * kWN + fr, fg);
-        if constexpr (kRowB) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sai[i] = sa0[wm * 64 + 16 * i + fr];
-        } else {
-            const float sb = sbp[0];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wi[i] = sa0[wm * 64 + 16 * i + fr] * sb;
-            sb_next = kblocks > 1 ? sbp[1] : 0.0f;
-        }
-    }
-    // steady state: slices kb + 2 and kb + 3 exist (no guards)
-    int kb = 0;
-    for (; kb + 4 <= kblocks; kb += 2) {
-        slice(kb, st0, sa0, sb0, st1, sa1, true);
-        slice(kb + 1, st1, sa1, sb1, st0, sa0, true);
-    }
-    // at most three slices remain; kb is even
-    if (kb < kblocks) slice(kb, st0, sa0, sb0, st1, sa1, false);
-    if (kb + 1 < kblocks) slice(kb + 1, st1, sa1, sb1, st0, sa0, false);
-    if (kb + 2 < kblocks) slice(kb + 2, st0, sa0, sb0, st1, sa1, false);
-
-    // epilogue: lane (fr, fg) of tile (i, j) holds C[row][4 consecutive cols]
-    const float out_scale = kOut >= kOutE4M3 ? 1.0f / *epi.out_si : 0.0f;
-    uint32_t m = 0;
-    {
-        // staged as in the per-tensor kernel: 64-row wave slabs are likewise
-        // wholly inside or outside C; four waves share each 64 KiB stage
-        typedef EpiStage<kWN, out_bytes<kOut>(), 64, kBSStageBytes / 4> ES;
-        const int64_t wrow0 = m0 + wm * 64, wcol0 = n0 + wn * kWN;
-        const bool inside = wrow0 < M && wcol0 < N;
-        uint8_t *ep = (w < 4 ? st0 : st1) + (w & 3) * (kBSStageBytes / 4);
-#pragma unroll
-        for (int ps = 0; ps < ES::kPasses; ++ps) {
-            __syncthreads(); // the stages (then the previous pass) are no longer read
-            if (inside) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if ((16 * i) / ES::kPassRows != ps) continue;
-#pragma unroll
-                    for (int j = 0; j < kTJ; ++j) {
-                        const uint4 bits =
-                            pack_out4<kOut, kAmax, kFuse>(wcol0 + 16 * j + 4 * fg, acc[i][j], m, epi, out_scale);
-                        ES::put(ep, 16 * i + fr - ps * ES::kPassRows, 4 * j + fg, bits);
-                    }
-                }
-            }
-            __syncthreads();
-            if (inside) ES::store(ep, C, N, wrow0 + ps * ES::kPassRows, wcol0, lane);
-        }
-    }
-    if constexpr (kAmax) {
-        m = block_max_u32<kBSThreads>(m, red);
-        if (tid == 0) atomicMax(&part[blockIdx.x % kParts], canonical_amax_bits(m));
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Block-scaled kernel with a ping-pong schedule (the launch of full 256x256
-// tiles).  The same tiles, operand stages and arithmetic as gemm_bs_kernel:
-// eight waves of 64x128 (4 x 8 tiles of 16x16, one v_mfma_f32_16x16x128 per
-// tile per 128-wide K slice, started from zero, promoted at once by
-// acc = fma(part, weight, acc)).  What differs is the order of work.  The
-// waves form two groups, X (waves 0-3) and Y (waves 4-7), one wave of each on
-// every SIMD, and a slice runs as four phases separated by barriers: in each
-// phase one group computes half of its slice (16 MFMAs, each followed by the
-// promotion of the tile two before it) from fragments already in registers,
-// while the other group reads its next fragments from LDS, finishes the
-// promotion of its last two tiles and (group X) issues global loads.  So
-// every SIMD always has one wave feeding its matrix pipe while the other
-// waits on memory, instead of both waves stalling together at one barrier
-// per slice (measured on the MI355X, fprop 4096x14336x4096: the matrix pipes
-// are busy 0.62 of the active cycles, against 0.46 with the lockstep
-// schedule).
-//
-// Memory: two 64 KiB stages (A rows 0..255, B rows 0..255 of one slice) plus
-// per-stage scales.  Every wave loads an eighth of each, in two groups per
-// slice, each in one of its read phases: group 1 (A, the B rows 0..63 and
-// 128..191 that both groups read first, the A row scales and B's scales) once
-// the stage's previous A and first-half B reads are over, group 2 (B rows
-// 64..127 and 192..255) once its second-half reads are over, at least five
-// phases before they are read.  Every wave issues the same loads in the same
-// order, so one vmcnt threshold at the end of every phase (G1 + G2 younger
-// loads outstanding) proves that the data the next phases read has landed.
-template <int kv> struct PhaseC {
-    static constexpr int value = kv;
-};
-
-template <int FA, int FB, bool kAmax, int kOut, bool kFuse, bool kRowB>
-__global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_pp_kernel(const uint8_t *__restrict__ A,
-                                                                   const uint8_t *__restrict__ B,
-                                                                   const float *__restrict__ sA,
-                                                                   const float *__restrict__ sB, int M, int N, int K,
-                                                                   void *__restrict__ C, Epi epi, uint32_t *part,
-                                                                   int n_main)
-{
-    // One LDS object per stage (the compiler's wait insertion tells the direct
-    // loads into different objects apart, so a read of one stage never waits
-    // for the loads landing in the other; within a stage the loads that a
-    // read does not need were issued four phases earlier).  Stage layout:
-    //   A      rows 0..255 of the tile (32 KiB)
-    //   B0     the B rows each wave reads first: tile rows 0..63 (group X)
-    //          then 128..191 (group Y) (16 KiB)
-    //   B1     the B rows each wave reads second: 64..127, then 192..255
-    //   SA     the slice's 256 A row scales
-    //   SB0    1x128 B: the scales of B0's rows; 128x128 B: the tile's two
-    //          block scales at [0], [1] (each loading wave writes a 64-float copy)
-    //   SB1    1x128 B: the scales of B1's rows
-    // B row n of the tile is row (n >> 7) * 64 + (n & 63) of B0 (n & 64 == 0)
-    // or B1.  Rows are 128 bytes with 16-byte chunks XOR-swizzled by row.
-    constexpr int kAB = kBM * kBK, kB2 = kBM / 2 * kBK; // code bytes of A, of B0 / B1
-    constexpr int oB0 = kAB, oB1 = kAB + kB2, oSA = kAB + 2 * kB2, oSB0 = oSA + 4 * kBM, oSB1 = oSB0 + 4 * kBM;
-    constexpr int kStage = oSB1 + 2 * kBM;
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[kStage];
-    __shared__ uint32_t red[kBSThreads / 64];
-    constexpr int G1 = 7;              // loads per wave in group 1
-    constexpr int G2 = kRowB ? 3 : 2;  // and in group 2
-    constexpr int kVm = G1 + G2;       // younger loads allowed at the end of every phase
-    auto fptr = [](uint8_t *st, int off) { return reinterpret_cast<float *>(st + off); };
-
-    int tm, tn;
-    const int tilesM = (M + kBM - 1) / kBM, tilesN = (N + kBM - 1) / kBM;
-    group_tile(xcd_order(blockIdx.x, n_main), tilesM, tilesN, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBM;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool gx = w < 4;
-    const int wm = w & 3, wn = w >> 2; // rows 64 wm .., columns 128 wn .. of the tile
-    const int fr = lane & 15, fg = lane >> 4;
-    const int kblocks = K / kBK;
-
-    const int64_t a_rows = min((int64_t)kBM, (int64_t)M - m0), b_rows = min((int64_t)kBM, (int64_t)N - n0);
     const __amdgpu_buffer_rsrc_t ra =
         __builtin_amdgcn_make_buffer_rsrc((void *)(A + m0 * K), 0, (int)(a_rows * K), kRawBufferWord3);
     const __amdgpu_buffer_rsrc_t rb =
@@ -933,11 +709,14 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_pp_kernel(const uint8_t
     const int voff = (lane >> 3) * K + (((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) << 4);
     // 128x128 B: lanes 0 and 1 fetch the scales of the tile's two column
     // blocks (clamped inside B for a tile column past N, whose results are
-    // never stored), the other lanes repeat them
-    const int sb_voff = kRowB ? lane * kblocks * 4 : min((int)(n0 / 128) + (lane & 1), N / 128 - 1) * kblocks * 4;
+    // never stored), the other lanes repeat them.  1x128 B: lane L fetches the
+    // scale of LDS row lrow + L of B0, lrow = 64 (w & 1) when B0 has 128 rows.
+    const int sb_lrow = kBN == kBM ? 64 * (w & 1) : 0;
+    const int sb_voff = kRowB ? (((sb_lrow + lane) / kQ) * 2 * kQ + (sb_lrow + lane) % kQ) * kblocks * 4
+                              : min((int)(n0 / 128) + (lane & 1), N / 128 - 1) * kblocks * 4;
 
-    // A: rows 8(w + 8u), u = 0..3; B half h: LDS rows 8(w + 8u), u = 0..1,
-    // holding tile rows (LDS row >> 6) * 128 + 64 h + (LDS row & 63)
+    // A: rows 8(w + 8u), u = 0..3; B half h: LDS rows 8(w + 8u), u < kBL,
+    // holding tile rows (LDS row / Q) * 2Q + Q h + LDS row % Q
     auto load_a = [&](uint8_t *dst, int kb) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -948,19 +727,18 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_pp_kernel(const uint8_t
     };
     auto load_b = [&](uint8_t *dst, int h, int kb) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < kBL; ++u) {
             const int row = 8 * (w + 8 * u);
-            const int trow = (row >> 6) * 128 + 64 * h + (row & 63);
+            const int trow = (row / kQ) * 2 * kQ + kQ * h + row % kQ;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(dst + row * kBK), 16, voff, trow * K + kb * kBK,
                                                      0, 0);
         }
     };
-    // 1x128 B: the scales of half h's LDS rows 64 (w & 1) .. + 63 (the other
-    // waves repeat waves 0 and 1, writing the same values)
+    // 1x128 B: the scales of half h's LDS rows sb_lrow .. + 63 (the waves
+    // that load the same rows write the same values)
     auto load_sb_rows = [&](float *dst, int h, int kb) {
-        const int lrow = 64 * (w & 1), trow = 128 * (w & 1) + 64 * h;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(dst + lrow), 4, sb_voff, (trow * kblocks + kb) * 4,
-                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(dst + sb_lrow), 4, sb_voff,
+                                                 (kQ * h * kblocks + kb) * 4, 0, 0);
     };
     // group 1 of slice kb: A, B's first half, and one scale load per wave
     // (waves 0-3: A row scales 64 w ..; waves 4-7: B's first-half scales)
@@ -982,15 +760,15 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_pp_kernel(const uint8_t
         if constexpr (kRowB) load_sb_rows(fptr(st, oSB1), 1, kb);
     };
 
-    v4f acc[4][8];
+    v4f acc[4][2 * kJT];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2 * kJT; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    v8i a[4], b[4];   // the slice's A fragments, the half's B fragments
+    v8i a[4], b[kJT]; // the slice's A fragments, the half's B fragments
     float wi[4];      // 128x128 B: weight of row i; 1x128 B: sA of row i
-    v4f sbq[4];       // 1x128 B: the half's column scales, per 16-column tile
+    v4f sbq[kJT];     // 1x128 B: the half's column scales, per 16-column tile
     v4f pr[3];        // MFMA results awaiting promotion (tile t in pr[t % 3])
 
     // weight of tile (i, column tile jj of the half) for element e
@@ -1001,28 +779,29 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_pp_kernel(const uint8_t
         const int i = t & 3, jj = t >> 2;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            acc[i][4 * h + jj][e] = __builtin_fmaf(pr[t % 3][e], weight(i, jj, e), acc[i][4 * h + jj][e]);
+            acc[i][kJT * h + jj][e] = __builtin_fmaf(pr[t % 3][e], weight(i, jj, e), acc[i][kJT * h + jj][e]);
         // keeps these FMAs in their phase (ordered with the phase boundary's
         // volatile statements)
-        asm volatile("" : "+v"(acc[i][4 * h + jj]));
+        asm volatile("" : "+v"(acc[i][kJT * h + jj]));
     };
     // compute phase of half h: MFMA of tile t, then the promotion of tile t - 2
-    // (its result has landed); tiles 14 and 15 are promoted by the next phase
+    // (its result has landed); the last two tiles are promoted by the next phase
+    constexpr int kT = 4 * kJT;
     auto compute = [&](auto hc) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
+        for (int t = 0; t < kT; ++t) {
             pr[t % 3] = mfma16x16x128<FB, FA>(b[t >> 2], a[t & 3], v4f{0.f, 0.f, 0.f, 0.f});
             if (t >= 2) promote(hc, t - 2);
         }
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
+        for (int t = 0; t < kT; ++t) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
             if (t >= 2) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0); // promotion FMAs
         }
     };
     auto tail = [&](auto hc) {
-        promote(hc, 14);
-        promote(hc, 15);
+        promote(hc, kT - 2);
+        promote(hc, kT - 1);
     };
     auto read_a = [&](const uint8_t *st) {
 #pragma unroll
@@ -1030,7 +809,7 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_pp_kernel(const uint8_t
     };
     auto read_b = [&](const uint8_t *st) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) b[jj] = read_frag(st, wn * 64 + 16 * jj + fr, fg);
+        for (int jj = 0; jj < kJT; ++jj) b[jj] = read_frag(st, wn * kQ + 16 * jj + fr, fg);
     };
     // the slice's weights (with the first half) and the half's 1x128 column scales
     auto read_scales = [&](const float *ssa_, const float *ssbh, int h) {
@@ -1039,15 +818,17 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_pp_kernel(const uint8_t
 #pragma unroll
                 for (int i = 0; i < 4; ++i) wi[i] = ssa_[wm * 64 + 16 * i + fr];
             } else {
-                const float sb = ssbh[wn];
+                // a wave's 2Q columns lie in column block wn of a full tile,
+                // in the one block of a half tile
+                const float sb = ssbh[kBN == kBM ? wn : 0];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) wi[i] = ssa_[wm * 64 + 16 * i + fr] * sb;
             }
         }
         if constexpr (kRowB) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                sbq[jj] = *reinterpret_cast<const v4f *>(ssbh + wn * 64 + 16 * jj + 4 * fg);
+            for (int jj = 0; jj < kJT; ++jj)
+                sbq[jj] = *reinterpret_cast<const v4f *>(ssbh + wn * kQ + 16 * jj + 4 * fg);
         }
     };
     // Phase boundaries.  The scheduling barriers keep every instruction on
@@ -1111,10 +892,9 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_pp_kernel(const uint8_t
 #pragma unroll
     for (int q = 0; q < 3; ++q) pr[q] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        wi[i] = 0.0f;
-        sbq[i] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int i = 0; i < 4; ++i) wi[i] = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < kJT; ++jj) sbq[jj] = v4f{0.f, 0.f, 0.f, 0.f};
     if (!gx) sync(); // group Y starts one phase later
     int kb = 0;
     for (; kb + 1 < kblocks; kb += 2) {
@@ -1130,12 +910,12 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_pp_kernel(const uint8_t
     asm volatile("" ::: "memory");
 
     // epilogue: lane (fr, fg) of tile (i, j) holds C[row][4 consecutive cols];
-    // each wave stages its 64x128 results in 16 KiB of the freed stages
+    // each wave stages its 64 x 2Q results in kB2 bytes of the freed stages
     const float out_scale = kOut >= kOutE4M3 ? 1.0f / *epi.out_si : 0.0f;
     uint32_t m = 0;
     {
-        typedef EpiStage<128, out_bytes<kOut>(), 64, kB2> ES;
-        const int64_t wrow0 = m0 + wm * 64, wcol0 = n0 + wn * 128;
+        typedef EpiStage<2 * kQ, out_bytes<kOut>(), 64, kB2> ES;
+        const int64_t wrow0 = m0 + wm * 64, wcol0 = n0 + wn * 2 * kQ;
         const bool inside = wrow0 < M && wcol0 < N;
         uint8_t *ep = (w < 4 ? st0 : st1) + (w & 3) * kB2;
 #pragma unroll
@@ -1146,7 +926,7 @@ __global__ __launch_bounds__(kBSThreads, 1) void gemm_bs_pp_kernel(const uint8_t
                 for (int i = 0; i < 4; ++i) {
                     if ((16 * i) / ES::kPassRows != ps) continue;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
+                    for (int j = 0; j < 2 * kJT; ++j) {
                         const uint4 bits =
                             pack_out4<kOut, kAmax, kFuse>(wcol0 + 16 * j + 4 * fg, acc[i][j], m, epi, out_scale);
                         ES::put(ep, 16 * i + fr - ps * ES::kPassRows, 4 * j + fg, bits);
@@ -1176,7 +956,6 @@ hipError_t launch_gemm_epi(const GemmArgs &a)
     const int n_main = (r > 0 && 2 * r <= a.cus) ? tiles - r : tiles;
     const int n_half = 2 * (tiles - n_main);
     uint32_t *part = a.gs ? a.gs->part : nullptr;
-    uint32_t *part_half = part;
     if (a.mode == 0 || a.mode == 3) {
 #define FP8Q_PT_LAUNCH(FLAG, BN, GRID, PART, BASE)                                                                  \
         do {                                                                                                        \
@@ -1189,40 +968,30 @@ hipError_t launch_gemm_epi(const GemmArgs &a)
         } while (0)
         if (a.mode == 0) {
             if (n_main > 0) FP8Q_PT_LAUNCH(false, kBM, n_main, part, 0);
-            if (n_half > 0) FP8Q_PT_LAUNCH(false, kBM / 2, n_half, part_half, n_main);
+            if (n_half > 0) FP8Q_PT_LAUNCH(false, kBM / 2, n_half, part, n_main);
         } else {
             if (n_main > 0) FP8Q_PT_LAUNCH(true, kBM, n_main, part, 0);
-            if (n_half > 0) FP8Q_PT_LAUNCH(true, kBM / 2, n_half, part_half, n_main);
+            if (n_half > 0) FP8Q_PT_LAUNCH(true, kBM / 2, n_half, part, n_main);
         }
 #undef FP8Q_PT_LAUNCH
     } else {
-#define FP8Q_BS_LAUNCH(ROWB, BN, GRID, PART, BASE)                                                                  \
+#define FP8Q_BS_PP_LAUNCH(ROWB, BN, GRID, BASE)                                                                     \
         do {                                                                                                        \
             if (a.amax_out)                                                                                         \
-                gemm_bs_kernel<FA, FB, true, kOut, kFuse, ROWB, BN><<<GRID, kBSThreads, 0, a.stream>>>(             \
-                    a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, PART, BASE, n_main);                                   \
+                gemm_bs_pp_kernel<FA, FB, true, kOut, kFuse, ROWB, BN><<<GRID, kBSThreads, 0, a.stream>>>(          \
+                    a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, part, BASE, n_main);                                   \
             else                                                                                                    \
-                gemm_bs_kernel<FA, FB, false, kOut, kFuse, ROWB, BN><<<GRID, kBSThreads, 0, a.stream>>>(            \
-                    a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, PART, BASE, n_main);                                   \
-        } while (0)
-#define FP8Q_BS_PP_LAUNCH(ROWB)                                                                                     \
-        do {                                                                                                        \
-            if (a.amax_out)                                                                                         \
-                gemm_bs_pp_kernel<FA, FB, true, kOut, kFuse, ROWB><<<n_main, kBSThreads, 0, a.stream>>>(            \
-                    a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, part, n_main);                                         \
-            else                                                                                                    \
-                gemm_bs_pp_kernel<FA, FB, false, kOut, kFuse, ROWB><<<n_main, kBSThreads, 0, a.stream>>>(           \
-                    a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, part, n_main);                                         \
+                gemm_bs_pp_kernel<FA, FB, false, kOut, kFuse, ROWB, BN><<<GRID, kBSThreads, 0, a.stream>>>(         \
+                    a.A, a.B, a.sA, a.sB, m, n, k, a.C, epi, part, BASE, n_main);                                   \
         } while (0)
         if (a.mode == 1) {
-            if (n_main > 0) FP8Q_BS_PP_LAUNCH(false);
-            if (n_half > 0) FP8Q_BS_LAUNCH(false, kBM / 2, n_half, part_half, n_main);
+            if (n_main > 0) FP8Q_BS_PP_LAUNCH(false, kBM, n_main, 0);
+            if (n_half > 0) FP8Q_BS_PP_LAUNCH(false, kBM / 2, n_half, n_main);
         } else {
-            if (n_main > 0) FP8Q_BS_PP_LAUNCH(true);
-            if (n_half > 0) FP8Q_BS_LAUNCH(true, kBM / 2, n_half, part_half, n_main);
+            if (n_main > 0) FP8Q_BS_PP_LAUNCH(true, kBM, n_main, 0);
+            if (n_half > 0) FP8Q_BS_PP_LAUNCH(true, kBM / 2, n_half, n_main);
         }
 #undef FP8Q_BS_PP_LAUNCH
-#undef FP8Q_BS_LAUNCH
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.amax_out) return e;
