@@ -10,9 +10,10 @@ distinct inputs (4 GiB) are resident in HBM before timing and cycled, so the
 
 value = algorithmic bytes moved per step (2 B read + 1 B written per element)
 / time, in GB/s, the time taken from two HIP events around the timed steps on
-the stream they run on.  One step is one launch of the fused entry point (the
-cast kernel and the one-block ring update behind it), so the roofline object
-uses that same per-step duration.
+the stream they run on.  One step is one call of the fused entry point, a
+single launch (the casting blocks and the finishing block that folds their
+amax partials and updates the ring), so the roofline object uses that same
+per-step duration.
 
 Every other row of the hot path (the per-tensor fp32 1024x1024 current-scaling
 workload, amax, current scaling, dequantize, rowwise + columnwise, 128x128
@@ -43,11 +44,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 FP8_MFMA_PEAK_TFLOPS = 5000.0
 MFMA_PEAK_SCLK_MHZ = 2400.0  # the clock the 5.0 PFLOP/s figure assumes (256 CUs x 8192 FP8 flop/clk)
-# HBM bytes of one delayed step (cast_kernel + delayed_kernel), from the
-# FETCH_SIZE and WRITE_SIZE counters scaled by the factors a plain copy gives
-# (profiles/hbm_traffic_bench_kernels.md); None whenever either kernel has
-# changed since the counters were taken.
-TRAFFIC_BYTES_PER_STEP = 201716184
+# HBM bytes of one delayed step (the cast kernel with its finishing block),
+# from the FETCH_SIZE and WRITE_SIZE counters scaled by the factors a plain
+# copy gives (profiles/hbm_traffic_bench_kernels.md); None whenever the kernel
+# has changed since the counters were taken.
+TRAFFIC_BYTES_PER_STEP = None
 
 # Seconds of untimed launches before each row is timed.  The GPU's clocks
 # take tens of milliseconds of sustained matrix work to settle: measured on
@@ -320,7 +321,7 @@ def headline(args, fq, torch, xs, stream, n):
                    "bytes_per_step": bytes_per_step, "host_wall_s": round(wall, 4),
                    "step_ms_p10_p50_p90": [spread["ms_p10"], spread["ms"], spread["ms_p90"]],
                    "sclk": spread.get("sclk")},
-        "roofline": {"kernel": "fp8_quantize_delayed: cast_kernel (fused amax) + delayed_kernel",
+        "roofline": {"kernel": "fp8_quantize_delayed: cast_kernel (fused amax, finishing block updates the ring)",
                      "bound": "hbm", "achieved": round(value, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
                      "traffic": TRAFFIC_BYTES_PER_STEP, "kernel_avg_us": round(ms_per_step * 1e3, 3),

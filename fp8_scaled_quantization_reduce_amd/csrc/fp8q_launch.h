@@ -9,14 +9,16 @@
 namespace fp8q {
 
 // Grid-wide reduction scratch.  A flat or tile kernel that reduces an amax
-// runs at most kParts blocks (grid-stride loops cover larger inputs) and
-// block b stores its canonical magnitude max to part[b]; a GEMM block folds
-// its max into part[b % kParts] with an unsigned atomic max (the canonical
-// magnitude bits order like the values, and the canonical NaN sorts above
-// +inf).  The cast statistics add each block's four counts into
-// cnt[k][b % kCntParts].  One small kernel then reads the slots the call used,
-// writes the result and puts them back to zero, so a scratch is all zeros
-// between calls (it starts zeroed, as a device global).
+// runs at most kParts producing blocks (grid-stride loops cover larger
+// inputs) and block b stores its canonical magnitude max, flagged by the top
+// bit, to part[b]; a GEMM block folds its max into part[b % kParts] with an
+// unsigned atomic max (the canonical magnitude bits order like the values, and
+// the canonical NaN sorts above +inf).  The cast statistics add each block's
+// four counts into cnt[k][b % kCntParts].  Then either the launch's own
+// finishing block (the amax, the cast with output amax and the delayed step)
+// waits for the flagged partials, or one small kernel follows; either reads
+// the slots the call used, writes the result and puts them back to zero, so a
+// scratch is all zeros between calls (it starts zeroed, as a device global).
 #ifndef FP8Q_REDUCE_GRID
 #define FP8Q_REDUCE_GRID 1024
 #endif

@@ -64,17 +64,29 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t v, hipStream_t s)
     return hipGetLastError();
 }
 
-// One block's magnitude max -> its partial slot (canonical amax bits).  Every
-// lane must reach it.  The launch has at most kParts blocks.
+// One block's magnitude max -> its partial slot: the canonical amax bits
+// (below 2^31) with the top bit set, so that a slot reads zero until its
+// block has published.  The store is an agent-scope atomic, visible to the
+// agent-scope loads of a finishing block running on another XCD while this
+// kernel still runs.  Every lane must reach it.  The launch has at most kParts
+// producing blocks.
+constexpr uint32_t kPartFlag = 0x80000000u;
+
 __device__ __forceinline__ void block_partial(uint32_t m, GridScratch *gs)
 {
     __shared__ uint32_t red[kThreads / 64];
     m = block_max_u32<kThreads>(m, red);
-    if (threadIdx.x == 0) gs->part[blockIdx.x] = canonical_amax_bits(m);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&gs->part[blockIdx.x], canonical_amax_bits(m) | kPartFlag, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Read partial slot i and put it back to zero (one round trip).
-__device__ __forceinline__ uint32_t take_partial(GridScratch *gs, int i) { return atomicExch(&gs->part[i], 0u); }
+// Read partial slot i and put it back to zero (one round trip).  GEMM blocks
+// fold unflagged maxima into their slots; either way the flag is dropped.
+__device__ __forceinline__ uint32_t take_partial(GridScratch *gs, int i)
+{
+    return atomicExch(&gs->part[i], 0u) & ~kPartFlag;
+}
 
 // Max of partial slots [0, nparts), which it leaves zero; kThreads lanes with
 // up to kParts / kThreads exchanges in flight each.  Every lane gets the result.
@@ -88,6 +100,123 @@ __device__ __forceinline__ uint32_t take_partials(GridScratch *gs, int nparts)
         if (i < nparts) m = max(m, take_partial(gs, i));
     }
     return block_max_u32<kThreads>(m, red);
+}
+
+// The finishing block of a launch (its last block, after nparts producing
+// blocks): every lane polls its slots with agent-scope loads, sleeping
+// briefly between rounds, until the whole block has seen all nparts partials
+// published, then the block returns their max to every lane and clears the
+// slots.  It waits only for blocks of its own launch, which never wait, so the
+// wait ends once they have run; the rounds are bounded all the same (about a
+// second and more of polling), after which the result is the canonical NaN.
+// This replaces a second, one-block kernel whose launch would follow the
+// producers' end.
+constexpr int kPollRounds = 1 << 21;
+
+__device__ __forceinline__ uint32_t collect_partials(GridScratch *gs, int nparts)
+{
+    __shared__ uint32_t red[kThreads / 64];
+    constexpr int kPer = kParts / kThreads;
+    uint32_t m = 0;
+    unsigned left = 0; // bit u: slot threadIdx.x + u * kThreads not seen yet
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+        if (threadIdx.x + u * kThreads < nparts) left |= 1u << u;
+    bool expired = true;
+    for (int round = 0; round < kPollRounds; ++round) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            if (left & (1u << u)) {
+                const uint32_t v = __hip_atomic_load(&gs->part[threadIdx.x + u * kThreads], __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                if (v & kPartFlag) {
+                    m = max(m, v & ~kPartFlag);
+                    left &= ~(1u << u);
+                }
+            }
+        }
+        if (__syncthreads_and(left == 0)) { // block-uniform
+            expired = false;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+        if (threadIdx.x + u * kThreads < nparts)
+            __hip_atomic_store(&gs->part[threadIdx.x + u * kThreads], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    m = block_max_u32<kThreads>(m, red);
+    return expired ? kCanonicalNaN : m;
+}
+
+// Delayed-scaling update ("Megatron FP8", section 5): write the step's amax
+// at slot step % L of column col of the ring hist[L][n_cols], reduce the
+// column (max, NaN-propagating; algo 0) or take the value just written (algo
+// 1), and derive s = eff / FP8_MAX * 2^margin (1 when eff is not > 0) and its
+// reciprocal for the column's next cast.  L may be any length.
+struct DelayedUpdate {
+    float *hist; // null: no update
+    int L, n_cols, col, slot;
+    float fmax;
+    int margin, algo;
+    float *scale, *scale_inv;
+};
+
+// Order-preserving key of a float for an unsigned max (negative values flip
+// all bits, positive values set the sign bit); every NaN maps above +inf, so
+// a NaN anywhere in the column wins the max.
+__device__ __forceinline__ uint32_t order_key(float h)
+{
+    const uint32_t b = __float_as_uint(h);
+    if (h != h) return 0xFFFFFFFFu;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// The largest key of the column other than the slot being overwritten; a
+// block of kThreads lanes, every lane gets it.
+__device__ __forceinline__ uint32_t ring_key(const DelayedUpdate &d)
+{
+    __shared__ uint32_t red[kThreads / 64];
+    uint32_t key = 0;
+    for (int j = threadIdx.x; j < d.L; j += kThreads)
+        if (j != d.slot) key = max(key, order_key(d.hist[(int64_t)j * d.n_cols + d.col]));
+    return block_max_u32<kThreads>(key, red);
+}
+
+// One lane: record amax a and write the column's new scales.
+__device__ __forceinline__ void ring_update(const DelayedUpdate &d, float a, uint32_t key)
+{
+    d.hist[(int64_t)d.slot * d.n_cols + d.col] = a;
+    key = max(key, order_key(a));
+    float eff;
+    if (d.algo == 0)
+        eff = key == 0xFFFFFFFFu ? __uint_as_float(kCanonicalNaN)
+                                 : __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+    else
+        eff = a;
+    const float sv = (eff > 0.0f) ? ldexpf(eff / d.fmax, d.margin) : 1.0f;
+    d.scale_inv[d.col] = sv;
+    d.scale[d.col] = 1.0f / sv;
+}
+
+// What the finishing block of a reducing launch does with the amax: publish
+// it (amax_out, canonical bits) and, for a delayed-scaling step, record it in
+// the ring.  A launch has a finishing block when either is set.
+struct Finish {
+    uint32_t *amax_out;
+    DelayedUpdate du;
+    __device__ __host__ bool active() const { return amax_out != nullptr || du.hist != nullptr; }
+};
+
+__device__ __forceinline__ void finish_block(const Finish &f, GridScratch *gs, int nparts)
+{
+    // the ring is read while the producers still run
+    const uint32_t key = f.du.hist ? ring_key(f.du) : 0u;
+    const uint32_t a = collect_partials(gs, nparts);
+    if (threadIdx.x == 0) {
+        if (f.amax_out) *f.amax_out = a;
+        if (f.du.hist) ring_update(f.du, __uint_as_float(a), key);
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void finish_amax_kernel(GridScratch *__restrict__ gs, int nparts,
@@ -166,16 +295,23 @@ hipError_t launch_clock_monitor(uint64_t *out, const uint32_t *stop, hipStream_t
 #endif
 constexpr int kAmaxU = FP8Q_AMAX_U;
 
+// The launch's last block is the finishing block, which writes the amax.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void amax_kernel(const void *__restrict__ x, int64_t n, GridScratch *gs)
+__global__ __launch_bounds__(kThreads) void amax_kernel(const void *__restrict__ x, int64_t n, GridScratch *gs,
+                                                        uint32_t *__restrict__ amax_out)
 {
+    const int nwork = gridDim.x - 1;
+    if (blockIdx.x == nwork) {
+        finish_block(Finish{amax_out, DelayedUpdate{}}, gs, nwork);
+        return;
+    }
     constexpr int kPer = DT == kBF16 ? 8 : 4; // elements per 16-byte vector
     const int64_t nvec = n / kPer;
     const int64_t units = ceil_div(nvec, (int64_t)kThreads * kAmaxU);
     const uint4 *__restrict__ xv = reinterpret_cast<const uint4 *>(x);
     uint32_t m = 0;
     u16x2 m2 = {0, 0};
-    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    for (int64_t unit = blockIdx.x; unit < units; unit += nwork) {
         const int64_t base = unit * kThreads * kAmaxU + threadIdx.x;
         // lanes past the end re-read the last vector (harmless for a max)
         uint4 v[kAmaxU];
@@ -213,14 +349,14 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void *__restrict__
 hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScratch *gs, hipStream_t s)
 {
     const int64_t nvec = n / (dtype == kBF16 ? 8 : 4);
-    const int grid = reduce_grid(ceil_div(nvec, (int64_t)kThreads * kAmaxU), kAmaxGrid);
+    // the producing blocks and the finishing block
+    const int grid = reduce_grid(ceil_div(nvec, (int64_t)kThreads * kAmaxU), kAmaxGrid) + 1;
+    uint32_t *out = reinterpret_cast<uint32_t *>(amax);
     if (dtype == kBF16)
-        amax_kernel<kBF16><<<grid, kThreads, 0, s>>>(x, n, gs);
+        amax_kernel<kBF16><<<grid, kThreads, 0, s>>>(x, n, gs, out);
     else
-        amax_kernel<kF32><<<grid, kThreads, 0, s>>>(x, n, gs);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_finish_amax(gs, grid, amax, s);
+        amax_kernel<kF32><<<grid, kThreads, 0, s>>>(x, n, gs, out);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ cast --
@@ -407,8 +543,14 @@ constexpr int kCastU = FP8Q_CAST_U;
 template <int F, int DT, bool kAmax, bool kCount = false>
 __global__ __launch_bounds__(kThreads) void cast_kernel(const void *__restrict__ x, int64_t n, ScaleSrc src,
                                                         uint8_t *__restrict__ q, float *scale_inv_out,
-                                                        float *scale_out, GridScratch *gs)
+                                                        float *scale_out, GridScratch *gs, Finish fin)
 {
+    // with a finisher (kAmax only) the launch's last block finishes the call
+    const int nwork = gridDim.x - (kAmax && fin.active() ? 1 : 0);
+    if (kAmax && blockIdx.x == nwork) {
+        finish_block(fin, gs, nwork);
+        return;
+    }
     const Scales sc = resolve_scales<F>(src);
     uint32_t T[kStats], g[kStats] = {0, 0, 0, 0};
     if constexpr (kCount) stat_thresholds<F>(sc.scale, T);
@@ -421,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const void *__restrict__
     uint4 *__restrict__ qv = reinterpret_cast<uint4 *>(q);
     uint32_t m = 0;
     u16x2 m2 = {0, 0};
-    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    for (int64_t unit = blockIdx.x; unit < units; unit += nwork) {
         const int64_t base = unit * kThreads * kCastU + threadIdx.x;
         // Lanes past the end re-read the last chunk (a valid address, so all
         // loads are unconditional and stay in registers) and store nothing;
@@ -472,18 +614,22 @@ static hipError_t launch_cast_t(const void *x, int64_t n, ScaleSrc src, uint8_t 
 {
     const int64_t units = ceil_div(n >> 4, (int64_t)kThreads * kCastU);
     const int grid = (amax_out || stats) ? reduce_grid(units) : flat_grid(units);
+    const Finish none{nullptr, DelayedUpdate{}};
     if (stats) {
+        // the counts are summed by the statistics kernel, which follows
         if (amax_out)
-            cast_kernel<F, DT, true, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs);
+            cast_kernel<F, DT, true, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs, none);
         else
-            cast_kernel<F, DT, false, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs);
+            cast_kernel<F, DT, false, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs, none);
     } else if (amax_out) {
-        cast_kernel<F, DT, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs);
+        // the producing blocks and the finishing block, which writes the amax
+        const Finish fin{reinterpret_cast<uint32_t *>(amax_out), DelayedUpdate{}};
+        cast_kernel<F, DT, true><<<grid + 1, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs, fin);
     } else {
-        cast_kernel<F, DT, false><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, nullptr);
+        cast_kernel<F, DT, false><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, nullptr, none);
     }
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && amax_out) e = launch_finish_amax(gs, grid, amax_out, s);
+    if (e == hipSuccess && stats && amax_out) e = launch_finish_amax(gs, grid, amax_out, s);
     if (e == hipSuccess && stats) e = launch_finish_stats(gs, stats, s);
     return e;
 }
@@ -736,116 +882,59 @@ hipError_t launch_error_feedback(const void *g, int dtype, float *residual, int6
 }
 
 // --------------------------------------------------------------- delayed --
-// Delayed-scaling update ("Megatron FP8", section 5): write the new amax at
-// slot step % L of column col, reduce the column (max, NaN-propagating) or take
-// the value just written, derive s = eff / FP8_MAX * 2^margin (1 when eff is
-// not > 0) and its reciprocal.  One block; L may be any length.  The new amax
-// is either read from memory or, for the fused step, reduced here from the
-// cast kernel's partial slots (which it leaves zero) and published to
-// amax_out.
-constexpr int kDelayedThreads = 256;
-
-// Order-preserving key of a float for an unsigned max (negative values flip
-// all bits, positive values set the sign bit); every NaN maps above +inf, so
-// a NaN anywhere in the column wins the max.
-__device__ __forceinline__ uint32_t order_key(float h)
+// The standalone update (fp8_update_delayed): the new amax is read from
+// memory; one block records it and derives the column's scales.
+__global__ __launch_bounds__(kThreads) void delayed_kernel(DelayedUpdate d, const float *__restrict__ new_amax)
 {
-    const uint32_t b = __float_as_uint(h);
-    if (h != h) return 0xFFFFFFFFu;
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-__global__ __launch_bounds__(kDelayedThreads) void delayed_kernel(float *__restrict__ hist, int L, int n_cols, int col,
-                                                                  const float *__restrict__ new_amax,
-                                                                  GridScratch *__restrict__ gs, int nparts,
-                                                                  float *__restrict__ amax_out, int slot, float fmax,
-                                                                  int margin, int algo, float *__restrict__ scale,
-                                                                  float *__restrict__ scale_inv)
-{
-    __shared__ uint32_t red_a[kDelayedThreads / 64];
-    __shared__ uint32_t red_k[kDelayedThreads / 64];
-    const int tid = threadIdx.x;
-    // The lane's first history entry is loaded before the partials so that
-    // both round trips overlap.
-    const bool h0_valid = tid < L && tid != slot;
-    const float h0 = h0_valid ? hist[(int64_t)tid * n_cols + col] : 0.0f;
-    uint32_t m0 = 0;
-    if (gs)
-#pragma unroll
-        for (int u = 0; u < kParts / kDelayedThreads; ++u)
-            if (tid + u * kDelayedThreads < nparts) m0 = max(m0, take_partial(gs, tid + u * kDelayedThreads));
-    // largest entry of the column other than the slot being overwritten
-    uint32_t key = h0_valid ? order_key(h0) : 0u;
-    for (int j = tid + kDelayedThreads; j < L; j += kDelayedThreads)
-        if (j != slot) key = max(key, order_key(hist[(int64_t)j * n_cols + col]));
-    // one exchange for both maxima
-    uint32_t m = wave_max_u32(m0);
-    key = wave_max_u32(key);
-    if ((tid & 63) == 0) {
-        red_a[tid >> 6] = m;
-        red_k[tid >> 6] = key;
-    }
-    __syncthreads();
-    if (tid == 0) {
-#pragma unroll
-        for (int w = 1; w < kDelayedThreads / 64; ++w) {
-            m = max(m, red_a[w]);
-            key = max(key, red_k[w]);
-        }
-        const float a = gs ? __uint_as_float(m) : *new_amax;
-        if (gs && amax_out) *amax_out = a;
-        hist[(int64_t)slot * n_cols + col] = a;
-        key = max(key, order_key(a));
-        float eff;
-        if (algo == 0)
-            eff = key == 0xFFFFFFFFu ? __uint_as_float(kCanonicalNaN)
-                                     : __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
-        else
-            eff = a;
-        const float s = (eff > 0.0f) ? ldexpf(eff / fmax, margin) : 1.0f;
-        scale_inv[col] = s;
-        scale[col] = 1.0f / s;
-    }
+    const uint32_t key = ring_key(d);
+    if (threadIdx.x == 0) ring_update(d, *new_amax, key);
 }
 
 static float fmax_of(int fmt) { return fmt == kE4M3 ? Fmt<kE4M3>::kMax : Fmt<kE5M2>::kMax; }
 
+static DelayedUpdate make_update(float *hist, int history_len, int n_cols, int col, int64_t step, int fmt, int margin,
+                                 int algo, float *scale, float *scale_inv)
+{
+    return DelayedUpdate{hist, history_len, n_cols, col, (int)(step % history_len), fmax_of(fmt), margin, algo,
+                         scale, scale_inv};
+}
+
 hipError_t launch_delayed(float *hist, int history_len, int n_cols, int col, const float *new_amax, int64_t step,
                           int fmt, int margin, int algo, float *scale, float *scale_inv, hipStream_t s)
 {
-    const int slot = (int)(step % history_len);
-    delayed_kernel<<<1, kDelayedThreads, 0, s>>>(hist, history_len, n_cols, col, new_amax, nullptr, 0, nullptr, slot,
-                                                 fmax_of(fmt), margin, algo, scale, scale_inv);
+    delayed_kernel<<<1, kThreads, 0, s>>>(make_update(hist, history_len, n_cols, col, step, fmt, margin, algo, scale,
+                                                      scale_inv),
+                                          new_amax);
     return hipGetLastError();
 }
 
-// One delayed-scaling step: cast x with the stored scale of column col
-// (scale_inv[col]), reducing the input's amax into per-block partials, then one
-// block folds the partial slots, publishes the amax and updates the ring and
-// the column's scales for the format of the next step.
+// One delayed-scaling step, one launch: the cast of x with the stored scale of
+// column col (scale_inv[col]) reduces the input's amax into per-block
+// partials, and the launch's finishing block folds them, publishes the amax
+// and updates the ring and the column's scales for the format of the next
+// step.  The scale it overwrites is read by every casting block at its start,
+// before that block publishes its partial, so no block of this launch casts
+// with the next step's scale.
 hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, float *hist, int history_len, int n_cols,
                                int col, int64_t step, int fmt_next, int margin, int algo, float *scale,
                                float *scale_inv, uint8_t *q, float *q_scale_inv_out, float *amax_out, GridScratch *gs,
                                hipStream_t s)
 {
     const ScaleSrc src{nullptr, scale_inv + col, 0};
-    const int grid = reduce_grid(ceil_div(n >> 4, (int64_t)kThreads * kCastU));
+    const Finish fin{reinterpret_cast<uint32_t *>(amax_out),
+                     make_update(hist, history_len, n_cols, col, step, fmt_next, margin, algo, scale, scale_inv)};
+    const int grid = reduce_grid(ceil_div(n >> 4, (int64_t)kThreads * kCastU)) + 1;
     if (fmt == kE4M3) {
         if (dtype == kBF16)
-            cast_kernel<kE4M3, kBF16, true><<<grid, kThreads, 0, s>>>(x, n, src, q, q_scale_inv_out, nullptr, gs);
+            cast_kernel<kE4M3, kBF16, true><<<grid, kThreads, 0, s>>>(x, n, src, q, q_scale_inv_out, nullptr, gs, fin);
         else
-            cast_kernel<kE4M3, kF32, true><<<grid, kThreads, 0, s>>>(x, n, src, q, q_scale_inv_out, nullptr, gs);
+            cast_kernel<kE4M3, kF32, true><<<grid, kThreads, 0, s>>>(x, n, src, q, q_scale_inv_out, nullptr, gs, fin);
     } else {
         if (dtype == kBF16)
-            cast_kernel<kE5M2, kBF16, true><<<grid, kThreads, 0, s>>>(x, n, src, q, q_scale_inv_out, nullptr, gs);
+            cast_kernel<kE5M2, kBF16, true><<<grid, kThreads, 0, s>>>(x, n, src, q, q_scale_inv_out, nullptr, gs, fin);
         else
-            cast_kernel<kE5M2, kF32, true><<<grid, kThreads, 0, s>>>(x, n, src, q, q_scale_inv_out, nullptr, gs);
+            cast_kernel<kE5M2, kF32, true><<<grid, kThreads, 0, s>>>(x, n, src, q, q_scale_inv_out, nullptr, gs, fin);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int slot = (int)(step % history_len);
-    delayed_kernel<<<1, kDelayedThreads, 0, s>>>(hist, history_len, n_cols, col, nullptr, gs, grid, amax_out, slot,
-                                                 fmax_of(fmt_next), margin, algo, scale, scale_inv);
     return hipGetLastError();
 }
 

@@ -19,7 +19,9 @@
  *    device and held until the process ends.  Each stream gets a slot of its
  *    own the first time it runs such a call (a host-side table; no device
  *    work), so calls on different streams never share partials.  The slot is
- *    all zeros between calls: the call's last kernel reads it and clears it.
+ *    all zeros between calls: the call's finishing block (the last block of
+ *    its reducing launch, which waits for the other blocks' partials) or its
+ *    last kernel reads it and clears it.
  *    While one call enqueues its kernels it holds a host lock on its slot, so
  *    host threads that share a stream are safe.  A device on which more than
  *    64 streams have run reducing calls returns FP8Q_EUNSUPPORTED.
