@@ -64,21 +64,14 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t v, hipStream_t s)
     return hipGetLastError();
 }
 
-// One block's magnitude max -> its partial slot: the canonical amax bits
-// (below 2^31) with the top bit set, so that a slot reads zero until its
-// block has published.  The store is an agent-scope atomic, visible to the
-// agent-scope loads of a finishing block running on another XCD while this
-// kernel still runs.  Every lane must reach it.  The launch has at most kParts
-// producing blocks.
-constexpr uint32_t kPartFlag = 0x80000000u;
+// One block's magnitude max -> its partial slot, flagged (publish_partial).
+// Every lane must reach it.  The launch has at most kParts producing blocks.
 
 __device__ __forceinline__ void block_partial(uint32_t m, GridScratch *gs)
 {
     __shared__ uint32_t red[kThreads / 64];
     m = block_max_u32<kThreads>(m, red);
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&gs->part[blockIdx.x], canonical_amax_bits(m) | kPartFlag, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) publish_partial(&gs->part[blockIdx.x], canonical_amax_bits(m));
 }
 
 // Read partial slot i and put it back to zero (one round trip).  GEMM blocks
@@ -102,52 +95,6 @@ __device__ __forceinline__ uint32_t take_partials(GridScratch *gs, int nparts)
     return block_max_u32<kThreads>(m, red);
 }
 
-// The finishing block of a launch (its last block, after nparts producing
-// blocks): every lane polls its slots with agent-scope loads, sleeping
-// briefly between rounds, until the whole block has seen all nparts partials
-// published, then the block returns their max to every lane and clears the
-// slots.  It waits only for blocks of its own launch, which never wait, so the
-// wait ends once they have run; the rounds are bounded all the same (about a
-// second and more of polling), after which the result is the canonical NaN.
-// This replaces a second, one-block kernel whose launch would follow the
-// producers' end.
-constexpr int kPollRounds = 1 << 21;
-
-__device__ __forceinline__ uint32_t collect_partials(GridScratch *gs, int nparts)
-{
-    __shared__ uint32_t red[kThreads / 64];
-    constexpr int kPer = kParts / kThreads;
-    uint32_t m = 0;
-    unsigned left = 0; // bit u: slot threadIdx.x + u * kThreads not seen yet
-#pragma unroll
-    for (int u = 0; u < kPer; ++u)
-        if (threadIdx.x + u * kThreads < nparts) left |= 1u << u;
-    bool expired = true;
-    for (int round = 0; round < kPollRounds; ++round) {
-#pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-            if (left & (1u << u)) {
-                const uint32_t v = __hip_atomic_load(&gs->part[threadIdx.x + u * kThreads], __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-                if (v & kPartFlag) {
-                    m = max(m, v & ~kPartFlag);
-                    left &= ~(1u << u);
-                }
-            }
-        }
-        if (__syncthreads_and(left == 0)) { // block-uniform
-            expired = false;
-            break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u)
-        if (threadIdx.x + u * kThreads < nparts)
-            __hip_atomic_store(&gs->part[threadIdx.x + u * kThreads], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    m = block_max_u32<kThreads>(m, red);
-    return expired ? kCanonicalNaN : m;
-}
 
 // Delayed-scaling update ("Megatron FP8", section 5): write the step's amax
 // at slot step % L of column col of the ring hist[L][n_cols], reduce the
@@ -212,7 +159,7 @@ __device__ __forceinline__ void finish_block(const Finish &f, GridScratch *gs, i
 {
     // the ring is read while the producers still run
     const uint32_t key = f.du.hist ? ring_key(f.du) : 0u;
-    const uint32_t a = collect_partials(gs, nparts);
+    const uint32_t a = collect_partials<kThreads, kParts>(gs->part, nparts);
     if (threadIdx.x == 0) {
         if (f.amax_out) *f.amax_out = a;
         if (f.du.hist) ring_update(f.du, __uint_as_float(a), key);
@@ -794,11 +741,18 @@ __global__ __launch_bounds__(kThreads) void error_feedback_kernel(const void *__
                                                                   float *__restrict__ residual, int64_t n,
                                                                   const float *__restrict__ scale_inv,
                                                                   uint8_t *__restrict__ q, GridScratch *gs,
-                                                                  bool amax)
+                                                                  uint32_t *amax_out)
 {
     // v - value * s is rounded twice (product, then difference), as defined:
     // no fused multiply-add
 #pragma clang fp contract(off)
+    // with an amax the launch's last block is the finishing block
+    const bool amax = amax_out != nullptr;
+    const int nwork = gridDim.x - (amax ? 1 : 0);
+    if (amax && blockIdx.x == nwork) {
+        finish_block(Finish{amax_out, DelayedUpdate{}}, gs, nwork);
+        return;
+    }
     const float s = *scale_inv;
     const float scale = 1.0f / s;
     const int64_t nch = n >> 4;
@@ -806,7 +760,7 @@ __global__ __launch_bounds__(kThreads) void error_feedback_kernel(const void *__
     float4 *__restrict__ rv = reinterpret_cast<float4 *>(residual);
     uint4 *__restrict__ qv = reinterpret_cast<uint4 *>(q);
     uint32_t m = 0;
-    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    for (int64_t unit = blockIdx.x; unit < units; unit += nwork) {
         const int64_t base = unit * kThreads * kEfU + threadIdx.x;
         Chunk16<DT> ch[kEfU];
         float4 r[kEfU][4];
@@ -866,9 +820,10 @@ __global__ __launch_bounds__(kThreads) void error_feedback_kernel(const void *__
 hipError_t launch_error_feedback(const void *g, int dtype, float *residual, int64_t n, int fmt,
                                  const float *scale_inv, uint8_t *q, float *amax_out, GridScratch *gs, hipStream_t s)
 {
-    const bool am = amax_out != nullptr;
+    uint32_t *am = reinterpret_cast<uint32_t *>(amax_out);
     const int64_t units = ceil_div(n >> 4, (int64_t)kThreads * kEfU);
-    const int grid = am ? reduce_grid(units) : flat_grid(units);
+    // with an amax: the producing blocks and the finishing block
+    const int grid = am ? reduce_grid(units) + 1 : flat_grid(units);
     if (fmt == kE4M3) {
         if (dtype == kBF16) error_feedback_kernel<kE4M3, kBF16><<<grid, kThreads, 0, s>>>(g, residual, n, scale_inv, q, gs, am);
         else error_feedback_kernel<kE4M3, kF32><<<grid, kThreads, 0, s>>>(g, residual, n, scale_inv, q, gs, am);
@@ -876,9 +831,7 @@ hipError_t launch_error_feedback(const void *g, int dtype, float *residual, int6
         if (dtype == kBF16) error_feedback_kernel<kE5M2, kBF16><<<grid, kThreads, 0, s>>>(g, residual, n, scale_inv, q, gs, am);
         else error_feedback_kernel<kE5M2, kF32><<<grid, kThreads, 0, s>>>(g, residual, n, scale_inv, q, gs, am);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !am) return e;
-    return launch_finish_amax(gs, grid, amax_out, s);
+    return hipGetLastError();
 }
 
 // --------------------------------------------------------------- delayed --
@@ -1148,15 +1101,22 @@ __device__ __forceinline__ void store_transposed(const uint32_t *tl, uint8_t *q_
 }
 
 // One block loops over tiles t = blockIdx.x, blockIdx.x + G, ... (tile row
-// t / tiles_per_row, tile column t % tiles_per_row).
+// t / tiles_per_row, tile column t % tiles_per_row), G the number of tile
+// blocks (with kAmax the launch has one more, its finishing block).
 template <int F, int DT, int kMode, bool kAmax>
 __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__ x, int64_t rows, int64_t cols,
                                                         ScaleSrc src, uint8_t *__restrict__ q_row,
                                                         uint8_t *__restrict__ q_col, void *__restrict__ s_row_p,
                                                         void *__restrict__ s_col_p, float *scale_inv_out,
                                                         float *scale_out, GridScratch *gs, ScaleSrc src_col,
-                                                        float *col_scale_inv_out)
+                                                        float *col_scale_inv_out, uint32_t *amax_out)
 {
+    // with kAmax the launch's last block is the finishing block
+    const int nwork = gridDim.x - (kAmax ? 1 : 0);
+    if (kAmax && blockIdx.x == nwork) {
+        finish_block(Finish{amax_out, DelayedUpdate{}}, gs, nwork);
+        return;
+    }
     constexpr bool kHybrid = kMode >= kTileHybrid;
     constexpr int FC = kHybrid ? ((kMode - kTileHybrid) & 1) : F; // format of the column codes
     constexpr bool kDeq = kHybrid && ((kMode - kTileHybrid) >> 1); // columns from the dequantized rows
@@ -1205,7 +1165,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
         if (r0 < rows && c0 < cols) raw.load(x, cols, r0, c0);
         else raw.zero();
     };
-    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    for (int64_t t = blockIdx.x; t < tiles; t += nwork) {
         const int64_t tr = t / tiles_c, tc = t - tr * tiles_c;
         const int64_t row0 = tr * kTile, col0 = tc * kTile;
         const int64_t r0 = row0 + 4 * ig, c0 = col0 + 16 * jg;
@@ -1512,18 +1472,17 @@ template <int F, int DT>
 static hipError_t launch_rc_t(const void *x, int64_t rows, int64_t cols, ScaleSrc src, uint8_t *q_row, uint8_t *q_col,
                               float *scale_inv_out, float *scale_out, float *amax_out, GridScratch *gs, hipStream_t s)
 {
-    const int grid = tile_grid(rows, cols, amax_out != nullptr);
+    // with an amax: the producing blocks and the finishing block
+    const int grid = tile_grid(rows, cols, amax_out != nullptr) + (amax_out ? 1 : 0);
     if (amax_out)
-        tile_kernel<F, DT, kTilePerTensor, true><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr,
-                                                                          nullptr, scale_inv_out, scale_out, gs,
-                                                                          ScaleSrc{}, nullptr);
+        tile_kernel<F, DT, kTilePerTensor, true><<<grid, kThreads, 0, s>>>(
+            x, rows, cols, src, q_row, q_col, nullptr, nullptr, scale_inv_out, scale_out, gs, ScaleSrc{}, nullptr,
+            reinterpret_cast<uint32_t *>(amax_out));
     else
         tile_kernel<F, DT, kTilePerTensor, false><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr,
                                                                            nullptr, scale_inv_out, scale_out, nullptr,
-                                                                           ScaleSrc{}, nullptr);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !amax_out) return e;
-    return launch_finish_amax(gs, grid, amax_out, s);
+                                                                           ScaleSrc{}, nullptr, nullptr);
+    return hipGetLastError();
 }
 
 hipError_t launch_rowwise_colwise(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, ScaleSrc src,
@@ -1550,18 +1509,18 @@ static hipError_t launch_hybrid_m(const void *x, int64_t rows, int64_t cols, Sca
                                   uint8_t *q_row, uint8_t *q_col, float *row_scale_inv_out, float *col_scale_inv_out,
                                   float *amax_out, GridScratch *gs, hipStream_t s)
 {
-    const int grid = tile_grid(rows, cols, amax_out != nullptr);
+    // with an amax: the producing blocks and the finishing block
+    const int grid = tile_grid(rows, cols, amax_out != nullptr) + (amax_out ? 1 : 0);
     if (amax_out)
         tile_kernel<F, DT, kMode, true><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr, nullptr,
                                                                  row_scale_inv_out, nullptr, gs, src_col,
-                                                                 col_scale_inv_out);
+                                                                 col_scale_inv_out,
+                                                                 reinterpret_cast<uint32_t *>(amax_out));
     else
         tile_kernel<F, DT, kMode, false><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr, nullptr,
                                                                   row_scale_inv_out, nullptr, nullptr, src_col,
-                                                                  col_scale_inv_out);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !amax_out) return e;
-    return launch_finish_amax(gs, grid, amax_out, s);
+                                                                  col_scale_inv_out, nullptr);
+    return hipGetLastError();
 }
 
 template <int F, int DT>
@@ -1621,11 +1580,11 @@ static hipError_t launch_block_t(const void *x, int64_t rows, int64_t cols, int 
     if (block_rows == 128)
         tile_kernel<F, DT, kTileBlock128, false><<<grid, kThreads, 0, s>>>(x, rows, cols, none, q_row, q_col, s_row,
                                                                           s_col, nullptr, nullptr, nullptr, none,
-                                                                          nullptr);
+                                                                          nullptr, nullptr);
     else
         tile_kernel<F, DT, kTileBlock1x128, false><<<grid, kThreads, 0, s>>>(x, rows, cols, none, q_row, q_col,
                                                                             s_row, s_col, nullptr, nullptr, nullptr,
-                                                                            none, nullptr);
+                                                                            none, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -1635,7 +1594,7 @@ static hipError_t launch_mx_t(const void *x, int64_t rows, int64_t cols, uint8_t
 {
     const ScaleSrc none{nullptr, nullptr, 0};
     tile_kernel<F, DT, kTileMX, false><<<tile_grid(rows, cols), kThreads, 0, s>>>(
-        x, rows, cols, none, q_row, q_col, s_row, s_col, nullptr, nullptr, nullptr, none, nullptr);
+        x, rows, cols, none, q_row, q_col, s_row, s_col, nullptr, nullptr, nullptr, none, nullptr, nullptr);
     return hipGetLastError();
 }
 
