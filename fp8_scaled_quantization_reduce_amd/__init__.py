@@ -53,6 +53,7 @@ SIGNATURES = {
     "fp8_cast_stats": [_VP, _I32, _I64, _I32, _VP, _VP, _VP],
     "fp8_quantize_error_feedback": [_VP, _I32, _VP, _I64, _I32, _VP, _VP, _VP, _VP],
     "fp8q_clock_monitor": [_VP, _VP, _VP],
+    "fp8q_set_finish_poll_rounds": [ctypes.c_uint32, _VP],
     "fp8q_last_error": [],
 }
 
@@ -402,6 +403,21 @@ def fp8q_clock_monitor(out, stop, stream=None):
     _need(out, "out", _STATS, 3 * CLOCK_BLOCKS + 1)
     _need(stop, "stop", (torch.int32,), 1)
     _check(lib.fp8q_clock_monitor(_ptr(out, "out"), _ptr(stop, "stop"), _stream(stream)))
+
+
+POLL_ROUNDS_DEFAULT = 0xFFFFFFFF
+
+
+def fp8q_set_finish_poll_rounds(rounds):
+    """Set the bound on a finishing block's polling rounds for later calls
+    (a failure-handling knob; 0 makes every finishing block give up at once,
+    POLL_ROUNDS_DEFAULT restores the default) and return the bound that was
+    in force."""
+    if not 0 <= int(rounds) <= 0xFFFFFFFF:
+        raise ValueError("rounds must fit in 32 bits")
+    prev = ctypes.c_uint32(0)
+    _check(lib.fp8q_set_finish_poll_rounds(ctypes.c_uint32(int(rounds)), ctypes.byref(prev)))
+    return prev.value
 
 
 def clock_mhz(sample):

@@ -21,6 +21,7 @@
 // and formats, the stream and scratch slot, and the status with its message.
 // The line is written after the kernels are enqueued; it never waits for the
 // device.
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -78,7 +79,11 @@ constexpr int kMaxDevices = 64;
 struct Slot {
     std::mutex mu;      // held across the launches of one call
     bool dirty = false; // a failed call may have left partials in the slot
+    uint32_t tag = 0;   // the tag of the slot's last call (tags are nonzero)
 };
+
+// Bound on a finishing block's polling rounds (fp8q_set_finish_poll_rounds).
+std::atomic<uint32_t> g_poll_rounds{fp8q::kPollRounds};
 
 struct StreamKey {
     hipStream_t s;
@@ -137,6 +142,8 @@ public:
             if (e != hipSuccess) return hip_status(e, fn);
             slot_->dirty = false;
         }
+        if (++slot_->tag == 0) ++slot_->tag;
+        tag = slot_->tag;
         return FP8Q_OK;
     }
     // record the outcome of the call's launches
@@ -147,6 +154,7 @@ public:
     }
     int index() const { return index_; }
     fp8q::GridScratch *gs = nullptr;
+    uint32_t tag = 0;
 
 private:
     Slot *slot_ = nullptr;
@@ -178,6 +186,14 @@ public:
     {
         const int st = lease_.acquire(fn_, (hipStream_t)stream_);
         *gs = st == FP8Q_OK ? lease_.gs : nullptr;
+        return st;
+    }
+    // the slot, this call's tag and the polling bound of its finishing block
+    int scratch(fp8q::Reduce *r)
+    {
+        const int st = lease_.acquire(fn_, (hipStream_t)stream_);
+        *r = st == FP8Q_OK ? fp8q::Reduce{lease_.gs, lease_.tag, g_poll_rounds.load(std::memory_order_relaxed)}
+                           : fp8q::Reduce{nullptr, 0u, 0u};
         return st;
     }
     int ret(int status)
@@ -252,6 +268,13 @@ extern "C" int fp8q_clock_monitor(uint64_t *out, const uint32_t *stop, void *str
     return c.ret(fp8q_clock_monitor_impl(out, stop, stream));
 }
 
+extern "C" int fp8q_set_finish_poll_rounds(uint32_t rounds, uint32_t *previous)
+{
+    const uint32_t was = g_poll_rounds.exchange(rounds == 0xFFFFFFFFu ? fp8q::kPollRounds : rounds);
+    if (previous) *previous = was;
+    return ok();
+}
+
 static int fp8_amax_impl(Call &c, const void *x, int32_t dtype, int64_t n, float *amax, void *stream)
 {
     const char *fn = "fp8_amax";
@@ -260,10 +283,10 @@ static int fp8_amax_impl(Call &c, const void *x, int32_t dtype, int64_t n, float
     if (!amax || !aligned(amax, 4)) return fail(FP8Q_EINVAL, "%s: amax must be a 4-byte aligned pointer", fn);
     if (n > 0 && (!x || !aligned(x, 16))) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
     if (overlap(x, n * dsize(dtype), amax, 4)) return fail(FP8Q_EINVAL, "%s: amax overlaps x", fn);
-    fp8q::GridScratch *gs = nullptr;
-    const int st = c.scratch(&gs);
+    fp8q::Reduce r{};
+    const int st = c.scratch(&r);
     if (st) return st;
-    return hip_status(fp8q::launch_amax(x, dtype, n, amax, gs, (hipStream_t)stream), fn);
+    return hip_status(fp8q::launch_amax(x, dtype, n, amax, r, (hipStream_t)stream), fn);
 }
 
 extern "C" int fp8_amax(const void *x, int32_t dtype, int64_t n, float *amax, void *stream)
@@ -296,13 +319,13 @@ static int quantize_tensor(Call &c, const char *fn, const void *x, int32_t dtype
         if (stats && (overlap(x, n * dsize(dtype), stats, 32) || overlap(q, n, stats, 32)))
             return fail(FP8Q_EINVAL, "%s: stats overlaps x or q", fn);
     }
-    fp8q::GridScratch *gs = nullptr;
+    fp8q::Reduce r{};
     if (amax_out || stats) {
-        const int st = c.scratch(&gs);
+        const int st = c.scratch(&r);
         if (st) return st;
     }
     return hip_status(fp8q::launch_cast(x, dtype, n, fmt, make_src(amax_in, margin, scale_inv_in), q, scale_inv_out,
-                                        scale_out, amax_out, stats, gs, (hipStream_t)stream),
+                                        scale_out, amax_out, stats, r, (hipStream_t)stream),
                       fn);
 }
 
@@ -388,13 +411,13 @@ static int fp8_quantize_rowwise_colwise_impl(Call &c, const void *x, int32_t dty
             overlap(q_row, n, q_col, n))
             return fail(FP8Q_EINVAL, "%s: output buffers overlap", fn);
     }
-    fp8q::GridScratch *gs = nullptr;
+    fp8q::Reduce r{};
     if (amax_out) {
-        const int st = c.scratch(&gs);
+        const int st = c.scratch(&r);
         if (st) return st;
     }
     return hip_status(fp8q::launch_rowwise_colwise(x, dtype, rows, cols, fmt, make_src(amax_in, margin, scale_inv_in),
-                                                   q_row, q_col, scale_inv_out, scale_out, amax_out, gs,
+                                                   q_row, q_col, scale_inv_out, scale_out, amax_out, r,
                                                    (hipStream_t)stream),
                       fn);
 }
@@ -553,11 +576,11 @@ static int fp8_quantize_delayed_impl(Call &c, const void *x, int32_t dtype, int6
             if (overlap(x, n * dsize(dtype), state[i], state_bytes[i]) || overlap(q, n, state[i], state_bytes[i]))
                 return fail(FP8Q_EINVAL, "%s: x or q overlaps the scaling state or a scalar output", fn);
     }
-    fp8q::GridScratch *gs = nullptr;
-    const int st = c.scratch(&gs);
+    fp8q::Reduce r{};
+    const int st = c.scratch(&r);
     if (st) return st;
     return hip_status(fp8q::launch_delayed_step(x, dtype, n, fmt, hist, history_len, n_cols, col, step, fmt_next, margin,
-                                                algo, scale, scale_inv, q, q_scale_inv_out, amax_out, gs,
+                                                algo, scale, scale_inv, q, q_scale_inv_out, amax_out, r,
                                                 (hipStream_t)stream),
                       fn);
 }
@@ -619,15 +642,15 @@ static int fp8_quantize_hybrid_impl(Call &c, const void *x, int32_t dtype, int64
             if (overlap(x, n * dsize(dtype), p, 4) || overlap(q_row, n, p, 4) || overlap(q_col, n, p, 4))
                 return fail(FP8Q_EINVAL, "%s: a scalar output overlaps x or the codes", fn);
     }
-    fp8q::GridScratch *gs = nullptr;
+    fp8q::Reduce r{};
     if (amax_out) {
-        const int st = c.scratch(&gs);
+        const int st = c.scratch(&r);
         if (st) return st;
     }
     const fp8q::ScaleSrc src{amax_in, row_scale_inv_in, (int)row_margin};
     const fp8q::ScaleSrc src_col{amax_in, col_scale_inv_in, (int)col_margin};
     return hip_status(fp8q::launch_hybrid(x, dtype, rows, cols, row_fmt, col_fmt, col_source, src, src_col, q_row,
-                                          q_col, row_scale_inv_out, col_scale_inv_out, amax_out, gs,
+                                          q_col, row_scale_inv_out, col_scale_inv_out, amax_out, r,
                                           (hipStream_t)stream),
                       fn);
 }
@@ -694,13 +717,13 @@ static int fp8_quantize_error_feedback_impl(Call &c, const void *g, int32_t dtyp
             overlap(g, ng, amax_out, 4) || overlap(residual, 4 * n, amax_out, 4) || overlap(q, n, amax_out, 4))
             return fail(FP8Q_EINVAL, "%s: a tensor overlaps scale_inv or amax_out", fn);
     }
-    fp8q::GridScratch *gs = nullptr;
+    fp8q::Reduce r{};
     if (amax_out) {
-        const int st = c.scratch(&gs);
+        const int st = c.scratch(&r);
         if (st) return st;
     }
     return hip_status(
-        fp8q::launch_error_feedback(g, dtype, residual, n, fmt, scale_inv, q, amax_out, gs, (hipStream_t)stream), fn);
+        fp8q::launch_error_feedback(g, dtype, residual, n, fmt, scale_inv, q, amax_out, r, (hipStream_t)stream), fn);
 }
 
 extern "C" int fp8_quantize_error_feedback(const void *g, int32_t dtype, float *residual, int64_t n, int32_t fmt,

@@ -194,31 +194,30 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *lds)
 }
 
 // ------------------------------------------------- grid-wide amax partials --
-// A producing block publishes its canonical magnitude max (below 2^31) with
-// the top bit set, so that a slot reads zero until its block has published.
-// The store is an agent-scope atomic, visible to the agent-scope loads of a
-// finishing block running on another XCD while the launch still runs.
-constexpr uint32_t kPartFlag = 0x80000000u;
-
-__device__ __forceinline__ void publish_partial(uint32_t *slot, uint32_t canonical_bits)
+// A producing block publishes its canonical magnitude max (below 2^31) to its
+// slot as tag << 32 | bits, the tag being the call's (nonzero, new for every
+// call on the slot).  The store is a 64-bit agent-scope atomic, visible to
+// the agent-scope loads of a finishing block running on another XCD while
+// the launch still runs.
+__device__ __forceinline__ void publish_partial(unsigned long long *slot, uint32_t tag, uint32_t canonical_bits)
 {
-    __hip_atomic_store(slot, canonical_bits | kPartFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(slot, ((unsigned long long)tag << 32) | canonical_bits, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The finishing block of a launch (its last block, after the producing
-// blocks): every lane polls its slots of part[0, nparts) with agent-scope
+// blocks): every lane polls its slots of pub[0, nparts) with agent-scope
 // loads, sleeping briefly between rounds, until the whole block has seen all
-// nparts partials published; then the block returns their max to every lane
-// and clears the slots.  It waits only for the other blocks of its launch,
-// which never wait, so the wait ends once they have run; the rounds are
-// bounded all the same (about a second and more of polling), after which the
-// result is the canonical NaN.  This replaces a second, one-block kernel
-// whose launch would follow the producers' end.  NT lanes, nparts <= kMax,
-// kMax a multiple of NT.
-constexpr int kPollRounds = 1 << 21;
-
+// nparts slots carry the call's tag; then every lane gets the max of their
+// values.  It waits only for the other blocks of its launch, which never
+// wait, so the wait ends once they have run; it is bounded all the same, by
+// `rounds` polling rounds, after which the result is the canonical NaN (a
+// partial that arrives later carries a tag no later call accepts).  This
+// replaces a second, one-block kernel whose launch would follow the
+// producers' end.  NT lanes, nparts <= kMax, kMax a multiple of NT.
 template <int NT, int kMax>
-__device__ __forceinline__ uint32_t collect_partials(uint32_t *part, int nparts)
+__device__ __forceinline__ uint32_t collect_partials(const unsigned long long *pub, int nparts, uint32_t tag,
+                                                     uint32_t rounds)
 {
     __shared__ uint32_t red[NT / 64];
     constexpr int kPer = kMax / NT;
@@ -229,14 +228,14 @@ __device__ __forceinline__ uint32_t collect_partials(uint32_t *part, int nparts)
     for (int u = 0; u < kPer; ++u)
         if ((int)threadIdx.x + u * NT < nparts) left |= 1u << u;
     bool expired = true;
-    for (int round = 0; round < kPollRounds; ++round) {
+    for (uint32_t round = 0; round < rounds; ++round) {
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             if (left & (1u << u)) {
-                const uint32_t v =
-                    __hip_atomic_load(&part[threadIdx.x + u * NT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (v & kPartFlag) {
-                    m = max(m, v & ~kPartFlag);
+                const unsigned long long v =
+                    __hip_atomic_load(&pub[threadIdx.x + u * NT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((uint32_t)(v >> 32) == tag) {
+                    m = max(m, (uint32_t)v);
                     left &= ~(1u << u);
                 }
             }
@@ -247,10 +246,6 @@ __device__ __forceinline__ uint32_t collect_partials(uint32_t *part, int nparts)
         }
         __builtin_amdgcn_s_sleep(2);
     }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u)
-        if ((int)threadIdx.x + u * NT < nparts)
-            __hip_atomic_store(&part[threadIdx.x + u * NT], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     m = block_max_u32<NT>(m, red);
     return expired ? kCanonicalNaN : m;
 }

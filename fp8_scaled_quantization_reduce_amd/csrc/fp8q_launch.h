@@ -10,15 +10,18 @@ namespace fp8q {
 
 // Grid-wide reduction scratch.  A flat or tile kernel that reduces an amax
 // runs at most kParts producing blocks (grid-stride loops cover larger
-// inputs) and block b stores its canonical magnitude max, flagged by the top
-// bit, to part[b]; a GEMM block folds its max into part[b % kParts] with an
-// unsigned atomic max (the canonical magnitude bits order like the values, and
-// the canonical NaN sorts above +inf).  The cast statistics add each block's
-// four counts into cnt[k][b % kCntParts].  Then either the launch's own
-// finishing block (the amax, the cast with output amax and the delayed step)
-// waits for the flagged partials, or one small kernel follows; either reads
-// the slots the call used, writes the result and puts them back to zero, so a
-// scratch is all zeros between calls (it starts zeroed, as a device global).
+// inputs).  When the launch ends in its own finishing block (the amax, the
+// casts with output amax and the delayed step), block b publishes its
+// canonical magnitude max to pub[b] tagged with the call's tag (tag << 32 |
+// bits), and the finishing block waits until all pub[0 .. nblocks) carry the
+// tag: values of earlier calls carry other tags and are never cleared.
+// Otherwise block b stores its max to part[b], a GEMM block folds its max into
+// part[b % kParts] with an unsigned atomic max (the canonical magnitude bits
+// order like the values, and the canonical NaN sorts above +inf), the cast
+// statistics add each block's four counts into cnt[k][b % kCntParts], and one
+// small kernel follows that reads the slots the call used, writes the result
+// and puts them back to zero, so part and cnt are all zeros between calls
+// (they start zeroed, as a device global).
 #ifndef FP8Q_REDUCE_GRID
 #define FP8Q_REDUCE_GRID 1024
 #endif
@@ -28,8 +31,19 @@ constexpr int kStats = 4; // overflows, underflows, NaNs, nonzeros
 struct GridScratch {
     uint32_t part[kParts];
     unsigned long long cnt[kStats][kCntParts];
+    unsigned long long pub[kParts];
 };
-static_assert(kParts % 256 == 0 && sizeof(GridScratch) == 4 * kParts + 2048, "scratch layout");
+static_assert(kParts % 256 == 0 && sizeof(GridScratch) == 12 * kParts + 2048, "scratch layout");
+
+// A reducing call's scratch slot, its tag (nonzero and new for every call on
+// the slot) and the bound on its finishing block's polling rounds.
+struct Reduce {
+    GridScratch *gs;
+    uint32_t tag;
+    uint32_t rounds;
+};
+// The default bound: about a second and more of polling.
+constexpr uint32_t kPollRounds = 1u << 21;
 
 // Flat launches that reduce nothing keep at most this many blocks.
 #ifndef FP8Q_MAX_GRID
@@ -64,17 +78,17 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t v, hipStream_t s);
 // Fold part[0 .. nparts) into *out and clear those slots.
 hipError_t launch_finish_amax(GridScratch *gs, int nparts, float *out, hipStream_t s);
 
-hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScratch *gs, hipStream_t s);
+hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, const Reduce &r, hipStream_t s);
 
 // stats (nullable): uint64[4] counts of the cast, reduced in the same pass
 hipError_t launch_cast(const void *x, int dtype, int64_t n, int fmt, ScaleSrc src, uint8_t *q, float *scale_inv_out,
-                       float *scale_out, float *amax_out, uint64_t *stats, GridScratch *gs, hipStream_t s);
+                       float *scale_out, float *amax_out, uint64_t *stats, const Reduce &r, hipStream_t s);
 
 hipError_t launch_dequant(const uint8_t *q, int fmt, int64_t n, const float *scale_inv, float *y, hipStream_t s);
 
 hipError_t launch_rowwise_colwise(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, ScaleSrc src,
                                   uint8_t *q_row, uint8_t *q_col, float *scale_inv_out, float *scale_out,
-                                  float *amax_out, GridScratch *gs, hipStream_t s);
+                                  float *amax_out, const Reduce &r, hipStream_t s);
 
 hipError_t launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int block_rows, uint8_t *q_row,
                         float *s_row, uint8_t *q_col, float *s_col, hipStream_t s);
@@ -84,7 +98,7 @@ hipError_t launch_mx(const void *x, int dtype, int64_t rows, int64_t cols, int f
 
 hipError_t launch_hybrid(const void *x, int dtype, int64_t rows, int64_t cols, int row_fmt, int col_fmt,
                          int col_source, ScaleSrc src, ScaleSrc src_col, uint8_t *q_row, uint8_t *q_col,
-                         float *row_scale_inv_out, float *col_scale_inv_out, float *amax_out, GridScratch *gs,
+                         float *row_scale_inv_out, float *col_scale_inv_out, float *amax_out, const Reduce &r,
                          hipStream_t s);
 
 // stats[0..3] (uint64): overflows, underflows, NaNs, nonzeros of the cast of
@@ -93,14 +107,14 @@ hipError_t launch_cast_stats(const void *x, int dtype, int64_t n, int fmt, const
                              GridScratch *gs, hipStream_t s);
 
 hipError_t launch_error_feedback(const void *g, int dtype, float *residual, int64_t n, int fmt,
-                                 const float *scale_inv, uint8_t *q, float *amax_out, GridScratch *gs, hipStream_t s);
+                                 const float *scale_inv, uint8_t *q, float *amax_out, const Reduce &r, hipStream_t s);
 
 hipError_t launch_delayed(float *hist, int history_len, int n_cols, int col, const float *new_amax, int64_t step,
                           int fmt, int margin, int algo, float *scale, float *scale_inv, hipStream_t s);
 
 hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, float *hist, int history_len, int n_cols,
                                int col, int64_t step, int fmt_next, int margin, int algo, float *scale,
-                               float *scale_inv, uint8_t *q, float *q_scale_inv_out, float *amax_out, GridScratch *gs,
+                               float *scale_inv, uint8_t *q, float *q_scale_inv_out, float *amax_out, const Reduce &r,
                                hipStream_t s);
 
 // out_kind: 0 bf16, 1 fp32, 2 E4M3FN codes, 3 E5M2 codes (cast with

@@ -64,22 +64,22 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t v, hipStream_t s)
     return hipGetLastError();
 }
 
-// One block's magnitude max -> its partial slot, flagged (publish_partial).
-// Every lane must reach it.  The launch has at most kParts producing blocks.
-
-__device__ __forceinline__ void block_partial(uint32_t m, GridScratch *gs)
+// One block's magnitude max -> its slot: published with the call's tag for
+// the launch's finishing block (tag != 0), or stored to part[] for a finish
+// kernel (tag 0).  Every lane must reach it.  The launch has at most kParts
+// producing blocks.
+__device__ __forceinline__ void block_partial(uint32_t m, GridScratch *gs, uint32_t tag)
 {
     __shared__ uint32_t red[kThreads / 64];
     m = block_max_u32<kThreads>(m, red);
-    if (threadIdx.x == 0) publish_partial(&gs->part[blockIdx.x], canonical_amax_bits(m));
+    if (threadIdx.x == 0) {
+        if (tag) publish_partial(&gs->pub[blockIdx.x], tag, canonical_amax_bits(m));
+        else gs->part[blockIdx.x] = canonical_amax_bits(m);
+    }
 }
 
-// Read partial slot i and put it back to zero (one round trip).  GEMM blocks
-// fold unflagged maxima into their slots; either way the flag is dropped.
-__device__ __forceinline__ uint32_t take_partial(GridScratch *gs, int i)
-{
-    return atomicExch(&gs->part[i], 0u) & ~kPartFlag;
-}
+// Read partial slot i and put it back to zero (one round trip).
+__device__ __forceinline__ uint32_t take_partial(GridScratch *gs, int i) { return atomicExch(&gs->part[i], 0u); }
 
 // Max of partial slots [0, nparts), which it leaves zero; kThreads lanes with
 // up to kParts / kThreads exchanges in flight each.  Every lane gets the result.
@@ -149,17 +149,24 @@ __device__ __forceinline__ void ring_update(const DelayedUpdate &d, float a, uin
 // What the finishing block of a reducing launch does with the amax: publish
 // it (amax_out, canonical bits) and, for a delayed-scaling step, record it in
 // the ring.  A launch has a finishing block when either is set.
+// tag, rounds: the call's tag and polling bound (Reduce).
 struct Finish {
     uint32_t *amax_out;
     DelayedUpdate du;
+    uint32_t tag, rounds;
     __device__ __host__ bool active() const { return amax_out != nullptr || du.hist != nullptr; }
 };
+
+static Finish finish_amax_to(float *amax_out, const Reduce &r)
+{
+    return Finish{reinterpret_cast<uint32_t *>(amax_out), DelayedUpdate{}, r.tag, r.rounds};
+}
 
 __device__ __forceinline__ void finish_block(const Finish &f, GridScratch *gs, int nparts)
 {
     // the ring is read while the producers still run
     const uint32_t key = f.du.hist ? ring_key(f.du) : 0u;
-    const uint32_t a = collect_partials<kThreads, kParts>(gs->part, nparts);
+    const uint32_t a = collect_partials<kThreads, kParts>(gs->pub, nparts, f.tag, f.rounds);
     if (threadIdx.x == 0) {
         if (f.amax_out) *f.amax_out = a;
         if (f.du.hist) ring_update(f.du, __uint_as_float(a), key);
@@ -245,11 +252,11 @@ constexpr int kAmaxU = FP8Q_AMAX_U;
 // The launch's last block is the finishing block, which writes the amax.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const void *__restrict__ x, int64_t n, GridScratch *gs,
-                                                        uint32_t *__restrict__ amax_out)
+                                                        Finish fin)
 {
     const int nwork = gridDim.x - 1;
     if (blockIdx.x == nwork) {
-        finish_block(Finish{amax_out, DelayedUpdate{}}, gs, nwork);
+        finish_block(fin, gs, nwork);
         return;
     }
     constexpr int kPer = DT == kBF16 ? 8 : 4; // elements per 16-byte vector
@@ -290,19 +297,19 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void *__restrict__
             m = max(m, reinterpret_cast<const uint32_t *>(x)[e] & 0x7FFFFFFFu);
     }
     if constexpr (DT == kBF16) m = max(m, bf16_absmax_to_f32bits(m2));
-    block_partial(m, gs);
+    block_partial(m, gs, fin.tag);
 }
 
-hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, GridScratch *gs, hipStream_t s)
+hipError_t launch_amax(const void *x, int dtype, int64_t n, float *amax, const Reduce &r, hipStream_t s)
 {
     const int64_t nvec = n / (dtype == kBF16 ? 8 : 4);
     // the producing blocks and the finishing block
     const int grid = reduce_grid(ceil_div(nvec, (int64_t)kThreads * kAmaxU), kAmaxGrid) + 1;
-    uint32_t *out = reinterpret_cast<uint32_t *>(amax);
+    const Finish fin = finish_amax_to(amax, r);
     if (dtype == kBF16)
-        amax_kernel<kBF16><<<grid, kThreads, 0, s>>>(x, n, gs, out);
+        amax_kernel<kBF16><<<grid, kThreads, 0, s>>>(x, n, r.gs, fin);
     else
-        amax_kernel<kF32><<<grid, kThreads, 0, s>>>(x, n, gs, out);
+        amax_kernel<kF32><<<grid, kThreads, 0, s>>>(x, n, r.gs, fin);
     return hipGetLastError();
 }
 
@@ -548,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const void *__restrict__
     }
     if constexpr (kAmax) {
         if constexpr (DT == kBF16) m = max(m, bf16_absmax_to_f32bits(m2));
-        block_partial(m, gs);
+        block_partial(m, gs, fin.active() ? fin.tag : 0u);
     }
     if constexpr (kCount) block_counts(g, gs);
 }
@@ -557,41 +564,43 @@ static hipError_t launch_finish_stats(GridScratch *gs, uint64_t *stats, hipStrea
 
 template <int F, int DT>
 static hipError_t launch_cast_t(const void *x, int64_t n, ScaleSrc src, uint8_t *q, float *scale_inv_out,
-                                float *scale_out, float *amax_out, uint64_t *stats, GridScratch *gs, hipStream_t s)
+                                float *scale_out, float *amax_out, uint64_t *stats, const Reduce &r, hipStream_t s)
 {
     const int64_t units = ceil_div(n >> 4, (int64_t)kThreads * kCastU);
     const int grid = (amax_out || stats) ? reduce_grid(units) : flat_grid(units);
-    const Finish none{nullptr, DelayedUpdate{}};
+    const Finish none{nullptr, DelayedUpdate{}, 0u, 0u};
     if (stats) {
         // the counts are summed by the statistics kernel, which follows
         if (amax_out)
-            cast_kernel<F, DT, true, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs, none);
+            cast_kernel<F, DT, true, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, r.gs,
+                                                                     none);
         else
-            cast_kernel<F, DT, false, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs, none);
+            cast_kernel<F, DT, false, true><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, r.gs,
+                                                                      none);
     } else if (amax_out) {
         // the producing blocks and the finishing block, which writes the amax
-        const Finish fin{reinterpret_cast<uint32_t *>(amax_out), DelayedUpdate{}};
-        cast_kernel<F, DT, true><<<grid + 1, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, gs, fin);
+        cast_kernel<F, DT, true><<<grid + 1, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, r.gs,
+                                                                finish_amax_to(amax_out, r));
     } else {
         cast_kernel<F, DT, false><<<grid, kThreads, 0, s>>>(x, n, src, q, scale_inv_out, scale_out, nullptr, none);
     }
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && stats && amax_out) e = launch_finish_amax(gs, grid, amax_out, s);
-    if (e == hipSuccess && stats) e = launch_finish_stats(gs, stats, s);
+    if (e == hipSuccess && stats && amax_out) e = launch_finish_amax(r.gs, grid, amax_out, s);
+    if (e == hipSuccess && stats) e = launch_finish_stats(r.gs, stats, s);
     return e;
 }
 
 hipError_t launch_cast(const void *x, int dtype, int64_t n, int fmt, ScaleSrc src, uint8_t *q, float *scale_inv_out,
-                       float *scale_out, float *amax_out, uint64_t *stats, GridScratch *gs, hipStream_t s)
+                       float *scale_out, float *amax_out, uint64_t *stats, const Reduce &r, hipStream_t s)
 {
     if (fmt == kE4M3) {
         if (dtype == kBF16)
-            return launch_cast_t<kE4M3, kBF16>(x, n, src, q, scale_inv_out, scale_out, amax_out, stats, gs, s);
-        return launch_cast_t<kE4M3, kF32>(x, n, src, q, scale_inv_out, scale_out, amax_out, stats, gs, s);
+            return launch_cast_t<kE4M3, kBF16>(x, n, src, q, scale_inv_out, scale_out, amax_out, stats, r, s);
+        return launch_cast_t<kE4M3, kF32>(x, n, src, q, scale_inv_out, scale_out, amax_out, stats, r, s);
     }
     if (dtype == kBF16)
-        return launch_cast_t<kE5M2, kBF16>(x, n, src, q, scale_inv_out, scale_out, amax_out, stats, gs, s);
-    return launch_cast_t<kE5M2, kF32>(x, n, src, q, scale_inv_out, scale_out, amax_out, stats, gs, s);
+        return launch_cast_t<kE5M2, kBF16>(x, n, src, q, scale_inv_out, scale_out, amax_out, stats, r, s);
+    return launch_cast_t<kE5M2, kF32>(x, n, src, q, scale_inv_out, scale_out, amax_out, stats, r, s);
 }
 
 // --------------------------------------------------------------- dequant --
@@ -741,16 +750,16 @@ __global__ __launch_bounds__(kThreads) void error_feedback_kernel(const void *__
                                                                   float *__restrict__ residual, int64_t n,
                                                                   const float *__restrict__ scale_inv,
                                                                   uint8_t *__restrict__ q, GridScratch *gs,
-                                                                  uint32_t *amax_out)
+                                                                  Finish fin)
 {
     // v - value * s is rounded twice (product, then difference), as defined:
     // no fused multiply-add
 #pragma clang fp contract(off)
     // with an amax the launch's last block is the finishing block
-    const bool amax = amax_out != nullptr;
+    const bool amax = fin.active();
     const int nwork = gridDim.x - (amax ? 1 : 0);
     if (amax && blockIdx.x == nwork) {
-        finish_block(Finish{amax_out, DelayedUpdate{}}, gs, nwork);
+        finish_block(fin, gs, nwork);
         return;
     }
     const float s = *scale_inv;
@@ -814,16 +823,17 @@ __global__ __launch_bounds__(kThreads) void error_feedback_kernel(const void *__
         residual[e] = v - dec2<F, false>(c).x * s;
         m = max(m, f32_absbits(v));
     }
-    if (amax) block_partial(m, gs);
+    if (amax) block_partial(m, gs, fin.tag);
 }
 
 hipError_t launch_error_feedback(const void *g, int dtype, float *residual, int64_t n, int fmt,
-                                 const float *scale_inv, uint8_t *q, float *amax_out, GridScratch *gs, hipStream_t s)
+                                 const float *scale_inv, uint8_t *q, float *amax_out, const Reduce &r, hipStream_t s)
 {
-    uint32_t *am = reinterpret_cast<uint32_t *>(amax_out);
+    const Finish am = finish_amax_to(amax_out, r);
+    GridScratch *gs = r.gs;
     const int64_t units = ceil_div(n >> 4, (int64_t)kThreads * kEfU);
     // with an amax: the producing blocks and the finishing block
-    const int grid = am ? reduce_grid(units) + 1 : flat_grid(units);
+    const int grid = amax_out ? reduce_grid(units) + 1 : flat_grid(units);
     if (fmt == kE4M3) {
         if (dtype == kBF16) error_feedback_kernel<kE4M3, kBF16><<<grid, kThreads, 0, s>>>(g, residual, n, scale_inv, q, gs, am);
         else error_feedback_kernel<kE4M3, kF32><<<grid, kThreads, 0, s>>>(g, residual, n, scale_inv, q, gs, am);
@@ -870,12 +880,14 @@ hipError_t launch_delayed(float *hist, int history_len, int n_cols, int col, con
 // with the next step's scale.
 hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, float *hist, int history_len, int n_cols,
                                int col, int64_t step, int fmt_next, int margin, int algo, float *scale,
-                               float *scale_inv, uint8_t *q, float *q_scale_inv_out, float *amax_out, GridScratch *gs,
+                               float *scale_inv, uint8_t *q, float *q_scale_inv_out, float *amax_out, const Reduce &r,
                                hipStream_t s)
 {
     const ScaleSrc src{nullptr, scale_inv + col, 0};
+    GridScratch *gs = r.gs;
     const Finish fin{reinterpret_cast<uint32_t *>(amax_out),
-                     make_update(hist, history_len, n_cols, col, step, fmt_next, margin, algo, scale, scale_inv)};
+                     make_update(hist, history_len, n_cols, col, step, fmt_next, margin, algo, scale, scale_inv),
+                     r.tag, r.rounds};
     const int grid = reduce_grid(ceil_div(n >> 4, (int64_t)kThreads * kCastU)) + 1;
     if (fmt == kE4M3) {
         if (dtype == kBF16)
@@ -1109,12 +1121,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                                                         uint8_t *__restrict__ q_col, void *__restrict__ s_row_p,
                                                         void *__restrict__ s_col_p, float *scale_inv_out,
                                                         float *scale_out, GridScratch *gs, ScaleSrc src_col,
-                                                        float *col_scale_inv_out, uint32_t *amax_out)
+                                                        float *col_scale_inv_out, Finish fin)
 {
     // with kAmax the launch's last block is the finishing block
     const int nwork = gridDim.x - (kAmax ? 1 : 0);
     if (kAmax && blockIdx.x == nwork) {
-        finish_block(Finish{amax_out, DelayedUpdate{}}, gs, nwork);
+        finish_block(fin, gs, nwork);
         return;
     }
     constexpr bool kHybrid = kMode >= kTileHybrid;
@@ -1459,7 +1471,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
         __syncthreads(); // the next tile reuses the LDS buffers
 #undef PV
     }
-    if constexpr (kAmax) block_partial(m_all, gs);
+    if constexpr (kAmax) block_partial(m_all, gs, fin.tag);
 }
 
 static int tile_grid(int64_t rows, int64_t cols, bool reduce = false)
@@ -1470,69 +1482,68 @@ static int tile_grid(int64_t rows, int64_t cols, bool reduce = false)
 
 template <int F, int DT>
 static hipError_t launch_rc_t(const void *x, int64_t rows, int64_t cols, ScaleSrc src, uint8_t *q_row, uint8_t *q_col,
-                              float *scale_inv_out, float *scale_out, float *amax_out, GridScratch *gs, hipStream_t s)
+                              float *scale_inv_out, float *scale_out, float *amax_out, const Reduce &r, hipStream_t s)
 {
     // with an amax: the producing blocks and the finishing block
     const int grid = tile_grid(rows, cols, amax_out != nullptr) + (amax_out ? 1 : 0);
     if (amax_out)
         tile_kernel<F, DT, kTilePerTensor, true><<<grid, kThreads, 0, s>>>(
-            x, rows, cols, src, q_row, q_col, nullptr, nullptr, scale_inv_out, scale_out, gs, ScaleSrc{}, nullptr,
-            reinterpret_cast<uint32_t *>(amax_out));
+            x, rows, cols, src, q_row, q_col, nullptr, nullptr, scale_inv_out, scale_out, r.gs, ScaleSrc{}, nullptr,
+            finish_amax_to(amax_out, r));
     else
         tile_kernel<F, DT, kTilePerTensor, false><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr,
                                                                            nullptr, scale_inv_out, scale_out, nullptr,
-                                                                           ScaleSrc{}, nullptr, nullptr);
+                                                                           ScaleSrc{}, nullptr, Finish{});
     return hipGetLastError();
 }
 
 hipError_t launch_rowwise_colwise(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, ScaleSrc src,
                                   uint8_t *q_row, uint8_t *q_col, float *scale_inv_out, float *scale_out,
-                                  float *amax_out, GridScratch *gs, hipStream_t s)
+                                  float *amax_out, const Reduce &r, hipStream_t s)
 {
     if (rows == 0 || cols == 0) {
         // still publish the scales and an amax of 0
-        return launch_cast(x, dtype, 0, fmt, src, nullptr, scale_inv_out, scale_out, amax_out, nullptr, gs, s);
+        return launch_cast(x, dtype, 0, fmt, src, nullptr, scale_inv_out, scale_out, amax_out, nullptr, r, s);
     }
     if (fmt == kE4M3) {
         if (dtype == kBF16)
-            return launch_rc_t<kE4M3, kBF16>(x, rows, cols, src, q_row, q_col, scale_inv_out, scale_out, amax_out, gs,
+            return launch_rc_t<kE4M3, kBF16>(x, rows, cols, src, q_row, q_col, scale_inv_out, scale_out, amax_out, r,
                                              s);
-        return launch_rc_t<kE4M3, kF32>(x, rows, cols, src, q_row, q_col, scale_inv_out, scale_out, amax_out, gs, s);
+        return launch_rc_t<kE4M3, kF32>(x, rows, cols, src, q_row, q_col, scale_inv_out, scale_out, amax_out, r, s);
     }
     if (dtype == kBF16)
-        return launch_rc_t<kE5M2, kBF16>(x, rows, cols, src, q_row, q_col, scale_inv_out, scale_out, amax_out, gs, s);
-    return launch_rc_t<kE5M2, kF32>(x, rows, cols, src, q_row, q_col, scale_inv_out, scale_out, amax_out, gs, s);
+        return launch_rc_t<kE5M2, kBF16>(x, rows, cols, src, q_row, q_col, scale_inv_out, scale_out, amax_out, r, s);
+    return launch_rc_t<kE5M2, kF32>(x, rows, cols, src, q_row, q_col, scale_inv_out, scale_out, amax_out, r, s);
 }
 
 template <int F, int DT, int kMode>
 static hipError_t launch_hybrid_m(const void *x, int64_t rows, int64_t cols, ScaleSrc src, ScaleSrc src_col,
                                   uint8_t *q_row, uint8_t *q_col, float *row_scale_inv_out, float *col_scale_inv_out,
-                                  float *amax_out, GridScratch *gs, hipStream_t s)
+                                  float *amax_out, const Reduce &r, hipStream_t s)
 {
     // with an amax: the producing blocks and the finishing block
     const int grid = tile_grid(rows, cols, amax_out != nullptr) + (amax_out ? 1 : 0);
     if (amax_out)
         tile_kernel<F, DT, kMode, true><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr, nullptr,
-                                                                 row_scale_inv_out, nullptr, gs, src_col,
-                                                                 col_scale_inv_out,
-                                                                 reinterpret_cast<uint32_t *>(amax_out));
+                                                                 row_scale_inv_out, nullptr, r.gs, src_col,
+                                                                 col_scale_inv_out, finish_amax_to(amax_out, r));
     else
         tile_kernel<F, DT, kMode, false><<<grid, kThreads, 0, s>>>(x, rows, cols, src, q_row, q_col, nullptr, nullptr,
                                                                   row_scale_inv_out, nullptr, nullptr, src_col,
-                                                                  col_scale_inv_out, nullptr);
+                                                                  col_scale_inv_out, Finish{});
     return hipGetLastError();
 }
 
 template <int F, int DT>
 static hipError_t launch_hybrid_t(const void *x, int64_t rows, int64_t cols, int col_fmt, int col_source, ScaleSrc src,
                                   ScaleSrc src_col, uint8_t *q_row, uint8_t *q_col, float *row_scale_inv_out,
-                                  float *col_scale_inv_out, float *amax_out, GridScratch *gs, hipStream_t s)
+                                  float *col_scale_inv_out, float *amax_out, const Reduce &r, hipStream_t s)
 {
     const int mode = kTileHybrid + col_fmt + 2 * col_source;
 #define FP8Q_HYBRID(M)                                                                                              \
     case M:                                                                                                         \
         return launch_hybrid_m<F, DT, M>(x, rows, cols, src, src_col, q_row, q_col, row_scale_inv_out,              \
-                                         col_scale_inv_out, amax_out, gs, s)
+                                         col_scale_inv_out, amax_out, r, s)
     switch (mode) {
         FP8Q_HYBRID(kTileHybrid);
         FP8Q_HYBRID(kTileHybrid + 1);
@@ -1545,13 +1556,13 @@ static hipError_t launch_hybrid_t(const void *x, int64_t rows, int64_t cols, int
 
 hipError_t launch_hybrid(const void *x, int dtype, int64_t rows, int64_t cols, int row_fmt, int col_fmt,
                          int col_source, ScaleSrc src, ScaleSrc src_col, uint8_t *q_row, uint8_t *q_col,
-                         float *row_scale_inv_out, float *col_scale_inv_out, float *amax_out, GridScratch *gs,
+                         float *row_scale_inv_out, float *col_scale_inv_out, float *amax_out, const Reduce &r,
                          hipStream_t s)
 {
     // an empty tensor still publishes both scales and an amax of 0: the grid
     // is one block with no tiles to visit
 #define FP8Q_ARGS x, rows, cols, col_fmt, col_source, src, src_col, q_row, q_col, row_scale_inv_out, col_scale_inv_out, \
-                  amax_out, gs, s
+                  amax_out, r, s
     if (row_fmt == kE4M3) {
         if (dtype == kBF16) return launch_hybrid_t<kE4M3, kBF16>(FP8Q_ARGS);
         return launch_hybrid_t<kE4M3, kF32>(FP8Q_ARGS);
@@ -1580,11 +1591,11 @@ static hipError_t launch_block_t(const void *x, int64_t rows, int64_t cols, int 
     if (block_rows == 128)
         tile_kernel<F, DT, kTileBlock128, false><<<grid, kThreads, 0, s>>>(x, rows, cols, none, q_row, q_col, s_row,
                                                                           s_col, nullptr, nullptr, nullptr, none,
-                                                                          nullptr, nullptr);
+                                                                          nullptr, Finish{});
     else
         tile_kernel<F, DT, kTileBlock1x128, false><<<grid, kThreads, 0, s>>>(x, rows, cols, none, q_row, q_col,
                                                                             s_row, s_col, nullptr, nullptr, nullptr,
-                                                                            none, nullptr, nullptr);
+                                                                            none, nullptr, Finish{});
     return hipGetLastError();
 }
 
@@ -1594,7 +1605,7 @@ static hipError_t launch_mx_t(const void *x, int64_t rows, int64_t cols, uint8_t
 {
     const ScaleSrc none{nullptr, nullptr, 0};
     tile_kernel<F, DT, kTileMX, false><<<tile_grid(rows, cols), kThreads, 0, s>>>(
-        x, rows, cols, none, q_row, q_col, s_row, s_col, nullptr, nullptr, nullptr, none, nullptr, nullptr);
+        x, rows, cols, none, q_row, q_col, s_row, s_col, nullptr, nullptr, nullptr, none, nullptr, Finish{});
     return hipGetLastError();
 }
 

@@ -15,13 +15,13 @@
  *  - The library never allocates device memory.  Calls that reduce over the
  *    whole grid (an amax, the cast statistics) keep per-block partials in a
  *    reduction scratch that is a device global of the library: 64 slots of
- *    6 KiB on each device, created with the library's code object on that
+ *    14 KiB on each device, created with the library's code object on that
  *    device and held until the process ends.  Each stream gets a slot of its
  *    own the first time it runs such a call (a host-side table; no device
- *    work), so calls on different streams never share partials.  The slot is
- *    all zeros between calls: the call's finishing block (the last block of
- *    its reducing launch, which waits for the other blocks' partials) or its
- *    last kernel reads it and clears it.
+ *    work), so calls on different streams never share partials.  Either the
+ *    call's finishing block (the last block of its reducing launch) waits for
+ *    the other blocks' partials, which carry a tag new to the call, or the
+ *    call's last kernel reads the partials and clears them.
  *    While one call enqueues its kernels it holds a host lock on its slot, so
  *    host threads that share a stream are safe.  A device on which more than
  *    64 streams have run reducing calls returns FP8Q_EUNSUPPORTED.
@@ -393,6 +393,22 @@ int fp8_quantize_error_feedback(const void *g, int32_t dtype, float *residual, i
  * FP8Q_EHIP from the launch.  Uses no scratch.
  */
 int fp8q_clock_monitor(uint64_t *out, const uint32_t *stop, void *stream);
+
+/*
+ * fp8q_set_finish_poll_rounds -- a failure-handling knob, not a step of the
+ * method.  A reducing call whose launch ends in a finishing block (fp8_amax,
+ * the casts with amax_out, fp8_quantize_delayed) has that block wait for the
+ * other blocks' partials for at most `rounds` polling rounds (default
+ * 2^21, about a second and more); past the bound the call's amax is the
+ * canonical NaN (and fp8_quantize_delayed records NaN in its ring).  Partials
+ * that arrive after the bound carry that call's tag and are ignored by every
+ * later call.  rounds = 0 makes every finishing block give up at once (used
+ * by the tests of this path); 0xFFFFFFFF restores the default.  Applies to
+ * calls made afterwards, in every thread, on every device.
+ * previous: host uint32 or NULL; receives the bound that was in force.
+ * Returns FP8Q_OK.  Enqueues nothing.
+ */
+int fp8q_set_finish_poll_rounds(uint32_t rounds, uint32_t *previous);
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char *fp8q_last_error(void);

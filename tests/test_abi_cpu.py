@@ -249,15 +249,28 @@ def test_last_error_is_thread_local_string():
     assert isinstance(msg, str) and msg.startswith("fp8_amax")
 
 
+def test_finish_poll_bound_knob_is_host_only():
+    """The knob enqueues nothing (no device needed) and reports the bound that
+    was in force; 0xFFFFFFFF restores the default of 2^21 rounds."""
+    prev = ctypes.c_uint32(0)
+    assert L.fp8q_set_finish_poll_rounds(ctypes.c_uint32(5), ctypes.byref(prev)) == 0
+    start = prev.value
+    assert L.fp8q_set_finish_poll_rounds(ctypes.c_uint32(0xFFFFFFFF), ctypes.byref(prev)) == 0
+    assert prev.value == 5
+    assert L.fp8q_set_finish_poll_rounds(ctypes.c_uint32(start), None) == 0
+    assert fq.fp8q_set_finish_poll_rounds(fq.POLL_ROUNDS_DEFAULT) == start
+    assert fq.fp8q_set_finish_poll_rounds(fq.POLL_ROUNDS_DEFAULT) == 1 << 21
+
+
 # --------------------------------------------------------- lifecycle ------
 # The library allocates no device memory: its reduction scratch is one device
-# global of fixed size (64 slots of 6 KiB per device), whose address on the
+# global of fixed size (64 slots of 14 KiB per device), whose address on the
 # current device comes from hipGetSymbolAddress.  Both facts are visible in the
 # built library without a GPU.
 ALLOCATORS = ("hipMalloc", "hipFree", "hipHostMalloc", "hipHostFree", "hipExtMallocWithFlags", "hipMallocAsync",
               "hipFreeAsync", "hipMallocManaged", "hipMallocPitch", "hipMalloc3D", "hipMallocArray",
               "hipMemPoolCreate", "hipMemCreate", "hipMemAddressReserve")
-SCRATCH_SLOTS, SLOT_BYTES = 64, 6144
+SCRATCH_SLOTS, SLOT_BYTES = 64, 14336
 
 
 def _nm(*flags):
