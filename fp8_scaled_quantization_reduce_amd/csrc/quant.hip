@@ -33,8 +33,8 @@ static int flat_grid(int64_t units)
 }
 
 // The grid of a launch that reduces into the scratch: one partial slot per
-// block, at most `cap` <= kParts blocks.  Fewer, longer-lived blocks make the
-// finish kernel's read-and-clear pass short; measured on the MI355X over
+// block, at most `cap` <= kParts blocks.  Fewer, longer-lived blocks leave
+// fewer partials to fold at the end; measured on the MI355X over
 // 8192x8192 bf16, a 1024-block cast with fused amax takes 38.8 us against
 // 40.2 us at 2048 blocks and 46.8 us at 8192, and the read-only amax pass is
 // fastest at 512 blocks (22.4 us, 23.2 us at 1024), where each lane still has
