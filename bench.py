@@ -641,6 +641,23 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
                                                                        Y, cam, stream=stream), 4)
         mfma(name, 2 * 4096 * 14336 * 4096, t,
              gemm_cpu(4096, 14336, 4096, oracle.E4M3FN, oracle.E4M3FN, oracle.BLOCK_1x128_128x128, 256))
+    # the same fprop on one GPU's share of a tensor-parallel layer: the 8-way
+    # column shard of W (N = 1792 = 14336 / 8), 112 tiles of 256x256, fewer
+    # than the CUs, so it runs as 224 half tiles
+    name = "gemm_block_fprop_tp8_shard_4096x1792x4096"
+    if want(name):
+        if Xq is None:
+            Xq = codes((4096, 4096), E4)
+            Wq = codes((14336, 4096), E4)
+        sx8 = torch.rand((4096, 32), device=dev, generator=g) + 0.5
+        sw8 = torch.rand((14, 32), device=dev, generator=g) + 0.5
+        W8 = Wq[:1792]
+        Y8 = torch.empty((4096, 1792), dtype=torch.bfloat16, device=dev)
+        t = timed(lambda i: fq.fp8_scaled_gemm(Xq, E4, sx8, W8, E4, sw8, fq.BLOCK_1x128_128x128, Y8, cam,
+                                               stream=stream), 4)
+        mfma(name, 2 * 4096 * 1792 * 4096, t,
+             gemm_cpu(4096, 1792, 4096, oracle.E4M3FN, oracle.E4M3FN, oracle.BLOCK_1x128_128x128, 512))
+        del Y8
     name = "gemm_block_dgrad_4096x4096x14336"
     if want(name):
         dYq = codes((4096, 14336), E5)

@@ -180,6 +180,18 @@ def test_gemm_block_full_size_fprop(mlp_operands):
     _check_tol_and_amax(C, am, oracle.gemm_reference(o["qx"], E4, o["sx"], o["qw"], E4, o["sw"], mode))
 
 
+def test_gemm_block_tp8_shard_fprop(mlp_operands):
+    """The fprop on one GPU's share of an 8-way column-parallel layer (W rows
+    0..1791: 4096 x 1792 x 4096, 112 tiles of 256x256, fewer than the CUs, so
+    the whole output comes from the half-tile launch), every output element
+    against the float64 oracle."""
+    o = mlp_operands
+    mode = fq.BLOCK_1x128_128x128
+    qw, sw = np.ascontiguousarray(o["qw"][:1792]), np.ascontiguousarray(o["sw"][:14])
+    C, am = _gpu_gemm(o["qx"], E4, o["sx"], qw, E4, sw, mode)
+    _check_tol_and_amax(C, am, oracle.gemm_reference(o["qx"], E4, o["sx"], qw, E4, sw, mode))
+
+
 def test_gemm_block_full_size_dgrad(mlp_operands):
     """Block-scaled dgrad dX = dY W (4096 x 4096 x 14336, E5M2 x E4M3, through
     W's columnwise copy), every output element against the float64 oracle."""
