@@ -209,14 +209,16 @@ __device__ __forceinline__ void publish_partial(unsigned long long *slot, uint32
 // blocks): every lane polls its slots of pub[0, nparts) with agent-scope
 // loads, sleeping briefly between rounds, until the whole block has seen all
 // nparts slots carry the call's tag; then every lane gets the max of their
-// values.  It waits only for the other blocks of its launch, which never
-// wait, so the wait ends once they have run; it is bounded all the same, by
-// `rounds` polling rounds, after which the result is the canonical NaN (a
-// partial that arrives later carries a tag no later call accepts).  This
-// replaces a second, one-block kernel whose launch would follow the
-// producers' end.  NT lanes, nparts <= kMax, kMax a multiple of NT.
+// values, and the slots are put back to zero, so that a launch replayed from
+// a captured graph (same tag) waits for its own partials again.  It waits
+// only for the other blocks of its launch, which never wait, so the wait ends
+// once they have run; it is bounded all the same, by `rounds` polling rounds,
+// after which the result is the canonical NaN (a partial that arrives later
+// carries a tag no later call accepts).  This replaces a second, one-block
+// kernel whose launch would follow the producers' end.  NT lanes, nparts <=
+// kMax, kMax a multiple of NT.
 template <int NT, int kMax>
-__device__ __forceinline__ uint32_t collect_partials(const unsigned long long *pub, int nparts, uint32_t tag,
+__device__ __forceinline__ uint32_t collect_partials(unsigned long long *pub, int nparts, uint32_t tag,
                                                      uint32_t rounds)
 {
     __shared__ uint32_t red[NT / 64];
@@ -246,6 +248,10 @@ __device__ __forceinline__ uint32_t collect_partials(const unsigned long long *p
         }
         __builtin_amdgcn_s_sleep(2);
     }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+        if ((int)threadIdx.x + u * NT < nparts)
+            __hip_atomic_store(&pub[threadIdx.x + u * NT], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     m = block_max_u32<NT>(m, red);
     return expired ? kCanonicalNaN : m;
 }

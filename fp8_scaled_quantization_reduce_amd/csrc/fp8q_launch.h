@@ -14,7 +14,8 @@ namespace fp8q {
 // casts with output amax and the delayed step), block b publishes its
 // canonical magnitude max to pub[b] tagged with the call's tag (tag << 32 |
 // bits), and the finishing block waits until all pub[0 .. nblocks) carry the
-// tag: values of earlier calls carry other tags and are never cleared.
+// tag, then puts them back to zero (a partial that arrives after its
+// finishing block gave up carries a tag that no later call accepts).
 // Otherwise block b stores its max to part[b], a GEMM block folds its max into
 // part[b % kParts] with an unsigned atomic max (the canonical magnitude bits
 // order like the values, and the canonical NaN sorts above +inf), the cast

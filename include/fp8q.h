@@ -20,8 +20,11 @@
  *    own the first time it runs such a call (a host-side table; no device
  *    work), so calls on different streams never share partials.  Either the
  *    call's finishing block (the last block of its reducing launch) waits for
- *    the other blocks' partials, which carry a tag new to the call, or the
- *    call's last kernel reads the partials and clears them.
+ *    the other blocks' partials, which carry a tag new to the call, and
+ *    puts the slots back to zero once it has them, or the call's last kernel
+ *    reads the partials and clears them.  Either way the slot is left empty,
+ *    so these calls can be captured in a HIP graph and replayed (a replay
+ *    keeps the tag of its capture and still waits for its own partials).
  *    While one call enqueues its kernels it holds a host lock on its slot, so
  *    host threads that share a stream are safe.  A device on which more than
  *    64 streams have run reducing calls returns FP8Q_EUNSUPPORTED.
@@ -402,7 +405,8 @@ int fp8q_clock_monitor(uint64_t *out, const uint32_t *stop, void *stream);
  * 2^21, about a second and more); past the bound the call's amax is the
  * canonical NaN (and fp8_quantize_delayed records NaN in its ring).  Partials
  * that arrive after the bound carry that call's tag and are ignored by every
- * later call.  rounds = 0 makes every finishing block give up at once (used
+ * later eager call (a graph replay reuses its capture's tag, so a replay
+ * after one that gave up could take such a late partial).  rounds = 0 makes every finishing block give up at once (used
  * by the tests of this path); 0xFFFFFFFF restores the default.  Applies to
  * calls made afterwards, in every thread, on every device.
  * previous: host uint32 or NULL; receives the bound that was in force.

@@ -1,0 +1,112 @@
+"""Reducing entry points captured into a HIP graph (torch.cuda.graph) and
+replayed.
+
+A captured launch keeps the arguments of its capture, so every replay of a
+finishing-block launch waits for the same tag: the finishing block clears the
+slots it collected, and each replay must see only its own partials.  Between
+replays the test does eager work of its own (new input contents copied into
+the captured buffer, a synchronization) and checks every replay against the
+oracle for the input it ran on, alternating large and small amaxes so that a
+replay that took the previous replay's partials would report the wrong one.
+The library records no memset into the graph: its kernels carry the whole
+call.  Expected values come from the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import f32_bits, host, scalar
+
+pytestmark = pytest.mark.gpu
+
+fq = pytest.importorskip("fp8_scaled_quantization_reduce_amd")
+E4, E5 = oracle.E4M3FN, oracle.E5M2
+SHAPE = (2048, 4096)  # 1024 producing blocks of the cast, 512 of the amax pass
+
+
+def _inputs(count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for r in range(count):
+        mag = 100.0 if r % 2 == 0 else 0.25
+        out.append(workloads.to_bf16_bits(rng.standard_normal(SHAPE) * mag))
+    return out
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+
+def test_amax_and_cast_with_amax_replayed():
+    xs = _inputs(6, seed=5)
+    x = torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda")
+    q = torch.empty(SHAPE, dtype=torch.uint8, device="cuda")
+    am1, am2, si = scalar(-1.0), scalar(-1.0), scalar(0.5)
+    x.copy_(_bf16(xs[0]))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # eager warm-up on the capturing stream's kind of stream
+        fq.fp8_amax(x, am1)
+        fq.fp8_quantize_tensor(x, E4, q, scale_inv_in=si, amax_out=am2)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fq.fp8_amax(x, am1)
+        fq.fp8_quantize_tensor(x, E4, q, scale_inv_in=si, amax_out=am2)
+    scale = oracle.reciprocal(np.float32(0.5))
+    for r, xr in enumerate(xs):
+        x.copy_(_bf16(xr))
+        am1.fill_(-1.0)
+        am2.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = f32_bits(oracle.amax(xr))
+        assert f32_bits(host(am1)[0]) == want, r
+        assert f32_bits(host(am2)[0]) == want, r
+        assert np.array_equal(host(q), oracle.quantize(xr, E4, scale)), r
+
+
+def test_delayed_step_replayed():
+    """One captured delayed-scaling step (fixed ring slot 1 of 4) replayed on
+    new inputs: each replay casts with the scale the previous replay left,
+    records its own amax and derives the next scale from the ring."""
+    xs = _inputs(5, seed=6)
+    L = 4
+    x = torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda")
+    q = torch.empty(SHAPE, dtype=torch.uint8, device="cuda")
+    hist = torch.zeros((L, 1), dtype=torch.float32, device="cuda")
+    scale, scale_inv, am, qsi = scalar(1.0), scalar(1.0), scalar(-1.0), scalar(-1.0)
+    x.copy_(_bf16(xs[0]))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fq.fp8_quantize_delayed(x, E4, hist, 0, 1, E4, 0, 0, scale, scale_inv, q, q_scale_inv_out=qsi,
+                                amax_out=am)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fq.fp8_quantize_delayed(x, E4, hist, 0, 1, E4, 0, 0, scale, scale_inv, q, q_scale_inv_out=qsi,
+                                amax_out=am)
+    for r, xr in enumerate(xs):
+        x.copy_(_bf16(xr))
+        am.fill_(-1.0)
+        h0 = host(hist)[:, 0].copy()
+        s_in = host(scale_inv)[0]
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a = oracle.amax(xr)
+        assert f32_bits(host(am)[0]) == f32_bits(a), r
+        assert f32_bits(host(qsi)[0]) == f32_bits(s_in), r
+        assert np.array_equal(host(q), oracle.quantize(xr, E4, oracle.reciprocal(np.float32(s_in)))), r
+        # the oracle's update of the ring as it stood before this replay
+        h = np.ascontiguousarray(h0.reshape(L, 1))
+        sc, sci = np.ones(1, np.float32), np.ones(1, np.float32)
+        oracle.delayed_update(h, 0, a, 1, E4, 0, 0, sc, sci)
+        assert np.array_equal(f32_bits(host(hist)), f32_bits(h)), r
+        assert f32_bits(host(scale_inv)[0]) == f32_bits(sci[0]), r
+        assert f32_bits(host(scale)[0]) == f32_bits(sc[0]), r
