@@ -211,7 +211,11 @@ template <int kOut> constexpr int out_bytes() { return kOut == kOutF32 ? 4 : kOu
 // kCols * kB contiguous bytes.  Rows are kCols * kB bytes whose 16-byte chunks
 // are XOR-swizzled by the row, so that both the quad writes and the row reads
 // spread over the banks.  A pass holds kPassRows rows (the whole wave tile
-// unless fp32 does not fit the wave's share of the stages).
+// unless fp32 does not fit the wave's share of the stages).  The stores carry
+// the non-temporal hint: C is not read again by the kernel, and measured on
+// the MI355X every GEMM ran the same or up to 2% faster with it (the
+// weight-gradient GEMM with fp32 output 280.1 -> 274.5 us, 8192^3 per-tensor
+// 374.7 -> 371.0 us, same box).
 template <int kCols, int kB, int kRows, int kBudget> struct EpiStage {
     static constexpr int kPitch = kCols * kB, kNC = kPitch / 16, kRowsPerStore = 64 / kNC;
     static constexpr int kPassRows = kRows * kPitch <= kBudget ? kRows : kBudget / kPitch;
@@ -236,7 +240,7 @@ template <int kCols, int kB, int kRows, int kBudget> struct EpiStage {
         for (int s = 0; s < kPassRows / kRowsPerStore; ++s) {
             const int r = s * kRowsPerStore + rr;
             const uint4 v = *reinterpret_cast<const uint4 *>(ep + addr(r, c));
-            *reinterpret_cast<uint4 *>(Cb + ((row0 + r) * N + col0) * kB + 16 * c) = v;
+            st_stream(Cb + ((row0 + r) * N + col0) * kB + 16 * c, v);
         }
     }
 };
