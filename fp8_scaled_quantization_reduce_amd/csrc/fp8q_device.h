@@ -105,7 +105,9 @@ __device__ __forceinline__ uint32_t encode1(float x, float scale)
 // not kept in L2 or the last-level cache, which leaves those to the data that
 // is re-used.  Measured on the MI355X over 128 MiB inputs: a read-only pass
 // moves 6.7 TB/s with the hint against 6.2 TB/s without, and a 2-byte read /
-// 1-byte write pass (the bf16 cast) 8% faster with both hints.
+// 1-byte write pass (the bf16 cast) 8% faster with both hints.  The one
+// exception is the tail of the amax pass, which the cast of current scaling
+// reads again at once (amax_kernel keeps it in the caches).
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 ld_stream(const void *p)
