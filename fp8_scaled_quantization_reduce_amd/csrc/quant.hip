@@ -1015,14 +1015,14 @@ __device__ __forceinline__ int tlds_addr(int j, int d)
 template <int DT> struct RawPatch {
     static constexpr int kVec = DT == kBF16 ? 2 : 4; // 16-byte vectors per row
     uint4 w[4][kVec];
-    __device__ __forceinline__ void load(const void *x, int64_t ld, int64_t r0, int64_t c0)
+    template <bool kNT> __device__ __forceinline__ void load(const void *x, int64_t ld, int64_t r0, int64_t c0)
     {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(x) +
                                                              ((r0 + r) * ld + c0) * (DT == kBF16 ? 2 : 4));
 #pragma unroll
-            for (int k = 0; k < kVec; ++k) w[r][k] = p[k];
+            for (int k = 0; k < kVec; ++k) w[r][k] = kNT ? ld_stream(p + k) : p[k];
         }
     }
     __device__ __forceinline__ void zero()
@@ -1134,6 +1134,7 @@ __device__ __forceinline__ void stage_transposed(uint32_t *tl, const uint32_t cw
 
 // Write the transposed tile from LDS to q_col [cols][rows]: output row
 // (tile column j), 16 consecutive rows k*16 .. k*16+15 per 16-byte store.
+template <bool kNT>
 __device__ __forceinline__ void store_transposed(const uint32_t *tl, uint8_t *q_col, int64_t rows, int64_t cols,
                                                  int64_t row0, int64_t col0)
 {
@@ -1143,7 +1144,8 @@ __device__ __forceinline__ void store_transposed(const uint32_t *tl, uint8_t *q_
         const int j = p >> 3, k = p & 7;
         if (col0 + j < cols && row0 + 16 * k < rows) {
             const uint4 v = *reinterpret_cast<const uint4 *>(tl + tlds_addr(j, 4 * k));
-            *reinterpret_cast<uint4 *>(q_col + (col0 + j) * rows + row0 + 16 * k) = v;
+            if constexpr (kNT) st_stream(q_col + (col0 + j) * rows + row0 + 16 * k, v);
+            else *reinterpret_cast<uint4 *>(q_col + (col0 + j) * rows + row0 + 16 * k) = v;
         }
     }
 }
@@ -1205,12 +1207,24 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
     }
     uint32_t m_all = 0; // per-tensor fused amax
 
+    // Cache hints, chosen per mode by measurement on the MI355X (unlike the
+    // flat kernels, a tile kernel's 128-byte row pieces and transposed
+    // columns do not all gain from the non-temporal hint): the per-tensor
+    // cast streams its loads and its column stores (8192x8192 bf16 55.3 ->
+    // 54.2 us), the block modes stream their column stores (128x128 blocks of
+    // 7168x4096 25.6 -> 24.5 us, 1x128 blocks of 4096x7168 30.5 -> 29.9 us),
+    // and the MXFP8 and per-direction modes, slower with either hint, keep
+    // plain accesses; streamed loads alone made the per-tensor cast 13%
+    // slower, and streamed row stores slowed every mode.
+    constexpr bool kNTLoad = kMode == kTilePerTensor;
+    constexpr bool kNTColStore = kMode == kTilePerTensor || kMode == kTileBlock128 || kMode == kTileBlock1x128;
+
     // The lane's patch of tile t (rows % 4 == 0 and cols % 16 == 0, so a patch
     // is either whole or entirely outside the matrix).
     auto load_patch = [&](int64_t t, RawPatch<DT> &raw) {
         const int64_t tr = t / tiles_c, tc = t - tr * tiles_c;
         const int64_t r0 = tr * kTile + 4 * ig, c0 = tc * kTile + 16 * jg;
-        if (r0 < rows && c0 < cols) raw.load(x, cols, r0, c0);
+        if (r0 < rows && c0 < cols) raw.template load<kNTLoad>(x, cols, r0, c0);
         else raw.zero();
     };
     for (int64_t t = blockIdx.x; t < tiles; t += nwork) {
@@ -1496,7 +1510,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 stage_transposed(tl, cw, ig, jg);
             }
             __syncthreads();
-            store_transposed(tl, q_col, rows, cols, row0, col0);
+            store_transposed<kNTColStore>(tl, q_col, rows, cols, row0, col0);
             if constexpr (kMode == kTileMX) {
                 const int64_t xcol = rows / 32;
                 if (threadIdx.x < kTile && col0 + threadIdx.x < cols)
