@@ -59,6 +59,34 @@ def test_amax_tensor_fp32_and_full_size_bf16():
     assert f32_bits(_gpu_amax(xb)) == f32_bits(oracle.amax(xb))
 
 
+def test_amax_streamed_head_and_cached_tail():
+    """Inputs of 160 MiB: the amax pass streams the head and loads the last
+    128 MiB plainly (kept in the caches for the cast that follows).  The
+    maximum is placed in the first element, on both sides of that boundary
+    (in units of 16 KiB counted from the start), in the last whole unit and in
+    the tail shorter than one 16-byte vector; each case against the oracle."""
+    unit_bytes, kept_bytes = 16 << 10, 128 << 20
+    rng = np.random.default_rng(44)
+    for dtype_bytes, n in ((2, (80 << 20) + 123), (4, (40 << 20) + 5)):
+        if dtype_bytes == 2:
+            base = workloads.to_bf16_bits(rng.standard_normal(n))
+            big = np.uint16(0x4700)    # 32768.0
+        else:
+            base = rng.standard_normal(n).astype(np.float32)
+            big = np.float32(-32768.5)
+        per_vec = 16 // dtype_bytes
+        units = -(-(n // per_vec) // 1024)
+        boundary = (units - kept_bytes // unit_bytes) * (unit_bytes // dtype_bytes)
+        xd = to_dev(base)
+        for pos in (0, boundary - 1, boundary, n - 200, n - 1):
+            x = base.copy()
+            x[pos] = big
+            xd.copy_(to_dev(x))
+            out = scalar(-1.0)
+            fq.fp8_amax(xd, out)
+            assert f32_bits(host(out)[0]) == f32_bits(oracle.amax(x)), (dtype_bytes, pos)
+
+
 # ---------------------------------------------------------- per-tensor cast --
 def _gpu_quantize(x, fmt, *, amax_in=None, margin=0, scale_inv_in=None, with_amax=False):
     xd = to_dev(x)
