@@ -250,20 +250,16 @@ hipError_t launch_clock_monitor(uint64_t *out, const uint32_t *stop, hipStream_t
 //
 // An amax is read to scale the same tensor's cast (current scaling), which
 // reads x again right after it.  The last kAmaxCacheKeep bytes of the input
-// are therefore loaded without the non-temporal hint, so that the cast finds
-// them in the caches: the L2 of each XCD (4 MB, 32 MiB over the 8) and the
-// 256 MB last-level cache; everything before them streams.  An L2 hit needs
-// the second pass to read a unit on the XCD that loaded it: unit u (16 KiB of
-// bf16 here, and one unit of the flat cast) runs on block u mod G, and blocks
-// are dealt round-robin to the XCDs, so both kernels read unit u on XCD
-// u mod 8 when G is a multiple of 8 (a cast that walked the units backwards,
-// putting each on another XCD, lost most of the gain in a probe).  Measured
-// on the MI355X, fp8_amax then fp8_quantize_tensor(amax_in) on 8192x8192
-// bf16 inputs rotating over 1 GiB: 57.3 us with every load streaming, 54.0
-// with the last 32 MiB kept, 52.6 with 64 MiB and 51.6 with all 128 MiB; the
-// amax alone takes 21.6, 21.2, 22.3 and 23.1 us.  The pair is what the method
-// runs (the delayed recipe fuses its amax into the cast), so it is the one
-// optimised.
+// are therefore loaded without the non-temporal hint, so that the 256 MB
+// last-level cache still holds them when the cast reads them; everything
+// before them streams.  Measured on the MI355X, fp8_amax then
+// fp8_quantize_tensor(amax_in) on 8192x8192 bf16 inputs rotating over 1 GiB:
+// 57.3 us with every load streaming, 54.0 with the last 32 MiB kept, 52.6
+// with 64 MiB and 51.6 with all 128 MiB; the amax alone takes 21.6, 21.2,
+// 22.3 and 23.1 us.  (The cast's L2 hits, misses and fetched bytes are those
+// of a cast of a cold input: the second read is served beyond the L2.)  The
+// pair is what the method runs (the delayed recipe fuses its amax into the
+// cast), so it is the one optimised.
 #ifndef FP8Q_AMAX_U
 #define FP8Q_AMAX_U 4
 #endif
@@ -287,9 +283,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void *__restrict__
     const int64_t nvec = n / kPer;
     const int64_t units = ceil_div(nvec, (int64_t)kThreads * kAmaxU);
     const uint4 *__restrict__ xv = reinterpret_cast<const uint4 *>(x);
-    // units from `kept` on are loaded into the caches (for fp32 input a cast
-    // unit spans two of these units on two XCDs, so only the last-level cache
-    // serves the cast)
+    // units from `kept` on are loaded without the streaming hint
     const int64_t kept = units - kAmaxCacheKeep / (kThreads * kAmaxU * 16);
     uint32_t m = 0;
     u16x2 m2 = {0, 0};
