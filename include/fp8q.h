@@ -103,6 +103,9 @@ extern "C" {
  *   amax   one float, written (overwritten) by the call
  * A NaN element gives the canonical NaN 0x7FC00000; n == 0 gives 0.
  * The result is exact (an integer max over magnitude bits, order-free).
+ * Cache use: the call streams x, except its last 128 MiB, which it reads
+ * with ordinary loads so that the cast of current scaling, which reads x
+ * again right after it, finds them in the last-level cache.
  */
 int fp8_amax(const void *x, int32_t dtype, int64_t n, float *amax, void *stream);
 
