@@ -178,6 +178,24 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// Max with the value of lane ^ 16 or lane ^ 32, through gfx950's lane-swap
+// instructions (vector ALU, no LDS round trip): with both operands the same
+// register, v_permlane16_swap leaves each lane its own value in one result
+// and its lane ^ 16 partner's in the other (odd and even 16-lane rows
+// exchanged), v_permlane32_swap likewise for the two 32-lane halves; the max
+// of the two results is the pair's max in every lane (checked lane by lane on
+// the MI355X).
+__device__ __forceinline__ uint32_t max_xor16(uint32_t m)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+    return max((uint32_t)p[0], (uint32_t)p[1]);
+}
+__device__ __forceinline__ uint32_t max_xor32(uint32_t m)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+    return max((uint32_t)p[0], (uint32_t)p[1]);
+}
+
 // Block max (blockDim.x = kThreads, a multiple of 64); every thread gets the
 // result.  `lds` must hold kThreads/64 words.
 template <int kThreads>

@@ -1322,8 +1322,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 for (int k = 0; k < 16; ++k) {
                     uint32_t m = cmax[k];
                     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xF, 0xF, false)); // lane ^ 8
-                    m = max(m, (uint32_t)__builtin_amdgcn_ds_swizzle((int)m, 0x401F));                    // lane ^ 16
-                    m = max(m, (uint32_t)__shfl_xor((int)m, 32));                                         // lane ^ 32
+                    m = max_xor16(m);                                                                     // lane ^ 16
+                    m = max_xor32(m);                                                                     // lane ^ 32
                     worst = max(worst, m);
                     const MxScale ms = mx_scale<F>(m);
                     cm[k] = ms.mult;
@@ -1364,7 +1364,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 uint32_t m = rm[r];
                 m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false)); // lane ^ 1
                 m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false)); // lane ^ 2
-                m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+                // lane 7 - i of the 8 (DPP row_half_mirror): the other quad
+                m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
                 const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
                 if (jg == 0) s_row[(r0 + r) * bcols + tc] = sc.s;
 #pragma unroll
@@ -1395,8 +1396,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 for (int k = 0; k < 16; ++k) {
                     uint32_t m = cm[k];
                     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xF, 0xF, false)); // lane ^ 8
-                    m = max(m, (uint32_t)__builtin_amdgcn_ds_swizzle((int)m, 0x401F));                    // lane ^ 16
-                    m = max(m, (uint32_t)__shfl_xor((int)m, 32));                                         // lane ^ 32
+                    m = max_xor16(m);                                                                     // lane ^ 16
+                    m = max_xor32(m);                                                                     // lane ^ 32
                     cm[k] = m;
                 }
                 if ((threadIdx.x & 63) < 8) {
