@@ -110,3 +110,73 @@ def test_delayed_step_replayed():
         assert np.array_equal(f32_bits(host(hist)), f32_bits(h)), r
         assert f32_bits(host(scale_inv)[0]) == f32_bits(sci[0]), r
         assert f32_bits(host(scale)[0]) == f32_bits(sc[0]), r
+
+
+def test_gemm_amax_and_cast_stats_replayed():
+    """The reductions folded by a following one-block kernel: a GEMM with output
+    amax (tile maxima into partial slots, folded and cleared by the finish
+    kernel) and the cast statistics (counts summed and cleared the same way),
+    captured once and replayed on new operands and scales.  Each replay's C
+    equals an eager call's on the same operands bit for bit, its amax is
+    max |C| of what it emitted, C is within the GEMM tolerance of the float64
+    oracle, and the counts equal the oracle's; the scales alternate by 2^8 so
+    that a replay folding a previous replay's partials would report the wrong
+    amax."""
+    rng = np.random.default_rng(9)
+    M, N, K = 512, 768, 512  # 2 x 3 tiles of 256 x 256
+    A = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    B = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sA, sB = scalar(1.0), scalar(1.0)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    am = scalar(-1.0)
+    x = torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda")
+    si = scalar(0.01)
+    st = torch.full((4,), -1, dtype=torch.int64, device="cuda")
+
+    def codes(shape):
+        v = workloads.to_bf16_bits(rng.standard_normal(shape))
+        r = oracle.quantize_tensor(v, E4, amax_in=oracle.amax(v))
+        return r["q"], r["scale_inv"]
+
+    def load(r):
+        a, sa = codes((M, K))
+        b, sb = codes((N, K))
+        sa = np.float32(sa * (256.0 if r % 2 == 0 else 1.0 / 256.0))
+        xs = workloads.to_bf16_bits(rng.standard_normal(SHAPE) * (100.0 if r % 2 == 0 else 0.001))
+        A.copy_(torch.from_numpy(a))
+        B.copy_(torch.from_numpy(b))
+        sA.fill_(float(sa))
+        sB.fill_(float(sb))
+        x.copy_(_bf16(xs))
+        return a, sa, b, sb, xs
+
+    load(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fq.fp8_scaled_gemm(A, E4, sA, B, E4, sB, fq.PER_TENSOR, C, am)
+        fq.fp8_cast_stats(x, E4, si, st)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fq.fp8_scaled_gemm(A, E4, sA, B, E4, sB, fq.PER_TENSOR, C, am)
+        fq.fp8_cast_stats(x, E4, si, st)
+    for r in range(4):
+        a, sa, b, sb, xs = load(r)
+        am.fill_(-1.0)
+        st.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        c_rep, am_rep, st_rep = host(C).copy(), host(am)[0], host(st).copy()
+        C2 = torch.empty_like(C)
+        am2 = scalar(-1.0)
+        fq.fp8_scaled_gemm(A, E4, sA, B, E4, sB, fq.PER_TENSOR, C2, am2)
+        torch.cuda.synchronize()
+        assert np.array_equal(c_rep.view(np.uint16), host(C2).view(np.uint16)), r
+        c32 = (c_rep.view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+        assert f32_bits(am_rep) == f32_bits(np.max(np.abs(c32))) == f32_bits(host(am2)[0]), r
+        R = oracle.gemm_reference(a, E4, sa, b, E4, sb)
+        assert np.max(np.abs(c32.astype(np.float64) - R)) <= 1e-2 * np.max(np.abs(R)), r
+        assert np.array_equal(st_rep.astype(np.uint64), oracle.cast_stats(xs, E4, np.float32(0.01)).astype(np.uint64)), r
