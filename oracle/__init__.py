@@ -30,6 +30,7 @@ E4M3FN, E5M2 = 0, 1
 F32, BF16 = 0, 1
 ALGO_MAX, ALGO_MOST_RECENT = 0, 1
 PER_TENSOR, BLOCK_1x128_128x128, BLOCK_1x128_1x128, MXFP8 = 0, 1, 2, 3
+SUBQ_BLOCK_128x128, SUBQ_BLOCK_1x128, SUBQ_MXFP8 = 0, 1, 2
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -483,6 +484,35 @@ def quantize_hybrid(x: np.ndarray, row_fmt: int, col_fmt: int, col_source: int, 
         sc_c = reciprocal(s_c)
     q_col = transpose(quantize(np.ascontiguousarray(src), col_fmt, sc_c))
     return dict(q_row=q_row, q_col=q_col, row_scale_inv=s_r, col_scale_inv=s_c)
+
+
+def _block_subquantizer(src: np.ndarray, recipe: int, fmt: int):
+    """(codes, scales) of one block sub-quantizer applied to the rows of src."""
+    if recipe == SUBQ_BLOCK_128x128:
+        return quantize_blocks(src, fmt, 128, 128)
+    if recipe == SUBQ_BLOCK_1x128:
+        return quantize_blocks(src, fmt, 1, 128)
+    if recipe == SUBQ_MXFP8:
+        return quantize_mx(src, fmt)
+    raise ValueError("unknown sub-quantizer %r" % recipe)
+
+
+def quantize_hybrid_blockwise(x: np.ndarray, row_recipe: int, row_fmt: int, col_recipe: int, col_fmt: int):
+    """Per-direction ("hybrid") quantization with block sub-quantizers
+    ("[Pytorch][Common] Hybrid quantization #2817": each direction has a
+    quantizer of its own, format and recipe, and blockwise or MXFP8
+    quantizers may fill either role; the columnwise copy is taken from the
+    original input here).
+
+    The rowwise copy is the row recipe in row_fmt applied to x; the
+    columnwise copy is the column recipe in col_fmt applied to x^T.  A recipe
+    is 128x128 blocks, 1x128 blocks (both with FP32 block scales, margin 0,
+    like quantize_block) or MXFP8 1x32 blocks with E8M0 scales (quantize_mx).
+    Returns dict(q_row [R][C], s_row, q_col [C][R], s_col)."""
+    x = np.ascontiguousarray(x)
+    q_row, s_row = _block_subquantizer(x, row_recipe, row_fmt)
+    q_col, s_col = _block_subquantizer(transpose(x), col_recipe, col_fmt)
+    return dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col)
 
 
 def cast_stats(x: np.ndarray, fmt: int, scale_inv) -> np.ndarray:

@@ -730,6 +730,66 @@ def test_hybrid_cross_format_directions_are_independent():
     assert np.array_equal(h["q_row"], r["q"]) and np.array_equal(h["q_col"], c["q"])
 
 
+SUBQ = (oracle.SUBQ_BLOCK_128x128, oracle.SUBQ_BLOCK_1x128, oracle.SUBQ_MXFP8)
+TOP_CODE = {E4: 0x7E, E5: 0x7B}  # +FP8_MAX: 448 = 1.75 * 2^8, 57344 = 1.75 * 2^15
+
+
+@pytest.mark.parametrize("recipe", SUBQ)
+def test_hybrid_blockwise_one_format_is_the_single_recipe(recipe):
+    """One format in both directions: the per-direction quantizer with block
+    sub-quantizers reduces to the block (resp. MXFP8) quantizer with its
+    columnwise copy, both pinned above."""
+    x = workloads.block_act(256, 384, seed=23)
+    for fmt in (E4, E5):
+        h = oracle.quantize_hybrid_blockwise(x, recipe, fmt, recipe, fmt)
+        if recipe == oracle.SUBQ_MXFP8:
+            want = oracle.quantize_mx(x, fmt) + oracle.quantize_mx_colwise(x, fmt)
+        else:
+            want = oracle.quantize_block(x, fmt, 128 if recipe == oracle.SUBQ_BLOCK_128x128 else 1)
+        for got, w in zip((h["q_row"], h["s_row"], h["q_col"], h["s_col"]), want):
+            assert got.dtype == w.dtype and np.array_equal(got, w)
+
+
+def test_hybrid_blockwise_cross_format_blocks_are_independent_tensors():
+    """E4M3 rows and E5M2 columns, 128x128 blocks: every block of the
+    columnwise copy is the per-tensor current-scaling cast of that block of
+    x^T in E5M2 (torch-pinned above), every block of the rowwise copy that of
+    x in E4M3; a block's maximum takes its own format's top code."""
+    x = workloads.block_weight(256, 384, seed=24, std=3.0)
+    h = oracle.quantize_hybrid_blockwise(x, oracle.SUBQ_BLOCK_128x128, E4, oracle.SUBQ_BLOCK_128x128, E5)
+    assert h["s_row"].shape == (2, 3) and h["s_col"].shape == (3, 2) and h["q_col"].shape == (384, 256)
+    for I in range(2):
+        for J in range(3):
+            rs, cs = slice(I * 128, (I + 1) * 128), slice(J * 128, (J + 1) * 128)
+            blk = np.ascontiguousarray(x[rs, cs])
+            r = oracle.quantize_tensor(blk, E4, amax_in=oracle.amax(blk))
+            c = oracle.quantize_tensor(np.ascontiguousarray(blk.T), E5, amax_in=oracle.amax(blk))
+            assert h["s_row"][I, J] == r["scale_inv"] and np.array_equal(h["q_row"][rs, cs], r["q"])
+            assert h["s_col"][J, I] == c["scale_inv"] and np.array_equal(h["q_col"][cs, rs], c["q"])
+            assert np.any((h["q_row"][rs, cs] & 0x7F) == TOP_CODE[E4])
+            assert np.any((h["q_col"][cs, rs] & 0x7F) == TOP_CODE[E5])
+
+
+def test_hybrid_blockwise_cross_recipe_directions():
+    """MXFP8 E4M3 rows with 1x128 E5M2 columns: the rowwise copy is MXFP8 of
+    x; each 128-row segment of a column is a tensor of its own cast to E5M2,
+    whose maximum takes E5M2's top code."""
+    x = workloads.block_act(256, 256, seed=25)
+    h = oracle.quantize_hybrid_blockwise(x, oracle.SUBQ_MXFP8, E4, oracle.SUBQ_BLOCK_1x128, E5)
+    q, sc = oracle.quantize_mx(x, E4)
+    assert np.array_equal(h["q_row"], q) and np.array_equal(h["s_row"], sc)
+    assert h["q_col"].shape == (256, 256) and h["s_col"].shape == (256, 2) and h["s_col"].dtype == np.float32
+    xf = workloads.bf16_bits_to_f32(x)
+    for j in (0, 77, 255):
+        for I in range(2):
+            seg = np.ascontiguousarray(x[I * 128:(I + 1) * 128, j])
+            r = oracle.quantize_tensor(seg, E5, amax_in=oracle.amax(seg))
+            assert h["s_col"][j, I] == r["scale_inv"]
+            assert np.array_equal(h["q_col"][j, I * 128:(I + 1) * 128], r["q"])
+            if np.abs(xf[I * 128:(I + 1) * 128, j]).max() > 0:
+                assert np.any((h["q_col"][j, I * 128:(I + 1) * 128] & 0x7F) == TOP_CODE[E5])
+
+
 def test_hybrid_rowwise_dequantized_is_idempotent_in_one_format():
     """Quantize, dequantize, quantize again with the same format and scale
     gives the same codes (the FP8 grid is far coarser than one fp32 rounding
