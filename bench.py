@@ -536,6 +536,23 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
                                    amax_in=oracle.amax(host_x()))
         hbm(name, 4 * n, t, cpu(hyb_cpu, 4 * n / 1e9, "GB/s"))
 
+    # next: per-direction quantization with MXFP8 sub-quantizers, E4M3
+    # forward copy and E5M2 backward copy of 8192^2 bf16 in one pass
+    # (2 + 1 + 1 B/elem + 2 scale bytes per 32 elements)
+    name = "hybrid_mxfp8_e4m3_rows_e5m2_cols_bf16_8192x8192"
+    if want(name):
+        sm = [torch.empty((8192, 256), dtype=torch.uint8, device=dev) for _ in range(4)]
+        smt = [torch.empty((8192, 256), dtype=torch.uint8, device=dev) for _ in range(4)]
+        t = timed(lambda i: fq.fp8_quantize_hybrid_blockwise(
+            x2[i], fq.SUBQ_MXFP8, E4, fq.SUBQ_MXFP8, E5, q_row=qr[i % 4], s_row=sm[i % 4], q_col=qc[i % 4],
+            s_col=smt[i % 4], stream=stream), 16, rotate=len(xs))
+
+        def hyb_mx_cpu():
+            oracle.quantize_hybrid_blockwise(host_x(), oracle.SUBQ_MXFP8, oracle.E4M3FN, oracle.SUBQ_MXFP8,
+                                             oracle.E5M2)
+        hbm(name, 4 * n + 2 * n // 32, t, cpu(hyb_mx_cpu, (4 * n + 2 * n // 32) / 1e9, "GB/s"))
+        del sm, smt
+
     # next: cast statistics (overflow / underflow counts) of 8192^2 bf16
     # under a given scale (2 B/elem read), alone and fused into the cast
     # (2 B read + 1 B written per element, against 3 B + 2 B for a cast

@@ -666,6 +666,69 @@ extern "C" int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, i
     return c.ret(fp8_quantize_hybrid_impl(c, x, dtype, rows, cols, row_fmt, col_fmt, col_source, amax_in, row_margin, col_margin, row_scale_inv_in, col_scale_inv_in, q_row, q_col, row_scale_inv_out, col_scale_inv_out, amax_out, stream));
 }
 
+// bytes of the scale buffer of one direction's copy of a [rows][cols] tensor
+// under a block sub-quantizer, rows and cols being the copy's own (x^T's for
+// the columnwise copy)
+static int64_t subq_scale_bytes(int32_t recipe, int64_t rows, int64_t cols)
+{
+    if (recipe == FP8Q_SUBQ_BLOCK_128x128) return (rows / 128) * (cols / 128) * 4;
+    if (recipe == FP8Q_SUBQ_BLOCK_1x128) return rows * (cols / 128) * 4;
+    return rows * (cols / 32);
+}
+
+static bool valid_subq(int32_t r)
+{
+    return r == FP8Q_SUBQ_BLOCK_128x128 || r == FP8Q_SUBQ_BLOCK_1x128 || r == FP8Q_SUBQ_MXFP8;
+}
+
+static int fp8_quantize_hybrid_blockwise_impl(Call &c, const void *x, int32_t dtype, int64_t rows, int64_t cols,
+                                              int32_t row_recipe, int32_t row_fmt, uint8_t *q_row, void *s_row,
+                                              int32_t col_recipe, int32_t col_fmt, uint8_t *q_col, void *s_col,
+                                              void *stream)
+{
+    const char *fn = "fp8_quantize_hybrid_blockwise";
+    if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
+    if (!valid_fmt(row_fmt) || !valid_fmt(col_fmt)) return fail(FP8Q_EINVAL, "%s: unknown format", fn);
+    if (!valid_subq(row_recipe) || !valid_subq(col_recipe))
+        return fail(FP8Q_EINVAL, "%s: unknown sub-quantizer (row %d, col %d)", fn, (int)row_recipe, (int)col_recipe);
+    if (rows < 0 || cols < 0) return fail(FP8Q_EINVAL, "%s: negative shape", fn);
+    if (rows % 128 || cols % 128) return fail(FP8Q_EUNSUPPORTED, "%s: rows and cols must be multiples of 128", fn);
+    if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 31)
+        return fail(FP8Q_EUNSUPPORTED, "%s: a dimension exceeds 2^31", fn);
+    if ((q_row == nullptr) != (s_row == nullptr)) return fail(FP8Q_EINVAL, "%s: give both q_row and s_row or neither", fn);
+    if ((q_col == nullptr) != (s_col == nullptr)) return fail(FP8Q_EINVAL, "%s: give both q_col and s_col or neither", fn);
+    const int64_t n = rows * cols;
+    if (n == 0) return ok();
+    if (!q_row && !q_col) return fail(FP8Q_EINVAL, "%s: at least one of the two copies is needed", fn);
+    if (!x || !aligned(x, 16)) return fail(FP8Q_EINVAL, "%s: x must be a 16-byte aligned pointer", fn);
+    if ((q_row && !aligned(q_row, 16)) || (q_col && !aligned(q_col, 16)))
+        return fail(FP8Q_EINVAL, "%s: q_row / q_col must be 16-byte aligned", fn);
+    if ((s_row && !aligned(s_row, 4)) || (s_col && !aligned(s_col, 4)))
+        return fail(FP8Q_EINVAL, "%s: s_row / s_col must be 4-byte aligned", fn);
+    const void *buf[5] = {x, q_row, s_row, q_col, s_col};
+    const int64_t len[5] = {n * dsize(dtype), n, subq_scale_bytes(row_recipe, rows, cols), n,
+                            subq_scale_bytes(col_recipe, cols, rows)};
+    for (int i = 0; i < 5; ++i)
+        for (int j = 0; j < i; ++j)
+            if (overlap(buf[i], len[i], buf[j], len[j])) return fail(FP8Q_EINVAL, "%s: buffers overlap", fn);
+    return hip_status(fp8q::launch_hybrid_blockwise(x, dtype, rows, cols, row_recipe, row_fmt, q_row, s_row,
+                                                    col_recipe, col_fmt, q_col, s_col, (hipStream_t)stream),
+                      fn);
+}
+
+extern "C" int fp8_quantize_hybrid_blockwise(const void *x, int32_t dtype, int64_t rows, int64_t cols,
+                                             int32_t row_recipe, int32_t row_fmt, uint8_t *q_row, void *s_row,
+                                             int32_t col_recipe, int32_t col_fmt, uint8_t *q_col, void *s_col,
+                                             void *stream)
+{
+    Call c("fp8_quantize_hybrid_blockwise", stream);
+    c.args("dtype=%lld rows=%lld cols=%lld row_recipe=%lld row_fmt=%lld col_recipe=%lld col_fmt=%lld",
+           (long long)dtype, (long long)rows, (long long)cols, (long long)row_recipe, (long long)row_fmt,
+           (long long)col_recipe, (long long)col_fmt);
+    return c.ret(fp8_quantize_hybrid_blockwise_impl(c, x, dtype, rows, cols, row_recipe, row_fmt, q_row, s_row,
+                                                    col_recipe, col_fmt, q_col, s_col, stream));
+}
+
 static int fp8_cast_stats_impl(Call &c, const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *scale_inv,
                                uint64_t *stats, void *stream)
 {

@@ -1147,7 +1147,7 @@ __device__ __forceinline__ void store_transposed(const uint32_t *tl, uint8_t *q_
 // One block loops over tiles t = blockIdx.x, blockIdx.x + G, ... (tile row
 // t / tiles_per_row, tile column t % tiles_per_row), G the number of tile
 // blocks (with kAmax the launch has one more, its finishing block).
-template <int F, int DT, int kMode, bool kAmax>
+template <int F, int DT, int kMode, bool kAmax, int FCol = F>
 __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__ x, int64_t rows, int64_t cols,
                                                         ScaleSrc src, uint8_t *__restrict__ q_row,
                                                         uint8_t *__restrict__ q_col, void *__restrict__ s_row_p,
@@ -1162,7 +1162,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
         return;
     }
     constexpr bool kHybrid = kMode >= kTileHybrid;
-    constexpr int FC = kHybrid ? ((kMode - kTileHybrid) & 1) : F; // format of the column codes
+    constexpr int FC = kHybrid ? ((kMode - kTileHybrid) & 1) : FCol; // format of the column codes
     constexpr bool kDeq = kHybrid && ((kMode - kTileHybrid) >> 1); // columns from the dequantized rows
     // block scales: fp32 (128x128, 1x128) or E8M0 bytes (MXFP8)
     float *__restrict__ s_row = reinterpret_cast<float *>(s_row_p);
@@ -1262,10 +1262,13 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
             patch_row_max<DT>(p, rm);
             uint32_t m = max(max(rm[0], rm[1]), max(rm[2], rm[3]));
             m = block_max_u32<kThreads>(m, red);
-            const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
+            const float amax_b = __uint_as_float(canonical_amax_bits(m));
+            const Scales sc = current_scales(amax_b, Fmt<F>::kMax, 0);
+            // columns in a format of their own: the same block amax, that format's scale
+            if constexpr (FC != F) sc_col = current_scales(amax_b, Fmt<FC>::kMax, 0);
             if (threadIdx.x == 0) {
-                s_row[tr * bcols + tc] = sc.s;
-                if (s_col) s_col[tc * brows + tr] = sc.s;
+                if (q_row) s_row[tr * bcols + tc] = sc.s;
+                if (s_col) s_col[tc * brows + tr] = FC != F ? sc_col.s : sc.s;
             }
             // the block scale is uniform: finite and nonzero exactly when the
             // block holds no NaN or infinity
@@ -1294,7 +1297,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 const uint32_t b1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ms.byte, 0x102, 0xF, 0xF, false);
                 const uint32_t b2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ms.byte, 0x104, 0xF, 0xF, false);
                 const uint32_t b3 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ms.byte, 0x106, 0xF, 0xF, false);
-                if (jg == 0 && valid)
+                if (jg == 0 && valid && q_row)
                     *reinterpret_cast<uint32_t *>(e_row + (r0 + r) * xrow + (col0 >> 5)) =
                         ms.byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
 #pragma unroll
@@ -1325,7 +1328,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     m = max_xor16(m);                                                                     // lane ^ 16
                     m = max_xor32(m);                                                                     // lane ^ 32
                     worst = max(worst, m);
-                    const MxScale ms = mx_scale<F>(m);
+                    const MxScale ms = mx_scale<FC>(m);
                     cm[k] = ms.mult;
                     cb[k] = ms.byte;
                 }
@@ -1344,8 +1347,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
 #pragma unroll
                         for (int q4 = 0; q4 < 4; ++q4) {
                             const int k = 4 * q4;
-                            cc[r][q4] = encode4s<F, kR>(PV(r, k), PV(r, k + 1), PV(r, k + 2), PV(r, k + 3), cm[k],
-                                                        cm[k + 1], cm[k + 2], cm[k + 3]);
+                            cc[r][q4] = encode4s<FC, kR>(PV(r, k), PV(r, k + 1), PV(r, k + 2), PV(r, k + 3), cm[k],
+                                                         cm[k + 1], cm[k + 2], cm[k + 3]);
                         }
                 };
                 enc_cols(Rep<false>{});
@@ -1367,7 +1370,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 // lane 7 - i of the 8 (DPP row_half_mirror): the other quad
                 m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
                 const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
-                if (jg == 0) s_row[(r0 + r) * bcols + tc] = sc.s;
+                if (jg == 0 && q_row) s_row[(r0 + r) * bcols + tc] = sc.s;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
                     cw[r][q4] = encode4<F, false>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
@@ -1411,7 +1414,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 if (threadIdx.x < kTile) {
                     const uint32_t m = max(max(colmax[threadIdx.x], colmax[kTile + threadIdx.x]),
                                            max(colmax[2 * kTile + threadIdx.x], colmax[3 * kTile + threadIdx.x]));
-                    const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
+                    const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<FC>::kMax, 0);
                     colscale[threadIdx.x] = sc.scale;
                     s_col[(col0 + threadIdx.x) * brows + tr] = sc.s;
                     if (!finite_nonzero(sc.scale)) colbad = 1;
@@ -1439,8 +1442,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                         for (int q4 = 0; q4 < 4; ++q4) {
                             const int k = 4 * q4;
                             const float *cs = colscale + 16 * jg + k;
-                            cc[r][q4] = encode4s<F, kR>(PV(r, k), PV(r, k + 1), PV(r, k + 2), PV(r, k + 3), cs[0],
-                                                        cs[1], cs[2], cs[3]);
+                            cc[r][q4] = encode4s<FC, kR>(PV(r, k), PV(r, k + 1), PV(r, k + 2), PV(r, k + 3), cs[0],
+                                                         cs[1], cs[2], cs[3]);
                         }
                 };
                 enc_cols(Rep<false>{});
@@ -1498,6 +1501,25 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     for (int r = 0; r < 4; ++r)
 #pragma unroll
                         for (int q4 = 0; q4 < 4; ++q4) asm volatile("" : "+v"(cw[r][q4]));
+                    enc_cols(Rep<true>{});
+                }
+                stage_transposed(tl, cc, ig, jg);
+            } else if constexpr (kMode == kTileBlock128 && FC != F) {
+                // the block's column codes in their own format, from x
+                opaque(p);
+                uint32_t cc[4][4];
+                auto enc_cols = [&](auto rep) {
+                    constexpr bool kR = decltype(rep)::value;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4)
+                            cc[r][q4] = encode4<FC, kR>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
+                                                        PV(r, 4 * q4 + 3), sc_col.scale);
+                };
+                enc_cols(Rep<false>{});
+                if (!finite_nonzero(sc_col.scale)) {
+                    opaque(p);
                     enc_cols(Rep<true>{});
                 }
                 stage_transposed(tl, cc, ig, jg);
@@ -1664,6 +1686,68 @@ hipError_t launch_mx(const void *x, int dtype, int64_t rows, int64_t cols, int f
     }
     if (dtype == kBF16) return launch_mx_t<kE5M2, kBF16>(x, rows, cols, q_row, s_row, q_col, s_col, s);
     return launch_mx_t<kE5M2, kF32>(x, rows, cols, q_row, s_row, q_col, s_col, s);
+}
+
+// One pass of a block recipe with the row codes in F and the column codes in
+// FC; either copy may be absent (its code and scale pointers null).
+template <int F, int FC, int DT, int kMode>
+static hipError_t launch_subq_m(const void *x, int64_t rows, int64_t cols, uint8_t *q_row, void *s_row,
+                                uint8_t *q_col, void *s_col, hipStream_t s)
+{
+    const int grid = kMode == kTileMX ? tile_grid(rows, cols) : min(tile_grid(rows, cols), kBlockQuantGrid);
+    const ScaleSrc none{nullptr, nullptr, 0};
+    tile_kernel<F, DT, kMode, false, FC><<<grid, kThreads, 0, s>>>(x, rows, cols, none, q_row, q_col, s_row, s_col,
+                                                                  nullptr, nullptr, nullptr, none, nullptr, Finish{});
+    return hipGetLastError();
+}
+
+template <int F, int FC, int DT>
+static hipError_t launch_subq_r(int recipe, const void *x, int64_t rows, int64_t cols, uint8_t *q_row, void *s_row,
+                                uint8_t *q_col, void *s_col, hipStream_t s)
+{
+    switch (recipe) {
+    case kSubqBlock128: return launch_subq_m<F, FC, DT, kTileBlock128>(x, rows, cols, q_row, s_row, q_col, s_col, s);
+    case kSubqBlock1x128: return launch_subq_m<F, FC, DT, kTileBlock1x128>(x, rows, cols, q_row, s_row, q_col, s_col, s);
+    case kSubqMX: return launch_subq_m<F, FC, DT, kTileMX>(x, rows, cols, q_row, s_row, q_col, s_col, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int F, int FC>
+static hipError_t launch_subq_d(int dtype, int recipe, const void *x, int64_t rows, int64_t cols, uint8_t *q_row,
+                                void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
+{
+    if (dtype == kBF16) return launch_subq_r<F, FC, kBF16>(recipe, x, rows, cols, q_row, s_row, q_col, s_col, s);
+    return launch_subq_r<F, FC, kF32>(recipe, x, rows, cols, q_row, s_row, q_col, s_col, s);
+}
+
+static hipError_t launch_subq(int dtype, int recipe, int row_fmt, int col_fmt, const void *x, int64_t rows,
+                              int64_t cols, uint8_t *q_row, void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
+{
+#define FP8Q_ARGS dtype, recipe, x, rows, cols, q_row, s_row, q_col, s_col, s
+    if (row_fmt == kE4M3)
+        return col_fmt == kE4M3 ? launch_subq_d<kE4M3, kE4M3>(FP8Q_ARGS) : launch_subq_d<kE4M3, kE5M2>(FP8Q_ARGS);
+    return col_fmt == kE4M3 ? launch_subq_d<kE5M2, kE4M3>(FP8Q_ARGS) : launch_subq_d<kE5M2, kE5M2>(FP8Q_ARGS);
+#undef FP8Q_ARGS
+}
+
+hipError_t launch_hybrid_blockwise(const void *x, int dtype, int64_t rows, int64_t cols, int row_recipe, int row_fmt,
+                                   uint8_t *q_row, void *s_row, int col_recipe, int col_fmt, uint8_t *q_col,
+                                   void *s_col, hipStream_t s)
+{
+    if (rows == 0 || cols == 0) return hipSuccess;
+    // one recipe in both directions: one pass over x, each copy in its own
+    // format; otherwise each direction is a pass of its own recipe
+    if (q_row && q_col && row_recipe == col_recipe)
+        return launch_subq(dtype, row_recipe, row_fmt, col_fmt, x, rows, cols, q_row, s_row, q_col, s_col, s);
+    if (q_row) {
+        const hipError_t e = launch_subq(dtype, row_recipe, row_fmt, row_fmt, x, rows, cols, q_row, s_row, nullptr,
+                                         nullptr, s);
+        if (e != hipSuccess) return e;
+    }
+    if (q_col)
+        return launch_subq(dtype, col_recipe, col_fmt, col_fmt, x, rows, cols, nullptr, nullptr, q_col, s_col, s);
+    return hipSuccess;
 }
 
 hipError_t launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int block_rows, uint8_t *q_row,

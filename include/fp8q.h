@@ -91,6 +91,12 @@ extern "C" {
 #define FP8Q_COLSRC_ORIGINAL 0
 #define FP8Q_COLSRC_ROWWISE_DEQUANTIZED 1
 
+/* block sub-quantizers of one direction in fp8_quantize_hybrid_blockwise,
+ * [HYBRID] (the per-direction quantizer may be a blockwise or MXFP8 one) */
+#define FP8Q_SUBQ_BLOCK_128x128 0 /* fp32 scale per 128x128 block, as fp8_quantize_block(block_rows 128) */
+#define FP8Q_SUBQ_BLOCK_1x128 1   /* fp32 scale per 1x128 segment, as fp8_quantize_block(block_rows 1) */
+#define FP8Q_SUBQ_MXFP8 2         /* E8M0 byte per 1x32 segment, as fp8_quantize_mx */
+
 /* epilogue activations, [MFP8] section 6 */
 #define FP8Q_ACT_NONE 0
 #define FP8Q_ACT_RELU 1
@@ -350,6 +356,32 @@ int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, int64_t cols
                         int32_t col_source, const float *amax_in, int32_t row_margin, int32_t col_margin,
                         const float *row_scale_inv_in, const float *col_scale_inv_in, uint8_t *q_row, uint8_t *q_col,
                         float *row_scale_inv_out, float *col_scale_inv_out, float *amax_out, void *stream);
+
+/*
+ * fp8_quantize_hybrid_blockwise -- per-direction ("hybrid") quantization with
+ * block sub-quantizers ([HYBRID]: each direction has a quantizer of its own,
+ * with its own format and recipe, blockwise and MXFP8 ones included; here
+ * both copies come from the original input).
+ *   x [rows][cols] of dtype; rows, cols multiples of 128.
+ *   Rowwise copy: row_recipe in row_fmt applied to x, exactly what
+ *     fp8_quantize_block / fp8_quantize_mx write as q_row and s_row:
+ *     q_row [rows][cols]; s_row float [rows/128][cols/128] (128x128),
+ *     float [rows][cols/128] (1x128) or E8M0 bytes [rows][cols/32] (MXFP8).
+ *   Columnwise copy: col_recipe in col_fmt applied to x^T, what those calls
+ *     write as q_col and s_col: q_col [cols][rows]; s_col float
+ *     [cols/128][rows/128], float [cols][rows/128] or bytes [cols][rows/32].
+ *   Either copy may be skipped (its code and scale pointers both NULL), not
+ *   both.  With one recipe in both directions the call is one pass over x
+ *   (both formats from the same block maxima); with two recipes it is one
+ *   pass per direction.  Scale pointers are void *: float or byte buffers as
+ *   above, 4-byte aligned; code buffers 16-byte aligned.
+ * Errors: FP8Q_EINVAL for unknown enums, a code pointer without its scale
+ * pointer (or the reverse), no copy at all, misalignment or overlapping
+ * buffers; FP8Q_EUNSUPPORTED for shapes that are not multiples of 128.
+ */
+int fp8_quantize_hybrid_blockwise(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t row_recipe,
+                                  int32_t row_fmt, uint8_t *q_row, void *s_row, int32_t col_recipe, int32_t col_fmt,
+                                  uint8_t *q_col, void *s_col, void *stream);
 
 /*
  * fp8_cast_stats -- diagnostics of the per-tensor cast of x with dequant

@@ -53,6 +53,9 @@ def test_enum_values_match_header():
     assert int(defs["FP8Q_COLSRC_ORIGINAL"]) == fq.COLSRC_ORIGINAL == oracle.COLSRC_ORIGINAL
     assert int(defs["FP8Q_COLSRC_ROWWISE_DEQUANTIZED"]) == fq.COLSRC_ROWWISE_DEQUANTIZED \
         == oracle.COLSRC_ROWWISE_DEQUANTIZED
+    assert int(defs["FP8Q_SUBQ_BLOCK_128x128"]) == fq.SUBQ_BLOCK_128x128 == oracle.SUBQ_BLOCK_128x128
+    assert int(defs["FP8Q_SUBQ_BLOCK_1x128"]) == fq.SUBQ_BLOCK_1x128 == oracle.SUBQ_BLOCK_1x128
+    assert int(defs["FP8Q_SUBQ_MXFP8"]) == fq.SUBQ_MXFP8 == oracle.SUBQ_MXFP8
 
 
 def _expect(status, code, fragment):
@@ -221,6 +224,35 @@ def test_hybrid_validation():
     _expect(call(ao=QC + 0x40), fq.EINVAL, "overlaps x or the codes")
 
 
+def test_hybrid_blockwise_validation():
+    h = L.fp8_quantize_hybrid_blockwise
+    X, QR, SR, QC, SC = BAD, BAD + 0x100000, BAD + 0x200000, BAD + 0x300000, BAD + 0x400000
+
+    def call(dtype=fq.BF16, rows=256, cols=384, rr=fq.SUBQ_MXFP8, rf=0, cr=fq.SUBQ_BLOCK_1x128, cf=1, x=X, qr=QR,
+             sr=SR, qc=QC, sc=SC):
+        return h(x, dtype, rows, cols, rr, rf, qr, sr, cr, cf, qc, sc, S)
+
+    _expect(call(dtype=5), fq.EINVAL, "dtype")
+    _expect(call(rf=2), fq.EINVAL, "format")
+    _expect(call(cf=-1), fq.EINVAL, "format")
+    _expect(call(rr=3), fq.EINVAL, "sub-quantizer")
+    _expect(call(cr=-1), fq.EINVAL, "sub-quantizer")
+    _expect(call(rows=-128), fq.EINVAL, "negative")
+    _expect(call(cols=200), fq.EUNSUPPORTED, "multiples of 128")
+    _expect(call(sr=None), fq.EINVAL, "q_row and s_row")
+    _expect(call(qc=None), fq.EINVAL, "q_col and s_col")
+    _expect(call(qr=None, sr=None, qc=None, sc=None), fq.EINVAL, "at least one")
+    _expect(call(x=None), fq.EINVAL, "x must be")
+    _expect(call(qr=QR + 8), fq.EINVAL, "16-byte aligned")
+    _expect(call(sc=SC + 2), fq.EINVAL, "4-byte aligned")
+    _expect(call(qc=QR + 0x100), fq.EINVAL, "overlap")
+    # the row scales of 256x384 MXFP8 are 256 * 12 bytes: a column scale
+    # buffer starting inside them overlaps, one just past them does not
+    _expect(call(sc=SR + 256 * 12 - 4), fq.EINVAL, "overlap")
+    _expect(call(sr=X + 256 * 384 * 2 - 4), fq.EINVAL, "overlap")
+    assert call(rows=0) == fq.OK and call(cols=0, qr=None, sr=None) == fq.OK
+
+
 def test_stats_and_error_feedback_validation():
     st = L.fp8_cast_stats
     _expect(st(BAD, 3, 64, 0, BAD + 0x1000, BAD + 0x2000, S), fq.EINVAL, "dtype")
@@ -318,6 +350,10 @@ def test_valid_calls_without_a_device_return_ehip():
         ("fp8_dequantize", lambda: L.fp8_dequantize(BAD, 0, 64, BAD + 0x800, BAD + 0x1000, S)),
         ("fp8_quantize_block", lambda: L.fp8_quantize_block(BAD, fq.BF16, 128, 128, 0, 128, BAD + 0x100000,
                                                             BAD + 0x200000, None, None, S)),
+        ("fp8_quantize_hybrid_blockwise",
+         lambda: L.fp8_quantize_hybrid_blockwise(BAD, fq.BF16, 128, 128, fq.SUBQ_MXFP8, 0, BAD + 0x100000,
+                                                 BAD + 0x200000, fq.SUBQ_BLOCK_128x128, 1, BAD + 0x300000,
+                                                 BAD + 0x400000, S)),
         ("fp8_update_scale_delayed", lambda: L.fp8_update_scale_delayed(BAD, 16, 1, 0, BAD + 0x100, 0, 0, 0, 0,
                                                                         BAD + 0x200, BAD + 0x300, S)),
         ("fp8_scaled_gemm", lambda: L.fp8_scaled_gemm(BAD + 0x100000, 0, BAD, BAD + 0x200000, 0, BAD + 4, 128, 128,

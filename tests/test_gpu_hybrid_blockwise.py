@@ -1,0 +1,143 @@
+"""GPU parity of the per-direction quantization with block sub-quantizers
+(fp8_quantize_hybrid_blockwise; "[Pytorch][Common] Hybrid quantization #2817":
+each direction has its own quantizer, format and recipe, blockwise and MXFP8
+ones included) against the oracle, bit for bit: codes, FP32 block scales and
+E8M0 scale bytes are all decided in binary32 or integer arithmetic on both
+sides.  Covers every pair of recipes with both format orders, bf16 and fp32
+inputs with planted specials, one direction alone, agreement with the
+single-format entry points, and the full-size block and MXFP8 workloads."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import first_mismatches, host, same_f32, to_dev
+
+pytestmark = pytest.mark.gpu
+
+fq = pytest.importorskip("fp8_scaled_quantization_reduce_amd")
+E4, E5 = oracle.E4M3FN, oracle.E5M2
+B128, B1x128, MX = oracle.SUBQ_BLOCK_128x128, oracle.SUBQ_BLOCK_1x128, oracle.SUBQ_MXFP8
+NAMES = {B128: "128x128", B1x128: "1x128", MX: "mxfp8"}
+
+
+def _scale_buf(recipe, rows, cols):
+    """Sentinel-filled scale buffer of one direction's copy ([rows][cols])."""
+    if recipe == MX:
+        return torch.full((rows, cols // 32), 0xA5, dtype=torch.uint8, device="cuda")
+    n = (rows // 128) * (cols // 128) if recipe == B128 else rows * (cols // 128)
+    return torch.full((n,), -7.25, dtype=torch.float32, device="cuda")
+
+
+def _gpu(x, row_recipe, row_fmt, col_recipe, col_fmt, want_row=True, want_col=True):
+    rows, cols = x.shape
+    q_row = s_row = q_col = s_col = None
+    if want_row:
+        q_row = torch.full((rows, cols), 0xA5, dtype=torch.uint8, device="cuda")
+        s_row = _scale_buf(row_recipe, rows, cols)
+    if want_col:
+        q_col = torch.full((cols, rows), 0xA5, dtype=torch.uint8, device="cuda")
+        s_col = _scale_buf(col_recipe, cols, rows)
+    fq.fp8_quantize_hybrid_blockwise(to_dev(x), row_recipe, row_fmt, col_recipe, col_fmt, q_row=q_row, s_row=s_row,
+                                     q_col=q_col, s_col=s_col)
+    return {k: None if v is None else host(v) for k, v in
+            dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col).items()}
+
+
+def _same_scales(got, want):
+    if want.dtype == np.uint8:
+        return np.array_equal(got.reshape(want.shape), want)
+    return same_f32(got.reshape(want.shape), want)
+
+
+def _check(got, want, which=("row", "col")):
+    for d in which:
+        q, s = got["q_" + d], got["s_" + d]
+        assert _same_scales(s, want["s_" + d]), (d, "scales")
+        assert np.array_equal(q, want["q_" + d]), (d, first_mismatches(q, want["q_" + d]))
+
+
+def _input(dtype, rows, cols, seed, specials=True):
+    # normal values times a magnitude drawn per 32x32 patch, so neighbouring
+    # blocks of every recipe get different scales
+    rng = np.random.default_rng(seed)
+    mag = np.exp(np.kron(rng.uniform(-4, 4, (rows // 32, cols // 32)), np.ones((32, 32))))
+    x64 = rng.standard_normal((rows, cols)) * mag
+    x = workloads.to_bf16_bits(x64) if dtype == "bf16" else x64.astype(np.float32)
+    if specials:
+        flat = x.reshape(-1)
+        if x.dtype == np.uint16:
+            vals = [0x7F80, 0xFF80, 0x7FC0, 0x0000, 0x8000, 0x7F7F, 0x0001]
+        else:
+            vals = np.float32([np.inf, -np.inf, np.nan, 0.0, -0.0, 3e38, 1e-40])
+        idx = np.linspace(11, flat.size - 5, len(vals)).astype(np.int64)
+        flat[idx] = vals
+        x[:128, 128:256] = 0  # an all-zero 128x128 block (and zero 1x128 / 1x32 segments)
+    return x
+
+
+@pytest.mark.parametrize("row_recipe", [B128, B1x128, MX], ids=lambda r: "row_" + NAMES[r])
+@pytest.mark.parametrize("col_recipe", [B128, B1x128, MX], ids=lambda r: "col_" + NAMES[r])
+@pytest.mark.parametrize("fmts", [(E4, E5), (E5, E4)], ids=["e4m3_e5m2", "e5m2_e4m3"])
+def test_every_recipe_pair_bf16(row_recipe, col_recipe, fmts):
+    x = _input("bf16", 384, 512, seed=301)
+    got = _gpu(x, row_recipe, fmts[0], col_recipe, fmts[1])
+    _check(got, oracle.quantize_hybrid_blockwise(x, row_recipe, fmts[0], col_recipe, fmts[1]))
+
+
+@pytest.mark.parametrize("recipe", [B128, B1x128, MX], ids=lambda r: NAMES[r])
+@pytest.mark.parametrize("fmts", [(E4, E5), (E5, E4), (E5, E5)], ids=["e4m3_e5m2", "e5m2_e4m3", "e5m2_e5m2"])
+def test_one_recipe_fp32(recipe, fmts):
+    x = _input("f32", 256, 640, seed=302)
+    got = _gpu(x, recipe, fmts[0], recipe, fmts[1])
+    _check(got, oracle.quantize_hybrid_blockwise(x, recipe, fmts[0], recipe, fmts[1]))
+
+
+@pytest.mark.parametrize("recipe", [B128, B1x128, MX], ids=lambda r: NAMES[r])
+def test_one_direction_alone(recipe):
+    """Only the rowwise or only the columnwise copy: the other copy's buffers
+    are not touched (they are not passed) and the given one matches."""
+    x = _input("bf16", 256, 384, seed=303)
+    want = oracle.quantize_hybrid_blockwise(x, recipe, E5, MX if recipe != MX else B128, E4)
+    got = _gpu(x, recipe, E5, MX if recipe != MX else B128, E4, want_col=False)
+    assert got["q_col"] is None
+    _check(got, want, ("row",))
+    got = _gpu(x, recipe, E5, MX if recipe != MX else B128, E4, want_row=False)
+    assert got["q_row"] is None
+    _check(got, want, ("col",))
+
+
+@pytest.mark.parametrize("recipe", [B128, B1x128, MX], ids=lambda r: NAMES[r])
+def test_one_format_equals_single_recipe_entry_point(recipe):
+    """With one format both ways the call writes exactly what
+    fp8_quantize_block / fp8_quantize_mx write."""
+    x = _input("bf16", 384, 256, seed=304)
+    xd = to_dev(x)
+    got = _gpu(x, recipe, E4, recipe, E4)
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    qc = torch.empty((cols, rows), dtype=torch.uint8, device="cuda")
+    s, sc = _scale_buf(recipe, rows, cols), _scale_buf(recipe, cols, rows)
+    if recipe == MX:
+        fq.fp8_quantize_mx(xd, E4, q, s, qc, sc)
+    else:
+        fq.fp8_quantize_block(xd, E4, 128 if recipe == B128 else 1, q, s, qc, sc)
+    for a, b in ((got["q_row"], host(q)), (got["q_col"], host(qc))):
+        assert np.array_equal(a, b)
+    for a, b in ((got["s_row"], host(s)), (got["s_col"], host(sc))):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("recipe,shape,make", [
+    (B128, (7168, 4096), lambda: workloads.block_weight()),
+    (B1x128, (4096, 7168), lambda: workloads.block_act()),
+    (MX, (8192, 8192), lambda: workloads.delayed_step(0)),
+], ids=["128x128_weight_7168x4096", "1x128_act_4096x7168", "mxfp8_8192x8192"])
+def test_full_size_e4m3_rows_e5m2_cols(recipe, shape, make):
+    """The block and MXFP8 workloads at their full size, E4M3 forward copy and
+    E5M2 backward copy in one pass, every code and scale compared."""
+    x = make()
+    assert x.shape == shape
+    got = _gpu(x, recipe, E4, recipe, E5)
+    _check(got, oracle.quantize_hybrid_blockwise(x, recipe, E4, recipe, E5))
