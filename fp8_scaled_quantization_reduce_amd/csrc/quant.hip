@@ -1147,7 +1147,7 @@ __device__ __forceinline__ void store_transposed(const uint32_t *tl, uint8_t *q_
 // One block loops over tiles t = blockIdx.x, blockIdx.x + G, ... (tile row
 // t / tiles_per_row, tile column t % tiles_per_row), G the number of tile
 // blocks (with kAmax the launch has one more, its finishing block).
-template <int F, int DT, int kMode, bool kAmax, int FCol = F>
+template <int F, int DT, int kMode, bool kAmax, int FCol = F, int kColMode = kMode>
 __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__ x, int64_t rows, int64_t cols,
                                                         ScaleSrc src, uint8_t *__restrict__ q_row,
                                                         uint8_t *__restrict__ q_col, void *__restrict__ s_row_p,
@@ -1164,6 +1164,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
     constexpr bool kHybrid = kMode >= kTileHybrid;
     constexpr int FC = kHybrid ? ((kMode - kTileHybrid) & 1) : FCol; // format of the column codes
     constexpr bool kDeq = kHybrid && ((kMode - kTileHybrid) >> 1); // columns from the dequantized rows
+    // the block recipe of the column codes (kColMode) may differ from that
+    // of the row codes (kMode): each direction's scales come from its own
+    // block maxima
+    constexpr bool kRow128 = kMode == kTileBlock128;
+    constexpr bool kCol128 = kColMode == kTileBlock128, kCol1x = kColMode == kTileBlock1x128,
+                   kColMX = kColMode == kTileMX;
     // block scales: fp32 (128x128, 1x128) or E8M0 bytes (MXFP8)
     float *__restrict__ s_row = reinterpret_cast<float *>(s_row_p);
     float *__restrict__ s_col = reinterpret_cast<float *>(s_col_p);
@@ -1171,9 +1177,9 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
     uint8_t *__restrict__ e_col = reinterpret_cast<uint8_t *>(s_col_p);
     __shared__ uint32_t tl[kTile * 32]; // transposed codes, 16 KiB
     __shared__ uint32_t red[kThreads / 64];
-    __shared__ uint32_t colmax[kMode == kTileBlock1x128 ? 4 * kTile : 1]; // per wave, per tile column
-    __shared__ float colscale[kMode == kTileBlock1x128 ? kTile : 1];
-    __shared__ uint32_t ecol[kMode == kTileMX ? kTile : 1]; // MXFP8: a tile column's 4 scale bytes
+    __shared__ uint32_t colmax[kCol1x ? 4 * kTile : 1]; // per wave, per tile column
+    __shared__ float colscale[kCol1x ? kTile : 1];
+    __shared__ uint32_t ecol[kColMX ? kTile : 1]; // MXFP8: a tile column's 4 scale bytes
     __shared__ uint32_t colbad; // 1x128: some column scale of the tile is NaN, infinite or zero
 
     const int ig = threadIdx.x >> 3, jg = threadIdx.x & 7;
@@ -1211,7 +1217,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
     // plain accesses; streamed loads alone made the per-tensor cast 13%
     // slower, and streamed row stores slowed every mode.
     constexpr bool kNTLoad = kMode == kTilePerTensor;
-    constexpr bool kNTColStore = kMode == kTilePerTensor || kMode == kTileBlock128 || kMode == kTileBlock1x128;
+    constexpr bool kNTColStore = kColMode == kTilePerTensor || kCol128 || kCol1x;
 
     // The lane's patch of tile t (rows % 4 == 0 and cols % 16 == 0, so a patch
     // is either whole or entirely outside the matrix).
@@ -1264,11 +1270,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
             m = block_max_u32<kThreads>(m, red);
             const float amax_b = __uint_as_float(canonical_amax_bits(m));
             const Scales sc = current_scales(amax_b, Fmt<F>::kMax, 0);
-            // columns in a format of their own: the same block amax, that format's scale
-            if constexpr (FC != F) sc_col = current_scales(amax_b, Fmt<FC>::kMax, 0);
+            // 128x128 columns in a format of their own: the same block amax,
+            // that format's scale (other column recipes set their scales below)
+            if constexpr (kCol128 && FC != F) sc_col = current_scales(amax_b, Fmt<FC>::kMax, 0);
             if (threadIdx.x == 0) {
                 if (q_row) s_row[tr * bcols + tc] = sc.s;
-                if (s_col) s_col[tc * brows + tr] = FC != F ? sc_col.s : sc.s;
+                if (kCol128 && s_col) s_col[tc * brows + tr] = FC != F ? sc_col.s : sc.s;
             }
             // the block scale is uniform: finite and nonzero exactly when the
             // block holds no NaN or infinity
@@ -1315,6 +1322,47 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) =
                         make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
             }
+        } else { // 1x128 blocks: one scale per row segment, one per column segment
+            // row segments: the 8 lanes jg = 0..7 of a row group hold the row's 128 columns
+            uint32_t rm[4];
+            patch_row_max<DT>(p, rm);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint32_t m = rm[r];
+                m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false)); // lane ^ 1
+                m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false)); // lane ^ 2
+                // lane 7 - i of the 8 (DPP row_half_mirror): the other quad
+                m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
+                const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
+                if (jg == 0 && q_row) s_row[(r0 + r) * bcols + tc] = sc.s;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    cw[r][q4] = encode4<F, false>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
+                                                  PV(r, 4 * q4 + 3), sc.scale);
+                if (!finite_nonzero(sc.scale)) {
+                    opaque(p);
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        cw[r][q4] = encode4<F, true>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
+                                                     PV(r, 4 * q4 + 3), sc.scale);
+                }
+                // stored now: the rowwise codes need not stay live through the column phase
+                if (q_row && valid)
+                    *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) =
+                        make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
+            }
+            opaque(p);
+        }
+
+        if (kMode != kTileBlock1x128 && kMode != kTileMX && q_row && valid) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) =
+                    make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
+        }
+
+        // column scales of the block recipes (and, for MXFP8, the column codes)
+        if constexpr (kColMX) {
             if (q_col) {
                 opaque(p);
                 uint32_t cmax[16];
@@ -1358,36 +1406,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 }
                 stage_transposed(tl, cc, ig, jg);
             }
-        } else { // 1x128 blocks: one scale per row segment, one per column segment
-            // row segments: the 8 lanes jg = 0..7 of a row group hold the row's 128 columns
-            uint32_t rm[4];
-            patch_row_max<DT>(p, rm);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint32_t m = rm[r];
-                m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false)); // lane ^ 1
-                m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false)); // lane ^ 2
-                // lane 7 - i of the 8 (DPP row_half_mirror): the other quad
-                m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
-                const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
-                if (jg == 0 && q_row) s_row[(r0 + r) * bcols + tc] = sc.s;
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    cw[r][q4] = encode4<F, false>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
-                                                  PV(r, 4 * q4 + 3), sc.scale);
-                if (!finite_nonzero(sc.scale)) {
-                    opaque(p);
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        cw[r][q4] = encode4<F, true>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
-                                                     PV(r, 4 * q4 + 3), sc.scale);
-                }
-                // stored now: the rowwise codes need not stay live through the column phase
-                if (q_row && valid)
-                    *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) =
-                        make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
-            }
-            opaque(p);
+        } else if constexpr (kCol1x) {
             // column segments: a column's 128 rows are 4 rows in each of 32
             // lanes; the 8 of them in one wave (lane bits 3..5) are reduced
             // with cross-lane moves, the 4 waves through LDS
@@ -1421,16 +1440,17 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 }
                 __syncthreads();
             }
-        }
-
-        if (kMode != kTileBlock1x128 && kMode != kTileMX && q_row && valid) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) =
-                    make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
+        } else if constexpr (kCol128 && !kRow128) {
+            if (q_col) {
+                uint32_t rm[4];
+                patch_row_max<DT>(p, rm);
+                const uint32_t m = block_max_u32<kThreads>(max(max(rm[0], rm[1]), max(rm[2], rm[3])), red);
+                sc_col = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<FC>::kMax, 0);
+                if (threadIdx.x == 0) s_col[tc * brows + tr] = sc_col.s;
+            }
         }
         if (q_col) {
-            if constexpr (kMode == kTileBlock1x128) {
+            if constexpr (kCol1x) {
                 // columnwise codes use the column-segment scales
                 opaque(p);
                 uint32_t cc[4][4];
@@ -1504,8 +1524,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     enc_cols(Rep<true>{});
                 }
                 stage_transposed(tl, cc, ig, jg);
-            } else if constexpr (kMode == kTileBlock128 && FC != F) {
-                // the block's column codes in their own format, from x
+            } else if constexpr (kCol128 && (FC != F || !kRow128)) {
+                // the block's column codes in their own format or recipe, from x
                 opaque(p);
                 uint32_t cc[4][4];
                 auto enc_cols = [&](auto rep) {
@@ -1523,12 +1543,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     enc_cols(Rep<true>{});
                 }
                 stage_transposed(tl, cc, ig, jg);
-            } else if constexpr (kMode != kTileMX) { // (MXFP8 staged its own column codes above)
+            } else if constexpr (!kColMX) { // (MXFP8 staged its own column codes above)
                 stage_transposed(tl, cw, ig, jg);
             }
             __syncthreads();
             store_transposed<kNTColStore>(tl, q_col, rows, cols, row0, col0);
-            if constexpr (kMode == kTileMX) {
+            if constexpr (kColMX) {
                 const int64_t xcol = rows / 32;
                 if (threadIdx.x < kTile && col0 + threadIdx.x < cols)
                     *reinterpret_cast<uint32_t *>(e_col + (col0 + threadIdx.x) * xcol + (row0 >> 5)) =
@@ -1688,46 +1708,57 @@ hipError_t launch_mx(const void *x, int dtype, int64_t rows, int64_t cols, int f
     return launch_mx_t<kE5M2, kF32>(x, rows, cols, q_row, s_row, q_col, s_col, s);
 }
 
-// One pass of a block recipe with the row codes in F and the column codes in
-// FC; either copy may be absent (its code and scale pointers null).
-template <int F, int FC, int DT, int kMode>
+// One pass over x: the row codes by the block recipe kMode in F, the column
+// codes by the block recipe kColMode in FC; either copy may be absent (its
+// code and scale pointers null).  A pass with MXFP8 codes runs one tile per
+// block, the block-scaled ones loop over tiles (the measured faster forms).
+template <int F, int FC, int DT, int kMode, int kColMode>
 static hipError_t launch_subq_m(const void *x, int64_t rows, int64_t cols, uint8_t *q_row, void *s_row,
                                 uint8_t *q_col, void *s_col, hipStream_t s)
 {
-    const int grid = kMode == kTileMX ? tile_grid(rows, cols) : min(tile_grid(rows, cols), kBlockQuantGrid);
+    const int grid = (kMode == kTileMX || kColMode == kTileMX) ? tile_grid(rows, cols)
+                                                               : min(tile_grid(rows, cols), kBlockQuantGrid);
     const ScaleSrc none{nullptr, nullptr, 0};
-    tile_kernel<F, DT, kMode, false, FC><<<grid, kThreads, 0, s>>>(x, rows, cols, none, q_row, q_col, s_row, s_col,
-                                                                  nullptr, nullptr, nullptr, none, nullptr, Finish{});
+    tile_kernel<F, DT, kMode, false, FC, kColMode><<<grid, kThreads, 0, s>>>(
+        x, rows, cols, none, q_row, q_col, s_row, s_col, nullptr, nullptr, nullptr, none, nullptr, Finish{});
     return hipGetLastError();
 }
 
-template <int F, int FC, int DT>
-static hipError_t launch_subq_r(int recipe, const void *x, int64_t rows, int64_t cols, uint8_t *q_row, void *s_row,
-                                uint8_t *q_col, void *s_col, hipStream_t s)
+template <int F, int FC, int DT, int kMode>
+static hipError_t launch_subq_c(int col_recipe, const void *x, int64_t rows, int64_t cols, uint8_t *q_row,
+                                void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
 {
-    switch (recipe) {
-    case kSubqBlock128: return launch_subq_m<F, FC, DT, kTileBlock128>(x, rows, cols, q_row, s_row, q_col, s_col, s);
-    case kSubqBlock1x128: return launch_subq_m<F, FC, DT, kTileBlock1x128>(x, rows, cols, q_row, s_row, q_col, s_col, s);
-    case kSubqMX: return launch_subq_m<F, FC, DT, kTileMX>(x, rows, cols, q_row, s_row, q_col, s_col, s);
+    switch (col_recipe) {
+    case kSubqBlock128:
+        return launch_subq_m<F, FC, DT, kMode, kTileBlock128>(x, rows, cols, q_row, s_row, q_col, s_col, s);
+    case kSubqBlock1x128:
+        return launch_subq_m<F, FC, DT, kMode, kTileBlock1x128>(x, rows, cols, q_row, s_row, q_col, s_col, s);
+    case kSubqMX: return launch_subq_m<F, FC, DT, kMode, kTileMX>(x, rows, cols, q_row, s_row, q_col, s_col, s);
     }
     return hipErrorInvalidValue;
 }
 
-template <int F, int FC>
-static hipError_t launch_subq_d(int dtype, int recipe, const void *x, int64_t rows, int64_t cols, uint8_t *q_row,
-                                void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
+template <int F, int FC, int DT>
+static hipError_t launch_subq_r(int row_recipe, int col_recipe, const void *x, int64_t rows, int64_t cols,
+                                uint8_t *q_row, void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
 {
-    if (dtype == kBF16) return launch_subq_r<F, FC, kBF16>(recipe, x, rows, cols, q_row, s_row, q_col, s_col, s);
-    return launch_subq_r<F, FC, kF32>(recipe, x, rows, cols, q_row, s_row, q_col, s_col, s);
+#define FP8Q_ARGS col_recipe, x, rows, cols, q_row, s_row, q_col, s_col, s
+    switch (row_recipe) {
+    case kSubqBlock128: return launch_subq_c<F, FC, DT, kTileBlock128>(FP8Q_ARGS);
+    case kSubqBlock1x128: return launch_subq_c<F, FC, DT, kTileBlock1x128>(FP8Q_ARGS);
+    case kSubqMX: return launch_subq_c<F, FC, DT, kTileMX>(FP8Q_ARGS);
+    }
+#undef FP8Q_ARGS
+    return hipErrorInvalidValue;
 }
 
-static hipError_t launch_subq(int dtype, int recipe, int row_fmt, int col_fmt, const void *x, int64_t rows,
-                              int64_t cols, uint8_t *q_row, void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
+template <int F, int FC>
+static hipError_t launch_subq_d(int dtype, int row_recipe, int col_recipe, const void *x, int64_t rows, int64_t cols,
+                                uint8_t *q_row, void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
 {
-#define FP8Q_ARGS dtype, recipe, x, rows, cols, q_row, s_row, q_col, s_col, s
-    if (row_fmt == kE4M3)
-        return col_fmt == kE4M3 ? launch_subq_d<kE4M3, kE4M3>(FP8Q_ARGS) : launch_subq_d<kE4M3, kE5M2>(FP8Q_ARGS);
-    return col_fmt == kE4M3 ? launch_subq_d<kE5M2, kE4M3>(FP8Q_ARGS) : launch_subq_d<kE5M2, kE5M2>(FP8Q_ARGS);
+#define FP8Q_ARGS row_recipe, col_recipe, x, rows, cols, q_row, s_row, q_col, s_col, s
+    if (dtype == kBF16) return launch_subq_r<F, FC, kBF16>(FP8Q_ARGS);
+    return launch_subq_r<F, FC, kF32>(FP8Q_ARGS);
 #undef FP8Q_ARGS
 }
 
@@ -1736,18 +1767,14 @@ hipError_t launch_hybrid_blockwise(const void *x, int dtype, int64_t rows, int64
                                    void *s_col, hipStream_t s)
 {
     if (rows == 0 || cols == 0) return hipSuccess;
-    // one recipe in both directions: one pass over x, each copy in its own
-    // format; otherwise each direction is a pass of its own recipe
-    if (q_row && q_col && row_recipe == col_recipe)
-        return launch_subq(dtype, row_recipe, row_fmt, col_fmt, x, rows, cols, q_row, s_row, q_col, s_col, s);
-    if (q_row) {
-        const hipError_t e = launch_subq(dtype, row_recipe, row_fmt, row_fmt, x, rows, cols, q_row, s_row, nullptr,
-                                         nullptr, s);
-        if (e != hipSuccess) return e;
-    }
-    if (q_col)
-        return launch_subq(dtype, col_recipe, col_fmt, col_fmt, x, rows, cols, nullptr, nullptr, q_col, s_col, s);
-    return hipSuccess;
+    // one direction alone: the single-format kernel of its recipe
+    if (!q_col) col_recipe = row_recipe, col_fmt = row_fmt;
+    if (!q_row) row_recipe = col_recipe, row_fmt = col_fmt;
+#define FP8Q_ARGS dtype, row_recipe, col_recipe, x, rows, cols, q_row, s_row, q_col, s_col, s
+    if (row_fmt == kE4M3)
+        return col_fmt == kE4M3 ? launch_subq_d<kE4M3, kE4M3>(FP8Q_ARGS) : launch_subq_d<kE4M3, kE5M2>(FP8Q_ARGS);
+    return col_fmt == kE4M3 ? launch_subq_d<kE5M2, kE4M3>(FP8Q_ARGS) : launch_subq_d<kE5M2, kE5M2>(FP8Q_ARGS);
+#undef FP8Q_ARGS
 }
 
 hipError_t launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int block_rows, uint8_t *q_row,

@@ -371,10 +371,10 @@ int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, int64_t cols
  *     write as q_col and s_col: q_col [cols][rows]; s_col float
  *     [cols/128][rows/128], float [cols][rows/128] or bytes [cols][rows/32].
  *   Either copy may be skipped (its code and scale pointers both NULL), not
- *   both.  With one recipe in both directions the call is one pass over x
- *   (both formats from the same block maxima); with two recipes it is one
- *   pass per direction.  Scale pointers are void *: float or byte buffers as
- *   above, 4-byte aligned; code buffers 16-byte aligned.
+ *   both.  The call reads x once, whatever the two recipes and formats (with
+ *   one recipe both ways, both formats take their scales from the same block
+ *   maxima).  Scale pointers are void *: float or byte buffers as above,
+ *   4-byte aligned; code buffers 16-byte aligned.
  * Errors: FP8Q_EINVAL for unknown enums, a code pointer without its scale
  * pointer (or the reverse), no copy at all, misalignment or overlapping
  * buffers; FP8Q_EUNSUPPORTED for shapes that are not multiples of 128.

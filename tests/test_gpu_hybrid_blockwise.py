@@ -3,9 +3,10 @@
 each direction has its own quantizer, format and recipe, blockwise and MXFP8
 ones included) against the oracle, bit for bit: codes, FP32 block scales and
 E8M0 scale bytes are all decided in binary32 or integer arithmetic on both
-sides.  Covers every pair of recipes with both format orders, bf16 and fp32
-inputs with planted specials, one direction alone, agreement with the
-single-format entry points, and the full-size block and MXFP8 workloads."""
+sides.  Covers every pair of recipes (one pass over x for any pair) with both
+format orders, bf16 and fp32 inputs with planted specials, one direction
+alone, agreement with the single-format entry points, and the full-size
+block and MXFP8 workloads."""
 import numpy as np
 import pytest
 import torch
@@ -86,12 +87,13 @@ def test_every_recipe_pair_bf16(row_recipe, col_recipe, fmts):
     _check(got, oracle.quantize_hybrid_blockwise(x, row_recipe, fmts[0], col_recipe, fmts[1]))
 
 
-@pytest.mark.parametrize("recipe", [B128, B1x128, MX], ids=lambda r: NAMES[r])
+@pytest.mark.parametrize("recipes", [(B128, B128), (B1x128, B1x128), (MX, MX), (B128, MX), (MX, B1x128),
+                                     (B1x128, B128)], ids=lambda r: NAMES[r[0]] + "_" + NAMES[r[1]])
 @pytest.mark.parametrize("fmts", [(E4, E5), (E5, E4), (E5, E5)], ids=["e4m3_e5m2", "e5m2_e4m3", "e5m2_e5m2"])
-def test_one_recipe_fp32(recipe, fmts):
+def test_recipe_pairs_fp32(recipes, fmts):
     x = _input("f32", 256, 640, seed=302)
-    got = _gpu(x, recipe, fmts[0], recipe, fmts[1])
-    _check(got, oracle.quantize_hybrid_blockwise(x, recipe, fmts[0], recipe, fmts[1]))
+    got = _gpu(x, recipes[0], fmts[0], recipes[1], fmts[1])
+    _check(got, oracle.quantize_hybrid_blockwise(x, recipes[0], fmts[0], recipes[1], fmts[1]))
 
 
 @pytest.mark.parametrize("recipe", [B128, B1x128, MX], ids=lambda r: NAMES[r])
@@ -129,15 +131,16 @@ def test_one_format_equals_single_recipe_entry_point(recipe):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-@pytest.mark.parametrize("recipe,shape,make", [
-    (B128, (7168, 4096), lambda: workloads.block_weight()),
-    (B1x128, (4096, 7168), lambda: workloads.block_act()),
-    (MX, (8192, 8192), lambda: workloads.delayed_step(0)),
-], ids=["128x128_weight_7168x4096", "1x128_act_4096x7168", "mxfp8_8192x8192"])
-def test_full_size_e4m3_rows_e5m2_cols(recipe, shape, make):
+@pytest.mark.parametrize("recipes,shape,make", [
+    ((B128, B128), (7168, 4096), lambda: workloads.block_weight()),
+    ((B1x128, B1x128), (4096, 7168), lambda: workloads.block_act()),
+    ((MX, MX), (8192, 8192), lambda: workloads.delayed_step(0)),
+    ((B1x128, MX), (8192, 8192), lambda: workloads.delayed_step(1)),
+], ids=["128x128_weight_7168x4096", "1x128_act_4096x7168", "mxfp8_8192x8192", "1x128_rows_mxfp8_cols_8192x8192"])
+def test_full_size_e4m3_rows_e5m2_cols(recipes, shape, make):
     """The block and MXFP8 workloads at their full size, E4M3 forward copy and
     E5M2 backward copy in one pass, every code and scale compared."""
     x = make()
     assert x.shape == shape
-    got = _gpu(x, recipe, E4, recipe, E5)
-    _check(got, oracle.quantize_hybrid_blockwise(x, recipe, E4, recipe, E5))
+    got = _gpu(x, recipes[0], E4, recipes[1], E5)
+    _check(got, oracle.quantize_hybrid_blockwise(x, recipes[0], E4, recipes[1], E5))
