@@ -497,21 +497,53 @@ def _block_subquantizer(src: np.ndarray, recipe: int, fmt: int):
     raise ValueError("unknown sub-quantizer %r" % recipe)
 
 
-def quantize_hybrid_blockwise(x: np.ndarray, row_recipe: int, row_fmt: int, col_recipe: int, col_fmt: int):
+def _row_dequant_scales(recipe: int, s_row: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """float32 [rows][cols]: each element's dequant scale under the row recipe
+    (its block's FP32 scale, or 2^(byte - 127) for MXFP8, NaN for byte 255)."""
+    if recipe == SUBQ_BLOCK_128x128:
+        d = np.repeat(np.repeat(s_row, 128, axis=0), 128, axis=1)
+    elif recipe == SUBQ_BLOCK_1x128:
+        d = np.repeat(s_row, 128, axis=1)
+    else:
+        d = np.repeat(e8m0_value(s_row), 32, axis=1)
+    assert d.shape == (rows, cols)
+    return d.astype(np.float32)
+
+
+def quantize_hybrid_blockwise(x: np.ndarray, row_recipe: int, row_fmt: int, col_recipe: int, col_fmt: int,
+                              col_source: int = 0):
     """Per-direction ("hybrid") quantization with block sub-quantizers
     ("[Pytorch][Common] Hybrid quantization #2817": each direction has a
     quantizer of its own, format and recipe, and blockwise or MXFP8
-    quantizers may fill either role; the columnwise copy is taken from the
-    original input here).
+    quantizers may fill either role; the columnwise copy is quantized from
+    the original input, or from the dequantized rowwise values).
 
     The rowwise copy is the row recipe in row_fmt applied to x; the
-    columnwise copy is the column recipe in col_fmt applied to x^T.  A recipe
-    is 128x128 blocks, 1x128 blocks (both with FP32 block scales, margin 0,
-    like quantize_block) or MXFP8 1x32 blocks with E8M0 scales (quantize_mx).
+    columnwise copy is the column recipe in col_fmt applied to y^T, with
+    y = x (original) or y = x' = fl32(value(q_row) * d) elementwise
+    (rowwise_dequantized), d the element's row-block dequant scale.  Where x'
+    is NaN (a NaN row code, or a zero code times an infinite block scale) it
+    is taken as the NaN carrying the row code's sign bit, so its column code
+    is the NaN code with that sign (the reading of the per-tensor
+    rowwise_dequantized source, extended to block scales).  A recipe is
+    128x128 blocks, 1x128 blocks (both with FP32 block scales, margin 0, like
+    quantize_block) or MXFP8 1x32 blocks with E8M0 scales (quantize_mx).
     Returns dict(q_row [R][C], s_row, q_col [C][R], s_col)."""
     x = np.ascontiguousarray(x)
+    rows, cols = x.shape
     q_row, s_row = _block_subquantizer(x, row_recipe, row_fmt)
-    q_col, s_col = _block_subquantizer(transpose(x), col_recipe, col_fmt)
+    if col_source == COLSRC_ORIGINAL:
+        src = x
+    elif col_source == COLSRC_ROWWISE_DEQUANTIZED:
+        v = decode_codes(q_row, row_fmt).astype(np.float32)  # exact: every code fits binary32
+        with np.errstate(invalid="ignore", over="ignore", under="ignore"):
+            src = v * _row_dequant_scales(row_recipe, s_row, rows, cols)
+        nan = np.isnan(src)
+        bits = src.view(np.uint32)
+        bits[nan] = np.uint32(0x7FC00000) | ((q_row[nan].astype(np.uint32) & 0x80) << 24)
+    else:
+        raise ValueError("unknown columnwise source %r" % col_source)
+    q_col, s_col = _block_subquantizer(transpose(np.ascontiguousarray(src)), col_recipe, col_fmt)
     return dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col)
 
 

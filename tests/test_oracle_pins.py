@@ -790,6 +790,61 @@ def test_hybrid_blockwise_cross_recipe_directions():
                 assert np.any((h["q_col"][j, I * 128:(I + 1) * 128] & 0x7F) == TOP_CODE[E5])
 
 
+def test_hybrid_blockwise_dequantized_128x128_one_format_is_the_transpose():
+    """128x128 blocks, one format, columns from the dequantized rows: a block
+    requantized from its own dequantized values gives back its codes (the FP8
+    grid is far coarser than the binary32 roundings of x' and of the new
+    scale), so q_col is q_row^T and s_col is s_row^T to within one binary32
+    step.  A block holding a NaN keeps its NaN codes; a block holding +inf
+    has scale inf, zero codes for its finite elements and x' = 0 * inf = NaN
+    everywhere, so every column code is the NaN code with the row code's sign."""
+    x = workloads.block_weight(384, 256, seed=26, std=3.0)
+    x[5, 9] = 0x7FC0         # NaN in block (0, 0)
+    x[130, 140] = 0x7F80     # +inf in block (1, 1)
+    x[131, 141] = 0xC000     # -2.0 in the same block
+    h = oracle.quantize_hybrid_blockwise(x, oracle.SUBQ_BLOCK_128x128, E4, oracle.SUBQ_BLOCK_128x128, E4,
+                                         oracle.COLSRC_ROWWISE_DEQUANTIZED)
+    qr, qc = h["q_row"], h["q_col"]
+    for I in range(3):
+        for J in range(2):
+            rs, cs = slice(I * 128, (I + 1) * 128), slice(J * 128, (J + 1) * 128)
+            if (I, J) == (1, 1):
+                assert np.isinf(h["s_row"][I, J]) and np.isnan(h["s_col"][J, I])
+                assert qr[131, 141] == 0x80 and (qr[130, 140] & 0x7F) == 0x7F
+                assert np.array_equal(qc[cs, rs], (qr[rs, cs] | 0x7F).T)
+            elif (I, J) == (0, 0):
+                assert np.isnan(h["s_row"][I, J]) and np.all((qr[rs, cs] & 0x7F) == 0x7F)
+                assert np.array_equal(qc[cs, rs], qr[rs, cs].T)
+            else:
+                assert np.array_equal(qc[cs, rs], qr[rs, cs].T)
+                d = int(f32_bits(h["s_col"][J, I])) - int(f32_bits(h["s_row"][I, J]))
+                assert abs(d) <= 1
+
+
+def test_hybrid_blockwise_dequantized_mx_rows_exact_values():
+    """MXFP8 E4M3 rows, 1x128 E5M2 columns from the dequantized rows: x' is
+    the E4M3 value times the row block's power of two (computed here in
+    float64, exact), and each 128-row segment of a column of x' is a tensor
+    of its own cast to E5M2 (pinned above)."""
+    x = workloads.block_act(256, 256, seed=27)
+    h = oracle.quantize_hybrid_blockwise(x, oracle.SUBQ_MXFP8, E4, oracle.SUBQ_BLOCK_1x128, E5,
+                                         oracle.COLSRC_ROWWISE_DEQUANTIZED)
+    q, sc = oracle.quantize_mx(x, E4)
+    assert np.array_equal(h["q_row"], q) and np.array_equal(h["s_row"], sc)
+    xp = oracle.decode_table(E4)[q] * np.ldexp(1.0, np.repeat(sc.astype(np.int64) - 127, 32, axis=1))
+    xp32 = xp.astype(np.float32)
+    assert np.array_equal(xp32.astype(np.float64), xp)  # every x' fits binary32
+    for j in (0, 31, 128, 255):
+        for I in range(2):
+            seg = np.ascontiguousarray(xp32[I * 128:(I + 1) * 128, j])
+            r = oracle.quantize_tensor(seg, E5, amax_in=oracle.amax(seg))
+            assert h["s_col"][j, I] == r["scale_inv"]
+            assert np.array_equal(h["q_col"][j, I * 128:(I + 1) * 128], r["q"])
+    # the original source gives other codes somewhere (the rows' rounding moved x)
+    o = oracle.quantize_hybrid_blockwise(x, oracle.SUBQ_MXFP8, E4, oracle.SUBQ_BLOCK_1x128, E5)
+    assert not np.array_equal(o["q_col"], h["q_col"])
+
+
 def test_hybrid_rowwise_dequantized_is_idempotent_in_one_format():
     """Quantize, dequantize, quantize again with the same format and scale
     gives the same codes (the FP8 grid is far coarser than one fp32 rounding
