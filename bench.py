@@ -553,6 +553,22 @@ def time_rows(fq, torch, np, workloads, to_dev, xs, stream, only, with_cpu):
         hbm(name, 4 * n + 2 * n // 32, t, cpu(hyb_mx_cpu, (4 * n + 2 * n // 32) / 1e9, "GB/s"))
         del sm, smt
 
+    # next: the same MXFP8 pair with the columnwise copy taken from the
+    # dequantized rowwise values (same bytes)
+    name = "hybrid_mxfp8_e4m3_rows_e5m2_cols_dequantized_bf16_8192x8192"
+    if want(name):
+        sm = [torch.empty((8192, 256), dtype=torch.uint8, device=dev) for _ in range(4)]
+        smt = [torch.empty((8192, 256), dtype=torch.uint8, device=dev) for _ in range(4)]
+        t = timed(lambda i: fq.fp8_quantize_hybrid_blockwise(
+            x2[i], fq.SUBQ_MXFP8, E4, fq.SUBQ_MXFP8, E5, col_source=fq.COLSRC_ROWWISE_DEQUANTIZED, q_row=qr[i % 4],
+            s_row=sm[i % 4], q_col=qc[i % 4], s_col=smt[i % 4], stream=stream), 16, rotate=len(xs))
+
+        def hyb_mxd_cpu():
+            oracle.quantize_hybrid_blockwise(host_x(), oracle.SUBQ_MXFP8, oracle.E4M3FN, oracle.SUBQ_MXFP8,
+                                             oracle.E5M2, oracle.COLSRC_ROWWISE_DEQUANTIZED)
+        hbm(name, 4 * n + 2 * n // 32, t, cpu(hyb_mxd_cpu, (4 * n + 2 * n // 32) / 1e9, "GB/s"))
+        del sm, smt
+
     # next: per-direction quantization with two recipes in one pass: 1x128
     # E4M3 rows (a row-scaled forward copy) and MXFP8 E5M2 columns of 8192^2
     # bf16 (2 + 1 + 1 B/elem + 4 B per 128 and 1 B per 32 elements)

@@ -51,7 +51,8 @@ SIGNATURES = {
                               _VP],
     "fp8_quantize_hybrid": [_VP, _I32, _I64, _I64, _I32, _I32, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
                             _VP, _VP],
-    "fp8_quantize_hybrid_blockwise": [_VP, _I32, _I64, _I64, _I32, _I32, _VP, _VP, _I32, _I32, _VP, _VP, _VP],
+    "fp8_quantize_hybrid_blockwise": [_VP, _I32, _I64, _I64, _I32, _I32, _VP, _VP, _I32, _I32, _I32, _VP, _VP,
+                                      _VP],
     "fp8_cast_stats": [_VP, _I32, _I64, _I32, _VP, _VP, _VP],
     "fp8_quantize_error_feedback": [_VP, _I32, _VP, _I64, _I32, _VP, _VP, _VP, _VP],
     "fp8q_clock_monitor": [_VP, _VP, _VP],
@@ -381,11 +382,12 @@ def _subq_scales(recipe, rows, cols):
     return _U8, rows * (cols // 32)
 
 
-def fp8_quantize_hybrid_blockwise(x, row_recipe, row_fmt, col_recipe, col_fmt, *, q_row=None, s_row=None,
-                                  q_col=None, s_col=None, stream=None):
+def fp8_quantize_hybrid_blockwise(x, row_recipe, row_fmt, col_recipe, col_fmt, *, col_source=COLSRC_ORIGINAL,
+                                  q_row=None, s_row=None, q_col=None, s_col=None, stream=None):
     """Per-direction block quantization: rowwise copy by row_recipe in row_fmt
     (codes [rows][cols]), columnwise copy by col_recipe in col_fmt applied to
-    x^T (codes [cols][rows]); scales float32 (blocks) or uint8 (MXFP8)."""
+    x^T or to the dequantized rows (codes [cols][rows]); scales float32
+    (blocks) or uint8 (MXFP8)."""
     rows, cols = _shape2(x)
     if row_recipe in (SUBQ_BLOCK_128x128, SUBQ_BLOCK_1x128, SUBQ_MXFP8):
         _need(q_row, "q_row", _U8, rows * cols)
@@ -395,7 +397,8 @@ def fp8_quantize_hybrid_blockwise(x, row_recipe, row_fmt, col_recipe, col_fmt, *
         _need(s_col, "s_col", *_subq_scales(col_recipe, cols, rows))
     _check(lib.fp8_quantize_hybrid_blockwise(_ptr(x, "x"), _dtype(x), rows, cols, row_recipe, row_fmt,
                                              _ptr(q_row, "q_row"), _ptr(s_row, "s_row"), col_recipe, col_fmt,
-                                             _ptr(q_col, "q_col"), _ptr(s_col, "s_col"), _stream(stream)))
+                                             col_source, _ptr(q_col, "q_col"), _ptr(s_col, "s_col"),
+                                             _stream(stream)))
 
 
 def fp8_cast_stats(x, fmt, scale_inv, stats, stream=None):

@@ -683,14 +683,16 @@ static bool valid_subq(int32_t r)
 
 static int fp8_quantize_hybrid_blockwise_impl(Call &c, const void *x, int32_t dtype, int64_t rows, int64_t cols,
                                               int32_t row_recipe, int32_t row_fmt, uint8_t *q_row, void *s_row,
-                                              int32_t col_recipe, int32_t col_fmt, uint8_t *q_col, void *s_col,
-                                              void *stream)
+                                              int32_t col_recipe, int32_t col_fmt, int32_t col_source,
+                                              uint8_t *q_col, void *s_col, void *stream)
 {
     const char *fn = "fp8_quantize_hybrid_blockwise";
     if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
     if (!valid_fmt(row_fmt) || !valid_fmt(col_fmt)) return fail(FP8Q_EINVAL, "%s: unknown format", fn);
     if (!valid_subq(row_recipe) || !valid_subq(col_recipe))
         return fail(FP8Q_EINVAL, "%s: unknown sub-quantizer (row %d, col %d)", fn, (int)row_recipe, (int)col_recipe);
+    if (col_source != FP8Q_COLSRC_ORIGINAL && col_source != FP8Q_COLSRC_ROWWISE_DEQUANTIZED)
+        return fail(FP8Q_EINVAL, "%s: unknown columnwise source %d", fn, (int)col_source);
     if (rows < 0 || cols < 0) return fail(FP8Q_EINVAL, "%s: negative shape", fn);
     if (rows % 128 || cols % 128) return fail(FP8Q_EUNSUPPORTED, "%s: rows and cols must be multiples of 128", fn);
     if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 31)
@@ -712,21 +714,23 @@ static int fp8_quantize_hybrid_blockwise_impl(Call &c, const void *x, int32_t dt
         for (int j = 0; j < i; ++j)
             if (overlap(buf[i], len[i], buf[j], len[j])) return fail(FP8Q_EINVAL, "%s: buffers overlap", fn);
     return hip_status(fp8q::launch_hybrid_blockwise(x, dtype, rows, cols, row_recipe, row_fmt, q_row, s_row,
-                                                    col_recipe, col_fmt, q_col, s_col, (hipStream_t)stream),
+                                                    col_recipe, col_fmt, q_col, s_col,
+                                                    col_source == FP8Q_COLSRC_ROWWISE_DEQUANTIZED,
+                                                    (hipStream_t)stream),
                       fn);
 }
 
 extern "C" int fp8_quantize_hybrid_blockwise(const void *x, int32_t dtype, int64_t rows, int64_t cols,
                                              int32_t row_recipe, int32_t row_fmt, uint8_t *q_row, void *s_row,
-                                             int32_t col_recipe, int32_t col_fmt, uint8_t *q_col, void *s_col,
-                                             void *stream)
+                                             int32_t col_recipe, int32_t col_fmt, int32_t col_source, uint8_t *q_col,
+                                             void *s_col, void *stream)
 {
     Call c("fp8_quantize_hybrid_blockwise", stream);
-    c.args("dtype=%lld rows=%lld cols=%lld row_recipe=%lld row_fmt=%lld col_recipe=%lld col_fmt=%lld",
+    c.args("dtype=%lld rows=%lld cols=%lld row_recipe=%lld row_fmt=%lld col_recipe=%lld col_fmt=%lld col_source=%lld",
            (long long)dtype, (long long)rows, (long long)cols, (long long)row_recipe, (long long)row_fmt,
-           (long long)col_recipe, (long long)col_fmt);
+           (long long)col_recipe, (long long)col_fmt, (long long)col_source);
     return c.ret(fp8_quantize_hybrid_blockwise_impl(c, x, dtype, rows, cols, row_recipe, row_fmt, q_row, s_row,
-                                                    col_recipe, col_fmt, q_col, s_col, stream));
+                                                    col_recipe, col_fmt, col_source, q_col, s_col, stream));
 }
 
 static int fp8_cast_stats_impl(Call &c, const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *scale_inv,

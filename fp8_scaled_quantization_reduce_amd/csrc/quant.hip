@@ -977,6 +977,13 @@ template <int F> __device__ __forceinline__ MxScale mx_scale(uint32_t abits)
     return {__uint_as_float(mbits), (uint32_t)(e + 127)};
 }
 
+// Value of an E8M0 scale byte: 2^(b - 127) (2^-127 is a subnormal), NaN for 255.
+__device__ __forceinline__ float e8m0_value(uint32_t b)
+{
+    if (b == 255u) return __uint_as_float(kCanonicalNaN);
+    return __uint_as_float(b ? b << 23 : 0x00400000u);
+}
+
 constexpr int kTile = 128;
 
 // 4x4 byte transpose: d[r] holds row r (bytes = columns 0..3); e[c] returns
@@ -1147,7 +1154,7 @@ __device__ __forceinline__ void store_transposed(const uint32_t *tl, uint8_t *q_
 // One block loops over tiles t = blockIdx.x, blockIdx.x + G, ... (tile row
 // t / tiles_per_row, tile column t % tiles_per_row), G the number of tile
 // blocks (with kAmax the launch has one more, its finishing block).
-template <int F, int DT, int kMode, bool kAmax, int FCol = F, int kColMode = kMode>
+template <int F, int DT, int kMode, bool kAmax, int FCol = F, int kColMode = kMode, bool kColDeq = false>
 __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__ x, int64_t rows, int64_t cols,
                                                         ScaleSrc src, uint8_t *__restrict__ q_row,
                                                         uint8_t *__restrict__ q_col, void *__restrict__ s_row_p,
@@ -1166,7 +1173,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
     constexpr bool kDeq = kHybrid && ((kMode - kTileHybrid) >> 1); // columns from the dequantized rows
     // the block recipe of the column codes (kColMode) may differ from that
     // of the row codes (kMode): each direction's scales come from its own
-    // block maxima
+    // block maxima, taken over x or, with kColDeq, over the dequantized row
+    // values x' = fl32(value(row code) * d), d the row block's dequant scale
     constexpr bool kRow128 = kMode == kTileBlock128;
     constexpr bool kCol128 = kColMode == kTileBlock128, kCol1x = kColMode == kTileBlock1x128,
                    kColMX = kColMode == kTileMX;
@@ -1238,6 +1246,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
 #define PV(r, k) patch_elem<DT>(p, (r), (k))
 
         uint32_t cw[4][4]; // rowwise codes
+        [[maybe_unused]] float dq[4]; // kColDeq: the dequant scale of each of the lane's rows
         // Encodes of the lane's 4 x 16 patch; kR selects the NaN-repairing
         // encode, needed only when some product can be NaN (a NaN input, or a
         // scale that is NaN, infinite or zero).  Every mode encodes with the
@@ -1270,12 +1279,17 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
             m = block_max_u32<kThreads>(m, red);
             const float amax_b = __uint_as_float(canonical_amax_bits(m));
             const Scales sc = current_scales(amax_b, Fmt<F>::kMax, 0);
-            // 128x128 columns in a format of their own: the same block amax,
-            // that format's scale (other column recipes set their scales below)
-            if constexpr (kCol128 && FC != F) sc_col = current_scales(amax_b, Fmt<FC>::kMax, 0);
+            // 128x128 columns of x in a format of their own: the same block
+            // amax, that format's scale (other column recipes, and columns of
+            // x', set their scales below)
+            if constexpr (kCol128 && FC != F && !kColDeq) sc_col = current_scales(amax_b, Fmt<FC>::kMax, 0);
+            if constexpr (kColDeq) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dq[r] = sc.s;
+            }
             if (threadIdx.x == 0) {
                 if (q_row) s_row[tr * bcols + tc] = sc.s;
-                if (kCol128 && s_col) s_col[tc * brows + tr] = FC != F ? sc_col.s : sc.s;
+                if (kCol128 && !kColDeq && s_col) s_col[tc * brows + tr] = FC != F ? sc_col.s : sc.s;
             }
             // the block scale is uniform: finite and nonzero exactly when the
             // block holds no NaN or infinity
@@ -1298,6 +1312,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 uint32_t m = rm[r];
                 m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false)); // lane ^ 1
                 const MxScale ms = mx_scale<F>(m);
+                if constexpr (kColDeq) dq[r] = e8m0_value(ms.byte);
                 // the row's 4 scale bytes of this tile sit in lanes jg = 0, 2, 4, 6:
                 // gather them into lane jg = 0 (row_shl:n reads lane + n) for one
                 // 4-byte store instead of four byte stores
@@ -1334,6 +1349,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 // lane 7 - i of the 8 (DPP row_half_mirror): the other quad
                 m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
                 const Scales sc = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<F>::kMax, 0);
+                if constexpr (kColDeq) dq[r] = sc.s;
                 if (jg == 0 && q_row) s_row[(r0 + r) * bcols + tc] = sc.s;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
@@ -1361,12 +1377,44 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
         }
 
+        // x'(r, k), the dequantized row value of the lane's element (r, k); the
+        // repairing form gives a NaN x' (a NaN row code, or a zero code times
+        // an infinite block scale) the sign of its row code
+        auto xq = [&](auto rep, int r, int k) -> float {
+            const uint32_t w = cw[r][k >> 2];
+            const float2 h = (k & 2) ? dec2<F, true>(w) : dec2<F, false>(w);
+            float v = ((k & 1) ? h.y : h.x) * dq[r];
+            if constexpr (decltype(rep)::value) {
+                if (v != v) v = __uint_as_float(kCanonicalNaN | (((w >> (8 * (k & 3))) & 0x80u) << 24));
+            }
+            return v;
+        };
+        // the value a column code is formed from: x, or x' with kColDeq
+        auto cv = [&](auto rep, int r, int k) -> float {
+            if constexpr (kColDeq) return xq(rep, r, k);
+            else return PV(r, k);
+        };
+        // the lane's column maxima (magnitude bits) over its 4 rows
+        auto col_max = [&](uint32_t cmx[16]) {
+            if constexpr (kColDeq) {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    uint32_t m = 0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m = max(m, __float_as_uint(xq(Rep<false>{}, r, k)) & 0x7FFFFFFFu);
+                    cmx[k] = m;
+                }
+            } else {
+                patch_col_max<DT>(p, cmx);
+            }
+        };
+
         // column scales of the block recipes (and, for MXFP8, the column codes)
         if constexpr (kColMX) {
             if (q_col) {
                 opaque(p);
                 uint32_t cmax[16];
-                patch_col_max<DT>(p, cmax);
+                col_max(cmax);
                 float cm[16];
                 uint32_t cb[16], worst = 0;
 #pragma unroll
@@ -1395,8 +1443,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
 #pragma unroll
                         for (int q4 = 0; q4 < 4; ++q4) {
                             const int k = 4 * q4;
-                            cc[r][q4] = encode4s<FC, kR>(PV(r, k), PV(r, k + 1), PV(r, k + 2), PV(r, k + 3), cm[k],
-                                                         cm[k + 1], cm[k + 2], cm[k + 3]);
+                            cc[r][q4] = encode4s<FC, kR>(cv(rep, r, k), cv(rep, r, k + 1), cv(rep, r, k + 2),
+                                                         cv(rep, r, k + 3), cm[k], cm[k + 1], cm[k + 2], cm[k + 3]);
                         }
                 };
                 enc_cols(Rep<false>{});
@@ -1413,7 +1461,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
             if (q_col) {
                 const int wv = threadIdx.x >> 6;
                 uint32_t cm[16];
-                patch_col_max<DT>(p, cm);
+                col_max(cm);
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
                     uint32_t m = cm[k];
@@ -1440,11 +1488,20 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                 }
                 __syncthreads();
             }
-        } else if constexpr (kCol128 && !kRow128) {
+        } else if constexpr (kCol128 && (!kRow128 || kColDeq)) {
             if (q_col) {
-                uint32_t rm[4];
-                patch_row_max<DT>(p, rm);
-                const uint32_t m = block_max_u32<kThreads>(max(max(rm[0], rm[1]), max(rm[2], rm[3])), red);
+                uint32_t lm = 0;
+                if constexpr (kColDeq) {
+                    uint32_t cmx[16];
+                    col_max(cmx);
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) lm = max(lm, cmx[k]);
+                } else {
+                    uint32_t rm[4];
+                    patch_row_max<DT>(p, rm);
+                    lm = max(max(rm[0], rm[1]), max(rm[2], rm[3]));
+                }
+                const uint32_t m = block_max_u32<kThreads>(lm, red);
                 sc_col = current_scales(__uint_as_float(canonical_amax_bits(m)), Fmt<FC>::kMax, 0);
                 if (threadIdx.x == 0) s_col[tc * brows + tr] = sc_col.s;
             }
@@ -1462,8 +1519,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                         for (int q4 = 0; q4 < 4; ++q4) {
                             const int k = 4 * q4;
                             const float *cs = colscale + 16 * jg + k;
-                            cc[r][q4] = encode4s<FC, kR>(PV(r, k), PV(r, k + 1), PV(r, k + 2), PV(r, k + 3), cs[0],
-                                                         cs[1], cs[2], cs[3]);
+                            cc[r][q4] = encode4s<FC, kR>(cv(rep, r, k), cv(rep, r, k + 1), cv(rep, r, k + 2),
+                                                         cv(rep, r, k + 3), cs[0], cs[1], cs[2], cs[3]);
                         }
                 };
                 enc_cols(Rep<false>{});
@@ -1524,8 +1581,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     enc_cols(Rep<true>{});
                 }
                 stage_transposed(tl, cc, ig, jg);
-            } else if constexpr (kCol128 && (FC != F || !kRow128)) {
-                // the block's column codes in their own format or recipe, from x
+            } else if constexpr (kCol128 && (FC != F || !kRow128 || kColDeq)) {
+                // the block's column codes in their own format or recipe, from x or x'
                 opaque(p);
                 uint32_t cc[4][4];
                 auto enc_cols = [&](auto rep) {
@@ -1534,8 +1591,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     for (int r = 0; r < 4; ++r)
 #pragma unroll
                         for (int q4 = 0; q4 < 4; ++q4)
-                            cc[r][q4] = encode4<FC, kR>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
-                                                        PV(r, 4 * q4 + 3), sc_col.scale);
+                            cc[r][q4] = encode4<FC, kR>(cv(rep, r, 4 * q4), cv(rep, r, 4 * q4 + 1),
+                                                        cv(rep, r, 4 * q4 + 2), cv(rep, r, 4 * q4 + 3), sc_col.scale);
                 };
                 enc_cols(Rep<false>{});
                 if (!finite_nonzero(sc_col.scale)) {
@@ -1711,68 +1768,75 @@ hipError_t launch_mx(const void *x, int dtype, int64_t rows, int64_t cols, int f
 }
 
 // One pass over x: the row codes by the block recipe kMode in F, the column
-// codes by the block recipe kColMode in FC; either copy may be absent (its
-// code and scale pointers null).  A pass with MXFP8 codes runs one tile per
-// block, the block-scaled ones loop over tiles (the measured faster forms).
-template <int F, int FC, int DT, int kMode, int kColMode>
+// codes by the block recipe kColMode in FC, from x or (kDeq) from the
+// dequantized row codes; either copy may be absent (its code and scale
+// pointers null).  A pass with MXFP8 codes runs one tile per block, the
+// block-scaled ones loop over tiles (the measured faster forms).
+template <int F, int FC, int DT, int kMode, int kColMode, bool kDeq>
 static hipError_t launch_subq_m(const void *x, int64_t rows, int64_t cols, uint8_t *q_row, void *s_row,
                                 uint8_t *q_col, void *s_col, hipStream_t s)
 {
     const int grid = (kMode == kTileMX || kColMode == kTileMX) ? tile_grid(rows, cols)
                                                                : min(tile_grid(rows, cols), kBlockQuantGrid);
     const ScaleSrc none{nullptr, nullptr, 0};
-    tile_kernel<F, DT, kMode, false, FC, kColMode><<<grid, kThreads, 0, s>>>(
+    tile_kernel<F, DT, kMode, false, FC, kColMode, kDeq><<<grid, kThreads, 0, s>>>(
         x, rows, cols, none, q_row, q_col, s_row, s_col, nullptr, nullptr, nullptr, none, nullptr, Finish{});
     return hipGetLastError();
 }
 
-template <int F, int FC, int DT, int kMode>
+template <int F, int FC, int DT, int kMode, bool kDeq>
 static hipError_t launch_subq_c(int col_recipe, const void *x, int64_t rows, int64_t cols, uint8_t *q_row,
                                 void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
 {
+#define FP8Q_ARGS x, rows, cols, q_row, s_row, q_col, s_col, s
     switch (col_recipe) {
-    case kSubqBlock128:
-        return launch_subq_m<F, FC, DT, kMode, kTileBlock128>(x, rows, cols, q_row, s_row, q_col, s_col, s);
-    case kSubqBlock1x128:
-        return launch_subq_m<F, FC, DT, kMode, kTileBlock1x128>(x, rows, cols, q_row, s_row, q_col, s_col, s);
-    case kSubqMX: return launch_subq_m<F, FC, DT, kMode, kTileMX>(x, rows, cols, q_row, s_row, q_col, s_col, s);
+    case kSubqBlock128: return launch_subq_m<F, FC, DT, kMode, kTileBlock128, kDeq>(FP8Q_ARGS);
+    case kSubqBlock1x128: return launch_subq_m<F, FC, DT, kMode, kTileBlock1x128, kDeq>(FP8Q_ARGS);
+    case kSubqMX: return launch_subq_m<F, FC, DT, kMode, kTileMX, kDeq>(FP8Q_ARGS);
     }
+#undef FP8Q_ARGS
     return hipErrorInvalidValue;
 }
 
-template <int F, int FC, int DT>
+template <int F, int FC, int DT, bool kDeq>
 static hipError_t launch_subq_r(int row_recipe, int col_recipe, const void *x, int64_t rows, int64_t cols,
                                 uint8_t *q_row, void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
 {
 #define FP8Q_ARGS col_recipe, x, rows, cols, q_row, s_row, q_col, s_col, s
     switch (row_recipe) {
-    case kSubqBlock128: return launch_subq_c<F, FC, DT, kTileBlock128>(FP8Q_ARGS);
-    case kSubqBlock1x128: return launch_subq_c<F, FC, DT, kTileBlock1x128>(FP8Q_ARGS);
-    case kSubqMX: return launch_subq_c<F, FC, DT, kTileMX>(FP8Q_ARGS);
+    case kSubqBlock128: return launch_subq_c<F, FC, DT, kTileBlock128, kDeq>(FP8Q_ARGS);
+    case kSubqBlock1x128: return launch_subq_c<F, FC, DT, kTileBlock1x128, kDeq>(FP8Q_ARGS);
+    case kSubqMX: return launch_subq_c<F, FC, DT, kTileMX, kDeq>(FP8Q_ARGS);
     }
 #undef FP8Q_ARGS
     return hipErrorInvalidValue;
 }
 
 template <int F, int FC>
-static hipError_t launch_subq_d(int dtype, int row_recipe, int col_recipe, const void *x, int64_t rows, int64_t cols,
-                                uint8_t *q_row, void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
+static hipError_t launch_subq_d(int dtype, bool deq, int row_recipe, int col_recipe, const void *x, int64_t rows,
+                                int64_t cols, uint8_t *q_row, void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
 {
 #define FP8Q_ARGS row_recipe, col_recipe, x, rows, cols, q_row, s_row, q_col, s_col, s
-    if (dtype == kBF16) return launch_subq_r<F, FC, kBF16>(FP8Q_ARGS);
-    return launch_subq_r<F, FC, kF32>(FP8Q_ARGS);
+    if (deq) {
+        if (dtype == kBF16) return launch_subq_r<F, FC, kBF16, true>(FP8Q_ARGS);
+        return launch_subq_r<F, FC, kF32, true>(FP8Q_ARGS);
+    }
+    if (dtype == kBF16) return launch_subq_r<F, FC, kBF16, false>(FP8Q_ARGS);
+    return launch_subq_r<F, FC, kF32, false>(FP8Q_ARGS);
 #undef FP8Q_ARGS
 }
 
 hipError_t launch_hybrid_blockwise(const void *x, int dtype, int64_t rows, int64_t cols, int row_recipe, int row_fmt,
                                    uint8_t *q_row, void *s_row, int col_recipe, int col_fmt, uint8_t *q_col,
-                                   void *s_col, hipStream_t s)
+                                   void *s_col, bool col_from_rows, hipStream_t s)
 {
     if (rows == 0 || cols == 0) return hipSuccess;
-    // one direction alone: the single-format kernel of its recipe
+    // one direction alone: the single-format kernel of its recipe (the
+    // dequantized source still forms the row codes, unstored)
+    const bool deq = col_from_rows && q_col;
     if (!q_col) col_recipe = row_recipe, col_fmt = row_fmt;
-    if (!q_row) row_recipe = col_recipe, row_fmt = col_fmt;
-#define FP8Q_ARGS dtype, row_recipe, col_recipe, x, rows, cols, q_row, s_row, q_col, s_col, s
+    if (!q_row && !deq) row_recipe = col_recipe, row_fmt = col_fmt;
+#define FP8Q_ARGS dtype, deq, row_recipe, col_recipe, x, rows, cols, q_row, s_row, q_col, s_col, s
     if (row_fmt == kE4M3)
         return col_fmt == kE4M3 ? launch_subq_d<kE4M3, kE4M3>(FP8Q_ARGS) : launch_subq_d<kE4M3, kE5M2>(FP8Q_ARGS);
     return col_fmt == kE4M3 ? launch_subq_d<kE5M2, kE4M3>(FP8Q_ARGS) : launch_subq_d<kE5M2, kE5M2>(FP8Q_ARGS);

@@ -87,7 +87,8 @@ extern "C" {
 #define FP8Q_OUT_E4M3FN 2
 #define FP8Q_OUT_E5M2 3
 
-/* source of the columnwise copy in fp8_quantize_hybrid, [HYBRID] */
+/* source of the columnwise copy in fp8_quantize_hybrid and
+ * fp8_quantize_hybrid_blockwise, [HYBRID] */
 #define FP8Q_COLSRC_ORIGINAL 0
 #define FP8Q_COLSRC_ROWWISE_DEQUANTIZED 1
 
@@ -360,16 +361,24 @@ int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, int64_t cols
 /*
  * fp8_quantize_hybrid_blockwise -- per-direction ("hybrid") quantization with
  * block sub-quantizers ([HYBRID]: each direction has a quantizer of its own,
- * with its own format and recipe, blockwise and MXFP8 ones included; here
- * both copies come from the original input).
+ * with its own format and recipe, blockwise and MXFP8 ones included; the
+ * columnwise copy is quantized from the original input or from the
+ * dequantized rowwise values).
  *   x [rows][cols] of dtype; rows, cols multiples of 128.
  *   Rowwise copy: row_recipe in row_fmt applied to x, exactly what
  *     fp8_quantize_block / fp8_quantize_mx write as q_row and s_row:
  *     q_row [rows][cols]; s_row float [rows/128][cols/128] (128x128),
  *     float [rows][cols/128] (1x128) or E8M0 bytes [rows][cols/32] (MXFP8).
- *   Columnwise copy: col_recipe in col_fmt applied to x^T, what those calls
+ *   Columnwise copy: col_recipe in col_fmt applied to y^T, what those calls
  *     write as q_col and s_col: q_col [cols][rows]; s_col float
  *     [cols/128][rows/128], float [cols][rows/128] or bytes [cols][rows/32].
+ *     col_source FP8Q_COLSRC_ORIGINAL: y = x;
+ *     FP8Q_COLSRC_ROWWISE_DEQUANTIZED: y = x' = fl32(value(q_row) * d)
+ *     elementwise, d the dequant scale of the element's row block (the FP32
+ *     block scale, or 2^(byte - 127) for MXFP8, NaN for byte 255); where x'
+ *     is NaN (a NaN row code, or a zero code times an infinite block scale)
+ *     its column code is the NaN code with the row code's sign bit.  The row
+ *     codes are formed even when q_row is NULL.
  *   Either copy may be skipped (its code and scale pointers both NULL), not
  *   both.  The call reads x once, whatever the two recipes and formats (with
  *   one recipe both ways, both formats take their scales from the same block
@@ -381,7 +390,7 @@ int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, int64_t cols
  */
 int fp8_quantize_hybrid_blockwise(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t row_recipe,
                                   int32_t row_fmt, uint8_t *q_row, void *s_row, int32_t col_recipe, int32_t col_fmt,
-                                  uint8_t *q_col, void *s_col, void *stream);
+                                  int32_t col_source, uint8_t *q_col, void *s_col, void *stream);
 
 /*
  * fp8_cast_stats -- diagnostics of the per-tensor cast of x with dequant

@@ -228,15 +228,16 @@ def test_hybrid_blockwise_validation():
     h = L.fp8_quantize_hybrid_blockwise
     X, QR, SR, QC, SC = BAD, BAD + 0x100000, BAD + 0x200000, BAD + 0x300000, BAD + 0x400000
 
-    def call(dtype=fq.BF16, rows=256, cols=384, rr=fq.SUBQ_MXFP8, rf=0, cr=fq.SUBQ_BLOCK_1x128, cf=1, x=X, qr=QR,
-             sr=SR, qc=QC, sc=SC):
-        return h(x, dtype, rows, cols, rr, rf, qr, sr, cr, cf, qc, sc, S)
+    def call(dtype=fq.BF16, rows=256, cols=384, rr=fq.SUBQ_MXFP8, rf=0, cr=fq.SUBQ_BLOCK_1x128, cf=1, src=0, x=X,
+             qr=QR, sr=SR, qc=QC, sc=SC):
+        return h(x, dtype, rows, cols, rr, rf, qr, sr, cr, cf, src, qc, sc, S)
 
     _expect(call(dtype=5), fq.EINVAL, "dtype")
     _expect(call(rf=2), fq.EINVAL, "format")
     _expect(call(cf=-1), fq.EINVAL, "format")
     _expect(call(rr=3), fq.EINVAL, "sub-quantizer")
     _expect(call(cr=-1), fq.EINVAL, "sub-quantizer")
+    _expect(call(src=2), fq.EINVAL, "columnwise source")
     _expect(call(rows=-128), fq.EINVAL, "negative")
     _expect(call(cols=200), fq.EUNSUPPORTED, "multiples of 128")
     _expect(call(sr=None), fq.EINVAL, "q_row and s_row")
@@ -352,7 +353,7 @@ def test_valid_calls_without_a_device_return_ehip():
                                                             BAD + 0x200000, None, None, S)),
         ("fp8_quantize_hybrid_blockwise",
          lambda: L.fp8_quantize_hybrid_blockwise(BAD, fq.BF16, 128, 128, fq.SUBQ_MXFP8, 0, BAD + 0x100000,
-                                                 BAD + 0x200000, fq.SUBQ_BLOCK_128x128, 1, BAD + 0x300000,
+                                                 BAD + 0x200000, fq.SUBQ_BLOCK_128x128, 1, 1, BAD + 0x300000,
                                                  BAD + 0x400000, S)),
         ("fp8_update_scale_delayed", lambda: L.fp8_update_scale_delayed(BAD, 16, 1, 0, BAD + 0x100, 0, 0, 0, 0,
                                                                         BAD + 0x200, BAD + 0x300, S)),

@@ -4,7 +4,8 @@ each direction has its own quantizer, format and recipe, blockwise and MXFP8
 ones included) against the oracle, bit for bit: codes, FP32 block scales and
 E8M0 scale bytes are all decided in binary32 or integer arithmetic on both
 sides.  Covers every pair of recipes (one pass over x for any pair) with both
-format orders, bf16 and fp32 inputs with planted specials, one direction
+format orders and both columnwise sources (the original input, the
+dequantized rows), bf16 and fp32 inputs with planted specials, one direction
 alone, agreement with the single-format entry points, and the full-size
 block and MXFP8 workloads."""
 import numpy as np
@@ -21,6 +22,7 @@ fq = pytest.importorskip("fp8_scaled_quantization_reduce_amd")
 E4, E5 = oracle.E4M3FN, oracle.E5M2
 B128, B1x128, MX = oracle.SUBQ_BLOCK_128x128, oracle.SUBQ_BLOCK_1x128, oracle.SUBQ_MXFP8
 NAMES = {B128: "128x128", B1x128: "1x128", MX: "mxfp8"}
+ORIG, DEQ = oracle.COLSRC_ORIGINAL, oracle.COLSRC_ROWWISE_DEQUANTIZED
 
 
 def _scale_buf(recipe, rows, cols):
@@ -31,7 +33,7 @@ def _scale_buf(recipe, rows, cols):
     return torch.full((n,), -7.25, dtype=torch.float32, device="cuda")
 
 
-def _gpu(x, row_recipe, row_fmt, col_recipe, col_fmt, want_row=True, want_col=True):
+def _gpu(x, row_recipe, row_fmt, col_recipe, col_fmt, want_row=True, want_col=True, src=0):
     rows, cols = x.shape
     q_row = s_row = q_col = s_col = None
     if want_row:
@@ -40,8 +42,8 @@ def _gpu(x, row_recipe, row_fmt, col_recipe, col_fmt, want_row=True, want_col=Tr
     if want_col:
         q_col = torch.full((cols, rows), 0xA5, dtype=torch.uint8, device="cuda")
         s_col = _scale_buf(col_recipe, cols, rows)
-    fq.fp8_quantize_hybrid_blockwise(to_dev(x), row_recipe, row_fmt, col_recipe, col_fmt, q_row=q_row, s_row=s_row,
-                                     q_col=q_col, s_col=s_col)
+    fq.fp8_quantize_hybrid_blockwise(to_dev(x), row_recipe, row_fmt, col_recipe, col_fmt, col_source=src,
+                                     q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col)
     return {k: None if v is None else host(v) for k, v in
             dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col).items()}
 
@@ -78,22 +80,51 @@ def _input(dtype, rows, cols, seed, specials=True):
     return x
 
 
+@pytest.mark.parametrize("src", [ORIG, DEQ], ids=["original", "dequantized"])
 @pytest.mark.parametrize("row_recipe", [B128, B1x128, MX], ids=lambda r: "row_" + NAMES[r])
 @pytest.mark.parametrize("col_recipe", [B128, B1x128, MX], ids=lambda r: "col_" + NAMES[r])
 @pytest.mark.parametrize("fmts", [(E4, E5), (E5, E4)], ids=["e4m3_e5m2", "e5m2_e4m3"])
-def test_every_recipe_pair_bf16(row_recipe, col_recipe, fmts):
+def test_every_recipe_pair_bf16(row_recipe, col_recipe, fmts, src):
     x = _input("bf16", 384, 512, seed=301)
-    got = _gpu(x, row_recipe, fmts[0], col_recipe, fmts[1])
-    _check(got, oracle.quantize_hybrid_blockwise(x, row_recipe, fmts[0], col_recipe, fmts[1]))
+    got = _gpu(x, row_recipe, fmts[0], col_recipe, fmts[1], src=src)
+    _check(got, oracle.quantize_hybrid_blockwise(x, row_recipe, fmts[0], col_recipe, fmts[1], src))
 
 
 @pytest.mark.parametrize("recipes", [(B128, B128), (B1x128, B1x128), (MX, MX), (B128, MX), (MX, B1x128),
                                      (B1x128, B128)], ids=lambda r: NAMES[r[0]] + "_" + NAMES[r[1]])
 @pytest.mark.parametrize("fmts", [(E4, E5), (E5, E4), (E5, E5)], ids=["e4m3_e5m2", "e5m2_e4m3", "e5m2_e5m2"])
-def test_recipe_pairs_fp32(recipes, fmts):
+@pytest.mark.parametrize("src", [ORIG, DEQ], ids=["original", "dequantized"])
+def test_recipe_pairs_fp32(recipes, fmts, src):
     x = _input("f32", 256, 640, seed=302)
-    got = _gpu(x, recipes[0], fmts[0], recipes[1], fmts[1])
-    _check(got, oracle.quantize_hybrid_blockwise(x, recipes[0], fmts[0], recipes[1], fmts[1]))
+    got = _gpu(x, recipes[0], fmts[0], recipes[1], fmts[1], src=src)
+    _check(got, oracle.quantize_hybrid_blockwise(x, recipes[0], fmts[0], recipes[1], fmts[1], src))
+
+
+@pytest.mark.parametrize("recipes", [(B128, B128), (MX, B1x128), (B1x128, MX)],
+                         ids=lambda r: NAMES[r[0]] + "_" + NAMES[r[1]])
+def test_dequantized_columns_without_row_copy(recipes):
+    """The dequantized source with no rowwise buffers: the row codes are still
+    formed (unstored) and the columnwise copy matches."""
+    x = _input("bf16", 256, 384, seed=305)
+    want = oracle.quantize_hybrid_blockwise(x, recipes[0], E4, recipes[1], E5, DEQ)
+    got = _gpu(x, recipes[0], E4, recipes[1], E5, want_row=False, src=DEQ)
+    _check(got, want, ("col",))
+
+
+def test_dequantized_block_with_infinity_and_nan():
+    """128x128 E4M3 rows and E5M2 columns from the dequantized rows, with a
+    block holding +inf next to negative values (its finite elements encode to
+    zero codes of either sign, x' = 0 * inf is NaN) and a block holding a
+    NaN: every column code there is the NaN code with its row code's sign."""
+    x = workloads.block_weight(256, 256, seed=306, std=3.0)
+    x[5, 9] = 0x7FC0
+    x[130, 140] = 0x7F80
+    x[131, 141] = 0xC000
+    for recipes in ((B128, B128), (B128, MX), (B128, B1x128)):
+        got = _gpu(x, recipes[0], E4, recipes[1], E5, src=DEQ)
+        want = oracle.quantize_hybrid_blockwise(x, recipes[0], E4, recipes[1], E5, DEQ)
+        _check(got, want)
+        assert np.array_equal(got["q_col"][128:, 128:], (got["q_row"][128:, 128:] | 0x7F).T)
 
 
 @pytest.mark.parametrize("recipe", [B128, B1x128, MX], ids=lambda r: NAMES[r])
@@ -137,10 +168,11 @@ def test_one_format_equals_single_recipe_entry_point(recipe):
     ((MX, MX), (8192, 8192), lambda: workloads.delayed_step(0)),
     ((B1x128, MX), (8192, 8192), lambda: workloads.delayed_step(1)),
 ], ids=["128x128_weight_7168x4096", "1x128_act_4096x7168", "mxfp8_8192x8192", "1x128_rows_mxfp8_cols_8192x8192"])
-def test_full_size_e4m3_rows_e5m2_cols(recipes, shape, make):
+@pytest.mark.parametrize("src", [ORIG, DEQ], ids=["original", "dequantized"])
+def test_full_size_e4m3_rows_e5m2_cols(recipes, shape, make, src):
     """The block and MXFP8 workloads at their full size, E4M3 forward copy and
     E5M2 backward copy in one pass, every code and scale compared."""
     x = make()
     assert x.shape == shape
-    got = _gpu(x, recipes[0], E4, recipes[1], E5)
-    _check(got, oracle.quantize_hybrid_blockwise(x, recipes[0], E4, recipes[1], E5))
+    got = _gpu(x, recipes[0], E4, recipes[1], E5, src=src)
+    _check(got, oracle.quantize_hybrid_blockwise(x, recipes[0], E4, recipes[1], E5, src))
