@@ -48,7 +48,7 @@ MFMA_PEAK_SCLK_MHZ = 2400.0  # the clock the 5.0 PFLOP/s figure assumes (256 CUs
 # from the FETCH_SIZE and WRITE_SIZE counters scaled by the factors a plain
 # copy gives (profiles/hbm_traffic_bench_kernels.md); None whenever the kernel
 # has changed since the counters were taken.
-TRAFFIC_BYTES_PER_STEP = 201784951
+TRAFFIC_BYTES_PER_STEP = 201781495
 
 # Seconds of untimed launches before each row is timed.  The GPU's clocks
 # take tens of milliseconds of sustained matrix work to settle: measured on

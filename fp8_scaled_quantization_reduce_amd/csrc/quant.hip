@@ -1834,8 +1834,14 @@ hipError_t launch_hybrid_blockwise(const void *x, int dtype, int64_t rows, int64
     // one direction alone: the single-format kernel of its recipe (the
     // dequantized source still forms the row codes, unstored)
     const bool deq = col_from_rows && q_col;
-    if (!q_col) col_recipe = row_recipe, col_fmt = row_fmt;
-    if (!q_row && !deq) row_recipe = col_recipe, row_fmt = col_fmt;
+    if (!q_col) {
+        col_recipe = row_recipe;
+        col_fmt = row_fmt;
+    }
+    if (!q_row && !deq) {
+        row_recipe = col_recipe;
+        row_fmt = col_fmt;
+    }
 #define FP8Q_ARGS dtype, deq, row_recipe, col_recipe, x, rows, cols, q_row, s_row, q_col, s_col, s
     if (row_fmt == kE4M3)
         return col_fmt == kE4M3 ? launch_subq_d<kE4M3, kE4M3>(FP8Q_ARGS) : launch_subq_d<kE4M3, kE5M2>(FP8Q_ARGS);
