@@ -1,7 +1,8 @@
 """GPU parity at sizes past 2^31 elements or bytes, where every index and
 offset must be 64-bit: the amax and the cast over 2^31 + 2^20 + 7 bf16
-elements, the rowwise + columnwise cast of a 65536 x 32784 bf16 tensor, and a
-GEMM whose A operand spans 2 GiB.  Inputs are a seeded pattern repeated over
+elements, the rowwise + columnwise cast of a 65536 x 32784 bf16 tensor, the
+per-direction block quantization (1x128 rows, MXFP8 columns) of a 65536 x
+32896 one, and a GEMM whose A operand spans 2 GiB.  Inputs are a seeded pattern repeated over
 the tensor with planted values past the 2^31 mark (so a 32-bit index would
 miss or misplace them); results are compared with the oracle on the whole
 amax and on sampled codes and outputs, the samples drawn across the whole
@@ -76,6 +77,45 @@ def test_rowwise_colwise_past_2_31_elements():
     ri, ci = torch.from_numpy(r).to("cuda"), torch.from_numpy(c).to("cuda")
     assert np.array_equal(host(q_row[ri, ci]), want)
     assert np.array_equal(host(q_col[ci, ri]), want)
+    assert host(q_row[rows - 1, cols - 1:])[0] == 0x7E
+
+
+def test_hybrid_blockwise_two_recipes_past_2_31_elements():
+    """1x128 E4M3 rows and MXFP8 E5M2 columns of a 65536 x 32896 bf16 tensor
+    in one pass: sampled row segments and column blocks, the tails and the
+    segments past the 2^31 mark included, against the oracle's quantizers of
+    those segments."""
+    rows, cols = 65536, 32896
+    x = _pattern_bf16(rows * cols, 13).reshape(rows, cols)
+    x[rows - 1, cols - 1] = 0x4600   # 8192.0 in the last element
+    r_big = (1 << 31) // cols + 1    # a row that starts past element 2^31
+    x[r_big, 5] = 0xC67F             # -16320.0
+    q_row = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    s_row = torch.empty((rows, cols // 128), dtype=torch.float32, device="cuda")
+    q_col = torch.empty((cols, rows), dtype=torch.uint8, device="cuda")
+    s_col = torch.empty((cols, rows // 32), dtype=torch.uint8, device="cuda")
+    fq.fp8_quantize_hybrid_blockwise(to_dev(x), fq.SUBQ_BLOCK_1x128, E4, fq.SUBQ_MXFP8, E5, q_row=q_row, s_row=s_row,
+                                     q_col=q_col, s_col=s_col)
+    rng = np.random.default_rng(3)
+    # row segments (row, segment of 128 columns)
+    rr = np.concatenate([rng.integers(0, rows, 2000), [rows - 1, r_big, 0]])
+    rs = np.concatenate([rng.integers(0, cols // 128, 2000), [cols // 128 - 1, 0, 0]])
+    seg = x[rr[:, None], rs[:, None] * 128 + np.arange(128)]
+    q_ref, s_ref = oracle.quantize_blocks(np.ascontiguousarray(seg), E4, 1, 128)
+    cidx = torch.from_numpy(rs[:, None] * 128 + np.arange(128)).to("cuda")
+    got_q = torch.gather(q_row[torch.from_numpy(rr).to("cuda")], 1, cidx)
+    assert np.array_equal(host(got_q), q_ref)
+    assert np.array_equal(f32_bits(host(s_row[torch.from_numpy(rr).to("cuda"), torch.from_numpy(rs).to("cuda")])),
+                          f32_bits(s_ref[:, 0]))
+    # column blocks (column, block of 32 rows)
+    cc = np.concatenate([rng.integers(0, cols, 2000), [cols - 1, 5, 0]])
+    cb = np.concatenate([rng.integers(0, rows // 32, 2000), [rows // 32 - 1, r_big // 32, 0]])
+    blk = x[cb[:, None] * 32 + np.arange(32), cc[:, None]]
+    qm_ref, sm_ref = oracle.quantize_mx(np.ascontiguousarray(blk), E5)
+    ridx = torch.from_numpy(cb[:, None] * 32 + np.arange(32)).to("cuda")
+    got_qc = torch.gather(q_col[torch.from_numpy(cc).to("cuda")], 1, ridx)
+    assert np.array_equal(host(got_qc), qm_ref)
+    assert np.array_equal(host(s_col[torch.from_numpy(cc).to("cuda"), torch.from_numpy(cb).to("cuda")]), sm_ref[:, 0])
     assert host(q_row[rows - 1, cols - 1:])[0] == 0x7E
 
 
