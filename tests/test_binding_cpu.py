@@ -77,6 +77,17 @@ BAD_CALLS = [
     (lambda: fq.fp8_scaled_gemm_fused(u8(256, 512), 0, f32(1), u8(384, 512), 0, f32(1), fq.PER_TENSOR,
                                       u8(256, 384), out_fmt=fq.E4M3FN), ValueError, "c_scale_inv"),
     (lambda: fq.fp8_quantize_hybrid(X, 0, 1, 0, q_row=u8(N), q_col=u8(N + 1), amax_in=f32(1)), ValueError, "q_col"),
+    (lambda: fq.fp8_quantize_hybrid_blockwise(X, fq.SUBQ_MXFP8, 0, fq.SUBQ_BLOCK_1x128, 1, q_row=u8(N),
+                                              s_row=u8(3071), q_col=u8(N), s_col=f32(768)), ValueError,
+     "s_row must have 3072"),
+    (lambda: fq.fp8_quantize_hybrid_blockwise(X, fq.SUBQ_MXFP8, 0, fq.SUBQ_BLOCK_1x128, 1, q_row=u8(N),
+                                              s_row=f32(3072), q_col=u8(N), s_col=f32(768)), TypeError,
+     "s_row must be"),
+    (lambda: fq.fp8_quantize_hybrid_blockwise(X, fq.SUBQ_MXFP8, 0, fq.SUBQ_BLOCK_1x128, 1, q_row=u8(N),
+                                              s_row=u8(3072), q_col=u8(N), s_col=f32(767)), ValueError,
+     "s_col must have 768"),
+    (lambda: fq.fp8_quantize_hybrid_blockwise(X, fq.SUBQ_BLOCK_128x128, 0, fq.SUBQ_BLOCK_128x128, 1, q_row=u8(N),
+                                              s_row=f32(6), q_col=u8(N - 1), s_col=f32(6)), ValueError, "q_col"),
     (lambda: fq.fp8_cast_stats(X, 0, f32(1), i64(5)), ValueError, "stats"),
     (lambda: fq.fp8_quantize_error_feedback(X, f32(N - 1), 0, f32(1), u8(N)), ValueError, "residual"),
     (lambda: fq.fp8_quantize_error_feedback(X, f32(N), 0, f32(1), u8(N), amax_out=f32(3)), ValueError, "amax_out"),
@@ -101,6 +112,8 @@ GOOD_SHAPES_ON_HOST = [
     lambda: fq.fp8_scaled_gemm(u8(256, 512), 0, u8(256 * 16), u8(384, 512), 0, u8(384 * 16), fq.MXFP8,
                                f32(256, 384)),
     lambda: fq.fp8_quantize_error_feedback(X, f32(N), 0, f32(1), u8(N)),
+    lambda: fq.fp8_quantize_hybrid_blockwise(X, fq.SUBQ_MXFP8, 0, fq.SUBQ_BLOCK_1x128, 1, q_row=u8(N),
+                                             s_row=u8(3072), q_col=u8(N), s_col=f32(768)),
 ]
 
 
