@@ -30,7 +30,7 @@ E4M3FN, E5M2 = 0, 1
 F32, BF16 = 0, 1
 ALGO_MAX, ALGO_MOST_RECENT = 0, 1
 PER_TENSOR, BLOCK_1x128_128x128, BLOCK_1x128_1x128, MXFP8 = 0, 1, 2, 3
-SUBQ_BLOCK_128x128, SUBQ_BLOCK_1x128, SUBQ_MXFP8 = 0, 1, 2
+SUBQ_BLOCK_128x128, SUBQ_BLOCK_1x128, SUBQ_MXFP8, SUBQ_PER_TENSOR = 0, 1, 2, 3
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -486,8 +486,13 @@ def quantize_hybrid(x: np.ndarray, row_fmt: int, col_fmt: int, col_source: int, 
     return dict(q_row=q_row, q_col=q_col, row_scale_inv=s_r, col_scale_inv=s_c)
 
 
-def _block_subquantizer(src: np.ndarray, recipe: int, fmt: int):
-    """(codes, scales) of one block sub-quantizer applied to the rows of src."""
+def _block_subquantizer(src: np.ndarray, recipe: int, fmt: int, pt=None):
+    """(codes, scales) of one sub-quantizer applied to the rows of src; a
+    per-tensor one takes its scale from pt = dict(amax_in, margin) or
+    dict(scale_inv_in) and reports its dequant scale as a one-element array."""
+    if recipe == SUBQ_PER_TENSOR:
+        r = quantize_tensor(src, fmt, **pt)
+        return r["q"], np.array([r["scale_inv"]], dtype=np.float32)
     if recipe == SUBQ_BLOCK_128x128:
         return quantize_blocks(src, fmt, 128, 128)
     if recipe == SUBQ_BLOCK_1x128:
@@ -499,8 +504,11 @@ def _block_subquantizer(src: np.ndarray, recipe: int, fmt: int):
 
 def _row_dequant_scales(recipe: int, s_row: np.ndarray, rows: int, cols: int) -> np.ndarray:
     """float32 [rows][cols]: each element's dequant scale under the row recipe
-    (its block's FP32 scale, or 2^(byte - 127) for MXFP8, NaN for byte 255)."""
-    if recipe == SUBQ_BLOCK_128x128:
+    (the tensor's or its block's FP32 scale, or 2^(byte - 127) for MXFP8, NaN
+    for byte 255)."""
+    if recipe == SUBQ_PER_TENSOR:
+        d = np.full((rows, cols), s_row[0], dtype=np.float32)
+    elif recipe == SUBQ_BLOCK_128x128:
         d = np.repeat(np.repeat(s_row, 128, axis=0), 128, axis=1)
     elif recipe == SUBQ_BLOCK_1x128:
         d = np.repeat(s_row, 128, axis=1)
@@ -511,7 +519,7 @@ def _row_dequant_scales(recipe: int, s_row: np.ndarray, rows: int, cols: int) ->
 
 
 def quantize_hybrid_blockwise(x: np.ndarray, row_recipe: int, row_fmt: int, col_recipe: int, col_fmt: int,
-                              col_source: int = 0):
+                              col_source: int = 0, *, amax_in=None, margin: int = 0, scale_inv_in=None):
     """Per-direction ("hybrid") quantization with block sub-quantizers
     ("[Pytorch][Common] Hybrid quantization #2817": each direction has a
     quantizer of its own, format and recipe, and blockwise or MXFP8
@@ -527,11 +535,14 @@ def quantize_hybrid_blockwise(x: np.ndarray, row_recipe: int, row_fmt: int, col_
     is the NaN code with that sign (the reading of the per-tensor
     rowwise_dequantized source, extended to block scales).  A recipe is
     128x128 blocks, 1x128 blocks (both with FP32 block scales, margin 0, like
-    quantize_block) or MXFP8 1x32 blocks with E8M0 scales (quantize_mx).
+    quantize_block), MXFP8 1x32 blocks with E8M0 scales (quantize_mx), or,
+    in one direction, per-tensor scaling (quantize_tensor with amax_in and
+    margin, or with scale_inv_in), whose scale is reported as [s].
     Returns dict(q_row [R][C], s_row, q_col [C][R], s_col)."""
     x = np.ascontiguousarray(x)
     rows, cols = x.shape
-    q_row, s_row = _block_subquantizer(x, row_recipe, row_fmt)
+    pt = dict(scale_inv_in=scale_inv_in) if amax_in is None else dict(amax_in=amax_in, margin=margin)
+    q_row, s_row = _block_subquantizer(x, row_recipe, row_fmt, pt)
     if col_source == COLSRC_ORIGINAL:
         src = x
     elif col_source == COLSRC_ROWWISE_DEQUANTIZED:
@@ -543,7 +554,7 @@ def quantize_hybrid_blockwise(x: np.ndarray, row_recipe: int, row_fmt: int, col_
         bits[nan] = np.uint32(0x7FC00000) | ((q_row[nan].astype(np.uint32) & 0x80) << 24)
     else:
         raise ValueError("unknown columnwise source %r" % col_source)
-    q_col, s_col = _block_subquantizer(transpose(np.ascontiguousarray(src)), col_recipe, col_fmt)
+    q_col, s_col = _block_subquantizer(transpose(np.ascontiguousarray(src)), col_recipe, col_fmt, pt)
     return dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col)
 
 

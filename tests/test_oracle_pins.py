@@ -845,6 +845,33 @@ def test_hybrid_blockwise_dequantized_mx_rows_exact_values():
     assert not np.array_equal(o["q_col"], h["q_col"])
 
 
+def test_hybrid_blockwise_with_one_per_tensor_direction():
+    """A per-tensor direction paired with a block one: per-tensor E4M3 rows
+    (current scaling, margin 1) with MXFP8 E5M2 columns reduce to the
+    per-tensor cast and the columnwise MXFP8 copy (both pinned above); 1x128
+    rows with per-tensor E5M2 columns of x^T likewise.  From the dequantized
+    per-tensor rows (a given scale), x' = fl32(value(q) * s) is the float64
+    product rounded once to binary32 (exact products of two binary32 values
+    fit float64), and the 128x128 columns are the block quantizer of x'^T."""
+    x = workloads.block_act(256, 384, seed=28)
+    am = oracle.amax(x)
+    h = oracle.quantize_hybrid_blockwise(x, oracle.SUBQ_PER_TENSOR, E4, oracle.SUBQ_MXFP8, E5, amax_in=am, margin=1)
+    r = oracle.quantize_tensor(x, E4, amax_in=am, margin=1)
+    qm, sm = oracle.quantize_mx_colwise(x, E5)
+    assert np.array_equal(h["q_row"], r["q"]) and h["s_row"].tolist() == [r["scale_inv"]]
+    assert np.array_equal(h["q_col"], qm) and np.array_equal(h["s_col"], sm)
+    h = oracle.quantize_hybrid_blockwise(x, oracle.SUBQ_BLOCK_1x128, E4, oracle.SUBQ_PER_TENSOR, E5, amax_in=am)
+    c = oracle.quantize_tensor(oracle.transpose(x), E5, amax_in=am)
+    assert np.array_equal(h["q_col"], c["q"]) and h["s_col"].tolist() == [c["scale_inv"]]
+    assert np.array_equal(h["q_row"], oracle.quantize_blocks(x, E4, 1, 128)[0])
+    s = np.float32(0.0037)
+    h = oracle.quantize_hybrid_blockwise(x, oracle.SUBQ_PER_TENSOR, E4, oracle.SUBQ_BLOCK_128x128, E4,
+                                         oracle.COLSRC_ROWWISE_DEQUANTIZED, scale_inv_in=s)
+    xp = (oracle.decode_table(E4)[h["q_row"]] * np.float64(s)).astype(np.float32)
+    q_ref, s_ref = oracle.quantize_blocks(np.ascontiguousarray(xp.T), E4, 128, 128)
+    assert np.array_equal(h["q_col"], q_ref) and np.array_equal(h["s_col"], s_ref)
+
+
 def test_hybrid_rowwise_dequantized_is_idempotent_in_one_format():
     """Quantize, dequantize, quantize again with the same format and scale
     gives the same codes (the FP8 grid is far coarser than one fp32 rounding
