@@ -27,7 +27,7 @@ PER_TENSOR, BLOCK_1x128_128x128, BLOCK_1x128_1x128, MXFP8 = 0, 1, 2, 3
 OUT_E4M3FN, OUT_E5M2 = 2, 3
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 COLSRC_ORIGINAL, COLSRC_ROWWISE_DEQUANTIZED = 0, 1
-SUBQ_BLOCK_128x128, SUBQ_BLOCK_1x128, SUBQ_MXFP8 = 0, 1, 2
+SUBQ_BLOCK_128x128, SUBQ_BLOCK_1x128, SUBQ_MXFP8, SUBQ_PER_TENSOR = 0, 1, 2, 3
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,7 +52,7 @@ SIGNATURES = {
     "fp8_quantize_hybrid": [_VP, _I32, _I64, _I64, _I32, _I32, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
                             _VP, _VP],
     "fp8_quantize_hybrid_blockwise": [_VP, _I32, _I64, _I64, _I32, _I32, _VP, _VP, _I32, _I32, _I32, _VP, _VP,
-                                      _VP],
+                                      _VP, _I32, _VP, _VP],
     "fp8_cast_stats": [_VP, _I32, _I64, _I32, _VP, _VP, _VP],
     "fp8_quantize_error_feedback": [_VP, _I32, _VP, _I64, _I32, _VP, _VP, _VP, _VP],
     "fp8q_clock_monitor": [_VP, _VP, _VP],
@@ -374,7 +374,9 @@ def fp8_quantize_hybrid(x, row_fmt, col_fmt, col_source, *, q_row=None, q_col=No
 
 def _subq_scales(recipe, rows, cols):
     """(dtype, element count) of the scale buffer of one direction's copy of a
-    [rows][cols] tensor under a block sub-quantizer."""
+    [rows][cols] tensor under a sub-quantizer."""
+    if recipe == SUBQ_PER_TENSOR:
+        return _F32, 1
     if recipe == SUBQ_BLOCK_128x128:
         return _F32, (rows // 128) * (cols // 128)
     if recipe == SUBQ_BLOCK_1x128:
@@ -383,21 +385,27 @@ def _subq_scales(recipe, rows, cols):
 
 
 def fp8_quantize_hybrid_blockwise(x, row_recipe, row_fmt, col_recipe, col_fmt, *, col_source=COLSRC_ORIGINAL,
-                                  q_row=None, s_row=None, q_col=None, s_col=None, stream=None):
-    """Per-direction block quantization: rowwise copy by row_recipe in row_fmt
-    (codes [rows][cols]), columnwise copy by col_recipe in col_fmt applied to
-    x^T or to the dequantized rows (codes [cols][rows]); scales float32
-    (blocks) or uint8 (MXFP8)."""
+                                  q_row=None, s_row=None, q_col=None, s_col=None, amax_in=None, margin=0,
+                                  scale_inv_in=None, stream=None):
+    """Per-direction quantization with block, MXFP8 or (in one direction)
+    per-tensor sub-quantizers: rowwise copy by row_recipe in row_fmt (codes
+    [rows][cols]), columnwise copy by col_recipe in col_fmt applied to x^T or
+    to the dequantized rows (codes [cols][rows]); scales float32 (blocks; one
+    float for a per-tensor direction, which takes amax_in or scale_inv_in) or
+    uint8 (MXFP8)."""
     rows, cols = _shape2(x)
-    if row_recipe in (SUBQ_BLOCK_128x128, SUBQ_BLOCK_1x128, SUBQ_MXFP8):
+    recipes = (SUBQ_BLOCK_128x128, SUBQ_BLOCK_1x128, SUBQ_MXFP8, SUBQ_PER_TENSOR)
+    if row_recipe in recipes:
         _need(q_row, "q_row", _U8, rows * cols)
         _need(s_row, "s_row", *_subq_scales(row_recipe, rows, cols))
-    if col_recipe in (SUBQ_BLOCK_128x128, SUBQ_BLOCK_1x128, SUBQ_MXFP8):
+    if col_recipe in recipes:
         _need(q_col, "q_col", _U8, rows * cols)
         _need(s_col, "s_col", *_subq_scales(col_recipe, cols, rows))
+    _scalars(amax_in=amax_in, scale_inv_in=scale_inv_in)
     _check(lib.fp8_quantize_hybrid_blockwise(_ptr(x, "x"), _dtype(x), rows, cols, row_recipe, row_fmt,
                                              _ptr(q_row, "q_row"), _ptr(s_row, "s_row"), col_recipe, col_fmt,
                                              col_source, _ptr(q_col, "q_col"), _ptr(s_col, "s_col"),
+                                             _ptr(amax_in, "amax_in"), margin, _ptr(scale_inv_in, "scale_inv_in"),
                                              _stream(stream)))
 
 

@@ -671,6 +671,7 @@ extern "C" int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, i
 // the columnwise copy)
 static int64_t subq_scale_bytes(int32_t recipe, int64_t rows, int64_t cols)
 {
+    if (recipe == FP8Q_SUBQ_PER_TENSOR) return 4;
     if (recipe == FP8Q_SUBQ_BLOCK_128x128) return (rows / 128) * (cols / 128) * 4;
     if (recipe == FP8Q_SUBQ_BLOCK_1x128) return rows * (cols / 128) * 4;
     return rows * (cols / 32);
@@ -678,13 +679,15 @@ static int64_t subq_scale_bytes(int32_t recipe, int64_t rows, int64_t cols)
 
 static bool valid_subq(int32_t r)
 {
-    return r == FP8Q_SUBQ_BLOCK_128x128 || r == FP8Q_SUBQ_BLOCK_1x128 || r == FP8Q_SUBQ_MXFP8;
+    return r == FP8Q_SUBQ_BLOCK_128x128 || r == FP8Q_SUBQ_BLOCK_1x128 || r == FP8Q_SUBQ_MXFP8 ||
+           r == FP8Q_SUBQ_PER_TENSOR;
 }
 
 static int fp8_quantize_hybrid_blockwise_impl(Call &c, const void *x, int32_t dtype, int64_t rows, int64_t cols,
                                               int32_t row_recipe, int32_t row_fmt, uint8_t *q_row, void *s_row,
                                               int32_t col_recipe, int32_t col_fmt, int32_t col_source,
-                                              uint8_t *q_col, void *s_col, void *stream)
+                                              uint8_t *q_col, void *s_col, const float *amax_in, int32_t margin,
+                                              const float *scale_inv_in, void *stream)
 {
     const char *fn = "fp8_quantize_hybrid_blockwise";
     if (!valid_dtype(dtype)) return fail(FP8Q_EINVAL, "%s: unknown dtype %d", fn, (int)dtype);
@@ -693,6 +696,21 @@ static int fp8_quantize_hybrid_blockwise_impl(Call &c, const void *x, int32_t dt
         return fail(FP8Q_EINVAL, "%s: unknown sub-quantizer (row %d, col %d)", fn, (int)row_recipe, (int)col_recipe);
     if (col_source != FP8Q_COLSRC_ORIGINAL && col_source != FP8Q_COLSRC_ROWWISE_DEQUANTIZED)
         return fail(FP8Q_EINVAL, "%s: unknown columnwise source %d", fn, (int)col_source);
+    // a per-tensor direction takes its scale from amax_in (current scaling
+    // with margin) or scale_inv_in; only one direction may be per-tensor
+    const int n_tensor = (row_recipe == FP8Q_SUBQ_PER_TENSOR) + (col_recipe == FP8Q_SUBQ_PER_TENSOR);
+    if (n_tensor == 2)
+        return fail(FP8Q_EINVAL, "%s: two per-tensor directions are fp8_quantize_hybrid's; here at most one", fn);
+    if (n_tensor == 1 && (amax_in == nullptr) == (scale_inv_in == nullptr))
+        return fail(FP8Q_EINVAL, "%s: the per-tensor direction needs exactly one of amax_in / scale_inv_in", fn);
+    if (n_tensor == 0 && (amax_in || scale_inv_in))
+        return fail(FP8Q_EINVAL, "%s: amax_in / scale_inv_in serve a per-tensor direction only", fn);
+    if ((amax_in && !aligned(amax_in, 4)) || (scale_inv_in && !aligned(scale_inv_in, 4)))
+        return fail(FP8Q_EINVAL, "%s: amax_in / scale_inv_in must be 4-byte aligned", fn);
+    if (col_recipe == FP8Q_SUBQ_PER_TENSOR && col_source == FP8Q_COLSRC_ROWWISE_DEQUANTIZED && amax_in)
+        return fail(FP8Q_EUNSUPPORTED,
+                    "%s: per-tensor columns of the dequantized rows need a given scale_inv_in (their amax is not "
+                    "known before the pass)", fn);
     if (rows < 0 || cols < 0) return fail(FP8Q_EINVAL, "%s: negative shape", fn);
     if (rows % 128 || cols % 128) return fail(FP8Q_EUNSUPPORTED, "%s: rows and cols must be multiples of 128", fn);
     if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 31)
@@ -707,15 +725,16 @@ static int fp8_quantize_hybrid_blockwise_impl(Call &c, const void *x, int32_t dt
         return fail(FP8Q_EINVAL, "%s: q_row / q_col must be 16-byte aligned", fn);
     if ((s_row && !aligned(s_row, 4)) || (s_col && !aligned(s_col, 4)))
         return fail(FP8Q_EINVAL, "%s: s_row / s_col must be 4-byte aligned", fn);
-    const void *buf[5] = {x, q_row, s_row, q_col, s_col};
-    const int64_t len[5] = {n * dsize(dtype), n, subq_scale_bytes(row_recipe, rows, cols), n,
+    const void *buf[7] = {x, amax_in, scale_inv_in, q_row, s_row, q_col, s_col};
+    const int64_t len[7] = {n * dsize(dtype), 4, 4, n, subq_scale_bytes(row_recipe, rows, cols), n,
                             subq_scale_bytes(col_recipe, cols, rows)};
-    for (int i = 0; i < 5; ++i)
+    for (int i = 3; i < 7; ++i) // the outputs against every other buffer
         for (int j = 0; j < i; ++j)
             if (overlap(buf[i], len[i], buf[j], len[j])) return fail(FP8Q_EINVAL, "%s: buffers overlap", fn);
+    const fp8q::ScaleSrc pt{amax_in, scale_inv_in, (int)margin};
     return hip_status(fp8q::launch_hybrid_blockwise(x, dtype, rows, cols, row_recipe, row_fmt, q_row, s_row,
                                                     col_recipe, col_fmt, q_col, s_col,
-                                                    col_source == FP8Q_COLSRC_ROWWISE_DEQUANTIZED,
+                                                    col_source == FP8Q_COLSRC_ROWWISE_DEQUANTIZED, pt,
                                                     (hipStream_t)stream),
                       fn);
 }
@@ -723,14 +742,17 @@ static int fp8_quantize_hybrid_blockwise_impl(Call &c, const void *x, int32_t dt
 extern "C" int fp8_quantize_hybrid_blockwise(const void *x, int32_t dtype, int64_t rows, int64_t cols,
                                              int32_t row_recipe, int32_t row_fmt, uint8_t *q_row, void *s_row,
                                              int32_t col_recipe, int32_t col_fmt, int32_t col_source, uint8_t *q_col,
-                                             void *s_col, void *stream)
+                                             void *s_col, const float *amax_in, int32_t margin,
+                                             const float *scale_inv_in, void *stream)
 {
     Call c("fp8_quantize_hybrid_blockwise", stream);
-    c.args("dtype=%lld rows=%lld cols=%lld row_recipe=%lld row_fmt=%lld col_recipe=%lld col_fmt=%lld col_source=%lld",
+    c.args("dtype=%lld rows=%lld cols=%lld row_recipe=%lld row_fmt=%lld col_recipe=%lld col_fmt=%lld col_source=%lld "
+           "margin=%lld",
            (long long)dtype, (long long)rows, (long long)cols, (long long)row_recipe, (long long)row_fmt,
-           (long long)col_recipe, (long long)col_fmt, (long long)col_source);
+           (long long)col_recipe, (long long)col_fmt, (long long)col_source, (long long)margin);
     return c.ret(fp8_quantize_hybrid_blockwise_impl(c, x, dtype, rows, cols, row_recipe, row_fmt, q_row, s_row,
-                                                    col_recipe, col_fmt, col_source, q_col, s_col, stream));
+                                                    col_recipe, col_fmt, col_source, q_col, s_col, amax_in, margin,
+                                                    scale_inv_in, stream));
 }
 
 static int fp8_cast_stats_impl(Call &c, const void *x, int32_t dtype, int64_t n, int32_t fmt, const float *scale_inv,

@@ -102,18 +102,20 @@ hipError_t launch_hybrid(const void *x, int dtype, int64_t rows, int64_t cols, i
                          float *row_scale_inv_out, float *col_scale_inv_out, float *amax_out, const Reduce &r,
                          hipStream_t s);
 
-// Block sub-quantizers of a per-direction quantization (values of the C
-// ABI's FP8Q_SUBQ_*).
-enum Subq { kSubqBlock128 = 0, kSubqBlock1x128 = 1, kSubqMX = 2 };
+// Sub-quantizers of a per-direction quantization (values of the C ABI's
+// FP8Q_SUBQ_*).
+enum Subq { kSubqBlock128 = 0, kSubqBlock1x128 = 1, kSubqMX = 2, kSubqTensor = 3 };
 
 // The rowwise copy by row_recipe in row_fmt and the columnwise copy by
 // col_recipe in col_fmt, both from one pass over x; the columnwise copy is
 // taken from x, or (col_from_rows) from the dequantized row codes.  A copy
 // whose code pointer is null is skipped.  Scale buffers: float for the
-// 128x128 and 1x128 blocks, E8M0 bytes for MXFP8.
+// 128x128 and 1x128 blocks, E8M0 bytes for MXFP8, one float (the s used) for
+// a per-tensor direction, whose scale comes from pt (at most one direction is
+// per-tensor).
 hipError_t launch_hybrid_blockwise(const void *x, int dtype, int64_t rows, int64_t cols, int row_recipe, int row_fmt,
                                    uint8_t *q_row, void *s_row, int col_recipe, int col_fmt, uint8_t *q_col,
-                                   void *s_col, bool col_from_rows, hipStream_t s);
+                                   void *s_col, bool col_from_rows, ScaleSrc pt, hipStream_t s);
 
 // stats[0..3] (uint64): overflows, underflows, NaNs, nonzeros of the cast of
 // x with dequant scale *scale_inv.

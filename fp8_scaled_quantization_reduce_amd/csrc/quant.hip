@@ -1213,6 +1213,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
         }
         if (blockIdx.x == 0 && threadIdx.x == 0 && col_scale_inv_out) *col_scale_inv_out = sc_col.s;
     }
+    // per-tensor column codes under a block recipe of the rows
+    constexpr bool kColTensor = kColMode == kTilePerTensor && kMode != kTilePerTensor;
+    if constexpr (kColTensor) {
+        sc_col = resolve_scales<FC>(src_col);
+        if (blockIdx.x == 0 && threadIdx.x == 0 && col_scale_inv_out) *col_scale_inv_out = sc_col.s;
+    }
     uint32_t m_all = 0; // per-tensor fused amax
 
     // Cache hints, chosen per mode by measurement on the MI355X (unlike the
@@ -1271,6 +1277,10 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
             if (!(pmax <= kInfBits && finite_nonzero(sc_tensor.scale))) {
                 opaque(p);
                 enc_rows(Rep<true>{}, sc_tensor.scale);
+            }
+            if constexpr (kColDeq) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dq[r] = sc_tensor.s;
             }
         } else if constexpr (kMode == kTileBlock128) {
             uint32_t rm[4];
@@ -1600,6 +1610,30 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                     enc_cols(Rep<true>{});
                 }
                 stage_transposed(tl, cc, ig, jg);
+            } else if constexpr (kColTensor) {
+                // per-tensor column codes of x or x' with their own scale
+                uint32_t cmx[16];
+                col_max(cmx);
+                uint32_t lm = 0;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) lm = max(lm, cmx[k]);
+                const bool clean = lm <= kInfBits && finite_nonzero(sc_col.scale);
+                uint32_t cc[4][4];
+                auto enc_cols = [&](auto rep) {
+                    constexpr bool kR = decltype(rep)::value;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4)
+                            cc[r][q4] = encode4<FC, kR>(cv(rep, r, 4 * q4), cv(rep, r, 4 * q4 + 1),
+                                                        cv(rep, r, 4 * q4 + 2), cv(rep, r, 4 * q4 + 3), sc_col.scale);
+                };
+                enc_cols(Rep<false>{});
+                if (!clean) {
+                    opaque(p);
+                    enc_cols(Rep<true>{});
+                }
+                stage_transposed(tl, cc, ig, jg);
             } else if constexpr (!kColMX) { // (MXFP8 staged its own column codes above)
                 stage_transposed(tl, cw, ig, jg);
             }
@@ -1767,86 +1801,100 @@ hipError_t launch_mx(const void *x, int dtype, int64_t rows, int64_t cols, int f
     return launch_mx_t<kE5M2, kF32>(x, rows, cols, q_row, s_row, q_col, s_col, s);
 }
 
-// One pass over x: the row codes by the block recipe kMode in F, the column
-// codes by the block recipe kColMode in FC, from x or (kDeq) from the
-// dequantized row codes; either copy may be absent (its code and scale
-// pointers null).  A pass with MXFP8 codes runs one tile per block, the
-// block-scaled ones loop over tiles (the measured faster forms).
+// The buffers and the per-tensor scale source of one per-direction pass.
+struct SubqArgs {
+    const void *x;
+    int64_t rows, cols;
+    uint8_t *q_row;
+    void *s_row; // block scales, or the one float a per-tensor direction reports its s in
+    uint8_t *q_col;
+    void *s_col;
+    ScaleSrc pt; // the per-tensor direction's scale source
+};
+
+// One pass over x: the row codes by the recipe kMode in F, the column codes by
+// the recipe kColMode in FC (block recipes, or per-tensor scaling in one of
+// the two directions), from x or (kDeq) from the dequantized row codes;
+// either copy may be absent (its code and scale pointers null).  A pass with
+// MXFP8 or per-tensor codes runs one tile per block, the block-scaled ones
+// loop over tiles (the measured faster forms).
 template <int F, int FC, int DT, int kMode, int kColMode, bool kDeq>
-static hipError_t launch_subq_m(const void *x, int64_t rows, int64_t cols, uint8_t *q_row, void *s_row,
-                                uint8_t *q_col, void *s_col, hipStream_t s)
+static hipError_t launch_subq_m(const SubqArgs &a, hipStream_t s)
 {
-    const int grid = (kMode == kTileMX || kColMode == kTileMX) ? tile_grid(rows, cols)
-                                                               : min(tile_grid(rows, cols), kBlockQuantGrid);
+    constexpr bool kRowT = kMode == kTilePerTensor, kColT = kColMode == kTilePerTensor;
+    const int grid = (kMode == kTileMX || kColMode == kTileMX || kRowT || kColT)
+                         ? tile_grid(a.rows, a.cols)
+                         : min(tile_grid(a.rows, a.cols), kBlockQuantGrid);
     const ScaleSrc none{nullptr, nullptr, 0};
     tile_kernel<F, DT, kMode, false, FC, kColMode, kDeq><<<grid, kThreads, 0, s>>>(
-        x, rows, cols, none, q_row, q_col, s_row, s_col, nullptr, nullptr, nullptr, none, nullptr, Finish{});
+        a.x, a.rows, a.cols, kRowT ? a.pt : none, a.q_row, a.q_col, kRowT ? nullptr : a.s_row,
+        kColT ? nullptr : a.s_col, kRowT ? reinterpret_cast<float *>(a.s_row) : nullptr, nullptr, nullptr,
+        kColT ? a.pt : none, kColT ? reinterpret_cast<float *>(a.s_col) : nullptr, Finish{});
     return hipGetLastError();
 }
 
 template <int F, int FC, int DT, int kMode, bool kDeq>
-static hipError_t launch_subq_c(int col_recipe, const void *x, int64_t rows, int64_t cols, uint8_t *q_row,
-                                void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
+static hipError_t launch_subq_c(int col_recipe, const SubqArgs &a, hipStream_t s)
 {
-#define FP8Q_ARGS x, rows, cols, q_row, s_row, q_col, s_col, s
     switch (col_recipe) {
-    case kSubqBlock128: return launch_subq_m<F, FC, DT, kMode, kTileBlock128, kDeq>(FP8Q_ARGS);
-    case kSubqBlock1x128: return launch_subq_m<F, FC, DT, kMode, kTileBlock1x128, kDeq>(FP8Q_ARGS);
-    case kSubqMX: return launch_subq_m<F, FC, DT, kMode, kTileMX, kDeq>(FP8Q_ARGS);
+    case kSubqBlock128: return launch_subq_m<F, FC, DT, kMode, kTileBlock128, kDeq>(a, s);
+    case kSubqBlock1x128: return launch_subq_m<F, FC, DT, kMode, kTileBlock1x128, kDeq>(a, s);
+    case kSubqMX: return launch_subq_m<F, FC, DT, kMode, kTileMX, kDeq>(a, s);
+    case kSubqTensor:
+        // (two per-tensor directions are the per-tensor hybrid's, not this pass's)
+        if constexpr (kMode != kTilePerTensor) return launch_subq_m<F, FC, DT, kMode, kTilePerTensor, kDeq>(a, s);
+        break;
     }
-#undef FP8Q_ARGS
     return hipErrorInvalidValue;
 }
 
 template <int F, int FC, int DT, bool kDeq>
-static hipError_t launch_subq_r(int row_recipe, int col_recipe, const void *x, int64_t rows, int64_t cols,
-                                uint8_t *q_row, void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
+static hipError_t launch_subq_r(int row_recipe, int col_recipe, const SubqArgs &a, hipStream_t s)
 {
-#define FP8Q_ARGS col_recipe, x, rows, cols, q_row, s_row, q_col, s_col, s
     switch (row_recipe) {
-    case kSubqBlock128: return launch_subq_c<F, FC, DT, kTileBlock128, kDeq>(FP8Q_ARGS);
-    case kSubqBlock1x128: return launch_subq_c<F, FC, DT, kTileBlock1x128, kDeq>(FP8Q_ARGS);
-    case kSubqMX: return launch_subq_c<F, FC, DT, kTileMX, kDeq>(FP8Q_ARGS);
+    case kSubqBlock128: return launch_subq_c<F, FC, DT, kTileBlock128, kDeq>(col_recipe, a, s);
+    case kSubqBlock1x128: return launch_subq_c<F, FC, DT, kTileBlock1x128, kDeq>(col_recipe, a, s);
+    case kSubqMX: return launch_subq_c<F, FC, DT, kTileMX, kDeq>(col_recipe, a, s);
+    case kSubqTensor: return launch_subq_c<F, FC, DT, kTilePerTensor, kDeq>(col_recipe, a, s);
     }
-#undef FP8Q_ARGS
     return hipErrorInvalidValue;
 }
 
 template <int F, int FC>
-static hipError_t launch_subq_d(int dtype, bool deq, int row_recipe, int col_recipe, const void *x, int64_t rows,
-                                int64_t cols, uint8_t *q_row, void *s_row, uint8_t *q_col, void *s_col, hipStream_t s)
+static hipError_t launch_subq_d(int dtype, bool deq, int row_recipe, int col_recipe, const SubqArgs &a,
+                                hipStream_t s)
 {
-#define FP8Q_ARGS row_recipe, col_recipe, x, rows, cols, q_row, s_row, q_col, s_col, s
     if (deq) {
-        if (dtype == kBF16) return launch_subq_r<F, FC, kBF16, true>(FP8Q_ARGS);
-        return launch_subq_r<F, FC, kF32, true>(FP8Q_ARGS);
+        if (dtype == kBF16) return launch_subq_r<F, FC, kBF16, true>(row_recipe, col_recipe, a, s);
+        return launch_subq_r<F, FC, kF32, true>(row_recipe, col_recipe, a, s);
     }
-    if (dtype == kBF16) return launch_subq_r<F, FC, kBF16, false>(FP8Q_ARGS);
-    return launch_subq_r<F, FC, kF32, false>(FP8Q_ARGS);
-#undef FP8Q_ARGS
+    if (dtype == kBF16) return launch_subq_r<F, FC, kBF16, false>(row_recipe, col_recipe, a, s);
+    return launch_subq_r<F, FC, kF32, false>(row_recipe, col_recipe, a, s);
 }
 
 hipError_t launch_hybrid_blockwise(const void *x, int dtype, int64_t rows, int64_t cols, int row_recipe, int row_fmt,
                                    uint8_t *q_row, void *s_row, int col_recipe, int col_fmt, uint8_t *q_col,
-                                   void *s_col, bool col_from_rows, hipStream_t s)
+                                   void *s_col, bool col_from_rows, ScaleSrc pt, hipStream_t s)
 {
     if (rows == 0 || cols == 0) return hipSuccess;
     // one direction alone: the single-format kernel of its recipe (the
-    // dequantized source still forms the row codes, unstored)
+    // dequantized source still forms the row codes, unstored); a per-tensor
+    // direction alone pairs with an unstored block copy of the other
     const bool deq = col_from_rows && q_col;
     if (!q_col) {
-        col_recipe = row_recipe;
+        col_recipe = row_recipe == kSubqTensor ? kSubqBlock128 : row_recipe;
         col_fmt = row_fmt;
     }
     if (!q_row && !deq) {
-        row_recipe = col_recipe;
+        row_recipe = col_recipe == kSubqTensor ? kSubqBlock128 : col_recipe;
         row_fmt = col_fmt;
     }
-#define FP8Q_ARGS dtype, deq, row_recipe, col_recipe, x, rows, cols, q_row, s_row, q_col, s_col, s
+    const SubqArgs a{x, rows, cols, q_row, s_row, q_col, s_col, pt};
     if (row_fmt == kE4M3)
-        return col_fmt == kE4M3 ? launch_subq_d<kE4M3, kE4M3>(FP8Q_ARGS) : launch_subq_d<kE4M3, kE5M2>(FP8Q_ARGS);
-    return col_fmt == kE4M3 ? launch_subq_d<kE5M2, kE4M3>(FP8Q_ARGS) : launch_subq_d<kE5M2, kE5M2>(FP8Q_ARGS);
-#undef FP8Q_ARGS
+        return col_fmt == kE4M3 ? launch_subq_d<kE4M3, kE4M3>(dtype, deq, row_recipe, col_recipe, a, s)
+                                : launch_subq_d<kE4M3, kE5M2>(dtype, deq, row_recipe, col_recipe, a, s);
+    return col_fmt == kE4M3 ? launch_subq_d<kE5M2, kE4M3>(dtype, deq, row_recipe, col_recipe, a, s)
+                            : launch_subq_d<kE5M2, kE5M2>(dtype, deq, row_recipe, col_recipe, a, s);
 }
 
 hipError_t launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int block_rows, uint8_t *q_row,

@@ -92,11 +92,12 @@ extern "C" {
 #define FP8Q_COLSRC_ORIGINAL 0
 #define FP8Q_COLSRC_ROWWISE_DEQUANTIZED 1
 
-/* block sub-quantizers of one direction in fp8_quantize_hybrid_blockwise,
- * [HYBRID] (the per-direction quantizer may be a blockwise or MXFP8 one) */
+/* sub-quantizers of one direction in fp8_quantize_hybrid_blockwise, [HYBRID]
+ * (the per-direction quantizer may be a blockwise, MXFP8 or per-tensor one) */
 #define FP8Q_SUBQ_BLOCK_128x128 0 /* fp32 scale per 128x128 block, as fp8_quantize_block(block_rows 128) */
 #define FP8Q_SUBQ_BLOCK_1x128 1   /* fp32 scale per 1x128 segment, as fp8_quantize_block(block_rows 1) */
 #define FP8Q_SUBQ_MXFP8 2         /* E8M0 byte per 1x32 segment, as fp8_quantize_mx */
+#define FP8Q_SUBQ_PER_TENSOR 3    /* one scale for the whole copy, as fp8_quantize_tensor */
 
 /* epilogue activations, [MFP8] section 6 */
 #define FP8Q_ACT_NONE 0
@@ -379,6 +380,15 @@ int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, int64_t cols
  *     is NaN (a NaN row code, or a zero code times an infinite block scale)
  *     its column code is the NaN code with the row code's sign bit.  The row
  *     codes are formed even when q_row is NULL.
+ *   FP8Q_SUBQ_PER_TENSOR in one direction (not both: two per-tensor
+ *     directions are fp8_quantize_hybrid's): that copy is the per-tensor cast
+ *     of fp8_quantize_tensor with the scale from amax_in (current scaling,
+ *     with margin) or from scale_inv_in (exactly one of them, device floats);
+ *     its scale buffer is one float that receives the dequant scale s used
+ *     (the dequantized rows of a per-tensor row copy use that s).  Per-tensor
+ *     columns of the dequantized rows take scale_inv_in only (their amax is
+ *     not known before the pass: FP8Q_EUNSUPPORTED with amax_in).  Without a
+ *     per-tensor direction amax_in and scale_inv_in must be NULL.
  *   Either copy may be skipped (its code and scale pointers both NULL), not
  *   both.  The call reads x once, whatever the two recipes and formats (with
  *   one recipe both ways, both formats take their scales from the same block
@@ -390,7 +400,8 @@ int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, int64_t cols
  */
 int fp8_quantize_hybrid_blockwise(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t row_recipe,
                                   int32_t row_fmt, uint8_t *q_row, void *s_row, int32_t col_recipe, int32_t col_fmt,
-                                  int32_t col_source, uint8_t *q_col, void *s_col, void *stream);
+                                  int32_t col_source, uint8_t *q_col, void *s_col, const float *amax_in,
+                                  int32_t margin, const float *scale_inv_in, void *stream);
 
 /*
  * fp8_cast_stats -- diagnostics of the per-tensor cast of x with dequant

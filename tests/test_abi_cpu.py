@@ -56,6 +56,7 @@ def test_enum_values_match_header():
     assert int(defs["FP8Q_SUBQ_BLOCK_128x128"]) == fq.SUBQ_BLOCK_128x128 == oracle.SUBQ_BLOCK_128x128
     assert int(defs["FP8Q_SUBQ_BLOCK_1x128"]) == fq.SUBQ_BLOCK_1x128 == oracle.SUBQ_BLOCK_1x128
     assert int(defs["FP8Q_SUBQ_MXFP8"]) == fq.SUBQ_MXFP8 == oracle.SUBQ_MXFP8
+    assert int(defs["FP8Q_SUBQ_PER_TENSOR"]) == fq.SUBQ_PER_TENSOR == oracle.SUBQ_PER_TENSOR
 
 
 def _expect(status, code, fragment):
@@ -229,15 +230,24 @@ def test_hybrid_blockwise_validation():
     X, QR, SR, QC, SC = BAD, BAD + 0x100000, BAD + 0x200000, BAD + 0x300000, BAD + 0x400000
 
     def call(dtype=fq.BF16, rows=256, cols=384, rr=fq.SUBQ_MXFP8, rf=0, cr=fq.SUBQ_BLOCK_1x128, cf=1, src=0, x=X,
-             qr=QR, sr=SR, qc=QC, sc=SC):
-        return h(x, dtype, rows, cols, rr, rf, qr, sr, cr, cf, src, qc, sc, S)
+             qr=QR, sr=SR, qc=QC, sc=SC, am=None, si=None):
+        return h(x, dtype, rows, cols, rr, rf, qr, sr, cr, cf, src, qc, sc, am, 0, si, S)
 
     _expect(call(dtype=5), fq.EINVAL, "dtype")
     _expect(call(rf=2), fq.EINVAL, "format")
     _expect(call(cf=-1), fq.EINVAL, "format")
-    _expect(call(rr=3), fq.EINVAL, "sub-quantizer")
+    _expect(call(rr=4), fq.EINVAL, "sub-quantizer")
     _expect(call(cr=-1), fq.EINVAL, "sub-quantizer")
     _expect(call(src=2), fq.EINVAL, "columnwise source")
+    A = BAD + 0x500000
+    _expect(call(rr=fq.SUBQ_PER_TENSOR, cr=fq.SUBQ_PER_TENSOR, am=A), fq.EINVAL, "two per-tensor")
+    _expect(call(rr=fq.SUBQ_PER_TENSOR), fq.EINVAL, "exactly one of amax_in")
+    _expect(call(rr=fq.SUBQ_PER_TENSOR, am=A, si=A + 4), fq.EINVAL, "exactly one of amax_in")
+    _expect(call(am=A), fq.EINVAL, "per-tensor direction only")
+    _expect(call(rr=fq.SUBQ_PER_TENSOR, am=A + 2), fq.EINVAL, "4-byte aligned")
+    _expect(call(cr=fq.SUBQ_PER_TENSOR, src=1, am=A), fq.EUNSUPPORTED, "given scale_inv_in")
+    _expect(call(rr=fq.SUBQ_PER_TENSOR, am=A, sr=QR + 0x10), fq.EINVAL, "overlap")
+    _expect(call(cr=fq.SUBQ_PER_TENSOR, si=A, sc=A), fq.EINVAL, "overlap")
     _expect(call(rows=-128), fq.EINVAL, "negative")
     _expect(call(cols=200), fq.EUNSUPPORTED, "multiples of 128")
     _expect(call(sr=None), fq.EINVAL, "q_row and s_row")
@@ -354,7 +364,7 @@ def test_valid_calls_without_a_device_return_ehip():
         ("fp8_quantize_hybrid_blockwise",
          lambda: L.fp8_quantize_hybrid_blockwise(BAD, fq.BF16, 128, 128, fq.SUBQ_MXFP8, 0, BAD + 0x100000,
                                                  BAD + 0x200000, fq.SUBQ_BLOCK_128x128, 1, 1, BAD + 0x300000,
-                                                 BAD + 0x400000, S)),
+                                                 BAD + 0x400000, None, 0, None, S)),
         ("fp8_update_scale_delayed", lambda: L.fp8_update_scale_delayed(BAD, 16, 1, 0, BAD + 0x100, 0, 0, 0, 0,
                                                                         BAD + 0x200, BAD + 0x300, S)),
         ("fp8_scaled_gemm", lambda: L.fp8_scaled_gemm(BAD + 0x100000, 0, BAD, BAD + 0x200000, 0, BAD + 4, 128, 128,

@@ -14,14 +14,15 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import first_mismatches, host, same_f32, to_dev
+from gpu_util import first_mismatches, host, same_f32, scalar, to_dev
 
 pytestmark = pytest.mark.gpu
 
 fq = pytest.importorskip("fp8_scaled_quantization_reduce_amd")
 E4, E5 = oracle.E4M3FN, oracle.E5M2
 B128, B1x128, MX = oracle.SUBQ_BLOCK_128x128, oracle.SUBQ_BLOCK_1x128, oracle.SUBQ_MXFP8
-NAMES = {B128: "128x128", B1x128: "1x128", MX: "mxfp8"}
+PT = oracle.SUBQ_PER_TENSOR
+NAMES = {B128: "128x128", B1x128: "1x128", MX: "mxfp8", PT: "tensor"}
 ORIG, DEQ = oracle.COLSRC_ORIGINAL, oracle.COLSRC_ROWWISE_DEQUANTIZED
 
 
@@ -29,11 +30,13 @@ def _scale_buf(recipe, rows, cols):
     """Sentinel-filled scale buffer of one direction's copy ([rows][cols])."""
     if recipe == MX:
         return torch.full((rows, cols // 32), 0xA5, dtype=torch.uint8, device="cuda")
+    if recipe == PT:
+        return torch.full((1,), -7.25, dtype=torch.float32, device="cuda")
     n = (rows // 128) * (cols // 128) if recipe == B128 else rows * (cols // 128)
     return torch.full((n,), -7.25, dtype=torch.float32, device="cuda")
 
 
-def _gpu(x, row_recipe, row_fmt, col_recipe, col_fmt, want_row=True, want_col=True, src=0):
+def _gpu(x, row_recipe, row_fmt, col_recipe, col_fmt, want_row=True, want_col=True, src=0, pt=None):
     rows, cols = x.shape
     q_row = s_row = q_col = s_col = None
     if want_row:
@@ -42,8 +45,10 @@ def _gpu(x, row_recipe, row_fmt, col_recipe, col_fmt, want_row=True, want_col=Tr
     if want_col:
         q_col = torch.full((cols, rows), 0xA5, dtype=torch.uint8, device="cuda")
         s_col = _scale_buf(col_recipe, cols, rows)
+    kw = {k: scalar(float(v)) for k, v in (pt or {}).items() if k != "margin"}
     fq.fp8_quantize_hybrid_blockwise(to_dev(x), row_recipe, row_fmt, col_recipe, col_fmt, col_source=src,
-                                     q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col)
+                                     q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col,
+                                     margin=(pt or {}).get("margin", 0), **kw)
     return {k: None if v is None else host(v) for k, v in
             dict(q_row=q_row, s_row=s_row, q_col=q_col, s_col=s_col).items()}
 
@@ -176,3 +181,28 @@ def test_full_size_e4m3_rows_e5m2_cols(recipes, shape, make, src):
     assert x.shape == shape
     got = _gpu(x, recipes[0], E4, recipes[1], E5, src=src)
     _check(got, oracle.quantize_hybrid_blockwise(x, recipes[0], E4, recipes[1], E5, src))
+
+
+@pytest.mark.parametrize("mode", ["current", "given", "dequantized"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("recipes", [(PT, B128), (PT, B1x128), (PT, MX), (B128, PT), (B1x128, PT), (MX, PT)],
+                         ids=lambda r: NAMES[r[0]] + "_" + NAMES[r[1]])
+def test_one_per_tensor_direction(recipes, dtype, mode):
+    """A per-tensor direction paired with a block or MXFP8 one, in one pass:
+    current scaling from amax_in with a margin (no specials: a NaN would make
+    the per-tensor scale NaN), a given scale (with specials, saturating), and
+    the dequantized rows (a given scale for per-tensor columns)."""
+    x = _input(dtype, 256, 384, seed=307, specials=mode != "current")
+    src = DEQ if mode == "dequantized" else ORIG
+    pt = dict(amax_in=oracle.amax(x), margin=1) if mode == "current" else dict(scale_inv_in=np.float32(0.0173))
+    got = _gpu(x, recipes[0], E4, recipes[1], E5, src=src, pt=pt)
+    _check(got, oracle.quantize_hybrid_blockwise(x, recipes[0], E4, recipes[1], E5, src, **pt))
+
+
+def test_per_tensor_rows_mxfp8_columns_full_size():
+    """Per-tensor current-scaled E4M3 rows with MXFP8 E5M2 columns of an
+    8192 x 8192 bf16 delayed-scaling input, every code and scale compared."""
+    x = workloads.delayed_step(2)
+    pt = dict(amax_in=oracle.amax(x), margin=0)
+    got = _gpu(x, PT, E4, MX, E5, pt=pt)
+    _check(got, oracle.quantize_hybrid_blockwise(x, PT, E4, MX, E5, **pt))
