@@ -947,6 +947,13 @@ hipError_t launch_delayed_step(const void *x, int dtype, int64_t n, int fmt, flo
 // kTileHybrid + colF + 2 * dequantized_source: per-direction per-tensor
 // quantization (row codes in format F, column codes in format colF with their
 // own scale, from x or from the dequantized row codes).
+//
+// tile_kernel<F, DT, kMode, kAmax, FCol, kColMode, kColDeq>: the row codes by
+// the recipe kMode in format F; the column codes in format FCol by the recipe
+// kColMode (by default the row recipe, so the single-recipe modes above are
+// tile_kernel<F, DT, kMode, kAmax>), from x or, with kColDeq, from the
+// dequantized row codes.  A pass quantizes each direction with its own block
+// maxima; at most one of the two directions is per-tensor when they differ.
 enum TileMode { kTilePerTensor = 0, kTileBlock128 = 1, kTileBlock1x128 = 2, kTileMX = 3, kTileHybrid = 4 };
 
 // MXFP8 shared scale of one 32-element block from its magnitude max (float
