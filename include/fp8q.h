@@ -395,8 +395,11 @@ int fp8_quantize_hybrid(const void *x, int32_t dtype, int64_t rows, int64_t cols
  *   maxima).  Scale pointers are void *: float or byte buffers as above,
  *   4-byte aligned; code buffers 16-byte aligned.
  * Errors: FP8Q_EINVAL for unknown enums, a code pointer without its scale
- * pointer (or the reverse), no copy at all, misalignment or overlapping
- * buffers; FP8Q_EUNSUPPORTED for shapes that are not multiples of 128.
+ * pointer (or the reverse), no copy at all, two per-tensor directions, a
+ * per-tensor direction without exactly one of amax_in / scale_inv_in (or
+ * either of them without a per-tensor direction), misalignment or overlapping
+ * buffers; FP8Q_EUNSUPPORTED for shapes that are not multiples of 128 and for
+ * per-tensor columns of the dequantized rows with amax_in.
  */
 int fp8_quantize_hybrid_blockwise(const void *x, int32_t dtype, int64_t rows, int64_t cols, int32_t row_recipe,
                                   int32_t row_fmt, uint8_t *q_row, void *s_row, int32_t col_recipe, int32_t col_fmt,
