@@ -1379,7 +1379,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(const void *__restrict__
                         cw[r][q4] = encode4<F, true>(PV(r, 4 * q4), PV(r, 4 * q4 + 1), PV(r, 4 * q4 + 2),
                                                      PV(r, 4 * q4 + 3), sc.scale);
                 }
-                // stored now: the rowwise codes need not stay live through the column phase
+                // stored now (unless the column codes come from them, the rowwise
+                // codes need not stay live through the column phase)
                 if (q_row && valid)
                     *reinterpret_cast<uint4 *>(q_row + (r0 + r) * cols + c0) =
                         make_uint4(cw[r][0], cw[r][1], cw[r][2], cw[r][3]);
