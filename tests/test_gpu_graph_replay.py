@@ -180,3 +180,42 @@ def test_gemm_amax_and_cast_stats_replayed():
         R = oracle.gemm_reference(a, E4, sa, b, E4, sb)
         assert np.max(np.abs(c32.astype(np.float64) - R)) <= 1e-2 * np.max(np.abs(R)), r
         assert np.array_equal(st_rep.astype(np.uint64), oracle.cast_stats(xs, E4, np.float32(0.01)).astype(np.uint64)), r
+
+
+def test_hybrid_blockwise_replayed():
+    """The per-direction quantization (per-tensor E4M3 rows with a given
+    scale, MXFP8 E5M2 columns of the dequantized rows) captured once and
+    replayed on new inputs: every replay matches the oracle for its own
+    input, codes and scales bit for bit."""
+    xs = _inputs(4, seed=9)
+    x = torch.empty(SHAPE, dtype=torch.bfloat16, device="cuda")
+    rows, cols = SHAPE
+    q_row = torch.empty(SHAPE, dtype=torch.uint8, device="cuda")
+    q_col = torch.empty((cols, rows), dtype=torch.uint8, device="cuda")
+    s_row = scalar(-1.0)
+    s_col = torch.empty((cols, rows // 32), dtype=torch.uint8, device="cuda")
+    si = scalar(0.05)
+
+    def call():
+        fq.fp8_quantize_hybrid_blockwise(x, fq.SUBQ_PER_TENSOR, E4, fq.SUBQ_MXFP8, E5,
+                                         col_source=fq.COLSRC_ROWWISE_DEQUANTIZED, q_row=q_row, s_row=s_row,
+                                         q_col=q_col, s_col=s_col, scale_inv_in=si)
+    x.copy_(_bf16(xs[0]))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for xr in xs:
+        x.copy_(_bf16(xr))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = oracle.quantize_hybrid_blockwise(xr, oracle.SUBQ_PER_TENSOR, E4, oracle.SUBQ_MXFP8, E5,
+                                                oracle.COLSRC_ROWWISE_DEQUANTIZED, scale_inv_in=np.float32(0.05))
+        assert np.array_equal(host(q_row), want["q_row"]) and f32_bits(host(s_row)[0]) == f32_bits(want["s_row"][0])
+        assert np.array_equal(host(q_col), want["q_col"]) and np.array_equal(host(s_col), want["s_col"])
